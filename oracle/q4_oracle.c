@@ -1,0 +1,318 @@
+/*
+ * q4_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * The plain, slow, single-threaded fp64 CPU definition of what the INT4
+ * weight-streaming decode path computes.  Only the tests, the smoke check
+ * and the CPU-baseline leg of the benchmark may load this library; the
+ * product path never calls it and shares no code, header or table with it.
+ *
+ * What is computed, and where it comes from:
+ *
+ *   PIPO: Pipelined Offloading for Efficient Inference on Consumer Devices,
+ *   "Method", bullet "Computation optimization": the kernel multiplies a
+ *   vector directly by 4-bit quantized weights without first dequantizing
+ *   them.  The result it reaches is, up to summation order, the ordinary
+ *   matrix-vector product with the dequantized matrix, so this file writes
+ *   that definition out: dequantize one weight, multiply, add, in k order.
+ *
+ *   The pages give no bit layout.  The reading used throughout (and stated
+ *   in the design notes):
+ *     - codes are unsigned 4-bit values 0..15 with zero point 8;
+ *     - weight w[n][k] = s[n][k/32] * (c[n][k] - 8);
+ *     - one IEEE binary16 scale per group of 32 consecutive k, scales stored
+ *       row-major [N][K/32];
+ *     - two codes per byte, row-major [N][K/2]: byte j of a row holds
+ *       code 2j in bits 0..3 and code 2j+1 in bits 4..7;
+ *     - codes given to pack are masked to their low nibble.
+ *
+ *   The decode-layer glue (RMSNorm, one-token attention stand-in, SiLU gate)
+ *   is not described on the pages at all; what is written here is the plain
+ *   Llama-shaped reading of a per-layer decode step whose matrices are fused
+ *   QKV, O, fused gate+up and down (see q4o_decode_layer).
+ *
+ * Everything is fp64 except where the method itself stores fp16: the
+ * activation vectors fed to each matrix product are binary16, rounded
+ * to nearest-even by q4o_f64_to_f16 below.
+ *
+ * Parity pins for every function live in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* binary16 <-> double, written from the IEEE 754 definition            */
+/* ------------------------------------------------------------------ */
+
+/* IEEE 754-2008 binary16: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits.  exponent 0 = zero/subnormal (value = f * 2^-24),
+ * exponent 31 = inf/nan, otherwise (1024 + f) * 2^(e - 25). */
+double q4o_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* Round a non-negative double that holds an exact value q (< 2^12) to the
+ * nearest integer, ties to even. */
+static double round_half_even(double q)
+{
+    double fl = floor(q);
+    double fr = q - fl; /* exact: q has few integer bits */
+    if (fr > 0.5)
+        return fl + 1.0;
+    if (fr < 0.5)
+        return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* double -> binary16, round to nearest, ties to even; overflow -> inf. */
+uint16_t q4o_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7E00u);
+    /* 65504 is the largest finite value; 65520 is the midpoint to the next
+     * (virtual) step, and ties go to the even neighbour, which is inf. */
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: fixed quantum 2^-24.  r may reach 1024, which is
+         * exactly the encoding of the smallest normal number. */
+        double r = round_half_even(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    int e2;
+    frexp(a, &e2); /* a in [2^(e2-1), 2^e2) */
+    int unb = e2 - 1; /* unbiased exponent, -14..15 */
+    double r = round_half_even(ldexp(a, 10 - unb)); /* in [1024, 2048] */
+    /* r == 2048 carries into the exponent field, which is what the plain
+     * sum below does. */
+    uint32_t bits = ((uint32_t)(unb + 15) << 10) + ((uint32_t)r - 1024u);
+    return (uint16_t)(sign | bits);
+}
+
+void q4o_f16_to_f64_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = q4o_f16_to_f64(h[i]);
+}
+
+void q4o_f64_to_f16_array(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = q4o_f64_to_f16(v[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* packing                                                              */
+/* ------------------------------------------------------------------ */
+
+/* codes u8[N][K] (only the low nibble is used) -> packed u8[N][K/2]. */
+void q4o_pack(const uint8_t *codes, uint8_t *packed, int64_t N, int64_t K)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j) {
+            uint8_t lo = codes[n * K + 2 * j] & 0x0F;
+            uint8_t hi = codes[n * K + 2 * j + 1] & 0x0F;
+            packed[n * (K / 2) + j] = (uint8_t)(lo | (hi << 4));
+        }
+}
+
+/* packed u8[N][K/2] -> codes u8[N][K], each 0..15. */
+void q4o_unpack(const uint8_t *packed, uint8_t *codes, int64_t N, int64_t K)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j) {
+            uint8_t b = packed[n * (K / 2) + j];
+            codes[n * K + 2 * j] = b & 0x0F;
+            codes[n * K + 2 * j + 1] = b >> 4;
+        }
+}
+
+/* One dequantized weight, straight from the definition. */
+static double weight_at(const uint8_t *packed, const uint16_t *scales,
+                        int64_t K, int64_t n, int64_t k)
+{
+    uint8_t b = packed[n * (K / 2) + k / 2];
+    int code = (k % 2 == 0) ? (b & 0x0F) : (b >> 4);
+    double s = q4o_f16_to_f64(scales[n * (K / 32) + k / 32]);
+    return s * (double)(code - 8);
+}
+
+/* Dense fp64 dequantized matrix W[N][K] (small cases only). */
+void q4o_dequant(const uint8_t *packed, const uint16_t *scales, double *W,
+                 int64_t N, int64_t K)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[n * K + k] = weight_at(packed, scales, K, n, k);
+}
+
+/* ------------------------------------------------------------------ */
+/* matrix-vector and small-batch products                               */
+/* ------------------------------------------------------------------ */
+
+/* One output row: y = sum_k w[n][k] * x[k] in k order, and the magnitude
+ * m = sum_k |w[n][k] * x[k]| that scales the acceptance bound. */
+static void row_dot(const uint8_t *packed, const uint16_t *scales,
+                    const double *x, int64_t K, int64_t n,
+                    double *y, double *m)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double t = weight_at(packed, scales, K, n, k) * x[k];
+        acc += t;
+        mag += fabs(t);
+    }
+    *y = acc;
+    if (m)
+        *m = mag;
+}
+
+/* y[n] = sum_k w[n][k] * x[k] for binary16 x.  mag may be NULL. */
+void q4o_gemv(const uint8_t *packed, const uint16_t *scales,
+              const uint16_t *x_f16, int64_t N, int64_t K,
+              double *y, double *mag)
+{
+    double *x = (double *)malloc(sizeof(double) * (size_t)K);
+    q4o_f16_to_f64_array(x_f16, x, K);
+    for (int64_t n = 0; n < N; ++n)
+        row_dot(packed, scales, x, K, n, &y[n], mag ? &mag[n] : NULL);
+    free(x);
+}
+
+/* Same product for a chosen subset of rows (used to check very large
+ * matrices one output at a time).  y and mag are indexed like rows. */
+void q4o_gemv_rows(const uint8_t *packed, const uint16_t *scales,
+                   const uint16_t *x_f16, int64_t K,
+                   const int64_t *rows, int64_t nrows,
+                   double *y, double *mag)
+{
+    double *x = (double *)malloc(sizeof(double) * (size_t)K);
+    q4o_f16_to_f64_array(x_f16, x, K);
+    for (int64_t i = 0; i < nrows; ++i)
+        row_dot(packed, scales, x, K, rows[i], &y[i], mag ? &mag[i] : NULL);
+    free(x);
+}
+
+/* Y[b][n] = sum_k w[n][k] * X[b][k]; X is binary16 [B][K]. */
+void q4o_gemm(const uint8_t *packed, const uint16_t *scales,
+              const uint16_t *X_f16, int64_t N, int64_t K, int64_t B,
+              double *Y, double *M)
+{
+    for (int64_t b = 0; b < B; ++b)
+        q4o_gemv(packed, scales, X_f16 + b * K, N, K, Y + b * N,
+                 M ? M + b * N : NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* decode-layer glue (a reading: the pages describe none of it)          */
+/* ------------------------------------------------------------------ */
+
+/* a = f16(h / sqrt(mean(h^2) + eps)), unit gain. */
+void q4o_rmsnorm_f16(const double *h, int64_t d, double eps, uint16_t *a)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i)
+        ss += h[i] * h[i];
+    double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int64_t i = 0; i < d; ++i)
+        a[i] = q4o_f64_to_f16(h[i] * r);
+}
+
+/* One-token attention: with a single key, softmax is 1 and RoPE at
+ * position 0 is the identity, so query head hq outputs the V vector of its
+ * key/value group hq / (H / Hkv).  qkv holds Q | K | V (H*hd, Hkv*hd,
+ * Hkv*hd values); out is f16[H*hd]. */
+void q4o_gqa_gather_f16(const double *qkv, int64_t H, int64_t Hkv,
+                        int64_t hd, uint16_t *out)
+{
+    const double *V = qkv + (H + Hkv) * hd;
+    int64_t per_group = H / Hkv;
+    for (int64_t hq = 0; hq < H; ++hq) {
+        int64_t g = hq / per_group;
+        for (int64_t i = 0; i < hd; ++i)
+            out[hq * hd + i] = q4o_f64_to_f16(V[g * hd + i]);
+    }
+}
+
+/* mlp[j] = f16(silu(gate[j]) * up[j]), gate | up stacked in gu. */
+void q4o_silu_mul_f16(const double *gu, int64_t dff, uint16_t *out)
+{
+    for (int64_t j = 0; j < dff; ++j) {
+        double g = gu[j];
+        double silu = g / (1.0 + exp(-g));
+        out[j] = q4o_f64_to_f16(silu * gu[dff + j]);
+    }
+}
+
+/* One quantized matrix as the caller lays it out. */
+typedef struct {
+    const uint8_t *packed;
+    const uint16_t *scales;
+} q4o_mat;
+
+/*
+ * One decoder layer on the residual h (fp64, in place):
+ *   a   = f16(rmsnorm(h))
+ *   qkv = Wqkv a                 rows: Q [0,H*hd) | K | V
+ *   o   = f16(gather V by GQA group)
+ *   h  += Wo o
+ *   a2  = f16(rmsnorm(h))
+ *   gu  = Wgu a2                 rows: gate [0,dff) | up [dff,2dff)
+ *   m   = f16(silu(gate) * up)
+ *   h  += Wdown m
+ * mag_h (may be NULL) accumulates, per element of h, the magnitudes
+ * sum_k |w*x| of the two products added into h, which bounds how far a
+ * correctly rounded fp32 evaluation may drift from this fp64 one.
+ */
+void q4o_decode_layer(const q4o_mat *qkv_m, const q4o_mat *o_m,
+                      const q4o_mat *gu_m, const q4o_mat *down_m,
+                      int64_t d, int64_t H, int64_t Hkv, int64_t hd,
+                      int64_t dff, double eps, double *h, double *mag_h)
+{
+    int64_t nqkv = (H + 2 * Hkv) * hd;
+    uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(d > dff ? d : dff));
+    uint16_t *o = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(H * hd));
+    double *qkv = (double *)malloc(sizeof(double) * (size_t)nqkv);
+    double *gu = (double *)malloc(sizeof(double) * (size_t)(2 * dff));
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    double *m = (double *)malloc(sizeof(double) * (size_t)d);
+
+    q4o_rmsnorm_f16(h, d, eps, a);
+    q4o_gemv(qkv_m->packed, qkv_m->scales, a, nqkv, d, qkv, NULL);
+    q4o_gqa_gather_f16(qkv, H, Hkv, hd, o);
+    q4o_gemv(o_m->packed, o_m->scales, o, d, H * hd, y, m);
+    for (int64_t i = 0; i < d; ++i) {
+        h[i] += y[i];
+        if (mag_h)
+            mag_h[i] += m[i];
+    }
+    q4o_rmsnorm_f16(h, d, eps, a);
+    q4o_gemv(gu_m->packed, gu_m->scales, a, 2 * dff, d, gu, NULL);
+    q4o_silu_mul_f16(gu, dff, a);
+    q4o_gemv(down_m->packed, down_m->scales, a, d, dff, y, m);
+    for (int64_t i = 0; i < d; ++i) {
+        h[i] += y[i];
+        if (mag_h)
+            mag_h[i] += m[i];
+    }
+    free(a);
+    free(o);
+    free(qkv);
+    free(gu);
+    free(y);
+    free(m);
+}

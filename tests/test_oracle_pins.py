@@ -1,0 +1,291 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each test checks the oracle against a library routine, a closed form, an
+invariant or a brute-force path written independently here, chosen so that a
+dropped term, a wrong sign or index, or a transposed operand fails at least
+one of them.  No GPU is needed.
+"""
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f16_bits(v):
+    return np.asarray(v, np.float64).astype(np.float16).view(np.uint16)
+
+
+def _rand_mat(rng, N, K, scale_kind="random"):
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    if scale_kind == "random":
+        s = (np.abs(rng.standard_normal((N, K // 32))) * 0.02).astype(np.float16)
+    elif scale_kind == "int":
+        s = rng.integers(1, 4, size=(N, K // 32)).astype(np.float16)
+    else:
+        raise ValueError(scale_kind)
+    return codes, s
+
+
+# ------------------------------------------------------------- binary16
+def test_f16_decode_exhaustive():
+    """All 65,536 bit patterns decode exactly as numpy's float16."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zero and the subnormal/normal boundary, explicitly
+    assert np.signbit(oracle.f16_to_f64(np.array([0x8000], np.uint16))[0])
+    assert oracle.f16_to_f64(np.array([0x0001], np.uint16))[0] == 2.0 ** -24
+    assert oracle.f16_to_f64(np.array([0x0400], np.uint16))[0] == 2.0 ** -14
+
+
+def test_f16_round_nearest_even():
+    """f64 -> f16 agrees with numpy's correctly rounded conversion on exact
+    values, on every rounding midpoint and next to it, and at overflow."""
+    bits = np.arange(0x7C00, dtype=np.uint16)  # all finite non-negative
+    vals = bits.view(np.float16).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0  # exact midpoints between neighbours
+    cases = [vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)]
+    rng = np.random.default_rng(1)
+    cases.append(rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 5, 200000))
+    cases.append(np.array([65504.0, 65519.99, 65520.0, 70000.0, 1e300, 2.0 ** -25,
+                           2.0 ** -25 * 1.0000001, 3 * 2.0 ** -25, 2.0 ** -26]))
+    for c in cases:
+        for v in (c, -c):
+            ours = oracle.f64_to_f16(v)
+            with np.errstate(over="ignore"):
+                ref = v.astype(np.float16).view(np.uint16)
+            assert np.array_equal(ours, ref), v[ours != ref][:5]
+    assert oracle.f64_to_f16(np.array([np.nan]))[0] & 0x7C00 == 0x7C00
+
+
+# ------------------------------------------------------------- packing
+def test_pack_unpack_all_bytes_and_pairs():
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    c = oracle.unpack(b)
+    assert np.array_equal(c[0, 0::2], np.arange(256) & 0xF)
+    assert np.array_equal(c[0, 1::2], np.arange(256) >> 4)
+    assert np.array_equal(oracle.pack(c), b)
+    lo, hi = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
+    pairs = np.stack([lo.ravel(), hi.ravel()], axis=1).reshape(1, 512).astype(np.uint8)
+    packed = oracle.pack(pairs)
+    assert np.array_equal(packed[0], (lo.ravel() | (hi.ravel() << 4)).astype(np.uint8))
+
+
+def test_pack_masks_high_bits():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 256, size=(7, 64), dtype=np.uint8)
+    assert np.array_equal(oracle.pack(codes), oracle.pack(codes & 0xF))
+    assert np.array_equal(oracle.unpack(oracle.pack(codes)), codes & 0xF)
+
+
+# ------------------------------------------------------------- products
+def _dense_reference(codes, s_f16, x):
+    """Independent path: build W in numpy from the codes and float16 scales."""
+    s = s_f16.astype(np.float64)
+    W = np.repeat(s, 32, axis=1) * (codes.astype(np.float64) - 8.0)
+    return W @ x, W
+
+
+def test_brute_force_8x64_exact_integers():
+    rng = np.random.default_rng(3)
+    codes, s = _rand_mat(rng, 8, 64, "int")
+    x = rng.integers(-4, 5, size=64).astype(np.float16)
+    y, m = oracle.gemv(oracle.pack(codes), s.view(np.uint16), x.view(np.uint16))
+    yr, W = _dense_reference(codes, s, x.astype(np.float64))
+    assert np.array_equal(y, yr)
+    assert np.array_equal(m, np.abs(W * x.astype(np.float64)).sum(axis=1))
+    assert np.array_equal(oracle.dequant(oracle.pack(codes), s.view(np.uint16)), W)
+
+
+def test_brute_force_8x64_random():
+    rng = np.random.default_rng(4)
+    codes, s = _rand_mat(rng, 8, 64)
+    x = rng.standard_normal(64).astype(np.float16)
+    y, _ = oracle.gemv(oracle.pack(codes), s.view(np.uint16), x.view(np.uint16))
+    yr, _ = _dense_reference(codes, s, x.astype(np.float64))
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-15)
+
+
+def test_allones_closed_form_and_hand_case():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "allones_hand_case.txt"))
+            if l.strip() and not l.startswith("#")]
+    codes = (np.arange(32) % 16).astype(np.uint8).reshape(1, 32)
+    ones = _f16_bits(np.ones(32))
+    for sc, expect in rows:
+        s = _f16_bits([[float(sc)]])
+        y, _ = oracle.gemv(oracle.pack(codes), s, ones)
+        assert y[0] == float(expect)
+    # closed form on a random matrix: y_n = sum_g s_ng * (sum_{k in g} c_nk - 256)
+    rng = np.random.default_rng(5)
+    codes, s = _rand_mat(rng, 16, 256)
+    y, _ = oracle.gemv(oracle.pack(codes), s.view(np.uint16), _f16_bits(np.ones(256)))
+    gsum = codes.reshape(16, 8, 32).astype(np.int64).sum(axis=2) - 256
+    closed = (s.astype(np.float64) * gsum).sum(axis=1)
+    np.testing.assert_allclose(y, closed, rtol=1e-15, atol=0)
+
+
+def test_zero_point_gives_exact_zero():
+    rng = np.random.default_rng(6)
+    codes = np.full((5, 128), 8, np.uint8)
+    s = (np.abs(rng.standard_normal((5, 4))) + 0.1).astype(np.float16)
+    x = rng.standard_normal(128).astype(np.float16)
+    y, m = oracle.gemv(oracle.pack(codes), s.view(np.uint16), x.view(np.uint16))
+    assert np.all(y == 0.0) and np.all(m == 0.0)
+
+
+def test_impulse_picks_one_weight():
+    rng = np.random.default_rng(7)
+    codes, s = _rand_mat(rng, 6, 96)
+    packed = oracle.pack(codes)
+    for k in (0, 1, 31, 32, 63, 95):
+        x = np.zeros(96)
+        x[k] = 1.0
+        y, _ = oracle.gemv(packed, s.view(np.uint16), _f16_bits(x))
+        expect = s[:, k // 32].astype(np.float64) * (codes[:, k].astype(np.float64) - 8)
+        assert np.array_equal(y, expect)
+
+
+def test_linearity_small_integers():
+    rng = np.random.default_rng(8)
+    codes, s = _rand_mat(rng, 12, 512)
+    packed, sb = oracle.pack(codes), s.view(np.uint16)
+    x1 = rng.integers(-4, 5, 512).astype(np.float64)
+    x2 = rng.integers(-4, 5, 512).astype(np.float64)
+    y1, _ = oracle.gemv(packed, sb, _f16_bits(x1))
+    y2, _ = oracle.gemv(packed, sb, _f16_bits(x2))
+    y12, _ = oracle.gemv(packed, sb, _f16_bits(x1 + x2))
+    y1d, _ = oracle.gemv(packed, sb, _f16_bits(2 * x1))
+    assert np.array_equal(y12, y1 + y2)
+    assert np.array_equal(y1d, 2 * y1)
+    yneg, _ = oracle.gemv(packed, sb, _f16_bits(-x1))
+    assert np.array_equal(yneg, -y1)
+
+
+def test_gemm_is_stacked_gemv_and_rows_subset():
+    rng = np.random.default_rng(9)
+    codes, s = _rand_mat(rng, 40, 160)
+    packed, sb = oracle.pack(codes), s.view(np.uint16)
+    X = rng.standard_normal((5, 160)).astype(np.float16)
+    Y, M = oracle.gemm(packed, sb, X.view(np.uint16))
+    for b in range(5):
+        y, m = oracle.gemv(packed, sb, X[b].view(np.uint16))
+        assert np.array_equal(Y[b], y) and np.array_equal(M[b], m)
+    rows = np.array([39, 0, 17, 17], np.int64)
+    yr, mr = oracle.gemv_rows(packed, sb, X[2].view(np.uint16), rows)
+    assert np.array_equal(yr, Y[2][rows]) and np.array_equal(mr, M[2][rows])
+    # the row/column roles: a transposed product would not match the dense one
+    yd, _ = _dense_reference(codes, s, X[3].astype(np.float64))
+    np.testing.assert_allclose(Y[3], yd, rtol=1e-12, atol=1e-15)
+
+
+def test_subnormal_scales_are_honoured():
+    codes = np.full((1, 32), 9, np.uint8)  # w = s
+    s = np.array([[0x0001]], np.uint16)  # 2^-24
+    y, _ = oracle.gemv(oracle.pack(codes), s, _f16_bits(np.ones(32)))
+    assert y[0] == 32 * 2.0 ** -24
+
+
+# ------------------------------------------------------------- glue
+def test_rmsnorm_closed_forms():
+    for c in (2.0, -0.375, 1e-3):
+        a = oracle.rmsnorm_f16(np.full(64, c))
+        expect = _f16_bits([c / np.sqrt(c * c + 1e-5)])[0]
+        assert np.all(a == expect)
+    a = oracle.rmsnorm_f16(np.array([1.0, -1.0] * 16))
+    assert np.array_equal(a, _f16_bits([1.0, -1.0] * 16))
+    rng = np.random.default_rng(10)
+    h = rng.standard_normal(128)
+    # with eps = 0 the norm is exactly invariant to power-of-two scaling
+    assert np.array_equal(oracle.rmsnorm_f16(h, eps=0.0),
+                          oracle.rmsnorm_f16(h * 8.0, eps=0.0))
+    assert np.array_equal(oracle.rmsnorm_f16(-h, eps=0.0),
+                          oracle.rmsnorm_f16(h, eps=0.0) ^ np.uint16(0x8000))
+
+
+def test_gqa_gather_hand_case():
+    lines = [l.split() for l in open(os.path.join(GOLDEN, "gqa_gather_hand_case.txt"))
+             if l.strip() and not l.startswith("#")]
+    H, Hkv, hd = map(int, lines[0])
+    qkv = np.array(lines[1], np.float64)
+    expect = np.array(lines[2], np.float64)
+    out = oracle.gqa_gather_f16(qkv, H, Hkv, hd)
+    assert np.array_equal(out, _f16_bits(expect))
+
+
+def test_silu_mul_against_expit():
+    g = np.array([0.0, 1.0, -1.0, 20.0, -20.0, 3.5, -0.25])
+    u = np.array([5.0, 1.0, 2.0, 1.0, 1.0, -2.0, 4.0])
+    out = oracle.silu_mul_f16(np.concatenate([g, u]))
+    assert out[0] == 0 and out[3] == _f16_bits([20.0])[0]
+    ref = _f16_bits(g * expit(g) * u)
+    assert np.array_equal(out, ref)
+
+
+def _identity_mat(N, K, sign=1, col_offset=0, rows=None):
+    """Codes/scales with w[n][n + col_offset] = sign for n in rows, else 0."""
+    codes = np.full((N, K), 8, np.uint8)
+    rows = range(N) if rows is None else rows
+    for n in rows:
+        codes[n, n + col_offset] = 8 + sign
+    s = np.ones((N, K // 32), np.float16)
+    return oracle.pack(codes), s.view(np.uint16)
+
+
+def _tiny_dims():
+    return dict(d=32, H=2, Hkv=1, hd=16, dff=32)
+
+
+def test_decode_layer_zero_weights_is_identity():
+    dims = _tiny_dims()
+    zero = lambda N, K: (oracle.pack(np.full((N, K), 8, np.uint8)),
+                         np.ones((N, K // 32), np.uint16) * 0x3C00)
+    layer = {"qkv": zero(64, 32), "o": zero(32, 32), "gate_up": zero(64, 32),
+             "down": zero(32, 32)}
+    h = np.random.default_rng(11).standard_normal(32)
+    h0 = h.copy()
+    mag = np.zeros(32)
+    oracle.decode_layer(layer, dims, h, mag)
+    assert np.array_equal(h, h0) and np.all(mag == 0)
+
+
+def test_decode_layer_routing_hand_built():
+    """Identity-shaped weights route values through each stage: the V block
+    of QKV, the GQA gather, a negated O, gate|up order and down."""
+    dims = _tiny_dims()
+    d = 32
+    qkv_codes = np.full((64, 32), 8, np.uint8)
+    for n in range(16):  # V rows 48..63 pick a[0..15]; Q, K rows stay zero
+        qkv_codes[48 + n, n] = 9
+        qkv_codes[n, n] = 15  # Q rows are nonzero but must not reach the output
+    qkv = (oracle.pack(qkv_codes), np.ones((64, 1), np.float16).view(np.uint16))
+    o = _identity_mat(32, 32, sign=-1)
+    gu_codes = np.full((64, 32), 8, np.uint8)
+    for j in range(32):
+        gu_codes[j, j] = 9         # gate = a2
+        gu_codes[32 + j, j] = 7    # up = -a2
+    gate_up = (oracle.pack(gu_codes), np.ones((64, 1), np.float16).view(np.uint16))
+    down = _identity_mat(32, 32, sign=1)
+    layer = {"qkv": qkv, "o": o, "gate_up": gate_up, "down": down}
+
+    rng = np.random.default_rng(12)
+    h0 = rng.standard_normal(d) * 3.0
+    h = h0.copy()
+    oracle.decode_layer(layer, dims, h)
+
+    def rms_f16(v):
+        return (v / np.sqrt(np.mean(v * v) + 1e-5)).astype(np.float16).astype(np.float64)
+
+    a = rms_f16(h0)
+    h1 = h0 - np.concatenate([a[:16], a[:16]])
+    a2 = rms_f16(h1)
+    mlp = (a2 * expit(a2) * -a2).astype(np.float16).astype(np.float64)
+    expect = h1 + mlp
+    np.testing.assert_allclose(h, expect, rtol=0, atol=1e-12)
