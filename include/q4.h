@@ -1,0 +1,246 @@
+/*
+ * q4.h -- C ABI of libq4stream, the MI355X (gfx950) INT4 weight-streaming
+ * decode library.
+ *
+ * The library computes the per-token matrix-vector product over 4-bit,
+ * group-quantized weights without writing dequantized weights to memory
+ * (PIPO: Pipelined Offloading for Efficient Inference on Consumer Devices,
+ * "Method", bullet "Computation optimization"), a small-batch variant of it
+ * for batches below 16 (same page, bullet "Automatic configuration", and
+ * "Limitations"), a per-token layer loop captured once per context-length
+ * bucket as a HIP graph (PipeLLM: Faster Local LLM Inference Than llama.cpp
+ * via System-Level Optimizations, "Layer 1: CUDA Graph Compilation"), and
+ * double-buffered streaming of whole layers from pinned host memory over a
+ * copy stream (same page, "Layer 2: Asynchronous Weight Prefetching"; PIPO,
+ * "Method", bullets "Pipeline design", "Two pipeline modes" and "Data
+ * transfer suite").
+ *
+ * Weight format (the pages give no bit layout; this is the reading used):
+ *   - N x K matrix, K a multiple of 32;
+ *   - packed: u8[N][K/2], row-major; byte j of row n holds the unsigned code
+ *     of column 2j in bits 0..3 and of column 2j+1 in bits 4..7;
+ *   - scales: IEEE binary16 bit patterns u16[N][K/32], row-major, one per
+ *     group of 32 consecutive columns;
+ *   - weight w[n][k] = scale[n][k/32] * (code[n][k] - 8).
+ * Activations are binary16 bit patterns; outputs and the residual are fp32.
+ *
+ * Conventions for every function below:
+ *   - Pointers are DEVICE pointers unless marked "host".  The library never
+ *     allocates, frees or retains caller memory beyond the objects
+ *     documented as retaining pointers (decoder, weight stream).
+ *   - GPU work is enqueued on the given stream and is asynchronous with
+ *     respect to the host; a NULL stream means the default stream.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     error nothing is enqueued and a non-zero status is returned, with a
+ *     message available from q4_last_error() on the same thread.
+ *   - Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Every kernel uses a fixed reduction order and no floating-point
+ *     atomics: repeated calls give bitwise identical results.
+ *   - Distinct objects may be used from distinct threads; one object must
+ *     not be used from two threads at once.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+
+typedef int32_t q4_status;
+#define Q4_OK 0
+#define Q4_ERR_INVALID_ARG 1 /* bad pointer, size, alignment or range */
+#define Q4_ERR_UNSUPPORTED 2 /* valid request outside what is implemented */
+#define Q4_ERR_HIP 3         /* a HIP runtime call failed */
+#define Q4_ERR_STATE 4       /* call out of order (e.g. wait before begin) */
+#define Q4_ERR_OOM 5         /* host allocation failed */
+
+/* Largest K accepted by the products (the activation vector of one
+ * workgroup lives in LDS: 2*K bytes). */
+#define Q4_MAX_K 32768
+/* Largest batch of q4_gemm_smallbatch. */
+#define Q4_MAX_BATCH 16
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The string stays valid until the next library call on this thread. */
+const char *q4_last_error(void);
+int32_t q4_abi_version(void);
+
+/* ------------------------------------------------------------------ */
+/* Packing                                                              */
+/* ------------------------------------------------------------------ */
+
+/* codes u8[N][K] (one code per byte; only bits 0..3 are used, higher bits
+ * are ignored) -> packed u8[N][K/2] in the layout above.  N >= 1, K >= 2
+ * and even.  Bit-exact; no alignment requirement. */
+q4_status q4_pack(const uint8_t *codes, uint8_t *packed, int64_t N, int64_t K,
+                  hipStream_t stream);
+
+/* packed u8[N][K/2] -> codes u8[N][K] (each 0..15). */
+q4_status q4_unpack(const uint8_t *packed, uint8_t *codes, int64_t N,
+                    int64_t K, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Products (PIPO, "Method", "Computation optimization")                 */
+/* ------------------------------------------------------------------ */
+
+/* y[n] = sum_k w[n][k] * x[k] for n < N.
+ *   packed  u8[N][K/2], 16-byte aligned;  scales u16[N][K/32], 2-byte aligned;
+ *   x_f16   u16[K] binary16, 16-byte aligned;  y f32[N], 4-byte aligned.
+ *   1 <= N <= 2^31-1;  32 <= K <= Q4_MAX_K;  K % 32 == 0.
+ * Each group's 32 products are formed exactly (binary16 x binary16) and
+ * summed in fp32, then scaled by the group's scale in fp32. */
+q4_status q4_gemv(const uint8_t *packed, const uint16_t *scales,
+                  const uint16_t *x_f16, float *y, int64_t N, int64_t K,
+                  hipStream_t stream);
+
+/* Y[b][n] = sum_k w[n][k] * X[b][k] for b < B, n < N.
+ *   X_f16 u16[B][K] binary16 (each activation vector contiguous),
+ *   16-byte aligned;  Y f32[B][N], 4-byte aligned;  1 <= B <= Q4_MAX_BATCH;
+ *   other arguments as q4_gemv.  B == 1 runs the q4_gemv kernel. */
+q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
+                             const uint16_t *X_f16, float *Y, int64_t N,
+                             int64_t K, int32_t B, hipStream_t stream);
+
+/* Tuning variants of the two products, for measurement: the same
+ * arithmetic with an explicit launch shape.  rows_per_slot, k_split in
+ * {1, 2, 4}: rows held by each 16-lane row of a wave, and waves sharing one
+ * row's k range.  row_tiles in {1, 2, 4, 8} (8 only with waves == 4),
+ * waves in {4, 8}: 16-row tiles per workgroup and waves splitting k.  B == 1
+ * is allowed here and runs the matrix-core kernel.  UNSUPPORTED for other
+ * values. */
+q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales,
+                        const uint16_t *x_f16, float *y, int64_t N, int64_t K,
+                        int32_t rows_per_slot, int32_t k_split, hipStream_t stream);
+q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
+                        const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
+                        int32_t B, int32_t row_tiles, int32_t waves,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Decode step (PipeLLM, "Layer 1: CUDA Graph Compilation")               */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const uint8_t *packed;  /* device u8[N][K/2], 16-byte aligned */
+    const uint16_t *scales; /* device u16[N][K/32] */
+    int64_t N, K;
+} q4_matrix;
+
+/* One decoder layer: fused QKV (rows Q | K | V), O, fused gate+up
+ * (rows gate | up) and down. */
+typedef struct {
+    q4_matrix qkv, o, gate_up, down;
+} q4_layer;
+
+typedef struct {
+    int32_t n_layers;
+    int32_t d_model;    /* d */
+    int32_t n_heads;    /* H query heads */
+    int32_t n_kv_heads; /* Hkv key/value heads, H % Hkv == 0 */
+    int32_t head_dim;   /* hd */
+    int32_t d_ff;       /* dff */
+    float eps;          /* RMSNorm epsilon */
+    /* host array of n_layers layers, copied at create; may be NULL when the
+     * decoder is only driven layer by layer (q4_decode_layer). */
+    const q4_layer *layers;
+    float *h;                  /* device f32[d]: residual in/out, retained */
+    /* device, 256-byte aligned, retained.  After a layer it holds, each
+     * section starting at a 256-byte boundary in this order: the binary16
+     * normed activation of the second norm (max(d, dff) slots), the fp32
+     * QKV output ((H + 2*Hkv)*hd), the binary16 attention output (H*hd)
+     * and the binary16 gated MLP activation (dff). */
+    void *workspace;
+    size_t workspace_bytes;    /* >= q4_decoder_workspace_bytes() */
+} q4_model_desc;
+
+/*
+ * Per layer, on the fp32 residual h (a reading: the pages list the four
+ * products of a decode layer but none of the glue between them):
+ *   a   = f16(h / sqrt(mean(h^2) + eps))
+ *   qkv = Wqkv a;  o = f16(V of the key/value group of each query head)
+ *   h  += Wo o
+ *   a2  = f16(h / sqrt(mean(h^2) + eps))
+ *   gu  = Wgu a2;  m = f16(silu(gate) * up)
+ *   h  += Wdown m
+ * The gather is one-token attention: with a single cached key, softmax is 1
+ * and rotary position 0 is the identity.
+ */
+q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out);
+/* Validates and copies the description; creates no GPU work.  Shapes must
+ * match the dimensions and satisfy the q4_gemv limits. */
+q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
+/* Runs all layers for one token.  ctx_len picks the context bucket: the
+ * smallest of 512, 1024, 2048, 4096 that is >= ctx_len; the first call for a
+ * bucket captures the layer loop into a HIP graph on `stream` (which must
+ * not be the NULL stream), later calls replay it.  ctx_len <= 0 is
+ * INVALID_ARG, ctx_len > 4096 is UNSUPPORTED.  Graphs bake in every pointer
+ * of the description: those buffers must outlive the decoder. */
+q4_status decode_step_graph(void *dec, int32_t ctx_len, hipStream_t stream);
+/* Same layer loop, enqueued eagerly without a graph (for checking). */
+q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
+/* One layer, eagerly, with the weights given (e.g. a streamed slot). */
+q4_status q4_decode_layer(void *dec, const q4_layer *layer, hipStream_t stream);
+/* Frees graphs and host state.  Call after the last step has completed. */
+q4_status q4_decoder_destroy(void *dec);
+
+/* ------------------------------------------------------------------ */
+/* Layer weight streaming (PipeLLM, "Layer 2: Asynchronous Weight        */
+/* Prefetching"; PIPO, "Method", "Pipeline design", "Data transfer suite") */
+/* ------------------------------------------------------------------ */
+
+/* One layer's four matrices merged into one blob (one copy per layer):
+ * sections, in order, qkv.packed, qkv.scales, o.packed, o.scales,
+ * gate_up.packed, gate_up.scales, down.packed, down.scales, each starting
+ * at a 256-byte aligned offset.  shapes: host; only N and K are read.
+ * offsets: host size_t[8]; bytes: host, total blob size. */
+q4_status q4_layer_blob_layout(const q4_layer *shapes, size_t offsets[8],
+                               size_t *bytes);
+/* q4_layer whose pointers point into a blob at `base` (device). */
+q4_status q4_layer_from_blob(const q4_layer *shapes, const void *base,
+                             q4_layer *out);
+
+typedef struct {
+    int32_t n_layers;
+    const void *const *host_blobs; /* host array [n_layers] of pinned host
+                                      pointers (hipHostMalloc / pinned torch) */
+    const size_t *blob_bytes;      /* host array [n_layers] */
+    void *slot[2];                 /* two device buffers of slot_bytes */
+    size_t slot_bytes;             /* >= every blob_bytes[l] */
+    hipStream_t copy;              /* copy stream, not NULL */
+} q4_wstream_desc;
+
+/* Copies the description and creates events; retains every pointer. */
+q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws);
+/* Starts the host->device copy of `layer` into the next slot (slots
+ * alternate by call count).  If that slot was handed out by an earlier
+ * weight_stream_wait, all work enqueued on that call's compute stream
+ * before THIS call is treated as its last use: the copy waits for it.
+ * STATE if the next slot holds a layer that was begun but not yet waited. */
+q4_status weight_stream_begin(void *ws, int32_t layer);
+/* Makes `compute` wait until `layer`'s copy has landed and returns its slot
+ * (device pointer to the blob) in *slot_ptr.  Layers must be waited in the
+ * order they were begun; STATE otherwise. */
+q4_status weight_stream_wait(void *ws, int32_t layer, hipStream_t compute,
+                             void **slot_ptr);
+/* Destroys events.  Call after all enqueued work has completed. */
+q4_status q4_wstream_destroy(void *ws);
+
+/* One token of the decoder with every layer streamed through `ws`: layer 0
+ * is begun (unless already begun by the previous token), then for each
+ * layer l the copy of l+1 is begun before l is waited and computed on
+ * `compute`.  The blob layout must be q4_layer_blob_layout of the decoder's
+ * shapes.  The copy of the next token's layer 0 is begun at the end. */
+q4_status q4_decode_token_streamed(void *dec, void *ws, hipStream_t compute);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

@@ -1,0 +1,455 @@
+// Per-token decode loop, its HIP-graph cache keyed by context bucket, and
+// double-buffered layer streaming from pinned host memory.
+//
+// Graph capture: PipeLLM: Faster Local LLM Inference Than llama.cpp via
+// System-Level Optimizations, "Layer 1: CUDA Graph Compilation" -- the
+// decoding loop is captured once as a static graph, with context-length
+// buckets 512/1024/2048/4096 and the graph chosen by sequence length (we take
+// the smallest bucket that holds ctx_len).
+//
+// Streaming: same page, "Layer 2: Asynchronous Weight Prefetching" (separate
+// compute and copy streams, pinned host buffers, double-buffered staging),
+// and PIPO: Pipelined Offloading for Efficient Inference on Consumer
+// Devices, "Method": "Pipeline design" (load the next layer, wait for the
+// current layer's load, compute), "Two pipeline modes" (the performance mode
+// keeps two layers on the GPU) and "Data transfer suite" (a layer's tensors
+// merged into one transfer).  PIPO's three transfer threads become one copy
+// stream plus events: a pinned host->device copy needs no host thread.
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kBuckets[4] = {512, 1024, 2048, 4096};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+    int64_t d, H, Hkv, hd, dff, nqkv;
+};
+
+struct Decoder {
+    q4_model_desc desc;
+    std::vector<q4_layer> layers;
+    Dims dims;
+    uint16_t *a16 = nullptr; // f16[max(d, dff)] normed activation
+    float *qkv = nullptr;    // f32[nqkv]
+    uint16_t *oin = nullptr; // f16[H*hd]
+    uint16_t *mlp = nullptr; // f16[dff]
+    hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+
+q4_status dims_of(const q4_model_desc *m, Dims *out) {
+    if (!m)
+        return fail(Q4_ERR_INVALID_ARG, "decoder: null description");
+    if (m->n_layers < 1 || m->d_model < 32 || m->n_heads < 1 || m->n_kv_heads < 1 ||
+        m->head_dim < 1 || m->d_ff < 32)
+        return fail(Q4_ERR_INVALID_ARG, "decoder: non-positive or too small dimension");
+    if (m->n_heads % m->n_kv_heads != 0)
+        return fail(Q4_ERR_INVALID_ARG, "decoder: n_heads %% n_kv_heads != 0");
+    if (!(m->eps >= 0.0f))
+        return fail(Q4_ERR_INVALID_ARG, "decoder: eps must be >= 0");
+    Dims d;
+    d.d = m->d_model;
+    d.H = m->n_heads;
+    d.Hkv = m->n_kv_heads;
+    d.hd = m->head_dim;
+    d.dff = m->d_ff;
+    d.nqkv = (d.H + 2 * d.Hkv) * d.hd;
+    if (d.d % 32 || (d.H * d.hd) % 32 || d.dff % 32)
+        return fail(Q4_ERR_INVALID_ARG,
+                    "decoder: d_model, n_heads*head_dim and d_ff must be multiples of 32");
+    *out = d;
+    return Q4_OK;
+}
+
+size_t workspace_bytes(const Dims &d) {
+    return align256(std::max(d.d, d.dff) * 2) + align256(d.nqkv * 4) + align256(d.H * d.hd * 2) +
+           align256(d.dff * 2);
+}
+
+void layer_shapes(const Dims &d, q4_layer *s) {
+    *s = q4_layer{};
+    s->qkv.N = d.nqkv;
+    s->qkv.K = d.d;
+    s->o.N = d.d;
+    s->o.K = d.H * d.hd;
+    s->gate_up.N = 2 * d.dff;
+    s->gate_up.K = d.d;
+    s->down.N = d.d;
+    s->down.K = d.dff;
+}
+
+q4_status check_layer(const Dims &d, const q4_layer &L, int idx) {
+    q4_layer want;
+    layer_shapes(d, &want);
+    const q4_matrix *got[4] = {&L.qkv, &L.o, &L.gate_up, &L.down};
+    const q4_matrix *exp[4] = {&want.qkv, &want.o, &want.gate_up, &want.down};
+    const char *names[4] = {"qkv", "o", "gate_up", "down"};
+    for (int i = 0; i < 4; ++i) {
+        if (got[i]->N != exp[i]->N || got[i]->K != exp[i]->K)
+            return fail(Q4_ERR_INVALID_ARG, "decoder: layer %d %s is %lldx%lld, expected %lldx%lld",
+                        idx, names[i], (long long)got[i]->N, (long long)got[i]->K,
+                        (long long)exp[i]->N, (long long)exp[i]->K);
+        Q4_CHECK(check_matrix(got[i]->packed, got[i]->scales, got[i]->N, got[i]->K, names[i]));
+    }
+    return Q4_OK;
+}
+
+// Enqueue one layer on `s`.
+q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s) {
+    const Dims &d = dec->dims;
+    float *h = dec->desc.h;
+    EpiArgs ea{};
+
+    Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
+    ea = EpiArgs{};
+    ea.y = dec->qkv;
+    ea.out16 = dec->oin;
+    ea.v_off = (d.H + d.Hkv) * d.hd;
+    ea.hd = (int32_t)d.hd;
+    ea.group = (int32_t)(d.H / d.Hkv);
+    Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->a16, L.qkv.N, L.qkv.K,
+                         Epi::QkvGather, ea, s));
+    ea = EpiArgs{};
+    ea.y = h;
+    Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oin, L.o.N, L.o.K, Epi::Residual, ea, s));
+
+    Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
+    ea = EpiArgs{};
+    ea.out16 = dec->mlp;
+    ea.pair_off = d.dff;
+    Q4_CHECK(launch_gemv(L.gate_up.packed, L.gate_up.scales, dec->a16, L.gate_up.N,
+                         L.gate_up.K, Epi::SiluPair, ea, s));
+    ea = EpiArgs{};
+    ea.y = h;
+    Q4_CHECK(launch_gemv(L.down.packed, L.down.scales, dec->mlp, L.down.N, L.down.K,
+                         Epi::Residual, ea, s));
+    return Q4_OK;
+}
+
+q4_status enqueue_all(Decoder *dec, hipStream_t s) {
+    for (size_t l = 0; l < dec->layers.size(); ++l)
+        Q4_CHECK(enqueue_layer(dec, dec->layers[l], s));
+    return Q4_OK;
+}
+
+// ------------------------------------------------------------ streaming
+enum SlotState { kEmpty = 0, kLoading = 1, kInUse = 2 };
+
+struct WStream {
+    int32_t n_layers = 0;
+    std::vector<const void *> blobs;
+    std::vector<size_t> bytes;
+    void *slot[2] = {nullptr, nullptr};
+    size_t slot_bytes = 0;
+    hipStream_t copy = nullptr;
+    hipEvent_t loaded[2] = {nullptr, nullptr};
+    hipEvent_t freed[2] = {nullptr, nullptr};
+    int state[2] = {kEmpty, kEmpty};
+    int32_t layer_in[2] = {-1, -1};
+    hipStream_t consumer[2] = {nullptr, nullptr};
+    int64_t n_begun = 0;
+    int64_t n_waited = 0;
+};
+
+void destroy_wstream(WStream *w) {
+    for (int i = 0; i < 2; ++i) {
+        if (w->loaded[i])
+            (void)hipEventDestroy(w->loaded[i]);
+        if (w->freed[i])
+            (void)hipEventDestroy(w->freed[i]);
+    }
+    delete w;
+}
+
+} // namespace
+} // namespace q4
+
+using q4::Decoder;
+using q4::WStream;
+
+extern "C" q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out) {
+    q4::Dims d;
+    Q4_CHECK(q4::dims_of(m, &d));
+    if (!out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_workspace_bytes: null out");
+    *out = q4::workspace_bytes(d);
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
+    if (!dec_out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: null out pointer");
+    *dec_out = nullptr;
+    q4::Dims d;
+    Q4_CHECK(q4::dims_of(m, &d));
+    if (!m->h || !q4::aligned(m->h, 4))
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: null or misaligned h");
+    if (!m->workspace || !q4::aligned(m->workspace, 256))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_decoder_create: workspace null or not 256-byte aligned");
+    if (m->workspace_bytes < q4::workspace_bytes(d))
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: workspace of %zu bytes < %zu",
+                        m->workspace_bytes, q4::workspace_bytes(d));
+    if (m->layers) {
+        for (int32_t l = 0; l < m->n_layers; ++l)
+            Q4_CHECK(q4::check_layer(d, m->layers[l], l));
+    }
+    Decoder *dec = new (std::nothrow) Decoder();
+    if (!dec)
+        return q4::fail(Q4_ERR_OOM, "q4_decoder_create: out of host memory");
+    dec->desc = *m;
+    dec->dims = d;
+    if (m->layers)
+        dec->layers.assign(m->layers, m->layers + m->n_layers);
+    dec->desc.layers = nullptr;
+    char *ws = static_cast<char *>(m->workspace);
+    dec->a16 = reinterpret_cast<uint16_t *>(ws);
+    ws += q4::align256(std::max(d.d, d.dff) * 2);
+    dec->qkv = reinterpret_cast<float *>(ws);
+    ws += q4::align256(d.nqkv * 4);
+    dec->oin = reinterpret_cast<uint16_t *>(ws);
+    ws += q4::align256(d.H * d.hd * 2);
+    dec->mlp = reinterpret_cast<uint16_t *>(ws);
+    *dec_out = dec;
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decode_step_eager(void *decp, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_eager: null decoder");
+    if (dec->layers.empty())
+        return q4::fail(Q4_ERR_STATE, "q4_decode_step_eager: decoder has no resident layers");
+    return q4::enqueue_all(dec, stream);
+}
+
+extern "C" q4_status decode_step_graph(void *decp, int32_t ctx_len, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return q4::fail(Q4_ERR_INVALID_ARG, "decode_step_graph: null decoder");
+    if (ctx_len <= 0)
+        return q4::fail(Q4_ERR_INVALID_ARG, "decode_step_graph: ctx_len=%d <= 0", ctx_len);
+    if (ctx_len > q4::kBuckets[3])
+        return q4::fail(Q4_ERR_UNSUPPORTED, "decode_step_graph: ctx_len=%d above %d", ctx_len,
+                        q4::kBuckets[3]);
+    if (!stream)
+        return q4::fail(Q4_ERR_INVALID_ARG, "decode_step_graph: capture needs a non-NULL stream");
+    if (dec->layers.empty())
+        return q4::fail(Q4_ERR_STATE, "decode_step_graph: decoder has no resident layers");
+    int b = 0;
+    while (q4::kBuckets[b] < ctx_len)
+        ++b;
+    if (!dec->exec[b]) {
+        Q4_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+        q4_status st = q4::enqueue_all(dec, stream);
+        hipGraph_t graph = nullptr;
+        hipError_t e = hipStreamEndCapture(stream, &graph);
+        if (st != Q4_OK) {
+            if (graph)
+                (void)hipGraphDestroy(graph);
+            return st;
+        }
+        if (e != hipSuccess)
+            return q4::fail(Q4_ERR_HIP, "decode_step_graph: end capture: %s",
+                            hipGetErrorString(e));
+        hipGraphExec_t exec = nullptr;
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (e != hipSuccess)
+            return q4::fail(Q4_ERR_HIP, "decode_step_graph: instantiate: %s",
+                            hipGetErrorString(e));
+        dec->exec[b] = exec;
+    }
+    Q4_HIP(hipGraphLaunch(dec->exec[b], stream));
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decode_layer(void *decp, const q4_layer *layer, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec || !layer)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer: null decoder or layer");
+    Q4_CHECK(q4::check_layer(dec->dims, *layer, -1));
+    return q4::enqueue_layer(dec, *layer, stream);
+}
+
+extern "C" q4_status q4_decoder_destroy(void *decp) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return Q4_OK;
+    for (auto &e : dec->exec)
+        if (e)
+            (void)hipGraphExecDestroy(e);
+    delete dec;
+    return Q4_OK;
+}
+
+// ---------------------------------------------------------------- blobs
+extern "C" q4_status q4_layer_blob_layout(const q4_layer *shapes, size_t offsets[8],
+                                          size_t *bytes) {
+    if (!shapes || !offsets || !bytes)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_layer_blob_layout: null argument");
+    const q4_matrix *m[4] = {&shapes->qkv, &shapes->o, &shapes->gate_up, &shapes->down};
+    size_t off = 0;
+    for (int i = 0; i < 4; ++i) {
+        if (m[i]->N < 1 || m[i]->K < 32 || m[i]->K % 32)
+            return q4::fail(Q4_ERR_INVALID_ARG, "q4_layer_blob_layout: bad shape %d", i);
+        offsets[2 * i] = off;
+        off = q4::align256(off + (size_t)m[i]->N * (size_t)m[i]->K / 2);
+        offsets[2 * i + 1] = off;
+        off = q4::align256(off + (size_t)m[i]->N * (size_t)(m[i]->K / 32) * 2);
+    }
+    *bytes = off;
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_layer_from_blob(const q4_layer *shapes, const void *base,
+                                        q4_layer *out) {
+    if (!base || !out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_layer_from_blob: null argument");
+    size_t off[8], bytes;
+    Q4_CHECK(q4_layer_blob_layout(shapes, off, &bytes));
+    const char *b = static_cast<const char *>(base);
+    q4_layer L = *shapes;
+    q4_matrix *m[4] = {&L.qkv, &L.o, &L.gate_up, &L.down};
+    for (int i = 0; i < 4; ++i) {
+        m[i]->packed = reinterpret_cast<const uint8_t *>(b + off[2 * i]);
+        m[i]->scales = reinterpret_cast<const uint16_t *>(b + off[2 * i + 1]);
+    }
+    *out = L;
+    return Q4_OK;
+}
+
+// ------------------------------------------------------------- wstream
+extern "C" q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws_out) {
+    if (!d || !ws_out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: null argument");
+    *ws_out = nullptr;
+    if (d->n_layers < 1 || !d->host_blobs || !d->blob_bytes)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: need n_layers >= 1 and arrays");
+    if (!d->slot[0] || !d->slot[1] || !d->copy)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: null slot or copy stream");
+    if (!q4::aligned(d->slot[0], 256) || !q4::aligned(d->slot[1], 256))
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: slots must be 256-byte aligned");
+    for (int32_t l = 0; l < d->n_layers; ++l) {
+        if (!d->host_blobs[l])
+            return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: null blob %d", l);
+        if (d->blob_bytes[l] > d->slot_bytes)
+            return q4::fail(Q4_ERR_INVALID_ARG,
+                            "q4_wstream_create: blob %d (%zu bytes) larger than a slot (%zu)", l,
+                            d->blob_bytes[l], d->slot_bytes);
+    }
+    WStream *w = new (std::nothrow) WStream();
+    if (!w)
+        return q4::fail(Q4_ERR_OOM, "q4_wstream_create: out of host memory");
+    w->n_layers = d->n_layers;
+    w->blobs.assign(d->host_blobs, d->host_blobs + d->n_layers);
+    w->bytes.assign(d->blob_bytes, d->blob_bytes + d->n_layers);
+    w->slot[0] = d->slot[0];
+    w->slot[1] = d->slot[1];
+    w->slot_bytes = d->slot_bytes;
+    w->copy = d->copy;
+    for (int i = 0; i < 2; ++i) {
+        hipError_t e1 = hipEventCreateWithFlags(&w->loaded[i], hipEventDisableTiming);
+        hipError_t e2 = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+            q4::destroy_wstream(w);
+            return q4::fail(Q4_ERR_HIP, "q4_wstream_create: event creation failed");
+        }
+    }
+    *ws_out = w;
+    return Q4_OK;
+}
+
+extern "C" q4_status weight_stream_begin(void *wsp, int32_t layer) {
+    WStream *w = static_cast<WStream *>(wsp);
+    if (!w)
+        return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_begin: null stream object");
+    if (layer < 0 || layer >= w->n_layers)
+        return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_begin: layer %d out of range", layer);
+    const int s = (int)(w->n_begun & 1);
+    if (w->state[s] == q4::kLoading)
+        return q4::fail(Q4_ERR_STATE,
+                        "weight_stream_begin: slot %d still holds layer %d, begun but not waited",
+                        s, w->layer_in[s]);
+    if (w->state[s] == q4::kInUse) {
+        // Everything enqueued so far on the consumer stream is the last use
+        // of this slot: the copy may overwrite it only after that work.
+        Q4_HIP(hipEventRecord(w->freed[s], w->consumer[s]));
+        Q4_HIP(hipStreamWaitEvent(w->copy, w->freed[s], 0));
+    }
+    Q4_HIP(hipMemcpyAsync(w->slot[s], w->blobs[layer], w->bytes[layer], hipMemcpyHostToDevice,
+                          w->copy));
+    Q4_HIP(hipEventRecord(w->loaded[s], w->copy));
+    w->state[s] = q4::kLoading;
+    w->layer_in[s] = layer;
+    w->consumer[s] = nullptr;
+    ++w->n_begun;
+    return Q4_OK;
+}
+
+extern "C" q4_status weight_stream_wait(void *wsp, int32_t layer, hipStream_t compute,
+                                        void **slot_ptr) {
+    WStream *w = static_cast<WStream *>(wsp);
+    if (!w || !slot_ptr)
+        return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_wait: null argument");
+    if (layer < 0 || layer >= w->n_layers)
+        return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_wait: layer %d out of range", layer);
+    const int s = (int)(w->n_waited & 1);
+    if (w->state[s] != q4::kLoading || w->layer_in[s] != layer)
+        return q4::fail(Q4_ERR_STATE, "weight_stream_wait: layer %d is not the next begun layer",
+                        layer);
+    Q4_HIP(hipStreamWaitEvent(compute, w->loaded[s], 0));
+    w->state[s] = q4::kInUse;
+    w->consumer[s] = compute;
+    ++w->n_waited;
+    *slot_ptr = w->slot[s];
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_wstream_destroy(void *wsp) {
+    if (wsp)
+        q4::destroy_wstream(static_cast<WStream *>(wsp));
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t compute) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    WStream *w = static_cast<WStream *>(wsp);
+    if (!dec || !w)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_token_streamed: null argument");
+    if (w->n_layers != dec->desc.n_layers)
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_decode_token_streamed: stream has %d layers, decoder %d",
+                        w->n_layers, dec->desc.n_layers);
+    q4_layer shapes;
+    q4::layer_shapes(dec->dims, &shapes);
+    size_t off[8], bytes;
+    Q4_CHECK(q4_layer_blob_layout(&shapes, off, &bytes));
+    for (int32_t l = 0; l < w->n_layers; ++l)
+        if (w->bytes[l] < bytes)
+            return q4::fail(Q4_ERR_INVALID_ARG,
+                            "q4_decode_token_streamed: blob %d has %zu bytes, layout needs %zu", l,
+                            w->bytes[l], bytes);
+    const int L = w->n_layers;
+    const int s0 = (int)(w->n_waited & 1);
+    const bool prefetched = w->state[s0] == q4::kLoading && w->layer_in[s0] == 0;
+    if (!prefetched)
+        Q4_CHECK(weight_stream_begin(w, 0));
+    for (int l = 0; l < L; ++l) {
+        // The copy of the following layer (after the last layer: the next
+        // token's first layer) overlaps this layer's compute.
+        Q4_CHECK(weight_stream_begin(w, (l + 1) % L));
+        void *slot = nullptr;
+        Q4_CHECK(weight_stream_wait(w, l, compute, &slot));
+        q4_layer layer;
+        Q4_CHECK(q4_layer_from_blob(&shapes, slot, &layer));
+        Q4_CHECK(q4::enqueue_layer(dec, layer, compute));
+    }
+    return Q4_OK;
+}

@@ -1,0 +1,232 @@
+// Small-batch INT4 product Y[b] = W X[b] (2 <= B <= 16) on gfx950 matrix
+// cores.
+//
+// Operation: PIPO: Pipelined Offloading for Efficient Inference on Consumer
+// Devices, "Method", bullets "Computation optimization" and "Automatic
+// configuration" -- the 4-bit kernel serves batches below 16; a batch of B
+// activation vectors (e.g. a speculative-verify batch) reuses every unpacked
+// weight B times.  At B > 2 the dot2 path of the B = 1 kernel runs out of
+// VALU issue slots before HBM saturates, so the multiply-adds go to
+// v_mfma_f32_16x16x32_f16 and the VALU only unpacks.
+//
+// One MFMA covers 16 weight rows x 32 k x 16 batch columns (B padded with
+// zeros).  Lane l supplies row (l % 16) / column (l % 16) and the 8-value k
+// block l / 16.  A lane loads one whole 16-byte group (32 codes) of its row
+// for the group g0 + l/16 of a "quad" of four groups; word p of that group
+// feeds MFMA p.  Because an MFMA then spans four different groups, each
+// weight is scaled on the A side: (code - 8) * scale rounded once to
+// binary16, a relative change below 2^-11 per weight.  The k order inside a
+// word is the unpack order (k0,k4,k1,k5,k2,k6,k3,k7); the activation block is
+// permuted in registers to match.
+#include <algorithm>
+
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) {
+    return __builtin_bit_cast(half2_t, v);
+}
+
+__device__ __forceinline__ uint32_t as_u32(half2_t v) {
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Natural-order block of 8 halves -> unpack order.
+__device__ __forceinline__ uint4 permute_block(uint4 v) {
+    uint4 o;
+    o.x = (v.x & 0xFFFFu) | (v.z << 16);
+    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    o.z = (v.y & 0xFFFFu) | (v.w << 16);
+    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return o;
+}
+
+// 8 codes of one 32-bit word -> 8 scaled binary16 weights in unpack order.
+__device__ __forceinline__ half8_t dequant_word(uint32_t v, half2_t s2) {
+    const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t bias = 0x64006400u;
+    half2_t p0 = (as_h2((v & 0x000F000Fu) | bias) - off) * s2;
+    half2_t p1 = (as_h2(((v >> 4) & 0x000F000Fu) | bias) - off) * s2;
+    half2_t p2 = (as_h2(((v >> 8) & 0x000F000Fu) | bias) - off) * s2;
+    half2_t p3 = (as_h2(((v >> 12) & 0x000F000Fu) | bias) - off) * s2;
+    uint4 u = {as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
+    return __builtin_bit_cast(half8_t, u);
+}
+
+template <int RT, int NW>
+__global__ void __launch_bounds__(64 * NW)
+gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
+                 const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
+                 int B) {
+    __shared__ float4_t red[NW][RT][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int kq = lane >> 4;
+    const int C = K >> 5;
+    const int nquads = (C + 3) >> 2;
+    const size_t row_bytes = (size_t)K >> 1;
+    const int64_t row0 = (int64_t)blockIdx.x * (16 * RT);
+
+    const bool bvalid = i16 < B;
+    const uint16_t *xb = X16 + (size_t)(bvalid ? i16 : 0) * K;
+
+    const uint8_t *wrow[RT];
+    const uint16_t *srow[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        int64_t row = row0 + t * 16 + i16;
+        row = row < N ? row : N - 1;
+        wrow[t] = W + (size_t)row * row_bytes;
+        srow[t] = S + (size_t)row * C;
+    }
+
+    float4_t acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int q = wave; q < nquads; q += NW) {
+        const int g = q * 4 + kq;
+        const bool gvalid = g < C;
+        const int gc = gvalid ? g : C - 1;
+        uint4 w[RT];
+        uint16_t s[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            w[t] = *reinterpret_cast<const uint4 *>(wrow[t] + (size_t)gc * 16);
+            s[t] = gvalid ? srow[t][gc] : (uint16_t)0;
+        }
+        half8_t bop[4];
+        {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xb + (size_t)gc * 32);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint4 v = (bvalid && gvalid) ? xp[p] : uint4{0u, 0u, 0u, 0u};
+                bop[p] = __builtin_bit_cast(half8_t, permute_block(v));
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const _Float16 sh = __builtin_bit_cast(_Float16, s[t]);
+            const half2_t s2 = {sh, sh};
+            const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(wd[p], s2), bop[p],
+                                                                acc[t], 0, 0, 0);
+        }
+    }
+
+    if constexpr (NW > 1) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            red[wave][t][lane] = acc[t];
+        __syncthreads();
+        if (wave != 0)
+            return;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            float4_t v = red[0][t][lane];
+            for (int w2 = 1; w2 < NW; ++w2)
+                v += red[w2][t][lane];
+            acc[t] = v;
+        }
+    }
+    // D layout: lane holds rows 4*(lane/16) + 0..3 of column lane % 16.
+    if (!bvalid)
+        return;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = row0 + t * 16 + 4 * kq + e;
+            if (row < N)
+                Y[(size_t)i16 * N + row] = acc[t][e];
+        }
+    }
+}
+
+using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
+                        int, int);
+
+GemmFn pick_gemm(int RT, int NW) {
+#define Q4_PICK(rt, nw)                                                          \
+    if (RT == rt && NW == nw)                                                    \
+        return gemm_mfma_kernel<rt, nw>;
+    Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
+    Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
+#undef Q4_PICK
+    return nullptr;
+}
+
+} // namespace
+
+q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
+                               const uint16_t *X16, float *Y, int64_t N, int64_t K,
+                               int32_t B, int RT, int NW, hipStream_t stream) {
+    GemmFn fn = pick_gemm(RT, NW);
+    if (!fn)
+        return fail(Q4_ERR_UNSUPPORTED, "gemm: no kernel for row_tiles=%d waves=%d", RT, NW);
+    const int64_t blocks = (N + 16 * RT - 1) / (16 * RT);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, packed, scales,
+                       X16, Y, N, (int)K, B);
+    Q4_HIP(hipGetLastError());
+    return Q4_OK;
+}
+
+q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
+                           float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream) {
+    const int64_t tiles = (N + 15) / 16;
+    const int cus = device_cus();
+    int RT = 4;
+    while (RT > 1 && tiles / RT < 2 * cus)
+        RT /= 2;
+    int NW = (tiles / RT < 4LL * cus) ? 8 : 4;
+    return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream);
+}
+
+} // namespace q4
+
+extern "C" q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
+                                        const uint16_t *X_f16, float *Y, int64_t N,
+                                        int64_t K, int32_t B, hipStream_t stream) {
+    Q4_CHECK(q4::check_matrix(packed, scales, N, K, "q4_gemm_smallbatch"));
+    if (!X_f16 || !Y)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemm_smallbatch: null X or Y");
+    if (B < 1 || B > Q4_MAX_BATCH)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemm_smallbatch: B=%d outside [1, %d]", B,
+                        Q4_MAX_BATCH);
+    if (!q4::aligned(X_f16, 16) || !q4::aligned(Y, 4))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_gemm_smallbatch: X must be 16-byte and Y 4-byte aligned");
+    if (B == 1) {
+        q4::EpiArgs ea{};
+        ea.y = Y;
+        return q4::launch_gemv(packed, scales, X_f16, N, K, q4::Epi::Store, ea, stream);
+    }
+    return q4::launch_gemm_mfma(packed, scales, X_f16, Y, N, K, B, stream);
+}
+
+extern "C" q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
+                                   const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
+                                   int32_t B, int32_t row_tiles, int32_t waves,
+                                   hipStream_t stream) {
+    Q4_CHECK(q4::check_matrix(packed, scales, N, K, "q4_gemm_tuned"));
+    if (!X_f16 || !Y)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemm_tuned: null X or Y");
+    if (B < 1 || B > Q4_MAX_BATCH)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemm_tuned: B=%d outside [1, %d]", B,
+                        Q4_MAX_BATCH);
+    if (!q4::aligned(X_f16, 16) || !q4::aligned(Y, 4))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_gemm_tuned: X must be 16-byte and Y 4-byte aligned");
+    return q4::launch_gemm_mfma_cfg(packed, scales, X_f16, Y, N, K, B, row_tiles, waves,
+                                    stream);
+}

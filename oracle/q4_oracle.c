@@ -164,17 +164,40 @@ void q4o_dequant(const uint8_t *packed, const uint16_t *scales, double *W,
 /* matrix-vector and small-batch products                               */
 /* ------------------------------------------------------------------ */
 
+/* binary16 -> double for every bit pattern, filled once from
+ * q4o_f16_to_f64 above (a lookup, not a second decoder). */
+static double g_f16_table[65536];
+static int g_f16_table_ready = 0;
+
+static void f16_table_init(void)
+{
+    if (!g_f16_table_ready) {
+        for (uint32_t h = 0; h < 65536; ++h)
+            g_f16_table[h] = q4o_f16_to_f64((uint16_t)h);
+        g_f16_table_ready = 1;
+    }
+}
+
 /* One output row: y = sum_k w[n][k] * x[k] in k order, and the magnitude
- * m = sum_k |w[n][k] * x[k]| that scales the acceptance bound. */
+ * m = sum_k |w[n][k] * x[k]| that scales the acceptance bound.  The scale
+ * of a group is decoded once for its 32 columns. */
 static void row_dot(const uint8_t *packed, const uint16_t *scales,
                     const double *x, int64_t K, int64_t n,
                     double *y, double *m)
 {
     double acc = 0.0, mag = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-        double t = weight_at(packed, scales, K, n, k) * x[k];
-        acc += t;
-        mag += fabs(t);
+    const uint8_t *prow = packed + n * (K / 2);
+    const uint16_t *srow = scales + n * (K / 32);
+    for (int64_t g = 0; g < K / 32; ++g) {
+        double s = g_f16_table[srow[g]];
+        for (int64_t k = 32 * g; k < 32 * g + 32; ++k) {
+            uint8_t b = prow[k / 2];
+            int code = (k % 2 == 0) ? (b & 0x0F) : (b >> 4);
+            double w = s * (double)(code - 8);
+            double t = w * x[k];
+            acc += t;
+            mag += fabs(t);
+        }
     }
     *y = acc;
     if (m)
@@ -187,6 +210,7 @@ void q4o_gemv(const uint8_t *packed, const uint16_t *scales,
               double *y, double *mag)
 {
     double *x = (double *)malloc(sizeof(double) * (size_t)K);
+    f16_table_init();
     q4o_f16_to_f64_array(x_f16, x, K);
     for (int64_t n = 0; n < N; ++n)
         row_dot(packed, scales, x, K, n, &y[n], mag ? &mag[n] : NULL);
@@ -201,6 +225,7 @@ void q4o_gemv_rows(const uint8_t *packed, const uint16_t *scales,
                    double *y, double *mag)
 {
     double *x = (double *)malloc(sizeof(double) * (size_t)K);
+    f16_table_init();
     q4o_f16_to_f64_array(x_f16, x, K);
     for (int64_t i = 0; i < nrows; ++i)
         row_dot(packed, scales, x, K, rows[i], &y[i], mag ? &mag[i] : NULL);

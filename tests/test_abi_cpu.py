@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/q4.h declares, and rejects bad arguments before enqueuing anything.
+
+Only host-side validation paths are exercised here (they return before any
+HIP call); nothing below launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_weight_streaming_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+INVALID, UNSUPPORTED, STATE = 1, 2, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(
+        r"^\s*(?:q4_status|const char \*|int32_t)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = q4.lib()
+    names = declared_functions()
+    assert len(names) >= 20, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert q4.abi_version() == 1
+
+
+def _err():
+    return q4.lib().q4_last_error().decode()
+
+
+def test_gemv_argument_checks():
+    L = q4.lib()
+    buf = 4096  # fake, 16-byte aligned, never dereferenced
+    assert L.q4_gemv(0, buf, buf, buf, 16, 64, None) == INVALID
+    assert "null" in _err()
+    assert L.q4_gemv(buf, buf, buf, buf, 0, 64, None) == INVALID
+    assert L.q4_gemv(buf, buf, buf, buf, 16, 48, None) == INVALID
+    assert "multiple of 32" in _err()
+    assert L.q4_gemv(buf, buf, buf, buf, 16, 16, None) == INVALID
+    assert L.q4_gemv(buf, buf, buf, buf, 16, 65536, None) == UNSUPPORTED
+    assert L.q4_gemv(buf + 8, buf, buf, buf, 16, 64, None) == INVALID
+    assert "16-byte" in _err()
+    assert L.q4_gemv(buf, buf + 1, buf, buf, 16, 64, None) == INVALID
+    assert L.q4_gemv(buf, buf, buf + 2, buf, 16, 64, None) == INVALID
+    assert L.q4_gemv(buf, buf, buf, buf + 2, 16, 64, None) == INVALID
+    assert L.q4_gemv(buf, buf, buf, 0, 16, 64, None) == INVALID
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 3, 1, None) == INVALID
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 8, None) == INVALID
+
+
+def test_gemm_argument_checks():
+    L = q4.lib()
+    buf = 4096
+    assert L.q4_gemm_smallbatch(buf, buf, buf, buf, 16, 64, 0, None) == INVALID
+    assert L.q4_gemm_smallbatch(buf, buf, buf, buf, 16, 64, 17, None) == INVALID
+    assert "outside [1, 16]" in _err()
+    assert L.q4_gemm_smallbatch(buf, buf, buf + 4, buf, 16, 64, 4, None) == INVALID
+    assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 3, 4, None) == UNSUPPORTED
+    assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 8, 8, None) == UNSUPPORTED
+
+
+def test_pack_argument_checks():
+    L = q4.lib()
+    assert L.q4_pack(0, 4096, 4, 8, None) == INVALID
+    assert L.q4_pack(4096, 4096, 4, 7, None) == INVALID
+    assert L.q4_unpack(4096, 4096, 0, 8, None) == INVALID
+
+
+DIMS = dict(d=64, H=4, Hkv=2, hd=16, dff=96)
+
+
+def _desc(**over):
+    kw = dict(n_layers=2, d_model=64, n_heads=4, n_kv_heads=2, head_dim=16, d_ff=96,
+              eps=1e-5, layers=None, h=4096, workspace=4096, workspace_bytes=1 << 20)
+    kw.update(over)
+    return q4.ModelDesc(**kw)
+
+
+def test_decoder_workspace_and_create_checks():
+    L = q4.lib()
+    out = ctypes.c_size_t()
+    assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(out)) == 0
+    # a16 f16[max(d, dff)], qkv f32[(H+2Hkv)hd], o_in f16[H hd], mlp f16[dff],
+    # each rounded up to 256 bytes
+    assert out.value == 256 + 512 + 256 + 256
+    assert q4.workspace_bytes(DIMS) == out.value
+    h = ctypes.c_void_p()
+    assert L.q4_decoder_create(ctypes.byref(_desc(n_heads=3)), ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(d_model=48)), ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(workspace=4100)), ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(workspace_bytes=100)),
+                               ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(h=0)), ctypes.byref(h)) == INVALID
+    # a layer with a wrong shape is rejected at create
+    bad = q4.layer_shapes(DIMS)
+    for m in (bad.qkv, bad.o, bad.gate_up, bad.down):
+        m.packed, m.scales = 4096, 4096
+    bad.o.N = 32
+    arr = (q4.Layer * 2)(bad, bad)
+    assert L.q4_decoder_create(ctypes.byref(_desc(layers=arr)), ctypes.byref(h)) == INVALID
+    assert "expected" in _err()
+
+
+def test_decoder_host_object_and_step_checks():
+    """A decoder without resident layers is a host object only; graph steps
+    validate ctx_len and the stream before touching HIP."""
+    L = q4.lib()
+    h = ctypes.c_void_p()
+    assert L.q4_decoder_create(ctypes.byref(_desc()), ctypes.byref(h)) == 0
+    try:
+        assert L.decode_step_graph(h, 0, 1234) == INVALID
+        assert L.decode_step_graph(h, -5, 1234) == INVALID
+        assert L.decode_step_graph(h, 4097, 1234) == UNSUPPORTED
+        assert L.decode_step_graph(h, 100, None) == INVALID  # NULL stream
+        assert L.decode_step_graph(h, 100, 1234) == STATE    # no resident layers
+        assert L.q4_decode_step_eager(h, None) == STATE
+        assert L.q4_decode_layer(h, None, None) == INVALID
+    finally:
+        assert L.q4_decoder_destroy(h) == 0
+    assert L.decode_step_graph(None, 100, 1234) == INVALID
+
+
+def test_blob_layout_is_aligned_and_ordered():
+    offs, total = q4.layer_blob_layout(DIMS)
+    sizes = [(128 * 64) // 2, 128 * 2 * 2, 64 * 64 // 2, 64 * 2 * 2,
+             192 * 64 // 2, 192 * 2 * 2, 64 * 96 // 2, 64 * 3 * 2]
+    assert offs[0] == 0
+    for i in range(8):
+        assert offs[i] % 256 == 0
+        end = offs[i] + sizes[i]
+        nxt = offs[i + 1] if i < 7 else total
+        assert end <= nxt < end + 256
+    # 8B shapes: the merged blob is the four matrices plus scales, padded
+    dims8 = dict(d=4096, H=32, Hkv=8, hd=128, dff=14336)
+    _, total8 = q4.layer_blob_layout(dims8)
+    assert 122683392 <= total8 < 122683392 + 8 * 256
+    layer = q4.layer_from_blob(DIMS, 1 << 20)
+    assert layer.o.packed == (1 << 20) + offs[2] and layer.down.scales == (1 << 20) + offs[7]
+
+
+def test_wstream_argument_checks():
+    L = q4.lib()
+    out = ctypes.c_void_p()
+    blobs = (ctypes.c_void_p * 2)(4096, 8192)
+    sizes = (ctypes.c_size_t * 2)(1000, 5000)
+    d = q4.WStreamDesc(2, blobs, sizes, (ctypes.c_void_p * 2)(4096, 8192), 4096, 1234)
+    assert L.q4_wstream_create(ctypes.byref(d), ctypes.byref(out)) == INVALID  # 5000 > slot
+    assert "larger than a slot" in _err()
+    d2 = q4.WStreamDesc(2, blobs, sizes, (ctypes.c_void_p * 2)(4096, 0), 8192, 1234)
+    assert L.q4_wstream_create(ctypes.byref(d2), ctypes.byref(out)) == INVALID
+    d3 = q4.WStreamDesc(0, blobs, sizes, (ctypes.c_void_p * 2)(4096, 8192), 8192, 1234)
+    assert L.q4_wstream_create(ctypes.byref(d3), ctypes.byref(out)) == INVALID
+    d4 = q4.WStreamDesc(2, blobs, sizes, (ctypes.c_void_p * 2)(4096, 8192), 8192, None)
+    assert L.q4_wstream_create(ctypes.byref(d4), ctypes.byref(out)) == INVALID
+    assert L.weight_stream_begin(None, 0) == INVALID
+    slot = ctypes.c_void_p()
+    assert L.weight_stream_wait(None, 0, None, ctypes.byref(slot)) == INVALID

@@ -1,0 +1,237 @@
+"""GPU parity of q4_pack / q4_unpack / q4_gemv / q4_gemm_smallbatch against the
+CPU oracle, through the C ABI.
+
+Bar: packing bit-exact; products within |y - y_ref| <= 2e-3 * sum|w x| + 1e-6
+per output.  Shapes span several tiles, ragged tails (N not a multiple of the
+row tile, K not a multiple of the lane stride) and the full workload shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import int4_weight_streaming_q4_amd as q4
+from int4_weight_streaming_q4_amd import inputs
+from helpers import DEV, assert_within, rel_err_stats, sync, u16, u8
+
+pytestmark = pytest.mark.gpu
+
+CFG = 1  # seeds of the single-GEMV workload
+
+
+def _mat(N, K, seed, device=DEV):
+    """Random packed weights + scales drawn on `device` (bytes identical for
+    the oracle, which gets a host copy)."""
+    packed = inputs.random_bytes(N, K, seed, device=device)
+    scales = inputs.scales(N, K, seed + 1, device=device)
+    return packed.to(DEV), scales.to(DEV)
+
+
+def _gemv(packed, scales, x):
+    y = torch.empty(packed.shape[0], dtype=torch.float32, device=DEV)
+    q4.q4_gemv(packed, scales, x, y)
+    sync()
+    return y.cpu().numpy()
+
+
+# --------------------------------------------------------------- packing
+def test_pack_bit_exact_config_shape():
+    codes = inputs.codes(4096, 4096, inputs.seed_of(CFG, 0, 7))
+    dcodes = codes.to(DEV)
+    packed = torch.empty(4096, 2048, dtype=torch.uint8, device=DEV)
+    q4.q4_pack(dcodes, packed)
+    sync()
+    ref = oracle.pack(codes.numpy())
+    assert np.array_equal(u8(packed), ref)
+    back = torch.empty_like(dcodes)
+    q4.q4_unpack(packed, back)
+    sync()
+    assert np.array_equal(u8(back), codes.numpy())
+
+
+@pytest.mark.parametrize("N,K", [(1, 2), (3, 34), (65, 96), (7, 4130)])
+def test_pack_ragged_and_high_bits(N, K):
+    g = torch.Generator().manual_seed(N * 1000 + K)
+    codes = torch.randint(0, 256, (N, K), dtype=torch.uint8, generator=g)  # high bits set
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    q4.q4_pack(codes.to(DEV), packed)
+    sync()
+    assert np.array_equal(u8(packed), oracle.pack(codes.numpy()))
+    back = torch.empty(N, K, dtype=torch.uint8, device=DEV)
+    q4.q4_unpack(packed, back)
+    sync()
+    assert np.array_equal(u8(back), oracle.unpack(u8(packed)))
+
+
+# --------------------------------------------------------------- gemv
+def test_gemv_config1_full_parity_and_determinism():
+    N = K = 4096
+    codes = inputs.codes(N, K, inputs.seed_of(CFG, 0, 0))
+    scales = inputs.scales(N, K, inputs.seed_of(CFG, 0, 1))
+    x = inputs.act_f16(K, inputs.seed_of(CFG, 0, 2))
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    q4.q4_pack(codes.to(DEV), packed)
+    ds, dx = scales.to(DEV), x.to(DEV)
+    y1 = _gemv(packed, ds, dx)
+    y2 = _gemv(packed, ds, dx)
+    assert np.array_equal(y1, y2), "repeated calls must be bitwise identical"
+    y_ref, mag = oracle.gemv(oracle.pack(codes.numpy()), u16(scales), u16(x))
+    assert_within(y1, y_ref, mag, "config 1 gemv")
+    print("config1 max/median rel err (vs sum|wx|):", rel_err_stats(y1, y_ref, mag))
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (65, 2080), (17, 4128), (4101, 512),
+                                 (130, 32768), (64, 28672)])
+def test_gemv_odd_shapes(N, K):
+    packed, scales = _mat(N, K, 1000 + N * 7 + K)
+    x = inputs.act_f16(K, 2000 + N + K, device=DEV)
+    y = _gemv(packed, scales, x)
+    y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
+    assert_within(y, y_ref, mag, f"gemv {N}x{K}")
+
+
+@pytest.mark.parametrize("rows_per_slot", [1, 2, 4])
+@pytest.mark.parametrize("k_split", [1, 2, 4])
+def test_gemv_every_launch_shape(rows_per_slot, k_split):
+    N, K = 333, 1056  # ragged in rows and in chunks per lane
+    packed, scales = _mat(N, K, 77)
+    x = inputs.act_f16(K, 78, device=DEV)
+    y = torch.empty(N, dtype=torch.float32, device=DEV)
+    q4.q4_gemv_tuned(packed, scales, x, y, rows_per_slot, k_split)
+    sync()
+    y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
+    assert_within(y.cpu().numpy(), y_ref, mag, f"gemv R={rows_per_slot} KS={k_split}")
+
+
+def _f16(v):
+    return torch.from_numpy(np.asarray(v, np.float64).astype(np.float16).view(np.int16))
+
+
+def test_gemv_special_values():
+    N, K = 48, 256
+    g = torch.Generator().manual_seed(5)
+    x = inputs.act_f16(K, 9)
+    dx = x.to(DEV)
+    # zero point: all codes 8 -> exactly 0
+    packed = torch.full((N, K // 2), 0x88, dtype=torch.uint8, device=DEV)
+    scales = inputs.scales(N, K, 10).to(DEV)
+    y = _gemv(packed, scales, dx)
+    assert np.all(np.abs(y) <= 1e-6) and np.all(y == 0.0)
+    # all codes 0 and all 15, subnormal / zero / max scales
+    for byte, sbits in [(0x00, 0x0001), (0xFF, 0x03FF), (0x00, 0x0000), (0xFF, 0x7BFF),
+                        (0x5A, 0x3C00)]:
+        packed = torch.full((N, K // 2), byte, dtype=torch.uint8, device=DEV)
+        sc = torch.full((N, K // 32), sbits, dtype=torch.int16, device=DEV)
+        xs = x if sbits != 0x7BFF else _f16(np.random.default_rng(1).standard_normal(K) * 1e-3)
+        y = _gemv(packed, sc, xs.to(DEV))
+        y_ref, mag = oracle.gemv(u8(packed), u16(sc), u16(xs))
+        assert_within(y, y_ref, mag, f"byte {byte:#x} scale {sbits:#x}")
+    # impulse x: one product, exact in fp32 -> bitwise equal to the oracle
+    packed, scales = _mat(N, K, 11)
+    for k in (0, 1, 4, 7, 31, 32, 200, 255):
+        e = np.zeros(K)
+        e[k] = 1.0
+        y = _gemv(packed, scales, _f16(e).to(DEV))
+        y_ref, _ = oracle.gemv(u8(packed), u16(scales), u16(_f16(e)))
+        assert np.array_equal(y.astype(np.float64), y_ref), k
+
+
+def test_gemv_linearity_small_integers():
+    N, K = 200, 1024
+    packed, scales = _mat(N, K, 21)
+    rng = np.random.default_rng(3)
+    x1 = rng.integers(-4, 5, K).astype(np.float64)
+    x2 = rng.integers(-4, 5, K).astype(np.float64)
+    y1 = _gemv(packed, scales, _f16(x1).to(DEV)).astype(np.float64)
+    y2 = _gemv(packed, scales, _f16(x2).to(DEV)).astype(np.float64)
+    y12 = _gemv(packed, scales, _f16(x1 + x2).to(DEV)).astype(np.float64)
+    _, m1 = oracle.gemv(u8(packed), u16(scales), u16(_f16(x1)))
+    _, m2 = oracle.gemv(u8(packed), u16(scales), u16(_f16(x2)))
+    assert np.all(np.abs(y12 - (y1 + y2)) <= 2e-3 * (m1 + m2) + 1e-6)
+
+
+WORKLOAD_SHAPES = {
+    "8b_qkv": (6144, 4096), "8b_o": (4096, 4096), "8b_gate_up": (28672, 4096),
+    "8b_down": (4096, 14336), "70b_qkv": (10240, 8192), "70b_o": (8192, 8192),
+    "70b_gate_up": (57344, 8192), "70b_down": (8192, 28672),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOAD_SHAPES))
+def test_gemv_workload_shapes_sampled_rows(name):
+    """Full-size shapes, launched as in the decode step; every 97th row plus
+    the last rows are checked one by one by the oracle."""
+    N, K = WORKLOAD_SHAPES[name]
+    packed, scales = _mat(N, K, inputs.seed_of(2, 0, list(WORKLOAD_SHAPES).index(name)))
+    x = inputs.act_f16(K, 555, device=DEV)
+    y = _gemv(packed, scales, x)
+    assert np.all(np.isfinite(y))
+    rows = np.unique(np.concatenate([np.arange(0, N, 97), np.arange(N - 5, N)]))
+    hp = u8(packed)
+    hs = u16(scales)
+    y_ref, mag = oracle.gemv_rows(hp, hs, u16(x), rows)
+    assert_within(y[rows], y_ref, mag, name)
+
+
+# --------------------------------------------------------------- gemm
+def _gemm(packed, scales, X, tuned=None):
+    B = X.shape[0]
+    Y = torch.empty(B, packed.shape[0], dtype=torch.float32, device=DEV)
+    if tuned:
+        q4.q4_gemm_tuned(packed, scales, X, Y, *tuned)
+    else:
+        q4.q4_gemm_smallbatch(packed, scales, X, Y)
+    sync()
+    return Y.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (65, 2080), (300, 1024)])
+def test_gemm_small_shapes(B, N, K):
+    packed, scales = _mat(N, K, 300 + B + N + K)
+    X = inputs.act_f16((B, K), 400 + B + K, device=DEV)
+    Y = _gemm(packed, scales, X)
+    Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
+    for b in range(B):
+        assert_within(Y[b], Y_ref[b], M[b], f"gemm B={B} {N}x{K} col {b}")
+
+
+@pytest.mark.parametrize("rt,nw", [(1, 4), (2, 4), (4, 4), (8, 4), (1, 8), (2, 8), (4, 8)])
+def test_gemm_every_launch_shape(rt, nw):
+    N, K, B = 200, 1184, 7  # 37 groups: ragged group quads
+    packed, scales = _mat(N, K, 900)
+    X = inputs.act_f16((B, K), 901, device=DEV)
+    Y = _gemm(packed, scales, X, tuned=(rt, nw))
+    Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
+    for b in range(B):
+        assert_within(Y[b], Y_ref[b], M[b], f"gemm rt={rt} nw={nw} col {b}")
+
+
+def test_gemm_b1_is_gemv_and_columns_match_gemv():
+    N, K = 512, 2048
+    packed, scales = _mat(N, K, 31)
+    X = inputs.act_f16((8, K), 32, device=DEV)
+    Y1 = _gemm(packed, scales, X[:1].contiguous())
+    assert np.array_equal(Y1[0], _gemv(packed, scales, X[0].contiguous()))
+    Y = _gemm(packed, scales, X)
+    Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
+    for b in range(8):
+        yv = _gemv(packed, scales, X[b].contiguous())
+        assert np.all(np.abs(Y[b].astype(np.float64) - yv) <= 2 * (2e-3 * M[b] + 1e-6))
+    Y2 = _gemm(packed, scales, X)
+    assert np.array_equal(Y, Y2)
+
+
+@pytest.mark.parametrize("name", ["8b_qkv", "8b_o", "8b_gate_up", "8b_down"])
+@pytest.mark.parametrize("B", [4, 8, 16])
+def test_gemm_workload_shapes_sampled_rows(name, B):
+    N, K = WORKLOAD_SHAPES[name]
+    packed, scales = _mat(N, K, inputs.seed_of(3, 0, list(WORKLOAD_SHAPES).index(name)))
+    X = inputs.act_f16((B, K), inputs.seed_of(3, 0, 9) + B, device=DEV)
+    Y = _gemm(packed, scales, X)
+    assert np.all(np.isfinite(Y))
+    rows = np.unique(np.concatenate([np.arange(0, N, 211), np.arange(N - 3, N)]))
+    hp, hs, hx = u8(packed), u16(scales), u16(X)
+    for b in range(B):
+        y_ref, mag = oracle.gemv_rows(hp, hs, hx[b], rows)
+        assert_within(Y[b][rows], y_ref, mag, f"{name} B={B} col {b}")
