@@ -185,6 +185,15 @@ q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
 q4_status decode_step_graph(void *dec, int32_t ctx_len, hipStream_t stream);
 /* Same layer loop, enqueued eagerly without a graph (for checking). */
 q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
+/* Layer-wise profiling (PipeLLM, "Layer 2: Asynchronous Weight
+ * Prefetching" lists per-layer analysis and event-based timing among its
+ * tools): the eager step with a timing event recorded on `stream` after
+ * every kernel.  Writes each kernel's duration in milliseconds to the host
+ * array ms_out in launch order -- per layer: norm, QKV, O, norm, gate+up,
+ * down (6 per layer) -- and their count to *n_out.  capacity must be at
+ * least 6 * n_layers.  Synchronises `stream` before returning. */
+q4_status q4_decode_step_profiled(void *dec, hipStream_t stream, float *ms_out,
+                                  int32_t capacity, int32_t *n_out);
 /* One layer, eagerly, with the weights given (e.g. a streamed slot). */
 q4_status q4_decode_layer(void *dec, const q4_layer *layer, hipStream_t stream);
 /* Frees graphs and host state.  Call after the last step has completed. */

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         "q4_decoder_create": (S, [ctypes.POINTER(ModelDesc), ctypes.POINTER(_P)]),
         "decode_step_graph": (S, [_P, _I32, _P]),
         "q4_decode_step_eager": (S, [_P, _P]),
+        "q4_decode_step_profiled": (S, [_P, _P, ctypes.POINTER(ctypes.c_float), _I32,
+                                        ctypes.POINTER(_I32)]),
         "q4_decode_layer": (S, [_P, ctypes.POINTER(Layer), _P]),
         "q4_decoder_destroy": (S, [_P]),
         "q4_layer_blob_layout": (S, [ctypes.POINTER(Layer), ctypes.c_size_t * 8,
@@ -221,6 +223,7 @@ class Decoder:
         if layers is not None:
             arr = (Layer * n)(*(make_layer(w) for w in layers))
         self._keep = (layers, h, workspace, arr)  # buffers the graphs bake in
+        self._n_layers = n
         desc = _model_desc(dims, n, arr, h, workspace, workspace.numel(), eps)
         handle = _P()
         _check(lib().q4_decoder_create(ctypes.byref(desc), ctypes.byref(handle)))
@@ -231,6 +234,16 @@ class Decoder:
 
     def step_eager(self, stream=None):
         _check(lib().q4_decode_step_eager(self.handle, _stream(stream)))
+
+    def step_profiled(self, stream=None):
+        """Eager step; returns per-kernel durations in ms (6 per layer)."""
+        n_layers = self._n_layers
+        cap = 6 * n_layers
+        buf = (ctypes.c_float * cap)()
+        n = _I32()
+        _check(lib().q4_decode_step_profiled(self.handle, _stream(stream), buf, cap,
+                                             ctypes.byref(n)))
+        return list(buf[:n.value])
 
     def layer(self, weights, stream=None):
         L = weights if isinstance(weights, Layer) else make_layer(weights)

@@ -25,6 +25,7 @@ namespace q4 {
 namespace {
 
 constexpr int kBuckets[4] = {512, 1024, 2048, 4096};
+constexpr int kKernelsPerLayer = 6;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -100,13 +101,29 @@ q4_status check_layer(const Dims &d, const q4_layer &L, int idx) {
     return Q4_OK;
 }
 
-// Enqueue one layer on `s`.
-q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s) {
+// Records a timing mark on `s` after each kernel when profiling.
+struct Marks {
+    std::vector<hipEvent_t> *ev = nullptr;
+    q4_status mark(hipStream_t s) {
+        if (!ev)
+            return Q4_OK;
+        hipEvent_t e = nullptr;
+        Q4_HIP(hipEventCreate(&e));
+        ev->push_back(e);
+        Q4_HIP(hipEventRecord(e, s));
+        return Q4_OK;
+    }
+};
+
+// Enqueue one layer on `s`: norm, QKV (+ attention-output gather), O
+// (+ residual), norm, gate+up (+ SiLU gate), down (+ residual).
+q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks marks = {}) {
     const Dims &d = dec->dims;
     float *h = dec->desc.h;
     EpiArgs ea{};
 
     Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
+    Q4_CHECK(marks.mark(s));
     ea = EpiArgs{};
     ea.y = dec->qkv;
     ea.out16 = dec->oin;
@@ -115,20 +132,25 @@ q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s) {
     ea.group = (int32_t)(d.H / d.Hkv);
     Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->a16, L.qkv.N, L.qkv.K,
                          Epi::QkvGather, ea, s));
+    Q4_CHECK(marks.mark(s));
     ea = EpiArgs{};
     ea.y = h;
     Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oin, L.o.N, L.o.K, Epi::Residual, ea, s));
+    Q4_CHECK(marks.mark(s));
 
     Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
+    Q4_CHECK(marks.mark(s));
     ea = EpiArgs{};
     ea.out16 = dec->mlp;
     ea.pair_off = d.dff;
     Q4_CHECK(launch_gemv(L.gate_up.packed, L.gate_up.scales, dec->a16, L.gate_up.N,
                          L.gate_up.K, Epi::SiluPair, ea, s));
+    Q4_CHECK(marks.mark(s));
     ea = EpiArgs{};
     ea.y = h;
     Q4_CHECK(launch_gemv(L.down.packed, L.down.scales, dec->mlp, L.down.N, L.down.K,
                          Epi::Residual, ea, s));
+    Q4_CHECK(marks.mark(s));
     return Q4_OK;
 }
 
@@ -452,4 +474,39 @@ extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t
         Q4_CHECK(q4::enqueue_layer(dec, layer, compute));
     }
     return Q4_OK;
+}
+
+extern "C" q4_status q4_decode_step_profiled(void *decp, hipStream_t stream, float *ms_out,
+                                             int32_t capacity, int32_t *n_out) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec || !ms_out || !n_out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_profiled: null argument");
+    if (dec->layers.empty())
+        return q4::fail(Q4_ERR_STATE, "q4_decode_step_profiled: decoder has no resident layers");
+    const int64_t need = (int64_t)dec->layers.size() * q4::kKernelsPerLayer;
+    if (capacity < need)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_profiled: capacity %d < %lld",
+                        capacity, (long long)need);
+    std::vector<hipEvent_t> ev;
+    q4::Marks marks;
+    marks.ev = &ev;
+    q4_status st = marks.mark(stream);
+    for (size_t l = 0; st == Q4_OK && l < dec->layers.size(); ++l)
+        st = q4::enqueue_layer(dec, dec->layers[l], stream, marks);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (st == Q4_OK && e != hipSuccess)
+        st = q4::fail(Q4_ERR_HIP, "q4_decode_step_profiled: %s", hipGetErrorString(e));
+    int32_t n = 0;
+    for (size_t i = 1; st == Q4_OK && i < ev.size(); ++i) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, ev[i - 1], ev[i]);
+        if (e != hipSuccess)
+            st = q4::fail(Q4_ERR_HIP, "q4_decode_step_profiled: elapsed: %s",
+                          hipGetErrorString(e));
+        ms_out[n++] = ms;
+    }
+    for (hipEvent_t x : ev)
+        (void)hipEventDestroy(x);
+    *n_out = n;
+    return st;
 }

@@ -1,0 +1,159 @@
+"""Double-buffered layer streaming: results equal to resident weights bitwise,
+under host-forced stalls of either stream, and ordering errors reported.
+
+Stalls use torch's spin kernel (torch.cuda._sleep) enqueued on the copy or the
+compute stream; every kernel exits normally.  A missing read-after-write edge
+(compute before the copy landed) or write-after-read edge (the copy
+overwriting a slot still being read) changes the result and fails the
+bitwise comparison.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_streaming_q4_amd as q4
+from int4_weight_streaming_q4_amd import inputs
+from helpers import DEV, u16, u8
+
+pytestmark = pytest.mark.gpu
+
+TINY = dict(d=64, H=4, Hkv=2, hd=16, dff=96)
+EPS = 1e-5
+
+
+def blobs_for(dims, layers):
+    """Merge each layer's tensors into one pinned host blob (one transfer per
+    layer) using the library's blob layout."""
+    offs, total = q4.layer_blob_layout(dims)
+    out = []
+    for L in layers:
+        b = torch.zeros(total, dtype=torch.uint8, pin_memory=True)
+        for i, name in enumerate(("qkv", "o", "gate_up", "down")):
+            p, s = L[name]
+            pb = p.cpu().contiguous().view(torch.uint8).reshape(-1)
+            sb = s.cpu().contiguous().view(torch.uint8).reshape(-1)
+            b[offs[2 * i]:offs[2 * i] + pb.numel()] = pb
+            b[offs[2 * i + 1]:offs[2 * i + 1] + sb.numel()] = sb
+        out.append(b)
+    return out, total
+
+
+def resident_tokens(dims, layers, h0s):
+    h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
+    ws = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+    dec = q4.Decoder(dims, layers, h, ws, EPS)
+    s = torch.cuda.Stream()
+    outs = []
+    for h0 in h0s:
+        h.copy_(h0.to(DEV))
+        torch.cuda.synchronize()
+        dec.step_eager(s)
+        s.synchronize()
+        outs.append(h.cpu().clone())
+    dec.close()
+    return outs
+
+
+class Streamed:
+    def __init__(self, dims, layers):
+        self.dims = dims
+        self.blobs, total = blobs_for(dims, layers)
+        self.slots = [torch.empty(total, dtype=torch.uint8, device=DEV) for _ in range(2)]
+        self.copy = torch.cuda.Stream()
+        self.compute = torch.cuda.Stream()
+        self.ws = q4.WeightStream(self.blobs, self.slots, self.copy)
+        self.h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
+        self.wsp = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+        self.dec = q4.Decoder(dims, None, self.h, self.wsp, EPS, n_layers=len(layers))
+        self.n = len(layers)
+
+    def set_h(self, h0):
+        self.h.copy_(h0.to(DEV))
+        torch.cuda.synchronize()
+
+    def token_native(self):
+        self.dec.token_streamed(self.ws, self.compute)
+        self.compute.synchronize()
+        return self.h.cpu().clone()
+
+    def token_python(self, stall_copy=0, stall_compute=0, poison=False):
+        """Same loop driven from Python, with optional stalls."""
+        n = self.n
+        for l in range(n):
+            if l == 0 and not getattr(self, "_pref", False):
+                if stall_copy:
+                    with torch.cuda.stream(self.copy):
+                        torch.cuda._sleep(stall_copy)
+                self.ws.begin(0)
+            if stall_copy:
+                with torch.cuda.stream(self.copy):
+                    torch.cuda._sleep(stall_copy)
+            self.ws.begin((l + 1) % n)
+            self._pref = True
+            ptr = self.ws.wait(l, self.compute)
+            if stall_compute:
+                with torch.cuda.stream(self.compute):
+                    torch.cuda._sleep(stall_compute)
+            self.dec.layer(q4.layer_from_blob(self.dims, ptr), self.compute)
+        self.compute.synchronize()
+        return self.h.cpu().clone()
+
+
+def _h0s(dims, config, n):
+    return [inputs.residual_f32(dims["d"], inputs.seed_of(config, t, 9)) for t in range(n)]
+
+
+@pytest.mark.parametrize("n_layers", [1, 2, 5])
+def test_streamed_equals_resident(n_layers):
+    layers = [inputs.layer_weights(TINY, 95, l, device=DEV) for l in range(n_layers)]
+    h0s = _h0s(TINY, 95, 3)
+    want = resident_tokens(TINY, layers, h0s)
+    st = Streamed(TINY, layers)
+    for t, h0 in enumerate(h0s):
+        st.set_h(h0)
+        assert torch.equal(st.token_native(), want[t]), (n_layers, t)
+
+
+def test_streamed_under_stalls_equals_resident():
+    n = 5
+    layers = [inputs.layer_weights(TINY, 96, l, device=DEV) for l in range(n)]
+    h0s = _h0s(TINY, 96, 2)
+    want = resident_tokens(TINY, layers, h0s)
+    for kind in ("copy", "compute"):
+        st = Streamed(TINY, layers)
+        for t, h0 in enumerate(h0s):
+            st.set_h(h0)
+            got = st.token_python(stall_copy=2_000_000 if kind == "copy" else 0,
+                                  stall_compute=2_000_000 if kind == "compute" else 0)
+            assert torch.equal(got, want[t]), (kind, t)
+
+
+def test_wstream_ordering_errors():
+    layers = [inputs.layer_weights(TINY, 97, l, device=DEV) for l in range(3)]
+    st = Streamed(TINY, layers)
+    with pytest.raises(q4.Q4Error, match="STATE"):
+        st.ws.wait(0, st.compute)              # wait before begin
+    st.ws.begin(0)
+    st.ws.begin(1)
+    with pytest.raises(q4.Q4Error, match="STATE"):
+        st.ws.begin(2)                         # both slots hold unconsumed layers
+    with pytest.raises(q4.Q4Error, match="STATE"):
+        st.ws.wait(1, st.compute)              # out of order
+    with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
+        st.ws.begin(3)                         # out of range
+    st.ws.wait(0, st.compute)
+    st.ws.wait(1, st.compute)
+    st.compute.synchronize()
+    st.copy.synchronize()
+
+
+def test_70b_shapes_streamed_equals_resident():
+    """Four layers of the 70B shapes (481 MB blobs) streamed vs resident."""
+    dims = {k: v for k, v in inputs.MODEL_DIMS["70b"].items() if k != "n_layers"}
+    layers = [inputs.layer_weights(dims, 5, l, device=DEV) for l in range(4)]
+    h0s = _h0s(dims, 5, 2)
+    want = resident_tokens(dims, layers, h0s)
+    st = Streamed(dims, layers)
+    for t, h0 in enumerate(h0s):
+        st.set_h(h0)
+        assert torch.equal(st.token_native(), want[t]), t
