@@ -29,9 +29,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--profiled-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for "
+                         "hardware byte counters)")
     return ap.parse_args()
 
 
@@ -71,6 +73,13 @@ def main():
     ws = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
     dec = q4.Decoder(dims, layers, h, ws)
     stream = torch.cuda.Stream()
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written by one plain copy kernel
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     ctx_len = 512
     torch.cuda.synchronize()
 
@@ -97,19 +106,18 @@ def main():
     ms_per_step = ms / args.steps
     tokens_per_s = 1000.0 / ms_per_step
 
-    # dominant kernel: gate+up, timed with events around every kernel of an
-    # eager step on the same stream
-    prof = []
+    # Per-kernel durations, each kernel launched back to back between two
+    # events on the decode stream, cycling through the 32 layers (the
+    # dominant one, gate+up, gives the roofline line).
+    reps = 3 * n_layers
+    names = ["qkv", "o", "gate_up", "down"]
     with torch.cuda.stream(stream):
-        for _ in range(args.profiled_steps):
-            prof.append(dec.step_profiled(stream))
-    prof = np.array(prof)  # [steps, 6 * n_layers]
-    per_kernel = prof.reshape(prof.shape[0], n_layers, 6).mean(axis=(0, 1))  # ms
-    names = ["norm1", "qkv", "o", "norm2", "gate_up", "down"]
-    gu_N, gu_K = shapes[2]
-    gu_bytes = gu_N * gu_K // 2 + gu_N * (gu_K // 32) * 2 + gu_K * 2 + (gu_N // 2) * 2
-    gu_ms = float(per_kernel[4])
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        kern_us = [dec.kernel_time_us(k, reps, stream) for k in range(4)]
+    kbytes = kernel_bytes(dims)
+    gu_us = kern_us[2]
+    achieved = kbytes[2] / (gu_us * 1e-6) / 1e9
+    traffic = recorded_traffic()
+    gemv1 = single_gemv(q4, inputs, torch)
 
     result = {
         "metric": "INT4 GEMV HBM GB/s (% of peak) + 8B-shape batch-1 decode tokens/s",
@@ -132,16 +140,103 @@ def main():
         "hbm_frac_step": round(bytes_per_token * tokens_per_s / 1e9 / HBM_PEAK_GBS, 4),
         "us_per_layer": round(ms_per_step * 1000.0 / n_layers, 3),
         "wall_s_timed": round(wall, 4),
-        "kernel_us_eager": {n: round(float(v) * 1000.0, 3) for n, v in zip(names, per_kernel)},
-        "roofline": {"bound": "hbm", "kernel": "gate_up product 28672x4096 (SiLU-gated epilogue)",
+        "kernels": {n: {"us": round(u, 3), "GB/s": round(b / u / 1e3, 1)}
+                    for n, u, b in zip(names, kern_us, kbytes)},
+        "gemv_4096x4096": gemv1,
+        "roofline": {"bound": "hbm",
+                     "kernel": "gate_up product 28672x4096 (RMSNorm prologue, SiLU-gate epilogue)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1000.0, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": kbytes[2], "avg_launch_us": round(gu_us, 3)},
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_tokens)
     print(json.dumps(result), flush=True)
+
+
+def kernel_bytes(dims):
+    """Algorithmic bytes of each decode kernel: packed codes and binary16
+    scales once, the activation read (fp32 residual for the two kernels
+    that normalise it, binary16 otherwise) and the output written."""
+    d, H, Hkv, hd, dff = (dims[k] for k in ("d", "H", "Hkv", "hd", "dff"))
+    nqkv = (H + 2 * Hkv) * hd
+    w = lambda N, K: N * K // 2 + N * (K // 32) * 2
+    return [w(nqkv, d) + 4 * d + 4 * nqkv + 2 * H * hd,     # qkv: h in, qkv f32 + o_in f16 out
+            w(d, H * hd) + 2 * H * hd + 8 * d,               # o: o_in in, h read + written
+            w(2 * dff, d) + 4 * d + 2 * dff,                 # gate+up: h in, gated f16 out
+            w(d, dff) + 2 * dff + 8 * d]                     # down: gated in, h read + written
+
+
+KERNEL_SOURCES = ["int4_weight_streaming_q4_amd/csrc/q4_gemv.hip",
+                  "int4_weight_streaming_q4_amd/csrc/q4_internal.h"]
+PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
+
+
+def kernel_source_hash():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(root, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per gate+up launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, PMC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("    ") and ":" in line:
+            k, v = line.strip().split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def single_gemv(q4, inputs, torch):
+    """The 4096 x 4096 single product: 64 distinct weight copies (605 MB, more
+    than the 256 MB last-level cache) launched round-robin inside one
+    captured graph, replayed; average per launch."""
+    N = K = 4096
+    copies = 64
+    Ws = [(inputs.random_bytes(N, K, inputs.seed_of(1, i, 0), device="cuda"),
+           inputs.scales(N, K, inputs.seed_of(1, i, 1), device="cuda")) for i in range(copies)]
+    x = inputs.act_f16(K, inputs.seed_of(1, 0, 2), device="cuda")
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for p, sc in Ws:  # warm the launch-shape cache outside the capture
+            q4.q4_gemv(p, sc, x, y, stream=s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for p, sc in Ws:
+            q4.q4_gemv(p, sc, x, y, stream=s)
+    reps = 20
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):  # replay and events on the same stream
+        g.replay()
+        s.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * copies)
+    nbytes = N * K // 2 + N * (K // 32) * 2 + 2 * K + 4 * N
+    gbs = nbytes / us / 1e3
+    return {"us": round(us, 3), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nbytes}
 
 
 def cpu_baseline(layers, dims, h0, n_tokens):

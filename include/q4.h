@@ -109,15 +109,18 @@ q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
                              int64_t K, int32_t B, hipStream_t stream);
 
 /* Tuning variants of the two products, for measurement: the same
- * arithmetic with an explicit launch shape.  rows_per_slot, k_split in
- * {1, 2, 4}: rows held by each 16-lane row of a wave, and waves sharing one
- * row's k range.  row_tiles in {1, 2, 4, 8} (8 only with waves == 4),
- * waves in {4, 8}: 16-row tiles per workgroup and waves splitting k.  B == 1
- * is allowed here and runs the matrix-core kernel.  UNSUPPORTED for other
- * values. */
+ * arithmetic with an explicit launch shape.  q4_gemv_tuned: rows_per_slot
+ * and k_split in {1, 2, 4} (rows held by each 16-lane row of a wave, waves
+ * sharing one row's k range), chunks_in_flight in {4, 8} (16-byte chunks of
+ * each row a lane loads before using them), nontemporal 0/1 (weight loads
+ * marked non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} (8 only
+ * with waves == 4) and waves in {4, 8} (16-row tiles per workgroup, waves
+ * splitting k); B == 1 is allowed and runs the matrix-core kernel.
+ * INVALID_ARG / UNSUPPORTED for other values. */
 q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales,
                         const uint16_t *x_f16, float *y, int64_t N, int64_t K,
-                        int32_t rows_per_slot, int32_t k_split, hipStream_t stream);
+                        int32_t rows_per_slot, int32_t k_split, int32_t chunks_in_flight,
+                        int32_t nontemporal, hipStream_t stream);
 q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
                         const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
                         int32_t B, int32_t row_tiles, int32_t waves,
@@ -150,10 +153,10 @@ typedef struct {
     /* host array of n_layers layers, copied at create; may be NULL when the
      * decoder is only driven layer by layer (q4_decode_layer). */
     const q4_layer *layers;
-    float *h;                  /* device f32[d]: residual in/out, retained */
+    float *h;                  /* device f32[d], 16-byte aligned: residual in/out, retained */
     /* device, 256-byte aligned, retained.  After a layer it holds, each
      * section starting at a 256-byte boundary in this order: the binary16
-     * normed activation of the second norm (max(d, dff) slots), the fp32
+     * normed input of gate+up, i.e. the second norm (max(d, dff) slots), the fp32
      * QKV output ((H + 2*Hkv)*hd), the binary16 attention output (H*hd)
      * and the binary16 gated MLP activation (dff). */
     void *workspace;
@@ -189,11 +192,19 @@ q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
  * Prefetching" lists per-layer analysis and event-based timing among its
  * tools): the eager step with a timing event recorded on `stream` after
  * every kernel.  Writes each kernel's duration in milliseconds to the host
- * array ms_out in launch order -- per layer: norm, QKV, O, norm, gate+up,
- * down (6 per layer) -- and their count to *n_out.  capacity must be at
- * least 6 * n_layers.  Synchronises `stream` before returning. */
+ * array ms_out in launch order -- per layer: QKV (with the first norm), O,
+ * gate+up (with the second norm and the SiLU gate), down: 4 per layer --
+ * and their count to *n_out.  capacity must be at least 4 * n_layers.
+ * Synchronises `stream` before returning. */
 q4_status q4_decode_step_profiled(void *dec, hipStream_t stream, float *ms_out,
                                   int32_t capacity, int32_t *n_out);
+/* Average duration in microseconds of one of the four kernels of a layer
+ * (which: 0 QKV, 1 O, 2 gate+up, 3 down), launched `reps` times back to back
+ * on `stream` between two timing events, cycling through the resident
+ * layers so no launch rereads cached weights.  The O and down kernels add
+ * into h on every launch: h is clobbered.  Synchronises `stream`. */
+q4_status q4_decode_kernel_time(void *dec, int32_t which, int32_t reps,
+                                hipStream_t stream, float *avg_us);
 /* One layer, eagerly, with the weights given (e.g. a streamed slot). */
 q4_status q4_decode_layer(void *dec, const q4_layer *layer, hipStream_t stream);
 /* Frees graphs and host state.  Call after the last step has completed. */

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         "q4_unpack": (S, [_P, _P, _I64, _I64, _P]),
         "q4_gemv": (S, [_P, _P, _P, _P, _I64, _I64, _P]),
         "q4_gemm_smallbatch": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _P]),
-        "q4_gemv_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
+        "q4_gemv_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P]),
         "q4_gemm_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P]),
         "q4_decoder_workspace_bytes": (S, [ctypes.POINTER(ModelDesc),
                                            ctypes.POINTER(ctypes.c_size_t)]),
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "q4_decode_step_profiled": (S, [_P, _P, ctypes.POINTER(ctypes.c_float), _I32,
                                         ctypes.POINTER(_I32)]),
         "q4_decode_layer": (S, [_P, ctypes.POINTER(Layer), _P]),
+        "q4_decode_kernel_time": (S, [_P, _I32, _I32, _P, ctypes.POINTER(ctypes.c_float)]),
         "q4_decoder_destroy": (S, [_P]),
         "q4_layer_blob_layout": (S, [ctypes.POINTER(Layer), ctypes.c_size_t * 8,
                                      ctypes.POINTER(ctypes.c_size_t)]),
@@ -158,10 +159,12 @@ def q4_gemm_smallbatch(packed, scales, X16, Y, B=None, N=None, K=None, stream=No
                                     B, _stream(stream)))
 
 
-def q4_gemv_tuned(packed, scales, x16, y, rows_per_slot, k_split, stream=None):
+def q4_gemv_tuned(packed, scales, x16, y, rows_per_slot, k_split, chunks_in_flight=4,
+                  nontemporal=1, stream=None):
     N, K = packed.shape[0], 2 * packed.shape[1]
     _check(lib().q4_gemv_tuned(_ptr(packed), _ptr(scales), _ptr(x16), _ptr(y), N, K,
-                               rows_per_slot, k_split, _stream(stream)))
+                               rows_per_slot, k_split, chunks_in_flight, nontemporal,
+                               _stream(stream)))
 
 
 def q4_gemm_tuned(packed, scales, X16, Y, row_tiles, waves, stream=None):
@@ -236,14 +239,23 @@ class Decoder:
         _check(lib().q4_decode_step_eager(self.handle, _stream(stream)))
 
     def step_profiled(self, stream=None):
-        """Eager step; returns per-kernel durations in ms (6 per layer)."""
+        """Eager step; returns per-kernel durations in ms (4 per layer: QKV,
+        O, gate+up, down)."""
         n_layers = self._n_layers
-        cap = 6 * n_layers
+        cap = 4 * n_layers
         buf = (ctypes.c_float * cap)()
         n = _I32()
         _check(lib().q4_decode_step_profiled(self.handle, _stream(stream), buf, cap,
                                              ctypes.byref(n)))
         return list(buf[:n.value])
+
+    def kernel_time_us(self, which: int, reps: int, stream=None) -> float:
+        """Average us of kernel `which` (0 QKV, 1 O, 2 gate+up, 3 down) over
+        `reps` back-to-back launches cycling through the layers.  Clobbers h."""
+        out = ctypes.c_float()
+        _check(lib().q4_decode_kernel_time(self.handle, which, reps, _stream(stream),
+                                           ctypes.byref(out)))
+        return out.value
 
     def layer(self, weights, stream=None):
         L = weights if isinstance(weights, Layer) else make_layer(weights)

@@ -38,7 +38,7 @@ def _compile(src: str) -> str:
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr[:6000]}")
     if r.stderr.strip():
         # keep warnings visible, minus the host pass's note about the
         # device-only feature flag

@@ -25,7 +25,7 @@ namespace q4 {
 namespace {
 
 constexpr int kBuckets[4] = {512, 1024, 2048, 4096};
-constexpr int kKernelsPerLayer = 6;
+constexpr int kKernelsPerLayer = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -115,42 +115,53 @@ struct Marks {
     }
 };
 
-// Enqueue one layer on `s`: norm, QKV (+ attention-output gather), O
-// (+ residual), norm, gate+up (+ SiLU gate), down (+ residual).
-q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks marks = {}) {
+// The four kernels of a layer, in order.
+enum Kern { kQkv = 0, kO = 1, kGateUp = 2, kDown = 3 };
+
+q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int which, hipStream_t s) {
     const Dims &d = dec->dims;
     float *h = dec->desc.h;
     EpiArgs ea{};
+    switch (which) {
+    case kQkv:
+        // QKV with the first RMSNorm in its prologue; V rows also land, as
+        // binary16, in the attention output of every query head of their
+        // group.
+        ea.y = dec->qkv;
+        ea.out16 = dec->oin;
+        ea.v_off = (d.H + d.Hkv) * d.hd;
+        ea.hd = (int32_t)d.hd;
+        ea.group = (int32_t)(d.H / d.Hkv);
+        ea.eps = dec->desc.eps;
+        return launch_gemv(L.qkv.packed, L.qkv.scales, h, Pro::RmsNorm, L.qkv.N, L.qkv.K,
+                           Epi::QkvGather, ea, s);
+    case kO:
+        ea.y = h;
+        return launch_gemv(L.o.packed, L.o.scales, dec->oin, Pro::F16, L.o.N, L.o.K,
+                           Epi::Residual, ea, s);
+    case kGateUp:
+        // gate+up with the second RMSNorm in its prologue and the SiLU gate
+        // in its epilogue (rows j and dff + j meet in one 16-lane row).
+        ea.out16 = dec->mlp;
+        ea.pair_off = d.dff;
+        ea.eps = dec->desc.eps;
+        ea.norm_out = dec->a16;
+        return launch_gemv(L.gate_up.packed, L.gate_up.scales, h, Pro::RmsNorm, L.gate_up.N,
+                           L.gate_up.K, Epi::SiluPair, ea, s);
+    case kDown:
+        ea.y = h;
+        return launch_gemv(L.down.packed, L.down.scales, dec->mlp, Pro::F16, L.down.N,
+                           L.down.K, Epi::Residual, ea, s);
+    }
+    return fail(Q4_ERR_INVALID_ARG, "decoder: kernel index %d", which);
+}
 
-    Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
-    Q4_CHECK(marks.mark(s));
-    ea = EpiArgs{};
-    ea.y = dec->qkv;
-    ea.out16 = dec->oin;
-    ea.v_off = (d.H + d.Hkv) * d.hd;
-    ea.hd = (int32_t)d.hd;
-    ea.group = (int32_t)(d.H / d.Hkv);
-    Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->a16, L.qkv.N, L.qkv.K,
-                         Epi::QkvGather, ea, s));
-    Q4_CHECK(marks.mark(s));
-    ea = EpiArgs{};
-    ea.y = h;
-    Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oin, L.o.N, L.o.K, Epi::Residual, ea, s));
-    Q4_CHECK(marks.mark(s));
-
-    Q4_CHECK(launch_rmsnorm_f16(h, dec->a16, (int32_t)d.d, dec->desc.eps, s));
-    Q4_CHECK(marks.mark(s));
-    ea = EpiArgs{};
-    ea.out16 = dec->mlp;
-    ea.pair_off = d.dff;
-    Q4_CHECK(launch_gemv(L.gate_up.packed, L.gate_up.scales, dec->a16, L.gate_up.N,
-                         L.gate_up.K, Epi::SiluPair, ea, s));
-    Q4_CHECK(marks.mark(s));
-    ea = EpiArgs{};
-    ea.y = h;
-    Q4_CHECK(launch_gemv(L.down.packed, L.down.scales, dec->mlp, L.down.N, L.down.K,
-                         Epi::Residual, ea, s));
-    Q4_CHECK(marks.mark(s));
+// Enqueue one layer on `s`: four kernels.
+q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks marks = {}) {
+    for (int k = kQkv; k <= kDown; ++k) {
+        Q4_CHECK(enqueue_kernel(dec, L, k, s));
+        Q4_CHECK(marks.mark(s));
+    }
     return Q4_OK;
 }
 
@@ -210,8 +221,9 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     *dec_out = nullptr;
     q4::Dims d;
     Q4_CHECK(q4::dims_of(m, &d));
-    if (!m->h || !q4::aligned(m->h, 4))
-        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: null or misaligned h");
+    if (!m->h || !q4::aligned(m->h, 16))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_decoder_create: h null or not 16-byte aligned");
     if (!m->workspace || !q4::aligned(m->workspace, 256))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decoder_create: workspace null or not 256-byte aligned");
@@ -508,5 +520,42 @@ extern "C" q4_status q4_decode_step_profiled(void *decp, hipStream_t stream, flo
     for (hipEvent_t x : ev)
         (void)hipEventDestroy(x);
     *n_out = n;
+    return st;
+}
+
+extern "C" q4_status q4_decode_kernel_time(void *decp, int32_t which, int32_t reps,
+                                           hipStream_t stream, float *avg_us) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec || !avg_us)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_kernel_time: null argument");
+    if (dec->layers.empty())
+        return q4::fail(Q4_ERR_STATE, "q4_decode_kernel_time: decoder has no resident layers");
+    if (which < 0 || which > 3 || reps < 1)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_kernel_time: which=%d reps=%d", which,
+                        reps);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    Q4_HIP(hipEventCreate(&e0));
+    hipError_t e = hipEventCreate(&e1);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: %s", hipGetErrorString(e));
+    }
+    q4_status st = Q4_OK;
+    const size_t L = dec->layers.size();
+    if (hipEventRecord(e0, stream) != hipSuccess)
+        st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: event record failed");
+    for (int32_t i = 0; st == Q4_OK && i < reps; ++i)
+        st = q4::enqueue_kernel(dec, dec->layers[(size_t)i % L], which, stream);
+    if (st == Q4_OK && hipEventRecord(e1, stream) != hipSuccess)
+        st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: event record failed");
+    if (st == Q4_OK && (e = hipEventSynchronize(e1)) != hipSuccess)
+        st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: %s", hipGetErrorString(e));
+    float ms = 0.0f;
+    if (st == Q4_OK && (e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess)
+        st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: %s", hipGetErrorString(e));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st == Q4_OK)
+        *avg_us = ms * 1000.0f / (float)reps;
     return st;
 }

@@ -209,7 +209,8 @@ extern "C" q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *s
     if (B == 1) {
         q4::EpiArgs ea{};
         ea.y = Y;
-        return q4::launch_gemv(packed, scales, X_f16, N, K, q4::Epi::Store, ea, stream);
+        return q4::launch_gemv(packed, scales, X_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,
+                              stream);
     }
     return q4::launch_gemm_mfma(packed, scales, X_f16, Y, N, K, B, stream);
 }

@@ -61,9 +61,18 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// A loop-invariant constant held in a VGPR.  gfx9 VOP3 instructions take no
+// literal and at most one SGPR, so `(v & mask) | bias` fuses into one
+// v_and_or_b32 only when one of the two constants sits in a VGPR.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
 // One chunk (32 codes, 16 bytes) against its 32 permuted activations.
 __device__ __forceinline__ float chunk_acc(uint4 w, const uint4 (&xq)[4], float s,
-                                           float acc) {
+                                           float acc, uint32_t bias) {
     const half2_t off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
     const half2_t off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
@@ -72,10 +81,10 @@ __device__ __forceinline__ float chunk_acc(uint4 w, const uint4 (&xq)[4], float 
     for (int i = 0; i < 4; ++i) {
         const uint32_t v = wd[i];
         const uint32_t u = v >> 8;
-        half2_t a = as_h2((v & 0x000F000Fu) | 0x64006400u) - off_lo;
-        half2_t b = as_h2((v & 0x00F000F0u) | 0x64006400u) - off_hi;
-        half2_t c = as_h2((u & 0x000F000Fu) | 0x64006400u) - off_lo;
-        half2_t d = as_h2((u & 0x00F000F0u) | 0x64006400u) - off_hi;
+        half2_t a = as_h2((v & 0x000F000Fu) | bias) - off_lo;
+        half2_t b = as_h2((v & 0x00F000F0u) | bias) - off_hi;
+        half2_t c = as_h2((u & 0x000F000Fu) | bias) - off_lo;
+        half2_t d = as_h2((u & 0x00F000F0u) | bias) - off_hi;
         tlo = __builtin_amdgcn_fdot2(a, as_h2(xq[i].x), tlo, false);
         thi = __builtin_amdgcn_fdot2(b, as_h2(xq[i].y), thi, false);
         tlo = __builtin_amdgcn_fdot2(c, as_h2(xq[i].z), tlo, false);
@@ -100,37 +109,146 @@ __device__ __forceinline__ int64_t row_of(int64_t unit, int r, const EpiArgs &ea
         return unit * R + r;
 }
 
+// 8 binary16 values in natural order -> the four activation pairs in unpack
+// order: (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ uint4 permute8(uint4 v) {
+    uint4 o;
+    o.x = (v.x & 0xFFFFu) | (v.z << 16);
+    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    o.z = (v.y & 0xFFFFu) | (v.w << 16);
+    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return o;
+}
+
 // Stage x (binary16, K values) into LDS as xs[p * C + c] = the four
 // activation pairs of 8-block p of chunk c, in unpack order.
-__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x16, uint4 *xs,
-                                        int K) {
+__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x16, uint4 *xs, int K) {
     const int C = K >> 5;
-    for (int b = threadIdx.x; b < (K >> 3); b += blockDim.x) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(x16 + 8 * (size_t)b);
-        uint4 o;
-        o.x = (v.x & 0xFFFFu) | (v.z << 16);          // (x0, x4)
-        o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);      // (x1, x5)
-        o.z = (v.y & 0xFFFFu) | (v.w << 16);          // (x2, x6)
-        o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);      // (x3, x7)
-        xs[(b & 3) * C + (b >> 2)] = o;
+    for (int b = threadIdx.x; b < (K >> 3); b += kThreads)
+        xs[(b & 3) * C + (b >> 2)] = permute8(gload16(x16 + 8 * (size_t)b));
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ void load_f32x8(const float *p, float (&f)[8]) {
+    const uint4 lo = gload16(p);
+    const uint4 hi = gload16(p + 4);
+    f[0] = __uint_as_float(lo.x);
+    f[1] = __uint_as_float(lo.y);
+    f[2] = __uint_as_float(lo.z);
+    f[3] = __uint_as_float(lo.w);
+    f[4] = __uint_as_float(hi.x);
+    f[5] = __uint_as_float(hi.y);
+    f[6] = __uint_as_float(hi.z);
+    f[7] = __uint_as_float(hi.w);
+}
+
+// Stage a = f16(h / sqrt(mean(h^2) + eps)) (RMSNorm with unit gain) from the
+// fp32 residual h.  Every workgroup computes the same sum in the same order,
+// so all of them stage identical bits.  Workgroup 0 also writes `a` (natural
+// order) to norm_out when given.
+__device__ __forceinline__ void stage_rmsnorm(const float *__restrict__ h, uint4 *xs, int K,
+                                              float eps, uint16_t *norm_out, float *wsum) {
+    const int C = K >> 5;
+    float ss = 0.0f;
+    for (int b = threadIdx.x; b < (K >> 3); b += kThreads) {
+        float f[8];
+        load_f32x8(h + 8 * (size_t)b, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ss = fmaf(f[i], f[i], ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0)
+        wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = wsum[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        tot += wsum[w];
+    const float r = 1.0f / sqrtf(tot / (float)K + eps);
+    for (int b = threadIdx.x; b < (K >> 3); b += kThreads) {
+        float f[8];
+        load_f32x8(h + 8 * (size_t)b, f);
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p[i] = (uint32_t)f32_to_f16(f[2 * i] * r) |
+                   ((uint32_t)f32_to_f16(f[2 * i + 1] * r) << 16);
+        const uint4 v = {p[0], p[1], p[2], p[3]};
+        xs[(b & 3) * C + (b >> 2)] = permute8(v);
+        if (norm_out && blockIdx.x == 0)
+            *reinterpret_cast<uint4 *>(norm_out + 8 * (size_t)b) = v;
     }
 }
 
-template <int R, int KS, Epi E>
+// Weight loads: each byte is read exactly once per call, so NT marks them
+// non-temporal (streamed past the caches' retention policy).
+template <bool NT>
+__device__ __forceinline__ uint4 wload16(const void *p) {
+    if constexpr (NT) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef const __attribute__((address_space(1))) u32x4 global_t;
+        const u32x4 v = __builtin_nontemporal_load((global_t *)p);
+        return uint4{v.x, v.y, v.z, v.w};
+    } else {
+        return gload16(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ uint16_t wload2(const uint16_t *p) {
+    if constexpr (NT) {
+        typedef const __attribute__((address_space(1))) uint16_t global_t;
+        return __builtin_nontemporal_load((global_t *)p);
+    } else {
+        return gload(p);
+    }
+}
+
+// Loads of one group of U chunks of R rows; chunks past this lane's count
+// are not loaded (their registers are zeroed and never used).
+template <int U, int R, bool NT>
+__device__ __forceinline__ void load_chunks(uint4 (&w)[U][R], uint16_t (&s)[U][R],
+                                            const uint8_t *const (&wp)[R],
+                                            const uint16_t *const (&sp)[R], int first, int nl,
+                                            int cstep) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool ok = first + u < nl;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (ok) {
+                w[u][r] = wload16<NT>(wp[r] + (size_t)(first + u) * cstep * 16);
+                s[u][r] = wload2<NT>(sp[r] + (size_t)(first + u) * cstep);
+            } else {
+                w[u][r] = uint4{0u, 0u, 0u, 0u};
+                s[u][r] = 0;
+            }
+        }
+    }
+}
+
+// R rows per 16-lane row, KS waves per row's k range, U chunks of each row
+// loaded per lane before use, NT non-temporal weight loads.
+template <int R, int KS, int U, bool NT, Epi E, Pro P>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
-            const uint16_t *__restrict__ x16, int64_t N, int K, int64_t n_units,
-            EpiArgs ea) {
-    constexpr int U = (8 / R) > 1 ? (8 / R) : 1; // chunks in flight per row
+            const void *__restrict__ xin, int64_t N, int K, int64_t n_units, EpiArgs ea) {
     constexpr int kRowGroups = kWaves / KS;
     constexpr int kUnitsPerBlock = kRowGroups * kSlots;
     extern __shared__ uint4 xs[];
     __shared__ float red[kWaves][kSlots][R];
+    __shared__ float wsum[kWaves];
 
     const int C = K >> 5;
-    stage_x(x16, xs, K);
-    __syncthreads();
-
+    const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sl = lane & 15;
@@ -139,49 +257,62 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int kpart = wave % KS;
     const int64_t nblk = (n_units + kUnitsPerBlock - 1) / kUnitsPerBlock;
     const size_t row_bytes = (size_t)K >> 1;
+    // This lane's chunks: cfirst, cfirst + cstep, ... < C  (nl of them).
+    const int cstep = 16 * KS;
+    const int cfirst = kpart * 16 + sl;
+    const int nl = cfirst < C ? (C - cfirst + cstep - 1) / cstep : 0;
+    const int niter = (nl + U - 1) / U;
 
-    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
+    const uint8_t *wp[R];
+    const uint16_t *sp[R];
+    uint4 w[U][R];
+    uint16_t s[U][R];
+    auto setup_rows = [&](int64_t b) {
+        const int64_t unit = b * kUnitsPerBlock + rgroup * kSlots + slot;
         const int64_t lunit = unit < n_units ? unit : n_units - 1;
-        const uint8_t *wrow[R];
-        const uint16_t *srow[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             int64_t row = row_of<E, R>(lunit, r, ea);
             row = row < N ? row : N - 1;
-            wrow[r] = W + (size_t)row * row_bytes;
-            srow[r] = S + (size_t)row * C;
+            wp[r] = W + (size_t)row * row_bytes + (size_t)cfirst * 16;
+            sp[r] = S + (size_t)row * C + cfirst;
         }
+    };
+
+    // The first weight loads go out before the activation is staged, so
+    // their HBM latency overlaps the prologue.
+    int64_t blk = blockIdx.x;
+    if (blk < nblk) {
+        setup_rows(blk);
+        load_chunks<U, R, NT>(w, s, wp, sp, 0, nl, cstep);
+    }
+    if constexpr (P == Pro::RmsNorm)
+        stage_rmsnorm(static_cast<const float *>(xin), xs, K, ea.eps, ea.norm_out, wsum);
+    else
+        stage_x(static_cast<const uint16_t *>(xin), xs, K);
+    __syncthreads();
+
+    for (; blk < nblk; blk += gridDim.x) {
+        const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
             acc[r] = 0.0f;
 
-        const int cstep = 16 * KS;
-        for (int c0 = kpart * 16 + sl; c0 < C; c0 += cstep * U) {
-            uint4 w[U][R];
-            uint16_t s[U][R];
+        for (int it = 0; it < niter; ++it) {
+            if (it > 0)
+                load_chunks<U, R, NT>(w, s, wp, sp, it * U, nl, cstep);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * cstep;
-                const int cc = c < C ? c : c0;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    w[u][r] = *reinterpret_cast<const uint4 *>(wrow[r] + (size_t)cc * 16);
-                    s[u][r] = srow[r][cc];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * cstep;
-                if (c < C) {
+                const int j = it * U + u;
+                if (j < nl) {
                     uint4 xq[4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p)
-                        xq[p] = xs[p * C + c];
+                        xq[p] = xs[p * C + cfirst + j * cstep];
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        acc[r] = chunk_acc(w[u][r], xq, f16_to_f32(s[u][r]), acc[r]);
+                        acc[r] = chunk_acc(w[u][r], xq, f16_to_f32(s[u][r]), acc[r], bias);
                 }
             }
         }
@@ -206,6 +337,12 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                 }
             }
             __syncthreads();
+        }
+
+        // The next row block's first loads go out before this epilogue.
+        if (blk + gridDim.x < nblk) {
+            setup_rows(blk + gridDim.x);
+            load_chunks<U, R, NT>(w, s, wp, sp, 0, nl, cstep);
         }
 
         if (kpart == 0 && sl == 0 && unit < n_units) {
@@ -240,55 +377,57 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     }
 }
 
-// RMSNorm of one vector by one workgroup, fixed summation order.
-constexpr int kNormThreads = 1024;
+// ---------------------------------------------------------------- launch
+using KernelFn = void (*)(const uint8_t *, const uint16_t *, const void *, int64_t, int,
+                          int64_t, EpiArgs);
 
-__global__ void __launch_bounds__(kNormThreads)
-rmsnorm_f16_kernel(const float *__restrict__ h, uint16_t *__restrict__ a, int d, float eps) {
-    __shared__ float part[kNormThreads];
-    float ss = 0.0f;
-    for (int i = threadIdx.x; i < d; i += kNormThreads)
-        ss = fmaf(h[i], h[i], ss);
-    part[threadIdx.x] = ss;
-    __syncthreads();
-    for (int w = kNormThreads / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w)
-            part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
-    }
-    const float r = 1.0f / sqrtf(part[0] / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += kNormThreads)
-        a[i] = f32_to_f16(h[i] * r);
+// Launch shape of one product kernel.
+struct Cfg {
+    int R, KS, U;
+    bool NT;
+};
+
+template <Epi E, Pro P, int R, int KS>
+KernelFn pick_ut(const Cfg &c) {
+    if (c.U == 4)
+        return c.NT ? gemv_kernel<R, KS, 4, true, E, P> : gemv_kernel<R, KS, 4, false, E, P>;
+    if (c.U == 8)
+        return c.NT ? gemv_kernel<R, KS, 8, true, E, P> : gemv_kernel<R, KS, 8, false, E, P>;
+    return nullptr;
 }
 
-// ---------------------------------------------------------------- launch
-using KernelFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, int64_t,
-                          int, int64_t, EpiArgs);
-
-template <Epi E>
-KernelFn pick(int R, int KS) {
+template <Epi E, Pro P>
+KernelFn pick(const Cfg &c) {
 #define Q4_PICK(r, ks)                                                           \
-    if (R == r && KS == ks)                                                      \
-        return gemv_kernel<r, ks, E>;
-    Q4_PICK(1, 1) Q4_PICK(1, 2) Q4_PICK(1, 4)
-    Q4_PICK(2, 1) Q4_PICK(2, 2) Q4_PICK(2, 4)
-    Q4_PICK(4, 1) Q4_PICK(4, 2) Q4_PICK(4, 4)
+    if (c.R == r && c.KS == ks)                                                  \
+        return pick_ut<E, P, r, ks>(c);
+    if constexpr (E == Epi::SiluPair) {
+        Q4_PICK(2, 1) Q4_PICK(2, 2) Q4_PICK(2, 4)
+    } else if constexpr (E == Epi::Store) {
+        Q4_PICK(1, 1) Q4_PICK(1, 2) Q4_PICK(1, 4)
+        Q4_PICK(2, 1) Q4_PICK(2, 2) Q4_PICK(2, 4)
+        Q4_PICK(4, 1) Q4_PICK(4, 2) Q4_PICK(4, 4)
+    } else {
+        Q4_PICK(1, 2) Q4_PICK(1, 4)
+        Q4_PICK(2, 1) Q4_PICK(2, 2) Q4_PICK(2, 4)
+    }
 #undef Q4_PICK
     return nullptr;
 }
 
-KernelFn pick_kernel(Epi e, int R, int KS) {
+KernelFn pick_kernel(Epi e, Pro p, const Cfg &c) {
+    if (p == Pro::RmsNorm) {
+        switch (e) {
+        case Epi::QkvGather: return pick<Epi::QkvGather, Pro::RmsNorm>(c);
+        case Epi::SiluPair: return pick<Epi::SiluPair, Pro::RmsNorm>(c);
+        default: return nullptr;
+        }
+    }
     switch (e) {
-    case Epi::Store: return pick<Epi::Store>(R, KS);
-    case Epi::Residual: return pick<Epi::Residual>(R, KS);
-    case Epi::QkvGather: return pick<Epi::QkvGather>(R, KS);
-    case Epi::SiluPair:
-        if (R != 2)
-            return nullptr;
-        if (KS == 1) return gemv_kernel<2, 1, Epi::SiluPair>;
-        if (KS == 2) return gemv_kernel<2, 2, Epi::SiluPair>;
-        if (KS == 4) return gemv_kernel<2, 4, Epi::SiluPair>;
-        return nullptr;
+    case Epi::Store: return pick<Epi::Store, Pro::F16>(c);
+    case Epi::Residual: return pick<Epi::Residual, Pro::F16>(c);
+    case Epi::QkvGather: return pick<Epi::QkvGather, Pro::F16>(c);
+    case Epi::SiluPair: return pick<Epi::SiluPair, Pro::F16>(c);
     }
     return nullptr;
 }
@@ -312,32 +451,44 @@ int resident_blocks(KernelFn fn, size_t lds) {
     return total;
 }
 
-// Shape heuristic: enough waves to cover the chip several times over, rows
-// per slot raised only when rows are plentiful, k-split when they are not.
-void choose_config(Epi e, int64_t n_units_r1, int64_t K, int *R, int *KS) {
-    const int64_t want_waves = 8LL * device_cus();
+// Default launch shape, from rocprofv3 kernel traces of every shape on the
+// decode matrices (non-temporal loads won or tied everywhere):
+//   * two rows per 16-lane row with a 4-way k split is best or within 3% on
+//     every 4096-wide product and on the largest ones (57344 x 8192);
+//   * K = 8192 with 8192..12288 rows prefers one row per 16-lane row
+//     (10240 x 8192: 12.2 vs 14.5 us; 8192 x 8192 with 8 chunks in flight:
+//     11.0 vs 12.6 us);
+//   * K = 28672 prefers a 2-way split (27.4 vs 28.2 us).
+// The epilogue variant (paired rows) needs two rows per slot.
+Cfg choose_config(Epi e, int64_t N, int64_t K) {
     const int64_t C = K / 32;
-    if (e == Epi::SiluPair) {
-        *R = 2;
-    } else {
-        *R = 1;
+    Cfg c{2, 4, 4, true};
+    if (e != Epi::SiluPair && K >= 8192 && K < 12288 && N <= 12288) {
+        c.R = 1;
+        if (N > 8192) {
+            c.KS = 2;
+        } else {
+            c.KS = 4;
+            c.U = 8;
+        }
+    } else if (K >= 16384) {
+        c.KS = 2;
     }
-    int64_t units = (e == Epi::SiluPair) ? n_units_r1 : (n_units_r1 + *R - 1) / *R;
-    int ks = 1;
-    while (ks < 4 && (units / kSlots) * ks < want_waves && C / (16 * ks * 2) >= 2)
-        ks *= 2;
-    *KS = ks;
+    while (c.KS > 1 && C < 16 * c.KS)
+        c.KS /= 2;
+    return c;
 }
 
 } // namespace
 
-q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales,
-                          const uint16_t *x16, int64_t N, int64_t K, Epi epi,
-                          const EpiArgs &ea, int R, int KS, hipStream_t stream) {
-    KernelFn fn = pick_kernel(epi, R, KS);
+q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const void *xin,
+                          Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
+                          int KS, int U, bool NT, hipStream_t stream) {
+    Cfg cfg{R, KS, U, NT};
+    KernelFn fn = pick_kernel(epi, pro, cfg);
     if (!fn)
-        return fail(Q4_ERR_UNSUPPORTED, "gemv: no kernel for rows_per_slot=%d k_split=%d", R,
-                    KS);
+        return fail(Q4_ERR_UNSUPPORTED,
+                    "gemv: no kernel for rows_per_slot=%d k_split=%d chunks=%d", R, KS, U);
     int64_t n_units;
     if (epi == Epi::SiluPair) {
         if (ea.pair_off * 2 != N)
@@ -351,25 +502,15 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales,
     const size_t lds = (size_t)K * 2;
     const int64_t grid = std::min<int64_t>(nblk, resident_blocks(fn, lds));
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), lds, stream, packed, scales,
-                       x16, N, (int)K, n_units, ea);
+                       xin, N, (int)K, n_units, ea);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }
 
-q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const uint16_t *x16,
-                      int64_t N, int64_t K, Epi epi, const EpiArgs &ea,
-                      hipStream_t stream) {
-    int R, KS;
-    choose_config(epi, epi == Epi::SiluPair ? ea.pair_off : N, K, &R, &KS);
-    return launch_gemv_cfg(packed, scales, x16, N, K, epi, ea, R, KS, stream);
-}
-
-q4_status launch_rmsnorm_f16(const float *h, uint16_t *a, int32_t d, float eps,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(1), dim3(kNormThreads), 0, stream, h, a, d,
-                       eps);
-    Q4_HIP(hipGetLastError());
-    return Q4_OK;
+q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
+                      int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream) {
+    const Cfg c = choose_config(epi, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K);
+    return launch_gemv_cfg(packed, scales, xin, pro, N, K, epi, ea, c.R, c.KS, c.U, c.NT, stream);
 }
 
 } // namespace q4
@@ -384,12 +525,14 @@ extern "C" q4_status q4_gemv(const uint8_t *packed, const uint16_t *scales,
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemv: x must be 16-byte and y 4-byte aligned");
     q4::EpiArgs ea{};
     ea.y = y;
-    return q4::launch_gemv(packed, scales, x_f16, N, K, q4::Epi::Store, ea, stream);
+    return q4::launch_gemv(packed, scales, x_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,
+                            stream);
 }
 
 extern "C" q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales,
                                    const uint16_t *x_f16, float *y, int64_t N, int64_t K,
                                    int32_t rows_per_slot, int32_t k_split,
+                                   int32_t chunks_in_flight, int32_t nontemporal,
                                    hipStream_t stream) {
     Q4_CHECK(q4::check_matrix(packed, scales, N, K, "q4_gemv_tuned"));
     if (!x_f16 || !y)
@@ -398,11 +541,14 @@ extern "C" q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_gemv_tuned: x must be 16-byte and y 4-byte aligned");
     if (!(rows_per_slot == 1 || rows_per_slot == 2 || rows_per_slot == 4) ||
-        !(k_split == 1 || k_split == 2 || k_split == 4))
+        !(k_split == 1 || k_split == 2 || k_split == 4) ||
+        !(chunks_in_flight == 4 || chunks_in_flight == 8))
         return q4::fail(Q4_ERR_INVALID_ARG,
-                        "q4_gemv_tuned: rows_per_slot and k_split must be 1, 2 or 4");
+                        "q4_gemv_tuned: rows_per_slot and k_split must be 1, 2 or 4, "
+                        "chunks_in_flight 4 or 8");
     q4::EpiArgs ea{};
     ea.y = y;
-    return q4::launch_gemv_cfg(packed, scales, x_f16, N, K, q4::Epi::Store, ea, rows_per_slot,
-                               k_split, stream);
+    return q4::launch_gemv_cfg(packed, scales, x_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,
+                               rows_per_slot, k_split, chunks_in_flight, nontemporal != 0,
+                               stream);
 }

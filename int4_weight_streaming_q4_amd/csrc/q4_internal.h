@@ -32,6 +32,23 @@ q4_status ok();
             return s_;                                                      \
     } while (0)
 
+// Device loads through explicit global (address space 1) pointers: the
+// compiler otherwise may emit flat loads, which also count against the LDS
+// wait counter and serialise LDS reads behind outstanding HBM loads.
+template <class T>
+__device__ __forceinline__ T gload(const T *p) {
+    typedef const __attribute__((address_space(1))) T global_t;
+    return *(global_t *)(p);
+}
+
+// 16-byte variant (HIP's uint4 cannot be copied out of address space 1).
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4 global_t;
+    const u32x4 v = *(global_t *)(p);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
 inline bool aligned(const void *p, size_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
@@ -54,6 +71,12 @@ enum class Epi : int {
     SiluPair = 3, // rows (j, j + dff): out_f16[j] = f16(silu(gate) * up)
 };
 
+// How the workgroup stages its activation vector.
+enum class Pro : int {
+    F16 = 0,     // binary16 x given
+    RmsNorm = 1, // x = f16(h / sqrt(mean(h^2) + eps)) from the fp32 residual h
+};
+
 struct EpiArgs {
     float *y;          // Store / QkvGather: f32 out; Residual: h
     uint16_t *out16;   // QkvGather: o_in f16[H*hd]; SiluPair: m f16[dff]
@@ -61,21 +84,24 @@ struct EpiArgs {
     int32_t hd;        // QkvGather: head dim
     int32_t group;     // QkvGather: query heads per key/value head
     int64_t pair_off;  // SiluPair: dff
+    float eps;         // RmsNorm prologue: epsilon
+    uint16_t *norm_out;// RmsNorm prologue: workgroup 0 writes the normed f16 x here
 };
 
-// Launches the product kernel: rows of W (N x K) against the binary16
-// vector x16 (u16[K]) with the chosen epilogue.
-q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales,
-                      const uint16_t *x16, int64_t N, int64_t K, Epi epi,
-                      const EpiArgs &ea, hipStream_t stream);
+// Launches the product kernel: rows of W (N x K) against the activation
+// given by `xin` (binary16 u16[K] for Pro::F16, the fp32 residual f32[K] for
+// Pro::RmsNorm) with the chosen epilogue.  launch_gemv picks the launch
+// shape; launch_gemv_cfg takes it (R rows per 16-lane row, KS-way k split, U
+// chunks per row in flight, NT non-temporal weight loads).
+q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
+                      int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream);
+q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const void *xin,
+                          Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
+                          int KS, int U, bool NT, hipStream_t stream);
 
 // Small-batch product with matrix cores (2 <= B <= 16).
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales,
                            const uint16_t *X16, float *Y, int64_t N, int64_t K,
                            int32_t B, hipStream_t stream);
-
-// a = f16(h / sqrt(mean(h^2) + eps)) with one workgroup.
-q4_status launch_rmsnorm_f16(const float *h, uint16_t *a, int32_t d, float eps,
-                             hipStream_t stream);
 
 } // namespace q4

@@ -54,8 +54,9 @@ def test_gemv_argument_checks():
     assert L.q4_gemv(buf, buf, buf + 2, buf, 16, 64, None) == INVALID
     assert L.q4_gemv(buf, buf, buf, buf + 2, 16, 64, None) == INVALID
     assert L.q4_gemv(buf, buf, buf, 0, 16, 64, None) == INVALID
-    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 3, 1, None) == INVALID
-    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 8, None) == INVALID
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 3, 1, 4, 1, None) == INVALID
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 8, 4, 1, None) == INVALID
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 1, 6, 1, None) == INVALID
 
 
 def test_gemm_argument_checks():
@@ -101,6 +102,7 @@ def test_decoder_workspace_and_create_checks():
     assert L.q4_decoder_create(ctypes.byref(_desc(workspace_bytes=100)),
                                ctypes.byref(h)) == INVALID
     assert L.q4_decoder_create(ctypes.byref(_desc(h=0)), ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(h=4104)), ctypes.byref(h)) == INVALID
     # a layer with a wrong shape is rejected at create
     bad = q4.layer_shapes(DIMS)
     for m in (bad.qkv, bad.o, bad.gate_up, bad.down):

@@ -92,15 +92,17 @@ def test_gemv_odd_shapes(N, K):
 
 @pytest.mark.parametrize("rows_per_slot", [1, 2, 4])
 @pytest.mark.parametrize("k_split", [1, 2, 4])
-def test_gemv_every_launch_shape(rows_per_slot, k_split):
+@pytest.mark.parametrize("chunks,nt", [(4, 1), (8, 0)])
+def test_gemv_every_launch_shape(rows_per_slot, k_split, chunks, nt):
     N, K = 333, 1056  # ragged in rows and in chunks per lane
     packed, scales = _mat(N, K, 77)
     x = inputs.act_f16(K, 78, device=DEV)
     y = torch.empty(N, dtype=torch.float32, device=DEV)
-    q4.q4_gemv_tuned(packed, scales, x, y, rows_per_slot, k_split)
+    q4.q4_gemv_tuned(packed, scales, x, y, rows_per_slot, k_split, chunks, nt)
     sync()
     y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
-    assert_within(y.cpu().numpy(), y_ref, mag, f"gemv R={rows_per_slot} KS={k_split}")
+    assert_within(y.cpu().numpy(), y_ref, mag,
+                  f"gemv R={rows_per_slot} KS={k_split} U={chunks} NT={nt}")
 
 
 def _f16(v):
