@@ -12,6 +12,9 @@ dominant kernel (the gate+up product) measured with HIP events on the stream
 it runs on, and the CPU oracle timed on a bounded sample of the same work.
 
 Usage: python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-cpu-baseline]
+       python bench.py --config 3|4|5   (the other workloads, one JSON line each:
+       3 small-batch GEMM sweep on the 8B shapes, 4 Llama-3-70B-shaped resident
+       decode, 5 the same 70B weights streamed from pinned host memory)
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,6 +64,12 @@ def main():
     from int4_weight_streaming_q4_amd import inputs
 
     torch.cuda.set_device(0)
+    if args.config == 3:
+        return bench_gemm(args, q4, inputs, torch)
+    if args.config == 4:
+        return bench_70b_resident(args, q4, inputs, torch)
+    if args.config == 5:
+        return bench_70b_offload(args, q4, inputs, torch)
     dims = {k: v for k, v in inputs.MODEL_DIMS["8b"].items() if k != "n_layers"}
     n_layers = inputs.MODEL_DIMS["8b"]["n_layers"]
     CONFIG = 2
@@ -70,7 +80,7 @@ def main():
     h0 = torch.stack([inputs.residual_f32(dims["d"], inputs.seed_of(CONFIG, t, 9),
                                           device="cuda") for t in range(total_tokens)])
     h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
-    ws = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
     dec = q4.Decoder(dims, layers, h, ws)
     stream = torch.cuda.Stream()
     if args.copy_calibration:
@@ -112,6 +122,8 @@ def main():
     reps = 3 * n_layers
     names = ["qkv", "o", "gate_up", "down"]
     with torch.cuda.stream(stream):
+        for k in range(4):  # first launches load the kernels; keep them out
+            dec.kernel_time_us(k, 2, stream)
         kern_us = [dec.kernel_time_us(k, reps, stream) for k in range(4)]
     kbytes = kernel_bytes(dims)
     gu_us = kern_us[2]
@@ -169,6 +181,7 @@ def kernel_bytes(dims):
 
 
 KERNEL_SOURCES = ["int4_weight_streaming_q4_amd/csrc/q4_gemv.hip",
+                  "int4_weight_streaming_q4_amd/csrc/q4_gemv_core.h",
                   "int4_weight_streaming_q4_amd/csrc/q4_internal.h"]
 PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
 
@@ -237,6 +250,244 @@ def single_gemv(q4, inputs, torch):
     gbs = nbytes / us / 1e3
     return {"us": round(us, 3), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
             "bytes_per_launch": nbytes}
+
+
+def graph_avg_us(torch, launches, stream, reps=10):
+    """Average microseconds per launch of the callables in `launches`,
+    captured once into a graph on `stream` and replayed `reps` times."""
+    with torch.cuda.stream(stream):
+        for f in launches:
+            f(stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in launches:
+            f(stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (reps * len(launches))
+
+
+def base_result(metric, value, unit, steps, warmup, workload, extra=None):
+    r = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+         "warmup": warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+         "dtype": "int4 weights (group-32 fp16 scales), fp16 activations, fp32 accumulate",
+         "data": "synthetic (seeded random INT4 weights and N(0,1) activations)",
+         "config": {"workload": workload, "parallelism": "single GPU"}}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def bench_gemm(args, q4, inputs, torch):
+    """Small-batch product on the four 8B matrix shapes, B in {1, 4, 8, 16}:
+    distinct weight copies (> 512 MB per shape) launched round-robin inside a
+    captured graph; GB/s and effective TFLOP/s = 2NKB / t."""
+    shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096),
+              "down": (4096, 14336)}
+    stream = torch.cuda.Stream()
+    table = {}
+    for name, (N, K) in shapes.items():
+        wbytes = N * K // 2 + N * (K // 32) * 2
+        copies = max(2, -(-600_000_000 // wbytes))
+        Ws = [(inputs.random_bytes(N, K, inputs.seed_of(3, i, 0), device="cuda"),
+               inputs.scales(N, K, inputs.seed_of(3, i, 1), device="cuda"))
+              for i in range(copies)]
+        for B in (1, 4, 8, 16):
+            X = inputs.act_f16((B, K), inputs.seed_of(3, 0, 2) + B, device="cuda")
+            Y = torch.empty(B, N, dtype=torch.float32, device="cuda")
+            launches = [(lambda st, p=p, sc=sc: q4.q4_gemm_smallbatch(p, sc, X, Y, stream=st))
+                        for p, sc in Ws]
+            us = graph_avg_us(torch, launches, stream)
+            nbytes = wbytes + 2 * B * K + 4 * B * N
+            table[f"{name}_B{B}"] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                                     "TFLOP/s": round(2 * N * K * B / us / 1e6, 2)}
+        del Ws
+        torch.cuda.empty_cache()
+    top = table["gate_up_B16"]
+    res = base_result("INT4 small-batch GEMM effective TFLOP/s (8B shapes, B=1..16)",
+                      top["TFLOP/s"], "TFLOP/s", 10, 1,
+                      "speculative-verify small-batch INT4 GEMM on Llama-3-8B layer shapes; "
+                      "value = gate+up 28672x4096 at B=16",
+                      {"shapes": table,
+                       "roofline": {"bound": "hbm", "kernel": "gate+up 28672x4096, B=16",
+                                    "achieved": top["GB/s"], "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(top["GB/s"] / HBM_PEAK_GBS, 4),
+                                    "traffic": None}})
+    print(json.dumps(res), flush=True)
+
+
+def make_70b(q4, inputs, torch, device="cuda"):
+    dims = {k: v for k, v in inputs.MODEL_DIMS["70b"].items() if k != "n_layers"}
+    n_layers = inputs.MODEL_DIMS["70b"]["n_layers"]
+    return dims, n_layers
+
+
+def bench_70b_resident(args, q4, inputs, torch):
+    dims, n_layers = make_70b(q4, inputs, torch)
+    steps = args.steps if args.steps != 256 else 64
+    warmup = args.warmup if args.warmup != 8 else 4
+    layers = [inputs.layer_weights(dims, 4, l, device="cuda") for l in range(n_layers)]
+    per_layer, _ = layer_bytes(dims)
+    total = steps + warmup
+    h0 = torch.stack([inputs.residual_f32(dims["d"], inputs.seed_of(4, t, 9), device="cuda")
+                      for t in range(total)])
+    h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
+    dec = q4.Decoder(dims, layers, h, ws)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for t in range(warmup):
+            h.copy_(h0[t], non_blocking=True)
+            dec.step_graph(2048, stream)
+        stream.synchronize()
+        e0.record(stream)
+        for t in range(warmup, total):
+            h.copy_(h0[t], non_blocking=True)
+            dec.step_graph(2048, stream)
+        e1.record(stream)
+        stream.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tps = 1000.0 / ms
+    with torch.cuda.stream(stream):
+        for k in range(4):
+            dec.kernel_time_us(k, 2, stream)
+        kern_us = [dec.kernel_time_us(k, n_layers, stream) for k in range(4)]
+    kb = kernel_bytes(dims)
+    gbs = per_layer * n_layers * tps / 1e9
+    res = base_result("70B-shape batch-1 decode tokens/s (HBM-resident INT4)", round(tps, 2),
+                      "tokens/s", steps, warmup,
+                      "llama3-70b-shaped INT4 decode step, batch 1, 80 layers (38.5 GB resident), "
+                      "graph-captured, context bucket 2048",
+                      {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1000 / n_layers, 2),
+                       "hbm_gbps_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
+                       "kernels": {n: {"us": round(u, 3), "GB/s": round(b / u / 1e3, 1)}
+                                   for n, u, b in zip(["qkv", "o", "gate_up", "down"], kern_us, kb)},
+                       "roofline": {"bound": "hbm", "kernel": "gate_up 57344x8192",
+                                    "achieved": round(kb[2] / kern_us[2] / 1e3, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(kb[2] / kern_us[2] / 1e3 / HBM_PEAK_GBS, 4),
+                                    "traffic": None, "avg_launch_us": round(kern_us[2], 3)}})
+    print(json.dumps(res), flush=True)
+
+
+def bench_70b_offload(args, q4, inputs, torch):
+    """70B weights in 80 pinned host blobs (one merged blob per layer),
+    streamed through two device slots on a copy stream while the compute
+    stream runs each layer.  Reports the host->device link peak (best pinned
+    copy of one blob), achieved H2D GB/s, the overlap fraction
+    (T_copy + T_compute - T_wall) / min(T_copy, T_compute) with T_copy the
+    80 copies alone and T_compute the 80 layers alone, and tokens/s."""
+    dims, n_layers = make_70b(q4, inputs, torch)
+    steps = args.steps if args.steps != 256 else 64
+    warmup = args.warmup if args.warmup != 8 else 2
+    offs, blob_bytes = q4.layer_blob_layout(dims)
+    blobs = []
+    for l in range(n_layers):
+        L = inputs.layer_weights(dims, 4, l, device="cuda")
+        dev = torch.empty(blob_bytes, dtype=torch.uint8, device="cuda")
+        for i, name in enumerate(("qkv", "o", "gate_up", "down")):
+            p, sc = L[name]
+            pb = p.reshape(-1).view(torch.uint8)
+            sb = sc.reshape(-1).view(torch.uint8)
+            dev[offs[2 * i]:offs[2 * i] + pb.numel()].copy_(pb)
+            dev[offs[2 * i + 1]:offs[2 * i + 1] + sb.numel()].copy_(sb)
+        hb = torch.empty(blob_bytes, dtype=torch.uint8, pin_memory=True)
+        hb.copy_(dev)
+        blobs.append(hb)
+        del L, dev
+    torch.cuda.synchronize()
+    print(f"[config 5] {n_layers} pinned blobs of {blob_bytes} bytes ready", file=sys.stderr,
+          flush=True)
+    slots = [torch.empty(blob_bytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    copy_s = torch.cuda.Stream()
+    comp_s = torch.cuda.Stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    # link peak: best single pinned blob copy
+    best = 1e30
+    with torch.cuda.stream(copy_s):
+        for i in range(10):
+            e0.record(copy_s)
+            slots[i % 2].copy_(blobs[i % n_layers], non_blocking=True)
+            e1.record(copy_s)
+            copy_s.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+    link_gbs = blob_bytes / (best * 1e-3) / 1e9
+    # copies alone
+    with torch.cuda.stream(copy_s):
+        e0.record(copy_s)
+        for l in range(n_layers):
+            slots[l % 2].copy_(blobs[l], non_blocking=True)
+        e1.record(copy_s)
+        copy_s.synchronize()
+    t_copy = e0.elapsed_time(e1)
+    h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
+    dec = q4.Decoder(dims, None, h, ws, n_layers=n_layers)
+    # compute alone: the 80 layers from the two resident slots
+    slot_layers = [q4.layer_from_blob(dims, s.data_ptr()) for s in slots]
+    h.copy_(inputs.residual_f32(dims["d"], inputs.seed_of(4, 0, 9), device="cuda"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(comp_s):
+        e0.record(comp_s)
+        for l in range(n_layers):
+            dec.layer(slot_layers[l % 2], comp_s)
+        e1.record(comp_s)
+        comp_s.synchronize()
+    t_compute = e0.elapsed_time(e1)
+    print(f"[config 5] link peak {link_gbs:.1f} GB/s, copies alone {t_copy:.1f} ms, "
+          f"compute alone {t_compute:.2f} ms", file=sys.stderr, flush=True)
+    wstream = q4.WeightStream(blobs, slots, copy_s)
+    h0 = [inputs.residual_f32(dims["d"], inputs.seed_of(4, t, 9), device="cuda")
+          for t in range(steps + warmup)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(comp_s):
+        for t in range(warmup):
+            h.copy_(h0[t], non_blocking=True)
+            dec.token_streamed(wstream, comp_s)
+        comp_s.synchronize()
+        copy_s.synchronize()
+        t0 = time.perf_counter()
+        e0.record(comp_s)
+        for t in range(warmup, warmup + steps):
+            h.copy_(h0[t], non_blocking=True)
+            dec.token_streamed(wstream, comp_s)
+        e1.record(comp_s)
+        comp_s.synchronize()
+        wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    t_wall = e0.elapsed_time(e1) / steps
+    tps = 1000.0 / t_wall
+    h2d = blob_bytes * n_layers * tps / 1e9
+    overlap = (t_copy + t_compute - t_wall) / min(t_copy, t_compute)
+    res = base_result("70B-shape offload decode tokens/s (pinned host -> 2-slot HBM pool)",
+                      round(tps, 4), "tokens/s", steps, warmup,
+                      "llama3-70b-shaped INT4 decode, batch 1, 80 layers streamed per token "
+                      "from 80 pinned host blobs of 481 MB into two device slots",
+                      {"ms_per_step": round(t_wall, 3), "wall_s_timed": round(wall, 3),
+                       "h2d_gbps": round(h2d, 2), "link_peak_gbps": round(link_gbs, 2),
+                       "frac_of_link_peak": round(h2d / link_gbs, 4),
+                       "t_copy_ms": round(t_copy, 3), "t_compute_ms": round(t_compute, 3),
+                       "overlap_fraction": round(overlap, 4),
+                       "roofline": {"bound": "host-to-device link", "kernel": "H2D layer copies",
+                                    "achieved": round(h2d, 2), "peak": round(link_gbs, 2),
+                                    "unit": "GB/s", "frac": round(h2d / link_gbs, 4),
+                                    "traffic": None}})
+    wstream.close()
+    dec.close()
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(layers, dims, h0, n_tokens):

@@ -157,8 +157,9 @@ typedef struct {
     /* device, 256-byte aligned, retained.  After a layer it holds, each
      * section starting at a 256-byte boundary in this order: the binary16
      * normed input of gate+up, i.e. the second norm (max(d, dff) slots), the fp32
-     * QKV output ((H + 2*Hkv)*hd), the binary16 attention output (H*hd)
-     * and the binary16 gated MLP activation (dff). */
+     * QKV output ((H + 2*Hkv)*hd), the binary16 attention output (H*hd),
+     * the binary16 gated MLP activation (dff), 256 bytes of barrier words
+     * and the device layer table (n_layers entries of 64 bytes). */
     void *workspace;
     size_t workspace_bytes;    /* >= q4_decoder_workspace_bytes() */
 } q4_model_desc;
@@ -176,9 +177,22 @@ typedef struct {
  * and rotary position 0 is the identity.
  */
 q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out);
-/* Validates and copies the description; creates no GPU work.  Shapes must
- * match the dimensions and satisfy the q4_gemv limits. */
+/* Validates and copies the description.  Shapes must match the dimensions
+ * and satisfy the q4_gemv limits.  With resident layers it also writes, with
+ * synchronous copies, a device copy of the layer table and zeroed barrier
+ * words into the workspace; the step starts as four kernels per layer (the
+ * persistent step below is opt-in).  Without layers no GPU work. */
 q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
+/* Step implementation for resident layers: on = one persistent kernel per
+ * token (all layers, products separated by grid-wide barriers, each
+ * workgroup prefetching its next product's weights before the barrier);
+ * off = four kernels per layer.  Same arithmetic per output; cached graphs
+ * are dropped on a change.  UNSUPPORTED if the activations exceed LDS. */
+q4_status q4_decoder_set_persistent(void *dec, int32_t on);
+/* After the stream has completed a persistent step: Q4_OK, or Q4_ERR_HIP if
+ * a grid barrier gave up waiting (the step's results are then invalid; the
+ * flag is cleared).  Synchronous. */
+q4_status q4_decoder_check(void *dec);
 /* Runs all layers for one token.  ctx_len picks the context bucket: the
  * smallest of 512, 1024, 2048, 4096 that is >= ctx_len; the first call for a
  * bucket captures the layer loop into a HIP graph on `stream` (which must

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         "q4_decode_layer": (S, [_P, ctypes.POINTER(Layer), _P]),
         "q4_decode_kernel_time": (S, [_P, _I32, _I32, _P, ctypes.POINTER(ctypes.c_float)]),
         "q4_decoder_destroy": (S, [_P]),
+        "q4_decoder_set_persistent": (S, [_P, _I32]),
+        "q4_decoder_check": (S, [_P]),
         "q4_layer_blob_layout": (S, [ctypes.POINTER(Layer), ctypes.c_size_t * 8,
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "q4_layer_from_blob": (S, [ctypes.POINTER(Layer), _P, ctypes.POINTER(Layer)]),
@@ -206,8 +208,9 @@ def _model_desc(dims, n_layers, layers_arr, h, workspace, ws_bytes, eps):
                      eps, layers_arr, _ptr(h), _ptr(workspace), ws_bytes)
 
 
-def workspace_bytes(dims: dict, eps: float = 1e-5) -> int:
-    desc = _model_desc(dims, 1, None, 0, 0, 0, eps)
+def workspace_bytes(dims: dict, n_layers: int = None, eps: float = 1e-5) -> int:
+    n = n_layers if n_layers is not None else dims.get("n_layers", 1)
+    desc = _model_desc(dims, n, None, 0, 0, 0, eps)
     out = ctypes.c_size_t()
     _check(lib().q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
     return out.value
@@ -234,6 +237,13 @@ class Decoder:
 
     def step_graph(self, ctx_len: int, stream=None):
         _check(lib().decode_step_graph(self.handle, ctx_len, _stream(stream)))
+
+    def set_persistent(self, on: bool):
+        _check(lib().q4_decoder_set_persistent(self.handle, 1 if on else 0))
+
+    def check(self):
+        """Raise if a persistent step's grid barrier timed out (synchronous)."""
+        _check(lib().q4_decoder_check(self.handle))
 
     def step_eager(self, stream=None):
         _check(lib().q4_decode_step_eager(self.handle, _stream(stream)))

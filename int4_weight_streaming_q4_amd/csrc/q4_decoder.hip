@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "q4_internal.h"
+#include "q4_persistent.h"
 
 namespace q4 {
 namespace {
@@ -41,6 +42,9 @@ struct Decoder {
     float *qkv = nullptr;    // f32[nqkv]
     uint16_t *oin = nullptr; // f16[H*hd]
     uint16_t *mlp = nullptr; // f16[dff]
+    uint32_t *bar = nullptr; // grid-barrier words of the persistent kernel
+    DevLayer *dev_layers = nullptr; // device copy of the layer table
+    bool persistent = false;
     hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 
@@ -68,9 +72,9 @@ q4_status dims_of(const q4_model_desc *m, Dims *out) {
     return Q4_OK;
 }
 
-size_t workspace_bytes(const Dims &d) {
+size_t workspace_bytes(const Dims &d, int64_t n_layers) {
     return align256(std::max(d.d, d.dff) * 2) + align256(d.nqkv * 4) + align256(d.H * d.hd * 2) +
-           align256(d.dff * 2);
+           align256(d.dff * 2) + kBarBytes + align256((size_t)n_layers * sizeof(DevLayer));
 }
 
 void layer_shapes(const Dims &d, q4_layer *s) {
@@ -166,6 +170,24 @@ q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks ma
 }
 
 q4_status enqueue_all(Decoder *dec, hipStream_t s) {
+    if (dec->persistent) {
+        PersistArgs a{};
+        a.layers = dec->dev_layers;
+        a.n_layers = (int32_t)dec->layers.size();
+        a.h = dec->desc.h;
+        a.qkv = dec->qkv;
+        a.oin = dec->oin;
+        a.mlp = dec->mlp;
+        a.norm_out = dec->a16;
+        a.d = (int32_t)dec->dims.d;
+        a.H = (int32_t)dec->dims.H;
+        a.Hkv = (int32_t)dec->dims.Hkv;
+        a.hd = (int32_t)dec->dims.hd;
+        a.dff = (int32_t)dec->dims.dff;
+        a.eps = dec->desc.eps;
+        a.bar = dec->bar;
+        return launch_persistent(a, s);
+    }
     for (size_t l = 0; l < dec->layers.size(); ++l)
         Q4_CHECK(enqueue_layer(dec, dec->layers[l], s));
     return Q4_OK;
@@ -211,7 +233,7 @@ extern "C" q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *
     Q4_CHECK(q4::dims_of(m, &d));
     if (!out)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_workspace_bytes: null out");
-    *out = q4::workspace_bytes(d);
+    *out = q4::workspace_bytes(d, m->n_layers);
     return Q4_OK;
 }
 
@@ -227,9 +249,9 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     if (!m->workspace || !q4::aligned(m->workspace, 256))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decoder_create: workspace null or not 256-byte aligned");
-    if (m->workspace_bytes < q4::workspace_bytes(d))
+    if (m->workspace_bytes < q4::workspace_bytes(d, m->n_layers))
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: workspace of %zu bytes < %zu",
-                        m->workspace_bytes, q4::workspace_bytes(d));
+                        m->workspace_bytes, q4::workspace_bytes(d, m->n_layers));
     if (m->layers) {
         for (int32_t l = 0; l < m->n_layers; ++l)
             Q4_CHECK(q4::check_layer(d, m->layers[l], l));
@@ -250,6 +272,36 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     dec->oin = reinterpret_cast<uint16_t *>(ws);
     ws += q4::align256(d.H * d.hd * 2);
     dec->mlp = reinterpret_cast<uint16_t *>(ws);
+    ws += q4::align256(d.dff * 2);
+    dec->bar = reinterpret_cast<uint32_t *>(ws);
+    ws += q4::kBarBytes;
+    dec->dev_layers = reinterpret_cast<q4::DevLayer *>(ws);
+    if (m->layers) {
+        // Resident layers: the persistent kernel reads a device copy of the
+        // layer table and keeps its barrier words next to it.
+        std::vector<q4::DevLayer> table(m->n_layers);
+        for (int32_t l = 0; l < m->n_layers; ++l) {
+            const q4_matrix *mm[4] = {&m->layers[l].qkv, &m->layers[l].o, &m->layers[l].gate_up,
+                                      &m->layers[l].down};
+            for (int i = 0; i < 4; ++i) {
+                table[l].packed[i] = mm[i]->packed;
+                table[l].scales[i] = mm[i]->scales;
+            }
+        }
+        hipError_t e = hipMemset(dec->bar, 0, q4::kBarBytes);
+        if (e == hipSuccess)
+            e = hipMemcpy(dec->dev_layers, table.data(), table.size() * sizeof(q4::DevLayer),
+                          hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            delete dec;
+            return q4::fail(Q4_ERR_HIP, "q4_decoder_create: workspace setup: %s",
+                            hipGetErrorString(e));
+        }
+        // Four kernels per layer by default: on MI355X they stream the
+        // weights faster than the persistent kernel's barrier-separated
+        // phases; the persistent step is opt-in.
+        dec->persistent = false;
+    }
     *dec_out = dec;
     return Q4_OK;
 }
@@ -558,4 +610,43 @@ extern "C" q4_status q4_decode_kernel_time(void *decp, int32_t which, int32_t re
     if (st == Q4_OK)
         *avg_us = ms * 1000.0f / (float)reps;
     return st;
+}
+
+extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t on) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: null decoder");
+    if (on && dec->layers.empty())
+        return q4::fail(Q4_ERR_STATE, "q4_decoder_set_persistent: no resident layers");
+    if (on && q4::persistent_lds_bytes((int32_t)dec->dims.d, (int32_t)dec->dims.H,
+                                       (int32_t)dec->dims.hd, (int32_t)dec->dims.dff) > 65536)
+        return q4::fail(Q4_ERR_UNSUPPORTED, "q4_decoder_set_persistent: activations exceed LDS");
+    const bool want = on != 0;
+    if (want != dec->persistent) {
+        for (auto &e : dec->exec)
+            if (e) {
+                (void)hipGraphExecDestroy(e);
+                e = nullptr;
+            }
+        dec->persistent = want;
+    }
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decoder_check(void *decp) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_check: null decoder");
+    if (dec->layers.empty())
+        return Q4_OK;
+    uint32_t err = 0;
+    Q4_HIP(hipMemcpy(&err, dec->bar + q4::kBarErr, sizeof(err), hipMemcpyDeviceToHost));
+    if (err) {
+        // A barrier that gave up leaves arrival words in an unknown state:
+        // start over from zero (parity 0, no arrivals).
+        Q4_HIP(hipMemset(dec->bar, 0, q4::kBarBytes));
+        return q4::fail(Q4_ERR_HIP, "persistent decode: a grid barrier timed out; the step's "
+                                    "results are invalid");
+    }
+    return Q4_OK;
 }

@@ -47,10 +47,16 @@ __device__ __forceinline__ uint4 permute_block(uint4 v) {
     return o;
 }
 
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
 // 8 codes of one 32-bit word -> 8 scaled binary16 weights in unpack order.
-__device__ __forceinline__ half8_t dequant_word(uint32_t v, half2_t s2) {
+// `bias` (0x64006400) lives in a VGPR so each pair is one v_and_or_b32.
+__device__ __forceinline__ half8_t dequant_word(uint32_t v, half2_t s2, uint32_t bias) {
     const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const uint32_t bias = 0x64006400u;
     half2_t p0 = (as_h2((v & 0x000F000Fu) | bias) - off) * s2;
     half2_t p1 = (as_h2(((v >> 4) & 0x000F000Fu) | bias) - off) * s2;
     half2_t p2 = (as_h2(((v >> 8) & 0x000F000Fu) | bias) - off) * s2;
@@ -59,12 +65,71 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t v, half2_t s2) {
     return __builtin_bit_cast(half8_t, u);
 }
 
+__device__ __forceinline__ uint4 ntload16(const void *p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4 global_t;
+    const u32x4 v = __builtin_nontemporal_load((global_t *)p);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ uint16_t ntload2(const uint16_t *p) {
+    typedef const __attribute__((address_space(1))) uint16_t global_t;
+    return __builtin_nontemporal_load((global_t *)p);
+}
+
+// Operands of one group quad: for each row tile the lane's 16-byte group of
+// codes and its scale, and the lane's 32 activations of its batch column.
+template <int RT>
+struct Quad {
+    uint4 w[RT];
+    uint32_t s[RT]; // binary16 bits, zero-extended (keeps the struct in registers)
+    uint4 x[4];
+};
+
+template <int RT>
+__device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wrow)[RT],
+                                          const uint16_t *const (&srow)[RT],
+                                          const uint16_t *xb, int q, int kq, int C,
+                                          bool bvalid) {
+    const int g = q * 4 + kq;
+    const bool gvalid = g < C;
+    const int gc = gvalid ? g : C - 1;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        o.w[t] = ntload16(wrow[t] + (size_t)gc * 16);
+        o.s[t] = gvalid ? (uint32_t)ntload2(srow[t] + gc) : 0u;
+    }
+    const uint16_t *xp = xb + (size_t)gc * 32;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        o.x[p] = (bvalid && gvalid) ? gload16(xp + 8 * p) : uint4{0u, 0u, 0u, 0u};
+}
+
+template <int RT>
+__device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT], uint32_t bias) {
+    half8_t bop[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        bop[p] = __builtin_bit_cast(half8_t, permute_block(o.x[p]));
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)o.s[t]);
+        const half2_t s2 = {sh, sh};
+        const uint32_t wd[4] = {o.w[t].x, o.w[t].y, o.w[t].z, o.w[t].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(wd[p], s2, bias),
+                                                            bop[p], acc[t], 0, 0, 0);
+    }
+}
+
 template <int RT, int NW>
 __global__ void __launch_bounds__(64 * NW)
 gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
                  int B) {
     __shared__ float4_t red[NW][RT][64];
+    const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15;
@@ -92,36 +157,23 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     for (int t = 0; t < RT; ++t)
         acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int q = wave; q < nquads; q += NW) {
-        const int g = q * 4 + kq;
-        const bool gvalid = g < C;
-        const int gc = gvalid ? g : C - 1;
-        uint4 w[RT];
-        uint16_t s[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            w[t] = *reinterpret_cast<const uint4 *>(wrow[t] + (size_t)gc * 16);
-            s[t] = gvalid ? srow[t][gc] : (uint16_t)0;
-        }
-        half8_t bop[4];
-        {
-            const uint4 *xp = reinterpret_cast<const uint4 *>(xb + (size_t)gc * 32);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint4 v = (bvalid && gvalid) ? xp[p] : uint4{0u, 0u, 0u, 0u};
-                bop[p] = __builtin_bit_cast(half8_t, permute_block(v));
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const _Float16 sh = __builtin_bit_cast(_Float16, s[t]);
-            const half2_t s2 = {sh, sh};
-            const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(wd[p], s2), bop[p],
-                                                                acc[t], 0, 0, 0);
-        }
+    // Two register buffers: the next quad's loads are in flight while the
+    // current one is unpacked and multiplied.
+    Quad<RT> qa, qb;
+    int q = wave;
+    if (q < nquads)
+        load_quad<RT>(qa, wrow, srow, xb, q, kq, C, bvalid);
+    while (q < nquads) {
+        if (q + NW < nquads)
+            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C, bvalid);
+        mma_quad<RT>(qa, acc, bias);
+        q += NW;
+        if (q >= nquads)
+            break;
+        if (q + NW < nquads)
+            load_quad<RT>(qa, wrow, srow, xb, q + NW, kq, C, bvalid);
+        mma_quad<RT>(qb, acc, bias);
+        q += NW;
     }
 
     if constexpr (NW > 1) {

@@ -1,0 +1,593 @@
+// Device code of the INT4 product, shared by the standalone product kernel
+// (q4_gemv.hip) and the persistent decode kernel (q4_persistent.hip).
+//
+// Operation: PIPO: Pipelined Offloading for Efficient Inference on Consumer
+// Devices, "Method", bullet "Computation optimization" -- the vector is
+// multiplied directly by the 4-bit weights; no dequantized matrix is ever
+// written.  The decomposition and unpack are described in q4_gemv.hip.
+#pragma once
+
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlots = 4; // 16-lane rows per wave
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) {
+    return __builtin_bit_cast(half2_t, v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total
+// (the adds are commutative pairs, so all lanes hold the same bits).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v); // row_half_mirror
+    v += dpp_f<0x140>(v); // row_mirror
+    return v;
+}
+
+// A loop-invariant constant held in a VGPR.  gfx9 VOP3 instructions take no
+// literal and at most one SGPR, so `(v & mask) | bias` fuses into one
+// v_and_or_b32 only when one of the two constants sits in a VGPR.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
+// One chunk (32 codes, 16 bytes) against its 32 permuted activations.
+__device__ __forceinline__ float chunk_acc(uint4 w, const uint4 (&xq)[4], float s,
+                                           float acc, uint32_t bias) {
+    const half2_t off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    float tlo = 0.0f, thi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t v = wd[i];
+        const uint32_t u = v >> 8;
+        half2_t a = as_h2((v & 0x000F000Fu) | bias) - off_lo;
+        half2_t b = as_h2((v & 0x00F000F0u) | bias) - off_hi;
+        half2_t c = as_h2((u & 0x000F000Fu) | bias) - off_lo;
+        half2_t d = as_h2((u & 0x00F000F0u) | bias) - off_hi;
+        tlo = __builtin_amdgcn_fdot2(a, as_h2(xq[i].x), tlo, false);
+        thi = __builtin_amdgcn_fdot2(b, as_h2(xq[i].y), thi, false);
+        tlo = __builtin_amdgcn_fdot2(c, as_h2(xq[i].z), tlo, false);
+        thi = __builtin_amdgcn_fdot2(d, as_h2(xq[i].w), thi, false);
+    }
+    return fmaf(s, fmaf(thi, 0.0625f, tlo), acc);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <Epi E, int R>
+__device__ __forceinline__ int64_t row_of(int64_t unit, int r, const EpiArgs &ea) {
+    if constexpr (E == Epi::SiluPair)
+        return unit + r * ea.pair_off;
+    else
+        return unit * R + r;
+}
+
+// Activation accesses.  COH = false: ordinary loads and stores (one kernel
+// per product; the kernel boundary publishes the data).  COH = true: the
+// persistent kernel, where workgroups on different XCDs exchange the small
+// activation vectors inside one launch: every store of such a vector is an
+// agent-scope atomic store (written through to the coherence point), and
+// after each grid barrier a workgroup invalidates its caches once (an
+// agent-scope acquire), so the ordinary cached loads below see every
+// workgroup's writes while each XCD still fetches a vector only once.
+template <bool COH>
+__device__ __forceinline__ uint4 act_load16(const void *p) {
+    return gload16(p);
+}
+
+template <bool COH>
+__device__ __forceinline__ void act_store16(void *p, uint4 v) {
+    if constexpr (COH) {
+        uint64_t *q = static_cast<uint64_t *>(p);
+        __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *static_cast<uint4 *>(p) = v;
+    }
+}
+
+template <bool COH>
+__device__ __forceinline__ float act_load_f32(const float *p) {
+    return gload(p);
+}
+
+template <bool COH>
+__device__ __forceinline__ void act_store_f32(float *p, float v) {
+    if constexpr (COH)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+template <bool COH>
+__device__ __forceinline__ void act_store_u16(uint16_t *p, uint16_t v) {
+    if constexpr (COH)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+// 8 binary16 values in natural order -> the four activation pairs in unpack
+// order: (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ uint4 permute8(uint4 v) {
+    uint4 o;
+    o.x = (v.x & 0xFFFFu) | (v.z << 16);
+    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    o.z = (v.y & 0xFFFFu) | (v.w << 16);
+    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return o;
+}
+
+// Stage x (binary16, K values) into LDS as xs[p * C + c] = the four
+// activation pairs of 8-block p of chunk c, in unpack order.
+template <bool COH>
+__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x16, uint4 *xs, int K) {
+    const int C = K >> 5;
+    for (int b = threadIdx.x; b < (K >> 3); b += kThreads)
+        xs[(b & 3) * C + (b >> 2)] = permute8(act_load16<COH>(x16 + 8 * (size_t)b));
+}
+
+__device__ __forceinline__ float eps_of(const EpiArgs &ea) { return ea.eps; }
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <bool COH>
+__device__ __forceinline__ void load_f32x8(const float *p, float (&f)[8]) {
+    const uint4 lo = act_load16<COH>(p);
+    const uint4 hi = act_load16<COH>(p + 4);
+    f[0] = __uint_as_float(lo.x);
+    f[1] = __uint_as_float(lo.y);
+    f[2] = __uint_as_float(lo.z);
+    f[3] = __uint_as_float(lo.w);
+    f[4] = __uint_as_float(hi.x);
+    f[5] = __uint_as_float(hi.y);
+    f[6] = __uint_as_float(hi.z);
+    f[7] = __uint_as_float(hi.w);
+}
+
+// Stage a = f16(h / sqrt(mean(h^2) + eps)) (RMSNorm with unit gain) from the
+// fp32 residual h.  Every workgroup computes the same sum in the same order,
+// so all of them stage identical bits.  Workgroup 0 also writes `a` (natural
+// order) to norm_out when given.
+template <bool COH>
+__device__ __forceinline__ void stage_rmsnorm(const float *__restrict__ h, uint4 *xs, int K,
+                                              float eps, uint16_t *norm_out, float *wsum) {
+    // Up to kKeep 8-value blocks per thread stay in registers between the
+    // sum of squares and the scaling (K <= 8192 with 256 threads); larger K
+    // rereads the rest.
+    constexpr int kKeep = 4;
+    const int C = K >> 5;
+    const int nb8 = K >> 3;
+    float keep[kKeep][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) {
+        const int b = threadIdx.x + j * kThreads;
+        if (b < nb8) {
+            load_f32x8<COH>(h + 8 * (size_t)b, keep[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ss = fmaf(keep[j][i], keep[j][i], ss);
+        }
+    }
+    for (int b = threadIdx.x + kKeep * kThreads; b < nb8; b += kThreads) {
+        float f[8];
+        load_f32x8<COH>(h + 8 * (size_t)b, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ss = fmaf(f[i], f[i], ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0)
+        wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = wsum[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        tot += wsum[w];
+    const float r = 1.0f / sqrtf(tot / (float)K + eps);
+    auto emit = [&](int b, const float (&f)[8]) {
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p[i] = (uint32_t)f32_to_f16(f[2 * i] * r) |
+                   ((uint32_t)f32_to_f16(f[2 * i + 1] * r) << 16);
+        const uint4 v = {p[0], p[1], p[2], p[3]};
+        xs[(b & 3) * C + (b >> 2)] = permute8(v);
+        if (norm_out && blockIdx.x == 0)
+            act_store16<COH>(norm_out + 8 * (size_t)b, v);
+    };
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) {
+        const int b = threadIdx.x + j * kThreads;
+        if (b < nb8)
+            emit(b, keep[j]);
+    }
+    for (int b = threadIdx.x + kKeep * kThreads; b < nb8; b += kThreads) {
+        float f[8];
+        load_f32x8<COH>(h + 8 * (size_t)b, f);
+        emit(b, f);
+    }
+}
+
+// Two-step staging.  Loads of one wave return in issue order, so activation
+// loads issued after a batch of weight loads would wait for that batch: the
+// activation is therefore loaded first (stage_issue, up to kXR 16-byte
+// values per thread held in registers), the weight prefetch goes out next,
+// and stage_finish then reduces, normalises, permutes and writes LDS.
+constexpr int kXR = 8;
+
+struct XStage {
+    uint4 v[kXR];
+};
+
+template <Pro P, bool COH>
+__device__ __forceinline__ void stage_issue(const void *xin, int K, XStage &st) {
+    if constexpr (P == Pro::F16) {
+        const uint16_t *x16 = static_cast<const uint16_t *>(xin);
+        const int nb = K >> 3;
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            const int b = threadIdx.x + j * kThreads;
+            st.v[j] = b < nb ? act_load16<COH>(x16 + 8 * (size_t)b) : uint4{0u, 0u, 0u, 0u};
+        }
+    } else {
+        const float *h = static_cast<const float *>(xin);
+        const int nb8 = K >> 3;
+#pragma unroll
+        for (int j = 0; j < kXR / 2; ++j) {
+            const int b = threadIdx.x + j * kThreads;
+            if (b < nb8) {
+                st.v[2 * j] = act_load16<COH>(h + 8 * (size_t)b);
+                st.v[2 * j + 1] = act_load16<COH>(h + 8 * (size_t)b + 4);
+            } else {
+                st.v[2 * j] = st.v[2 * j + 1] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void unpack_f32x8(const uint4 &lo, const uint4 &hi, float (&f)[8]) {
+    f[0] = __uint_as_float(lo.x);
+    f[1] = __uint_as_float(lo.y);
+    f[2] = __uint_as_float(lo.z);
+    f[3] = __uint_as_float(lo.w);
+    f[4] = __uint_as_float(hi.x);
+    f[5] = __uint_as_float(hi.y);
+    f[6] = __uint_as_float(hi.z);
+    f[7] = __uint_as_float(hi.w);
+}
+
+template <Pro P, bool COH>
+__device__ __forceinline__ void stage_finish(const void *xin, uint4 *xs, int K, const EpiArgs &ea,
+                                             float *wsum, const XStage &st) {
+    const int C = K >> 5;
+    if constexpr (P == Pro::F16) {
+        const uint16_t *x16 = static_cast<const uint16_t *>(xin);
+        const int nb = K >> 3;
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+            const int b = threadIdx.x + j * kThreads;
+            if (b < nb)
+                xs[(b & 3) * C + (b >> 2)] = permute8(st.v[j]);
+        }
+        for (int b = threadIdx.x + kXR * kThreads; b < nb; b += kThreads)
+            xs[(b & 3) * C + (b >> 2)] = permute8(act_load16<COH>(x16 + 8 * (size_t)b));
+    } else {
+        // a = f16(h / sqrt(mean(h^2) + eps)), unit gain; every workgroup sums
+        // in the same order, so all stage identical bits.
+        const float *h = static_cast<const float *>(xin);
+        const int nb8 = K >> 3;
+        constexpr int kKeep = kXR / 2;
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) {
+            float f[8];
+            unpack_f32x8(st.v[2 * j], st.v[2 * j + 1], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ss = fmaf(f[i], f[i], ss);
+        }
+        for (int b = threadIdx.x + kKeep * kThreads; b < nb8; b += kThreads) {
+            float f[8];
+            load_f32x8<COH>(h + 8 * (size_t)b, f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ss = fmaf(f[i], f[i], ss);
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0)
+            wsum[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        float tot = wsum[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            tot += wsum[w];
+        const float r = 1.0f / sqrtf(tot / (float)K + eps_of(ea));
+        auto emit = [&](int b, const float (&f)[8]) {
+            uint32_t p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p[i] = (uint32_t)f32_to_f16(f[2 * i] * r) |
+                       ((uint32_t)f32_to_f16(f[2 * i + 1] * r) << 16);
+            const uint4 v = {p[0], p[1], p[2], p[3]};
+            xs[(b & 3) * C + (b >> 2)] = permute8(v);
+            if (ea.norm_out && blockIdx.x == 0)
+                act_store16<COH>(ea.norm_out + 8 * (size_t)b, v);
+        };
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) {
+            const int b = threadIdx.x + j * kThreads;
+            if (b < nb8) {
+                float f[8];
+                unpack_f32x8(st.v[2 * j], st.v[2 * j + 1], f);
+                emit(b, f);
+            }
+        }
+        for (int b = threadIdx.x + kKeep * kThreads; b < nb8; b += kThreads) {
+            float f[8];
+            load_f32x8<COH>(h + 8 * (size_t)b, f);
+            emit(b, f);
+        }
+    }
+}
+
+// Weight loads: each byte is read exactly once per call, so NT marks them
+// non-temporal (streamed past the caches' retention policy).
+template <bool NT>
+__device__ __forceinline__ uint4 wload16(const void *p) {
+    if constexpr (NT) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef const __attribute__((address_space(1))) u32x4 global_t;
+        const u32x4 v = __builtin_nontemporal_load((global_t *)p);
+        return uint4{v.x, v.y, v.z, v.w};
+    } else {
+        return gload16(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ uint16_t wload2(const uint16_t *p) {
+    if constexpr (NT) {
+        typedef const __attribute__((address_space(1))) uint16_t global_t;
+        return __builtin_nontemporal_load((global_t *)p);
+    } else {
+        return gload(p);
+    }
+}
+
+// Loads of one group of U chunks of R rows; chunks past this lane's count
+// are not loaded (their registers are zeroed and never used).
+template <int U, int R, bool NT>
+__device__ __forceinline__ void load_chunks(uint4 (&w)[U][R], uint16_t (&s)[U][R],
+                                            const uint8_t *const (&wp)[R],
+                                            const uint16_t *const (&sp)[R], int first, int nl,
+                                            int cstep) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool ok = first + u < nl;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (ok) {
+                w[u][r] = wload16<NT>(wp[r] + (size_t)(first + u) * cstep * 16);
+                s[u][r] = wload2<NT>(sp[r] + (size_t)(first + u) * cstep);
+            } else {
+                w[u][r] = uint4{0u, 0u, 0u, 0u};
+                s[u][r] = 0;
+            }
+        }
+    }
+}
+
+template <Epi E, int R, int KS>
+struct Geometry {
+    static constexpr int kRowGroups = kWaves / KS;
+    static constexpr int kUnitsPerBlock = kRowGroups * kSlots;
+};
+
+// Points wp/sp at this lane's first chunk of the R rows of row block `blk`.
+template <int R, int KS, Epi E>
+__device__ __forceinline__ void setup_rows(const uint8_t *W, const uint16_t *S, int64_t N, int C,
+                                           int64_t n_units, const EpiArgs &ea, int64_t blk,
+                                           const uint8_t *(&wp)[R], const uint16_t *(&sp)[R]) {
+    constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slot = lane >> 4;
+    const int rgroup = wave / KS;
+    const int cfirst = (wave % KS) * 16 + (lane & 15);
+    const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
+    const int64_t lunit = unit < n_units ? unit : n_units - 1;
+    const size_t row_bytes = (size_t)(C * 16);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t row = row_of<E, R>(lunit, r, ea);
+        row = row < N ? row : N - 1;
+        wp[r] = W + (size_t)row * row_bytes + (size_t)cfirst * 16;
+        sp[r] = S + (size_t)row * C + cfirst;
+    }
+}
+
+// Number of row blocks of a product and this lane's chunk count.
+template <int R, int KS, Epi E>
+__device__ __forceinline__ int64_t row_blocks(int64_t n_units) {
+    constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
+    return (n_units + kUnitsPerBlock - 1) / kUnitsPerBlock;
+}
+
+template <int KS>
+__device__ __forceinline__ int lane_chunks(int C) {
+    const int cstep = 16 * KS;
+    const int cfirst = ((threadIdx.x >> 6) % KS) * 16 + (threadIdx.x & 15);
+    return cfirst < C ? (C - cfirst + cstep - 1) / cstep : 0;
+}
+
+// Issues the first chunk loads of row block `blk` (if it exists).
+template <int R, int KS, int U, bool NT, Epi E>
+__device__ __forceinline__ void prefetch_block(const uint8_t *W, const uint16_t *S, int64_t N,
+                                               int K, int64_t n_units, const EpiArgs &ea,
+                                               int64_t blk, uint4 (&w)[U][R],
+                                               uint16_t (&s)[U][R], const uint8_t *(&wp)[R],
+                                               const uint16_t *(&sp)[R]) {
+    const int C = K >> 5;
+    if (blk < row_blocks<R, KS, E>(n_units)) {
+        setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk, wp, sp);
+        load_chunks<U, R, NT>(w, s, wp, sp, 0, lane_chunks<KS>(C), 16 * KS);
+    }
+}
+
+// Processes row blocks blk, blk + stride, ... of one product with the
+// activation already staged in LDS.  Precondition: the first chunk loads of
+// `blk` are in w/s (prefetch_block).  Every thread of the workgroup must
+// call this (the k-split reduction synchronises the workgroup).
+template <int R, int KS, int U, bool NT, Epi E, bool COH = false>
+__device__ __forceinline__ void run_units(const uint8_t *W, const uint16_t *S, int64_t N, int K,
+                                          int64_t n_units, const EpiArgs &ea, int64_t blk,
+                                          int64_t stride, const uint4 *xs,
+                                          float (*red)[kSlots][R], uint4 (&w)[U][R],
+                                          uint16_t (&s)[U][R], const uint8_t *(&wp)[R],
+                                          const uint16_t *(&sp)[R], uint32_t bias) {
+    constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
+    const int C = K >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sl = lane & 15;
+    const int slot = lane >> 4;
+    const int rgroup = wave / KS;
+    const int kpart = wave % KS;
+    const int64_t nblk = row_blocks<R, KS, E>(n_units);
+    const int cstep = 16 * KS;
+    const int cfirst = kpart * 16 + sl;
+    const int nl = lane_chunks<KS>(C);
+    const int niter = (nl + U - 1) / U;
+
+    for (; blk < nblk; blk += stride) {
+        const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = 0.0f;
+
+        for (int it = 0; it < niter; ++it) {
+            if (it > 0)
+                load_chunks<U, R, NT>(w, s, wp, sp, it * U, nl, cstep);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = it * U + u;
+                if (j < nl) {
+                    uint4 xq[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        xq[p] = xs[p * C + cfirst + j * cstep];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r] = chunk_acc(w[u][r], xq, f16_to_f32(s[u][r]), acc[r], bias);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = row16_sum(acc[r]);
+
+        if constexpr (KS > 1) {
+            if (sl == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    red[wave][slot][r] = acc[r];
+            }
+            __syncthreads();
+            if (kpart == 0 && sl == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float t = red[wave][slot][r];
+                    for (int k = 1; k < KS; ++k)
+                        t += red[wave + k][slot][r];
+                    acc[r] = t;
+                }
+            }
+            __syncthreads();
+        }
+
+        // The next row block's first loads go out before this epilogue.
+        if (blk + stride < nblk) {
+            setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk + stride, wp, sp);
+            load_chunks<U, R, NT>(w, s, wp, sp, 0, nl, cstep);
+        }
+
+        if (kpart == 0 && sl == 0 && unit < n_units) {
+            if constexpr (E == Epi::SiluPair) {
+                static_assert(R == 2, "paired rows need two rows per slot");
+                const float g = acc[0], up = acc[1];
+                const float silu = g / (1.0f + expf(-g));
+                act_store_u16<COH>(ea.out16 + unit, f32_to_f16(silu * up));
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t row = unit * R + r;
+                    if (row < N) {
+                        if constexpr (E == Epi::Residual) {
+                            act_store_f32<COH>(ea.y + row, act_load_f32<COH>(ea.y + row) + acc[r]);
+                        } else {
+                            act_store_f32<COH>(ea.y + row, acc[r]);
+                            if constexpr (E == Epi::QkvGather) {
+                                if (row >= ea.v_off) {
+                                    const int64_t v = row - ea.v_off;
+                                    const int64_t g = v / ea.hd, i = v % ea.hd;
+                                    const uint16_t h16 = f32_to_f16(acc[r]);
+                                    for (int q = 0; q < ea.group; ++q)
+                                        act_store_u16<COH>(
+                                            ea.out16 + (g * ea.group + q) * ea.hd + i, h16);
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Stages the activation of a product into LDS.
+template <Pro P, bool COH = false>
+__device__ __forceinline__ void stage_activation(const void *xin, uint4 *xs, int K,
+                                                 const EpiArgs &ea, float *wsum) {
+    if constexpr (P == Pro::RmsNorm)
+        stage_rmsnorm<COH>(static_cast<const float *>(xin), xs, K, ea.eps, ea.norm_out, wsum);
+    else
+        stage_x<COH>(static_cast<const uint16_t *>(xin), xs, K);
+}
+
+} // namespace
+} // namespace q4

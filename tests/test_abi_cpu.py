@@ -92,9 +92,10 @@ def test_decoder_workspace_and_create_checks():
     out = ctypes.c_size_t()
     assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(out)) == 0
     # a16 f16[max(d, dff)], qkv f32[(H+2Hkv)hd], o_in f16[H hd], mlp f16[dff],
-    # each rounded up to 256 bytes
-    assert out.value == 256 + 512 + 256 + 256
-    assert q4.workspace_bytes(DIMS) == out.value
+    # barrier area (64 + 4096 + 1 words, rounded up: 16896 bytes), device layer
+    # table (2 x 64 bytes), each rounded up to 256
+    assert out.value == 256 + 512 + 256 + 256 + 16896 + 256
+    assert q4.workspace_bytes(DIMS, n_layers=2) == out.value
     h = ctypes.c_void_p()
     assert L.q4_decoder_create(ctypes.byref(_desc(n_heads=3)), ctypes.byref(h)) == INVALID
     assert L.q4_decoder_create(ctypes.byref(_desc(d_model=48)), ctypes.byref(h)) == INVALID

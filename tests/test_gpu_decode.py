@@ -60,7 +60,8 @@ class Model:
     def __init__(self, dims, layers, resident=True):
         self.dims = dims
         self.h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
-        self.ws = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+        self.ws = torch.zeros(q4.workspace_bytes(dims, n_layers=len(layers)), dtype=torch.uint8,
+                              device=DEV)
         self.dec = q4.Decoder(dims, layers if resident else None, self.h, self.ws, EPS,
                               n_layers=len(layers))
 
@@ -111,11 +112,13 @@ def test_tiny_eager_layers_match_oracle():
                 assert np.all(np.abs(got - V[idx]) <= 2e-3 * Vm[idx] + 1e-6 + ulp)
 
 
-def test_tiny_graph_equals_eager_all_buckets():
+@pytest.mark.parametrize("persistent", [True, False])
+def test_tiny_graph_equals_eager_all_buckets(persistent):
     n = 3
     layers = make_layers(TINY, 91, n)
     h0 = inputs.residual_f32(TINY["d"], inputs.seed_of(91, 0, 9))
     m = Model(TINY, layers)
+    m.dec.set_persistent(persistent)
     s = torch.cuda.Stream()
     m.set_h(h0)
     torch.cuda.synchronize()
@@ -132,19 +135,22 @@ def test_tiny_graph_equals_eager_all_buckets():
             m.dec.step_graph(ctx, s)
             s.synchronize()
             assert torch.equal(m.h.cpu(), h_eager), (ctx, rep)
+    m.dec.check()
     with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
         m.dec.step_graph(4097, s)
     with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
         m.dec.step_graph(0, s)
 
 
-def test_tiny_token_loop_graph_replays():
+@pytest.mark.parametrize("persistent", [True, False])
+def test_tiny_token_loop_graph_replays(persistent):
     """Several tokens through one captured graph, fed a new residual each
     token, equal to the oracle token by token."""
     n = 4
     layers = make_layers(TINY, 92, n)
     host = to_host(layers)
     m = Model(TINY, layers)
+    m.dec.set_persistent(persistent)
     s = torch.cuda.Stream()
     for t in range(4):
         h0 = inputs.residual_f32(TINY["d"], inputs.seed_of(92, t, 9))
@@ -154,6 +160,7 @@ def test_tiny_token_loop_graph_replays():
         s.synchronize()
         ref = oracle_run(host, TINY, h0.numpy())
         check_h(m.h.cpu().numpy(), ref[-1][0], ref[-1][1], f"tiny token {t}")
+    m.dec.check()
 
 
 def _big(dims_name, config, n_layers):
@@ -163,7 +170,9 @@ def _big(dims_name, config, n_layers):
 
 
 def test_8b_full_step_graph_matches_oracle():
-    """Llama-3-8B shapes, all 32 layers, graph-captured, token 0."""
+    """Llama-3-8B shapes, all 32 layers, graph-captured (four kernels per
+    layer, the default step), token 0; the persistent kernel uses the same
+    per-output arithmetic on these matrices, so it must agree bitwise."""
     dims, layers = _big("8b", 2, 32)
     h0 = inputs.residual_f32(dims["d"], inputs.seed_of(2, 0, 9))
     m = Model(dims, layers)
@@ -172,12 +181,21 @@ def test_8b_full_step_graph_matches_oracle():
     torch.cuda.synchronize()
     m.dec.step_graph(512, s)
     s.synchronize()
+    m.dec.check()
     h_graph = m.h.cpu().clone()
     m.set_h(h0)
     torch.cuda.synchronize()
     m.dec.step_eager(s)
     s.synchronize()
     assert torch.equal(m.h.cpu(), h_graph), "graph and eager differ"
+    m.dec.set_persistent(True)
+    for step in (lambda: m.dec.step_eager(s), lambda: m.dec.step_graph(512, s)):
+        m.set_h(h0)
+        torch.cuda.synchronize()
+        step()
+        s.synchronize()
+        m.dec.check()
+        assert torch.equal(m.h.cpu(), h_graph), "persistent kernel differs from per-layer"
     host = to_host(layers)
     del layers
     ref = oracle_run(host, dims, h0.numpy())
@@ -186,28 +204,40 @@ def test_8b_full_step_graph_matches_oracle():
 
 
 def test_70b_first_layers_and_full_graph():
-    """Llama-3-70B shapes: layers 0-1 against the oracle, then the full
-    80-layer model (about 38.5 GB resident) graph == eager, finite."""
+    """Llama-3-70B shapes: layers 0-1 against the oracle through both step
+    implementations, then the full 80-layer model (about 38.5 GB resident):
+    graph == eager, finite, persistent within the bound of the per-layer
+    kernels' result."""
     dims = {k: v for k, v in inputs.MODEL_DIMS["70b"].items() if k != "n_layers"}
     layers = make_layers(dims, 4, 80)
     h0 = inputs.residual_f32(dims["d"], inputs.seed_of(4, 0, 9))
-    m = Model(dims, layers)
     s = torch.cuda.Stream()
-    # two layers eagerly, checked by the oracle
+    host2 = to_host(layers[:2])
+    ref = oracle_run(host2, dims, h0.numpy())
+    # two layers, eagerly per layer
     m2 = Model(dims, layers[:2], resident=False)
     m2.set_h(h0)
     torch.cuda.synchronize()
     for l in range(2):
         m2.dec.layer(layers[l], s)
     s.synchronize()
-    host2 = to_host(layers[:2])
-    ref = oracle_run(host2, dims, h0.numpy())
-    check_h(m2.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1")
+    check_h(m2.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1 per-layer kernels")
+    # the same two layers through the persistent kernel
+    m3 = Model(dims, layers[:2])
+    m3.dec.set_persistent(True)
+    m3.set_h(h0)
+    torch.cuda.synchronize()
+    m3.dec.step_eager(s)
+    s.synchronize()
+    m3.dec.check()
+    check_h(m3.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1 persistent")
     # full model
+    m = Model(dims, layers)
     m.set_h(h0)
     torch.cuda.synchronize()
     m.dec.step_graph(2048, s)
     s.synchronize()
+    m.dec.check()
     h_graph = m.h.cpu().clone()
     assert torch.isfinite(h_graph).all()
     m.set_h(h0)

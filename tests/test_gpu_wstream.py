@@ -40,7 +40,8 @@ def blobs_for(dims, layers):
 
 def resident_tokens(dims, layers, h0s):
     h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
-    ws = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers=len(layers)), dtype=torch.uint8,
+                     device=DEV)
     dec = q4.Decoder(dims, layers, h, ws, EPS)
     s = torch.cuda.Stream()
     outs = []
@@ -63,7 +64,8 @@ class Streamed:
         self.compute = torch.cuda.Stream()
         self.ws = q4.WeightStream(self.blobs, self.slots, self.copy)
         self.h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
-        self.wsp = torch.zeros(q4.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+        self.wsp = torch.zeros(q4.workspace_bytes(dims, n_layers=len(layers)), dtype=torch.uint8,
+                               device=DEV)
         self.dec = q4.Decoder(dims, None, self.h, self.wsp, EPS, n_layers=len(layers))
         self.n = len(layers)
 
