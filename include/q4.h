@@ -221,6 +221,14 @@ q4_status q4_decode_kernel_time(void *dec, int32_t which, int32_t reps,
                                 hipStream_t stream, float *avg_us);
 /* One layer, eagerly, with the weights given (e.g. a streamed slot). */
 q4_status q4_decode_layer(void *dec, const q4_layer *layer, hipStream_t stream);
+/* One product of a layer, eagerly: which = 0 QKV (RMSNorm of h, V gather
+ * into the attention output), 1 O (h += ...), 2 gate+up (RMSNorm of h, its
+ * binary16 result kept in the workspace, SiLU gate into the MLP activation),
+ * 3 down (h += ...).  Calling 0..3 in order equals q4_decode_layer; single
+ * products let a caller inspect every intermediate (the workspace sections
+ * listed above).  INVALID_ARG for another index or bad shapes. */
+q4_status q4_decode_layer_part(void *dec, const q4_layer *layer, int32_t which,
+                               hipStream_t stream);
 /* Frees graphs and host state.  Call after the last step has completed. */
 q4_status q4_decoder_destroy(void *dec);
 

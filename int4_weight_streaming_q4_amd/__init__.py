@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "q4_decode_step_profiled": (S, [_P, _P, ctypes.POINTER(ctypes.c_float), _I32,
                                         ctypes.POINTER(_I32)]),
         "q4_decode_layer": (S, [_P, ctypes.POINTER(Layer), _P]),
+        "q4_decode_layer_part": (S, [_P, ctypes.POINTER(Layer), _I32, _P]),
         "q4_decode_kernel_time": (S, [_P, _I32, _I32, _P, ctypes.POINTER(ctypes.c_float)]),
         "q4_decoder_destroy": (S, [_P]),
         "q4_decoder_set_persistent": (S, [_P, _I32]),
@@ -270,6 +271,12 @@ class Decoder:
     def layer(self, weights, stream=None):
         L = weights if isinstance(weights, Layer) else make_layer(weights)
         _check(lib().q4_decode_layer(self.handle, ctypes.byref(L), _stream(stream)))
+
+    def layer_part(self, weights, which: int, stream=None):
+        """One product of a layer: 0 QKV, 1 O, 2 gate+up, 3 down."""
+        L = weights if isinstance(weights, Layer) else make_layer(weights)
+        _check(lib().q4_decode_layer_part(self.handle, ctypes.byref(L), int(which),
+                                          _stream(stream)))
 
     def token_streamed(self, ws: "WeightStream", stream=None):
         _check(lib().q4_decode_token_streamed(self.handle, ws.handle, _stream(stream)))

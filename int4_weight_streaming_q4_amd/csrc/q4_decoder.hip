@@ -364,6 +364,17 @@ extern "C" q4_status q4_decode_layer(void *decp, const q4_layer *layer, hipStrea
     return q4::enqueue_layer(dec, *layer, stream);
 }
 
+extern "C" q4_status q4_decode_layer_part(void *decp, const q4_layer *layer, int32_t which,
+                                          hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec || !layer)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer_part: null decoder or layer");
+    if (which < q4::kQkv || which > q4::kDown)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer_part: product index %d", which);
+    Q4_CHECK(q4::check_layer(dec->dims, *layer, -1));
+    return q4::enqueue_kernel(dec, *layer, which, stream);
+}
+
 extern "C" q4_status q4_decoder_destroy(void *decp) {
     Decoder *dec = static_cast<Decoder *>(decp);
     if (!dec)

@@ -50,7 +50,9 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     uint4 w[U][R];
     uint16_t s[U][R];
     // Activation loads first, then the first weight loads, then the rest of
-    // the prologue while the weights are in flight.
+    // the prologue while the weights are in flight.  (Waiting for the
+    // activation before issuing any weight load measured slower on every
+    // decode shape.)
     XStage st;
     stage_issue<P, false>(xin, K, st);
     prefetch_block<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, w, s, wp, sp);
@@ -134,19 +136,32 @@ int resident_blocks(KernelFn fn, size_t lds) {
     return total;
 }
 
-// Default launch shape, from rocprofv3 kernel traces of every shape on the
-// decode matrices (non-temporal loads won or tied everywhere):
-//   * two rows per 16-lane row with a 4-way k split is best or within 3% on
-//     every 4096-wide product and on the largest ones (57344 x 8192);
+// Default launch shape, from back-to-back launch timings of every shape on
+// the decode matrices with their real prologues and epilogues (non-temporal
+// loads won or tied everywhere):
+//   * K = 4096: one row per 16-lane row, 4-way k split, 8 chunks in flight
+//     (6144 x 4096: 6.9 vs 7.3 us for two rows; 4096 x 4096: 5.45 vs 5.67);
+//     the paired gate+up rows prefer a 2-way split (28672 x 4096: 14.5-14.8
+//     vs 15.0-15.5 us);
 //   * K = 8192 with 8192..12288 rows prefers one row per 16-lane row
 //     (10240 x 8192: 12.2 vs 14.5 us; 8192 x 8192 with 8 chunks in flight:
 //     11.0 vs 12.6 us);
-//   * K = 28672 prefers a 2-way split (27.4 vs 28.2 us).
+//   * K = 14336: one row, 4-way split (4096 x 14336: 10.0 vs 10.25 us);
+//   * K = 28672 prefers a 2-way split (27.4 vs 28.2 us);
+//   * otherwise two rows per 16-lane row with a 4-way k split (best or
+//     within 3% on the largest products, 57344 x 8192).
 // The epilogue variant (paired rows) needs two rows per slot.
 Cfg choose_config(Epi e, int64_t N, int64_t K) {
     const int64_t C = K / 32;
     Cfg c{2, 4, 4, true};
-    if (e != Epi::SiluPair && K >= 8192 && K < 12288 && N <= 12288) {
+    if (K < 8192) {
+        if (e == Epi::SiluPair) {
+            c.KS = 2;
+        } else {
+            c.R = 1;
+            c.U = 8;
+        }
+    } else if (e != Epi::SiluPair && K < 12288 && N <= 12288) {
         c.R = 1;
         if (N > 8192) {
             c.KS = 2;
@@ -156,9 +171,15 @@ Cfg choose_config(Epi e, int64_t N, int64_t K) {
         }
     } else if (K >= 16384) {
         c.KS = 2;
+    } else if (e != Epi::SiluPair && K >= 12288) {
+        c.R = 1;
     }
     while (c.KS > 1 && C < 16 * c.KS)
         c.KS /= 2;
+    // Narrow rows without a k split exist only with two rows per slot for the
+    // decode epilogues.
+    if (c.KS == 1 && c.R == 1 && e != Epi::Store)
+        c.R = 2;
     return c;
 }
 

@@ -128,6 +128,12 @@ def test_decoder_host_object_and_step_checks():
         assert L.decode_step_graph(h, 100, 1234) == STATE    # no resident layers
         assert L.q4_decode_step_eager(h, None) == STATE
         assert L.q4_decode_layer(h, None, None) == INVALID
+        shapes = q4.layer_shapes(DIMS)
+        for which in (-1, 4):
+            assert L.q4_decode_layer_part(h, ctypes.byref(shapes), which, None) == INVALID
+        assert L.q4_decode_layer_part(h, None, 0, None) == INVALID
+        # shapes without device pointers fail the matrix checks, before any launch
+        assert L.q4_decode_layer_part(h, ctypes.byref(shapes), 0, None) == INVALID
     finally:
         assert L.q4_decoder_destroy(h) == 0
     assert L.decode_step_graph(None, 100, 1234) == INVALID

@@ -68,7 +68,7 @@ class Model:
     def set_h(self, h0):
         self.h.copy_(torch.as_tensor(h0, dtype=torch.float32, device=DEV))
 
-    def workspace_sections(self):
+    def workspace_sections(self, with_norm=False):
         d = self.dims
         a = lambda n: (n + 255) // 256 * 256
         o1 = a(max(d["d"], d["dff"]) * 2)
@@ -79,7 +79,68 @@ class Model:
         qkv = ws[o1:o1 + nqkv * 4].view(torch.float32).numpy()
         oin = ws[o2:o2 + d["H"] * d["hd"] * 2].view(torch.int16).numpy().view(np.uint16)
         mlp = ws[o3:o3 + d["dff"] * 2].view(torch.int16).numpy().view(np.uint16)
+        if with_norm:
+            a16 = ws[:d["d"] * 2].view(torch.int16).numpy().view(np.uint16)
+            return qkv, oin, mlp, a16
         return qkv, oin, mlp
+
+
+def f16_ulp(v):
+    """Spacing of binary16 values at |v| (2^-24 below the normal range)."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -14)
+    return 2.0 ** (np.floor(np.log2(a)) - 10)
+
+
+def teacher_forced_layer(m, L_dev, L_host, what, s):
+    """Runs one layer product by product and checks each against the oracle
+    computed from the GPU's own inputs to that product (the product bound),
+    and each glue step against its definition from the GPU's fp32 values:
+    V gather exact, RMSNorm within 1 binary16 ulp, SiLU gate within the
+    propagated product bound plus 1 ulp."""
+    d = m.dims
+    H, Hkv, hd, dff = d["H"], d["Hkv"], d["hd"], d["dff"]
+    s.synchronize()  # earlier layers may still be in flight on s
+    h_in = m.h.cpu().numpy().astype(np.float64)
+    # QKV from the normed residual
+    m.dec.layer_part(L_dev, 0, s)
+    s.synchronize()
+    qkv, oin, _ = m.workspace_sections()
+    q_ref, q_mag = oracle.gemv(*L_host["qkv"], oracle.rmsnorm_f16(h_in, EPS))
+    assert oracle.within_bound(qkv, q_ref, q_mag).all(), f"{what}: QKV product"
+    assert np.array_equal(oin, oracle.gqa_gather_f16(qkv.astype(np.float64), H, Hkv, hd)), \
+        f"{what}: V gather is not the binary16 rounding of the GPU's V rows"
+    # O, residual add
+    m.dec.layer_part(L_dev, 1, s)
+    s.synchronize()
+    h_mid = m.h.cpu().numpy().astype(np.float64)
+    o_ref, o_mag = oracle.gemv(*L_host["o"], oin)
+    ref = h_in + o_ref
+    assert np.all(np.abs(h_mid - ref) <= 2e-3 * o_mag + 1e-6 + np.abs(ref) * 2.0 ** -23), \
+        f"{what}: O product + residual"
+    # gate+up from the second norm, SiLU gate
+    m.dec.layer_part(L_dev, 2, s)
+    s.synchronize()
+    _, _, mlp, a16 = m.workspace_sections(with_norm=True)
+    a_ref = oracle.rmsnorm_f16(h_mid, EPS)
+    got, want = oracle.f16_to_f64(a16), oracle.f16_to_f64(a_ref)
+    assert np.all(np.abs(got - want) <= f16_ulp(want)), f"{what}: second RMSNorm"
+    g_ref, g_mag = oracle.gemv(*L_host["gate_up"], a16)
+    g, u = g_ref[:dff], g_ref[dff:]
+    dg, du = 2e-3 * g_mag[:dff] + 1e-6, 2e-3 * g_mag[dff:] + 1e-6
+    silu = g / (1.0 + np.exp(-g))
+    want = silu * u
+    # |silu'| <= 1.1 everywhere
+    bound = 1.1 * dg * (np.abs(u) + du) + np.abs(silu) * du + f16_ulp(want)
+    got = oracle.f16_to_f64(mlp)
+    assert np.all(np.abs(got - want) <= bound), f"{what}: SiLU gate"
+    # down, residual add
+    m.dec.layer_part(L_dev, 3, s)
+    s.synchronize()
+    h_out = m.h.cpu().numpy().astype(np.float64)
+    d_ref, d_mag = oracle.gemv(*L_host["down"], mlp)
+    ref = h_mid + d_ref
+    assert np.all(np.abs(h_out - ref) <= 2e-3 * d_mag + 1e-6 + np.abs(ref) * 2.0 ** -23), \
+        f"{what}: down product + residual"
 
 
 def test_tiny_eager_layers_match_oracle():
@@ -171,8 +232,10 @@ def _big(dims_name, config, n_layers):
 
 def test_8b_full_step_graph_matches_oracle():
     """Llama-3-8B shapes, all 32 layers, graph-captured (four kernels per
-    layer, the default step), token 0; the persistent kernel uses the same
-    per-output arithmetic on these matrices, so it must agree bitwise."""
+    layer, the default step), token 0, against the oracle; graph == eager
+    bitwise for both step implementations, and the persistent kernel (its
+    own fixed launch shape, so its own summation order) within the same
+    bound."""
     dims, layers = _big("8b", 2, 32)
     h0 = inputs.residual_f32(dims["d"], inputs.seed_of(2, 0, 9))
     m = Model(dims, layers)
@@ -189,18 +252,44 @@ def test_8b_full_step_graph_matches_oracle():
     s.synchronize()
     assert torch.equal(m.h.cpu(), h_graph), "graph and eager differ"
     m.dec.set_persistent(True)
+    outs = []
     for step in (lambda: m.dec.step_eager(s), lambda: m.dec.step_graph(512, s)):
         m.set_h(h0)
         torch.cuda.synchronize()
         step()
         s.synchronize()
         m.dec.check()
-        assert torch.equal(m.h.cpu(), h_graph), "persistent kernel differs from per-layer"
+        outs.append(m.h.cpu().clone())
+    assert torch.equal(outs[0], outs[1]), "persistent graph and eager differ"
     host = to_host(layers)
     del layers
     ref = oracle_run(host, dims, h0.numpy())
     rel = check_h(h_graph.numpy(), ref[-1][0], ref[-1][1], "8b 32 layers")
     assert rel < 1e-2
+    rel = check_h(outs[0].numpy(), ref[-1][0], ref[-1][1], "8b 32 layers persistent")
+    assert rel < 1e-2
+
+
+def test_8b_teacher_forced_all_layers():
+    """Llama-3-8B shapes, tokens 0 and 255, every product of all 32 layers
+    checked from the GPU's own inputs (no error accumulates between
+    products); the per-layer products equal the graph step bitwise."""
+    dims, layers = _big("8b", 2, 32)
+    host = to_host(layers)
+    m = Model(dims, layers)
+    s = torch.cuda.Stream()
+    for t in (0, 255):
+        h0 = inputs.residual_f32(dims["d"], inputs.seed_of(2, t, 9))
+        m.set_h(h0)
+        torch.cuda.synchronize()
+        for l in range(32):
+            teacher_forced_layer(m, layers[l], host[l], f"token {t} layer {l}", s)
+        h_parts = m.h.cpu().clone()
+        m.set_h(h0)
+        torch.cuda.synchronize()
+        m.dec.step_graph(512, s)
+        s.synchronize()
+        assert torch.equal(m.h.cpu(), h_parts), t
 
 
 def test_70b_first_layers_and_full_graph():
@@ -243,5 +332,17 @@ def test_70b_first_layers_and_full_graph():
     m.set_h(h0)
     torch.cuda.synchronize()
     m.dec.step_eager(s)
+    s.synchronize()
+    assert torch.equal(m.h.cpu(), h_graph)
+    # teacher-forced products of layers 0, 39 and 79
+    m.set_h(h0)
+    torch.cuda.synchronize()
+    checked = {0, 39, 79}
+    host_c = {l: to_host([layers[l]])[0] for l in checked}
+    for l in range(80):
+        if l in checked:
+            teacher_forced_layer(m, layers[l], host_c[l], f"70b layer {l}", s)
+        else:
+            m.dec.layer(layers[l], s)
     s.synchronize()
     assert torch.equal(m.h.cpu(), h_graph)
