@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--step-mode", type=int, default=None, choices=[0, 1, 2],
+                    help="decode step implementation: 0 four kernels per layer, 1 persistent, "
+                         "2 streaming persistent (default: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for "
                          "hardware byte counters)")
@@ -82,6 +85,8 @@ def main():
     h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
     ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
     dec = q4.Decoder(dims, layers, h, ws)
+    if args.step_mode is not None:
+        dec.set_persistent(args.step_mode)
     stream = torch.cuda.Stream()
     if args.copy_calibration:
         # 1 GiB read + 1 GiB written by one plain copy kernel
@@ -343,6 +348,8 @@ def bench_70b_resident(args, q4, inputs, torch):
     h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
     ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
     dec = q4.Decoder(dims, layers, h, ws)
+    if args.step_mode is not None:
+        dec.set_persistent(args.step_mode)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)

@@ -183,15 +183,25 @@ q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out);
  * words into the workspace; the step starts as four kernels per layer (the
  * persistent step below is opt-in).  Without layers no GPU work. */
 q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
-/* Step implementation for resident layers: on = one persistent kernel per
- * token (all layers, products separated by grid-wide barriers, each
- * workgroup prefetching its next product's weights before the barrier);
- * off = four kernels per layer.  Same arithmetic per output; cached graphs
- * are dropped on a change.  UNSUPPORTED if the activations exceed LDS. */
-q4_status q4_decoder_set_persistent(void *dec, int32_t on);
-/* After the stream has completed a persistent step: Q4_OK, or Q4_ERR_HIP if
- * a grid barrier gave up waiting (the step's results are then invalid; the
- * flag is cleared).  Synchronous. */
+/* Step implementation for resident layers (cached graphs are dropped on a
+ * change):
+ *   0 four kernels per layer (the default);
+ *   1 one persistent kernel per token: all layers, products separated by
+ *     grid-wide barriers, each workgroup prefetching its next product's
+ *     first weights into registers before the barrier (UNSUPPORTED if the
+ *     largest activation exceeds 64 KB of LDS);
+ *   2 one streaming persistent kernel per token: one workgroup per CU whose
+ *     producer waves copy the weights of every product, in order, from HBM
+ *     into an LDS ring while its consumer waves compute, so the weight
+ *     stream runs through the grid barriers (UNSUPPORTED unless every K is a
+ *     multiple of 64 and the activation plus the ring fit in LDS).
+ * Each output is the same dot product within the same bound; the summation
+ * order, and so the low bits, differ between implementations.  INVALID_ARG
+ * for another mode, STATE without resident layers. */
+q4_status q4_decoder_set_persistent(void *dec, int32_t mode);
+/* After the stream has completed a persistent step (mode 1 or 2): Q4_OK, or
+ * Q4_ERR_HIP if a bounded wait (grid barrier, ring slot, ring space) gave up
+ * (the step's results are then invalid; the flag is cleared).  Synchronous. */
 q4_status q4_decoder_check(void *dec);
 /* Runs all layers for one token.  ctx_len picks the context bucket: the
  * smallest of 512, 1024, 2048, 4096 that is >= ctx_len; the first call for a

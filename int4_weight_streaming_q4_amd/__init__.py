@@ -239,8 +239,10 @@ class Decoder:
     def step_graph(self, ctx_len: int, stream=None):
         _check(lib().decode_step_graph(self.handle, ctx_len, _stream(stream)))
 
-    def set_persistent(self, on: bool):
-        _check(lib().q4_decoder_set_persistent(self.handle, 1 if on else 0))
+    def set_persistent(self, mode):
+        """Step implementation: False/0 four kernels per layer, True/1 the
+        persistent kernel, 2 the streaming persistent kernel."""
+        _check(lib().q4_decoder_set_persistent(self.handle, int(mode)))
 
     def check(self):
         """Raise if a persistent step's grid barrier timed out (synchronous)."""

@@ -44,7 +44,7 @@ struct Decoder {
     uint16_t *mlp = nullptr; // f16[dff]
     uint32_t *bar = nullptr; // grid-barrier words of the persistent kernel
     DevLayer *dev_layers = nullptr; // device copy of the layer table
-    bool persistent = false;
+    int32_t mode = 0; // 0 four kernels per layer, 1 persistent, 2 streaming persistent
     hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 
@@ -170,7 +170,7 @@ q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks ma
 }
 
 q4_status enqueue_all(Decoder *dec, hipStream_t s) {
-    if (dec->persistent) {
+    if (dec->mode != 0) {
         PersistArgs a{};
         a.layers = dec->dev_layers;
         a.n_layers = (int32_t)dec->layers.size();
@@ -186,7 +186,7 @@ q4_status enqueue_all(Decoder *dec, hipStream_t s) {
         a.dff = (int32_t)dec->dims.dff;
         a.eps = dec->desc.eps;
         a.bar = dec->bar;
-        return launch_persistent(a, s);
+        return dec->mode == 2 ? launch_stream(a, s) : launch_persistent(a, s);
     }
     for (size_t l = 0; l < dec->layers.size(); ++l)
         Q4_CHECK(enqueue_layer(dec, dec->layers[l], s));
@@ -300,7 +300,7 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
         // Four kernels per layer by default: on MI355X they stream the
         // weights faster than the persistent kernel's barrier-separated
         // phases; the persistent step is opt-in.
-        dec->persistent = false;
+        dec->mode = 0;
     }
     *dec_out = dec;
     return Q4_OK;
@@ -623,23 +623,27 @@ extern "C" q4_status q4_decode_kernel_time(void *decp, int32_t which, int32_t re
     return st;
 }
 
-extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t on) {
+extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t mode) {
     Decoder *dec = static_cast<Decoder *>(decp);
     if (!dec)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: null decoder");
-    if (on && dec->layers.empty())
+    if (mode < 0 || mode > 2)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: mode %d", mode);
+    if (mode != 0 && dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "q4_decoder_set_persistent: no resident layers");
-    if (on && q4::persistent_lds_bytes((int32_t)dec->dims.d, (int32_t)dec->dims.H,
-                                       (int32_t)dec->dims.hd, (int32_t)dec->dims.dff) > 65536)
+    const int32_t d = (int32_t)dec->dims.d, H = (int32_t)dec->dims.H,
+                  hd = (int32_t)dec->dims.hd, dff = (int32_t)dec->dims.dff;
+    if (mode == 1 && q4::persistent_lds_bytes(d, H, hd, dff) > 65536)
         return q4::fail(Q4_ERR_UNSUPPORTED, "q4_decoder_set_persistent: activations exceed LDS");
-    const bool want = on != 0;
-    if (want != dec->persistent) {
+    if (mode == 2)
+        Q4_CHECK(q4::stream_supported(d, H, hd, dff, nullptr));
+    if (mode != dec->mode) {
         for (auto &e : dec->exec)
             if (e) {
                 (void)hipGraphExecDestroy(e);
                 e = nullptr;
             }
-        dec->persistent = want;
+        dec->mode = mode;
     }
     return Q4_OK;
 }

@@ -88,15 +88,21 @@ __device__ __forceinline__ int64_t row_of(int64_t unit, int r, const EpiArgs &ea
 
 // Activation accesses.  COH = false: ordinary loads and stores (one kernel
 // per product; the kernel boundary publishes the data).  COH = true: the
-// persistent kernel, where workgroups on different XCDs exchange the small
-// activation vectors inside one launch: every store of such a vector is an
-// agent-scope atomic store (written through to the coherence point), and
-// after each grid barrier a workgroup invalidates its caches once (an
-// agent-scope acquire), so the ordinary cached loads below see every
-// workgroup's writes while each XCD still fetches a vector only once.
+// persistent kernels, where workgroups on different XCDs exchange the small
+// activation vectors inside one launch: every store and every load of such
+// a vector is an agent-scope atomic access, which goes to the coherence
+// point instead of an XCD's own L2, so no cache writeback or invalidation
+// is needed at the grid barriers (each of those is a whole-L2 operation).
 template <bool COH>
 __device__ __forceinline__ uint4 act_load16(const void *p) {
-    return gload16(p);
+    if constexpr (COH) {
+        const uint64_t *q = static_cast<const uint64_t *>(p);
+        const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return uint4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+    } else {
+        return gload16(p);
+    }
 }
 
 template <bool COH>
@@ -114,7 +120,10 @@ __device__ __forceinline__ void act_store16(void *p, uint4 v) {
 
 template <bool COH>
 __device__ __forceinline__ float act_load_f32(const float *p) {
-    return gload(p);
+    if constexpr (COH)
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return gload(p);
 }
 
 template <bool COH>

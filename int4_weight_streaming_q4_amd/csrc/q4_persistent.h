@@ -36,4 +36,11 @@ constexpr size_t kBarBytes = ((size_t)(kBarFlags + kMaxPersistentGrid + 1) * 4 +
 size_t persistent_lds_bytes(int32_t d, int32_t H, int32_t hd, int32_t dff);
 q4_status launch_persistent(const PersistArgs &a, hipStream_t stream);
 
+// Streaming persistent step (producer waves fill an LDS ring): Q4_OK if the
+// shapes and the device allow it (every K a multiple of 64, the activation
+// plus a ring of at least one unit in LDS, one workgroup per CU resident);
+// *nslots gets the ring size.
+q4_status stream_supported(int32_t d, int32_t H, int32_t hd, int32_t dff, int *nslots);
+q4_status launch_stream(const PersistArgs &a, hipStream_t stream);
+
 } // namespace q4

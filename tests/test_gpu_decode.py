@@ -224,6 +224,57 @@ def test_tiny_token_loop_graph_replays(persistent):
     m.dec.check()
 
 
+# Small model whose widths are multiples of 64 (the streaming step's need).
+SMALL = dict(d=256, H=4, Hkv=2, hd=64, dff=384)
+
+
+def test_streaming_step_unsupported_shapes():
+    layers = make_layers(TINY, 93, 1)
+    m = Model(TINY, layers)
+    with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
+        m.dec.set_persistent(2)  # dff = 96 is not a multiple of 64
+    with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
+        m.dec.set_persistent(3)
+
+
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_streaming_step_small_matches_oracle(n_layers):
+    """Streaming persistent step on a small model: eager against the oracle,
+    graph replays over every bucket bitwise equal to eager, a token loop
+    through one graph against the oracle token by token."""
+    layers = make_layers(SMALL, 94, n_layers)
+    host = to_host(layers)
+    m = Model(SMALL, layers)
+    m.dec.set_persistent(2)
+    s = torch.cuda.Stream()
+    h0 = inputs.residual_f32(SMALL["d"], inputs.seed_of(94, 0, 9))
+    m.set_h(h0)
+    torch.cuda.synchronize()
+    m.dec.step_eager(s)
+    s.synchronize()
+    m.dec.check()
+    h_eager = m.h.cpu().clone()
+    ref = oracle_run(host, SMALL, h0.numpy())
+    check_h(h_eager.numpy(), ref[-1][0], ref[-1][1], f"small streaming {n_layers} layers")
+    for ctx in (1, 700, 2048, 4096):
+        for rep in range(2):
+            m.set_h(h0)
+            torch.cuda.synchronize()
+            m.dec.step_graph(ctx, s)
+            s.synchronize()
+            m.dec.check()
+            assert torch.equal(m.h.cpu(), h_eager), (ctx, rep)
+    for t in range(1, 4):
+        h0 = inputs.residual_f32(SMALL["d"], inputs.seed_of(94, t, 9))
+        with torch.cuda.stream(s):
+            m.h.copy_(h0.to(DEV, non_blocking=False))
+            m.dec.step_graph(600, s)
+        s.synchronize()
+        m.dec.check()
+        ref = oracle_run(host, SMALL, h0.numpy())
+        check_h(m.h.cpu().numpy(), ref[-1][0], ref[-1][1], f"small streaming token {t}")
+
+
 def _big(dims_name, config, n_layers):
     dims = {k: v for k, v in inputs.MODEL_DIMS[dims_name].items() if k != "n_layers"}
     layers = make_layers(dims, config, n_layers)
@@ -251,23 +302,29 @@ def test_8b_full_step_graph_matches_oracle():
     m.dec.step_eager(s)
     s.synchronize()
     assert torch.equal(m.h.cpu(), h_graph), "graph and eager differ"
-    m.dec.set_persistent(True)
-    outs = []
-    for step in (lambda: m.dec.step_eager(s), lambda: m.dec.step_graph(512, s)):
-        m.set_h(h0)
-        torch.cuda.synchronize()
-        step()
-        s.synchronize()
-        m.dec.check()
-        outs.append(m.h.cpu().clone())
-    assert torch.equal(outs[0], outs[1]), "persistent graph and eager differ"
+    outs = {}
+    for mode in (1, 2):
+        m.dec.set_persistent(mode)
+        got = []
+        for step in (lambda: m.dec.step_eager(s), lambda: m.dec.step_graph(512, s),
+                     lambda: m.dec.step_graph(512, s)):
+            m.set_h(h0)
+            torch.cuda.synchronize()
+            step()
+            s.synchronize()
+            m.dec.check()
+            got.append(m.h.cpu().clone())
+        assert torch.equal(got[0], got[1]) and torch.equal(got[0], got[2]), \
+            f"mode {mode}: graph and eager differ"
+        outs[mode] = got[0]
     host = to_host(layers)
     del layers
     ref = oracle_run(host, dims, h0.numpy())
     rel = check_h(h_graph.numpy(), ref[-1][0], ref[-1][1], "8b 32 layers")
     assert rel < 1e-2
-    rel = check_h(outs[0].numpy(), ref[-1][0], ref[-1][1], "8b 32 layers persistent")
-    assert rel < 1e-2
+    for mode, h in outs.items():
+        rel = check_h(h.numpy(), ref[-1][0], ref[-1][1], f"8b 32 layers step mode {mode}")
+        assert rel < 1e-2
 
 
 def test_8b_teacher_forced_all_layers():
@@ -311,15 +368,16 @@ def test_70b_first_layers_and_full_graph():
         m2.dec.layer(layers[l], s)
     s.synchronize()
     check_h(m2.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1 per-layer kernels")
-    # the same two layers through the persistent kernel
+    # the same two layers through both persistent kernels
     m3 = Model(dims, layers[:2])
-    m3.dec.set_persistent(True)
-    m3.set_h(h0)
-    torch.cuda.synchronize()
-    m3.dec.step_eager(s)
-    s.synchronize()
-    m3.dec.check()
-    check_h(m3.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1 persistent")
+    for mode in (1, 2):
+        m3.dec.set_persistent(mode)
+        m3.set_h(h0)
+        torch.cuda.synchronize()
+        m3.dec.step_eager(s)
+        s.synchronize()
+        m3.dec.check()
+        check_h(m3.h.cpu().numpy(), ref[-1][0], ref[-1][1], f"70b layers 0-1 step mode {mode}")
     # full model
     m = Model(dims, layers)
     m.set_h(h0)
