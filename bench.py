@@ -35,9 +35,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=3)
-    ap.add_argument("--step-mode", type=int, default=None, choices=[0, 1, 2],
+    ap.add_argument("--step-mode", type=int, default=None, choices=[0, 1, 2, 3],
                     help="decode step implementation: 0 four kernels per layer, 1 persistent, "
-                         "2 streaming persistent (default: the library's choice)")
+                         "2 streaming persistent, 3 streaming workgroups per product "
+                         "(default: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for "
                          "hardware byte counters)")

@@ -194,7 +194,9 @@ q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
  *     producer waves copy the weights of every product, in order, from HBM
  *     into an LDS ring while its consumer waves compute, so the weight
  *     stream runs through the grid barriers (UNSUPPORTED unless every K is a
- *     multiple of 64 and the activation plus the ring fit in LDS).
+ *     multiple of 64 and the activation plus the ring fit in LDS);
+ *   3 the same producer/consumer workgroups as mode 2, one launch per
+ *     product (four per layer, no grid barriers; same limits as mode 2).
  * Each output is the same dot product within the same bound; the summation
  * order, and so the low bits, differ between implementations.  INVALID_ARG
  * for another mode, STATE without resident layers. */

@@ -241,7 +241,8 @@ class Decoder:
 
     def set_persistent(self, mode):
         """Step implementation: False/0 four kernels per layer, True/1 the
-        persistent kernel, 2 the streaming persistent kernel."""
+        persistent kernel, 2 the streaming persistent kernel, 3 streaming
+        workgroups with one launch per product."""
         _check(lib().q4_decoder_set_persistent(self.handle, int(mode)))
 
     def check(self):

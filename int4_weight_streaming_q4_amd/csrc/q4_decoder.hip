@@ -44,7 +44,8 @@ struct Decoder {
     uint16_t *mlp = nullptr; // f16[dff]
     uint32_t *bar = nullptr; // grid-barrier words of the persistent kernel
     DevLayer *dev_layers = nullptr; // device copy of the layer table
-    int32_t mode = 0; // 0 four kernels per layer, 1 persistent, 2 streaming persistent
+    int32_t mode = 0; // 0 four kernels per layer, 1 persistent, 2 streaming persistent,
+                      // 3 streaming workgroups, one launch per product
     hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 
@@ -186,6 +187,12 @@ q4_status enqueue_all(Decoder *dec, hipStream_t s) {
         a.dff = (int32_t)dec->dims.dff;
         a.eps = dec->desc.eps;
         a.bar = dec->bar;
+        if (dec->mode == 3) {
+            for (int32_t l = 0; l < a.n_layers; ++l)
+                for (int32_t k = 0; k < 4; ++k)
+                    Q4_CHECK(launch_stream_product(a, l, k, s));
+            return Q4_OK;
+        }
         return dec->mode == 2 ? launch_stream(a, s) : launch_persistent(a, s);
     }
     for (size_t l = 0; l < dec->layers.size(); ++l)
@@ -627,7 +634,7 @@ extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t mode) {
     Decoder *dec = static_cast<Decoder *>(decp);
     if (!dec)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: null decoder");
-    if (mode < 0 || mode > 2)
+    if (mode < 0 || mode > 3)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: mode %d", mode);
     if (mode != 0 && dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "q4_decoder_set_persistent: no resident layers");
@@ -635,7 +642,7 @@ extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t mode) {
                   hd = (int32_t)dec->dims.hd, dff = (int32_t)dec->dims.dff;
     if (mode == 1 && q4::persistent_lds_bytes(d, H, hd, dff) > 65536)
         return q4::fail(Q4_ERR_UNSUPPORTED, "q4_decoder_set_persistent: activations exceed LDS");
-    if (mode == 2)
+    if (mode == 2 || mode == 3)
         Q4_CHECK(q4::stream_supported(d, H, hd, dff, nullptr));
     if (mode != dec->mode) {
         for (auto &e : dec->exec)

@@ -42,5 +42,9 @@ q4_status launch_persistent(const PersistArgs &a, hipStream_t stream);
 // *nslots gets the ring size.
 q4_status stream_supported(int32_t d, int32_t H, int32_t hd, int32_t dff, int *nslots);
 q4_status launch_stream(const PersistArgs &a, hipStream_t stream);
+// One product (0 QKV, 1 O, 2 gate+up, 3 down) of one layer with the same
+// producer/consumer workgroups, as its own launch (no grid barrier).
+q4_status launch_stream_product(const PersistArgs &a, int32_t layer, int32_t which,
+                                hipStream_t stream);
 
 } // namespace q4

@@ -161,7 +161,8 @@ __device__ __forceinline__ int64_t unit_row(const Geo &g, const PersistArgs &a, 
 template <int kDepth> // slots in flight per producer wave
 __device__ __forceinline__ void producer(const PersistArgs &a,
                                          const DevLayer *__restrict__ layers, const Geo &gs_lds,
-                                         uint32_t *ctl, char *ring, uint32_t nslots, int pw) {
+                                         uint32_t *ctl, char *ring, uint32_t nslots, int pw,
+                                         int p0, int p1) {
     // A register copy of the shapes, taken before the first direct-to-LDS
     // load: ordinary LDS reads after that point would make the compiler wait
     // for every outstanding load first.
@@ -172,11 +173,13 @@ __device__ __forceinline__ void producer(const PersistArgs &a,
     uint32_t issued = 0;
     uint32_t gs = 0, pos = 0, gen = 0; // slot, its ring position and pass
     bool abort = false;
-    for (int l = 0; l < a.n_layers && !abort; ++l) {
+    for (int l = p0 / 4; l <= (p1 - 1) / 4 && !abort; ++l) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (abort)
                 break;
+            if (l * 4 + k < p0 || l * 4 + k >= p1)
+                continue;
             // scalar loads (read-only table): they do not share the vector
             // memory counter with the ring loads
             const uint8_t *W = layers[l].packed[k];
@@ -389,14 +392,16 @@ __device__ __forceinline__ void grid_sync(CState &cs, const PersistArgs &a, int 
 }
 
 // binary16 activation -> LDS (consumer threads only).
+template <bool COH>
 __device__ __forceinline__ void cons_stage_f16(const uint16_t *x16, uint4 *xs, int K, int tc) {
     const int C = K >> 5;
     for (int b = tc; b < (K >> 3); b += kConsThreads)
-        xs[(b & 3) * C + (b >> 2)] = permute8(act_load16<true>(x16 + 8 * (size_t)b));
+        xs[(b & 3) * C + (b >> 2)] = permute8(act_load16<COH>(x16 + 8 * (size_t)b));
 }
 
 // RMSNorm of the fp32 residual -> LDS (consumer threads only); every
 // workgroup sums in the same order, so all stage identical bits.
+template <bool COH>
 __device__ __forceinline__ void cons_stage_rms(CState &cs, const PersistArgs &a, uint4 *xs,
                                                int K, int tc, int cw, uint16_t *norm_out) {
     constexpr int kKeep = 2;
@@ -408,7 +413,7 @@ __device__ __forceinline__ void cons_stage_rms(CState &cs, const PersistArgs &a,
     for (int j = 0; j < kKeep; ++j) {
         const int b = tc + j * kConsThreads;
         if (b < nb8) {
-            load_f32x8<true>(a.h + 8 * (size_t)b, keep[j]);
+            load_f32x8<COH>(a.h + 8 * (size_t)b, keep[j]);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 ss = fmaf(keep[j][i], keep[j][i], ss);
@@ -416,7 +421,7 @@ __device__ __forceinline__ void cons_stage_rms(CState &cs, const PersistArgs &a,
     }
     for (int b = tc + kKeep * kConsThreads; b < nb8; b += kConsThreads) {
         float f[8];
-        load_f32x8<true>(a.h + 8 * (size_t)b, f);
+        load_f32x8<COH>(a.h + 8 * (size_t)b, f);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             ss = fmaf(f[i], f[i], ss);
@@ -440,7 +445,7 @@ __device__ __forceinline__ void cons_stage_rms(CState &cs, const PersistArgs &a,
         const uint4 v = {p[0], p[1], p[2], p[3]};
         xs[(b & 3) * C + (b >> 2)] = permute8(v);
         if (norm_out && blockIdx.x == 0)
-            act_store16<true>(norm_out + 8 * (size_t)b, v);
+            act_store16<COH>(norm_out + 8 * (size_t)b, v);
     };
 #pragma unroll
     for (int j = 0; j < kKeep; ++j) {
@@ -450,7 +455,7 @@ __device__ __forceinline__ void cons_stage_rms(CState &cs, const PersistArgs &a,
     }
     for (int b = tc + kKeep * kConsThreads; b < nb8; b += kConsThreads) {
         float f[8];
-        load_f32x8<true>(a.h + 8 * (size_t)b, f);
+        load_f32x8<COH>(a.h + 8 * (size_t)b, f);
         emit(b, f);
     }
 }
@@ -495,8 +500,10 @@ __device__ __forceinline__ void free_slot(uint32_t *ctl, uint32_t gs, uint32_t n
                        __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+template <bool COH>
 __device__ __forceinline__ void consumer(const PersistArgs &a, const Geo &g, uint32_t *ctl,
-                                         uint4 *xs, const char *ring, uint32_t nslots, int cw) {
+                                         uint4 *xs, const char *ring, uint32_t nslots, int cw,
+                                         int p0, int p1) {
     const int lane = threadIdx.x & 63;
     const int tc = threadIdx.x - kProd * 64;
     const uint32_t bias = vgpr_const(0x64006400u);
@@ -507,19 +514,23 @@ __device__ __forceinline__ void consumer(const PersistArgs &a, const Geo &g, uin
     const int64_t v_off = (int64_t)(a.H + a.Hkv) * a.hd;
     const int group = a.H / a.Hkv;
     const uint32_t layer_slots = (uint32_t)g.slot_pre[4];
-    for (int l = 0; l < a.n_layers && !cs.abort; ++l) {
+    // slot index of the first slot of phase p0 (slots count from 0 per launch)
+    const uint32_t base = (uint32_t)(p0 / 4) * layer_slots + (uint32_t)g.slot_pre[p0 % 4];
+    for (int l = p0 / 4; l <= (p1 - 1) / 4 && !cs.abort; ++l) {
         for (int k = 0; k < 4 && !cs.abort; ++k) {
+            if (l * 4 + k < p0 || l * 4 + k >= p1)
+                continue;
             const int K = g.K[k], C = g.C[k], S = g.S[k], nu = g.nu[k];
             if (k == 0)
-                cons_stage_rms(cs, a, xs, K, tc, cw, nullptr);
+                cons_stage_rms<COH>(cs, a, xs, K, tc, cw, nullptr);
             else if (k == 1)
-                cons_stage_f16(a.oin, xs, K, tc);
+                cons_stage_f16<COH>(a.oin, xs, K, tc);
             else if (k == 2)
-                cons_stage_rms(cs, a, xs, K, tc, cw, a.norm_out);
+                cons_stage_rms<COH>(cs, a, xs, K, tc, cw, a.norm_out);
             else
-                cons_stage_f16(a.mlp, xs, K, tc);
+                cons_stage_f16<COH>(a.mlp, xs, K, tc);
             cons_barrier(cs, a.bar);
-            const uint32_t pb = (uint32_t)l * layer_slots + (uint32_t)g.slot_pre[k];
+            const uint32_t pb = (uint32_t)l * layer_slots + (uint32_t)g.slot_pre[k] - base;
             // Unit j0 + cw of every group of kCons units (producer order).
             for (int j0 = 0; j0 + cw < nu && !cs.abort; j0 += kCons) {
                 const int nj = min(kCons, nu - j0);
@@ -531,9 +542,9 @@ __device__ __forceinline__ void consumer(const PersistArgs &a, const Geo &g, uin
                 float y0 = 0.0f, y1 = 0.0f;
                 if (k == 1 || k == 3) {
                     if (lane == 0)
-                        y0 = act_load_f32<true>(a.h + row0);
+                        y0 = act_load_f32<COH>(a.h + row0);
                     if (lane == 1 && v1)
-                        y1 = act_load_f32<true>(a.h + row1);
+                        y1 = act_load_f32<COH>(a.h + row1);
                 }
                 float acc0 = 0.0f, acc1 = 0.0f;
                 for (int sg = 0; sg < S; ++sg) {
@@ -576,43 +587,47 @@ __device__ __forceinline__ void consumer(const PersistArgs &a, const Geo &g, uin
                     if (lane < 2 && (lane == 0 || v1)) {
                         const int64_t row = lane ? row1 : row0;
                         const float t = lane ? t1 : t0;
-                        act_store_f32<true>(a.qkv + row, t);
+                        act_store_f32<COH>(a.qkv + row, t);
                         if (row >= v_off) {
                             const int64_t v = row - v_off;
                             const int64_t gq = v / a.hd, e = v % a.hd;
                             const uint16_t h16 = f32_to_f16(t);
                             for (int q = 0; q < group; ++q)
-                                act_store_u16<true>(a.oin + (gq * group + q) * a.hd + e, h16);
+                                act_store_u16<COH>(a.oin + (gq * group + q) * a.hd + e, h16);
                         }
                     }
                 } else if (k == 2) {
                     if (lane == 0) {
                         const float silu = t0 / (1.0f + expf(-t0));
-                        act_store_u16<true>(a.mlp + u, f32_to_f16(silu * t1));
+                        act_store_u16<COH>(a.mlp + u, f32_to_f16(silu * t1));
                     }
                 } else {
                     if (lane == 0)
-                        act_store_f32<true>(a.h + row0, y0 + t0);
+                        act_store_f32<COH>(a.h + row0, y0 + t0);
                     if (lane == 1 && v1)
-                        act_store_f32<true>(a.h + row1, y1 + t1);
+                        act_store_f32<COH>(a.h + row1, y1 + t1);
                 }
             }
-            const bool last = l + 1 == a.n_layers && k == 3;
+            const bool last = l * 4 + k + 1 == p1;
             if (!last && !cs.abort)
                 grid_sync(cs, a, cw);
         }
     }
     if (cs.abort && lane == 0)
         __hip_atomic_store(ctl + kAbort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (cw == 0 && blockIdx.x == 0 && lane == 0 && !cs.abort)
+    // the launch parity alternates only for launches that used grid barriers
+    if (p1 - p0 > 1 && cw == 0 && blockIdx.x == 0 && lane == 0 && !cs.abort)
         __hip_atomic_store(a.bar + kBarParity, cs.parity ^ 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kDepth>
+// Phases [p0, p1) of the schedule (phase 4 l + k is product k of layer l).
+// COH: several phases with grid barriers in between (coherent activation
+// accesses); otherwise a single phase, published by the kernel boundary.
+template <int kDepth, bool COH>
 __global__ void __launch_bounds__(kSThreads)
 decode_stream(PersistArgs a, const DevLayer *__restrict__ layers, int32_t xbytes,
-              int32_t nslots) {
+              int32_t nslots, int32_t p0, int32_t p1) {
     extern __shared__ uint4 lds[];
     uint32_t *ctl = reinterpret_cast<uint32_t *>(lds);
     uint4 *xs = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) + kCtlBytes);
@@ -629,9 +644,9 @@ decode_stream(PersistArgs a, const DevLayer *__restrict__ layers, int32_t xbytes
     // the weight-pointer loads scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (wave < kProd)
-        producer<kDepth>(a, layers, g, ctl, ring, (uint32_t)nslots, wave);
+        producer<kDepth>(a, layers, g, ctl, ring, (uint32_t)nslots, wave, p0, p1);
     else
-        consumer(a, g, ctl, xs, ring, (uint32_t)nslots, wave - kProd);
+        consumer<COH>(a, g, ctl, xs, ring, (uint32_t)nslots, wave - kProd, p0, p1);
 }
 
 struct StreamCfg {
@@ -663,13 +678,14 @@ StreamCfg stream_cfg() {
         optin = 0;
     c.lds = (size_t)std::max(max_lds, optin);
     bool ok = c.lds > 0;
-    for (const void *fn : {(const void *)decode_stream<kDepthHi>,
-                           (const void *)decode_stream<kDepthLo>})
+    for (const void *fn :
+         {(const void *)decode_stream<kDepthHi, true>, (const void *)decode_stream<kDepthLo, true>,
+          (const void *)decode_stream<kDepthHi, false>, (const void *)decode_stream<kDepthLo, false>})
         ok = ok && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)c.lds) == hipSuccess;
     int nb = 0;
     if (ok &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream<kDepthHi>, kSThreads,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream<kDepthHi, true>, kSThreads,
                                                      c.lds) == hipSuccess &&
         nb >= 1)
         c.grid = device_cus();
@@ -707,19 +723,34 @@ q4_status stream_supported(int32_t d, int32_t H, int32_t hd, int32_t dff, int *n
     return Q4_OK;
 }
 
-q4_status launch_stream(const PersistArgs &a, hipStream_t stream) {
+namespace {
+
+q4_status launch_range(const PersistArgs &a, int32_t p0, int32_t p1, hipStream_t stream) {
     int nslots = 0;
     Q4_CHECK(stream_supported(a.d, a.H, a.hd, a.dff, &nslots));
     const size_t xb = stream_xbytes(a.d, a.H, a.hd, a.dff);
     const StreamCfg c = stream_cfg();
-    if (nslots >= (int64_t)kProd * kDepthHi + kHeld)
-        hipLaunchKernelGGL(decode_stream<kDepthHi>, dim3((unsigned)c.grid), dim3(kSThreads),
-                           c.lds, stream, a, a.layers, (int32_t)xb, (int32_t)nslots);
-    else
-        hipLaunchKernelGGL(decode_stream<kDepthLo>, dim3((unsigned)c.grid), dim3(kSThreads),
-                           c.lds, stream, a, a.layers, (int32_t)xb, (int32_t)nslots);
+    const bool hi = nslots >= (int64_t)kProd * kDepthHi + kHeld;
+    const bool coh = p1 - p0 > 1;
+    auto fn = hi ? (coh ? decode_stream<kDepthHi, true> : decode_stream<kDepthHi, false>)
+                 : (coh ? decode_stream<kDepthLo, true> : decode_stream<kDepthLo, false>);
+    hipLaunchKernelGGL(fn, dim3((unsigned)c.grid), dim3(kSThreads), c.lds, stream, a, a.layers,
+                       (int32_t)xb, (int32_t)nslots, p0, p1);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
+}
+
+} // namespace
+
+q4_status launch_stream(const PersistArgs &a, hipStream_t stream) {
+    return launch_range(a, 0, 4 * a.n_layers, stream);
+}
+
+q4_status launch_stream_product(const PersistArgs &a, int32_t layer, int32_t which,
+                                hipStream_t stream) {
+    if (layer < 0 || layer >= a.n_layers || which < 0 || which > 3)
+        return fail(Q4_ERR_INVALID_ARG, "streaming product: layer %d product %d", layer, which);
+    return launch_range(a, 4 * layer + which, 4 * layer + which + 1, stream);
 }
 
 } // namespace q4

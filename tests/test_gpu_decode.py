@@ -233,19 +233,22 @@ def test_streaming_step_unsupported_shapes():
     m = Model(TINY, layers)
     with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
         m.dec.set_persistent(2)  # dff = 96 is not a multiple of 64
-    with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
+    with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
         m.dec.set_persistent(3)
+    with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
+        m.dec.set_persistent(4)
 
 
+@pytest.mark.parametrize("mode", [2, 3])
 @pytest.mark.parametrize("n_layers", [1, 3])
-def test_streaming_step_small_matches_oracle(n_layers):
+def test_streaming_step_small_matches_oracle(n_layers, mode):
     """Streaming persistent step on a small model: eager against the oracle,
     graph replays over every bucket bitwise equal to eager, a token loop
     through one graph against the oracle token by token."""
     layers = make_layers(SMALL, 94, n_layers)
     host = to_host(layers)
     m = Model(SMALL, layers)
-    m.dec.set_persistent(2)
+    m.dec.set_persistent(mode)
     s = torch.cuda.Stream()
     h0 = inputs.residual_f32(SMALL["d"], inputs.seed_of(94, 0, 9))
     m.set_h(h0)
@@ -255,7 +258,7 @@ def test_streaming_step_small_matches_oracle(n_layers):
     m.dec.check()
     h_eager = m.h.cpu().clone()
     ref = oracle_run(host, SMALL, h0.numpy())
-    check_h(h_eager.numpy(), ref[-1][0], ref[-1][1], f"small streaming {n_layers} layers")
+    check_h(h_eager.numpy(), ref[-1][0], ref[-1][1], f"small streaming mode {mode}, {n_layers} layers")
     for ctx in (1, 700, 2048, 4096):
         for rep in range(2):
             m.set_h(h0)
@@ -303,7 +306,7 @@ def test_8b_full_step_graph_matches_oracle():
     s.synchronize()
     assert torch.equal(m.h.cpu(), h_graph), "graph and eager differ"
     outs = {}
-    for mode in (1, 2):
+    for mode in (1, 2, 3):
         m.dec.set_persistent(mode)
         got = []
         for step in (lambda: m.dec.step_eager(s), lambda: m.dec.step_graph(512, s),
@@ -370,7 +373,7 @@ def test_70b_first_layers_and_full_graph():
     check_h(m2.h.cpu().numpy(), ref[-1][0], ref[-1][1], "70b layers 0-1 per-layer kernels")
     # the same two layers through both persistent kernels
     m3 = Model(dims, layers[:2])
-    for mode in (1, 2):
+    for mode in (1, 2, 3):
         m3.dec.set_persistent(mode)
         m3.set_h(h0)
         torch.cuda.synchronize()
