@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
             "q4o_gqa_gather_f16": [P, I, I, I, P],
             "q4o_silu_mul_f16": [P, I, P],
             "q4o_decode_layer": [P, P, P, P, I, I, I, I, I, D, P, P],
+            "q4o_rope": [P, I, I, D],
+            "q4o_attention": [P, I, I, I, I, I, D, P, P, P, P],
+            "q4o_decode_layer_attn": [P, P, P, P, I, I, I, I, I, D, I, I, D, P, P, P, P],
         }.items():
             fn = getattr(L, name)
             fn.restype = None
@@ -208,6 +211,38 @@ def silu_mul_f16(gu) -> np.ndarray:
     return out
 
 
+def rope(x, pos, base=500000.0) -> np.ndarray:
+    """Rotate-half rotary embedding of one head vector at position pos."""
+    x = np.array(x, np.float64, copy=True, order="C")
+    assert x.ndim == 1 and x.size % 2 == 0
+    lib().q4o_rope(_ptr(x), x.size, pos, base)
+    return x
+
+
+def kv_cache(dims, max_ctx):
+    """Empty binary16 K and V caches of one layer, [Hkv][max_ctx][hd]."""
+    shape = (dims["Hkv"], max_ctx, dims["hd"])
+    return np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+
+
+def attention(qkv, dims, pos, kcache, vcache, base=500000.0):
+    """Decode attention at position pos (writes row pos of both caches).
+    Returns (o, mag): fp64 [H*hd] output and sum_j p_j |v_j|."""
+    H, Hkv, hd = dims["H"], dims["Hkv"], dims["hd"]
+    qkv = _c(qkv, np.float64)
+    assert qkv.size == (H + 2 * Hkv) * hd and H % Hkv == 0
+    assert kcache.dtype == np.uint16 and vcache.dtype == np.uint16
+    assert kcache.flags["C_CONTIGUOUS"] and vcache.flags["C_CONTIGUOUS"]
+    assert kcache.shape == vcache.shape and kcache.shape[0] == Hkv and kcache.shape[2] == hd
+    max_ctx = kcache.shape[1]
+    assert 0 <= pos < max_ctx
+    out = np.empty(H * hd, np.float64)
+    mag = np.empty(H * hd, np.float64)
+    lib().q4o_attention(_ptr(qkv), H, Hkv, hd, pos, max_ctx, base, _ptr(kcache),
+                        _ptr(vcache), _ptr(out), _ptr(mag))
+    return out, mag
+
+
 class _Mat(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
@@ -235,4 +270,31 @@ def decode_layer(layer, dims, h, mag_h=None, eps=1e-5):
     lib().q4o_decode_layer(*(ctypes.addressof(m) for m in mats), d, H, Hkv, hd,
                            dff, eps, _ptr(h),
                            _ptr(mag_h) if mag_h is not None else None)
+    return h
+
+
+def decode_layer_attn(layer, dims, h, pos, kcache, vcache, mag_h=None, eps=1e-5,
+                      base=500000.0):
+    """decode_layer with attention over this layer's caches at position pos
+    (row pos of both caches is written)."""
+    d, H, Hkv, hd, dff = (dims[k] for k in ("d", "H", "Hkv", "hd", "dff"))
+    shapes = {"qkv": ((H + 2 * Hkv) * hd, d), "o": (d, H * hd),
+              "gate_up": (2 * dff, d), "down": (d, dff)}
+    keep = []
+    mats = []
+    for name in ("qkv", "o", "gate_up", "down"):
+        p, s, N, K = _check_mat(*layer[name])
+        assert (N, K) == shapes[name], (name, (N, K), shapes[name])
+        keep += [p, s]
+        mats.append(_Mat(p.ctypes.data, s.ctypes.data))
+    assert h.dtype == np.float64 and h.flags["C_CONTIGUOUS"] and h.shape == (d,)
+    assert kcache.shape == vcache.shape == (Hkv, kcache.shape[1], hd)
+    assert kcache.dtype == vcache.dtype == np.uint16
+    max_ctx = kcache.shape[1]
+    assert 0 <= pos < max_ctx
+    if mag_h is not None:
+        assert mag_h.dtype == np.float64 and mag_h.shape == (d,)
+    lib().q4o_decode_layer_attn(*(ctypes.addressof(m) for m in mats), d, H, Hkv, hd,
+                                dff, eps, pos, max_ctx, base, _ptr(kcache), _ptr(vcache),
+                                _ptr(h), _ptr(mag_h) if mag_h is not None else None)
     return h

@@ -273,6 +273,90 @@ void q4o_gqa_gather_f16(const double *qkv, int64_t H, int64_t Hkv,
     }
 }
 
+/* Rotary position embedding, rotate-half form: for i < hd/2, dims i and
+ * i + hd/2 of a head vector turn by the angle pos * base^(-2i/hd). */
+void q4o_rope(double *x, int64_t hd, int64_t pos, double base)
+{
+    int64_t half = hd / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double ang = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
+        double c = cos(ang), s = sin(ang);
+        double a = x[i], b = x[i + half];
+        x[i] = a * c - b * s;
+        x[i + half] = a * s + b * c;
+    }
+}
+
+/*
+ * Decode attention of one token at position pos with grouped-query heads
+ * (query head hq reads key/value head hq / (H / Hkv)).  qkv holds Q | K | V
+ * for this token.  The rotated key and the value are first stored, rounded
+ * to binary16, into row pos of the caches (layout [Hkv][max_ctx][hd]); then
+ * every query head, rotated at pos, attends over rows 0..pos of its
+ * group's caches:
+ *     s_j = (q . k_j) / sqrt(hd),   p = softmax(s),   o = sum_j p_j v_j.
+ * out: o (fp64, [H*hd]); mag (may be NULL): sum_j p_j |v_j| per element,
+ * the scale of the rounding error of an fp32 evaluation.
+ */
+void q4o_attention(const double *qkv, int64_t H, int64_t Hkv, int64_t hd,
+                   int64_t pos, int64_t max_ctx, double base,
+                   uint16_t *kcache, uint16_t *vcache, double *out, double *mag)
+{
+    int64_t per_group = H / Hkv;
+    double *q = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *k = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(pos + 1));
+    for (int64_t g = 0; g < Hkv; ++g) {
+        const double *kn = qkv + (H + g) * hd;
+        const double *vn = qkv + (H + Hkv + g) * hd;
+        for (int64_t i = 0; i < hd; ++i)
+            k[i] = kn[i];
+        q4o_rope(k, hd, pos, base);
+        uint16_t *krow = kcache + (g * max_ctx + pos) * hd;
+        uint16_t *vrow = vcache + (g * max_ctx + pos) * hd;
+        for (int64_t i = 0; i < hd; ++i) {
+            krow[i] = q4o_f64_to_f16(k[i]);
+            vrow[i] = q4o_f64_to_f16(vn[i]);
+        }
+    }
+    double scale = 1.0 / sqrt((double)hd);
+    for (int64_t hq = 0; hq < H; ++hq) {
+        int64_t g = hq / per_group;
+        for (int64_t i = 0; i < hd; ++i)
+            q[i] = qkv[hq * hd + i];
+        q4o_rope(q, hd, pos, base);
+        double smax = -INFINITY;
+        for (int64_t j = 0; j <= pos; ++j) {
+            const uint16_t *kr = kcache + (g * max_ctx + j) * hd;
+            double dot = 0.0;
+            for (int64_t i = 0; i < hd; ++i)
+                dot += q[i] * q4o_f16_to_f64(kr[i]);
+            s[j] = dot * scale;
+            if (s[j] > smax)
+                smax = s[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j <= pos; ++j) {
+            s[j] = exp(s[j] - smax);
+            sum += s[j];
+        }
+        for (int64_t i = 0; i < hd; ++i) {
+            double acc = 0.0, m = 0.0;
+            for (int64_t j = 0; j <= pos; ++j) {
+                double v = q4o_f16_to_f64(vcache[(g * max_ctx + j) * hd + i]);
+                acc += (s[j] / sum) * v;
+                m += (s[j] / sum) * fabs(v);
+            }
+            out[hq * hd + i] = acc;
+            if (mag)
+                mag[hq * hd + i] = m;
+        }
+    }
+    free(q);
+    free(k);
+    free(s);
+}
+
 /* mlp[j] = f16(silu(gate[j]) * up[j]), gate | up stacked in gu. */
 void q4o_silu_mul_f16(const double *gu, int64_t dff, uint16_t *out)
 {
@@ -303,6 +387,56 @@ typedef struct {
  * sum_k |w*x| of the two products added into h, which bounds how far a
  * correctly rounded fp32 evaluation may drift from this fp64 one.
  */
+/*
+ * The same layer with attention over the caches in place of the one-token
+ * stand-in: o = f16(attention at position pos) (q4o_attention; the caches
+ * of this layer gain row pos).  Everything else as q4o_decode_layer.
+ */
+void q4o_decode_layer_attn(const q4o_mat *qkv_m, const q4o_mat *o_m,
+                           const q4o_mat *gu_m, const q4o_mat *down_m,
+                           int64_t d, int64_t H, int64_t Hkv, int64_t hd,
+                           int64_t dff, double eps, int64_t pos, int64_t max_ctx,
+                           double base, uint16_t *kcache, uint16_t *vcache,
+                           double *h, double *mag_h)
+{
+    int64_t nqkv = (H + 2 * Hkv) * hd;
+    uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(d > dff ? d : dff));
+    uint16_t *o = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(H * hd));
+    double *att = (double *)malloc(sizeof(double) * (size_t)(H * hd));
+    double *qkv = (double *)malloc(sizeof(double) * (size_t)nqkv);
+    double *gu = (double *)malloc(sizeof(double) * (size_t)(2 * dff));
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    double *m = (double *)malloc(sizeof(double) * (size_t)d);
+
+    q4o_rmsnorm_f16(h, d, eps, a);
+    q4o_gemv(qkv_m->packed, qkv_m->scales, a, nqkv, d, qkv, NULL);
+    q4o_attention(qkv, H, Hkv, hd, pos, max_ctx, base, kcache, vcache, att, NULL);
+    for (int64_t i = 0; i < H * hd; ++i)
+        o[i] = q4o_f64_to_f16(att[i]);
+    q4o_gemv(o_m->packed, o_m->scales, o, d, H * hd, y, m);
+    for (int64_t i = 0; i < d; ++i) {
+        h[i] += y[i];
+        if (mag_h)
+            mag_h[i] += m[i];
+    }
+    q4o_rmsnorm_f16(h, d, eps, a);
+    q4o_gemv(gu_m->packed, gu_m->scales, a, 2 * dff, d, gu, NULL);
+    q4o_silu_mul_f16(gu, dff, a);
+    q4o_gemv(down_m->packed, down_m->scales, a, d, dff, y, m);
+    for (int64_t i = 0; i < d; ++i) {
+        h[i] += y[i];
+        if (mag_h)
+            mag_h[i] += m[i];
+    }
+    free(a);
+    free(o);
+    free(att);
+    free(qkv);
+    free(gu);
+    free(y);
+    free(m);
+}
+
 void q4o_decode_layer(const q4o_mat *qkv_m, const q4o_mat *o_m,
                       const q4o_mat *gu_m, const q4o_mat *down_m,
                       int64_t d, int64_t H, int64_t Hkv, int64_t hd,

@@ -289,3 +289,127 @@ def test_decode_layer_routing_hand_built():
     mlp = (a2 * expit(a2) * -a2).astype(np.float16).astype(np.float64)
     expect = h1 + mlp
     np.testing.assert_allclose(h, expect, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- attention
+# Decode attention over binary16 caches with rotary positions is not on the
+# pages (the next step around the products); the pins below fix it by
+# closed forms, by its reduction to the one-token stand-in at position 0,
+# and by invariants of the rotation.
+
+def test_rope_hand_case_and_invariants():
+    # hd = 2: the single pair turns by pos * base^0 = pos radians
+    got = oracle.rope([1.0, 0.0], 1, 10.0)
+    assert np.allclose(got, [np.cos(1.0), np.sin(1.0)], rtol=0, atol=1e-15)
+    # hd = 4, base 100: pair (1, 3) turns by pos * 100^(-1/2) = pos / 10
+    got = oracle.rope([0.0, 1.0, 0.0, 0.0], 5, 100.0)
+    assert np.allclose(got, [0.0, np.cos(0.5), 0.0, np.sin(0.5)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(128)
+    assert np.array_equal(oracle.rope(x, 0), x)                     # position 0: identity
+    y = oracle.rope(x, 37)
+    pairs = lambda v: v[:64] ** 2 + v[64:] ** 2
+    assert np.allclose(pairs(y), pairs(x), rtol=1e-13)              # each pair keeps its norm
+    assert np.allclose(oracle.rope(oracle.rope(x, 11), 26), y, rtol=0, atol=1e-9)  # a then b = a+b
+
+
+ATT_DIMS = dict(H=4, Hkv=2, hd=8)
+
+
+def _qkv(rng, dims=ATT_DIMS):
+    return rng.standard_normal((dims["H"] + 2 * dims["Hkv"]) * dims["hd"])
+
+
+def test_attention_at_position_zero_is_the_one_token_gather():
+    rng = np.random.default_rng(2)
+    qkv = _qkv(rng)
+    k, v = oracle.kv_cache(ATT_DIMS, 16)
+    o, _ = oracle.attention(qkv, ATT_DIMS, 0, k, v)
+    assert np.array_equal(oracle.f64_to_f16(o),
+                          oracle.gqa_gather_f16(qkv, ATT_DIMS["H"], ATT_DIMS["Hkv"],
+                                                ATT_DIMS["hd"]))
+
+
+def test_attention_writes_rotated_key_and_value_rows():
+    rng = np.random.default_rng(3)
+    qkv = _qkv(rng)
+    H, Hkv, hd = ATT_DIMS["H"], ATT_DIMS["Hkv"], ATT_DIMS["hd"]
+    k, v = oracle.kv_cache(ATT_DIMS, 16)
+    oracle.attention(qkv, ATT_DIMS, 9, k, v)
+    for g in range(Hkv):
+        kn = qkv[(H + g) * hd:(H + g + 1) * hd]
+        vn = qkv[(H + Hkv + g) * hd:(H + Hkv + g + 1) * hd]
+        assert np.array_equal(k[g, 9], oracle.f64_to_f16(oracle.rope(kn, 9)))
+        assert np.array_equal(v[g, 9], oracle.f64_to_f16(vn))
+    assert not k[:, :9].any() and not k[:, 10:].any()               # other rows untouched
+
+
+def test_attention_equal_keys_average_the_values():
+    rng = np.random.default_rng(4)
+    qkv = _qkv(rng)
+    H, Hkv, hd = ATT_DIMS["H"], ATT_DIMS["Hkv"], ATT_DIMS["hd"]
+    pos = 6
+    k, v = oracle.kv_cache(ATT_DIMS, 16)
+    for g in range(Hkv):
+        kn = qkv[(H + g) * hd:(H + g + 1) * hd]
+        k[g, :pos] = oracle.f64_to_f16(oracle.rope(kn, pos))        # the key this token writes
+        v[g, :pos] = oracle.f64_to_f16(rng.standard_normal((pos, hd)))
+    o, _ = oracle.attention(qkv, ATT_DIMS, pos, k, v)
+    for hq in range(H):
+        g = hq // (H // Hkv)
+        want = oracle.f16_to_f64(v[g, :pos + 1]).mean(axis=0)
+        assert np.allclose(o[hq * hd:(hq + 1) * hd], want, rtol=0, atol=1e-12)
+
+
+def test_attention_dominant_key_selects_its_value():
+    rng = np.random.default_rng(5)
+    H, Hkv, hd = ATT_DIMS["H"], ATT_DIMS["Hkv"], ATT_DIMS["hd"]
+    pos = 3
+    qkv = np.zeros((H + 2 * Hkv) * hd)
+    qkv[0] = 100.0                  # query head 0 (group 0): along dim 0 before rotation
+    k, v = oracle.kv_cache(ATT_DIMS, 8)
+    v[0, :pos] = oracle.f64_to_f16(rng.standard_normal((pos, hd)))
+    # row 1 of group 0 holds the rotated query direction, scaled: score 2^11 * 100 / sqrt(8)
+    kdir = oracle.rope(np.eye(hd)[0], pos)
+    k[0, 1] = oracle.f64_to_f16(kdir * 2048.0)
+    o, _ = oracle.attention(qkv, ATT_DIMS, pos, k, v)
+    assert np.allclose(o[:hd], oracle.f16_to_f64(v[0, 1]), rtol=0, atol=1e-12)
+
+
+def test_attention_layer_at_position_zero_equals_stand_in_layer():
+    dims = dict(d=64, H=4, Hkv=2, hd=16, dff=96)
+    rng = np.random.default_rng(6)
+    layer = {}
+    for name, (N, K) in {"qkv": (128, 64), "o": (64, 64), "gate_up": (192, 64),
+                         "down": (64, 96)}.items():
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        scales = oracle.f64_to_f16(np.abs(rng.standard_normal((N, K // 32))) * 0.02)
+        layer[name] = (oracle.pack(codes), scales)
+    h0 = rng.standard_normal(64)
+    h1, m1 = h0.copy(), np.zeros(64)
+    oracle.decode_layer(layer, dims, h1, m1)
+    h2, m2 = h0.copy(), np.zeros(64)
+    k, v = oracle.kv_cache(dims, 4)
+    oracle.decode_layer_attn(layer, dims, h2, 0, k, v, m2)
+    assert np.array_equal(h1, h2) and np.array_equal(m1, m2)
+
+
+def test_attention_two_positions_logistic_weights():
+    """Two positions: the weights are the logistic function of the score
+    difference, with scores (rotated q . k) / sqrt(hd); a 1/hd or unscaled
+    score, or a dropped rotation of q, fails this."""
+    rng = np.random.default_rng(7)
+    H, Hkv, hd = ATT_DIMS["H"], ATT_DIMS["Hkv"], ATT_DIMS["hd"]
+    qkv = _qkv(rng) * 2.0
+    k, v = oracle.kv_cache(ATT_DIMS, 4)
+    k[:, 0] = oracle.f64_to_f16(rng.standard_normal((Hkv, hd)) * 2.0)
+    v[:, 0] = oracle.f64_to_f16(rng.standard_normal((Hkv, hd)))
+    o, _ = oracle.attention(qkv, ATT_DIMS, 1, k, v)
+    for hq in range(H):
+        g = hq // (H // Hkv)
+        qr = oracle.rope(qkv[hq * hd:(hq + 1) * hd], 1)
+        s0 = qr @ oracle.f16_to_f64(k[g, 0]) / np.sqrt(hd)
+        s1 = qr @ oracle.f16_to_f64(k[g, 1]) / np.sqrt(hd)
+        p1 = 1.0 / (1.0 + np.exp(s0 - s1))
+        want = (1 - p1) * oracle.f16_to_f64(v[g, 0]) + p1 * oracle.f16_to_f64(v[g, 1])
+        assert np.allclose(o[hq * hd:(hq + 1) * hd], want, rtol=0, atol=1e-12)
