@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 typedef int32_t q4_status;
 #define Q4_OK 0
@@ -162,6 +162,22 @@ typedef struct {
      * and the device layer table (n_layers entries of 64 bytes). */
     void *workspace;
     size_t workspace_bytes;    /* >= q4_decoder_workspace_bytes() */
+    /* Attention over a KV cache, optional (PipeLLM, "Layer 1: CUDA Graph
+     * Compilation": graphs per sequence-length bucket; PIPO, "Method",
+     * "Pipeline design": KV cache state beside the weights).  NULL: the
+     * one-token stand-in described below.  Otherwise device binary16 caches,
+     * 16-byte aligned, retained, 2 * n_layers * n_kv_heads * max_ctx *
+     * head_dim elements: for layer l the keys at element offset
+     * 2*l*S and the values at (2*l + 1)*S, S = n_kv_heads*max_ctx*head_dim,
+     * each laid out [n_kv_heads][max_ctx][head_dim].  A step at context
+     * length c stores the current token's rotated key and its value in row
+     * c - 1 and attends over rows 0..c-1.  With a cache the workspace also
+     * holds, after the layer table, a position word (256 bytes) and the
+     * per-chunk attention partials.  Needs n_heads / n_kv_heads in {1, 2, 4,
+     * 8} and head_dim 64 or 128; only the four-kernels step (mode 0). */
+    void *kv_cache;
+    int32_t max_ctx;           /* rows per cache, >= 1 */
+    float rope_base;           /* rotary base (theta), > 0, e.g. 500000 */
 } q4_model_desc;
 
 /*
@@ -181,7 +197,8 @@ q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out);
  * and satisfy the q4_gemv limits.  With resident layers it also writes, with
  * synchronous copies, a device copy of the layer table and zeroed barrier
  * words into the workspace; the step starts as four kernels per layer (the
- * persistent step below is opt-in).  Without layers no GPU work. */
+ * persistent step below is opt-in).  With a KV cache it zeroes the position
+ * word (context length 1).  Otherwise no GPU work. */
 q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
 /* Step implementation for resident layers (cached graphs are dropped on a
  * change):
@@ -199,7 +216,8 @@ q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
  *     product (four per layer, no grid barriers; same limits as mode 2).
  * Each output is the same dot product within the same bound; the summation
  * order, and so the low bits, differ between implementations.  INVALID_ARG
- * for another mode, STATE without resident layers. */
+ * for another mode, STATE without resident layers, UNSUPPORTED for modes
+ * 1-3 on a decoder with a KV cache. */
 q4_status q4_decoder_set_persistent(void *dec, int32_t mode);
 /* After the stream has completed a persistent step (mode 1 or 2): Q4_OK, or
  * Q4_ERR_HIP if a bounded wait (grid barrier, ring slot, ring space) gave up
@@ -210,9 +228,15 @@ q4_status q4_decoder_check(void *dec);
  * bucket captures the layer loop into a HIP graph on `stream` (which must
  * not be the NULL stream), later calls replay it.  ctx_len <= 0 is
  * INVALID_ARG, ctx_len > 4096 is UNSUPPORTED.  Graphs bake in every pointer
- * of the description: those buffers must outlive the decoder. */
+ * of the description: those buffers must outlive the decoder.  With a KV
+ * cache, ctx_len above max_ctx is INVALID_ARG; the call first enqueues the
+ * write of the position word (ctx_len - 1), outside the graph, and the
+ * graph's attention covers min(bucket, max_ctx) positions, of which those
+ * past the position contribute nothing. */
 q4_status decode_step_graph(void *dec, int32_t ctx_len, hipStream_t stream);
-/* Same layer loop, enqueued eagerly without a graph (for checking). */
+/* Same layer loop, enqueued eagerly without a graph (for checking); with a
+ * KV cache at the context length of the last q4_decoder_set_context
+ * (or decode_step_graph) call, 1 before any. */
 q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
 /* Layer-wise profiling (PipeLLM, "Layer 2: Asynchronous Weight
  * Prefetching" lists per-layer analysis and event-based timing among its
@@ -220,7 +244,9 @@ q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
  * every kernel.  Writes each kernel's duration in milliseconds to the host
  * array ms_out in launch order -- per layer: QKV (with the first norm), O,
  * gate+up (with the second norm and the SiLU gate), down: 4 per layer --
- * and their count to *n_out.  capacity must be at least 4 * n_layers.
+ * and their count to *n_out.  With a KV cache the attention kernels get a
+ * mark of their own after QKV: 5 per layer.  capacity must be at least that
+ * count times n_layers.
  * Synchronises `stream` before returning. */
 q4_status q4_decode_step_profiled(void *dec, hipStream_t stream, float *ms_out,
                                   int32_t capacity, int32_t *n_out);
@@ -228,15 +254,26 @@ q4_status q4_decode_step_profiled(void *dec, hipStream_t stream, float *ms_out,
  * (which: 0 QKV, 1 O, 2 gate+up, 3 down), launched `reps` times back to back
  * on `stream` between two timing events, cycling through the resident
  * layers so no launch rereads cached weights.  The O and down kernels add
- * into h on every launch: h is clobbered.  Synchronises `stream`. */
+ * into h on every launch: h is clobbered.  QKV is timed without attention.
+ * Synchronises `stream`. */
 q4_status q4_decode_kernel_time(void *dec, int32_t which, int32_t reps,
                                 hipStream_t stream, float *avg_us);
-/* One layer, eagerly, with the weights given (e.g. a streamed slot). */
+/* One layer, eagerly, with the weights given (e.g. a streamed slot).  With a
+ * KV cache, layers driven one at a time must come in order 0..n_layers-1
+ * per token (the cache slice follows that order); q4_decoder_set_context
+ * or a completed token restarts it at layer 0. */
 q4_status q4_decode_layer(void *dec, const q4_layer *layer, hipStream_t stream);
+/* Decoders with a KV cache: sets the context length (1..max_ctx) of the
+ * next eager step or layer-by-layer token and enqueues, on `stream`, the
+ * write of the position word the attention kernels read.  decode_step_graph
+ * does this itself.  Without a cache: STATE. */
+q4_status q4_decoder_set_context(void *dec, int32_t ctx_len, hipStream_t stream);
 /* One product of a layer, eagerly: which = 0 QKV (RMSNorm of h, V gather
  * into the attention output), 1 O (h += ...), 2 gate+up (RMSNorm of h, its
  * binary16 result kept in the workspace, SiLU gate into the MLP activation),
- * 3 down (h += ...).  Calling 0..3 in order equals q4_decode_layer; single
+ * 3 down (h += ...).  With a KV cache, 0 is followed by attention over the
+ * cache slice of the current layer (which advances after 3).  Calling 0..3
+ * in order equals q4_decode_layer; single
  * products let a caller inspect every intermediate (the workspace sections
  * listed above).  INVALID_ARG for another index or bad shapes. */
 q4_status q4_decode_layer_part(void *dec, const q4_layer *layer, int32_t which,
@@ -290,7 +327,9 @@ q4_status q4_wstream_destroy(void *ws);
  * is begun (unless already begun by the previous token), then for each
  * layer l the copy of l+1 is begun before l is waited and computed on
  * `compute`.  The blob layout must be q4_layer_blob_layout of the decoder's
- * shapes.  The copy of the next token's layer 0 is begun at the end. */
+ * shapes.  The copy of the next token's layer 0 is begun at the end.  With
+ * a KV cache layer l attends over cache slice l at the context length set
+ * by q4_decoder_set_context. */
 q4_status q4_decode_token_streamed(void *dec, void *ws, hipStream_t compute);
 
 #ifdef __cplusplus

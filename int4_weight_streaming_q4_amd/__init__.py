@@ -47,7 +47,8 @@ class ModelDesc(ctypes.Structure):
     _fields_ = [("n_layers", _I32), ("d_model", _I32), ("n_heads", _I32),
                 ("n_kv_heads", _I32), ("head_dim", _I32), ("d_ff", _I32),
                 ("eps", ctypes.c_float), ("layers", ctypes.POINTER(Layer)),
-                ("h", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+                ("h", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("kv_cache", _P), ("max_ctx", _I32), ("rope_base", ctypes.c_float)]
 
 
 class WStreamDesc(ctypes.Structure):
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "q4_decoder_destroy": (S, [_P]),
         "q4_decoder_set_persistent": (S, [_P, _I32]),
         "q4_decoder_check": (S, [_P]),
+        "q4_decoder_set_context": (S, [_P, _I32, _P]),
         "q4_layer_blob_layout": (S, [ctypes.POINTER(Layer), ctypes.c_size_t * 8,
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "q4_layer_from_blob": (S, [ctypes.POINTER(Layer), _P, ctypes.POINTER(Layer)]),
@@ -204,14 +206,26 @@ def layer_blob_layout(dims: dict):
     return list(offs), total.value
 
 
-def _model_desc(dims, n_layers, layers_arr, h, workspace, ws_bytes, eps):
+def _model_desc(dims, n_layers, layers_arr, h, workspace, ws_bytes, eps, kv_cache=None,
+                max_ctx=0, rope_base=500000.0):
     return ModelDesc(n_layers, dims["d"], dims["H"], dims["Hkv"], dims["hd"], dims["dff"],
-                     eps, layers_arr, _ptr(h), _ptr(workspace), ws_bytes)
+                     eps, layers_arr, _ptr(h), _ptr(workspace), ws_bytes, _ptr(kv_cache),
+                     int(max_ctx), float(rope_base))
 
 
-def workspace_bytes(dims: dict, n_layers: int = None, eps: float = 1e-5) -> int:
+def kv_cache_elems(dims: dict, n_layers: int, max_ctx: int) -> int:
+    """binary16 elements of a decoder's KV cache: per layer K then V, each
+    [Hkv][max_ctx][hd]."""
+    return 2 * n_layers * dims["Hkv"] * max_ctx * dims["hd"]
+
+
+def workspace_bytes(dims: dict, n_layers: int = None, eps: float = 1e-5,
+                    max_ctx: int = 0) -> int:
+    """Workspace bytes of a decoder; max_ctx > 0 sizes it for a KV cache of
+    that many rows (the attention partials)."""
     n = n_layers if n_layers is not None else dims.get("n_layers", 1)
-    desc = _model_desc(dims, n, None, 0, 0, 0, eps)
+    # a non-NULL stand-in: only the sizes of a cache are read here
+    desc = _model_desc(dims, n, None, 0, 0, 0, eps, 256 if max_ctx > 0 else None, max_ctx)
     out = ctypes.c_size_t()
     _check(lib().q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
     return out.value
@@ -223,15 +237,18 @@ class Decoder:
     residual and ``workspace`` a device uint8 tensor of workspace_bytes()."""
 
     def __init__(self, dims: dict, layers, h, workspace, eps: float = 1e-5,
-                 n_layers=None):
+                 n_layers=None, kv_cache=None, max_ctx: int = 0,
+                 rope_base: float = 500000.0):
         self.dims = dict(dims)
         n = len(layers) if layers is not None else (n_layers or dims.get("n_layers", 1))
         arr = None
         if layers is not None:
             arr = (Layer * n)(*(make_layer(w) for w in layers))
-        self._keep = (layers, h, workspace, arr)  # buffers the graphs bake in
+        self._keep = (layers, h, workspace, arr, kv_cache)  # buffers the graphs bake in
         self._n_layers = n
-        desc = _model_desc(dims, n, arr, h, workspace, workspace.numel(), eps)
+        self._has_kv = kv_cache is not None
+        desc = _model_desc(dims, n, arr, h, workspace, workspace.numel(), eps, kv_cache,
+                           max_ctx, rope_base)
         handle = _P()
         _check(lib().q4_decoder_create(ctypes.byref(desc), ctypes.byref(handle)))
         self.handle = handle.value
@@ -245,6 +262,11 @@ class Decoder:
         workgroups with one launch per product."""
         _check(lib().q4_decoder_set_persistent(self.handle, int(mode)))
 
+    def set_context(self, ctx_len: int, stream=None):
+        """Context length of the next eager step or layer-by-layer token
+        (decoders with a KV cache)."""
+        _check(lib().q4_decoder_set_context(self.handle, int(ctx_len), _stream(stream)))
+
     def check(self):
         """Raise if a persistent step's grid barrier timed out (synchronous)."""
         _check(lib().q4_decoder_check(self.handle))
@@ -254,9 +276,10 @@ class Decoder:
 
     def step_profiled(self, stream=None):
         """Eager step; returns per-kernel durations in ms (4 per layer: QKV,
-        O, gate+up, down)."""
+        O, gate+up, down; with a KV cache 5: QKV, attention, O, gate+up,
+        down)."""
         n_layers = self._n_layers
-        cap = 4 * n_layers
+        cap = (5 if self._has_kv else 4) * n_layers
         buf = (ctypes.c_float * cap)()
         n = _I32()
         _check(lib().q4_decode_step_profiled(self.handle, _stream(stream), buf, cap,

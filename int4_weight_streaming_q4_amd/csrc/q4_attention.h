@@ -1,0 +1,25 @@
+// Decode attention over binary16 KV caches (internal interface).
+#pragma once
+
+#include "q4_internal.h"
+
+namespace q4 {
+
+struct AttnArgs {
+    const float *qkv;       // this token's Q | K | V (fp32)
+    uint16_t *kc, *vc;      // this layer's caches, [Hkv][max_ctx][hd] binary16
+    const int32_t *pos_dev; // device word: position of the token (context - 1)
+    int32_t max_ctx, H, Hkv, hd;
+    float rope_base;
+    float *part;            // partials, attention_partial_bytes()
+    int32_t nchunk;         // chunks launched (covers the context bucket)
+    uint16_t *out;          // binary16 [H * hd] attention output
+};
+
+bool attention_supported(int32_t H, int32_t Hkv, int32_t hd);
+size_t attention_partial_bytes(int32_t H, int32_t Hkv, int32_t hd, int32_t max_ctx);
+int attention_chunks(int32_t ctx_len);
+q4_status launch_set_pos(int32_t *pos_dev, int32_t pos, hipStream_t s);
+q4_status launch_attention(const AttnArgs &a, hipStream_t s);
+
+} // namespace q4

@@ -21,6 +21,7 @@
 
 #include "q4_internal.h"
 #include "q4_persistent.h"
+#include "q4_attention.h"
 
 namespace q4 {
 namespace {
@@ -47,6 +48,13 @@ struct Decoder {
     int32_t mode = 0; // 0 four kernels per layer, 1 persistent, 2 streaming persistent,
                       // 3 streaming workgroups, one launch per product
     hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
+    // attention over the KV cache (kv == nullptr: one-token stand-in)
+    uint16_t *kv = nullptr;
+    int32_t *pos_dev = nullptr;  // position word the attention kernels read
+    float *att_part = nullptr;   // per-chunk partials
+    int32_t ctx = 1;             // context length of eager / layer-by-layer steps
+    int32_t att_chunks = 1;      // chunks the attention kernels cover
+    int32_t cursor = 0;          // next layer of a layer-by-layer token
 };
 
 q4_status dims_of(const q4_model_desc *m, Dims *out) {
@@ -69,13 +77,30 @@ q4_status dims_of(const q4_model_desc *m, Dims *out) {
     if (d.d % 32 || (d.H * d.hd) % 32 || d.dff % 32)
         return fail(Q4_ERR_INVALID_ARG,
                     "decoder: d_model, n_heads*head_dim and d_ff must be multiples of 32");
+    if (m->kv_cache) {
+        if (!aligned(m->kv_cache, 16))
+            return fail(Q4_ERR_INVALID_ARG, "decoder: kv_cache not 16-byte aligned");
+        if (m->max_ctx < 1)
+            return fail(Q4_ERR_INVALID_ARG, "decoder: max_ctx %d < 1", m->max_ctx);
+        if (!(m->rope_base > 0.0f))
+            return fail(Q4_ERR_INVALID_ARG, "decoder: rope_base must be > 0");
+        if (!attention_supported(m->n_heads, m->n_kv_heads, m->head_dim))
+            return fail(Q4_ERR_UNSUPPORTED,
+                        "decoder: attention needs n_heads/n_kv_heads in {1,2,4,8} and head_dim "
+                        "64 or 128");
+    }
     *out = d;
     return Q4_OK;
 }
 
-size_t workspace_bytes(const Dims &d, int64_t n_layers) {
-    return align256(std::max(d.d, d.dff) * 2) + align256(d.nqkv * 4) + align256(d.H * d.hd * 2) +
-           align256(d.dff * 2) + kBarBytes + align256((size_t)n_layers * sizeof(DevLayer));
+size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) {
+    size_t b = align256(std::max(d.d, d.dff) * 2) + align256(d.nqkv * 4) +
+               align256(d.H * d.hd * 2) + align256(d.dff * 2) + kBarBytes +
+               align256((size_t)n_layers * sizeof(DevLayer));
+    if (m && m->kv_cache)
+        b += 256 + align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv,
+                                                    (int32_t)d.hd, m->max_ctx));
+    return b;
 }
 
 void layer_shapes(const Dims &d, q4_layer *s) {
@@ -123,7 +148,31 @@ struct Marks {
 // The four kernels of a layer, in order.
 enum Kern { kQkv = 0, kO = 1, kGateUp = 2, kDown = 3 };
 
-q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int which, hipStream_t s) {
+// Attention of layer `layer` over its cache slice, after the QKV product.
+q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s) {
+    const Dims &d = dec->dims;
+    const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
+    AttnArgs a{};
+    a.qkv = dec->qkv;
+    a.kc = dec->kv + 2 * (size_t)layer * S;
+    a.vc = a.kc + S;
+    a.pos_dev = dec->pos_dev;
+    a.max_ctx = dec->desc.max_ctx;
+    a.H = (int32_t)d.H;
+    a.Hkv = (int32_t)d.Hkv;
+    a.hd = (int32_t)d.hd;
+    a.rope_base = dec->desc.rope_base;
+    a.part = dec->att_part;
+    a.nchunk = dec->att_chunks;
+    a.out = dec->oin;
+    return launch_attention(a, s);
+}
+
+// One product of a layer; `layer` >= 0 names its cache slice: with a KV
+// cache the QKV product is followed by attention over that slice (layer < 0:
+// the product alone, for timing).
+q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int32_t layer, int which,
+                         hipStream_t s) {
     const Dims &d = dec->dims;
     float *h = dec->desc.h;
     EpiArgs ea{};
@@ -131,15 +180,18 @@ q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int which, hipStream_t
     case kQkv:
         // QKV with the first RMSNorm in its prologue; V rows also land, as
         // binary16, in the attention output of every query head of their
-        // group.
+        // group (the one-token output; attention overwrites it).
         ea.y = dec->qkv;
         ea.out16 = dec->oin;
         ea.v_off = (d.H + d.Hkv) * d.hd;
         ea.hd = (int32_t)d.hd;
         ea.group = (int32_t)(d.H / d.Hkv);
         ea.eps = dec->desc.eps;
-        return launch_gemv(L.qkv.packed, L.qkv.scales, h, Pro::RmsNorm, L.qkv.N, L.qkv.K,
-                           Epi::QkvGather, ea, s);
+        Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, h, Pro::RmsNorm, L.qkv.N, L.qkv.K,
+                             Epi::QkvGather, ea, s));
+        if (dec->kv && layer >= 0)
+            return enqueue_attention(dec, layer, s);
+        return Q4_OK;
     case kO:
         ea.y = h;
         return launch_gemv(L.o.packed, L.o.scales, dec->oin, Pro::F16, L.o.N, L.o.K,
@@ -161,11 +213,16 @@ q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int which, hipStream_t
     return fail(Q4_ERR_INVALID_ARG, "decoder: kernel index %d", which);
 }
 
-// Enqueue one layer on `s`: four kernels.
-q4_status enqueue_layer(Decoder *dec, const q4_layer &L, hipStream_t s, Marks marks = {}) {
+// Enqueue layer `layer` on `s`: four products (plus attention with a cache).
+q4_status enqueue_layer(Decoder *dec, const q4_layer &L, int32_t layer, hipStream_t s,
+                        Marks marks = {}) {
     for (int k = kQkv; k <= kDown; ++k) {
-        Q4_CHECK(enqueue_kernel(dec, L, k, s));
+        Q4_CHECK(enqueue_kernel(dec, L, -1, k, s));
         Q4_CHECK(marks.mark(s));
+        if (k == kQkv && dec->kv && layer >= 0) {
+            Q4_CHECK(enqueue_attention(dec, layer, s));
+            Q4_CHECK(marks.mark(s));
+        }
     }
     return Q4_OK;
 }
@@ -196,7 +253,7 @@ q4_status enqueue_all(Decoder *dec, hipStream_t s) {
         return dec->mode == 2 ? launch_stream(a, s) : launch_persistent(a, s);
     }
     for (size_t l = 0; l < dec->layers.size(); ++l)
-        Q4_CHECK(enqueue_layer(dec, dec->layers[l], s));
+        Q4_CHECK(enqueue_layer(dec, dec->layers[l], (int32_t)l, s));
     return Q4_OK;
 }
 
@@ -240,7 +297,7 @@ extern "C" q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *
     Q4_CHECK(q4::dims_of(m, &d));
     if (!out)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_workspace_bytes: null out");
-    *out = q4::workspace_bytes(d, m->n_layers);
+    *out = q4::workspace_bytes(d, m->n_layers, m);
     return Q4_OK;
 }
 
@@ -256,9 +313,9 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     if (!m->workspace || !q4::aligned(m->workspace, 256))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decoder_create: workspace null or not 256-byte aligned");
-    if (m->workspace_bytes < q4::workspace_bytes(d, m->n_layers))
+    if (m->workspace_bytes < q4::workspace_bytes(d, m->n_layers, m))
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_create: workspace of %zu bytes < %zu",
-                        m->workspace_bytes, q4::workspace_bytes(d, m->n_layers));
+                        m->workspace_bytes, q4::workspace_bytes(d, m->n_layers, m));
     if (m->layers) {
         for (int32_t l = 0; l < m->n_layers; ++l)
             Q4_CHECK(q4::check_layer(d, m->layers[l], l));
@@ -283,6 +340,20 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     dec->bar = reinterpret_cast<uint32_t *>(ws);
     ws += q4::kBarBytes;
     dec->dev_layers = reinterpret_cast<q4::DevLayer *>(ws);
+    ws += q4::align256((size_t)m->n_layers * sizeof(q4::DevLayer));
+    if (m->kv_cache) {
+        dec->kv = static_cast<uint16_t *>(m->kv_cache);
+        dec->pos_dev = reinterpret_cast<int32_t *>(ws);
+        ws += 256;
+        dec->att_part = reinterpret_cast<float *>(ws);
+        // context length 1 until the caller sets another
+        hipError_t e = hipMemset(dec->pos_dev, 0, 256);
+        if (e != hipSuccess) {
+            delete dec;
+            return q4::fail(Q4_ERR_HIP, "q4_decoder_create: position word: %s",
+                            hipGetErrorString(e));
+        }
+    }
     if (m->layers) {
         // Resident layers: the persistent kernel reads a device copy of the
         // layer table and keeps its barrier words next to it.
@@ -319,6 +390,7 @@ extern "C" q4_status q4_decode_step_eager(void *decp, hipStream_t stream) {
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_eager: null decoder");
     if (dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "q4_decode_step_eager: decoder has no resident layers");
+    dec->att_chunks = q4::attention_chunks(dec->ctx);
     return q4::enqueue_all(dec, stream);
 }
 
@@ -335,10 +407,21 @@ extern "C" q4_status decode_step_graph(void *decp, int32_t ctx_len, hipStream_t 
         return q4::fail(Q4_ERR_INVALID_ARG, "decode_step_graph: capture needs a non-NULL stream");
     if (dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "decode_step_graph: decoder has no resident layers");
+    if (dec->kv && ctx_len > dec->desc.max_ctx)
+        return q4::fail(Q4_ERR_INVALID_ARG, "decode_step_graph: ctx_len=%d above max_ctx %d",
+                        ctx_len, dec->desc.max_ctx);
     int b = 0;
     while (q4::kBuckets[b] < ctx_len)
         ++b;
+    if (dec->kv) {
+        // The position word sits outside the graph: one graph per bucket
+        // serves every context length in it.
+        Q4_CHECK(q4::launch_set_pos(dec->pos_dev, ctx_len - 1, stream));
+        dec->ctx = ctx_len;
+        dec->cursor = 0;
+    }
     if (!dec->exec[b]) {
+        dec->att_chunks = q4::attention_chunks(std::min(q4::kBuckets[b], dec->desc.max_ctx));
         Q4_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
         q4_status st = q4::enqueue_all(dec, stream);
         hipGraph_t graph = nullptr;
@@ -368,7 +451,10 @@ extern "C" q4_status q4_decode_layer(void *decp, const q4_layer *layer, hipStrea
     if (!dec || !layer)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer: null decoder or layer");
     Q4_CHECK(q4::check_layer(dec->dims, *layer, -1));
-    return q4::enqueue_layer(dec, *layer, stream);
+    dec->att_chunks = q4::attention_chunks(dec->ctx);
+    Q4_CHECK(q4::enqueue_layer(dec, *layer, dec->cursor, stream));
+    dec->cursor = (dec->cursor + 1) % dec->desc.n_layers;
+    return Q4_OK;
 }
 
 extern "C" q4_status q4_decode_layer_part(void *decp, const q4_layer *layer, int32_t which,
@@ -379,7 +465,26 @@ extern "C" q4_status q4_decode_layer_part(void *decp, const q4_layer *layer, int
     if (which < q4::kQkv || which > q4::kDown)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer_part: product index %d", which);
     Q4_CHECK(q4::check_layer(dec->dims, *layer, -1));
-    return q4::enqueue_kernel(dec, *layer, which, stream);
+    dec->att_chunks = q4::attention_chunks(dec->ctx);
+    Q4_CHECK(q4::enqueue_kernel(dec, *layer, dec->cursor, which, stream));
+    if (which == q4::kDown)
+        dec->cursor = (dec->cursor + 1) % dec->desc.n_layers;
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_decoder_set_context(void *decp, int32_t ctx_len, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    if (!dec)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_context: null decoder");
+    if (!dec->kv)
+        return q4::fail(Q4_ERR_STATE, "q4_decoder_set_context: decoder has no KV cache");
+    if (ctx_len < 1 || ctx_len > dec->desc.max_ctx)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_context: ctx_len=%d outside 1..%d",
+                        ctx_len, dec->desc.max_ctx);
+    Q4_CHECK(q4::launch_set_pos(dec->pos_dev, ctx_len - 1, stream));
+    dec->ctx = ctx_len;
+    dec->cursor = 0;
+    return Q4_OK;
 }
 
 extern "C" q4_status q4_decoder_destroy(void *decp) {
@@ -541,6 +646,7 @@ extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t
                             "q4_decode_token_streamed: blob %d has %zu bytes, layout needs %zu", l,
                             w->bytes[l], bytes);
     const int L = w->n_layers;
+    dec->att_chunks = q4::attention_chunks(dec->ctx);
     const int s0 = (int)(w->n_waited & 1);
     const bool prefetched = w->state[s0] == q4::kLoading && w->layer_in[s0] == 0;
     if (!prefetched)
@@ -553,7 +659,7 @@ extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t
         Q4_CHECK(weight_stream_wait(w, l, compute, &slot));
         q4_layer layer;
         Q4_CHECK(q4_layer_from_blob(&shapes, slot, &layer));
-        Q4_CHECK(q4::enqueue_layer(dec, layer, compute));
+        Q4_CHECK(q4::enqueue_layer(dec, layer, l, compute));
     }
     return Q4_OK;
 }
@@ -565,16 +671,18 @@ extern "C" q4_status q4_decode_step_profiled(void *decp, hipStream_t stream, flo
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_profiled: null argument");
     if (dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "q4_decode_step_profiled: decoder has no resident layers");
-    const int64_t need = (int64_t)dec->layers.size() * q4::kKernelsPerLayer;
+    const int64_t need =
+        (int64_t)dec->layers.size() * (q4::kKernelsPerLayer + (dec->kv ? 1 : 0));
     if (capacity < need)
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_step_profiled: capacity %d < %lld",
                         capacity, (long long)need);
+    dec->att_chunks = q4::attention_chunks(dec->ctx);
     std::vector<hipEvent_t> ev;
     q4::Marks marks;
     marks.ev = &ev;
     q4_status st = marks.mark(stream);
     for (size_t l = 0; st == Q4_OK && l < dec->layers.size(); ++l)
-        st = q4::enqueue_layer(dec, dec->layers[l], stream, marks);
+        st = q4::enqueue_layer(dec, dec->layers[l], (int32_t)l, stream, marks);
     hipError_t e = hipStreamSynchronize(stream);
     if (st == Q4_OK && e != hipSuccess)
         st = q4::fail(Q4_ERR_HIP, "q4_decode_step_profiled: %s", hipGetErrorString(e));
@@ -615,7 +723,7 @@ extern "C" q4_status q4_decode_kernel_time(void *decp, int32_t which, int32_t re
     if (hipEventRecord(e0, stream) != hipSuccess)
         st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: event record failed");
     for (int32_t i = 0; st == Q4_OK && i < reps; ++i)
-        st = q4::enqueue_kernel(dec, dec->layers[(size_t)i % L], which, stream);
+        st = q4::enqueue_kernel(dec, dec->layers[(size_t)i % L], -1, which, stream);
     if (st == Q4_OK && hipEventRecord(e1, stream) != hipSuccess)
         st = q4::fail(Q4_ERR_HIP, "q4_decode_kernel_time: event record failed");
     if (st == Q4_OK && (e = hipEventSynchronize(e1)) != hipSuccess)
@@ -638,6 +746,9 @@ extern "C" q4_status q4_decoder_set_persistent(void *decp, int32_t mode) {
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_decoder_set_persistent: mode %d", mode);
     if (mode != 0 && dec->layers.empty())
         return q4::fail(Q4_ERR_STATE, "q4_decoder_set_persistent: no resident layers");
+    if (mode != 0 && dec->kv)
+        return q4::fail(Q4_ERR_UNSUPPORTED,
+                        "q4_decoder_set_persistent: persistent steps have no attention");
     const int32_t d = (int32_t)dec->dims.d, H = (int32_t)dec->dims.H,
                   hd = (int32_t)dec->dims.hd, dff = (int32_t)dec->dims.dff;
     if (mode == 1 && q4::persistent_lds_bytes(d, H, hd, dff) > 65536)

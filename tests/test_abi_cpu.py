@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 20, names
     for n in names:
         assert hasattr(L, n), n
-    assert q4.abi_version() == 1
+    assert q4.abi_version() == 2
 
 
 def _err():
@@ -112,6 +112,40 @@ def test_decoder_workspace_and_create_checks():
     arr = (q4.Layer * 2)(bad, bad)
     assert L.q4_decoder_create(ctypes.byref(_desc(layers=arr)), ctypes.byref(h)) == INVALID
     assert "expected" in _err()
+
+
+def test_decoder_kv_cache_description_checks():
+    """A KV cache adds a position word and the attention partials to the
+    workspace; its description is validated before any HIP call."""
+    L = q4.lib()
+    dims = dict(d=128, H=4, Hkv=2, hd=64, dff=96)
+    base = dict(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=64, d_ff=96)
+    plain, with_kv = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc(**base)), ctypes.byref(plain)) == 0
+    desc = _desc(**base, kv_cache=4096, max_ctx=100, rope_base=500000.0)
+    assert L.q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(with_kv)) == 0
+    # position word (256) + partials H * ceil(max_ctx / 64) * (hd + 2) fp32,
+    # rounded up to 256: 4 * 2 * 66 * 4 = 2112 -> 2304
+    assert with_kv.value - plain.value == 256 + 2304
+    assert q4.workspace_bytes(dims, n_layers=2, max_ctx=100) == with_kv.value
+    assert q4.kv_cache_elems(dims, 2, 100) == 2 * 2 * 2 * 100 * 64
+    out = ctypes.c_size_t()
+    for over, want in ((dict(kv_cache=4100), INVALID), (dict(max_ctx=0), INVALID),
+                       (dict(rope_base=0.0), INVALID), (dict(rope_base=float("nan")), INVALID),
+                       (dict(head_dim=32), UNSUPPORTED),
+                       (dict(n_heads=6, d_model=192), UNSUPPORTED)):
+        kw = dict(base, kv_cache=4096, max_ctx=100, rope_base=500000.0)
+        kw.update(over)
+        assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc(**kw)), ctypes.byref(out)) \
+            == want, over
+    # a decoder without a cache has no context to set
+    h = ctypes.c_void_p()
+    assert L.q4_decoder_create(ctypes.byref(_desc()), ctypes.byref(h)) == 0
+    try:
+        assert L.q4_decoder_set_context(h, 1, None) == STATE
+    finally:
+        assert L.q4_decoder_destroy(h) == 0
+    assert L.q4_decoder_set_context(None, 1, None) == INVALID
 
 
 def test_decoder_host_object_and_step_checks():
