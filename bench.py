@@ -39,6 +39,9 @@ def parse():
                     help="decode step implementation: 0 four kernels per layer, 1 persistent, "
                          "2 streaming persistent, 3 streaming workgroups per product "
                          "(default: the library's choice)")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the extra measurement of the step with attention over "
+                         "4096-row KV caches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for "
                          "hardware byte counters)")
@@ -168,9 +171,60 @@ def main():
                      "bytes_per_launch": kbytes[2], "avg_launch_us": round(gu_us, 3)},
     }
 
+    if not args.no_attention:
+        dec.close()
+        del ws
+        result["with_attention"] = attention_step(args, q4, inputs, torch, dims, layers, h0)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_tokens)
     print(json.dumps(result), flush=True)
+
+
+def attention_step(args, q4, inputs, torch, dims, layers, h0, max_ctx=4096):
+    """The same 8B step with decode attention over binary16 KV caches of
+    max_ctx rows: the last warmup + steps tokens of a 4096-token context
+    (all in the 4096 bucket), rows before the first of them prefilled with
+    N(0,1) binary16 values standing in for earlier tokens.  Returns
+    tokens/s and the attention kernels' share, timed per kernel with
+    events at the final context length."""
+    n_layers = len(layers)
+    total = args.warmup + args.steps
+    first = max_ctx - total + 1
+    kv = inputs.act_f16((q4.kv_cache_elems(dims, n_layers, max_ctx),),
+                        inputs.seed_of(2, 0, 8), device="cuda")
+    h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers, max_ctx=max_ctx), dtype=torch.uint8,
+                     device="cuda")
+    dec = q4.Decoder(dims, layers, h, ws, kv_cache=kv, max_ctx=max_ctx)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            h.copy_(h0[t], non_blocking=True)
+            dec.step_graph(first + t, stream)
+        stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for t in range(args.warmup, total):
+            h.copy_(h0[t], non_blocking=True)
+            dec.step_graph(first + t, stream)
+        end.record(stream)
+        stream.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        dec.set_context(max_ctx, stream)
+        dec.step_profiled(stream)  # first profiled pass creates events; keep it out
+        prof = dec.step_profiled(stream)
+    attn_ms = sum(prof[1::5]) / n_layers
+    step_ms = sum(prof) / n_layers
+    # K and V rows read per layer at the final context, binary16
+    kv_bytes = 2 * dims["Hkv"] * max_ctx * dims["hd"] * 2
+    dec.close()
+    return {"context": [first, max_ctx], "tokens_per_s": round(1000.0 / ms, 2),
+            "ms_per_step": round(ms, 5),
+            "attention_us_per_layer_at_4096": round(attn_ms * 1000.0, 3),
+            "attention_share_of_layer": round(attn_ms / step_ms, 4),
+            "attention_kv_GBps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1)}
 
 
 def kernel_bytes(dims):

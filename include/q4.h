@@ -172,11 +172,12 @@ typedef struct {
      * each laid out [n_kv_heads][max_ctx][head_dim].  A step at context
      * length c stores the current token's rotated key and its value in row
      * c - 1 and attends over rows 0..c-1.  With a cache the workspace also
-     * holds, after the layer table, a position word (256 bytes) and the
-     * per-chunk attention partials.  Needs n_heads / n_kv_heads in {1, 2, 4,
-     * 8} and head_dim 64 or 128; only the four-kernels step (mode 0). */
+     * holds, after the layer table, a position word (256 bytes), the
+     * per-chunk attention partials and a rotation table (max_ctx * head_dim
+     * * 4 bytes).  Needs n_heads / n_kv_heads in {1, 2, 4, 8} and head_dim
+     * 64 or 128; only the four-kernels step (mode 0). */
     void *kv_cache;
-    int32_t max_ctx;           /* rows per cache, >= 1 */
+    int32_t max_ctx;           /* rows per cache, 1..2^20 */
     float rope_base;           /* rotary base (theta), > 0, e.g. 500000 */
 } q4_model_desc;
 
@@ -198,7 +199,8 @@ q4_status q4_decoder_workspace_bytes(const q4_model_desc *m, size_t *out);
  * synchronous copies, a device copy of the layer table and zeroed barrier
  * words into the workspace; the step starts as four kernels per layer (the
  * persistent step below is opt-in).  With a KV cache it zeroes the position
- * word (context length 1).  Otherwise no GPU work. */
+ * word (context length 1) and fills the rotation table (cos and sin of every
+ * position's angles, taken in fp64), synchronously.  Otherwise no GPU work. */
 q4_status q4_decoder_create(const q4_model_desc *m, void **dec);
 /* Step implementation for resident layers (cached graphs are dropped on a
  * change):

@@ -10,7 +10,7 @@ struct AttnArgs {
     uint16_t *kc, *vc;      // this layer's caches, [Hkv][max_ctx][hd] binary16
     const int32_t *pos_dev; // device word: position of the token (context - 1)
     int32_t max_ctx, H, Hkv, hd;
-    float rope_base;
+    const void *rope;       // rotation table, float2 [max_ctx][hd/2] (cos, sin)
     float *part;            // partials, attention_partial_bytes()
     int32_t nchunk;         // chunks launched (covers the context bucket)
     uint16_t *out;          // binary16 [H * hd] attention output
@@ -19,6 +19,11 @@ struct AttnArgs {
 bool attention_supported(int32_t H, int32_t Hkv, int32_t hd);
 size_t attention_partial_bytes(int32_t H, int32_t Hkv, int32_t hd, int32_t max_ctx);
 int attention_chunks(int32_t ctx_len);
+size_t rope_table_bytes(int32_t max_ctx, int32_t hd);
+// Fills the rotation table: entry [p][i] = (cos, sin) of p * base^(-2i/hd),
+// evaluated in fp64 and rounded to fp32.
+q4_status launch_rope_table(void *rope, int32_t max_ctx, int32_t hd, float base,
+                            hipStream_t s);
 q4_status launch_set_pos(int32_t *pos_dev, int32_t pos, hipStream_t s);
 q4_status launch_attention(const AttnArgs &a, hipStream_t s);
 

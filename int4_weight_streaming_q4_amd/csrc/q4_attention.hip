@@ -14,12 +14,13 @@
 //
 // Two kernels per layer, split over the context like flash decoding:
 //   attn_partial  one workgroup per (key/value head, chunk of 64 positions):
-//                 rotates the group's queries (angles in fp64), the chunk
-//                 that holds the current position also rotates the new key
-//                 and stores it and the new value into the caches; then
-//                 scores, a softmax over the chunk and the weighted value
-//                 sum, written as a partial (chunk max, chunk sum,
-//                 unnormalised output).
+//                 loads its cache tile, rotates the group's queries (a
+//                 table of cos/sin per position, angles taken in fp64 once
+//                 when the decoder is created), the chunk that holds the
+//                 current position also rotates the new key and stores it
+//                 and the new value into the caches; then scores, a softmax
+//                 over the chunk and the weighted value sum, written as a
+//                 partial (chunk max, chunk sum, unnormalised output).
 //   attn_combine  one workgroup per query head: merges the partials of the
 //                 chunks up to the current position and writes the
 //                 binary16 attention output the O product reads.
@@ -35,6 +36,7 @@ namespace {
 
 constexpr int kAP = 64;        // positions per chunk
 constexpr int kAThreads = 256;
+constexpr int kCThreads = 1024; // combine workgroup
 
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -46,23 +48,50 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 
 __global__ void set_pos_kernel(int32_t *pos_dev, int32_t pos) { *pos_dev = pos; }
 
-// QH query heads per key/value head, HD head dimension.
+// Rotation table (cos, sin) of every position and frequency, angles in fp64
+// rounded once to fp32: rope[p * half + i] at angle p * base^(-2i/hd).
+__global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, double base) {
+    const int half = hd / 2;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)max_ctx * half)
+        return;
+    const int p = (int)(i / half), f = (int)(i % half);
+    const double ang = (double)p * pow(base, -2.0 * (double)f / (double)hd);
+    rope[i] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+__device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = h2f((uint16_t)(w[e] & 0xFFFFu));
+        f[2 * e + 1] = h2f((uint16_t)(w[e] >> 16));
+    }
+}
+
+// QH query heads per key/value head, HD head dimension.  The workgroup's
+// cache tile (64 K rows and 64 V rows of its group) is loaded into
+// registers first, so its latency overlaps the rotation of the queries.
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
-             const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
-             float rope_base, float *__restrict__ part, int32_t nchunk) {
+             const float2 *__restrict__ rope, const int32_t *__restrict__ pos_dev,
+             int32_t max_ctx, int32_t H, int32_t Hkv, float *__restrict__ part, int32_t nchunk) {
     constexpr int HALF = HD / 2;
-    constexpr int DB = HD / 8;                 // 16-byte blocks per head row
+    constexpr int QD = HD / 4;                 // dims per lane in the scores
+    constexpr int KL = QD / 8;                 // 16-byte K loads per lane
+    constexpr int DB = HD / 8;                 // 16-byte blocks per row
     constexpr int PG = kAThreads / DB;         // position groups in the value sum
+    constexpr int VL = kAP / PG;               // V rows per lane
+    constexpr int NW = kAThreads / 64;
     static_assert(HD % 32 == 0 && HD <= 256, "head dimension");
-    static_assert(kAThreads % DB == 0, "value-sum layout");
+    static_assert(kAThreads % DB == 0 && kAP % PG == 0 && 64 % DB == 0, "value-sum layout");
     __shared__ float qr[QH][HD];               // rotated queries
-    __shared__ float cs[HALF], sn[HALF];
     __shared__ __align__(16) uint16_t knew[HD];
     __shared__ __align__(16) uint16_t vnew[HD];
     __shared__ float sc[QH][kAP];              // scores, then weights
     __shared__ float mx[QH], sm[QH];
+    __shared__ float vred[NW][QH][HD];
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x;
@@ -79,32 +108,52 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         return;
     }
     const int n = min(kAP, pos + 1 - c0);
-    const bool has_new = pos < c0 + kAP;
+    const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
+    const size_t gbase = (size_t)g * max_ctx + c0;
 
-    // rotation angles of this position, in fp64 then rounded
-    if (t < HALF) {
-        const double inv = pow((double)rope_base, -2.0 * (double)t / (double)HD);
-        const double ang = (double)pos * inv;
-        cs[t] = (float)cos(ang);
-        sn[t] = (float)sin(ang);
+    // cache tile loads; the row of the new token is replaced from LDS below
+    const int jj = t >> 2, qq = t & 3;
+    uint4 kreg[KL];
+#pragma unroll
+    for (int b = 0; b < KL; ++b)
+        kreg[b] = make_uint4(0, 0, 0, 0);
+    if (jj < n) {
+        const uint16_t *kr = kc + (gbase + jj) * HD + qq * QD;
+#pragma unroll
+        for (int b = 0; b < KL; ++b)
+            kreg[b] = *reinterpret_cast<const uint4 *>(kr + b * 8);
     }
-    __syncthreads();
+    const int db = t % DB, pg = t / DB;
+    uint4 vreg[VL];
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+        const int r = pg + i * PG;
+        vreg[i] = make_uint4(0, 0, 0, 0);
+        if (r < n)
+            vreg[i] = *reinterpret_cast<const uint4 *>(vc + (gbase + r) * HD + db * 8);
+    }
+
+    // rotate the group's queries; the chunk of the new token also rotates
+    // its key and stores key and value into row pos of the caches
+    const float2 *rp = rope + (size_t)pos * HALF;
     for (int i = t; i < QH * HALF; i += kAThreads) {
         const int h = i / HALF, d = i % HALF;
         const float *q = qkv + (size_t)(g * QH + h) * HD;
+        const float2 cs = rp[d];
         const float a = q[d], b = q[d + HALF];
-        qr[h][d] = a * cs[d] - b * sn[d];
-        qr[h][d + HALF] = a * sn[d] + b * cs[d];
+        qr[h][d] = a * cs.x - b * cs.y;
+        qr[h][d + HALF] = a * cs.y + b * cs.x;
     }
-    if (has_new) {
+    if (jn < kAP) {
         const float *k = qkv + (size_t)(H + g) * HD;
         const float *v = qkv + (size_t)(H + Hkv + g) * HD;
-        uint16_t *krow = kc + ((size_t)g * max_ctx + pos) * HD;
-        uint16_t *vrow = vc + ((size_t)g * max_ctx + pos) * HD;
+        uint16_t *krow = kc + (gbase + jn) * HD;
+        uint16_t *vrow = vc + (gbase + jn) * HD;
         for (int d = t; d < HALF; d += kAThreads) {
+            const float2 cs = rp[d];
             const float a = k[d], b = k[d + HALF];
-            const uint16_t r0 = f2h(a * cs[d] - b * sn[d]);
-            const uint16_t r1 = f2h(a * sn[d] + b * cs[d]);
+            const uint16_t r0 = f2h(a * cs.x - b * cs.y);
+            const uint16_t r1 = f2h(a * cs.y + b * cs.x);
             knew[d] = r0;
             knew[d + HALF] = r1;
             krow[d] = r0;
@@ -120,29 +169,25 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 
     // scores: four lanes per position, each a quarter of the head dimension
     {
-        constexpr int QD = HD / 4;
-        const int jj = t >> 2, qq = t & 3;
+        if (jj == jn) {
+#pragma unroll
+            for (int b = 0; b < KL; ++b)
+                kreg[b] = *reinterpret_cast<const uint4 *>(knew + qq * QD + b * 8);
+        }
         float acc[QH];
 #pragma unroll
         for (int h = 0; h < QH; ++h)
             acc[h] = 0.0f;
-        if (jj < n) {
-            const int j = c0 + jj;
-            const uint16_t *kr = (j == pos) ? knew : kc + ((size_t)g * max_ctx + j) * HD;
 #pragma unroll
-            for (int b = 0; b < QD / 8; ++b) {
-                const int d0 = qq * QD + b * 8;
-                const uint4 kv = *reinterpret_cast<const uint4 *>(kr + d0);
-                const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+        for (int b = 0; b < KL; ++b) {
+            const int d0 = qq * QD + b * 8;
+            float kf[8];
+            unpack8(kreg[b], kf);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float k0 = h2f((uint16_t)(w[e] & 0xFFFFu));
-                    const float k1 = h2f((uint16_t)(w[e] >> 16));
+            for (int e = 0; e < 8; e += 2)
 #pragma unroll
-                    for (int h = 0; h < QH; ++h)
-                        acc[h] = fmaf(qr[h][d0 + 2 * e], k0, fmaf(qr[h][d0 + 2 * e + 1], k1, acc[h]));
-                }
-            }
+                for (int h = 0; h < QH; ++h)
+                    acc[h] = fmaf(qr[h][d0 + e], kf[e], fmaf(qr[h][d0 + e + 1], kf[e + 1], acc[h]));
         }
         const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
@@ -150,7 +195,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
             float v = acc[h];
             v += __shfl_xor(v, 1);
             v += __shfl_xor(v, 2);
-            if (qq == 0 && jj < kAP)
+            if (qq == 0)
                 sc[h][jj] = v * scale;
         }
     }
@@ -159,7 +204,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     // softmax over the chunk: one wave per head
     {
         const int w = t >> 6, lane = t & 63;
-        for (int h = w; h < QH; h += kAThreads / 64) {
+        for (int h = w; h < QH; h += NW) {
             const float s = lane < n ? sc[h][lane] : -INFINITY;
             float m = s;
 #pragma unroll
@@ -179,46 +224,52 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     }
     __syncthreads();
 
-    // weighted value sum: thread = (16-byte block of the row, position group)
+    // weighted value sum: lane = (16-byte block of the row, position group);
+    // rows past the context have weight 0 and zero values
     {
-        const int db = t % DB, pg = t / DB;
         float acc[QH][8];
 #pragma unroll
         for (int h = 0; h < QH; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 acc[h][e] = 0.0f;
-        for (int jj = pg; jj < n; jj += PG) {
-            const int j = c0 + jj;
-            const uint16_t *vr = (j == pos) ? vnew : vc + ((size_t)g * max_ctx + j) * HD;
-            const uint4 vv = *reinterpret_cast<const uint4 *>(vr + db * 8);
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-            float vf[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vf[2 * e] = h2f((uint16_t)(w[e] & 0xFFFFu));
-                vf[2 * e + 1] = h2f((uint16_t)(w[e] >> 16));
-            }
+        for (int i = 0; i < VL; ++i) {
+            const int r = pg + i * PG;
+            if (r == jn)
+                vreg[i] = *reinterpret_cast<const uint4 *>(vnew + db * 8);
+            float vf[8];
+            unpack8(vreg[i], vf);
 #pragma unroll
             for (int h = 0; h < QH; ++h) {
-                const float p = sc[h][jj];
+                const float p = sc[h][r];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     acc[h][e] = fmaf(p, vf[e], acc[h][e]);
             }
         }
-        // reduce over the position groups through LDS, in a fixed order
-        __shared__ float vred[PG][QH][8 * DB];
+        // position groups of one wave: lanes DB, 2 DB, ... apart
 #pragma unroll
-        for (int h = 0; h < QH; ++h)
+        for (int o = DB; o < 64; o <<= 1)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vred[pg][h][db * 8 + e] = acc[h][e];
+            for (int h = 0; h < QH; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[h][e] += __shfl_xor(acc[h][e], o);
+        const int w = t >> 6, lane = t & 63;
+        if (lane < DB) {
+#pragma unroll
+            for (int h = 0; h < QH; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vred[w][h][db * 8 + e] = acc[h][e];
+        }
         __syncthreads();
         for (int i = t; i < QH * HD; i += kAThreads) {
             const int h = i / HD, d = i % HD;
             float s = 0.0f;
-            for (int q = 0; q < PG; ++q)
+#pragma unroll
+            for (int q = 0; q < NW; ++q)
                 s += vred[q][h][d];
             pout[h * prow + d] = s;
         }
@@ -229,32 +280,82 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     }
 }
 
-// One workgroup per query head: merges the chunk partials.
+// One workgroup per query head merges the chunk partials (chunk max m_c,
+// chunk sum l_c, unnormalised o_c): o = sum_c o_c e^(m_c - M) / sum_c l_c
+// e^(m_c - M), M the largest m_c.  Lane (slice s, dim d) merges chunks s,
+// s + S, ... with a running maximum, U chunks per round, then the S slices
+// merge through LDS.
 template <int QH, int HD>
-__global__ void __launch_bounds__(HD)
+__global__ void __launch_bounds__(kCThreads)
 attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev,
              int32_t nchunk, uint16_t *__restrict__ out) {
-    const int hq = blockIdx.x, d = threadIdx.x;
+    constexpr int S = kCThreads / HD;
+    constexpr int U = 8;
+    __shared__ float ored[S][HD];
+    __shared__ float ms[S], ls[S];
+    const int hq = blockIdx.x, t = threadIdx.x;
+    const int d = t % HD, s = t / HD;
     const int g = hq / QH, h = hq % QH;
     const int pos = *pos_dev;
-    const int last = min(nchunk - 1, pos / kAP);
+    const int nc = min(nchunk, pos / kAP + 1);
     const size_t prow = (size_t)(HD + 2);
+    const size_t cstride = (size_t)QH * prow;
     const float *base = part + ((size_t)g * nchunk * QH + h) * prow;
-    float M = -INFINITY;
-    for (int c = 0; c <= last; ++c)
-        M = fmaxf(M, base[(size_t)c * QH * prow + HD]);
-    float L = 0.0f, o = 0.0f;
-    for (int c = 0; c <= last; ++c) {
-        const float *pc = base + (size_t)c * QH * prow;
-        const float w = expf(pc[HD] - M);
-        L = fmaf(pc[HD + 1], w, L);
-        o = fmaf(pc[d], w, o);
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    for (int c1 = s; c1 < nc; c1 += S * U) {
+        float mv[U], lv[U], ov[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c1 + u * S;
+            mv[u] = -INFINITY;
+            lv[u] = 0.0f;
+            ov[u] = 0.0f;
+            if (cc < nc) {
+                const float *pc = base + (size_t)cc * cstride;
+                mv[u] = pc[HD];
+                lv[u] = pc[HD + 1];
+                ov[u] = pc[d];
+            }
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            mn = fmaxf(mn, mv[u]);
+        const float r = expf(m - mn);
+        l *= r;
+        o *= r;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = expf(mv[u] - mn);
+            l = fmaf(lv[u], w, l);
+            o = fmaf(ov[u], w, o);
+        }
+        m = mn;
     }
-    out[(size_t)hq * HD + d] = f2h(o / L);
+    ored[s][d] = o;
+    if (d == 0) {
+        ms[s] = m;
+        ls[s] = l;
+    }
+    __syncthreads();
+    if (s == 0) {
+        float M = ms[0];
+#pragma unroll
+        for (int q = 1; q < S; ++q)
+            M = fmaxf(M, ms[q]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            const float w = expf(ms[q] - M);
+            L = fmaf(ls[q], w, L);
+            O = fmaf(ored[q][d], w, O);
+        }
+        out[(size_t)hq * HD + d] = f2h(O / L);
+    }
 }
 
-using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const int32_t *, int32_t,
-                           int32_t, int32_t, float, float *, int32_t);
+using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *,
+                           const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
 using CombineFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
 template <int QH, int HD>
@@ -282,6 +383,19 @@ size_t attention_partial_bytes(int32_t H, int32_t Hkv, int32_t hd, int32_t max_c
 
 int attention_chunks(int32_t ctx_len) { return (ctx_len + kAP - 1) / kAP; }
 
+size_t rope_table_bytes(int32_t max_ctx, int32_t hd) {
+    return (size_t)max_ctx * (size_t)(hd / 2) * sizeof(float2);
+}
+
+q4_status launch_rope_table(void *rope, int32_t max_ctx, int32_t hd, float base,
+                            hipStream_t s) {
+    const int64_t n = (int64_t)max_ctx * (hd / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<float2 *>(rope), max_ctx, hd, (double)base);
+    Q4_HIP(hipGetLastError());
+    return Q4_OK;
+}
+
 q4_status launch_set_pos(int32_t *pos_dev, int32_t pos, hipStream_t s) {
     hipLaunchKernelGGL(set_pos_kernel, dim3(1), dim3(1), 0, s, pos_dev, pos);
     Q4_HIP(hipGetLastError());
@@ -302,10 +416,10 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
         return fail(Q4_ERR_INVALID_ARG, "attention: %d chunks for max_ctx %d", a.nchunk,
                     a.max_ctx);
     hipLaunchKernelGGL(pf, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), 0, s,
-                       a.qkv, a.kc, a.vc, a.pos_dev, a.max_ctx, a.H, a.Hkv, a.rope_base, a.part,
-                       a.nchunk);
+                       a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
+                       a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
     Q4_HIP(hipGetLastError());
-    hipLaunchKernelGGL(cf, dim3((unsigned)a.H), dim3((unsigned)a.hd), 0, s, a.part, a.pos_dev,
+    hipLaunchKernelGGL(cf, dim3((unsigned)a.H), dim3(kCThreads), 0, s, a.part, a.pos_dev,
                        a.nchunk, a.out);
     Q4_HIP(hipGetLastError());
     return Q4_OK;

@@ -52,6 +52,7 @@ struct Decoder {
     uint16_t *kv = nullptr;
     int32_t *pos_dev = nullptr;  // position word the attention kernels read
     float *att_part = nullptr;   // per-chunk partials
+    void *rope = nullptr;        // rotation table
     int32_t ctx = 1;             // context length of eager / layer-by-layer steps
     int32_t att_chunks = 1;      // chunks the attention kernels cover
     int32_t cursor = 0;          // next layer of a layer-by-layer token
@@ -80,8 +81,9 @@ q4_status dims_of(const q4_model_desc *m, Dims *out) {
     if (m->kv_cache) {
         if (!aligned(m->kv_cache, 16))
             return fail(Q4_ERR_INVALID_ARG, "decoder: kv_cache not 16-byte aligned");
-        if (m->max_ctx < 1)
-            return fail(Q4_ERR_INVALID_ARG, "decoder: max_ctx %d < 1", m->max_ctx);
+        if (m->max_ctx < 1 || m->max_ctx > (1 << 20))
+            return fail(Q4_ERR_INVALID_ARG, "decoder: max_ctx %d outside 1..%d", m->max_ctx,
+                        1 << 20);
         if (!(m->rope_base > 0.0f))
             return fail(Q4_ERR_INVALID_ARG, "decoder: rope_base must be > 0");
         if (!attention_supported(m->n_heads, m->n_kv_heads, m->head_dim))
@@ -98,8 +100,10 @@ size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) 
                align256(d.H * d.hd * 2) + align256(d.dff * 2) + kBarBytes +
                align256((size_t)n_layers * sizeof(DevLayer));
     if (m && m->kv_cache)
-        b += 256 + align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv,
-                                                    (int32_t)d.hd, m->max_ctx));
+        b += 256 +
+             align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv, (int32_t)d.hd,
+                                              m->max_ctx)) +
+             align256(rope_table_bytes(m->max_ctx, (int32_t)d.hd));
     return b;
 }
 
@@ -161,7 +165,7 @@ q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s) {
     a.H = (int32_t)d.H;
     a.Hkv = (int32_t)d.Hkv;
     a.hd = (int32_t)d.hd;
-    a.rope_base = dec->desc.rope_base;
+    a.rope = dec->rope;
     a.part = dec->att_part;
     a.nchunk = dec->att_chunks;
     a.out = dec->oin;
@@ -346,8 +350,19 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
         dec->pos_dev = reinterpret_cast<int32_t *>(ws);
         ws += 256;
         dec->att_part = reinterpret_cast<float *>(ws);
-        // context length 1 until the caller sets another
+        ws += q4::align256(q4::attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv,
+                                                       (int32_t)d.hd, m->max_ctx));
+        dec->rope = ws;
+        // context length 1 until the caller sets another; the rotation table
+        q4_status st = q4::launch_rope_table(dec->rope, m->max_ctx, (int32_t)d.hd,
+                                             m->rope_base, nullptr);
+        if (st != Q4_OK) {
+            delete dec;
+            return st;
+        }
         hipError_t e = hipMemset(dec->pos_dev, 0, 256);
+        if (e == hipSuccess)
+            e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             delete dec;
             return q4::fail(Q4_ERR_HIP, "q4_decoder_create: position word: %s",

@@ -125,12 +125,14 @@ def test_decoder_kv_cache_description_checks():
     desc = _desc(**base, kv_cache=4096, max_ctx=100, rope_base=500000.0)
     assert L.q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(with_kv)) == 0
     # position word (256) + partials H * ceil(max_ctx / 64) * (hd + 2) fp32,
-    # rounded up to 256: 4 * 2 * 66 * 4 = 2112 -> 2304
-    assert with_kv.value - plain.value == 256 + 2304
+    # rounded up to 256: 4 * 2 * 66 * 4 = 2112 -> 2304, + rotation table
+    # max_ctx * hd/2 (cos, sin) fp32 pairs: 100 * 32 * 8 = 25600
+    assert with_kv.value - plain.value == 256 + 2304 + 25600
     assert q4.workspace_bytes(dims, n_layers=2, max_ctx=100) == with_kv.value
     assert q4.kv_cache_elems(dims, 2, 100) == 2 * 2 * 2 * 100 * 64
     out = ctypes.c_size_t()
     for over, want in ((dict(kv_cache=4100), INVALID), (dict(max_ctx=0), INVALID),
+                       (dict(max_ctx=(1 << 20) + 1), INVALID),
                        (dict(rope_base=0.0), INVALID), (dict(rope_base=float("nan")), INVALID),
                        (dict(head_dim=32), UNSUPPORTED),
                        (dict(n_heads=6, d_model=192), UNSUPPORTED)):
