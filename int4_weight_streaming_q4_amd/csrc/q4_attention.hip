@@ -60,6 +60,62 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
     rope[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
+// Cross-lane steps as VALU operations (DPP and gfx950's lane swaps) rather
+// than LDS permutes: they sit on the critical path of every reduction.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1; // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E; // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+// Values of the lanes 16 and 32 away, pairwise combined: every lane gets
+// op(x[row r], x[row r ^ 1]) (16-lane rows) resp. op(x[lane], x[lane ^ 32]).
+struct Rows16 {
+    unsigned a, b;
+    __device__ __forceinline__ Rows16(float x) {
+        auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+        a = r[0];
+        b = r[1];
+    }
+};
+struct Halves32 {
+    unsigned a, b;
+    __device__ __forceinline__ Halves32(float x) {
+        auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+        a = r[0];
+        b = r[1];
+    }
+};
+__device__ __forceinline__ float fa(unsigned u) { return __builtin_bit_cast(float, u); }
+
+// Sum / max over all 64 lanes, result in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<kQuadXor1>(x);
+    x += dpp<kQuadXor2>(x);
+    x += dpp<kRowRor4>(x);
+    x += dpp<kRowRor8>(x);
+    const Rows16 r(x);
+    x = fa(r.a) + fa(r.b);
+    const Halves32 h(x);
+    return fa(h.a) + fa(h.b);
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<kQuadXor1>(x));
+    x = fmaxf(x, dpp<kQuadXor2>(x));
+    x = fmaxf(x, dpp<kRowRor4>(x));
+    x = fmaxf(x, dpp<kRowRor8>(x));
+    const Rows16 r(x);
+    x = fmaxf(fa(r.a), fa(r.b));
+    const Halves32 h(x);
+    return fmaxf(fa(h.a), fa(h.b));
+}
+
 __device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -85,7 +141,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     constexpr int VL = kAP / PG;               // V rows per lane
     constexpr int NW = kAThreads / 64;
     static_assert(HD % 32 == 0 && HD <= 256, "head dimension");
-    static_assert(kAThreads % DB == 0 && kAP % PG == 0 && 64 % DB == 0, "value-sum layout");
+    static_assert(kAThreads % DB == 0 && kAP % PG == 0 && (DB == 8 || DB == 16), "value-sum layout");
     __shared__ float qr[QH][HD];               // rotated queries
     __shared__ __align__(16) uint16_t knew[HD];
     __shared__ __align__(16) uint16_t vnew[HD];
@@ -193,8 +249,8 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 #pragma unroll
         for (int h = 0; h < QH; ++h) {
             float v = acc[h];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
+            v += dpp<kQuadXor1>(v);
+            v += dpp<kQuadXor2>(v);
             if (qq == 0)
                 sc[h][jj] = v * scale;
         }
@@ -206,15 +262,9 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         const int w = t >> 6, lane = t & 63;
         for (int h = w; h < QH; h += NW) {
             const float s = lane < n ? sc[h][lane] : -INFINITY;
-            float m = s;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1)
-                m = fmaxf(m, __shfl_xor(m, o));
+            const float m = wave_max(s);
             const float e = lane < n ? expf(s - m) : 0.0f;
-            float l = e;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1)
-                l += __shfl_xor(l, o);
+            const float l = wave_sum(e);
             sc[h][lane] = e;
             if (lane == 0) {
                 mx[h] = m;
@@ -248,14 +298,20 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
                     acc[h][e] = fmaf(p, vf[e], acc[h][e]);
             }
         }
-        // position groups of one wave: lanes DB, 2 DB, ... apart
+        // position groups of one wave (lanes DB, 2 DB, ... apart): half
+        // rows for 8 blocks per row, then rows, then wave halves
 #pragma unroll
-        for (int o = DB; o < 64; o <<= 1)
+        for (int h = 0; h < QH; ++h)
 #pragma unroll
-            for (int h = 0; h < QH; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[h][e] += __shfl_xor(acc[h][e], o);
+            for (int e = 0; e < 8; ++e) {
+                float x = acc[h][e];
+                if (DB == 8)
+                    x += dpp<kRowRor8>(x);
+                const Rows16 r(x);
+                x = fa(r.a) + fa(r.b);
+                const Halves32 hh(x);
+                acc[h][e] = fa(hh.a) + fa(hh.b);
+            }
         const int w = t >> 6, lane = t & 63;
         if (lane < DB) {
 #pragma unroll
@@ -280,21 +336,26 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     }
 }
 
-// One workgroup per query head merges the chunk partials (chunk max m_c,
-// chunk sum l_c, unnormalised o_c): o = sum_c o_c e^(m_c - M) / sum_c l_c
-// e^(m_c - M), M the largest m_c.  Lane (slice s, dim d) merges chunks s,
-// s + S, ... with a running maximum, U chunks per round, then the S slices
+// One workgroup per (query head, 64 dims of it) merges the chunk partials
+// (chunk max m_c, chunk sum l_c, unnormalised o_c): o = sum_c o_c e^(m_c -
+// M) / sum_c l_c e^(m_c - M), M the largest m_c.  Wave s merges chunks s,
+// s + S, ... with a running maximum, U chunks per round, then the S waves
 // merge through LDS.
+constexpr int kCDims = 64;
 template <int QH, int HD>
 __global__ void __launch_bounds__(kCThreads)
 attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev,
              int32_t nchunk, uint16_t *__restrict__ out) {
-    constexpr int S = kCThreads / HD;
-    constexpr int U = 8;
-    __shared__ float ored[S][HD];
+    constexpr int S = kCThreads / kCDims;
+    static_assert(HD % kCDims == 0, "dims per workgroup");
+    constexpr int U = 4;
+    __shared__ float ored[S][kCDims];
     __shared__ float ms[S], ls[S];
     const int hq = blockIdx.x, t = threadIdx.x;
-    const int d = t % HD, s = t / HD;
+    const int d = blockIdx.y * kCDims + t % kCDims;
+    // the wave index is the slice: every chunk index is wave-uniform, so
+    // chunk max and sum come from scalar loads
+    const int s = __builtin_amdgcn_readfirstlane(t / kCDims);
     const int g = hq / QH, h = hq % QH;
     const int pos = *pos_dev;
     const int nc = min(nchunk, pos / kAP + 1);
@@ -332,8 +393,8 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
         }
         m = mn;
     }
-    ored[s][d] = o;
-    if (d == 0) {
+    ored[s][t % kCDims] = o;
+    if (t % kCDims == 0) {
         ms[s] = m;
         ls[s] = l;
     }
@@ -348,7 +409,7 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
         for (int q = 0; q < S; ++q) {
             const float w = expf(ms[q] - M);
             L = fmaf(ls[q], w, L);
-            O = fmaf(ored[q][d], w, O);
+            O = fmaf(ored[q][t], w, O);
         }
         out[(size_t)hq * HD + d] = f2h(O / L);
     }
@@ -419,8 +480,8 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
                        a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                        a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
     Q4_HIP(hipGetLastError());
-    hipLaunchKernelGGL(cf, dim3((unsigned)a.H), dim3(kCThreads), 0, s, a.part, a.pos_dev,
-                       a.nchunk, a.out);
+    hipLaunchKernelGGL(cf, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims)), dim3(kCThreads), 0, s,
+                       a.part, a.pos_dev, a.nchunk, a.out);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }
