@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "q4o_rope": [P, I, I, D],
             "q4o_attention": [P, I, I, I, I, I, D, P, P, P, P],
             "q4o_decode_layer_attn": [P, P, P, P, I, I, I, I, I, D, I, I, D, P, P, P, P],
+            "q4o_quantize_f32": [P, I, I, P, P],
+            "q4o_quantize_f16": [P, I, I, P, P],
         }.items():
             fn = getattr(L, name)
             fn.restype = None
@@ -241,6 +243,25 @@ def attention(qkv, dims, pos, kcache, vcache, base=500000.0):
     lib().q4o_attention(_ptr(qkv), H, Hkv, hd, pos, max_ctx, base, _ptr(kcache),
                         _ptr(vcache), _ptr(out), _ptr(mag))
     return out, mag
+
+
+def quantize(w):
+    """Symmetric round-to-nearest per group of 32 (see q4o_quantize_f32).
+    ``w``: float32 [N][K], or binary16 bit patterns as uint16 [N][K].
+    Returns (codes u8[N][K], scales u16[N][K/32])."""
+    w = np.asarray(w)
+    assert w.ndim == 2 and w.shape[1] % 32 == 0
+    N, K = w.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint16)
+    if w.dtype == np.uint16:
+        w = np.ascontiguousarray(w)
+        lib().q4o_quantize_f16(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    else:
+        assert w.dtype == np.float32, w.dtype
+        w = np.ascontiguousarray(w)
+        lib().q4o_quantize_f32(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 class _Mat(ctypes.Structure):

@@ -357,6 +357,72 @@ void q4o_attention(const double *qkv, int64_t H, int64_t Hkv, int64_t hd,
     free(s);
 }
 
+/* ------------------------------------------------------------------ */
+/* quantization of real weights                                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The pages name 4-bit weights (PIPO, "Method", bullet "Computation
+ * optimization") but no rule for producing them.  Reading: symmetric
+ * round-to-nearest per group of 32 consecutive k, in the format above:
+ *     amax = max |w| over the group
+ *     s    = binary16(amax / 8), round to nearest even (the stored scale)
+ *     c    = clamp(rint(w / s) + 8, 0, 15)   (rint: ties to even)
+ * The quotient w / s is one IEEE binary32 division of the binary32 values
+ * of w and s: a rounding step decides an integer code, so it is fixed to
+ * the precision the kernel uses.  A group whose stored scale is 0 (all
+ * zero, or amax / 8 below half the smallest binary16 subnormal) gets code 8
+ * everywhere.  The largest weight of a group, when positive, maps to
+ * w / s = 8 and is clipped to code 15 (7 s).  Inputs are finite with
+ * amax / 8 below 65520 (else the scale is infinite).
+ * codes: u8[N][K], one code per byte; scales: u16[N][K/32].
+ */
+static void quantize_group(const float *w, uint8_t *codes, uint16_t *scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)w[i]);
+        if (a > amax)
+            amax = a;
+    }
+    uint16_t s16 = q4o_f64_to_f16(amax / 8.0); /* amax / 8 is exact in fp64 */
+    *scale = s16;
+    float s = (float)q4o_f16_to_f64(s16);
+    for (int i = 0; i < 32; ++i) {
+        if (s == 0.0f) {
+            codes[i] = 8;
+            continue;
+        }
+        volatile float q = w[i] / s; /* one binary32 division */
+        float r = rintf(q);
+        float c = r + 8.0f;
+        if (c < 0.0f)
+            c = 0.0f;
+        if (c > 15.0f)
+            c = 15.0f;
+        codes[i] = (uint8_t)c;
+    }
+}
+
+void q4o_quantize_f32(const float *w, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < K / 32; ++g)
+            quantize_group(w + n * K + g * 32, codes + n * K + g * 32, scales + n * (K / 32) + g);
+}
+
+/* binary16 weights (bit patterns): each value is exactly a binary32. */
+void q4o_quantize_f16(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales)
+{
+    float buf[32];
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < K / 32; ++g) {
+            for (int i = 0; i < 32; ++i)
+                buf[i] = (float)q4o_f16_to_f64(w[n * K + g * 32 + i]);
+            quantize_group(buf, codes + n * K + g * 32, scales + n * (K / 32) + g);
+        }
+}
+
 /* mlp[j] = f16(silu(gate[j]) * up[j]), gate | up stacked in gu. */
 void q4o_silu_mul_f16(const double *gu, int64_t dff, uint16_t *out)
 {

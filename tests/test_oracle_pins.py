@@ -413,3 +413,97 @@ def test_attention_two_positions_logistic_weights():
         p1 = 1.0 / (1.0 + np.exp(s0 - s1))
         want = (1 - p1) * oracle.f16_to_f64(v[g, 0]) + p1 * oracle.f16_to_f64(v[g, 1])
         assert np.allclose(o[hq * hd:(hq + 1) * hd], want, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------- quantization
+def test_quantize_hand_case():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "quantize_hand_case.txt"))
+            if l.strip() and not l.startswith("#")]
+    w = np.zeros((1, 32), np.float32)
+    want = np.full(32, 8, np.uint8)
+    for i, (v, c) in enumerate(rows):
+        w[0, i] = np.float32(v)
+        want[i] = int(c)
+    codes, s = oracle.quantize(w)
+    assert oracle.f16_to_f64(s)[0, 0] == 1.0
+    assert np.array_equal(codes[0], want), (codes[0], want)
+    # the same values as binary16 inputs (3.49, -7.6 round; their codes do not move)
+    codes16, s16 = oracle.quantize(w.astype(np.float16).view(np.uint16))
+    assert np.array_equal(codes16, codes) and np.array_equal(s16, s)
+
+
+def test_quantize_recovers_codes_on_the_grid():
+    """Weights that are exactly s * (c - 8), with code 0 present in every
+    group (so max|w| = 8 s): quantization returns the same codes and s."""
+    rng = np.random.default_rng(21)
+    N, K = 16, 256
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes.reshape(N, K // 32, 32)[:, :, 0] = 0
+    s = (np.abs(rng.standard_normal((N, K // 32))) * 0.02 + 1e-3).astype(np.float16)
+    w = (codes.reshape(N, K // 32, 32).astype(np.float64) - 8) * s.astype(np.float64)[..., None]
+    w = w.reshape(N, K).astype(np.float32)          # exact: small integer times binary16
+    got_c, got_s = oracle.quantize(w)
+    assert np.array_equal(got_s, s.view(np.uint16))
+    assert np.array_equal(got_c, codes)
+    # and through binary16 inputs where the products are binary16 values
+    s2 = np.full((N, K // 32), 0.25, np.float16)
+    w2 = ((codes.astype(np.float64) - 8) * 0.25).astype(np.float16)
+    c2, q2 = oracle.quantize(w2.view(np.uint16))
+    assert np.array_equal(c2, codes) and np.array_equal(q2, s2.view(np.uint16))
+
+
+def test_quantize_is_nearest_code_and_error_bound():
+    """Brute force over all 16 codes: the chosen code is a nearest grid
+    point for the stored scale (up to the binary32 quotient deciding near
+    ties), and the error is at most s/2, or the clip at +8 s."""
+    rng = np.random.default_rng(22)
+    N, K = 32, 512
+    w = (rng.standard_normal((N, K)) * rng.uniform(0.01, 3.0, (N, 1))).astype(np.float32)
+    codes, s = oracle.quantize(w)
+    sg = np.repeat(oracle.f16_to_f64(s), 32, axis=1)
+    wd = w.astype(np.float64)
+    grid = (np.arange(16, dtype=np.float64) - 8)[None, None, :] * sg[..., None]
+    err_all = np.abs(grid - wd[..., None])
+    best = err_all.min(axis=2)
+    got = np.take_along_axis(err_all, codes[..., None].astype(np.int64), axis=2)[..., 0]
+    assert np.all(got <= best + sg * 2.0 ** -20)
+    clipped = wd / sg > 7.5
+    assert np.all(got[~clipped] <= sg[~clipped] * (0.5 + 2.0 ** -20))
+    # s = binary16(max|w| / 8) may sit half a binary16 ulp below max|w| / 8,
+    # so w / s reaches 8 (1 + 2^-11) and the clip error s (1 + 2^-8)
+    assert np.all(got[clipped] <= sg[clipped] * (1.0 + 2.0 ** -8))
+    # the scale is max|w| / 8 rounded to binary16
+    amax = np.abs(wd).reshape(N, K // 32, 32).max(axis=2)
+    ref = (amax / 8).astype(np.float16).view(np.uint16)
+    assert np.array_equal(s, ref)
+
+
+def test_quantize_zero_and_tiny_groups_and_power_of_two_invariance():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 32:] = np.float32(2.0 ** -28)          # max/8 below half the least subnormal
+    codes, s = oracle.quantize(w)
+    assert np.all(codes == 8) and np.all(s == 0)
+    rng = np.random.default_rng(23)
+    w = rng.standard_normal((8, 128)).astype(np.float32)
+    c1, s1 = oracle.quantize(w)
+    for k in (-3, 2, 5):
+        ck, sk = oracle.quantize((w * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(ck, c1)
+        assert np.array_equal(oracle.f16_to_f64(sk), oracle.f16_to_f64(s1) * 2.0 ** k)
+
+
+def test_quantize_quotient_is_one_binary32_division():
+    """The code is decided by one IEEE binary32 division w / s (numpy's
+    float32 division is the independent reference).  Here w / s is exactly
+    3.5 in binary32 (ties to even: code 12), while multiplying by the
+    binary32 reciprocal of s gives just below 3.5 (code 11)."""
+    s = np.float32(np.float16(1.612))
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = np.float32(8.0) * s                        # max|w| = 8 s: stored scale is s
+    w[0, 1] = np.float32(float.fromhex("0x1.6928p+2"))   # 5.6430664
+    q_div = np.rint(w[0, 1] / s)
+    q_rcp = np.rint(w[0, 1] * (np.float32(1.0) / s))
+    assert q_div == 4.0 and q_rcp == 3.0
+    codes, sc = oracle.quantize(w)
+    assert oracle.f16_to_f64(sc)[0, 0] == float(s)
+    assert codes[0, 0] == 15 and codes[0, 1] == 12 and np.all(codes[0, 2:] == 8)
