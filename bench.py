@@ -171,6 +171,7 @@ def main():
                      "bytes_per_launch": kbytes[2], "avg_launch_us": round(gu_us, 3)},
     }
 
+    result["quantize"] = quantize_rate(q4, torch)
     if not args.no_attention:
         dec.close()
         del ws
@@ -178,6 +179,34 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_tokens)
     print(json.dumps(result), flush=True)
+
+
+def quantize_rate(q4, torch, N=28672, K=4096, reps=10):
+    """q4_quantize on the gate+up shape from binary32 and binary16 weights
+    (N(0,1) values): average us over `reps` back-to-back launches and the
+    algorithmic bytes moved per second (weights read, codes and scales
+    written)."""
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(11)
+    w32 = torch.randn(N, K, generator=g, device="cuda")
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(N, K // 32, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.Stream()
+    for name, w in (("f32", w32), ("f16", w32.half())):
+        with torch.cuda.stream(stream):
+            q4.q4_quantize(w, packed, scales, stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                q4.q4_quantize(w, packed, scales, stream)
+            e1.record(stream)
+        stream.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        nbytes = N * K * w.element_size() + N * K // 2 + N * (K // 32) * 2
+        out[f"{name}_{N}x{K}"] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1)}
+    del w32
+    return out
 
 
 def attention_step(args, q4, inputs, torch, dims, layers, h0, max_ctx=4096):

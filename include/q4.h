@@ -87,6 +87,30 @@ q4_status q4_unpack(const uint8_t *packed, uint8_t *codes, int64_t N,
                     int64_t K, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Quantization of real weights                                         */
+/* ------------------------------------------------------------------ */
+
+#define Q4_DTYPE_F32 0
+#define Q4_DTYPE_F16 1
+
+/* Real weights -> the 4-bit format above (PIPO, "Method", "Computation
+ * optimization" runs on 4-bit weights but gives no rule to produce them;
+ * the rule here is symmetric round-to-nearest per group of 32 k):
+ *   s = binary16(max|w| / 8) over the group (nearest even);
+ *   code = clamp(rint(w / s) + 8, 0, 15), w / s one IEEE binary32 division,
+ *   rint ties to even; a group whose s is 0 gets code 8 everywhere.
+ * The largest positive weight of a group maps to w / s = 8, clipped to 15.
+ *   w       device [N][K], row-major, w_dtype Q4_DTYPE_F32 (binary32) or
+ *           Q4_DTYPE_F16 (binary16 bit patterns), 16-byte aligned; finite,
+ *           with max|w| / 8 < 65520 per group (else the scale is infinite);
+ *   packed  device u8[N][K/2] out, 16-byte aligned;
+ *   scales  device u16[N][K/32] out, 2-byte aligned.
+ * N >= 1, K >= 32, K % 32 == 0; INVALID_ARG otherwise, nothing enqueued.
+ * Bit-exact: the same codes and scales on every run. */
+q4_status q4_quantize(const void *w, int32_t w_dtype, uint8_t *packed,
+                      uint16_t *scales, int64_t N, int64_t K, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Products (PIPO, "Method", "Computation optimization")                 */
 /* ------------------------------------------------------------------ */
 

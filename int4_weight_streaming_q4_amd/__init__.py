@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "q4_abi_version": (_I32, []),
         "q4_pack": (S, [_P, _P, _I64, _I64, _P]),
         "q4_unpack": (S, [_P, _P, _I64, _I64, _P]),
+        "q4_quantize": (S, [_P, _I32, _P, _P, _I64, _I64, _P]),
         "q4_gemv": (S, [_P, _P, _P, _P, _I64, _I64, _P]),
         "q4_gemm_smallbatch": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _P]),
         "q4_gemv_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P]),
@@ -147,6 +148,24 @@ def q4_pack(codes, packed, stream=None):
 def q4_unpack(packed, codes, stream=None):
     N, K = codes.shape
     _check(lib().q4_unpack(_ptr(packed), _ptr(codes), N, K, _stream(stream)))
+
+
+DTYPE_F32, DTYPE_F16 = 0, 1
+
+
+def q4_quantize(w, packed, scales, stream=None):
+    """Quantize device weights ``w`` [N][K] (float32, or float16 / int16
+    binary16 bit patterns) into ``packed`` u8[N][K/2] and ``scales``
+    int16[N][K/32]."""
+    N, K = w.shape
+    name = str(w.dtype)
+    if name.endswith("float32"):
+        dt = DTYPE_F32
+    elif name.endswith("float16") or name.endswith("int16"):
+        dt = DTYPE_F16
+    else:
+        raise ValueError(f"q4_quantize: unsupported weight dtype {w.dtype}")
+    _check(lib().q4_quantize(_ptr(w), dt, _ptr(packed), _ptr(scales), N, K, _stream(stream)))
 
 
 def q4_gemv(packed, scales, x16, y, N=None, K=None, stream=None):

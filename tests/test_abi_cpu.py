@@ -114,6 +114,19 @@ def test_decoder_workspace_and_create_checks():
     assert "expected" in _err()
 
 
+def test_quantize_argument_checks():
+    L = q4.lib()
+    ok = dict(w=4096, dt=0, p=4096, s=4096, N=4, K=64)
+    def call(**over):
+        a = dict(ok, **over)
+        return L.q4_quantize(a["w"], a["dt"], a["p"], a["s"], a["N"], a["K"], None)
+    for over in (dict(w=0), dict(p=0), dict(s=0), dict(dt=2), dict(dt=-1), dict(N=0),
+                 dict(K=16), dict(K=48), dict(w=4100), dict(p=4104), dict(s=4097),
+                 dict(N=1 << 41)):
+        assert call(**over) == INVALID, over
+    assert "q4_quantize" in _err()
+
+
 def test_decoder_kv_cache_description_checks():
     """A KV cache adds a position word and the attention partials to the
     workspace; its description is validated before any HIP call."""
