@@ -577,6 +577,50 @@ def bench_70b_offload(args, q4, inputs, torch):
                                     "unit": "GB/s", "frac": round(h2d / link_gbs, 4),
                                     "traffic": None}})
     wstream.close()
+
+    def streamed_rate(ws, n_tok):
+        with torch.cuda.stream(comp_s):
+            for t in range(warmup):
+                h.copy_(h0[t], non_blocking=True)
+                dec.token_streamed(ws, comp_s)
+            comp_s.synchronize()
+            e0.record(comp_s)
+            for t in range(n_tok):
+                h.copy_(h0[(warmup + t) % len(h0)], non_blocking=True)
+                dec.token_streamed(ws, comp_s)
+            e1.record(comp_s)
+            comp_s.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_tok
+
+    # the same stream in 32 MB pieces alternating over two copy streams
+    copy2_s = torch.cuda.Stream()
+    chunk = 32 << 20
+    ws2 = q4.WeightStream(blobs, slots, copy_s, copy2=copy2_s, chunk_bytes=chunk)
+    ms2 = streamed_rate(ws2, steps)
+    ws2.close()
+    variants = {"one_copy_stream_whole_blobs": {"ms_per_token": round(t_wall, 3),
+                                                "tokens_per_s": round(tps, 4),
+                                                "h2d_gbps": round(h2d, 2)},
+                "two_copy_streams_32MB_pieces": {
+                    "ms_per_token": round(ms2, 3), "tokens_per_s": round(1000.0 / ms2, 4),
+                    "h2d_gbps": round(blob_bytes * n_layers / ms2 / 1e6, 2)}}
+    # partial residency: a budget of 40 layer blobs of HBM, placed by
+    # q4_offload_plan (two slots + 38 resident layers spread over the depth)
+    budget = 40 * blob_bytes
+    mask = q4.offload_plan(n_layers, blob_bytes, budget)
+    resident = [blobs[l].to("cuda") if m else None for l, m in enumerate(mask)]
+    torch.cuda.synchronize()
+    ws3 = q4.WeightStream([None if m else b for b, m in zip(blobs, mask)], slots, copy_s,
+                          copy2=copy2_s, chunk_bytes=chunk, resident=resident)
+    ms3 = streamed_rate(ws3, max(4, steps // 2))
+    ws3.close()
+    n_str = n_layers - sum(mask)
+    variants[f"resident_{sum(mask)}_of_{n_layers}_budget_40_blobs"] = {
+        "ms_per_token": round(ms3, 3), "tokens_per_s": round(1000.0 / ms3, 4),
+        "h2d_gbps": round(blob_bytes * n_str / ms3 / 1e6, 2), "streamed_layers": n_str}
+    del resident
+    res["variants"] = variants
     dec.close()
     print(json.dumps(res), flush=True)
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 
 typedef int32_t q4_status;
 #define Q4_OK 0
@@ -326,17 +326,46 @@ q4_status q4_layer_from_blob(const q4_layer *shapes, const void *base,
 typedef struct {
     int32_t n_layers;
     const void *const *host_blobs; /* host array [n_layers] of pinned host
-                                      pointers (hipHostMalloc / pinned torch) */
-    const size_t *blob_bytes;      /* host array [n_layers] */
+                                      pointers (hipHostMalloc / pinned torch);
+                                      may be NULL for resident layers */
+    const size_t *blob_bytes;      /* host array [n_layers], every layer */
     void *slot[2];                 /* two device buffers of slot_bytes */
     size_t slot_bytes;             /* >= every blob_bytes[l] */
     hipStream_t copy;              /* copy stream, not NULL */
+    /* Chunked transfer over two copy streams (PIPO, "Method", "Data
+     * transfer suite": blockwise transfer, several transfer threads).
+     * copy2: a second copy stream, or NULL for one.  chunk_bytes: a layer's
+     * copy is split into pieces of this many bytes (multiple of 256),
+     * alternating between the copy streams; 0 = one piece per layer. */
+    hipStream_t copy2;
+    size_t chunk_bytes;
+    /* Partial residency (PIPO, "Method", "Automatic configuration" and the
+     * performance / memory-efficient pipeline modes): host array
+     * [n_layers] of device pointers, 256-byte aligned, each a blob of
+     * layer l in q4_layer_blob_layout already in HBM; NULL entries (or a
+     * NULL array) are streamed.  Resident layers are never copied; the
+     * two slots serve only the streamed layers. */
+    void *const *resident;
 } q4_wstream_desc;
 
-/* Copies the description and creates events; retains every pointer. */
+/* Copies the description and creates events; retains every pointer.
+ * INVALID_ARG for a chunk size not a multiple of 256 or a misaligned
+ * resident blob. */
 q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws);
+/* Placement rule for partial residency (PIPO, "Method", "Automatic
+ * configuration": its Eq. 1 is missing from the page; reading: keep
+ * everything resident when it fits, else keep as many layers as the budget
+ * holds after the two streaming slots, spread evenly over the depth).
+ *   all n_layers * layer_bytes <= budget_bytes: every layer resident;
+ *   else k = min(n_layers - 1, (budget_bytes - 2 * layer_bytes) /
+ *   layer_bytes) layers resident, layer floor((2i + 1) * n_layers / (2k))
+ *   for i < k; UNSUPPORTED if the budget holds less than the two slots.
+ * resident: host int32[n_layers] out (1 resident, 0 streamed);
+ * *n_resident: host out, their count.  Host-only, no GPU work. */
+q4_status q4_offload_plan(int32_t n_layers, size_t layer_bytes, size_t budget_bytes,
+                          int32_t *resident, int32_t *n_resident);
 /* Starts the host->device copy of `layer` into the next slot (slots
- * alternate by call count).  If that slot was handed out by an earlier
+ * alternate by call count); STATE for a resident layer.  If that slot was handed out by an earlier
  * weight_stream_wait, all work enqueued on that call's compute stream
  * before THIS call is treated as its last use: the copy waits for it.
  * STATE if the next slot holds a layer that was begun but not yet waited. */
@@ -349,13 +378,14 @@ q4_status weight_stream_wait(void *ws, int32_t layer, hipStream_t compute,
 /* Destroys events.  Call after all enqueued work has completed. */
 q4_status q4_wstream_destroy(void *ws);
 
-/* One token of the decoder with every layer streamed through `ws`: layer 0
- * is begun (unless already begun by the previous token), then for each
- * layer l the copy of l+1 is begun before l is waited and computed on
- * `compute`.  The blob layout must be q4_layer_blob_layout of the decoder's
- * shapes.  The copy of the next token's layer 0 is begun at the end.  With
- * a KV cache layer l attends over cache slice l at the context length set
- * by q4_decoder_set_context. */
+/* One token of the decoder with its layers streamed through `ws`: the
+ * first streamed layer is begun (unless already begun by the previous
+ * token), then for each layer l in order: a resident layer is computed
+ * from its blob; a streamed layer has the copy of the next streamed layer
+ * (wrapping to the next token's first) begun before l is waited and
+ * computed on `compute`.  The blob layout must be q4_layer_blob_layout of
+ * the decoder's shapes.  With a KV cache layer l attends over cache slice
+ * l at the context length set by q4_decoder_set_context. */
 q4_status q4_decode_token_streamed(void *dec, void *ws, hipStream_t compute);
 
 #ifdef __cplusplus

@@ -54,7 +54,8 @@ class ModelDesc(ctypes.Structure):
 class WStreamDesc(ctypes.Structure):
     _fields_ = [("n_layers", _I32), ("host_blobs", ctypes.POINTER(_P)),
                 ("blob_bytes", ctypes.POINTER(ctypes.c_size_t)), ("slot", _P * 2),
-                ("slot_bytes", ctypes.c_size_t), ("copy", _P)]
+                ("slot_bytes", ctypes.c_size_t), ("copy", _P), ("copy2", _P),
+                ("chunk_bytes", ctypes.c_size_t), ("resident", ctypes.POINTER(_P))]
 
 
 _lib = None
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "q4_layer_from_blob": (S, [ctypes.POINTER(Layer), _P, ctypes.POINTER(Layer)]),
         "q4_wstream_create": (S, [ctypes.POINTER(WStreamDesc), ctypes.POINTER(_P)]),
+        "q4_offload_plan": (S, [_I32, ctypes.c_size_t, ctypes.c_size_t, ctypes.POINTER(_I32),
+                                ctypes.POINTER(_I32)]),
         "weight_stream_begin": (S, [_P, _I32]),
         "weight_stream_wait": (S, [_P, _I32, _P, ctypes.POINTER(_P)]),
         "q4_wstream_destroy": (S, [_P]),
@@ -345,16 +348,23 @@ def decode_step_graph(dec: Decoder, ctx_len: int, stream=None):
 class WeightStream:
     """Two-slot device pool fed from pinned host blobs over a copy stream."""
 
-    def __init__(self, host_blobs, slots, copy_stream):
+    def __init__(self, host_blobs, slots, copy_stream, copy2=None, chunk_bytes=0,
+                 resident=None):
+        """``host_blobs``: pinned host tensors per layer (None where
+        ``resident`` holds the layer's device blob); ``copy2`` and
+        ``chunk_bytes``: chunked transfer over two copy streams."""
         n = len(host_blobs)
+        resident = resident or [None] * n
+        sizes = [(b if b is not None else r) for b, r in zip(host_blobs, resident)]
         self._blob_ptrs = (_P * n)(*(_ptr(b) for b in host_blobs))
-        self._blob_bytes = (ctypes.c_size_t * n)(*(b.numel() * b.element_size()
-                                                   for b in host_blobs))
+        self._blob_bytes = (ctypes.c_size_t * n)(*(t.numel() * t.element_size() for t in sizes))
+        self._resident = (_P * n)(*(_ptr(r) for r in resident))
         slot_bytes = min(s.numel() * s.element_size() for s in slots)
         desc = WStreamDesc(n, self._blob_ptrs, self._blob_bytes,
                            (_P * 2)(_ptr(slots[0]), _ptr(slots[1])), slot_bytes,
-                           _stream(copy_stream))
-        self._keep = (host_blobs, slots, copy_stream)
+                           _stream(copy_stream), _stream(copy2) if copy2 is not None else None,
+                           int(chunk_bytes), self._resident)
+        self._keep = (host_blobs, slots, copy_stream, copy2, resident)
         handle = _P()
         _check(lib().q4_wstream_create(ctypes.byref(desc), ctypes.byref(handle)))
         self.handle = handle.value
@@ -378,6 +388,14 @@ class WeightStream:
             self.close()
         except Exception:
             pass
+
+
+def offload_plan(n_layers: int, layer_bytes: int, budget_bytes: int):
+    """Resident flags (list of 0/1) chosen by q4_offload_plan."""
+    out = (_I32 * n_layers)()
+    k = _I32()
+    _check(lib().q4_offload_plan(n_layers, layer_bytes, budget_bytes, out, ctypes.byref(k)))
+    return list(out)
 
 
 def weight_stream_begin(ws: WeightStream, layer: int):

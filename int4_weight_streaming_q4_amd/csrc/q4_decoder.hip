@@ -271,7 +271,11 @@ struct WStream {
     void *slot[2] = {nullptr, nullptr};
     size_t slot_bytes = 0;
     hipStream_t copy = nullptr;
+    hipStream_t copy2 = nullptr;       // second copy stream (chunked transfer), may be null
+    size_t chunk = 0;                  // bytes per piece, 0 = whole blob
+    std::vector<void *> resident;      // device blob per layer, null = streamed
     hipEvent_t loaded[2] = {nullptr, nullptr};
+    hipEvent_t loaded2[2] = {nullptr, nullptr}; // on copy2
     hipEvent_t freed[2] = {nullptr, nullptr};
     int state[2] = {kEmpty, kEmpty};
     int32_t layer_in[2] = {-1, -1};
@@ -284,6 +288,8 @@ void destroy_wstream(WStream *w) {
     for (int i = 0; i < 2; ++i) {
         if (w->loaded[i])
             (void)hipEventDestroy(w->loaded[i]);
+        if (w->loaded2[i])
+            (void)hipEventDestroy(w->loaded2[i]);
         if (w->freed[i])
             (void)hipEventDestroy(w->freed[i]);
     }
@@ -560,7 +566,16 @@ extern "C" q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws_out) 
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: null slot or copy stream");
     if (!q4::aligned(d->slot[0], 256) || !q4::aligned(d->slot[1], 256))
         return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: slots must be 256-byte aligned");
+    if (d->chunk_bytes % 256 != 0)
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_wstream_create: chunk_bytes %zu not a multiple of 256", d->chunk_bytes);
     for (int32_t l = 0; l < d->n_layers; ++l) {
+        if (d->resident && d->resident[l]) {
+            if (!q4::aligned(d->resident[l], 256))
+                return q4::fail(Q4_ERR_INVALID_ARG,
+                                "q4_wstream_create: resident blob %d not 256-byte aligned", l);
+            continue;
+        }
         if (!d->host_blobs[l])
             return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_create: null blob %d", l);
         if (d->blob_bytes[l] > d->slot_bytes)
@@ -578,10 +593,17 @@ extern "C" q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws_out) 
     w->slot[1] = d->slot[1];
     w->slot_bytes = d->slot_bytes;
     w->copy = d->copy;
+    w->copy2 = d->copy2;
+    w->chunk = d->chunk_bytes;
+    w->resident.assign((size_t)d->n_layers, nullptr);
+    if (d->resident)
+        for (int32_t l = 0; l < d->n_layers; ++l)
+            w->resident[l] = d->resident[l];
     for (int i = 0; i < 2; ++i) {
         hipError_t e1 = hipEventCreateWithFlags(&w->loaded[i], hipEventDisableTiming);
         hipError_t e2 = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
-        if (e1 != hipSuccess || e2 != hipSuccess) {
+        hipError_t e3 = hipEventCreateWithFlags(&w->loaded2[i], hipEventDisableTiming);
+        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
             q4::destroy_wstream(w);
             return q4::fail(Q4_ERR_HIP, "q4_wstream_create: event creation failed");
         }
@@ -596,6 +618,8 @@ extern "C" q4_status weight_stream_begin(void *wsp, int32_t layer) {
         return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_begin: null stream object");
     if (layer < 0 || layer >= w->n_layers)
         return q4::fail(Q4_ERR_INVALID_ARG, "weight_stream_begin: layer %d out of range", layer);
+    if (w->resident[layer])
+        return q4::fail(Q4_ERR_STATE, "weight_stream_begin: layer %d is resident", layer);
     const int s = (int)(w->n_begun & 1);
     if (w->state[s] == q4::kLoading)
         return q4::fail(Q4_ERR_STATE,
@@ -606,10 +630,22 @@ extern "C" q4_status weight_stream_begin(void *wsp, int32_t layer) {
         // of this slot: the copy may overwrite it only after that work.
         Q4_HIP(hipEventRecord(w->freed[s], w->consumer[s]));
         Q4_HIP(hipStreamWaitEvent(w->copy, w->freed[s], 0));
+        if (w->copy2)
+            Q4_HIP(hipStreamWaitEvent(w->copy2, w->freed[s], 0));
     }
-    Q4_HIP(hipMemcpyAsync(w->slot[s], w->blobs[layer], w->bytes[layer], hipMemcpyHostToDevice,
-                          w->copy));
+    const size_t total = w->bytes[layer];
+    const size_t piece = w->chunk ? w->chunk : total;
+    char *dst = static_cast<char *>(w->slot[s]);
+    const char *src = static_cast<const char *>(w->blobs[layer]);
+    int k = 0;
+    for (size_t off = 0; off < total; off += piece, ++k) {
+        const size_t n = std::min(piece, total - off);
+        hipStream_t cs = (w->copy2 && (k & 1)) ? w->copy2 : w->copy;
+        Q4_HIP(hipMemcpyAsync(dst + off, src + off, n, hipMemcpyHostToDevice, cs));
+    }
     Q4_HIP(hipEventRecord(w->loaded[s], w->copy));
+    if (w->copy2)
+        Q4_HIP(hipEventRecord(w->loaded2[s], w->copy2));
     w->state[s] = q4::kLoading;
     w->layer_in[s] = layer;
     w->consumer[s] = nullptr;
@@ -629,10 +665,36 @@ extern "C" q4_status weight_stream_wait(void *wsp, int32_t layer, hipStream_t co
         return q4::fail(Q4_ERR_STATE, "weight_stream_wait: layer %d is not the next begun layer",
                         layer);
     Q4_HIP(hipStreamWaitEvent(compute, w->loaded[s], 0));
+    if (w->copy2)
+        Q4_HIP(hipStreamWaitEvent(compute, w->loaded2[s], 0));
     w->state[s] = q4::kInUse;
     w->consumer[s] = compute;
     ++w->n_waited;
     *slot_ptr = w->slot[s];
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_offload_plan(int32_t n_layers, size_t layer_bytes, size_t budget_bytes,
+                                     int32_t *resident, int32_t *n_resident) {
+    if (n_layers < 1 || layer_bytes == 0 || !resident || !n_resident)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_offload_plan: need n_layers >= 1, layer_bytes > 0 "
+                                            "and output arrays");
+    for (int32_t l = 0; l < n_layers; ++l)
+        resident[l] = 0;
+    if (budget_bytes / layer_bytes >= (size_t)n_layers) {
+        for (int32_t l = 0; l < n_layers; ++l)
+            resident[l] = 1;
+        *n_resident = n_layers;
+        return Q4_OK;
+    }
+    if (budget_bytes / layer_bytes < 2)
+        return q4::fail(Q4_ERR_UNSUPPORTED,
+                        "q4_offload_plan: budget of %zu bytes holds fewer than the two slots",
+                        budget_bytes);
+    const int64_t k = std::min<int64_t>(n_layers - 1, (int64_t)(budget_bytes / layer_bytes) - 2);
+    for (int64_t i = 0; i < k; ++i)
+        resident[(2 * i + 1) * n_layers / (2 * k)] = 1;
+    *n_resident = (int32_t)k;
     return Q4_OK;
 }
 
@@ -662,18 +724,33 @@ extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t
                             w->bytes[l], bytes);
     const int L = w->n_layers;
     dec->att_chunks = q4::attention_chunks(dec->ctx);
-    const int s0 = (int)(w->n_waited & 1);
-    const bool prefetched = w->state[s0] == q4::kLoading && w->layer_in[s0] == 0;
-    if (!prefetched)
-        Q4_CHECK(weight_stream_begin(w, 0));
+    std::vector<int32_t> streamed;
+    for (int l = 0; l < L; ++l)
+        if (!w->resident[l])
+            streamed.push_back(l);
+    const int S = (int)streamed.size();
+    if (S > 0) {
+        const int s0 = (int)(w->n_waited & 1);
+        const bool prefetched =
+            w->state[s0] == q4::kLoading && w->layer_in[s0] == streamed[0];
+        if (!prefetched)
+            Q4_CHECK(weight_stream_begin(w, streamed[0]));
+    }
+    int j = 0; // position of the next streamed layer
     for (int l = 0; l < L; ++l) {
-        // The copy of the following layer (after the last layer: the next
-        // token's first layer) overlaps this layer's compute.
-        Q4_CHECK(weight_stream_begin(w, (l + 1) % L));
-        void *slot = nullptr;
-        Q4_CHECK(weight_stream_wait(w, l, compute, &slot));
         q4_layer layer;
-        Q4_CHECK(q4_layer_from_blob(&shapes, slot, &layer));
+        if (w->resident[l]) {
+            Q4_CHECK(q4_layer_from_blob(&shapes, w->resident[l], &layer));
+        } else {
+            // The copy of the following streamed layer (after the last: the
+            // next token's first) overlaps this layer's compute and that of
+            // the resident layers in between.
+            Q4_CHECK(weight_stream_begin(w, streamed[(j + 1) % S]));
+            void *slot = nullptr;
+            Q4_CHECK(weight_stream_wait(w, l, compute, &slot));
+            Q4_CHECK(q4_layer_from_blob(&shapes, slot, &layer));
+            ++j;
+        }
         Q4_CHECK(q4::enqueue_layer(dec, layer, l, compute));
     }
     return Q4_OK;

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 20, names
     for n in names:
         assert hasattr(L, n), n
-    assert q4.abi_version() == 2
+    assert q4.abi_version() == 3
 
 
 def _err():
@@ -220,6 +220,46 @@ def test_wstream_argument_checks():
     assert L.q4_wstream_create(ctypes.byref(d3), ctypes.byref(out)) == INVALID
     d4 = q4.WStreamDesc(2, blobs, sizes, (ctypes.c_void_p * 2)(4096, 8192), 8192, None)
     assert L.q4_wstream_create(ctypes.byref(d4), ctypes.byref(out)) == INVALID
+    # chunked transfer: pieces of a multiple of 256 bytes
+    d5 = q4.WStreamDesc(2, blobs, sizes, (ctypes.c_void_p * 2)(4096, 8192), 8192, 1234, 5678,
+                        100, None)
+    assert L.q4_wstream_create(ctypes.byref(d5), ctypes.byref(out)) == INVALID
+    assert "multiple of 256" in _err()
+    # a resident blob must be 256-byte aligned; a resident layer needs no host blob
+    res = (ctypes.c_void_p * 2)(4096 + 16, None)
+    d6 = q4.WStreamDesc(2, (ctypes.c_void_p * 2)(None, 8192), sizes,
+                        (ctypes.c_void_p * 2)(4096, 8192), 8192, 1234, None, 0, res)
+    assert L.q4_wstream_create(ctypes.byref(d6), ctypes.byref(out)) == INVALID
+    assert "aligned" in _err()
     assert L.weight_stream_begin(None, 0) == INVALID
     slot = ctypes.c_void_p()
     assert L.weight_stream_wait(None, 0, None, ctypes.byref(slot)) == INVALID
+
+
+def test_offload_plan():
+    """Placement for partial residency: everything resident when it fits;
+    else the budget minus two streaming slots, spread evenly; too small a
+    budget is UNSUPPORTED."""
+    LB = 481_296_384                     # 70B layer blob
+    assert q4.offload_plan(80, LB, 80 * LB) == [1] * 80
+    assert q4.offload_plan(80, LB, 200 * LB) == [1] * 80
+    flags = q4.offload_plan(80, LB, 2 * LB)
+    assert flags == [0] * 80             # only the two slots fit
+    for budget_layers in (3, 10, 42, 79):
+        flags = q4.offload_plan(80, LB, budget_layers * LB + LB // 2)
+        k = budget_layers - 2
+        assert sum(flags) == k
+        idx = [i for i, f in enumerate(flags) if f]
+        assert idx == [(2 * i + 1) * 80 // (2 * k) for i in range(k)]
+        gaps = [b - a for a, b in zip(idx, idx[1:])]
+        assert not gaps or max(gaps) - min(gaps) <= 1       # evenly spread
+        assert (k + 2) * LB <= budget_layers * LB + LB // 2  # within the budget
+    assert q4.offload_plan(1, LB, LB) == [1]
+    flags = q4.offload_plan(5, 10, 49)   # 4 fit after nothing else: 4 - 2 = 2 resident
+    assert sum(flags) == 2
+    L = q4.lib()
+    arr = (ctypes.c_int32 * 4)()
+    k = ctypes.c_int32()
+    assert L.q4_offload_plan(4, 100, 150, arr, ctypes.byref(k)) == UNSUPPORTED
+    assert L.q4_offload_plan(0, 100, 150, arr, ctypes.byref(k)) == INVALID
+    assert L.q4_offload_plan(4, 0, 150, arr, ctypes.byref(k)) == INVALID

@@ -56,13 +56,21 @@ def resident_tokens(dims, layers, h0s):
 
 
 class Streamed:
-    def __init__(self, dims, layers):
+    def __init__(self, dims, layers, copy2=False, chunk=0, resident_mask=None):
         self.dims = dims
         self.blobs, total = blobs_for(dims, layers)
         self.slots = [torch.empty(total, dtype=torch.uint8, device=DEV) for _ in range(2)]
         self.copy = torch.cuda.Stream()
+        self.copy2 = torch.cuda.Stream() if copy2 else None
         self.compute = torch.cuda.Stream()
-        self.ws = q4.WeightStream(self.blobs, self.slots, self.copy)
+        host, resident = list(self.blobs), None
+        if resident_mask is not None:
+            resident = [b.to(DEV) if m else None for b, m in zip(self.blobs, resident_mask)]
+            host = [None if m else b for b, m in zip(self.blobs, resident_mask)]
+            torch.cuda.synchronize()
+        self.resident_mask = resident_mask or [0] * len(layers)
+        self.ws = q4.WeightStream(host, self.slots, self.copy, copy2=self.copy2,
+                                  chunk_bytes=chunk, resident=resident)
         self.h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
         self.wsp = torch.zeros(q4.workspace_bytes(dims, n_layers=len(layers)), dtype=torch.uint8,
                                device=DEV)
@@ -78,18 +86,21 @@ class Streamed:
         self.compute.synchronize()
         return self.h.cpu().clone()
 
+    def _stall_copies(self, cycles):
+        for cs in (self.copy, self.copy2):
+            if cs is not None and cycles:
+                with torch.cuda.stream(cs):
+                    torch.cuda._sleep(cycles)
+
     def token_python(self, stall_copy=0, stall_compute=0, poison=False):
-        """Same loop driven from Python, with optional stalls."""
+        """Same loop driven from Python (every layer streamed), with optional
+        stalls of the copy streams or of the compute stream."""
         n = self.n
         for l in range(n):
             if l == 0 and not getattr(self, "_pref", False):
-                if stall_copy:
-                    with torch.cuda.stream(self.copy):
-                        torch.cuda._sleep(stall_copy)
+                self._stall_copies(stall_copy)
                 self.ws.begin(0)
-            if stall_copy:
-                with torch.cuda.stream(self.copy):
-                    torch.cuda._sleep(stall_copy)
+            self._stall_copies(stall_copy)
             self.ws.begin((l + 1) % n)
             self._pref = True
             ptr = self.ws.wait(l, self.compute)
@@ -156,6 +167,71 @@ def test_70b_shapes_streamed_equals_resident():
     h0s = _h0s(dims, 5, 2)
     want = resident_tokens(dims, layers, h0s)
     st = Streamed(dims, layers)
+    for t, h0 in enumerate(h0s):
+        st.set_h(h0)
+        assert torch.equal(st.token_native(), want[t]), t
+
+
+@pytest.mark.parametrize("mask", [[1, 0, 1, 0, 1, 0], [0, 1, 1, 1, 1, 1], [1, 1, 1, 1, 1, 0],
+                                  [1, 1, 1, 1, 1, 1], [0, 0, 0, 0, 0, 0], "plan"])
+def test_partial_residency_equals_resident(mask):
+    """Resident layers are computed from their device blobs, the others are
+    streamed through the two slots: the same residual bitwise."""
+    n = 6
+    layers = [inputs.layer_weights(TINY, 98, l, device=DEV) for l in range(n)]
+    if mask == "plan":
+        _, total = q4.layer_blob_layout(TINY)
+        mask = q4.offload_plan(n, total, 5 * total)       # 3 resident, spread
+        assert mask == [0, 1, 0, 1, 0, 1]
+    h0s = _h0s(TINY, 98, 3)
+    want = resident_tokens(TINY, layers, h0s)
+    st = Streamed(TINY, layers, resident_mask=mask)
+    for t, h0 in enumerate(h0s):
+        st.set_h(h0)
+        assert torch.equal(st.token_native(), want[t]), (mask, t)
+    if any(mask):
+        with pytest.raises(q4.Q4Error, match="STATE"):
+            st.ws.begin(mask.index(1))                     # a resident layer is not streamed
+    st.copy.synchronize()
+
+
+@pytest.mark.parametrize("copy2,chunk", [(False, 256), (True, 256), (True, 4096), (True, 0)])
+def test_chunked_two_streams_equals_resident(copy2, chunk):
+    n = 5
+    layers = [inputs.layer_weights(TINY, 99, l, device=DEV) for l in range(n)]
+    h0s = _h0s(TINY, 99, 3)
+    want = resident_tokens(TINY, layers, h0s)
+    st = Streamed(TINY, layers, copy2=copy2, chunk=chunk)
+    for t, h0 in enumerate(h0s):
+        st.set_h(h0)
+        assert torch.equal(st.token_native(), want[t]), (copy2, chunk, t)
+
+
+def test_chunked_two_streams_under_stalls():
+    """Stalls on both copy streams (read-after-write: compute must wait for
+    the pieces on either stream) and on the compute stream (write-after-
+    read: neither copy stream may overwrite a slot still being read)."""
+    n = 5
+    layers = [inputs.layer_weights(TINY, 100, l, device=DEV) for l in range(n)]
+    h0s = _h0s(TINY, 100, 2)
+    want = resident_tokens(TINY, layers, h0s)
+    for kind in ("copy", "compute"):
+        st = Streamed(TINY, layers, copy2=True, chunk=256)
+        for t, h0 in enumerate(h0s):
+            st.set_h(h0)
+            got = st.token_python(stall_copy=2_000_000 if kind == "copy" else 0,
+                                  stall_compute=2_000_000 if kind == "compute" else 0)
+            assert torch.equal(got, want[t]), (kind, t)
+
+
+def test_70b_shapes_partial_residency_chunked():
+    """Four 70B-shape layers, two resident and two streamed in 32 MB pieces
+    over two copy streams, equal to all-resident bitwise."""
+    dims = {k: v for k, v in inputs.MODEL_DIMS["70b"].items() if k != "n_layers"}
+    layers = [inputs.layer_weights(dims, 5, l, device=DEV) for l in range(4)]
+    h0s = _h0s(dims, 5, 2)
+    want = resident_tokens(dims, layers, h0s)
+    st = Streamed(dims, layers, copy2=True, chunk=32 << 20, resident_mask=[1, 0, 0, 1])
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
         assert torch.equal(st.token_native(), want[t]), t
