@@ -172,6 +172,7 @@ def main():
     }
 
     result["quantize"] = quantize_rate(q4, torch)
+    result["verify_step"] = verify_rates(q4, inputs, torch, dims, layers, ms_per_step)
     if not args.no_attention:
         dec.close()
         del ws
@@ -179,6 +180,37 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_tokens)
     print(json.dumps(result), flush=True)
+
+
+def verify_rates(q4, inputs, torch, dims, layers, decode_ms, reps=20):
+    """Verify step of a speculative draft (B token columns through the 32
+    layers together, graph-captured) at B = 1, 2, 4, 8, 9, 16: ms per step
+    and the tokens it checks per second, next to B single-token steps."""
+    mb = 16
+    h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
+    hb = torch.stack([inputs.residual_f32(dims["d"], inputs.seed_of(2, t, 9), device="cuda")
+                      for t in range(mb)])
+    ws = torch.zeros(q4.workspace_bytes(dims, len(layers), max_batch=mb), dtype=torch.uint8,
+                     device="cuda")
+    dec = q4.Decoder(dims, layers, h, ws, max_batch=mb, h_batch=hb)
+    stream = torch.cuda.Stream()
+    out = {}
+    for B in (1, 2, 4, 8, 9, 16):
+        with torch.cuda.stream(stream):
+            dec.verify_graph(B, stream)
+            dec.verify_graph(B, stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                dec.verify_graph(B, stream)
+            e1.record(stream)
+        stream.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"B{B}"] = {"ms": round(ms, 4), "tokens_checked_per_s": round(B * 1000.0 / ms, 1),
+                        "vs_B_decode_steps": round(B * decode_ms / ms, 3)}
+    dec.close()
+    return out
 
 
 def quantize_rate(q4, torch, N=28672, K=4096, reps=10):

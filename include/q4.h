@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 
 typedef int32_t q4_status;
 #define Q4_OK 0
@@ -203,6 +203,18 @@ typedef struct {
     void *kv_cache;
     int32_t max_ctx;           /* rows per cache, 1..2^20 */
     float rope_base;           /* rotary base (theta), > 0, e.g. 500000 */
+    /* Batched verify step (PipeInfer, "Run" / "Tuning PipeInfer":
+     * speculative micro-batches of a few draft tokens; PIPO, "Method",
+     * "Automatic configuration": 4-bit kernel below batch 16).  max_batch
+     * 0 = none, else 1..16 columns; h_batch: device f32[max_batch][d_model],
+     * 16-byte aligned, retained, the residual columns in/out.  With
+     * max_batch > 0 the workspace also holds, after the sections above,
+     * 256-byte aligned: binary16 [max_batch][d_model] (normed input),
+     * fp32 [max_batch][(H + 2 Hkv) hd] (QKV), binary16 [max_batch][H hd]
+     * (attention output), fp32 [max_batch][2 d_ff] (gate+up), binary16
+     * [max_batch][d_ff] (gated MLP activation). */
+    int32_t max_batch;
+    float *h_batch;
 } q4_model_desc;
 
 /*
@@ -304,6 +316,21 @@ q4_status q4_decoder_set_context(void *dec, int32_t ctx_len, hipStream_t stream)
  * listed above).  INVALID_ARG for another index or bad shapes. */
 q4_status q4_decode_layer_part(void *dec, const q4_layer *layer, int32_t which,
                                hipStream_t stream);
+/* Verify step: the first B columns of h_batch (1 <= B <= max_batch), each
+ * the residual of one token, go through all resident layers together: per
+ * layer, per column RMSNorm to binary16, the QKV, O, gate+up and down
+ * products as small-batch INT4 products of B columns (q4_gemm_smallbatch's
+ * kernels; O and down add into h_batch), and the one-token glue between
+ * them per column.  Column b ends exactly as if its token were decoded
+ * alone (B = 1 runs the single-token kernels and equals
+ * q4_decode_step_eager bitwise).  Eager enqueue on `stream`.  STATE
+ * without resident layers or without max_batch; UNSUPPORTED with a KV
+ * cache (causal attention across the batch is not built); INVALID_ARG for
+ * B outside 1..max_batch. */
+q4_status q4_decode_verify_eager(void *dec, int32_t B, hipStream_t stream);
+/* The same, captured once per B as a HIP graph on `stream` (not NULL) and
+ * replayed. */
+q4_status q4_decode_verify_graph(void *dec, int32_t B, hipStream_t stream);
 /* Frees graphs and host state.  Call after the last step has completed. */
 q4_status q4_decoder_destroy(void *dec);
 

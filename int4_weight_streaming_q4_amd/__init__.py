@@ -48,7 +48,8 @@ class ModelDesc(ctypes.Structure):
                 ("n_kv_heads", _I32), ("head_dim", _I32), ("d_ff", _I32),
                 ("eps", ctypes.c_float), ("layers", ctypes.POINTER(Layer)),
                 ("h", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-                ("kv_cache", _P), ("max_ctx", _I32), ("rope_base", ctypes.c_float)]
+                ("kv_cache", _P), ("max_ctx", _I32), ("rope_base", ctypes.c_float),
+                ("max_batch", _I32), ("h_batch", _P)]
 
 
 class WStreamDesc(ctypes.Structure):
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         "q4_decoder_set_persistent": (S, [_P, _I32]),
         "q4_decoder_check": (S, [_P]),
         "q4_decoder_set_context": (S, [_P, _I32, _P]),
+        "q4_decode_verify_eager": (S, [_P, _I32, _P]),
+        "q4_decode_verify_graph": (S, [_P, _I32, _P]),
         "q4_layer_blob_layout": (S, [ctypes.POINTER(Layer), ctypes.c_size_t * 8,
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "q4_layer_from_blob": (S, [ctypes.POINTER(Layer), _P, ctypes.POINTER(Layer)]),
@@ -229,10 +232,10 @@ def layer_blob_layout(dims: dict):
 
 
 def _model_desc(dims, n_layers, layers_arr, h, workspace, ws_bytes, eps, kv_cache=None,
-                max_ctx=0, rope_base=500000.0):
+                max_ctx=0, rope_base=500000.0, max_batch=0, h_batch=None):
     return ModelDesc(n_layers, dims["d"], dims["H"], dims["Hkv"], dims["hd"], dims["dff"],
                      eps, layers_arr, _ptr(h), _ptr(workspace), ws_bytes, _ptr(kv_cache),
-                     int(max_ctx), float(rope_base))
+                     int(max_ctx), float(rope_base), int(max_batch), _ptr(h_batch))
 
 
 def kv_cache_elems(dims: dict, n_layers: int, max_ctx: int) -> int:
@@ -242,12 +245,14 @@ def kv_cache_elems(dims: dict, n_layers: int, max_ctx: int) -> int:
 
 
 def workspace_bytes(dims: dict, n_layers: int = None, eps: float = 1e-5,
-                    max_ctx: int = 0) -> int:
+                    max_ctx: int = 0, max_batch: int = 0) -> int:
     """Workspace bytes of a decoder; max_ctx > 0 sizes it for a KV cache of
-    that many rows (the attention partials)."""
+    that many rows (the attention partials), max_batch > 0 for verify
+    batches of up to that many columns."""
     n = n_layers if n_layers is not None else dims.get("n_layers", 1)
     # a non-NULL stand-in: only the sizes of a cache are read here
-    desc = _model_desc(dims, n, None, 0, 0, 0, eps, 256 if max_ctx > 0 else None, max_ctx)
+    desc = _model_desc(dims, n, None, 0, 0, 0, eps, 256 if max_ctx > 0 else None, max_ctx,
+                       500000.0, max_batch)
     out = ctypes.c_size_t()
     _check(lib().q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
     return out.value
@@ -260,17 +265,17 @@ class Decoder:
 
     def __init__(self, dims: dict, layers, h, workspace, eps: float = 1e-5,
                  n_layers=None, kv_cache=None, max_ctx: int = 0,
-                 rope_base: float = 500000.0):
+                 rope_base: float = 500000.0, max_batch: int = 0, h_batch=None):
         self.dims = dict(dims)
         n = len(layers) if layers is not None else (n_layers or dims.get("n_layers", 1))
         arr = None
         if layers is not None:
             arr = (Layer * n)(*(make_layer(w) for w in layers))
-        self._keep = (layers, h, workspace, arr, kv_cache)  # buffers the graphs bake in
+        self._keep = (layers, h, workspace, arr, kv_cache, h_batch)  # buffers graphs bake in
         self._n_layers = n
         self._has_kv = kv_cache is not None
         desc = _model_desc(dims, n, arr, h, workspace, workspace.numel(), eps, kv_cache,
-                           max_ctx, rope_base)
+                           max_ctx, rope_base, max_batch, h_batch)
         handle = _P()
         _check(lib().q4_decoder_create(ctypes.byref(desc), ctypes.byref(handle)))
         self.handle = handle.value
@@ -288,6 +293,13 @@ class Decoder:
         """Context length of the next eager step or layer-by-layer token
         (decoders with a KV cache)."""
         _check(lib().q4_decoder_set_context(self.handle, int(ctx_len), _stream(stream)))
+
+    def verify_eager(self, B: int, stream=None):
+        """B residual columns of h_batch through all layers (verify step)."""
+        _check(lib().q4_decode_verify_eager(self.handle, int(B), _stream(stream)))
+
+    def verify_graph(self, B: int, stream=None):
+        _check(lib().q4_decode_verify_graph(self.handle, int(B), _stream(stream)))
 
     def check(self):
         """Raise if a persistent step's grid barrier timed out (synchronous)."""

@@ -22,6 +22,7 @@
 #include "q4_internal.h"
 #include "q4_persistent.h"
 #include "q4_attention.h"
+#include "q4_verify.h"
 
 namespace q4 {
 namespace {
@@ -56,6 +57,14 @@ struct Decoder {
     int32_t ctx = 1;             // context length of eager / layer-by-layer steps
     int32_t att_chunks = 1;      // chunks the attention kernels cover
     int32_t cursor = 0;          // next layer of a layer-by-layer token
+    // batched verify step (max_batch columns)
+    float *hb = nullptr;         // caller's f32[max_batch][d]
+    uint16_t *xb = nullptr;      // f16[max_batch][d]
+    float *qkvb = nullptr;       // f32[max_batch][nqkv]
+    uint16_t *oinb = nullptr;    // f16[max_batch][H*hd]
+    float *gub = nullptr;        // f32[max_batch][2 dff]
+    uint16_t *mlpb = nullptr;    // f16[max_batch][dff]
+    hipGraphExec_t vexec[Q4_MAX_BATCH + 1] = {};
 };
 
 q4_status dims_of(const q4_model_desc *m, Dims *out) {
@@ -91,8 +100,20 @@ q4_status dims_of(const q4_model_desc *m, Dims *out) {
                         "decoder: attention needs n_heads/n_kv_heads in {1,2,4,8} and head_dim "
                         "64 or 128");
     }
+    if (m->max_batch < 0 || m->max_batch > Q4_MAX_BATCH)
+        return fail(Q4_ERR_INVALID_ARG, "decoder: max_batch %d outside 0..%d", m->max_batch,
+                    Q4_MAX_BATCH);
     *out = d;
     return Q4_OK;
+}
+
+// Bytes of the verify-step sections for `mb` columns.
+size_t verify_bytes(const Dims &d, int32_t mb) {
+    if (mb <= 0)
+        return 0;
+    return align256((size_t)mb * d.d * 2) + align256((size_t)mb * d.nqkv * 4) +
+           align256((size_t)mb * d.H * d.hd * 2) + align256((size_t)mb * 2 * d.dff * 4) +
+           align256((size_t)mb * d.dff * 2);
 }
 
 size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) {
@@ -104,6 +125,8 @@ size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) 
              align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv, (int32_t)d.hd,
                                               m->max_ctx)) +
              align256(rope_table_bytes(m->max_ctx, (int32_t)d.hd));
+    if (m)
+        b += verify_bytes(d, m->max_batch);
     return b;
 }
 
@@ -261,6 +284,70 @@ q4_status enqueue_all(Decoder *dec, hipStream_t s) {
     return Q4_OK;
 }
 
+// Verify step: B residual columns of dec->hb through every resident layer.
+// B = 1 runs the single-token kernels on the batch buffers.
+q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
+    const Dims &d = dec->dims;
+    const float eps = dec->desc.eps;
+    for (const q4_layer &L : dec->layers) {
+        if (B == 1) {
+            EpiArgs ea{};
+            ea.y = dec->qkvb;
+            ea.out16 = dec->oinb;
+            ea.v_off = (d.H + d.Hkv) * d.hd;
+            ea.hd = (int32_t)d.hd;
+            ea.group = (int32_t)(d.H / d.Hkv);
+            ea.eps = eps;
+            Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->hb, Pro::RmsNorm, L.qkv.N,
+                                 L.qkv.K, Epi::QkvGather, ea, s));
+            ea = EpiArgs{};
+            ea.y = dec->hb;
+            Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oinb, Pro::F16, L.o.N, L.o.K,
+                                 Epi::Residual, ea, s));
+            ea = EpiArgs{};
+            ea.out16 = dec->mlpb;
+            ea.pair_off = d.dff;
+            ea.eps = eps;
+            ea.norm_out = dec->xb;
+            Q4_CHECK(launch_gemv(L.gate_up.packed, L.gate_up.scales, dec->hb, Pro::RmsNorm,
+                                 L.gate_up.N, L.gate_up.K, Epi::SiluPair, ea, s));
+            ea = EpiArgs{};
+            ea.y = dec->hb;
+            Q4_CHECK(launch_gemv(L.down.packed, L.down.scales, dec->mlpb, Pro::F16, L.down.N,
+                                 L.down.K, Epi::Residual, ea, s));
+            continue;
+        }
+        Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
+        Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb, L.qkv.N,
+                                  L.qkv.K, B, s));
+        Q4_CHECK(launch_gather_batch(dec->qkvb, dec->oinb, B, (int32_t)d.H, (int32_t)d.Hkv,
+                                     (int32_t)d.hd, s));
+        Q4_CHECK(launch_gemm_mfma(L.o.packed, L.o.scales, dec->oinb, dec->hb, L.o.N, L.o.K, B, s,
+                                  true));
+        Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
+        Q4_CHECK(launch_gemm_mfma(L.gate_up.packed, L.gate_up.scales, dec->xb, dec->gub,
+                                  L.gate_up.N, L.gate_up.K, B, s));
+        Q4_CHECK(launch_silu_batch(dec->gub, dec->mlpb, B, (int32_t)d.dff, s));
+        Q4_CHECK(launch_gemm_mfma(L.down.packed, L.down.scales, dec->mlpb, dec->hb, L.down.N,
+                                  L.down.K, B, s, true));
+    }
+    return Q4_OK;
+}
+
+q4_status check_verify(Decoder *dec, int32_t B, const char *what) {
+    if (!dec)
+        return fail(Q4_ERR_INVALID_ARG, "%s: null decoder", what);
+    if (dec->layers.empty())
+        return fail(Q4_ERR_STATE, "%s: decoder has no resident layers", what);
+    if (dec->desc.max_batch < 1)
+        return fail(Q4_ERR_STATE, "%s: decoder created without max_batch", what);
+    if (dec->kv)
+        return fail(Q4_ERR_UNSUPPORTED, "%s: no batched attention over a KV cache", what);
+    if (B < 1 || B > dec->desc.max_batch)
+        return fail(Q4_ERR_INVALID_ARG, "%s: B=%d outside 1..%d", what, B, dec->desc.max_batch);
+    return Q4_OK;
+}
+
 // ------------------------------------------------------------ streaming
 enum SlotState { kEmpty = 0, kLoading = 1, kInUse = 2 };
 
@@ -320,6 +407,9 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
     if (!m->h || !q4::aligned(m->h, 16))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decoder_create: h null or not 16-byte aligned");
+    if (m->max_batch > 0 && (!m->h_batch || !q4::aligned(m->h_batch, 16)))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_decoder_create: h_batch null or not 16-byte aligned");
     if (!m->workspace || !q4::aligned(m->workspace, 256))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decoder_create: workspace null or not 256-byte aligned");
@@ -366,6 +456,7 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
             delete dec;
             return st;
         }
+        ws += q4::align256(q4::rope_table_bytes(m->max_ctx, (int32_t)d.hd));
         hipError_t e = hipMemset(dec->pos_dev, 0, 256);
         if (e == hipSuccess)
             e = hipDeviceSynchronize();
@@ -374,6 +465,19 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
             return q4::fail(Q4_ERR_HIP, "q4_decoder_create: position word: %s",
                             hipGetErrorString(e));
         }
+    }
+    if (m->max_batch > 0) {
+        const size_t mb = (size_t)m->max_batch;
+        dec->hb = m->h_batch;
+        dec->xb = reinterpret_cast<uint16_t *>(ws);
+        ws += q4::align256(mb * d.d * 2);
+        dec->qkvb = reinterpret_cast<float *>(ws);
+        ws += q4::align256(mb * d.nqkv * 4);
+        dec->oinb = reinterpret_cast<uint16_t *>(ws);
+        ws += q4::align256(mb * d.H * d.hd * 2);
+        dec->gub = reinterpret_cast<float *>(ws);
+        ws += q4::align256(mb * 2 * d.dff * 4);
+        dec->mlpb = reinterpret_cast<uint16_t *>(ws);
     }
     if (m->layers) {
         // Resident layers: the persistent kernel reads a device copy of the
@@ -508,11 +612,51 @@ extern "C" q4_status q4_decoder_set_context(void *decp, int32_t ctx_len, hipStre
     return Q4_OK;
 }
 
+extern "C" q4_status q4_decode_verify_eager(void *decp, int32_t B, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    Q4_CHECK(q4::check_verify(dec, B, "q4_decode_verify_eager"));
+    return q4::enqueue_verify(dec, B, stream);
+}
+
+extern "C" q4_status q4_decode_verify_graph(void *decp, int32_t B, hipStream_t stream) {
+    Decoder *dec = static_cast<Decoder *>(decp);
+    Q4_CHECK(q4::check_verify(dec, B, "q4_decode_verify_graph"));
+    if (!stream)
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_decode_verify_graph: capture needs a non-NULL stream");
+    if (!dec->vexec[B]) {
+        Q4_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+        q4_status st = q4::enqueue_verify(dec, B, stream);
+        hipGraph_t graph = nullptr;
+        hipError_t e = hipStreamEndCapture(stream, &graph);
+        if (st != Q4_OK) {
+            if (graph)
+                (void)hipGraphDestroy(graph);
+            return st;
+        }
+        if (e != hipSuccess)
+            return q4::fail(Q4_ERR_HIP, "q4_decode_verify_graph: end capture: %s",
+                            hipGetErrorString(e));
+        hipGraphExec_t exec = nullptr;
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (e != hipSuccess)
+            return q4::fail(Q4_ERR_HIP, "q4_decode_verify_graph: instantiate: %s",
+                            hipGetErrorString(e));
+        dec->vexec[B] = exec;
+    }
+    Q4_HIP(hipGraphLaunch(dec->vexec[B], stream));
+    return Q4_OK;
+}
+
 extern "C" q4_status q4_decoder_destroy(void *decp) {
     Decoder *dec = static_cast<Decoder *>(decp);
     if (!dec)
         return Q4_OK;
     for (auto &e : dec->exec)
+        if (e)
+            (void)hipGraphExecDestroy(e);
+    for (auto &e : dec->vexec)
         if (e)
             (void)hipGraphExecDestroy(e);
     delete dec;

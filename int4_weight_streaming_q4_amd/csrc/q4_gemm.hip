@@ -123,7 +123,9 @@ __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT],
     }
 }
 
-template <int RT, int NW>
+// ACC: Y += W X (each output is written by one lane: no race) instead of
+// Y = W X.
+template <int RT, int NW, bool ACC>
 __global__ void __launch_bounds__(64 * NW)
 gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
@@ -199,8 +201,12 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t row = row0 + t * 16 + 4 * kq + e;
-            if (row < N)
-                Y[(size_t)i16 * N + row] = acc[t][e];
+            if (row < N) {
+                if constexpr (ACC)
+                    Y[(size_t)i16 * N + row] += acc[t][e];
+                else
+                    Y[(size_t)i16 * N + row] = acc[t][e];
+            }
         }
     }
 }
@@ -208,10 +214,11 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
                         int, int);
 
+template <bool ACC>
 GemmFn pick_gemm(int RT, int NW) {
 #define Q4_PICK(rt, nw)                                                          \
     if (RT == rt && NW == nw)                                                    \
-        return gemm_mfma_kernel<rt, nw>;
+        return gemm_mfma_kernel<rt, nw, ACC>;
     Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
     Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
 #undef Q4_PICK
@@ -222,8 +229,8 @@ GemmFn pick_gemm(int RT, int NW) {
 
 q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
                                const uint16_t *X16, float *Y, int64_t N, int64_t K,
-                               int32_t B, int RT, int NW, hipStream_t stream) {
-    GemmFn fn = pick_gemm(RT, NW);
+                               int32_t B, int RT, int NW, hipStream_t stream, bool accumulate) {
+    GemmFn fn = accumulate ? pick_gemm<true>(RT, NW) : pick_gemm<false>(RT, NW);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no kernel for row_tiles=%d waves=%d", RT, NW);
     const int64_t blocks = (N + 16 * RT - 1) / (16 * RT);
@@ -234,14 +241,15 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
 }
 
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
-                           float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream) {
+                           float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
+                           bool accumulate) {
     const int64_t tiles = (N + 15) / 16;
     const int cus = device_cus();
     int RT = 4;
     while (RT > 1 && tiles / RT < 2 * cus)
         RT /= 2;
     int NW = (tiles / RT < 4LL * cus) ? 8 : 4;
-    return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream);
+    return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream, accumulate);
 }
 
 } // namespace q4
@@ -264,7 +272,7 @@ extern "C" q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *s
         return q4::launch_gemv(packed, scales, X_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,
                               stream);
     }
-    return q4::launch_gemm_mfma(packed, scales, X_f16, Y, N, K, B, stream);
+    return q4::launch_gemm_mfma(packed, scales, X_f16, Y, N, K, B, stream, false);
 }
 
 extern "C" q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
@@ -281,5 +289,5 @@ extern "C" q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_gemm_tuned: X must be 16-byte and Y 4-byte aligned");
     return q4::launch_gemm_mfma_cfg(packed, scales, X_f16, Y, N, K, B, row_tiles, waves,
-                                    stream);
+                                    stream, false);
 }

@@ -102,6 +102,6 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
 // Small-batch product with matrix cores (2 <= B <= 16).
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales,
                            const uint16_t *X16, float *Y, int64_t N, int64_t K,
-                           int32_t B, hipStream_t stream);
+                           int32_t B, hipStream_t stream, bool accumulate = false);
 
 } // namespace q4

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 20, names
     for n in names:
         assert hasattr(L, n), n
-    assert q4.abi_version() == 3
+    assert q4.abi_version() == 4
 
 
 def _err():
@@ -161,6 +161,38 @@ def test_decoder_kv_cache_description_checks():
     finally:
         assert L.q4_decoder_destroy(h) == 0
     assert L.q4_decoder_set_context(None, 1, None) == INVALID
+
+
+def test_decoder_verify_checks():
+    """Verify-step sections: per column d f16, nqkv f32, H hd f16, 2 dff f32,
+    dff f16, each rounded up to 256; argument and state errors before HIP."""
+    L = q4.lib()
+    plain, with_b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(plain)) == 0
+    assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc(max_batch=9, h_batch=8192)),
+                                        ctypes.byref(with_b)) == 0
+    a = lambda n: (n + 255) // 256 * 256
+    # DIMS: d 64, nqkv (4 + 4) * 16 = 128, H hd 64, dff 96
+    want = a(9 * 64 * 2) + a(9 * 128 * 4) + a(9 * 64 * 2) + a(9 * 192 * 4) + a(9 * 96 * 2)
+    assert with_b.value - plain.value == want
+    assert q4.workspace_bytes(DIMS, n_layers=2, max_batch=9) == with_b.value
+    out = ctypes.c_size_t()
+    for mb in (-1, 17):
+        assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc(max_batch=mb)),
+                                            ctypes.byref(out)) == INVALID
+    h = ctypes.c_void_p()
+    big = dict(workspace_bytes=1 << 22)
+    assert L.q4_decoder_create(ctypes.byref(_desc(max_batch=4, **big)), ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(max_batch=4, h_batch=8200, **big)),
+                               ctypes.byref(h)) == INVALID
+    assert L.q4_decoder_create(ctypes.byref(_desc(max_batch=4, h_batch=8192, **big)),
+                               ctypes.byref(h)) == 0
+    try:
+        assert L.q4_decode_verify_eager(h, 1, None) == STATE    # no resident layers
+        assert L.q4_decode_verify_graph(h, 1, None) == STATE
+    finally:
+        assert L.q4_decoder_destroy(h) == 0
+    assert L.q4_decode_verify_eager(None, 1, None) == INVALID
 
 
 def test_decoder_host_object_and_step_checks():
