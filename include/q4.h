@@ -212,7 +212,8 @@ typedef struct {
      * 256-byte aligned: binary16 [max_batch][d_model] (normed input),
      * fp32 [max_batch][(H + 2 Hkv) hd] (QKV), binary16 [max_batch][H hd]
      * (attention output), fp32 [max_batch][2 d_ff] (gate+up), binary16
-     * [max_batch][d_ff] (gated MLP activation). */
+     * [max_batch][d_ff] (gated MLP activation).  With a KV cache too, the
+     * attention partials are sized for max_batch columns. */
     int32_t max_batch;
     float *h_batch;
 } q4_model_desc;
@@ -323,13 +324,19 @@ q4_status q4_decode_layer_part(void *dec, const q4_layer *layer, int32_t which,
  * kernels; O and down add into h_batch), and the one-token glue between
  * them per column.  Column b ends exactly as if its token were decoded
  * alone (B = 1 runs the single-token kernels and equals
- * q4_decode_step_eager bitwise).  Eager enqueue on `stream`.  STATE
- * without resident layers or without max_batch; UNSUPPORTED with a KV
- * cache (causal attention across the batch is not built); INVALID_ARG for
- * B outside 1..max_batch. */
+ * q4_decode_step_eager bitwise).  With a KV cache the columns are draft
+ * tokens at consecutive positions: column b at position ctx - 1 + b, ctx
+ * the context length of the last q4_decoder_set_context; per layer all B
+ * key/value rows are stored first, then every column attends causally over
+ * rows 0..ctx - 1 + b (the earlier columns included).  Eager enqueue on
+ * `stream`.  STATE without resident layers or without max_batch;
+ * INVALID_ARG for B outside 1..max_batch or ctx + B - 1 above max_ctx;
+ * UNSUPPORTED for ctx + B - 1 above 4096. */
 q4_status q4_decode_verify_eager(void *dec, int32_t B, hipStream_t stream);
-/* The same, captured once per B as a HIP graph on `stream` (not NULL) and
- * replayed. */
+/* The same, captured once per B (and, with a KV cache, per context bucket
+ * of ctx + B - 1) as a HIP graph on `stream` (not NULL) and replayed; the
+ * position word is not part of the graph (q4_decoder_set_context writes
+ * it). */
 q4_status q4_decode_verify_graph(void *dec, int32_t B, hipStream_t stream);
 /* Frees graphs and host state.  Call after the last step has completed. */
 q4_status q4_decoder_destroy(void *dec);

@@ -14,6 +14,10 @@ struct AttnArgs {
     float *part;            // partials, attention_partial_bytes()
     int32_t nchunk;         // chunks launched (covers the context bucket)
     uint16_t *out;          // binary16 [H * hd] attention output
+    // token columns (1..16).  Above 1: qkv, partials and out hold one
+    // block per column, column b sits at position *pos_dev + b, and all
+    // key/value rows are stored before any column attends (causal batch).
+    int32_t batch = 1;
 };
 
 bool attention_supported(int32_t H, int32_t Hkv, int32_t hd);

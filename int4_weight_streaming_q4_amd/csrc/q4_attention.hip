@@ -128,7 +128,12 @@ __device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
 // QH query heads per key/value head, HD head dimension.  The workgroup's
 // cache tile (64 K rows and 64 V rows of its group) is loaded into
 // registers first, so its latency overlaps the rotation of the queries.
-template <int QH, int HD>
+// BATCH: a batch of token columns (blockIdx.z = column b, at position
+// *pos_dev + b, its QKV row, partials and output each offset by b); their
+// key and value rows were all stored beforehand (kv_append_batch), so
+// every row comes from the caches and each column sees the columns before
+// it.
+template <int QH, int HD, bool BATCH>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
              const float2 *__restrict__ rope, const int32_t *__restrict__ pos_dev,
@@ -151,9 +156,14 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x;
-    const int pos = *pos_dev;
+    const int col = BATCH ? (int)blockIdx.z : 0;
+    const int pos = *pos_dev + col;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
+    if (BATCH) {
+        qkv += (size_t)col * (H + 2 * Hkv) * HD;
+        part += (size_t)col * Hkv * nchunk * QH * prow;
+    }
     float *pout = part + (((size_t)g * nchunk + c) * QH) * prow;
     if (c0 > pos) {
         // empty partial: no positions of this chunk are in the context
@@ -164,7 +174,8 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         return;
     }
     const int n = min(kAP, pos + 1 - c0);
-    const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
+    // row of the new token (>= kAP: not in this chunk, or already stored)
+    const int jn = BATCH ? kAP : pos - c0;
     const size_t gbase = (size_t)g * max_ctx + c0;
 
     // cache tile loads; the row of the new token is replaced from LDS below
@@ -342,7 +353,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 // s + S, ... with a running maximum, U chunks per round, then the S waves
 // merge through LDS.
 constexpr int kCDims = 64;
-template <int QH, int HD>
+template <int QH, int HD, bool BATCH>
 __global__ void __launch_bounds__(kCThreads)
 attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev,
              int32_t nchunk, uint16_t *__restrict__ out) {
@@ -357,7 +368,12 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
     // chunk max and sum come from scalar loads
     const int s = __builtin_amdgcn_readfirstlane(t / kCDims);
     const int g = hq / QH, h = hq % QH;
-    const int pos = *pos_dev;
+    const int col = BATCH ? (int)blockIdx.z : 0;
+    const int pos = *pos_dev + col;
+    if (BATCH) {
+        part += (size_t)col * (gridDim.x / QH) * nchunk * QH * (HD + 2);
+        out += (size_t)col * gridDim.x * HD;
+    }
     const int nc = min(nchunk, pos / kAP + 1);
     const size_t prow = (size_t)(HD + 2);
     const size_t cstride = (size_t)QH * prow;
@@ -415,16 +431,43 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
     }
 }
 
+// Key and value rows of a batch of token columns: column b (blockIdx.y) at
+// position *pos_dev + b, key rotated, both rounded to binary16.
+template <int HD>
+__global__ void __launch_bounds__(HD / 2)
+kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
+                uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
+                const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv) {
+    constexpr int HALF = HD / 2;
+    const int g = blockIdx.x, col = blockIdx.y, d = threadIdx.x;
+    const int pos = *pos_dev + col;
+    const float *row = qkv + (size_t)col * (H + 2 * Hkv) * HD;
+    const float *k = row + (size_t)(H + g) * HD;
+    const float *v = row + (size_t)(H + Hkv + g) * HD;
+    const float2 cs = rope[(size_t)pos * HALF + d];
+    const float a = k[d], b = k[d + HALF];
+    uint16_t *krow = kc + ((size_t)g * max_ctx + pos) * HD;
+    uint16_t *vrow = vc + ((size_t)g * max_ctx + pos) * HD;
+    krow[d] = f2h(a * cs.x - b * cs.y);
+    krow[d + HALF] = f2h(a * cs.y + b * cs.x);
+    vrow[d] = f2h(v[d]);
+    vrow[d + HALF] = f2h(v[d + HALF]);
+}
+
+using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *, const int32_t *,
+                          int32_t, int32_t, int32_t);
+
 using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *,
                            const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
 using CombineFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
 template <int QH, int HD>
-bool pick(int qh, int hd, PartialFn &p, CombineFn &c) {
+bool pick(int qh, int hd, bool batch, PartialFn &p, CombineFn &c, AppendFn &a) {
     if (qh != QH || hd != HD)
         return false;
-    p = attn_partial<QH, HD>;
-    c = attn_combine<QH, HD>;
+    p = batch ? attn_partial<QH, HD, true> : attn_partial<QH, HD, false>;
+    c = batch ? attn_combine<QH, HD, true> : attn_combine<QH, HD, false>;
+    a = kv_append_batch<HD>;
     return true;
 }
 
@@ -466,21 +509,33 @@ q4_status launch_set_pos(int32_t *pos_dev, int32_t pos, hipStream_t s) {
 q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
     PartialFn pf = nullptr;
     CombineFn cf = nullptr;
+    AppendFn af = nullptr;
     const int qh = a.H / a.Hkv;
-    if (!(pick<1, 64>(qh, a.hd, pf, cf) || pick<2, 64>(qh, a.hd, pf, cf) ||
-          pick<4, 64>(qh, a.hd, pf, cf) || pick<8, 64>(qh, a.hd, pf, cf) ||
-          pick<1, 128>(qh, a.hd, pf, cf) || pick<2, 128>(qh, a.hd, pf, cf) ||
-          pick<4, 128>(qh, a.hd, pf, cf) || pick<8, 128>(qh, a.hd, pf, cf)))
+    const bool bt = a.batch > 1;
+    if (a.batch < 1 || a.batch > 16)
+        return fail(Q4_ERR_INVALID_ARG, "attention: batch %d", a.batch);
+    if (!(pick<1, 64>(qh, a.hd, bt, pf, cf, af) || pick<2, 64>(qh, a.hd, bt, pf, cf, af) ||
+          pick<4, 64>(qh, a.hd, bt, pf, cf, af) || pick<8, 64>(qh, a.hd, bt, pf, cf, af) ||
+          pick<1, 128>(qh, a.hd, bt, pf, cf, af) || pick<2, 128>(qh, a.hd, bt, pf, cf, af) ||
+          pick<4, 128>(qh, a.hd, bt, pf, cf, af) || pick<8, 128>(qh, a.hd, bt, pf, cf, af)))
         return fail(Q4_ERR_UNSUPPORTED, "attention: %d query heads per group, head dim %d", qh,
                     a.hd);
     if (a.nchunk < 1 || a.nchunk * kAP > a.max_ctx + kAP - 1)
         return fail(Q4_ERR_INVALID_ARG, "attention: %d chunks for max_ctx %d", a.nchunk,
                     a.max_ctx);
-    hipLaunchKernelGGL(pf, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), 0, s,
+    if (bt) {
+        hipLaunchKernelGGL(af, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0, s,
+                           a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
+                           a.max_ctx, a.H, a.Hkv);
+        Q4_HIP(hipGetLastError());
+    }
+    hipLaunchKernelGGL(pf, dim3((unsigned)a.Hkv, (unsigned)a.nchunk, (unsigned)a.batch),
+                       dim3(kAThreads), 0, s,
                        a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                        a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
     Q4_HIP(hipGetLastError());
-    hipLaunchKernelGGL(cf, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims)), dim3(kCThreads), 0, s,
+    hipLaunchKernelGGL(cf, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims), (unsigned)a.batch),
+                       dim3(kCThreads), 0, s,
                        a.part, a.pos_dev, a.nchunk, a.out);
     Q4_HIP(hipGetLastError());
     return Q4_OK;

@@ -64,7 +64,7 @@ struct Decoder {
     uint16_t *oinb = nullptr;    // f16[max_batch][H*hd]
     float *gub = nullptr;        // f32[max_batch][2 dff]
     uint16_t *mlpb = nullptr;    // f16[max_batch][dff]
-    hipGraphExec_t vexec[Q4_MAX_BATCH + 1] = {};
+    hipGraphExec_t vexec[4][Q4_MAX_BATCH + 1] = {}; // [context bucket][B]
 };
 
 q4_status dims_of(const q4_model_desc *m, Dims *out) {
@@ -123,7 +123,8 @@ size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) 
     if (m && m->kv_cache)
         b += 256 +
              align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv, (int32_t)d.hd,
-                                              m->max_ctx)) +
+                                              m->max_ctx) *
+                      (size_t)std::max(1, m->max_batch)) +
              align256(rope_table_bytes(m->max_ctx, (int32_t)d.hd));
     if (m)
         b += verify_bytes(d, m->max_batch);
@@ -175,12 +176,14 @@ struct Marks {
 // The four kernels of a layer, in order.
 enum Kern { kQkv = 0, kO = 1, kGateUp = 2, kDown = 3 };
 
-// Attention of layer `layer` over its cache slice, after the QKV product.
-q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s) {
+// Attention of layer `layer` over its cache slice, after the QKV product:
+// `batch` token columns of qkv (default: the single-token buffers).
+q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s, int32_t batch = 1,
+                            const float *qkv = nullptr, uint16_t *out = nullptr) {
     const Dims &d = dec->dims;
     const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
     AttnArgs a{};
-    a.qkv = dec->qkv;
+    a.qkv = qkv ? qkv : dec->qkv;
     a.kc = dec->kv + 2 * (size_t)layer * S;
     a.vc = a.kc + S;
     a.pos_dev = dec->pos_dev;
@@ -191,7 +194,8 @@ q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s) {
     a.rope = dec->rope;
     a.part = dec->att_part;
     a.nchunk = dec->att_chunks;
-    a.out = dec->oin;
+    a.out = out ? out : dec->oin;
+    a.batch = batch;
     return launch_attention(a, s);
 }
 
@@ -289,7 +293,8 @@ q4_status enqueue_all(Decoder *dec, hipStream_t s) {
 q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
     const Dims &d = dec->dims;
     const float eps = dec->desc.eps;
-    for (const q4_layer &L : dec->layers) {
+    for (int32_t l = 0; l < (int32_t)dec->layers.size(); ++l) {
+        const q4_layer &L = dec->layers[(size_t)l];
         if (B == 1) {
             EpiArgs ea{};
             ea.y = dec->qkvb;
@@ -300,6 +305,8 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
             ea.eps = eps;
             Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->hb, Pro::RmsNorm, L.qkv.N,
                                  L.qkv.K, Epi::QkvGather, ea, s));
+            if (dec->kv)
+                Q4_CHECK(enqueue_attention(dec, l, s, 1, dec->qkvb, dec->oinb));
             ea = EpiArgs{};
             ea.y = dec->hb;
             Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oinb, Pro::F16, L.o.N, L.o.K,
@@ -320,8 +327,11 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
         Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
         Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb, L.qkv.N,
                                   L.qkv.K, B, s));
-        Q4_CHECK(launch_gather_batch(dec->qkvb, dec->oinb, B, (int32_t)d.H, (int32_t)d.Hkv,
-                                     (int32_t)d.hd, s));
+        if (dec->kv)
+            Q4_CHECK(enqueue_attention(dec, l, s, B, dec->qkvb, dec->oinb));
+        else
+            Q4_CHECK(launch_gather_batch(dec->qkvb, dec->oinb, B, (int32_t)d.H, (int32_t)d.Hkv,
+                                         (int32_t)d.hd, s));
         Q4_CHECK(launch_gemm_mfma(L.o.packed, L.o.scales, dec->oinb, dec->hb, L.o.N, L.o.K, B, s,
                                   true));
         Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
@@ -341,10 +351,14 @@ q4_status check_verify(Decoder *dec, int32_t B, const char *what) {
         return fail(Q4_ERR_STATE, "%s: decoder has no resident layers", what);
     if (dec->desc.max_batch < 1)
         return fail(Q4_ERR_STATE, "%s: decoder created without max_batch", what);
-    if (dec->kv)
-        return fail(Q4_ERR_UNSUPPORTED, "%s: no batched attention over a KV cache", what);
     if (B < 1 || B > dec->desc.max_batch)
         return fail(Q4_ERR_INVALID_ARG, "%s: B=%d outside 1..%d", what, B, dec->desc.max_batch);
+    if (dec->kv && dec->ctx + B - 1 > dec->desc.max_ctx)
+        return fail(Q4_ERR_INVALID_ARG, "%s: positions %d..%d beyond max_ctx %d", what,
+                    dec->ctx - 1, dec->ctx + B - 2, dec->desc.max_ctx);
+    if (dec->kv && dec->ctx + B - 1 > kBuckets[3])
+        return fail(Q4_ERR_UNSUPPORTED, "%s: context %d above %d", what, dec->ctx + B - 1,
+                    kBuckets[3]);
     return Q4_OK;
 }
 
@@ -447,7 +461,8 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
         ws += 256;
         dec->att_part = reinterpret_cast<float *>(ws);
         ws += q4::align256(q4::attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv,
-                                                       (int32_t)d.hd, m->max_ctx));
+                                                       (int32_t)d.hd, m->max_ctx) *
+                           (size_t)std::max(1, m->max_batch));
         dec->rope = ws;
         // context length 1 until the caller sets another; the rotation table
         q4_status st = q4::launch_rope_table(dec->rope, m->max_ctx, (int32_t)d.hd,
@@ -615,6 +630,7 @@ extern "C" q4_status q4_decoder_set_context(void *decp, int32_t ctx_len, hipStre
 extern "C" q4_status q4_decode_verify_eager(void *decp, int32_t B, hipStream_t stream) {
     Decoder *dec = static_cast<Decoder *>(decp);
     Q4_CHECK(q4::check_verify(dec, B, "q4_decode_verify_eager"));
+    dec->att_chunks = q4::attention_chunks(dec->ctx + B - 1);
     return q4::enqueue_verify(dec, B, stream);
 }
 
@@ -624,7 +640,14 @@ extern "C" q4_status q4_decode_verify_graph(void *decp, int32_t B, hipStream_t s
     if (!stream)
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_decode_verify_graph: capture needs a non-NULL stream");
-    if (!dec->vexec[B]) {
+    int bk = 0;
+    if (dec->kv)
+        while (q4::kBuckets[bk] < dec->ctx + B - 1)
+            ++bk;
+    if (!dec->vexec[bk][B]) {
+        if (dec->kv)
+            dec->att_chunks =
+                q4::attention_chunks(std::min(q4::kBuckets[bk], dec->desc.max_ctx));
         Q4_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
         q4_status st = q4::enqueue_verify(dec, B, stream);
         hipGraph_t graph = nullptr;
@@ -643,9 +666,9 @@ extern "C" q4_status q4_decode_verify_graph(void *decp, int32_t B, hipStream_t s
         if (e != hipSuccess)
             return q4::fail(Q4_ERR_HIP, "q4_decode_verify_graph: instantiate: %s",
                             hipGetErrorString(e));
-        dec->vexec[B] = exec;
+        dec->vexec[bk][B] = exec;
     }
-    Q4_HIP(hipGraphLaunch(dec->vexec[B], stream));
+    Q4_HIP(hipGraphLaunch(dec->vexec[bk][B], stream));
     return Q4_OK;
 }
 
@@ -656,9 +679,10 @@ extern "C" q4_status q4_decoder_destroy(void *decp) {
     for (auto &e : dec->exec)
         if (e)
             (void)hipGraphExecDestroy(e);
-    for (auto &e : dec->vexec)
-        if (e)
-            (void)hipGraphExecDestroy(e);
+    for (auto &row : dec->vexec)
+        for (auto &e : row)
+            if (e)
+                (void)hipGraphExecDestroy(e);
     delete dec;
     return Q4_OK;
 }

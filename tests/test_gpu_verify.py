@@ -12,10 +12,12 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import int4_weight_streaming_q4_amd as q4
 from int4_weight_streaming_q4_amd import inputs
-from helpers import DEV
+from helpers import DEV, u16
 from test_gpu_decode import SMALL, TINY, EPS, check_h, make_layers, oracle_run, to_host
+from test_gpu_attention import BASE, f16_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -103,8 +105,12 @@ def test_verify_argument_errors():
                      dtype=torch.uint8, device=DEV)
     dec = q4.Decoder(SMALL, make_layers(SMALL, 63, 1), h, ws, EPS, kv_cache=kv, max_ctx=64,
                      max_batch=2, h_batch=hb)
-    with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
-        dec.verify_eager(2, s)
+    dec.set_context(64, s)
+    with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
+        dec.verify_eager(2, s)                 # positions 63, 64: past the 64-row cache
+    dec.set_context(63, s)
+    dec.verify_eager(2, s)                     # positions 62, 63
+    s.synchronize()
 
 
 def test_8b_verify_two_columns_match_oracle():
@@ -123,3 +129,152 @@ def test_8b_verify_two_columns_match_oracle():
         ref = oracle_run(host, dims, H0[b].numpy())
         rel = check_h(got[b].numpy(), ref[-1][0], ref[-1][1], f"8b verify column {b}")
         assert rel < 1e-2
+
+
+# ------------------------------------------------------- attention in the batch
+def verify_sections(dims, ws, n_layers, max_ctx, mb, B):
+    """qkv (f32 [B][nqkv]) and attention output (binary16 [B][H hd]) of the
+    verify step, read from the end of the workspace."""
+    a = lambda n: (n + 255) // 256 * 256
+    d, H, Hkv, hd, dff = (dims[k] for k in ("d", "H", "Hkv", "hd", "dff"))
+    nqkv = (H + 2 * Hkv) * hd
+    vb = a(mb * d * 2) + a(mb * nqkv * 4) + a(mb * H * hd * 2) + a(mb * 2 * dff * 4) + \
+        a(mb * dff * 2)
+    total = q4.workspace_bytes(dims, n_layers=n_layers, max_ctx=max_ctx, max_batch=mb)
+    o_qkv = total - vb + a(mb * d * 2)
+    o_oin = o_qkv + a(mb * nqkv * 4)
+    w = ws.cpu()
+    qkv = w[o_qkv:o_qkv + B * nqkv * 4].view(torch.float32).numpy().reshape(B, nqkv)
+    oin = w[o_oin:o_oin + B * H * hd * 2].view(torch.int16).numpy().view(np.uint16)
+    return qkv, oin.reshape(B, H * hd)
+
+
+def teacher_forced_verify(dims, layers, max_ctx, ctx, B, prefill, H0, what, mb=16):
+    """One single-layer decoder per layer over that layer's cache slice, the
+    residual columns carried from layer to layer; after each layer the
+    attention of every column is checked against the oracle attending, in
+    column order, from the GPU's QKV rows (each column sees the rows the
+    oracle stored for the columns before it)."""
+    Hkv, hd, H = dims["Hkv"], dims["hd"], dims["H"]
+    n = len(layers)
+    S = Hkv * max_ctx * hd
+    kv = torch.from_numpy(prefill.view(np.int16)).to(DEV)
+    h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
+    hb = torch.zeros(mb, dims["d"], dtype=torch.float32, device=DEV)
+    hb[:B].copy_(H0.to(DEV))
+    s = torch.cuda.Stream()
+    worst = 0.0
+    for l in range(n):
+        kv_l = kv[2 * l * S:2 * (l + 1) * S]
+        ws = torch.zeros(q4.workspace_bytes(dims, n_layers=1, max_ctx=max_ctx, max_batch=mb),
+                         dtype=torch.uint8, device=DEV)
+        dec = q4.Decoder(dims, [layers[l]], h, ws, EPS, kv_cache=kv_l, max_ctx=max_ctx,
+                         max_batch=mb, h_batch=hb)
+        dec.set_context(ctx, s)
+        dec.verify_eager(B, s)
+        s.synchronize()
+        qkv, oin = verify_sections(dims, ws, 1, max_ctx, mb, B)
+        cache = u16(kv_l).reshape(2, Hkv, max_ctx, hd)
+        pre = prefill.reshape(n, 2, Hkv, max_ctx, hd)[l]
+        kref, vref = np.ascontiguousarray(pre[0]), np.ascontiguousarray(pre[1])
+        half = hd // 2
+        for b in range(B):
+            pos = ctx - 1 + b
+            o_ref, mag = oracle.attention(qkv[b].astype(np.float64), dims, pos, kref, vref, BASE)
+            v32 = qkv[b, (H + Hkv) * hd:].reshape(Hkv, hd)
+            assert np.array_equal(cache[1, :, pos], v32.astype(np.float16).view(np.uint16)), \
+                f"{what} layer {l} column {b}: V row"
+            k32 = qkv[b, H * hd:(H + Hkv) * hd].reshape(Hkv, hd).astype(np.float64)
+            pair = np.abs(k32[:, :half]) + np.abs(k32[:, half:])
+            pair = np.concatenate([pair, pair], axis=1)
+            kw = oracle.f16_to_f64(kref[:, pos])
+            kg = oracle.f16_to_f64(cache[0, :, pos])
+            kb = f16_ulp(np.maximum(np.abs(kw), np.abs(kg))) + pair * 2.0 ** -21
+            assert np.all(np.abs(kg - kw) <= kb), f"{what} layer {l} column {b}: K row"
+            got = oracle.f16_to_f64(oin[b])
+            bound = 2e-3 * mag + f16_ulp(o_ref) + 1e-6
+            err = np.abs(got - o_ref)
+            assert np.all(err <= bound), (
+                f"{what} layer {l} column {b}: {int((err > bound).sum())} outside, worst "
+                f"{float((err / bound).max()):.3g}")
+            worst = max(worst, float((err / bound).max()))
+        rows = np.ones(max_ctx, bool)
+        rows[ctx - 1:ctx - 1 + B] = False
+        assert np.array_equal(cache[:, :, rows], pre[:, :, rows]), f"{what} layer {l}: other rows"
+        dec.close()
+    print(f"{what}: worst attention err/bound {worst:.3g}")
+    return hb[:B].cpu().clone(), u16(kv).copy()
+
+
+@pytest.mark.parametrize("ctx,B", [(1, 2), (60, 9), (120, 16), (192, 9)])
+def test_verify_attention_teacher_forced(ctx, B):
+    """Draft columns spanning chunk boundaries (positions 59..67, 119..134)
+    and the end of a 200-row cache (191..199)."""
+    dims = SMALL
+    n, max_ctx = 2, 200
+    layers = make_layers(dims, 70, n)
+    prefill = u16(inputs.act_f16((q4.kv_cache_elems(dims, n, max_ctx),), inputs.seed_of(70, 0, 8)))
+    H0 = columns(dims, 70, B)
+    teacher_forced_verify(dims, layers, max_ctx, ctx, B, prefill, H0, f"ctx {ctx} B {B}")
+
+
+def test_verify_attention_paths_agree():
+    """With a KV cache: B = 1 equals the single-token step bitwise, graph
+    replays equal eager (residual columns and caches), and the resident
+    multi-layer decoder equals the chain of single-layer decoders."""
+    dims = SMALL
+    n, max_ctx, mb, ctx = 3, 200, 16, 100
+    layers = make_layers(dims, 71, n)
+    prefill = u16(inputs.act_f16((q4.kv_cache_elems(dims, n, max_ctx),), inputs.seed_of(71, 0, 8)))
+    kv = torch.empty(q4.kv_cache_elems(dims, n, max_ctx), dtype=torch.int16, device=DEV)
+    reset = lambda: (kv.copy_(torch.from_numpy(prefill.view(np.int16)).to(DEV)),
+                     torch.cuda.synchronize())
+    h = torch.zeros(dims["d"], dtype=torch.float32, device=DEV)
+    hb = torch.zeros(mb, dims["d"], dtype=torch.float32, device=DEV)
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers=n, max_ctx=max_ctx, max_batch=mb),
+                     dtype=torch.uint8, device=DEV)
+    dec = q4.Decoder(dims, layers, h, ws, EPS, kv_cache=kv, max_ctx=max_ctx, max_batch=mb,
+                     h_batch=hb)
+    s = torch.cuda.Stream()
+    H0 = columns(dims, 71, 9)
+    # B = 1 against the single-token step
+    reset()
+    h.copy_(H0[0].to(DEV))
+    dec.set_context(ctx, s)
+    dec.step_eager(s)
+    s.synchronize()
+    h_step, c_step = h.cpu().clone(), u16(kv).copy()
+    reset()
+    hb[:1].copy_(H0[:1].to(DEV))
+    dec.set_context(ctx, s)
+    dec.verify_eager(1, s)
+    s.synchronize()
+    assert torch.equal(hb[0].cpu(), h_step) and np.array_equal(u16(kv), c_step)
+    # B = 9: eager, graph replays
+    reset()
+    hb[:9].copy_(H0.to(DEV))
+    dec.set_context(ctx, s)
+    dec.verify_eager(9, s)
+    s.synchronize()
+    h_e, c_e = hb[:9].cpu().clone(), u16(kv).copy()
+    for rep in range(3):
+        reset()
+        hb[:9].copy_(H0.to(DEV))
+        dec.set_context(ctx, s)
+        dec.verify_graph(9, s)
+        s.synchronize()
+        assert torch.equal(hb[:9].cpu(), h_e), rep
+        assert np.array_equal(u16(kv), c_e), rep
+    h_tf, c_tf = teacher_forced_verify(dims, layers, max_ctx, ctx, 9, prefill, H0, "chain")
+    assert torch.equal(h_tf, h_e) and np.array_equal(c_tf, c_e)
+
+
+def test_8b_verify_attention_teacher_forced():
+    """Llama-3-8B shapes, all 32 layers, 4096-row caches, nine draft
+    columns at positions 3990..3998, attention checked at every layer."""
+    dims = {k: v for k, v in inputs.MODEL_DIMS["8b"].items() if k != "n_layers"}
+    n, max_ctx = 32, 4096
+    layers = make_layers(dims, 2, n)
+    prefill = u16(inputs.act_f16((q4.kv_cache_elems(dims, n, max_ctx),), inputs.seed_of(2, 0, 8)))
+    H0 = columns(dims, 72, 9)
+    teacher_forced_verify(dims, layers, max_ctx, 3991, 9, prefill, H0, "8b", mb=9)
