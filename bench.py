@@ -39,6 +39,9 @@ def parse():
                     help="decode step implementation: 0 four kernels per layer, 1 persistent, "
                          "2 streaming persistent, 3 streaming workgroups per product "
                          "(default: the library's choice)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the configured step and its roofline (no quantize, verify or "
+                         "attention legs), e.g. for counter runs")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the extra measurement of the step with attention over "
                          "4096-row KV caches")
@@ -171,9 +174,10 @@ def main():
                      "bytes_per_launch": kbytes[2], "avg_launch_us": round(gu_us, 3)},
     }
 
-    result["quantize"] = quantize_rate(q4, torch)
-    result["verify_step"] = verify_rates(q4, inputs, torch, dims, layers, ms_per_step)
-    if not args.no_attention:
+    if not args.no_extras:
+        result["quantize"] = quantize_rate(q4, torch)
+        result["verify_step"] = verify_rates(q4, inputs, torch, dims, layers, ms_per_step)
+    if not (args.no_attention or args.no_extras):
         dec.close()
         del ws
         result["with_attention"] = attention_step(args, q4, inputs, torch, dims, layers, h0)
@@ -281,7 +285,28 @@ def attention_step(args, q4, inputs, torch, dims, layers, h0, max_ctx=4096):
     # K and V rows read per layer at the final context, binary16
     kv_bytes = 2 * dims["Hkv"] * max_ctx * dims["hd"] * 2
     dec.close()
+    del ws
+    # verify step of nine draft tokens at positions 4086..4094, same caches
+    mb = 9
+    hb = h0[:mb].clone()
+    ws = torch.zeros(q4.workspace_bytes(dims, n_layers, max_ctx=max_ctx, max_batch=mb),
+                     dtype=torch.uint8, device="cuda")
+    dec = q4.Decoder(dims, layers, h, ws, kv_cache=kv, max_ctx=max_ctx, max_batch=mb,
+                     h_batch=hb)
+    with torch.cuda.stream(stream):
+        dec.set_context(max_ctx - mb, stream)
+        dec.verify_graph(mb, stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dec.verify_graph(mb, stream)
+        e1.record(stream)
+    stream.synchronize()
+    vms = e0.elapsed_time(e1) / 10
+    dec.close()
     return {"context": [first, max_ctx], "tokens_per_s": round(1000.0 / ms, 2),
+            "verify_B9_ms": round(vms, 4), "verify_B9_tokens_checked_per_s": round(9000.0 / vms, 1),
             "ms_per_step": round(ms, 5),
             "attention_us_per_layer_at_4096": round(attn_ms * 1000.0, 3),
             "attention_share_of_layer": round(attn_ms / step_ms, 4),
