@@ -30,9 +30,12 @@
 #include <cmath>
 
 #include "q4_attention.h"
+#include "q4_lanes.h"
 
 namespace q4 {
 namespace {
+
+using namespace lanes;
 
 constexpr int kAP = 64;        // positions per chunk
 constexpr int kAThreads = 256;
@@ -60,62 +63,6 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
     rope[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// Cross-lane steps as VALU operations (DPP and gfx950's lane swaps) rather
-// than LDS permutes: they sit on the critical path of every reduction.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kQuadXor1 = 0xB1; // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E; // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-
-// Values of the lanes 16 and 32 away, pairwise combined: every lane gets
-// op(x[row r], x[row r ^ 1]) (16-lane rows) resp. op(x[lane], x[lane ^ 32]).
-struct Rows16 {
-    unsigned a, b;
-    __device__ __forceinline__ Rows16(float x) {
-        auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-        a = r[0];
-        b = r[1];
-    }
-};
-struct Halves32 {
-    unsigned a, b;
-    __device__ __forceinline__ Halves32(float x) {
-        auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-        a = r[0];
-        b = r[1];
-    }
-};
-__device__ __forceinline__ float fa(unsigned u) { return __builtin_bit_cast(float, u); }
-
-// Sum / max over all 64 lanes, result in every lane.
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp<kQuadXor1>(x);
-    x += dpp<kQuadXor2>(x);
-    x += dpp<kRowRor4>(x);
-    x += dpp<kRowRor8>(x);
-    const Rows16 r(x);
-    x = fa(r.a) + fa(r.b);
-    const Halves32 h(x);
-    return fa(h.a) + fa(h.b);
-}
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kQuadXor1>(x));
-    x = fmaxf(x, dpp<kQuadXor2>(x));
-    x = fmaxf(x, dpp<kRowRor4>(x));
-    x = fmaxf(x, dpp<kRowRor8>(x));
-    const Rows16 r(x);
-    x = fmaxf(fa(r.a), fa(r.b));
-    const Halves32 h(x);
-    return fmaxf(fa(h.a), fa(h.b));
-}
-
 __device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -128,11 +75,11 @@ __device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
 // QH query heads per key/value head, HD head dimension.  The workgroup's
 // cache tile (64 K rows and 64 V rows of its group) is loaded into
 // registers first, so its latency overlaps the rotation of the queries.
-// BATCH: a batch of token columns (blockIdx.z = column b, at position
-// *pos_dev + b, its QKV row, partials and output each offset by b); their
-// key and value rows were all stored beforehand (kv_append_batch), so
-// every row comes from the caches and each column sees the columns before
-// it.
+// BATCH: a batch of `batch` token columns (column b at position *pos_dev +
+// b, its QKV row, partials and output each offset by b); their key and
+// value rows were all stored beforehand (kv_append_batch), so every row
+// comes from the caches and each column sees the columns before it
+// (blockIdx.z = column).
 template <int QH, int HD, bool BATCH>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
@@ -155,8 +102,8 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     __shared__ float vred[NW][QH][HD];
 
     const int g = blockIdx.x, c = blockIdx.y;
-    const int t = threadIdx.x;
     const int col = BATCH ? (int)blockIdx.z : 0;
+    const int t = threadIdx.x;
     const int pos = *pos_dev + col;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
@@ -530,9 +477,9 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
         Q4_HIP(hipGetLastError());
     }
     hipLaunchKernelGGL(pf, dim3((unsigned)a.Hkv, (unsigned)a.nchunk, (unsigned)a.batch),
-                       dim3(kAThreads), 0, s,
-                       a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
-                       a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
+                       dim3(kAThreads), 0, s, a.qkv, a.kc, a.vc,
+                       static_cast<const float2 *>(a.rope), a.pos_dev, a.max_ctx, a.H, a.Hkv,
+                       a.part, a.nchunk);
     Q4_HIP(hipGetLastError());
     hipLaunchKernelGGL(cf, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims), (unsigned)a.batch),
                        dim3(kCThreads), 0, s,

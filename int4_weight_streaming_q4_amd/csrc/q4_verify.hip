@@ -14,6 +14,7 @@
 #include <cmath>
 
 #include "q4_verify.h"
+#include "q4_lanes.h"
 
 namespace q4 {
 namespace {
@@ -24,29 +25,54 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// One workgroup per column.
-__global__ void __launch_bounds__(kVThreads)
+// One workgroup per column; the column stays in registers between the sum
+// of squares and the scaling (d <= 8192; a larger d rereads the rest).
+constexpr int kNThreads = 512;
+constexpr int kNKeep = 4; // float4 per thread held in registers
+
+__global__ void __launch_bounds__(kNThreads)
 rmsnorm_batch_kernel(const float *__restrict__ H, uint16_t *__restrict__ X, int32_t d,
                      float eps) {
-    __shared__ float part[kVThreads / 64];
-    const float *h = H + (size_t)blockIdx.x * d;
-    uint16_t *x = X + (size_t)blockIdx.x * d;
+    __shared__ float part[kNThreads / 64];
+    const float4 *h = reinterpret_cast<const float4 *>(H + (size_t)blockIdx.x * d);
+    uint2 *x = reinterpret_cast<uint2 *>(X + (size_t)blockIdx.x * d);
+    const int n4 = d / 4;
+    float4 keep[kNKeep];
     float ss = 0.0f;
-    for (int i = threadIdx.x; i < d; i += kVThreads)
-        ss = fmaf(h[i], h[i], ss);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        ss += __shfl_xor(ss, o);
+    for (int i = 0; i < kNKeep; ++i) {
+        const int j = threadIdx.x + i * kNThreads;
+        keep[i] = j < n4 ? h[j] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        ss = fmaf(keep[i].x, keep[i].x, ss);
+        ss = fmaf(keep[i].y, keep[i].y, ss);
+        ss = fmaf(keep[i].z, keep[i].z, ss);
+        ss = fmaf(keep[i].w, keep[i].w, ss);
+    }
+    for (int j = threadIdx.x + kNKeep * kNThreads; j < n4; j += kNThreads) {
+        const float4 v = h[j];
+        ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
+    ss = lanes::wave_sum(ss);
     if ((threadIdx.x & 63) == 0)
         part[threadIdx.x >> 6] = ss;
     __syncthreads();
     float tot = part[0];
 #pragma unroll
-    for (int w = 1; w < kVThreads / 64; ++w)
+    for (int w = 1; w < kNThreads / 64; ++w)
         tot += part[w];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += kVThreads)
-        x[i] = f2h(h[i] * r);
+    auto emit = [&](int j, const float4 &v) {
+        x[j] = make_uint2((uint32_t)f2h(v.x * r) | ((uint32_t)f2h(v.y * r) << 16),
+                          (uint32_t)f2h(v.z * r) | ((uint32_t)f2h(v.w * r) << 16));
+    };
+#pragma unroll
+    for (int i = 0; i < kNKeep; ++i) {
+        const int j = threadIdx.x + i * kNThreads;
+        if (j < n4)
+            emit(j, keep[i]);
+    }
+    for (int j = threadIdx.x + kNKeep * kNThreads; j < n4; j += kNThreads)
+        emit(j, h[j]);
 }
 
 __global__ void __launch_bounds__(kVThreads)
@@ -77,7 +103,7 @@ silu_batch_kernel(const float *__restrict__ gu, uint16_t *__restrict__ m, int32_
 
 q4_status launch_rmsnorm_batch(const float *H, uint16_t *X, int32_t B, int32_t d, float eps,
                                hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_batch_kernel, dim3((unsigned)B), dim3(kVThreads), 0, s, H, X, d,
+    hipLaunchKernelGGL(rmsnorm_batch_kernel, dim3((unsigned)B), dim3(kNThreads), 0, s, H, X, d,
                        eps);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
