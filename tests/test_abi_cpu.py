@@ -295,3 +295,23 @@ def test_offload_plan():
     assert L.q4_offload_plan(4, 100, 150, arr, ctypes.byref(k)) == UNSUPPORTED
     assert L.q4_offload_plan(0, 100, 150, arr, ctypes.byref(k)) == INVALID
     assert L.q4_offload_plan(4, 0, 150, arr, ctypes.byref(k)) == INVALID
+
+
+def test_plain_c_consumer(tmp_path):
+    """The C ABI used from a plain C program (gcc, include/q4.h, linked to
+    libq4stream.so): no Python or torch types cross the boundary."""
+    import shutil
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(root, "tests", "c", "abi_host_check.c")
+    libdir = os.path.dirname(q4.LIB_PATH)
+    exe = str(tmp_path / "abi_host_check")
+    subprocess.run([gcc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                    "-I", "/opt/rocm/include", src, "-o", exe, "-L", libdir, "-lq4stream",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "passed" in r.stdout
