@@ -75,12 +75,7 @@ __device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
 // QH query heads per key/value head, HD head dimension.  The workgroup's
 // cache tile (64 K rows and 64 V rows of its group) is loaded into
 // registers first, so its latency overlaps the rotation of the queries.
-// BATCH: a batch of `batch` token columns (column b at position *pos_dev +
-// b, its QKV row, partials and output each offset by b); their key and
-// value rows were all stored beforehand (kv_append_batch), so every row
-// comes from the caches and each column sees the columns before it
-// (blockIdx.z = column).
-template <int QH, int HD, bool BATCH>
+template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
              const float2 *__restrict__ rope, const int32_t *__restrict__ pos_dev,
@@ -102,15 +97,10 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     __shared__ float vred[NW][QH][HD];
 
     const int g = blockIdx.x, c = blockIdx.y;
-    const int col = BATCH ? (int)blockIdx.z : 0;
     const int t = threadIdx.x;
-    const int pos = *pos_dev + col;
+    const int pos = *pos_dev;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
-    if (BATCH) {
-        qkv += (size_t)col * (H + 2 * Hkv) * HD;
-        part += (size_t)col * Hkv * nchunk * QH * prow;
-    }
     float *pout = part + (((size_t)g * nchunk + c) * QH) * prow;
     if (c0 > pos) {
         // empty partial: no positions of this chunk are in the context
@@ -121,8 +111,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         return;
     }
     const int n = min(kAP, pos + 1 - c0);
-    // row of the new token (>= kAP: not in this chunk, or already stored)
-    const int jn = BATCH ? kAP : pos - c0;
+    const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
     const size_t gbase = (size_t)g * max_ctx + c0;
 
     // cache tile loads; the row of the new token is replaced from LDS below
@@ -401,6 +390,170 @@ kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
     vrow[d + HALF] = f2h(v[d + HALF]);
 }
 
+// Attention of a batch of draft columns, one workgroup per (key/value
+// head, chunk of 64 positions): the chunk's K and V rows are staged in LDS
+// once (rows padded by 16 bytes, so a row per lane reads without bank
+// conflicts) and shared by every column; wave w takes columns w, w + 4,
+// ...  and runs each one's chain alone: lane j scores position j against
+// the rotated queries (read as broadcasts from LDS), a softmax across the
+// wave's 64 lanes, and the weighted value sum with lanes over the head
+// dimension.  Column b sits at position *pos_dev + b; its key/value rows
+// were stored beforehand (kv_append_batch).  Partials as attn_partial's,
+// one block per column.
+template <int QH, int HD>
+__global__ void __launch_bounds__(kAThreads)
+attn_batch_tile(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
+                const uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
+                const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
+                float *__restrict__ part, int32_t nchunk, int32_t batch) {
+    constexpr int HALF = HD / 2;
+    constexpr int HP = HD + 8;                 // padded row, halves
+    constexpr int NW = kAThreads / 64;
+    constexpr int DPL = HD / 64;               // dims per lane in the value sum
+    static_assert(HD == 64 || HD == 128, "head dimension");
+    __shared__ __align__(16) uint16_t kt[kAP * HP];
+    __shared__ __align__(16) uint16_t vt[kAP * HP];
+    __shared__ __align__(16) float qr[NW][QH][HD];
+    __shared__ __align__(16) float pw[NW][QH][kAP];
+
+    const int g = blockIdx.x, c = blockIdx.y;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int pos0 = *pos_dev;
+    const int c0 = c * kAP;
+    const int rows = max(0, min(kAP, pos0 + batch - c0)); // rows any column reads
+    const size_t prow = (size_t)(HD + 2);
+    const size_t nqkv = (size_t)(H + 2 * Hkv) * HD;
+    const size_t colstride = (size_t)Hkv * nchunk * QH * prow;
+
+    // stage the tile (rows past the last column's position as zeros)
+    {
+        constexpr int CPR = HD / 8;            // 16-byte pieces per row
+        const size_t gbase = ((size_t)g * max_ctx + c0) * HD;
+        for (int i = t; i < kAP * CPR; i += kAThreads) {
+            const int r = i / CPR, cb = i % CPR;
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            if (r < rows) {
+                kv = *reinterpret_cast<const uint4 *>(kc + gbase + (size_t)r * HD + cb * 8);
+                vv = *reinterpret_cast<const uint4 *>(vc + gbase + (size_t)r * HD + cb * 8);
+            }
+            *reinterpret_cast<uint4 *>(kt + r * HP + cb * 8) = kv;
+            *reinterpret_cast<uint4 *>(vt + r * HP + cb * 8) = vv;
+        }
+    }
+    __syncthreads();
+
+    const float scale = 1.0f / sqrtf((float)HD);
+    for (int b = w; b < batch; b += NW) {
+        float *pout = part + (size_t)b * colstride + (((size_t)g * nchunk + c) * QH) * prow;
+        const int pos = pos0 + b;
+        const int n = max(0, min(kAP, pos + 1 - c0)); // positions of this chunk it sees
+        if (n == 0) {
+            for (int i = lane; i < QH * (HD + 2); i += 64) {
+                const int h = i / (HD + 2), e = i % (HD + 2);
+                pout[h * prow + e] = e == HD ? -INFINITY : 0.0f;
+            }
+            continue;
+        }
+        // rotated queries of this column
+        if (lane < HALF) {
+            const float2 cs = rope[(size_t)pos * HALF + lane];
+#pragma unroll
+            for (int h = 0; h < QH; ++h) {
+                const float *q = qkv + (size_t)b * nqkv + (size_t)(g * QH + h) * HD;
+                const float a = q[lane], bb = q[lane + HALF];
+                qr[w][h][lane] = a * cs.x - bb * cs.y;
+                qr[w][h][lane + HALF] = a * cs.y + bb * cs.x;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // scores: lane = position
+        float acc[QH];
+#pragma unroll
+        for (int h = 0; h < QH; ++h)
+            acc[h] = 0.0f;
+#pragma unroll 4
+        for (int d0 = 0; d0 < HD; d0 += 8) {
+            float kf[8];
+            unpack8(*reinterpret_cast<const uint4 *>(kt + lane * HP + d0), kf);
+#pragma unroll
+            for (int h = 0; h < QH; ++h) {
+                const float4 qa = *reinterpret_cast<const float4 *>(&qr[w][h][d0]);
+                const float4 qb = *reinterpret_cast<const float4 *>(&qr[w][h][d0 + 4]);
+                float a = acc[h];
+                a = fmaf(qa.x, kf[0], a);
+                a = fmaf(qa.y, kf[1], a);
+                a = fmaf(qa.z, kf[2], a);
+                a = fmaf(qa.w, kf[3], a);
+                a = fmaf(qb.x, kf[4], a);
+                a = fmaf(qb.y, kf[5], a);
+                a = fmaf(qb.z, kf[6], a);
+                a = fmaf(qb.w, kf[7], a);
+                acc[h] = a;
+            }
+        }
+        float mh[QH], lh[QH];
+#pragma unroll
+        for (int h = 0; h < QH; ++h) {
+            const float sv = lane < n ? acc[h] * scale : -INFINITY;
+            const float m = wave_max(sv);
+            const float e = lane < n ? expf(sv - m) : 0.0f;
+            mh[h] = m;
+            lh[h] = wave_sum(e);
+            pw[w][h][lane] = e;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // value sum: lane = DPL dims of the head dimension
+        float o[QH][DPL];
+#pragma unroll
+        for (int h = 0; h < QH; ++h)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                o[h][e] = 0.0f;
+        for (int j0 = 0; j0 < n; j0 += 4) {
+            float4 p4[QH];
+#pragma unroll
+            for (int h = 0; h < QH; ++h)
+                p4[h] = *reinterpret_cast<const float4 *>(&pw[w][h][j0]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t *vr = vt + (j0 + i) * HP + lane * DPL;
+                float vf[DPL];
+                if constexpr (DPL == 2) {
+                    const uint32_t v2 = *reinterpret_cast<const uint32_t *>(vr);
+                    vf[0] = h2f((uint16_t)(v2 & 0xFFFFu));
+                    vf[1] = h2f((uint16_t)(v2 >> 16));
+                } else {
+                    vf[0] = h2f(vr[0]);
+                }
+#pragma unroll
+                for (int h = 0; h < QH; ++h) {
+                    const float p = i == 0 ? p4[h].x : i == 1 ? p4[h].y : i == 2 ? p4[h].z : p4[h].w;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e)
+                        o[h][e] = fmaf(p, vf[e], o[h][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < QH; ++h) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                pout[h * prow + lane * DPL + e] = o[h][e];
+            if (lane == 0) {
+                pout[h * prow + HD] = mh[h];
+                pout[h * prow + HD + 1] = lh[h];
+            }
+        }
+        // the next column of this wave rewrites qr and pw
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *, const int32_t *,
                           int32_t, int32_t, int32_t);
 
@@ -408,13 +561,24 @@ using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *
                            const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
 using CombineFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
+using BatchFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
+                         const int32_t *, int32_t, int32_t, int32_t, float *, int32_t, int32_t);
+
+struct AttnFns {
+    PartialFn partial = nullptr;
+    BatchFn batch = nullptr;
+    CombineFn combine = nullptr;
+    AppendFn append = nullptr;
+};
+
 template <int QH, int HD>
-bool pick(int qh, int hd, bool batch, PartialFn &p, CombineFn &c, AppendFn &a) {
+bool pick(int qh, int hd, bool batch, AttnFns &f) {
     if (qh != QH || hd != HD)
         return false;
-    p = batch ? attn_partial<QH, HD, true> : attn_partial<QH, HD, false>;
-    c = batch ? attn_combine<QH, HD, true> : attn_combine<QH, HD, false>;
-    a = kv_append_batch<HD>;
+    f.partial = attn_partial<QH, HD>;
+    f.batch = attn_batch_tile<QH, HD>;
+    f.combine = batch ? attn_combine<QH, HD, true> : attn_combine<QH, HD, false>;
+    f.append = kv_append_batch<HD>;
     return true;
 }
 
@@ -454,34 +618,35 @@ q4_status launch_set_pos(int32_t *pos_dev, int32_t pos, hipStream_t s) {
 }
 
 q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
-    PartialFn pf = nullptr;
-    CombineFn cf = nullptr;
-    AppendFn af = nullptr;
+    AttnFns f;
     const int qh = a.H / a.Hkv;
     const bool bt = a.batch > 1;
     if (a.batch < 1 || a.batch > 16)
         return fail(Q4_ERR_INVALID_ARG, "attention: batch %d", a.batch);
-    if (!(pick<1, 64>(qh, a.hd, bt, pf, cf, af) || pick<2, 64>(qh, a.hd, bt, pf, cf, af) ||
-          pick<4, 64>(qh, a.hd, bt, pf, cf, af) || pick<8, 64>(qh, a.hd, bt, pf, cf, af) ||
-          pick<1, 128>(qh, a.hd, bt, pf, cf, af) || pick<2, 128>(qh, a.hd, bt, pf, cf, af) ||
-          pick<4, 128>(qh, a.hd, bt, pf, cf, af) || pick<8, 128>(qh, a.hd, bt, pf, cf, af)))
+    if (!(pick<1, 64>(qh, a.hd, bt, f) || pick<2, 64>(qh, a.hd, bt, f) ||
+          pick<4, 64>(qh, a.hd, bt, f) || pick<8, 64>(qh, a.hd, bt, f) ||
+          pick<1, 128>(qh, a.hd, bt, f) || pick<2, 128>(qh, a.hd, bt, f) ||
+          pick<4, 128>(qh, a.hd, bt, f) || pick<8, 128>(qh, a.hd, bt, f)))
         return fail(Q4_ERR_UNSUPPORTED, "attention: %d query heads per group, head dim %d", qh,
                     a.hd);
     if (a.nchunk < 1 || a.nchunk * kAP > a.max_ctx + kAP - 1)
         return fail(Q4_ERR_INVALID_ARG, "attention: %d chunks for max_ctx %d", a.nchunk,
                     a.max_ctx);
     if (bt) {
-        hipLaunchKernelGGL(af, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0, s,
-                           a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
+        hipLaunchKernelGGL(f.append, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0,
+                           s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                            a.max_ctx, a.H, a.Hkv);
         Q4_HIP(hipGetLastError());
+        hipLaunchKernelGGL(f.batch, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), 0,
+                           s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
+                           a.max_ctx, a.H, a.Hkv, a.part, a.nchunk, a.batch);
+    } else {
+        hipLaunchKernelGGL(f.partial, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads),
+                           0, s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope),
+                           a.pos_dev, a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
     }
-    hipLaunchKernelGGL(pf, dim3((unsigned)a.Hkv, (unsigned)a.nchunk, (unsigned)a.batch),
-                       dim3(kAThreads), 0, s, a.qkv, a.kc, a.vc,
-                       static_cast<const float2 *>(a.rope), a.pos_dev, a.max_ctx, a.H, a.Hkv,
-                       a.part, a.nchunk);
     Q4_HIP(hipGetLastError());
-    hipLaunchKernelGGL(cf, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims), (unsigned)a.batch),
+    hipLaunchKernelGGL(f.combine, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims), (unsigned)a.batch),
                        dim3(kCThreads), 0, s,
                        a.part, a.pos_dev, a.nchunk, a.out);
     Q4_HIP(hipGetLastError());
