@@ -27,6 +27,7 @@
 // The position comes from a device word, so one captured graph serves every
 // context length of its bucket: chunks past the position write an empty
 // partial.
+#include <algorithm>
 #include <cmath>
 
 #include "q4_attention.h"
@@ -390,168 +391,188 @@ kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
     vrow[d + HALF] = f2h(v[d + HALF]);
 }
 
-// Attention of a batch of draft columns, one workgroup per (key/value
-// head, chunk of 64 positions): the chunk's K and V rows are staged in LDS
-// once (rows padded by 16 bytes, so a row per lane reads without bank
-// conflicts) and shared by every column; wave w takes columns w, w + 4,
-// ...  and runs each one's chain alone: lane j scores position j against
-// the rotated queries (read as broadcasts from LDS), a softmax across the
-// wave's 64 lanes, and the weighted value sum with lanes over the head
-// dimension.  Column b sits at position *pos_dev + b; its key/value rows
-// were stored beforehand (kv_append_batch).  Partials as attn_partial's,
-// one block per column.
+// Matrix-core attention tile: one workgroup per (key/value head, chunk of
+// 64 positions) for all `batch` columns (column b at position *pos_dev + b;
+// rows r = b * QH + h of the query matrix).  Scores S = Q K^T and outputs
+// O = P V are v_mfma_f32_16x16x32_f16 products with fp32 accumulation; the
+// fp32 queries and weights enter as two binary16 halves (x = hi + lo, hi =
+// f16(x), lo = f16(x - hi)), so each product is two passes and agrees with
+// an fp32 evaluation to about 2^-22 relative; keys and values are binary16
+// already.  LDS: the K rows (row-major) and the V rows transposed (so both
+// operands are 16-byte reads), the query halves, the scores/weights.  Every
+// row comes from the caches: kv_append_batch stored the columns' rows
+// first.  Used for draft batches; a single token takes attn_partial, whose
+// loads overlap its arithmetic (this tile's fixed staging costs more there).
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
-attn_batch_tile(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
-                const uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
-                const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
-                float *__restrict__ part, int32_t nchunk, int32_t batch) {
+attn_tile_mfma(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
+               const uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
+               const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
+               float *__restrict__ part, int32_t nchunk, int32_t batch) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
     constexpr int HALF = HD / 2;
-    constexpr int HP = HD + 8;                 // padded row, halves
+    constexpr int HP = HD + 8;     // K tile / query row stride, halves
+    constexpr int VP = kAP + 8;    // transposed V row stride, halves
+    constexpr int SP = kAP + 4;    // score row stride, floats
+    constexpr int KT = HD / 32;    // k tiles of the scores
+    constexpr int DT = HD / 16;    // output column tiles
     constexpr int NW = kAThreads / 64;
-    constexpr int DPL = HD / 64;               // dims per lane in the value sum
     static_assert(HD == 64 || HD == 128, "head dimension");
-    __shared__ __align__(16) uint16_t kt[kAP * HP];
-    __shared__ __align__(16) uint16_t vt[kAP * HP];
-    __shared__ __align__(16) float qr[NW][QH][HD];
-    __shared__ __align__(16) float pw[NW][QH][kAP];
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int rows = batch * QH;
+    const int RT = (rows + 15) / 16;
+    const int RP = RT * 16;        // padded rows
+    uint16_t *kt = reinterpret_cast<uint16_t *>(smem);                 // [64][HP]
+    uint16_t *vt = kt + kAP * HP;                                      // [HD][VP]
+    uint16_t *qh = vt + HD * VP;                                       // [RP][HP]
+    uint16_t *ql = qh + RP * HP;                                       // [RP][HP]
+    float *ps = reinterpret_cast<float *>(ql + RP * HP);               // [RP][SP]
+    float *mrow = ps + RP * SP;                                        // [RP]
+    float *lrow = mrow + RP;                                           // [RP]
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int pos0 = *pos_dev;
+    const int pmax = pos0 + batch - 1;
     const int c0 = c * kAP;
-    const int rows = max(0, min(kAP, pos0 + batch - c0)); // rows any column reads
     const size_t prow = (size_t)(HD + 2);
     const size_t nqkv = (size_t)(H + 2 * Hkv) * HD;
     const size_t colstride = (size_t)Hkv * nchunk * QH * prow;
+    if (c0 > pmax) {
+        for (int i = t; i < rows * (HD + 2); i += kAThreads) {
+            const int r = i / (HD + 2), e = i % (HD + 2);
+            const int b = r / QH, h = r % QH;
+            part[b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow + e] =
+                e == HD ? -INFINITY : 0.0f;
+        }
+        return;
+    }
+    const int nrow = min(kAP, pmax + 1 - c0);   // rows any column reads
+    const size_t gbase = ((size_t)g * max_ctx + c0) * HD;
 
-    // stage the tile (rows past the last column's position as zeros)
+    // stage K (row-major) and V (transposed) of the chunk
     {
-        constexpr int CPR = HD / 8;            // 16-byte pieces per row
-        const size_t gbase = ((size_t)g * max_ctx + c0) * HD;
+        constexpr int CPR = HD / 8;
         for (int i = t; i < kAP * CPR; i += kAThreads) {
             const int r = i / CPR, cb = i % CPR;
             uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (r < rows) {
+            if (r < nrow) {
                 kv = *reinterpret_cast<const uint4 *>(kc + gbase + (size_t)r * HD + cb * 8);
                 vv = *reinterpret_cast<const uint4 *>(vc + gbase + (size_t)r * HD + cb * 8);
             }
             *reinterpret_cast<uint4 *>(kt + r * HP + cb * 8) = kv;
-            *reinterpret_cast<uint4 *>(vt + r * HP + cb * 8) = vv;
+            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vt[(cb * 8 + 2 * e) * VP + r] = (uint16_t)(vw[e] & 0xFFFFu);
+                vt[(cb * 8 + 2 * e + 1) * VP + r] = (uint16_t)(vw[e] >> 16);
+            }
+        }
+    }
+    // rotated queries as binary16 halves; padding rows are zero
+    for (int i = t; i < RP * HALF; i += kAThreads) {
+        const int r = i / HALF, d = i % HALF;
+        float a0 = 0.0f, a1 = 0.0f;
+        if (r < rows) {
+            const int b = r / QH, h = r % QH;
+            const float *q = qkv + (size_t)b * nqkv + (size_t)(g * QH + h) * HD;
+            const float2 cs = rope[(size_t)(pos0 + b) * HALF + d];
+            const float x = q[d], y = q[d + HALF];
+            a0 = x * cs.x - y * cs.y;
+            a1 = x * cs.y + y * cs.x;
+        }
+        const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+        qh[r * HP + d] = __builtin_bit_cast(uint16_t, h0);
+        qh[r * HP + d + HALF] = __builtin_bit_cast(uint16_t, h1);
+        ql[r * HP + d] = f2h(a0 - (float)h0);
+        ql[r * HP + d + HALF] = f2h(a1 - (float)h1);
+    }
+    __syncthreads();
+
+    // scores: wave w takes positions 16w .. 16w + 15 of every row tile
+    const float scale = 1.0f / sqrtf((float)HD);
+    const int li = lane & 15, lk = lane >> 4;
+    for (int rt = 0; rt < RT; ++rt) {
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int d0 = k * 32 + lk * 8;
+            const h8 bk = *reinterpret_cast<const h8 *>(kt + (w * 16 + li) * HP + d0);
+            const h8 ah = *reinterpret_cast<const h8 *>(qh + (rt * 16 + li) * HP + d0);
+            const h8 al = *reinterpret_cast<const h8 *>(ql + (rt * 16 + li) * HP + d0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bk, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bk, acc, 0, 0, 0);
+        }
+        // lane holds rows rt*16 + 4*lk + e of position column w*16 + li
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rt * 16 + 4 * lk + e;
+            const int j = w * 16 + li;
+            const bool live = r < rows && c0 + j <= pos0 + r / QH;
+            ps[r * SP + j] = live ? acc[e] * scale : -INFINITY;
         }
     }
     __syncthreads();
 
-    const float scale = 1.0f / sqrtf((float)HD);
-    for (int b = w; b < batch; b += NW) {
-        float *pout = part + (size_t)b * colstride + (((size_t)g * nchunk + c) * QH) * prow;
-        const int pos = pos0 + b;
-        const int n = max(0, min(kAP, pos + 1 - c0)); // positions of this chunk it sees
-        if (n == 0) {
-            for (int i = lane; i < QH * (HD + 2); i += 64) {
-                const int h = i / (HD + 2), e = i % (HD + 2);
-                pout[h * prow + e] = e == HD ? -INFINITY : 0.0f;
-            }
-            continue;
+    // softmax of each row over the chunk: rows w, w + 4, ...; lane = position
+    for (int r = w; r < RP; r += NW) {
+        const float sv = ps[r * SP + lane];
+        const float m = wave_max(sv);
+        const float e = m == -INFINITY ? 0.0f : expf(sv - m);
+        const float l = wave_sum(e);
+        ps[r * SP + lane] = e;
+        if (lane == 0) {
+            mrow[r] = m;
+            lrow[r] = l;
         }
-        // rotated queries of this column
-        if (lane < HALF) {
-            const float2 cs = rope[(size_t)pos * HALF + lane];
-#pragma unroll
-            for (int h = 0; h < QH; ++h) {
-                const float *q = qkv + (size_t)b * nqkv + (size_t)(g * QH + h) * HD;
-                const float a = q[lane], bb = q[lane + HALF];
-                qr[w][h][lane] = a * cs.x - bb * cs.y;
-                qr[w][h][lane + HALF] = a * cs.y + bb * cs.x;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // scores: lane = position
-        float acc[QH];
-#pragma unroll
-        for (int h = 0; h < QH; ++h)
-            acc[h] = 0.0f;
-#pragma unroll 4
-        for (int d0 = 0; d0 < HD; d0 += 8) {
-            float kf[8];
-            unpack8(*reinterpret_cast<const uint4 *>(kt + lane * HP + d0), kf);
-#pragma unroll
-            for (int h = 0; h < QH; ++h) {
-                const float4 qa = *reinterpret_cast<const float4 *>(&qr[w][h][d0]);
-                const float4 qb = *reinterpret_cast<const float4 *>(&qr[w][h][d0 + 4]);
-                float a = acc[h];
-                a = fmaf(qa.x, kf[0], a);
-                a = fmaf(qa.y, kf[1], a);
-                a = fmaf(qa.z, kf[2], a);
-                a = fmaf(qa.w, kf[3], a);
-                a = fmaf(qb.x, kf[4], a);
-                a = fmaf(qb.y, kf[5], a);
-                a = fmaf(qb.z, kf[6], a);
-                a = fmaf(qb.w, kf[7], a);
-                acc[h] = a;
-            }
-        }
-        float mh[QH], lh[QH];
-#pragma unroll
-        for (int h = 0; h < QH; ++h) {
-            const float sv = lane < n ? acc[h] * scale : -INFINITY;
-            const float m = wave_max(sv);
-            const float e = lane < n ? expf(sv - m) : 0.0f;
-            mh[h] = m;
-            lh[h] = wave_sum(e);
-            pw[w][h][lane] = e;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // value sum: lane = DPL dims of the head dimension
-        float o[QH][DPL];
-#pragma unroll
-        for (int h = 0; h < QH; ++h)
-#pragma unroll
-            for (int e = 0; e < DPL; ++e)
-                o[h][e] = 0.0f;
-        for (int j0 = 0; j0 < n; j0 += 4) {
-            float4 p4[QH];
-#pragma unroll
-            for (int h = 0; h < QH; ++h)
-                p4[h] = *reinterpret_cast<const float4 *>(&pw[w][h][j0]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t *vr = vt + (j0 + i) * HP + lane * DPL;
-                float vf[DPL];
-                if constexpr (DPL == 2) {
-                    const uint32_t v2 = *reinterpret_cast<const uint32_t *>(vr);
-                    vf[0] = h2f((uint16_t)(v2 & 0xFFFFu));
-                    vf[1] = h2f((uint16_t)(v2 >> 16));
-                } else {
-                    vf[0] = h2f(vr[0]);
-                }
-#pragma unroll
-                for (int h = 0; h < QH; ++h) {
-                    const float p = i == 0 ? p4[h].x : i == 1 ? p4[h].y : i == 2 ? p4[h].z : p4[h].w;
-#pragma unroll
-                    for (int e = 0; e < DPL; ++e)
-                        o[h][e] = fmaf(p, vf[e], o[h][e]);
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < QH; ++h) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e)
-                pout[h * prow + lane * DPL + e] = o[h][e];
-            if (lane == 0) {
-                pout[h * prow + HD] = mh[h];
-                pout[h * prow + HD + 1] = lh[h];
-            }
-        }
-        // the next column of this wave rewrites qr and pw
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();
+
+    // outputs: wave w takes column tiles w, w + 4, ... of every row tile
+    for (int dt = w; dt < DT; dt += NW) {
+        for (int rt = 0; rt < RT; ++rt) {
+            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < kAP / 32; ++k) {
+                const int j0 = k * 32 + lk * 8;
+                const float *pr = ps + (rt * 16 + li) * SP + j0;
+                const float4 p0 = *reinterpret_cast<const float4 *>(pr);
+                const float4 p1 = *reinterpret_cast<const float4 *>(pr + 4);
+                const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                h8 ph, pl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ph[e] = (_Float16)pv[e];
+                    pl[e] = (_Float16)(pv[e] - (float)ph[e]);
+                }
+                const h8 bv = *reinterpret_cast<const h8 *>(vt + (dt * 16 + li) * VP + j0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rt * 16 + 4 * lk + e;
+                if (r < rows) {
+                    const int b = r / QH, h = r % QH;
+                    float *pout = part + b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow;
+                    pout[dt * 16 + li] = acc[e];
+                }
+            }
+        }
+    }
+    for (int r = t; r < rows; r += kAThreads) {
+        const int b = r / QH, h = r % QH;
+        float *pout = part + b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow;
+        pout[HD] = mrow[r];
+        pout[HD + 1] = lrow[r];
+    }
+}
+
+size_t tile_mfma_lds(int qh, int hd, int batch) {
+    const int rp = (batch * qh + 15) / 16 * 16;
+    return (size_t)kAP * (hd + 8) * 2 + (size_t)hd * (kAP + 8) * 2 + 2 * (size_t)rp * (hd + 8) * 2 +
+           (size_t)rp * (kAP + 4) * 4 + 2 * (size_t)rp * 4;
 }
 
 using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *, const int32_t *,
@@ -561,24 +582,50 @@ using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *
                            const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
 using CombineFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
-using BatchFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
-                         const int32_t *, int32_t, int32_t, int32_t, float *, int32_t, int32_t);
+using TileFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
+                        const int32_t *, int32_t, int32_t, int32_t, float *, int32_t, int32_t);
 
 struct AttnFns {
     PartialFn partial = nullptr;
-    BatchFn batch = nullptr;
     CombineFn combine = nullptr;
     AppendFn append = nullptr;
+    TileFn tile = nullptr;
+    size_t tile_lds_max = 0; // dynamic LDS the tile kernel may use (0: not usable)
 };
+
+// The tile kernel's dynamic LDS may exceed the default per-block limit:
+// opt it into the device's maximum once.
+template <int QH, int HD>
+size_t tile_lds_limit() {
+    static const size_t lim = [] {
+        int dev = 0, max_lds = 0, optin = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return (size_t)0;
+        if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+            max_lds = 0;
+        if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) !=
+            hipSuccess)
+            optin = 0;
+        const int lds = std::max(max_lds, optin);
+        if (lds <= 0 || hipFuncSetAttribute((const void *)attn_tile_mfma<QH, HD>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            lds) != hipSuccess)
+            return (size_t)0;
+        return (size_t)lds;
+    }();
+    return lim;
+}
 
 template <int QH, int HD>
 bool pick(int qh, int hd, bool batch, AttnFns &f) {
     if (qh != QH || hd != HD)
         return false;
     f.partial = attn_partial<QH, HD>;
-    f.batch = attn_batch_tile<QH, HD>;
     f.combine = batch ? attn_combine<QH, HD, true> : attn_combine<QH, HD, false>;
     f.append = kv_append_batch<HD>;
+    f.tile = attn_tile_mfma<QH, HD>;
+    f.tile_lds_max = tile_lds_limit<QH, HD>();
     return true;
 }
 
@@ -633,11 +680,15 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
         return fail(Q4_ERR_INVALID_ARG, "attention: %d chunks for max_ctx %d", a.nchunk,
                     a.max_ctx);
     if (bt) {
+        const size_t lds = tile_mfma_lds(qh, a.hd, a.batch);
+        if (lds > f.tile_lds_max)
+            return fail(Q4_ERR_UNSUPPORTED, "attention: tile needs %zu bytes of LDS, %zu available",
+                        lds, f.tile_lds_max);
         hipLaunchKernelGGL(f.append, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0,
                            s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                            a.max_ctx, a.H, a.Hkv);
         Q4_HIP(hipGetLastError());
-        hipLaunchKernelGGL(f.batch, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), 0,
+        hipLaunchKernelGGL(f.tile, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), lds,
                            s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                            a.max_ctx, a.H, a.Hkv, a.part, a.nchunk, a.batch);
     } else {
