@@ -137,9 +137,10 @@ q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
  * and k_split in {1, 2, 4} (rows held by each 16-lane row of a wave, waves
  * sharing one row's k range), chunks_in_flight in {4, 8} (16-byte chunks of
  * each row a lane loads before using them), nontemporal 0/1 (weight loads
- * marked non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} (8 only
- * with waves == 4) and waves in {4, 8} (16-row tiles per workgroup, waves
- * splitting k); B == 1 is allowed and runs the matrix-core kernel.
+ * marked non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} and
+ * waves in {4, 8, 16} (16-row tiles per workgroup, waves splitting k), with
+ * row_tiles 8 only for 4 waves and 4 only up to 8 waves; B == 1 is allowed
+ * and runs the matrix-core kernel.
  * INVALID_ARG / UNSUPPORTED for other values. */
 q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales,
                         const uint16_t *x_f16, float *y, int64_t N, int64_t K,

@@ -84,25 +84,31 @@ struct Quad {
     uint4 w[RT];
     uint32_t s[RT]; // binary16 bits, zero-extended (keeps the struct in registers)
     uint4 x[4];
+    bool live;      // the lane's group exists (false: scale taken as 0)
 };
 
+// Every load is unconditional (addresses clamped into the matrix and into
+// column 0 of X), so the compiler's wait counts stay exact and the next
+// quad's loads remain in flight while the current quad is multiplied.  A
+// group past the last one (K / 32 not a multiple of 4) gets scale 0, which
+// zeroes its weights; a padding column multiplies real activations of column
+// 0 and its outputs are never stored.
 template <int RT>
 __device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wrow)[RT],
                                           const uint16_t *const (&srow)[RT],
-                                          const uint16_t *xb, int q, int kq, int C,
-                                          bool bvalid) {
+                                          const uint16_t *xb, int q, int kq, int C) {
     const int g = q * 4 + kq;
-    const bool gvalid = g < C;
-    const int gc = gvalid ? g : C - 1;
+    o.live = g < C;
+    const int gc = o.live ? g : C - 1;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         o.w[t] = ntload16(wrow[t] + (size_t)gc * 16);
-        o.s[t] = gvalid ? (uint32_t)ntload2(srow[t] + gc) : 0u;
+        o.s[t] = ntload2(srow[t] + gc);
     }
     const uint16_t *xp = xb + (size_t)gc * 32;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        o.x[p] = (bvalid && gvalid) ? gload16(xp + 8 * p) : uint4{0u, 0u, 0u, 0u};
+        o.x[p] = gload16(xp + 8 * p);
 }
 
 template <int RT>
@@ -113,7 +119,7 @@ __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT],
         bop[p] = __builtin_bit_cast(half8_t, permute_block(o.x[p]));
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)o.s[t]);
+        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(o.live ? o.s[t] : 0u));
         const half2_t s2 = {sh, sh};
         const uint32_t wd[4] = {o.w[t].x, o.w[t].y, o.w[t].z, o.w[t].w};
 #pragma unroll
@@ -133,7 +139,7 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     __shared__ float4_t red[NW][RT][64];
     const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i16 = lane & 15;
     const int kq = lane >> 4;
     const int C = K >> 5;
@@ -160,22 +166,30 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
         acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // Two register buffers: the next quad's loads are in flight while the
-    // current one is unpacked and multiplied.
+    // current one is unpacked and multiplied.  Inside the loop both
+    // prefetches are unconditional, so the compiler's wait before each
+    // multiply covers only the quad it needs.
     Quad<RT> qa, qb;
     int q = wave;
-    if (q < nquads)
-        load_quad<RT>(qa, wrow, srow, xb, q, kq, C, bvalid);
-    while (q < nquads) {
-        if (q + NW < nquads)
-            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C, bvalid);
-        mma_quad<RT>(qa, acc, bias);
-        q += NW;
-        if (q >= nquads)
-            break;
-        if (q + NW < nquads)
-            load_quad<RT>(qa, wrow, srow, xb, q + NW, kq, C, bvalid);
-        mma_quad<RT>(qb, acc, bias);
-        q += NW;
+    if (q < nquads) {
+        load_quad<RT>(qa, wrow, srow, xb, q, kq, C);
+        while (q + 2 * NW < nquads) {
+            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C);
+            __builtin_amdgcn_sched_barrier(0); // issue before waiting for qa
+            mma_quad<RT>(qa, acc, bias);
+            load_quad<RT>(qa, wrow, srow, xb, q + 2 * NW, kq, C);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_quad<RT>(qb, acc, bias);
+            q += 2 * NW;
+        }
+        if (q + NW < nquads) {
+            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_quad<RT>(qa, acc, bias);
+            mma_quad<RT>(qb, acc, bias);
+        } else {
+            mma_quad<RT>(qa, acc, bias);
+        }
     }
 
     if constexpr (NW > 1) {
@@ -221,6 +235,7 @@ GemmFn pick_gemm(int RT, int NW) {
         return gemm_mfma_kernel<rt, nw, ACC>;
     Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
     Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
+    Q4_PICK(1, 16) Q4_PICK(2, 16)
 #undef Q4_PICK
     return nullptr;
 }
@@ -243,12 +258,19 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
                            float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
                            bool accumulate) {
+    // Launch shape from a sweep over the 8B product shapes (6144, 4096,
+    // 28672 x 4096 and 4096 x 14336; B = 2, 4, 8, 16): every row tile a
+    // wave holds reuses the activation registers, so wider batches want
+    // more row tiles per wave, as long as about 3/4 of the CUs still get a
+    // workgroup; four waves split k unless the batch is narrow and the
+    // matrix tall.
     const int64_t tiles = (N + 15) / 16;
     const int cus = device_cus();
-    int RT = 4;
-    while (RT > 1 && tiles / RT < 2 * cus)
-        RT /= 2;
-    int NW = (tiles / RT < 4LL * cus) ? 8 : 4;
+    const int rt_cap = std::max(2, B / 2);
+    int RT = 1;
+    while (RT * 2 <= std::min(rt_cap, 8) && tiles / (RT * 2) >= (int64_t)cus * 3 / 4)
+        RT *= 2;
+    const int NW = (B <= 4 && RT == 2 && tiles / RT >= 2LL * cus) ? 8 : 4;
     return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream, accumulate);
 }
 

@@ -68,6 +68,7 @@ def test_gemm_argument_checks():
     assert L.q4_gemm_smallbatch(buf, buf, buf + 4, buf, 16, 64, 4, None) == INVALID
     assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 3, 4, None) == UNSUPPORTED
     assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 8, 8, None) == UNSUPPORTED
+    assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 4, 16, None) == UNSUPPORTED
 
 
 def test_pack_argument_checks():

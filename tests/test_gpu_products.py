@@ -198,7 +198,8 @@ def test_gemm_small_shapes(B, N, K):
         assert_within(Y[b], Y_ref[b], M[b], f"gemm B={B} {N}x{K} col {b}")
 
 
-@pytest.mark.parametrize("rt,nw", [(1, 4), (2, 4), (4, 4), (8, 4), (1, 8), (2, 8), (4, 8)])
+@pytest.mark.parametrize("rt,nw", [(1, 4), (2, 4), (4, 4), (8, 4), (1, 8), (2, 8), (4, 8),
+                                   (1, 16), (2, 16)])
 def test_gemm_every_launch_shape(rt, nw):
     N, K, B = 200, 1184, 7  # 37 groups: ragged group quads
     packed, scales = _mat(N, K, 900)
