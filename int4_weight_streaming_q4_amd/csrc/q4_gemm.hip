@@ -259,18 +259,19 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
                            float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
                            bool accumulate) {
     // Launch shape from a sweep over the 8B product shapes (6144, 4096,
-    // 28672 x 4096 and 4096 x 14336; B = 2, 4, 8, 16): every row tile a
+    // 28672 x 4096 and 4096 x 14336; B = 2, 4, 8, 16).  Every row tile a
     // wave holds reuses the activation registers, so wider batches want
     // more row tiles per wave, as long as about 3/4 of the CUs still get a
-    // workgroup; four waves split k unless the batch is narrow and the
-    // matrix tall.
+    // workgroup.  The row tiles do not change any output's summation order;
+    // the k split (waves per workgroup) does, so it stays fixed at four: a
+    // column's result is then independent of B and of the other columns.
     const int64_t tiles = (N + 15) / 16;
     const int cus = device_cus();
-    const int rt_cap = std::max(2, B / 2);
+    const int rt_cap = B <= 2 ? 2 : (B < 16 ? 4 : 8);
     int RT = 1;
-    while (RT * 2 <= std::min(rt_cap, 8) && tiles / (RT * 2) >= (int64_t)cus * 3 / 4)
+    while (RT * 2 <= rt_cap && tiles / (RT * 2) >= (int64_t)cus * 3 / 4)
         RT *= 2;
-    const int NW = (B <= 4 && RT == 2 && tiles / RT >= 2LL * cus) ? 8 : 4;
+    const int NW = 4;
     return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream, accumulate);
 }
 

@@ -238,3 +238,18 @@ def test_gemm_workload_shapes_sampled_rows(name, B):
     for b in range(B):
         y_ref, mag = oracle.gemv_rows(hp, hs, hx[b], rows)
         assert_within(Y[b][rows], y_ref, mag, f"{name} B={B} col {b}")
+
+
+@pytest.mark.parametrize("name", ["8b_gate_up", "8b_down"])
+def test_gemm_columns_independent_of_batch(name):
+    """The launch shape may change with B, but no output's summation order
+    does: column b of a B-column product equals column b of the 16-column
+    product bitwise, whatever B and the other columns are."""
+    N, K = WORKLOAD_SHAPES[name]
+    packed, scales = _mat(N, K, inputs.seed_of(3, 1, list(WORKLOAD_SHAPES).index(name)))
+    X = inputs.act_f16((16, K), inputs.seed_of(3, 1, 9), device=DEV)
+    full = _gemm(packed, scales, X)
+    for B in (2, 3, 4, 9):
+        assert np.array_equal(_gemm(packed, scales, X[:B].contiguous()), full[:B]), B
+    perm = torch.tensor([5, 0, 3])
+    assert np.array_equal(_gemm(packed, scales, X[perm].contiguous()), full[perm.numpy()])
