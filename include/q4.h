@@ -212,8 +212,8 @@ typedef struct {
      * max_batch > 0 the workspace also holds, after the sections above,
      * 256-byte aligned: binary16 [max_batch][d_model] (normed input),
      * fp32 [max_batch][(H + 2 Hkv) hd] (QKV), binary16 [max_batch][H hd]
-     * (attention output), fp32 [max_batch][2 d_ff] (gate+up), binary16
-     * [max_batch][d_ff] (gated MLP activation).  With a KV cache too, the
+     * (attention output), binary16 [max_batch][d_ff] (gated MLP
+     * activation).  With a KV cache too, the
      * attention partials are sized for max_batch columns. */
     int32_t max_batch;
     float *h_batch;

@@ -62,7 +62,6 @@ struct Decoder {
     uint16_t *xb = nullptr;      // f16[max_batch][d]
     float *qkvb = nullptr;       // f32[max_batch][nqkv]
     uint16_t *oinb = nullptr;    // f16[max_batch][H*hd]
-    float *gub = nullptr;        // f32[max_batch][2 dff]
     uint16_t *mlpb = nullptr;    // f16[max_batch][dff]
     hipGraphExec_t vexec[4][Q4_MAX_BATCH + 1] = {}; // [context bucket][B]
 };
@@ -112,8 +111,7 @@ size_t verify_bytes(const Dims &d, int32_t mb) {
     if (mb <= 0)
         return 0;
     return align256((size_t)mb * d.d * 2) + align256((size_t)mb * d.nqkv * 4) +
-           align256((size_t)mb * d.H * d.hd * 2) + align256((size_t)mb * 2 * d.dff * 4) +
-           align256((size_t)mb * d.dff * 2);
+           align256((size_t)mb * d.H * d.hd * 2) + align256((size_t)mb * d.dff * 2);
 }
 
 size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) {
@@ -335,9 +333,8 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
         Q4_CHECK(launch_gemm_mfma(L.o.packed, L.o.scales, dec->oinb, dec->hb, L.o.N, L.o.K, B, s,
                                   true));
         Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
-        Q4_CHECK(launch_gemm_mfma(L.gate_up.packed, L.gate_up.scales, dec->xb, dec->gub,
-                                  L.gate_up.N, L.gate_up.K, B, s));
-        Q4_CHECK(launch_silu_batch(dec->gub, dec->mlpb, B, (int32_t)d.dff, s));
+        Q4_CHECK(launch_gemm_silu_pair(L.gate_up.packed, L.gate_up.scales, dec->xb,
+                                       dec->mlpb, d.dff, L.gate_up.K, B, s));
         Q4_CHECK(launch_gemm_mfma(L.down.packed, L.down.scales, dec->mlpb, dec->hb, L.down.N,
                                   L.down.K, B, s, true));
     }
@@ -490,8 +487,6 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
         ws += q4::align256(mb * d.nqkv * 4);
         dec->oinb = reinterpret_cast<uint16_t *>(ws);
         ws += q4::align256(mb * d.H * d.hd * 2);
-        dec->gub = reinterpret_cast<float *>(ws);
-        ws += q4::align256(mb * 2 * d.dff * 4);
         dec->mlpb = reinterpret_cast<uint16_t *>(ws);
     }
     if (m->layers) {

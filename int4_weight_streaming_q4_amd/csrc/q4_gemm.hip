@@ -129,13 +129,19 @@ __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT],
     }
 }
 
-// ACC: Y += W X (each output is written by one lane: no race) instead of
-// Y = W X.
-template <int RT, int NW, bool ACC>
+// Epilogues.  Store: Y = W X.  Acc: Y += W X (each output is written by one
+// lane: no race).  SiluPair: W holds `npair` gate rows then `npair` up rows;
+// the first RT/2 row tiles of a wave are gate rows and the rest the up rows
+// of the same units, and the kernel writes M[b][u] = binary16(silu(g) * up)
+// (silu(g) = g / (1 + exp(-g)), in fp32) instead of the fp32 products.
+enum class GEpi { Store, Acc, SiluPair };
+
+template <int RT, int NW, GEpi E>
 __global__ void __launch_bounds__(64 * NW)
 gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
-                 int B) {
+                 int B, uint16_t *__restrict__ M, int64_t npair) {
+    static_assert(E != GEpi::SiluPair || RT % 2 == 0, "gate and up tiles come in pairs");
     __shared__ float4_t red[NW][RT][64];
     const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
@@ -145,7 +151,8 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int C = K >> 5;
     const int nquads = (C + 3) >> 2;
     const size_t row_bytes = (size_t)K >> 1;
-    const int64_t row0 = (int64_t)blockIdx.x * (16 * RT);
+    // first row (Store, Acc) or first unit (SiluPair) of this workgroup
+    const int64_t row0 = (int64_t)blockIdx.x * (E == GEpi::SiluPair ? 8 * RT : 16 * RT);
 
     const bool bvalid = i16 < B;
     const uint16_t *xb = X16 + (size_t)(bvalid ? i16 : 0) * K;
@@ -154,8 +161,17 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *srow[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        int64_t row = row0 + t * 16 + i16;
-        row = row < N ? row : N - 1;
+        int64_t row;
+        if constexpr (E == GEpi::SiluPair) {
+            const int th = t % (RT / 2);
+            row = row0 + th * 16 + i16;
+            row = row < npair ? row : npair - 1;
+            if (t >= RT / 2)
+                row += npair;
+        } else {
+            row = row0 + t * 16 + i16;
+            row = row < N ? row : N - 1;
+        }
         wrow[t] = W + (size_t)row * row_bytes;
         srow[t] = S + (size_t)row * C;
     }
@@ -210,34 +226,74 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     // D layout: lane holds rows 4*(lane/16) + 0..3 of column lane % 16.
     if (!bvalid)
         return;
+    if constexpr (E == GEpi::SiluPair) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
+        for (int t = 0; t < RT / 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = row0 + t * 16 + 4 * kq + e;
-            if (row < N) {
-                if constexpr (ACC)
-                    Y[(size_t)i16 * N + row] += acc[t][e];
-                else
-                    Y[(size_t)i16 * N + row] = acc[t][e];
+            for (int e = 0; e < 4; ++e) {
+                const int64_t unit = row0 + t * 16 + 4 * kq + e;
+                if (unit < npair) {
+                    const float g = acc[t][e], up = acc[t + RT / 2][e];
+                    const float silu = g / (1.0f + expf(-g));
+                    M[(size_t)i16 * npair + unit] =
+                        __builtin_bit_cast(uint16_t, (_Float16)(silu * up));
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = row0 + t * 16 + 4 * kq + e;
+                if (row < N) {
+                    if constexpr (E == GEpi::Acc)
+                        Y[(size_t)i16 * N + row] += acc[t][e];
+                    else
+                        Y[(size_t)i16 * N + row] = acc[t][e];
+                }
             }
         }
     }
 }
 
 using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
-                        int, int);
+                        int, int, uint16_t *, int64_t);
 
-template <bool ACC>
+template <GEpi E>
 GemmFn pick_gemm(int RT, int NW) {
 #define Q4_PICK(rt, nw)                                                          \
     if (RT == rt && NW == nw)                                                    \
-        return gemm_mfma_kernel<rt, nw, ACC>;
-    Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
-    Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
-    Q4_PICK(1, 16) Q4_PICK(2, 16)
+        return gemm_mfma_kernel<rt, nw, E>;
+    if constexpr (E == GEpi::SiluPair) {
+        Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
+    } else {
+        Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
+        Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
+        Q4_PICK(1, 16) Q4_PICK(2, 16)
+    }
 #undef Q4_PICK
     return nullptr;
+}
+
+// Row tiles per wave for a product of N rows and B columns, from a sweep
+// over the 8B product shapes (6144, 4096, 28672 x 4096 and 4096 x 14336;
+// B = 2, 4, 8, 16).  Every row tile a wave holds reuses the activation
+// registers, so wider batches want more row tiles per wave, as long as
+// about 3/4 of the CUs still get a workgroup.  The row tiles do not change
+// any output's summation order; the k split (waves per workgroup) does, so
+// it stays fixed at kGemmWaves: a column's result is then independent of B
+// and of the other columns.
+constexpr int kGemmWaves = 4;
+
+int pick_row_tiles(int64_t N, int32_t B) {
+    const int64_t tiles = (N + 15) / 16;
+    const int cus = device_cus();
+    const int rt_cap = B <= 2 ? 2 : (B < 16 ? 4 : 8);
+    int RT = 1;
+    while (RT * 2 <= rt_cap && tiles / (RT * 2) >= (int64_t)cus * 3 / 4)
+        RT *= 2;
+    return RT;
 }
 
 } // namespace
@@ -245,12 +301,12 @@ GemmFn pick_gemm(int RT, int NW) {
 q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
                                const uint16_t *X16, float *Y, int64_t N, int64_t K,
                                int32_t B, int RT, int NW, hipStream_t stream, bool accumulate) {
-    GemmFn fn = accumulate ? pick_gemm<true>(RT, NW) : pick_gemm<false>(RT, NW);
+    GemmFn fn = accumulate ? pick_gemm<GEpi::Acc>(RT, NW) : pick_gemm<GEpi::Store>(RT, NW);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no kernel for row_tiles=%d waves=%d", RT, NW);
     const int64_t blocks = (N + 16 * RT - 1) / (16 * RT);
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, packed, scales,
-                       X16, Y, N, (int)K, B);
+                       X16, Y, N, (int)K, B, nullptr, (int64_t)0);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }
@@ -258,21 +314,22 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
                            float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
                            bool accumulate) {
-    // Launch shape from a sweep over the 8B product shapes (6144, 4096,
-    // 28672 x 4096 and 4096 x 14336; B = 2, 4, 8, 16).  Every row tile a
-    // wave holds reuses the activation registers, so wider batches want
-    // more row tiles per wave, as long as about 3/4 of the CUs still get a
-    // workgroup.  The row tiles do not change any output's summation order;
-    // the k split (waves per workgroup) does, so it stays fixed at four: a
-    // column's result is then independent of B and of the other columns.
-    const int64_t tiles = (N + 15) / 16;
-    const int cus = device_cus();
-    const int rt_cap = B <= 2 ? 2 : (B < 16 ? 4 : 8);
-    int RT = 1;
-    while (RT * 2 <= rt_cap && tiles / (RT * 2) >= (int64_t)cus * 3 / 4)
-        RT *= 2;
-    const int NW = 4;
-    return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, RT, NW, stream, accumulate);
+    return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, pick_row_tiles(N, B),
+                                kGemmWaves, stream, accumulate);
+}
+
+q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
+                                const uint16_t *X16, uint16_t *M, int64_t npair, int64_t K,
+                                int32_t B, hipStream_t stream) {
+    const int RT = std::max(2, pick_row_tiles(2 * npair, B));
+    GemmFn fn = pick_gemm<GEpi::SiluPair>(RT, kGemmWaves);
+    if (!fn)
+        return fail(Q4_ERR_UNSUPPORTED, "gemm: no paired kernel for row_tiles=%d", RT);
+    const int64_t blocks = (npair + 8 * RT - 1) / (8 * RT);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * kGemmWaves), 0, stream, packed,
+                       scales, X16, nullptr, 2 * npair, (int)K, B, M, npair);
+    Q4_HIP(hipGetLastError());
+    return Q4_OK;
 }
 
 } // namespace q4

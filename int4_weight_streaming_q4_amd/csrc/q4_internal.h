@@ -103,5 +103,10 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales,
                            const uint16_t *X16, float *Y, int64_t N, int64_t K,
                            int32_t B, hipStream_t stream, bool accumulate = false);
+// Small-batch gate+up product with the SiLU gate fused: `packed` holds npair
+// gate rows then npair up rows; M[b][u] = binary16(silu(gate) * up).
+q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
+                                const uint16_t *X16, uint16_t *M, int64_t npair, int64_t K,
+                                int32_t B, hipStream_t stream);
 
 } // namespace q4

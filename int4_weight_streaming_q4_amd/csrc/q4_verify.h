@@ -13,8 +13,5 @@ q4_status launch_rmsnorm_batch(const float *H, uint16_t *X, int32_t B, int32_t d
 // of each row of qkv f32[B][nqkv].
 q4_status launch_gather_batch(const float *qkv, uint16_t *o, int32_t B, int32_t H,
                               int32_t Hkv, int32_t hd, hipStream_t s);
-// m[b][j] = f16(silu(gu[b][j]) * gu[b][dff + j]); gu f32[B][2 dff].
-q4_status launch_silu_batch(const float *gu, uint16_t *m, int32_t B, int32_t dff,
-                            hipStream_t s);
 
 } // namespace q4

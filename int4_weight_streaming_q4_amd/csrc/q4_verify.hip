@@ -8,9 +8,9 @@
 // target model; PIPO: Pipelined Offloading for Efficient Inference on
 // Consumer Devices, "Method", "Automatic configuration": its 4-bit kernel
 // serves batches below 16.  The glue is the same one-token glue as the
-// single-token step (RMSNorm to binary16, the V of each query head's group,
-// SiLU gate); a causal batch gives every column exactly the result of
-// decoding its token alone.
+// single-token step (RMSNorm to binary16, the V of each query head's group;
+// the SiLU gate runs in the gate+up product's epilogue); a causal batch
+// gives every column exactly the result of decoding its token alone.
 #include <cmath>
 
 #include "q4_verify.h"
@@ -87,18 +87,6 @@ gather_batch_kernel(const float *__restrict__ qkv, uint16_t *__restrict__ o, int
     o[(size_t)b * H * hd + j] = f2h(qkv[(size_t)b * nqkv + (H + Hkv) * hd + g * hd + j % hd]);
 }
 
-__global__ void __launch_bounds__(kVThreads)
-silu_batch_kernel(const float *__restrict__ gu, uint16_t *__restrict__ m, int32_t dff) {
-    const int b = blockIdx.y;
-    const int j = blockIdx.x * kVThreads + threadIdx.x;
-    if (j >= dff)
-        return;
-    const float g = gu[(size_t)b * 2 * dff + j];
-    const float u = gu[(size_t)b * 2 * dff + dff + j];
-    const float silu = g / (1.0f + expf(-g));
-    m[(size_t)b * dff + j] = f2h(silu * u);
-}
-
 } // namespace
 
 q4_status launch_rmsnorm_batch(const float *H, uint16_t *X, int32_t B, int32_t d, float eps,
@@ -114,15 +102,6 @@ q4_status launch_gather_batch(const float *qkv, uint16_t *o, int32_t B, int32_t 
     const unsigned gx = (unsigned)((H * hd + kVThreads - 1) / kVThreads);
     hipLaunchKernelGGL(gather_batch_kernel, dim3(gx, (unsigned)B), dim3(kVThreads), 0, s, qkv,
                        o, H, Hkv, hd);
-    Q4_HIP(hipGetLastError());
-    return Q4_OK;
-}
-
-q4_status launch_silu_batch(const float *gu, uint16_t *m, int32_t B, int32_t dff,
-                            hipStream_t s) {
-    const unsigned gx = (unsigned)((dff + kVThreads - 1) / kVThreads);
-    hipLaunchKernelGGL(silu_batch_kernel, dim3(gx, (unsigned)B), dim3(kVThreads), 0, s, gu, m,
-                       dff);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }

@@ -165,8 +165,9 @@ def test_decoder_kv_cache_description_checks():
 
 
 def test_decoder_verify_checks():
-    """Verify-step sections: per column d f16, nqkv f32, H hd f16, 2 dff f32,
-    dff f16, each rounded up to 256; argument and state errors before HIP."""
+    """Verify-step sections: per column d f16, nqkv f32, H hd f16, dff f16
+    (the gate+up product writes the gated activation directly), each
+    rounded up to 256; argument and state errors before HIP."""
     L = q4.lib()
     plain, with_b = ctypes.c_size_t(), ctypes.c_size_t()
     assert L.q4_decoder_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(plain)) == 0
@@ -174,7 +175,7 @@ def test_decoder_verify_checks():
                                         ctypes.byref(with_b)) == 0
     a = lambda n: (n + 255) // 256 * 256
     # DIMS: d 64, nqkv (4 + 4) * 16 = 128, H hd 64, dff 96
-    want = a(9 * 64 * 2) + a(9 * 128 * 4) + a(9 * 64 * 2) + a(9 * 192 * 4) + a(9 * 96 * 2)
+    want = a(9 * 64 * 2) + a(9 * 128 * 4) + a(9 * 64 * 2) + a(9 * 96 * 2)
     assert with_b.value - plain.value == want
     assert q4.workspace_bytes(DIMS, n_layers=2, max_batch=9) == with_b.value
     out = ctypes.c_size_t()

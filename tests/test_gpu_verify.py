@@ -138,8 +138,7 @@ def verify_sections(dims, ws, n_layers, max_ctx, mb, B):
     a = lambda n: (n + 255) // 256 * 256
     d, H, Hkv, hd, dff = (dims[k] for k in ("d", "H", "Hkv", "hd", "dff"))
     nqkv = (H + 2 * Hkv) * hd
-    vb = a(mb * d * 2) + a(mb * nqkv * 4) + a(mb * H * hd * 2) + a(mb * 2 * dff * 4) + \
-        a(mb * dff * 2)
+    vb = a(mb * d * 2) + a(mb * nqkv * 4) + a(mb * H * hd * 2) + a(mb * dff * 2)
     total = q4.workspace_bytes(dims, n_layers=n_layers, max_ctx=max_ctx, max_batch=mb)
     o_qkv = total - vb + a(mb * d * 2)
     o_oin = o_qkv + a(mb * nqkv * 4)
