@@ -135,9 +135,13 @@ q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
 /* Tuning variants of the two products, for measurement: the same
  * arithmetic with an explicit launch shape.  q4_gemv_tuned: rows_per_slot
  * and k_split in {1, 2, 4} (rows held by each 16-lane row of a wave, waves
- * sharing one row's k range), chunks_in_flight in {4, 8} (16-byte chunks of
- * each row a lane loads before using them), nontemporal 0/1 (weight loads
- * marked non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} and
+ * sharing one row's k range), chunks_in_flight in {2, 4, 8} (16-byte chunks
+ * of each row a lane loads before using them; 2 selects the software-
+ * pipelined loop, two register buffers of two chunks with the next batch
+ * always in flight, which needs K % (1024 * k_split) == 0 and nontemporal 1,
+ * else UNSUPPORTED; at equal rows_per_slot and k_split it gives the same
+ * bits as the single-buffer loop), nontemporal 0/1 (weight loads marked
+ * non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} and
  * waves in {4, 8, 16} (16-row tiles per workgroup, waves splitting k), with
  * row_tiles 8 only for 4 waves and 4 only up to 8 waves; B == 1 is allowed
  * and runs the matrix-core kernel.

@@ -62,11 +62,36 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                                wp, sp, bias);
 }
 
+// The same product with the software-pipelined loop: two register buffers
+// of U chunks x R rows, the next batch always in flight (q4_gemv_core.h).
+// Requires K % (512 * KS * U) == 0 and grid <= row blocks.
+template <int R, int KS, int U, bool NT, Epi E, Pro P>
+__global__ void __launch_bounds__(kThreads)
+gemv_pipe_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
+                 const void *__restrict__ xin, int64_t N, int K, int64_t n_units, EpiArgs ea) {
+    extern __shared__ uint4 xs[];
+    __shared__ float red[kWaves][kSlots][R];
+    __shared__ float wsum[kWaves];
+    const uint32_t bias = vgpr_const(0x64006400u);
+    uint4 wA[U][R], wB[U][R];
+    uint32_t sA[U][R], sB[U][R];
+    XStage st;
+    stage_issue<P, false>(xin, K, st);
+    prefetch_pipe<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, gridDim.x, wA, sA, wB,
+                                   sB);
+    stage_finish<P, false>(xin, xs, K, ea, wsum, st);
+    __syncthreads();
+    run_units_pipe<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, gridDim.x, xs, red, wA,
+                                    sA, wB, sB, bias);
+}
+
 // ---------------------------------------------------------------- launch
 using KernelFn = void (*)(const uint8_t *, const uint16_t *, const void *, int64_t, int,
                           int64_t, EpiArgs);
 
-// Launch shape of one product kernel.
+// Launch shape of one product kernel.  U == 2 selects the software-pipelined
+// loop (two buffers of two chunks per row, non-temporal loads only); U == 4
+// or 8 the single-buffer loop with U chunks in flight.
 struct Cfg {
     int R, KS, U;
     bool NT;
@@ -74,6 +99,8 @@ struct Cfg {
 
 template <Epi E, Pro P, int R, int KS>
 KernelFn pick_ut(const Cfg &c) {
+    if (c.U == 2)
+        return c.NT ? gemv_pipe_kernel<R, KS, 2, true, E, P> : nullptr;
     if (c.U == 4)
         return c.NT ? gemv_kernel<R, KS, 4, true, E, P> : gemv_kernel<R, KS, 4, false, E, P>;
     if (c.U == 8)
@@ -154,6 +181,12 @@ int resident_blocks(KernelFn fn, size_t lds) {
 Cfg choose_config(Epi e, int64_t N, int64_t K) {
     const int64_t C = K / 32;
     Cfg c{2, 4, 4, true};
+    // The paired gate+up rows at K >= 8192 (57344 x 8192) stream faster with
+    // the pipelined loop and a 2-way split (44.1-44.5 vs 46.6-47.5 us); the
+    // other decode shapes gain nothing from it (their time goes to the
+    // launch's start and tail, not to the steady stream).
+    if (e == Epi::SiluPair && K >= 8192 && C % 64 == 0)
+        return Cfg{2, 2, 2, true};
     if (K < 8192) {
         if (e == Epi::SiluPair) {
             c.KS = 2;
@@ -193,6 +226,10 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED,
                     "gemv: no kernel for rows_per_slot=%d k_split=%d chunks=%d", R, KS, U);
+    if (U == 2 && (K / 32) % (32 * KS) != 0)
+        return fail(Q4_ERR_UNSUPPORTED,
+                    "gemv: the pipelined loop needs K %% (1024 * k_split) == 0 (K=%lld)",
+                    (long long)K);
     int64_t n_units;
     if (epi == Epi::SiluPair) {
         if (ea.pair_off * 2 != N)
@@ -246,10 +283,10 @@ extern "C" q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales
                         "q4_gemv_tuned: x must be 16-byte and y 4-byte aligned");
     if (!(rows_per_slot == 1 || rows_per_slot == 2 || rows_per_slot == 4) ||
         !(k_split == 1 || k_split == 2 || k_split == 4) ||
-        !(chunks_in_flight == 4 || chunks_in_flight == 8))
+        !(chunks_in_flight == 2 || chunks_in_flight == 4 || chunks_in_flight == 8))
         return q4::fail(Q4_ERR_INVALID_ARG,
                         "q4_gemv_tuned: rows_per_slot and k_split must be 1, 2 or 4, "
-                        "chunks_in_flight 4 or 8");
+                        "chunks_in_flight 2, 4 or 8");
     q4::EpiArgs ea{};
     ea.y = y;
     return q4::launch_gemv_cfg(packed, scales, x_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,

@@ -477,6 +477,79 @@ __device__ __forceinline__ void prefetch_block(const uint8_t *W, const uint16_t 
     }
 }
 
+// Sums a row's partials over its 16 lanes and then over the KS waves that
+// split its k range (LDS, fixed order).  Afterwards lane 0 of each slot of
+// the first wave of a row group holds the row totals.  KS > 1 synchronises
+// the workgroup twice, so every thread must call it.
+template <int R, int KS>
+__device__ __forceinline__ void reduce_rows(float (&acc)[R], float (*red)[kSlots][R]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sl = lane & 15;
+    const int slot = lane >> 4;
+    const int kpart = wave % KS;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = row16_sum(acc[r]);
+    if constexpr (KS > 1) {
+        if (sl == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                red[wave][slot][r] = acc[r];
+        }
+        __syncthreads();
+        if (kpart == 0 && sl == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float t = red[wave][slot][r];
+                for (int k = 1; k < KS; ++k)
+                    t += red[wave + k][slot][r];
+                acc[r] = t;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Writes the totals of output unit `unit` (lane 0 of its slot in the first
+// wave of the row group) through the epilogue E.
+template <int R, int KS, Epi E, bool COH>
+__device__ __forceinline__ void store_unit(const float (&acc)[R], int64_t unit, int64_t N,
+                                           int64_t n_units, const EpiArgs &ea) {
+    const int lane = threadIdx.x & 63;
+    const int kpart = (threadIdx.x >> 6) % KS;
+    if (kpart == 0 && (lane & 15) == 0 && unit < n_units) {
+        if constexpr (E == Epi::SiluPair) {
+            static_assert(R == 2, "paired rows need two rows per slot");
+            const float g = acc[0], up = acc[1];
+            const float silu = g / (1.0f + expf(-g));
+            act_store_u16<COH>(ea.out16 + unit, f32_to_f16(silu * up));
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = unit * R + r;
+                if (row < N) {
+                    if constexpr (E == Epi::Residual) {
+                        act_store_f32<COH>(ea.y + row, act_load_f32<COH>(ea.y + row) + acc[r]);
+                    } else {
+                        act_store_f32<COH>(ea.y + row, acc[r]);
+                        if constexpr (E == Epi::QkvGather) {
+                            if (row >= ea.v_off) {
+                                const int64_t v = row - ea.v_off;
+                                const int64_t g = v / ea.hd, i = v % ea.hd;
+                                const uint16_t h16 = f32_to_f16(acc[r]);
+                                for (int q = 0; q < ea.group; ++q)
+                                    act_store_u16<COH>(
+                                        ea.out16 + (g * ea.group + q) * ea.hd + i, h16);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Processes row blocks blk, blk + stride, ... of one product with the
 // activation already staged in LDS.  Precondition: the first chunk loads of
 // `blk` are in w/s (prefetch_block).  Every thread of the workgroup must
@@ -526,65 +599,159 @@ __device__ __forceinline__ void run_units(const uint8_t *W, const uint16_t *S, i
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            acc[r] = row16_sum(acc[r]);
-
-        if constexpr (KS > 1) {
-            if (sl == 0) {
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    red[wave][slot][r] = acc[r];
-            }
-            __syncthreads();
-            if (kpart == 0 && sl == 0) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float t = red[wave][slot][r];
-                    for (int k = 1; k < KS; ++k)
-                        t += red[wave + k][slot][r];
-                    acc[r] = t;
-                }
-            }
-            __syncthreads();
-        }
+        reduce_rows<R, KS>(acc, red);
 
         // The next row block's first loads go out before this epilogue.
         if (blk + stride < nblk) {
             setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk + stride, wp, sp);
             load_chunks<U, R, NT>(w, s, wp, sp, 0, nl, cstep);
         }
+        store_unit<R, KS, E, COH>(acc, unit, N, n_units, ea);
+    }
+}
 
-        if (kpart == 0 && sl == 0 && unit < n_units) {
-            if constexpr (E == Epi::SiluPair) {
-                static_assert(R == 2, "paired rows need two rows per slot");
-                const float g = acc[0], up = acc[1];
-                const float silu = g / (1.0f + expf(-g));
-                act_store_u16<COH>(ea.out16 + unit, f32_to_f16(silu * up));
-            } else {
+// ------------------------------------------------ software-pipelined loop
+// The same products with every lane's chunk loads kept in flight across row
+// blocks: two register buffers of U chunks x R rows alternate, and the loads
+// of batch q + 2 are issued as soon as batch q has been multiplied, so one
+// batch is always on its way while the other is in use.  A batch is U chunks
+// of one row block; with C = K / 32 chunks per row, a row block is
+// C / (16 KS U) batches.  Requires C % (16 KS U) == 0 (every lane then has
+// the same chunk count and no chunk is out of range) and at least one row
+// block per workgroup.  Chunks are accumulated in the same order as
+// run_units, so both give bitwise-equal results for the same KS.
+//
+// Scales are held one per 32-bit register: two binary16 scales packed into
+// one register would make the wave wait for a batch right after issuing it.
+template <int R, int KS, int U, bool NT, Epi E>
+__device__ __forceinline__ void load_batch(const uint8_t *W, const uint16_t *S, int64_t N, int C,
+                                           int64_t n_units, const EpiArgs &ea, int64_t blk,
+                                           int it, uint4 (&w)[U][R], uint32_t (&s)[U][R]) {
+    const uint8_t *wp[R];
+    const uint16_t *sp[R];
+    setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk, wp, sp);
+    const size_t c0 = (size_t)it * U * 16 * KS;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int64_t row = unit * R + r;
-                    if (row < N) {
-                        if constexpr (E == Epi::Residual) {
-                            act_store_f32<COH>(ea.y + row, act_load_f32<COH>(ea.y + row) + acc[r]);
-                        } else {
-                            act_store_f32<COH>(ea.y + row, acc[r]);
-                            if constexpr (E == Epi::QkvGather) {
-                                if (row >= ea.v_off) {
-                                    const int64_t v = row - ea.v_off;
-                                    const int64_t g = v / ea.hd, i = v % ea.hd;
-                                    const uint16_t h16 = f32_to_f16(acc[r]);
-                                    for (int q = 0; q < ea.group; ++q)
-                                        act_store_u16<COH>(
-                                            ea.out16 + (g * ea.group + q) * ea.hd + i, h16);
-                                }
-                            }
-                        }
-                    }
-                }
-            }
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            w[u][r] = wload16<NT>(wp[r] + (c0 + (size_t)u * 16 * KS) * 16);
+            s[u][r] = wload2<NT>(sp[r] + c0 + (size_t)u * 16 * KS);
         }
+    }
+}
+
+template <int R, int KS, int U>
+__device__ __forceinline__ void mul_batch(const uint4 (&w)[U][R], const uint32_t (&s)[U][R],
+                                          const uint4 *xs, int C, int it, float (&acc)[R],
+                                          uint32_t bias) {
+    const int cfirst = ((threadIdx.x >> 6) % KS) * 16 + (threadIdx.x & 15);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = cfirst + (it * U + u) * 16 * KS;
+        uint4 xq[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            xq[p] = xs[p * C + c];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = chunk_acc(w[u][r], xq, f16_to_f32((uint16_t)s[u][r]), acc[r], bias);
+    }
+}
+
+// Batches of this workgroup: row blocks blk0, blk0 + stride, ... (blk0 <
+// nblk), C / (16 KS U) batches each.
+template <int R, int KS, int U, Epi E>
+__device__ __forceinline__ int64_t pipe_batches(int C, int64_t n_units, int64_t blk0,
+                                                int64_t stride) {
+    const int64_t nblk = row_blocks<R, KS, E>(n_units);
+    return (nblk - blk0 + stride - 1) / stride * (C / (16 * KS * U));
+}
+
+// Issues batch q of this workgroup: row block blk0 + (q / niter) * stride,
+// batch q % niter within it.
+template <int R, int KS, int U, bool NT, Epi E>
+__device__ __forceinline__ void load_batch_q(const uint8_t *W, const uint16_t *S, int64_t N,
+                                             int C, int64_t n_units, const EpiArgs &ea,
+                                             int64_t blk0, int64_t stride, int niter, int64_t q,
+                                             uint4 (&w)[U][R], uint32_t (&s)[U][R]) {
+    load_batch<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0 + (q / niter) * stride,
+                                (int)(q % niter), w, s);
+}
+
+// Issues batches 0 and 1 of this workgroup into A and B (a workgroup with
+// a single batch loads it into both, so B is always in flight).
+template <int R, int KS, int U, bool NT, Epi E>
+__device__ __forceinline__ void prefetch_pipe(const uint8_t *W, const uint16_t *S, int64_t N,
+                                              int K, int64_t n_units, const EpiArgs &ea,
+                                              int64_t blk0, int64_t stride, uint4 (&wA)[U][R],
+                                              uint32_t (&sA)[U][R], uint4 (&wB)[U][R],
+                                              uint32_t (&sB)[U][R]) {
+    const int C = K >> 5;
+    const int niter = C / (16 * KS * U);
+    const int64_t Q = pipe_batches<R, KS, U, E>(C, n_units, blk0, stride);
+    load_batch_q<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0, stride, niter, 0, wA, sA);
+    load_batch_q<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0, stride, niter, Q > 1 ? 1 : 0,
+                                  wB, sB);
+}
+
+// Precondition: prefetch_pipe issued batches 0 and 1.  The main loop runs
+// while batches q .. q + 3 all exist, so its loads are unconditional and
+// the compiler's wait before each multiply covers only that buffer's
+// loads; the last one to three batches follow in a short tail.  Every
+// thread of the workgroup must call this.
+template <int R, int KS, int U, bool NT, Epi E>
+__device__ __forceinline__ void run_units_pipe(const uint8_t *W, const uint16_t *S, int64_t N,
+                                               int K, int64_t n_units, const EpiArgs &ea,
+                                               int64_t blk0, int64_t stride, const uint4 *xs,
+                                               float (*red)[kSlots][R], uint4 (&wA)[U][R],
+                                               uint32_t (&sA)[U][R], uint4 (&wB)[U][R],
+                                               uint32_t (&sB)[U][R], uint32_t bias) {
+    constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
+    const int C = K >> 5;
+    const int niter = C / (16 * KS * U);
+    const int64_t Q = pipe_batches<R, KS, U, E>(C, n_units, blk0, stride);
+    const int wave = threadIdx.x >> 6;
+    const int64_t my_unit = (wave / KS) * kSlots + ((threadIdx.x & 63) >> 4);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+    auto finish = [&](int64_t q) {
+        if ((int)(q % niter) == niter - 1) {
+            reduce_rows<R, KS>(acc, red);
+            store_unit<R, KS, E, false>(acc, (blk0 + (q / niter) * stride) * kUnitsPerBlock +
+                                                 my_unit,
+                                        N, n_units, ea);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = 0.0f;
+        }
+    };
+    int64_t q = 0;
+    for (; q + 3 < Q; q += 2) {
+        mul_batch<R, KS, U>(wA, sA, xs, C, (int)(q % niter), acc, bias);
+        finish(q);
+        load_batch_q<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0, stride, niter, q + 2, wA,
+                                      sA);
+        mul_batch<R, KS, U>(wB, sB, xs, C, (int)((q + 1) % niter), acc, bias);
+        finish(q + 1);
+        load_batch_q<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0, stride, niter, q + 3, wB,
+                                      sB);
+    }
+    // Q - q batches remain (1 to 3): q in A, q + 1 in B.
+    mul_batch<R, KS, U>(wA, sA, xs, C, (int)(q % niter), acc, bias);
+    finish(q);
+    if (q + 2 < Q)
+        load_batch_q<R, KS, U, NT, E>(W, S, N, C, n_units, ea, blk0, stride, niter, q + 2, wA,
+                                      sA);
+    if (q + 1 < Q) {
+        mul_batch<R, KS, U>(wB, sB, xs, C, (int)((q + 1) % niter), acc, bias);
+        finish(q + 1);
+    }
+    if (q + 2 < Q) {
+        mul_batch<R, KS, U>(wA, sA, xs, C, (int)((q + 2) % niter), acc, bias);
+        finish(q + 2);
     }
 }
 

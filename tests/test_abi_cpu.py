@@ -57,6 +57,12 @@ def test_gemv_argument_checks():
     assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 3, 1, 4, 1, None) == INVALID
     assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 8, 4, 1, None) == INVALID
     assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 64, 1, 1, 6, 1, None) == INVALID
+    # the pipelined loop (two chunks in flight per buffer) needs K % (1024 *
+    # k_split) == 0 and non-temporal loads; refused before anything is launched
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 1056, 1, 1, 2, 1, None) == UNSUPPORTED
+    assert "pipelined" in _err()
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 1024, 1, 2, 2, 1, None) == UNSUPPORTED
+    assert L.q4_gemv_tuned(buf, buf, buf, buf, 16, 1024, 1, 1, 2, 0, None) == UNSUPPORTED
 
 
 def test_gemm_argument_checks():

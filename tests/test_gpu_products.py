@@ -105,6 +105,28 @@ def test_gemv_every_launch_shape(rows_per_slot, k_split, chunks, nt):
                   f"gemv R={rows_per_slot} KS={k_split} U={chunks} NT={nt}")
 
 
+# Pipelined loop (chunks_in_flight == 2): the same chunks in the same order
+# as the single-buffer loop, so at equal rows_per_slot and k_split the
+# outputs are bitwise equal.  Shapes: a single batch per workgroup (64 x
+# 1024), two and three batches per row block with ragged row counts, and
+# enough row blocks that workgroups take several (even and odd counts).
+@pytest.mark.parametrize("N,K,rows_per_slot,k_split", [
+    (64, 1024, 1, 1), (333, 2048, 1, 1), (5001, 3072, 1, 1), (4133, 4096, 2, 2),
+    (40000, 2048, 1, 1), (24577, 4096, 2, 1), (9000, 8192, 2, 4), (12289, 8192, 4, 2)])
+def test_gemv_pipelined_loop_bitwise(N, K, rows_per_slot, k_split):
+    packed, scales = _mat(N, K, 81)
+    x = inputs.act_f16(K, 82, device=DEV)
+    y2 = torch.empty(N, dtype=torch.float32, device=DEV)
+    y4 = torch.empty_like(y2)
+    q4.q4_gemv_tuned(packed, scales, x, y2, rows_per_slot, k_split, 2, 1)
+    q4.q4_gemv_tuned(packed, scales, x, y4, rows_per_slot, k_split, 4, 1)
+    sync()
+    assert torch.equal(y2, y4), f"pipelined != single-buffer at {N}x{K}"
+    if N * K <= 24577 * 4096:
+        y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
+        assert_within(y2.cpu().numpy(), y_ref, mag, f"pipelined gemv {N}x{K}")
+
+
 def _f16(v):
     return torch.from_numpy(np.asarray(v, np.float64).astype(np.float16).view(np.int16))
 
