@@ -434,12 +434,16 @@ def base_result(metric, value, unit, steps, warmup, workload, extra=None):
 
 
 def bench_gemm(args, q4, inputs, torch):
-    """Small-batch product on the four 8B matrix shapes, B in {1, 4, 8, 16}:
-    distinct weight copies (> 512 MB per shape) launched round-robin inside a
-    captured graph; GB/s and effective TFLOP/s = 2NKB / t."""
+    """Small-batch product on the four 8B matrix shapes, B in {1, 2, 4, 8,
+    16}: distinct weight copies (> 512 MB per shape) launched round-robin
+    inside a captured graph; GB/s and effective TFLOP/s = 2NKB / t for the
+    library's choice of kernel, plus both paths side by side (vector-ALU
+    batch kernel where its columns fit, matrix-core kernel) to show the
+    crossover in B."""
     shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096),
               "down": (4096, 14336)}
     stream = torch.cuda.Stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     table = {}
     for name, (N, K) in shapes.items():
         wbytes = N * K // 2 + N * (K // 32) * 2
@@ -447,15 +451,30 @@ def bench_gemm(args, q4, inputs, torch):
         Ws = [(inputs.random_bytes(N, K, inputs.seed_of(3, i, 0), device="cuda"),
                inputs.scales(N, K, inputs.seed_of(3, i, 1), device="cuda"))
               for i in range(copies)]
-        for B in (1, 4, 8, 16):
+        for B in (1, 2, 4, 8, 16):
             X = inputs.act_f16((B, K), inputs.seed_of(3, 0, 2) + B, device="cuda")
             Y = torch.empty(B, N, dtype=torch.float32, device="cuda")
+            nbytes = wbytes + 2 * B * K + 4 * B * N
+
+            def rate(us):
+                return {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                        "TFLOP/s": round(2 * N * K * B / us / 1e6, 2)}
             launches = [(lambda st, p=p, sc=sc: q4.q4_gemm_smallbatch(p, sc, X, Y, stream=st))
                         for p, sc in Ws]
-            us = graph_avg_us(torch, launches, stream)
-            nbytes = wbytes + 2 * B * K + 4 * B * N
-            table[f"{name}_B{B}"] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
-                                     "TFLOP/s": round(2 * N * K * B / us / 1e6, 2)}
+            table[f"{name}_B{B}"] = rate(graph_avg_us(torch, launches, stream))
+            if B > 1:
+                # the two paths side by side (the matrix-core kernel at the
+                # library's own launch shape is q4_gemm_tuned's default here)
+                tiles, cap, rt = (N + 15) // 16, (2 if B <= 2 else (4 if B < 16 else 8)), 1
+                while rt * 2 <= cap and tiles // (rt * 2) >= cus * 3 // 4:
+                    rt *= 2
+                mf = [(lambda st, p=p, sc=sc: q4.q4_gemm_tuned(p, sc, X, Y, rt, 4, stream=st))
+                      for p, sc in Ws]
+                table[f"{name}_B{B}"]["mfma_us"] = round(graph_avg_us(torch, mf, stream), 3)
+                if B in (2, 4, 8) and B * K * 2 <= 65536:
+                    va = [(lambda st, p=p, sc=sc: q4.q4_gemm_valu(p, sc, X, Y, stream=st))
+                          for p, sc in Ws]
+                    table[f"{name}_B{B}"]["valu_us"] = round(graph_avg_us(torch, va, stream), 3)
         del Ws
         torch.cuda.empty_cache()
     top = table["gate_up_B16"]

@@ -127,7 +127,11 @@ q4_status q4_gemv(const uint8_t *packed, const uint16_t *scales,
 /* Y[b][n] = sum_k w[n][k] * X[b][k] for b < B, n < N.
  *   X_f16 u16[B][K] binary16 (each activation vector contiguous),
  *   16-byte aligned;  Y f32[B][N], 4-byte aligned;  1 <= B <= Q4_MAX_BATCH;
- *   other arguments as q4_gemv.  B == 1 runs the q4_gemv kernel. */
+ *   other arguments as q4_gemv.  B == 1 runs the q4_gemv kernel; 2 <= B <= 4
+ *   with B * K * 2 <= 65536 runs the vector-ALU batch kernel, whose every
+ *   column equals q4_gemv of that column bitwise; wider batches run the
+ *   matrix-core kernel, whose columns do not depend on B or on the other
+ *   columns (bitwise), and differ from q4_gemv within the product bound. */
 q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
                              const uint16_t *X_f16, float *Y, int64_t N,
                              int64_t K, int32_t B, hipStream_t stream);
@@ -154,6 +158,15 @@ q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
                         const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
                         int32_t B, int32_t row_tiles, int32_t waves,
                         hipStream_t stream);
+
+/* Measurement variant: the vector-ALU batch kernel for B in {2, 3, 4, 8}
+ * (8 only here: beyond four columns the library uses the matrix cores),
+ * arguments as q4_gemm_smallbatch; needs B * K * 2 <= 65536 (the columns
+ * are staged in LDS).  UNSUPPORTED otherwise; every column equals q4_gemv
+ * of that column bitwise. */
+q4_status q4_gemm_valu(const uint8_t *packed, const uint16_t *scales,
+                       const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
+                       int32_t B, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* Decode step (PipeLLM, "Layer 1: CUDA Graph Compilation")               */

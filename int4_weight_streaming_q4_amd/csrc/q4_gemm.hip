@@ -5,9 +5,10 @@
 // Devices, "Method", bullets "Computation optimization" and "Automatic
 // configuration" -- the 4-bit kernel serves batches below 16; a batch of B
 // activation vectors (e.g. a speculative-verify batch) reuses every unpacked
-// weight B times.  At B > 2 the dot2 path of the B = 1 kernel runs out of
-// VALU issue slots before HBM saturates, so the multiply-adds go to
-// v_mfma_f32_16x16x32_f16 and the VALU only unpacks.
+// weight B times.  Up to four columns (whose binary16 copies fit 64 KB of
+// LDS) the dot2 kernel of q4_gemv_batch.hip is faster; beyond that its dot
+// products take over the VALU, so the multiply-adds go to
+// v_mfma_f32_16x16x32_f16 here and the VALU only unpacks.
 //
 // One MFMA covers 16 weight rows x 32 k x 16 batch columns (B padded with
 // zeros).  Lane l supplies row (l % 16) / column (l % 16) and the 8-value k
@@ -314,6 +315,12 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
                            float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
                            bool accumulate) {
+    if (gemv_batch_fits(B, K)) {
+        EpiArgs ea{};
+        ea.y = Y;
+        return launch_gemv_batch(packed, scales, X16, N, K, B,
+                                 accumulate ? Epi::Residual : Epi::Store, ea, stream);
+    }
     return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, pick_row_tiles(N, B),
                                 kGemmWaves, stream, accumulate);
 }
@@ -321,6 +328,13 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
 q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
                                 const uint16_t *X16, uint16_t *M, int64_t npair, int64_t K,
                                 int32_t B, hipStream_t stream) {
+    if (gemv_batch_fits(B, K)) {
+        EpiArgs ea{};
+        ea.out16 = M;
+        ea.pair_off = npair;
+        return launch_gemv_batch(packed, scales, X16, 2 * npair, K, B, Epi::SiluPair, ea,
+                                 stream);
+    }
     const int RT = std::max(2, pick_row_tiles(2 * npair, B));
     GemmFn fn = pick_gemm<GEpi::SiluPair>(RT, kGemmWaves);
     if (!fn)
@@ -370,4 +384,20 @@ extern "C" q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales
                         "q4_gemm_tuned: X must be 16-byte and Y 4-byte aligned");
     return q4::launch_gemm_mfma_cfg(packed, scales, X_f16, Y, N, K, B, row_tiles, waves,
                                     stream, false);
+}
+
+extern "C" q4_status q4_gemm_valu(const uint8_t *packed, const uint16_t *scales,
+                                  const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
+                                  int32_t B, hipStream_t stream) {
+    Q4_CHECK(q4::check_matrix(packed, scales, N, K, "q4_gemm_valu"));
+    if (!X_f16 || !Y)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_gemm_valu: null X or Y");
+    if (!(B == 2 || B == 3 || B == 4 || B == 8))
+        return q4::fail(Q4_ERR_UNSUPPORTED, "q4_gemm_valu: B=%d not in {2, 3, 4, 8}", B);
+    if (!q4::aligned(X_f16, 16) || !q4::aligned(Y, 4))
+        return q4::fail(Q4_ERR_INVALID_ARG,
+                        "q4_gemm_valu: X must be 16-byte and Y 4-byte aligned");
+    q4::EpiArgs ea{};
+    ea.y = Y;
+    return q4::launch_gemv_batch(packed, scales, X_f16, N, K, B, q4::Epi::Store, ea, stream);
 }

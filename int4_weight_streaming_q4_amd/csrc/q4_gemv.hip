@@ -218,6 +218,12 @@ Cfg choose_config(Epi e, int64_t N, int64_t K) {
 
 } // namespace
 
+void gemv_shape(Epi e, int64_t N, int64_t K, int *R, int *KS) {
+    const Cfg c = choose_config(e, N, K);
+    *R = c.R;
+    *KS = c.KS;
+}
+
 q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const void *xin,
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
                           int KS, int U, bool NT, hipStream_t stream) {

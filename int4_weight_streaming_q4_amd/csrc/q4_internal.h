@@ -99,6 +99,21 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
                           int KS, int U, bool NT, hipStream_t stream);
 
+// Rows per slot and k split the batch-1 product uses for an N x K product
+// with epilogue e (N counts both halves of paired rows).
+void gemv_shape(Epi e, int64_t N, int64_t K, int *R, int *KS);
+
+// Small-batch product on the vector ALUs (q4_gemv_batch.hip): B binary16
+// columns X16[B][K] staged in LDS, each column computed exactly as the
+// batch-1 product computes it.  Store / Residual: ea.y = Y f32 [B][N];
+// SiluPair: ea.out16 = M binary16 [B][pair_off].  Kernels exist for B in
+// {2, 3, 4} (and 8 for Store); the staged columns must fit kBatchStageBytes.
+constexpr int kBatchStageBytes = 65536;
+bool gemv_batch_fits(int32_t B, int64_t K); // 2 <= B <= 4 and B * K * 2 <= kBatchStageBytes
+q4_status launch_gemv_batch(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
+                            int64_t N, int64_t K, int32_t B, Epi epi, const EpiArgs &ea,
+                            hipStream_t stream);
+
 // Small-batch product with matrix cores (2 <= B <= 16).
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales,
                            const uint16_t *X16, float *Y, int64_t N, int64_t K,

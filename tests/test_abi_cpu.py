@@ -75,6 +75,13 @@ def test_gemm_argument_checks():
     assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 3, 4, None) == UNSUPPORTED
     assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 8, 8, None) == UNSUPPORTED
     assert L.q4_gemm_tuned(buf, buf, buf, buf, 16, 64, 4, 4, 16, None) == UNSUPPORTED
+    # vector-ALU batch kernel: B in {2, 3, 4, 8}, columns within 64 KB of LDS
+    assert L.q4_gemm_valu(buf, buf, buf, buf, 16, 64, 5, None) == UNSUPPORTED
+    assert L.q4_gemm_valu(buf, buf, buf, buf, 16, 64, 1, None) == UNSUPPORTED
+    assert L.q4_gemm_valu(buf, buf, buf, buf, 16, 14336, 3, None) == UNSUPPORTED
+    assert "LDS" in _err()
+    assert L.q4_gemm_valu(buf, buf, 0, buf, 16, 64, 2, None) == INVALID
+    assert L.q4_gemm_valu(buf, buf, buf + 2, buf, 16, 64, 2, None) == INVALID
 
 
 def test_pack_argument_checks():

@@ -248,7 +248,7 @@ def test_gemm_b1_is_gemv_and_columns_match_gemv():
 
 
 @pytest.mark.parametrize("name", ["8b_qkv", "8b_o", "8b_gate_up", "8b_down"])
-@pytest.mark.parametrize("B", [4, 8, 16])
+@pytest.mark.parametrize("B", [2, 4, 8, 16])
 def test_gemm_workload_shapes_sampled_rows(name, B):
     N, K = WORKLOAD_SHAPES[name]
     packed, scales = _mat(N, K, inputs.seed_of(3, 0, list(WORKLOAD_SHAPES).index(name)))
@@ -262,16 +262,62 @@ def test_gemm_workload_shapes_sampled_rows(name, B):
         assert_within(Y[b][rows], y_ref, mag, f"{name} B={B} col {b}")
 
 
+def _valu_path(B, K):
+    """The library's rule: 2 <= B <= 4 columns whose binary16 copies fit 64 KB
+    of LDS run the vector-ALU batch kernel; wider batches the matrix cores."""
+    return 2 <= B <= 4 and B * K * 2 <= 65536
+
+
 @pytest.mark.parametrize("name", ["8b_gate_up", "8b_down"])
 def test_gemm_columns_independent_of_batch(name):
     """The launch shape may change with B, but no output's summation order
-    does: column b of a B-column product equals column b of the 16-column
-    product bitwise, whatever B and the other columns are."""
+    does within a path: on the matrix-core path column b of a B-column
+    product equals column b of the 16-column product bitwise, whatever B and
+    the other columns are; on the vector-ALU path every column equals the
+    single-column product (q4_gemv) bitwise."""
     N, K = WORKLOAD_SHAPES[name]
     packed, scales = _mat(N, K, inputs.seed_of(3, 1, list(WORKLOAD_SHAPES).index(name)))
     X = inputs.act_f16((16, K), inputs.seed_of(3, 1, 9), device=DEV)
     full = _gemm(packed, scales, X)
-    for B in (2, 3, 4, 9):
-        assert np.array_equal(_gemm(packed, scales, X[:B].contiguous()), full[:B]), B
+    gemv_cols = [_gemv(packed, scales, X[b].contiguous()) for b in range(4)]
+    for B in (2, 3, 4, 5, 9):
+        Y = _gemm(packed, scales, X[:B].contiguous())
+        if _valu_path(B, K):
+            for b in range(B):
+                assert np.array_equal(Y[b], gemv_cols[b]), (B, b)
+        else:
+            assert np.array_equal(Y, full[:B]), B
     perm = torch.tensor([5, 0, 3])
-    assert np.array_equal(_gemm(packed, scales, X[perm].contiguous()), full[perm.numpy()])
+    Yp = _gemm(packed, scales, X[perm].contiguous())
+    if _valu_path(3, K):
+        for i, b in enumerate(perm.tolist()):
+            assert np.array_equal(Yp[i], _gemv(packed, scales, X[b].contiguous()))
+    else:
+        assert np.array_equal(Yp, full[perm.numpy()])
+    perm9 = torch.tensor([8, 3, 0, 5, 1, 7, 2, 6, 4])
+    assert np.array_equal(_gemm(packed, scales, X[perm9].contiguous()), full[perm9.numpy()])
+
+
+# Vector-ALU batch kernel: each column is computed exactly as q4_gemv
+# computes it (same unpack, same k split and order), so bitwise equal.
+# Shapes: ragged rows and chunks (333 x 1056), the 8B QKV and gate+up
+# widths, K = 8192 and the 8B down K (two columns fit the 64 KB stage).
+@pytest.mark.parametrize("N,K", [(333, 1056), (4133, 4096), (6144, 4096), (2050, 8192),
+                                 (700, 14336)])
+@pytest.mark.parametrize("B", [2, 3, 4, 8])
+def test_gemm_valu_columns_are_gemv(N, K, B):
+    if B * K * 2 > 65536:
+        pytest.skip("the columns do not fit the 64 KB LDS stage (UNSUPPORTED by design)")
+    packed, scales = _mat(N, K, 91)
+    X = inputs.act_f16((B, K), 92, device=DEV)
+    Y = torch.empty(B, N, dtype=torch.float32, device=DEV)
+    q4.q4_gemm_valu(packed, scales, X, Y)
+    sync()
+    Yh = Y.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(Yh[b], _gemv(packed, scales, X[b].contiguous())), (N, K, B, b)
+    if B <= 4:
+        assert np.array_equal(_gemm(packed, scales, X), Yh)
+    Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
+    for b in (0, B - 1):
+        assert_within(Yh[b], Y_ref[b], M[b], f"valu gemm {N}x{K} B={B} col {b}")
