@@ -54,12 +54,18 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     // activation before issuing any weight load measured slower on every
     // decode shape.)
     XStage st;
+    float hv[R];
     stage_issue<P, false>(xin, K, st);
-    prefetch_block<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, w, s, wp, sp);
+    if constexpr (E == Epi::Residual)
+        load_residual<R, KS, E>(ea, N, blockIdx.x, hv);
+    // (first batch issued unconditionally after a binary16 activation, see
+    // stage_issue)
+    prefetch_block<R, KS, U, NT, E, P == Pro::RmsNorm>(W, S, N, K, n_units, ea, blockIdx.x, w, s,
+                                                       wp, sp);
     stage_finish<P, false>(xin, xs, K, ea, wsum, st);
     __syncthreads();
     run_units<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, gridDim.x, xs, red, w, s,
-                               wp, sp, bias);
+                               wp, sp, bias, hv);
 }
 
 // The same product with the software-pipelined loop: two register buffers
@@ -89,18 +95,21 @@ gemv_pipe_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 using KernelFn = void (*)(const uint8_t *, const uint16_t *, const void *, int64_t, int,
                           int64_t, EpiArgs);
 
-// Launch shape of one product kernel.  U == 2 selects the software-pipelined
-// loop (two buffers of two chunks per row, non-temporal loads only); U == 4
-// or 8 the single-buffer loop with U chunks in flight.
+// Launch shape of one product kernel: U chunks of each row in flight per
+// lane (2, 4 or 8); pipe selects the software-pipelined loop (two buffers of
+// two chunks, non-temporal loads only) instead of the single-buffer loop.
 struct Cfg {
     int R, KS, U;
     bool NT;
+    bool pipe;
 };
 
 template <Epi E, Pro P, int R, int KS>
 KernelFn pick_ut(const Cfg &c) {
+    if (c.pipe)
+        return c.U == 2 && c.NT ? gemv_pipe_kernel<R, KS, 2, true, E, P> : nullptr;
     if (c.U == 2)
-        return c.NT ? gemv_pipe_kernel<R, KS, 2, true, E, P> : nullptr;
+        return c.NT ? gemv_kernel<R, KS, 2, true, E, P> : gemv_kernel<R, KS, 2, false, E, P>;
     if (c.U == 4)
         return c.NT ? gemv_kernel<R, KS, 4, true, E, P> : gemv_kernel<R, KS, 4, false, E, P>;
     if (c.U == 8)
@@ -178,15 +187,15 @@ int resident_blocks(KernelFn fn, size_t lds) {
 //   * otherwise two rows per 16-lane row with a 4-way k split (best or
 //     within 3% on the largest products, 57344 x 8192).
 // The epilogue variant (paired rows) needs two rows per slot.
-Cfg choose_config(Epi e, int64_t N, int64_t K) {
+Cfg choose_config(Epi e, Pro p, int64_t N, int64_t K) {
     const int64_t C = K / 32;
-    Cfg c{2, 4, 4, true};
+    Cfg c{2, 4, 4, true, false};
     // The paired gate+up rows at K >= 8192 (57344 x 8192) stream faster with
     // the pipelined loop and a 2-way split (44.1-44.5 vs 46.6-47.5 us); the
     // other decode shapes gain nothing from it (their time goes to the
     // launch's start and tail, not to the steady stream).
     if (e == Epi::SiluPair && K >= 8192 && C % 64 == 0)
-        return Cfg{2, 2, 2, true};
+        return Cfg{2, 2, 2, true, true};
     if (K < 8192) {
         if (e == Epi::SiluPair) {
             c.KS = 2;
@@ -213,26 +222,34 @@ Cfg choose_config(Epi e, int64_t N, int64_t K) {
     // decode epilogues.
     if (c.KS == 1 && c.R == 1 && e != Epi::Store)
         c.R = 2;
+    // After a binary16 activation the first batch is issued unconditionally,
+    // so no more chunks in flight than a lane has per row (K = 4096 with a
+    // 4-way split leaves two per lane); the RMSNorm prologue skips the extra
+    // loads and keeps the measured defaults (QKV 6.9 us with eight vs 7.1-7.5
+    // with two).
+    const int64_t nl = (C + 16 * c.KS - 1) / (16 * c.KS);
+    while (p == Pro::F16 && c.U > 2 && c.U / 2 >= nl)
+        c.U /= 2;
     return c;
 }
 
 } // namespace
 
 void gemv_shape(Epi e, int64_t N, int64_t K, int *R, int *KS) {
-    const Cfg c = choose_config(e, N, K);
+    const Cfg c = choose_config(e, Pro::F16, N, K);
     *R = c.R;
     *KS = c.KS;
 }
 
 q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const void *xin,
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
-                          int KS, int U, bool NT, hipStream_t stream) {
-    Cfg cfg{R, KS, U, NT};
+                          int KS, int U, bool NT, bool pipe, hipStream_t stream) {
+    Cfg cfg{R, KS, U, NT, pipe};
     KernelFn fn = pick_kernel(epi, pro, cfg);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED,
                     "gemv: no kernel for rows_per_slot=%d k_split=%d chunks=%d", R, KS, U);
-    if (U == 2 && (K / 32) % (32 * KS) != 0)
+    if (pipe && (K / 32) % (32 * KS) != 0)
         return fail(Q4_ERR_UNSUPPORTED,
                     "gemv: the pipelined loop needs K %% (1024 * k_split) == 0 (K=%lld)",
                     (long long)K);
@@ -256,8 +273,9 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
 
 q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
                       int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream) {
-    const Cfg c = choose_config(epi, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K);
-    return launch_gemv_cfg(packed, scales, xin, pro, N, K, epi, ea, c.R, c.KS, c.U, c.NT, stream);
+    const Cfg c = choose_config(epi, pro, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K);
+    return launch_gemv_cfg(packed, scales, xin, pro, N, K, epi, ea, c.R, c.KS, c.U, c.NT, c.pipe,
+                           stream);
 }
 
 } // namespace q4
@@ -295,7 +313,8 @@ extern "C" q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales
                         "chunks_in_flight 2, 4 or 8");
     q4::EpiArgs ea{};
     ea.y = y;
+    // chunks_in_flight == 2 selects the software-pipelined loop
     return q4::launch_gemv_cfg(packed, scales, x_f16, q4::Pro::F16, N, K, q4::Epi::Store, ea,
                                rows_per_slot, k_split, chunks_in_flight, nontemporal != 0,
-                               stream);
+                               chunks_in_flight == 2, stream);
 }

@@ -78,13 +78,15 @@ gemv_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 
     // Activation loads first (up to kXR per thread in registers), then the
     // first weight batch, then the LDS writes.
+    // (unconditional loads, indices past the end wrapping around, so the
+    // wait before the LDS writes covers only these loads)
     uint4 xr[kXR];
 #pragma unroll
     for (int j = 0; j < kXR; ++j) {
         const int i = threadIdx.x + j * kThreads;
-        xr[j] = i < B * nb ? gload16(X16 + 8 * (size_t)i) : uint4{0u, 0u, 0u, 0u};
+        xr[j] = gload16(X16 + 8 * (size_t)(i < B * nb ? i : i % (B * nb)));
     }
-    prefetch_block<R, KS, U, true, E>(W, S, N, K, n_units, ea, blockIdx.x, w, s, wp, sp);
+    prefetch_block<R, KS, U, true, E, false>(W, S, N, K, n_units, ea, blockIdx.x, w, s, wp, sp);
     auto put = [&](int i, uint4 v) {
         const int b = i / nb, k8 = i - b * nb;
         xs[b * xcol + (k8 & 3) * C + (k8 >> 2)] = permute8(v);
@@ -209,25 +211,27 @@ gemv_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 using BatchFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, int64_t, int,
                          int64_t, EpiArgs);
 
-template <int R, int KS, Epi E>
+template <int R, int KS, int U, Epi E>
 BatchFn pick_b(int B) {
     switch (B) {
-    case 2: return gemv_batch_kernel<R, KS, 4, 2, E>;
-    case 3: return gemv_batch_kernel<R, KS, 4, 3, E>;
-    case 4: return gemv_batch_kernel<R, KS, 4, 4, E>;
+    case 2: return gemv_batch_kernel<R, KS, U, 2, E>;
+    case 3: return gemv_batch_kernel<R, KS, U, 3, E>;
+    case 4: return gemv_batch_kernel<R, KS, U, 4, E>;
     case 8:
         if constexpr (E == Epi::Store)
-            return gemv_batch_kernel<R, KS, 4, 8, E>;
+            return gemv_batch_kernel<R, KS, U, 8, E>;
         return nullptr;
     default: return nullptr;
     }
 }
 
+// Four chunks in flight per lane, or two when a lane has no more per row
+// (the loads are unconditional, so extra ones would be wasted).
 template <Epi E>
-BatchFn pick_batch(int R, int KS, int B) {
+BatchFn pick_batch(int R, int KS, int B, int nl) {
 #define Q4_PICK(r, ks)                                                           \
     if (R == r && KS == ks)                                                      \
-        return pick_b<r, ks, E>(B);
+        return nl <= 2 ? pick_b<r, ks, 2, E>(B) : pick_b<r, ks, 4, E>(B);
     if constexpr (E == Epi::SiluPair) {
         Q4_PICK(2, 1) Q4_PICK(2, 2) Q4_PICK(2, 4)
     } else {
@@ -262,9 +266,10 @@ q4_status launch_gemv_batch(const uint8_t *packed, const uint16_t *scales, const
     // column's summation order is the batch-1 product's.
     int R = 0, KS = 0;
     gemv_shape(epi, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K, &R, &KS);
-    BatchFn fn = epi == Epi::SiluPair  ? pick_batch<Epi::SiluPair>(R, KS, B)
-                 : epi == Epi::Residual ? pick_batch<Epi::Residual>(R, KS, B)
-                 : epi == Epi::Store    ? pick_batch<Epi::Store>(R, KS, B)
+    const int nl = (int)((K / 32 + 16 * KS - 1) / (16 * KS));
+    BatchFn fn = epi == Epi::SiluPair  ? pick_batch<Epi::SiluPair>(R, KS, B, nl)
+                 : epi == Epi::Residual ? pick_batch<Epi::Residual>(R, KS, B, nl)
+                 : epi == Epi::Store    ? pick_batch<Epi::Store>(R, KS, B, nl)
                                         : nullptr;
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemv batch: no kernel for B=%d R=%d KS=%d", B, R, KS);

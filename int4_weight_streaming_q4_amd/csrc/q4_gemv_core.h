@@ -262,6 +262,15 @@ struct XStage {
     uint4 v[kXR];
 };
 
+// Every thread issues all kXR loads (indices past the end wrap around to
+// blocks other threads load anyway -- one common address for all of them
+// would queue the whole grid on one cache channel; stage_finish ignores
+// them): a load under a per-lane branch would make the compiler wait for
+// every load in flight, the weight prefetch included, before the first use
+// of the activation.
+// The RMSNorm prologue keeps the loads past the end skipped: measured on the
+// 8B shapes, issuing them all made its products slower (gate+up 15.05 vs
+// 14.55 us, QKV 7.06 vs 6.88), while the binary16 prologue gains.
 template <Pro P, bool COH>
 __device__ __forceinline__ void stage_issue(const void *xin, int K, XStage &st) {
     if constexpr (P == Pro::F16) {
@@ -270,7 +279,7 @@ __device__ __forceinline__ void stage_issue(const void *xin, int K, XStage &st) 
 #pragma unroll
         for (int j = 0; j < kXR; ++j) {
             const int b = threadIdx.x + j * kThreads;
-            st.v[j] = b < nb ? act_load16<COH>(x16 + 8 * (size_t)b) : uint4{0u, 0u, 0u, 0u};
+            st.v[j] = act_load16<COH>(x16 + 8 * (size_t)(b < nb ? b : b % nb));
         }
     } else {
         const float *h = static_cast<const float *>(xin);
@@ -323,11 +332,13 @@ __device__ __forceinline__ void stage_finish(const void *xin, uint4 *xs, int K, 
         float ss = 0.0f;
 #pragma unroll
         for (int j = 0; j < kKeep; ++j) {
-            float f[8];
-            unpack_f32x8(st.v[2 * j], st.v[2 * j + 1], f);
+            if (threadIdx.x + j * kThreads < nb8) {
+                float f[8];
+                unpack_f32x8(st.v[2 * j], st.v[2 * j + 1], f);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                ss = fmaf(f[i], f[i], ss);
+                for (int i = 0; i < 8; ++i)
+                    ss = fmaf(f[i], f[i], ss);
+            }
         }
         for (int b = threadIdx.x + kKeep * kThreads; b < nb8; b += kThreads) {
             float f[8];
@@ -397,21 +408,30 @@ __device__ __forceinline__ uint16_t wload2(const uint16_t *p) {
     }
 }
 
-// Loads of one group of U chunks of R rows; chunks past this lane's count
-// are not loaded (their registers are zeroed and never used).
-template <int U, int R, bool NT>
+// Loads of one group of U chunks of R rows.  ALL: every load is issued,
+// chunks past this lane's count loading the lane's last chunk again (or its
+// row's first chunk when it has none) and never used -- for the first batch
+// of a product, so that the wait before the activation staging covers only
+// the activation loads (a load behind a per-lane branch makes the next wait
+// cover every load in flight).  Otherwise chunks past the count are skipped
+// (in the steady loop, issuing them all lets the compiler reuse in-flight
+// loads' address registers as destinations and wait inside the issue
+// sequence).
+template <int U, int R, bool NT, bool ALL = false>
 __device__ __forceinline__ void load_chunks(uint4 (&w)[U][R], uint16_t (&s)[U][R],
                                             const uint8_t *const (&wp)[R],
                                             const uint16_t *const (&sp)[R], int first, int nl,
                                             int cstep) {
+    const int last = nl > 0 ? nl - 1 : 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const bool ok = first + u < nl;
+        const int c = ok ? first + u : last;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (ok) {
-                w[u][r] = wload16<NT>(wp[r] + (size_t)(first + u) * cstep * 16);
-                s[u][r] = wload2<NT>(sp[r] + (size_t)(first + u) * cstep);
+            if (ALL || ok) {
+                w[u][r] = wload16<NT>(wp[r] + (size_t)c * cstep * 16);
+                s[u][r] = wload2<NT>(sp[r] + (size_t)c * cstep);
             } else {
                 w[u][r] = uint4{0u, 0u, 0u, 0u};
                 s[u][r] = 0;
@@ -426,7 +446,10 @@ struct Geometry {
     static constexpr int kUnitsPerBlock = kRowGroups * kSlots;
 };
 
-// Points wp/sp at this lane's first chunk of the R rows of row block `blk`.
+// Points wp/sp at this lane's first chunk of the R rows of row block `blk`
+// (units past the end use the last unit; a lane with no chunk in its row,
+// cfirst >= C, points at the row's last chunk, which it loads but never
+// uses, so every address stays inside the matrix).
 template <int R, int KS, Epi E>
 __device__ __forceinline__ void setup_rows(const uint8_t *W, const uint16_t *S, int64_t N, int C,
                                            int64_t n_units, const EpiArgs &ea, int64_t blk,
@@ -436,7 +459,8 @@ __device__ __forceinline__ void setup_rows(const uint8_t *W, const uint16_t *S, 
     const int wave = threadIdx.x >> 6;
     const int slot = lane >> 4;
     const int rgroup = wave / KS;
-    const int cfirst = (wave % KS) * 16 + (lane & 15);
+    const int cf = (wave % KS) * 16 + (lane & 15);
+    const int cfirst = cf < C ? cf : C - 1;
     const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
     const int64_t lunit = unit < n_units ? unit : n_units - 1;
     const size_t row_bytes = (size_t)(C * 16);
@@ -463,17 +487,22 @@ __device__ __forceinline__ int lane_chunks(int C) {
     return cfirst < C ? (C - cfirst + cstep - 1) / cstep : 0;
 }
 
-// Issues the first chunk loads of row block `blk` (if it exists).
-template <int R, int KS, int U, bool NT, Epi E>
+// Issues the first chunk loads of row block `blk`.  GUARD: skip them when
+// the block does not exist (the persistent kernels prefetch a product whose
+// row blocks may be fewer than the workgroups); the per-product kernels
+// launch at most one workgroup per row block and issue them unconditionally
+// (a uniform branch around the loads would still make the compiler's next
+// wait cover them all).
+template <int R, int KS, int U, bool NT, Epi E, bool GUARD = true>
 __device__ __forceinline__ void prefetch_block(const uint8_t *W, const uint16_t *S, int64_t N,
                                                int K, int64_t n_units, const EpiArgs &ea,
                                                int64_t blk, uint4 (&w)[U][R],
                                                uint16_t (&s)[U][R], const uint8_t *(&wp)[R],
                                                const uint16_t *(&sp)[R]) {
     const int C = K >> 5;
-    if (blk < row_blocks<R, KS, E>(n_units)) {
+    if (!GUARD || blk < row_blocks<R, KS, E>(n_units)) {
         setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk, wp, sp);
-        load_chunks<U, R, NT>(w, s, wp, sp, 0, lane_chunks<KS>(C), 16 * KS);
+        load_chunks<U, R, NT, !GUARD>(w, s, wp, sp, 0, lane_chunks<KS>(C), 16 * KS);
     }
 }
 
@@ -550,17 +579,54 @@ __device__ __forceinline__ void store_unit(const float (&acc)[R], int64_t unit, 
     }
 }
 
+// Residual epilogue with the rows' old values already loaded (hv): the same
+// sum as store_unit's h[row] + acc.
+template <int R, int KS>
+__device__ __forceinline__ void store_residual(const float (&acc)[R], const float (&hv)[R],
+                                               int64_t unit, int64_t N, int64_t n_units,
+                                               const EpiArgs &ea) {
+    const int lane = threadIdx.x & 63;
+    const int kpart = (threadIdx.x >> 6) % KS;
+    if (kpart == 0 && (lane & 15) == 0 && unit < n_units) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = unit * R + r;
+            if (row < N)
+                ea.y[row] = hv[r] + acc[r];
+        }
+    }
+}
+
+// Loads the residual values of this lane's rows in row block blk (rows past
+// the end read row N - 1; every lane loads, so no load sits behind a
+// branch).
+template <int R, int KS, Epi E>
+__device__ __forceinline__ void load_residual(const EpiArgs &ea, int64_t N, int64_t blk,
+                                              float (&hv)[R]) {
+    constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
+    const int wave = threadIdx.x >> 6;
+    const int64_t unit = blk * kUnitsPerBlock + (wave / KS) * kSlots + ((threadIdx.x & 63) >> 4);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = unit * R + r;
+        hv[r] = gload(ea.y + (row < N ? row : N - 1));
+    }
+}
+
 // Processes row blocks blk, blk + stride, ... of one product with the
 // activation already staged in LDS.  Precondition: the first chunk loads of
-// `blk` are in w/s (prefetch_block).  Every thread of the workgroup must
-// call this (the k-split reduction synchronises the workgroup).
+// `blk` are in w/s (prefetch_block), and, for the Residual epilogue of the
+// per-product kernels (COH false), hv holds the old values of blk's rows
+// (load_residual).  Every thread of the workgroup must call this (the
+// k-split reduction synchronises the workgroup).
 template <int R, int KS, int U, bool NT, Epi E, bool COH = false>
 __device__ __forceinline__ void run_units(const uint8_t *W, const uint16_t *S, int64_t N, int K,
                                           int64_t n_units, const EpiArgs &ea, int64_t blk,
                                           int64_t stride, const uint4 *xs,
                                           float (*red)[kSlots][R], uint4 (&w)[U][R],
                                           uint16_t (&s)[U][R], const uint8_t *(&wp)[R],
-                                          const uint16_t *(&sp)[R], uint32_t bias) {
+                                          const uint16_t *(&sp)[R], uint32_t bias,
+                                          float (&hv)[R]) {
     constexpr int kUnitsPerBlock = Geometry<E, R, KS>::kUnitsPerBlock;
     const int C = K >> 5;
     const int lane = threadIdx.x & 63;
@@ -574,6 +640,12 @@ __device__ __forceinline__ void run_units(const uint8_t *W, const uint16_t *S, i
     const int cfirst = kpart * 16 + sl;
     const int nl = lane_chunks<KS>(C);
     const int niter = (nl + U - 1) / U;
+    // Residual epilogue, one kernel per product: the rows' old values are
+    // loaded ahead of the row block's weights instead of after the multiply
+    // (a kernel starts with cold caches, so that read would cost a full
+    // memory round trip at the end of every block).  The persistent kernels
+    // keep the late read.
+    constexpr bool kEarlyRes = E == Epi::Residual && !COH;
 
     for (; blk < nblk; blk += stride) {
         const int64_t unit = blk * kUnitsPerBlock + rgroup * kSlots + slot;
@@ -602,11 +674,20 @@ __device__ __forceinline__ void run_units(const uint8_t *W, const uint16_t *S, i
         reduce_rows<R, KS>(acc, red);
 
         // The next row block's first loads go out before this epilogue.
+        float hcur[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            hcur[r] = hv[r];
         if (blk + stride < nblk) {
+            if constexpr (kEarlyRes)
+                load_residual<R, KS, E>(ea, N, blk + stride, hv);
             setup_rows<R, KS, E>(W, S, N, C, n_units, ea, blk + stride, wp, sp);
             load_chunks<U, R, NT>(w, s, wp, sp, 0, nl, cstep);
         }
-        store_unit<R, KS, E, COH>(acc, unit, N, n_units, ea);
+        if constexpr (kEarlyRes)
+            store_residual<R, KS>(acc, hcur, unit, N, n_units, ea);
+        else
+            store_unit<R, KS, E, COH>(acc, unit, N, n_units, ea);
     }
 }
 

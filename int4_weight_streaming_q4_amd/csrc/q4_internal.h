@@ -92,12 +92,13 @@ struct EpiArgs {
 // given by `xin` (binary16 u16[K] for Pro::F16, the fp32 residual f32[K] for
 // Pro::RmsNorm) with the chosen epilogue.  launch_gemv picks the launch
 // shape; launch_gemv_cfg takes it (R rows per 16-lane row, KS-way k split, U
-// chunks per row in flight, NT non-temporal weight loads).
+// chunks per row in flight, NT non-temporal weight loads, pipe the
+// software-pipelined loop, which needs U == 2 and NT).
 q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
                       int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream);
 q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const void *xin,
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
-                          int KS, int U, bool NT, hipStream_t stream);
+                          int KS, int U, bool NT, bool pipe, hipStream_t stream);
 
 // Rows per slot and k split the batch-1 product uses for an N x K product
 // with epilogue e (N counts both halves of paired rows).

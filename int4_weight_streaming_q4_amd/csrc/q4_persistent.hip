@@ -112,6 +112,7 @@ __global__ void __launch_bounds__(kThreads) decode_persistent(PersistArgs a) {
     const uint16_t *sp[PR];
     uint4 w[PU][PR];
     uint16_t s[PU][PR];
+    float hvd[PR] = {}; // residual values: read late on this path
     const int64_t b0 = blockIdx.x, G = gridDim.x;
     // Barrier epochs of this launch: the parity bit alternates between
     // launches (workgroup 0 flips it at its end, after every workgroup has
@@ -146,7 +147,7 @@ __global__ void __launch_bounds__(kThreads) decode_persistent(PersistArgs a) {
             stage_activation<Pro::RmsNorm, true>(a.h, xs, p.K, e_qkv, wsum);
             __syncthreads();
             run_units<PR, PKS, PU, PNT, Epi::QkvGather, true>(p.W, p.S, p.N, p.K, p.n_units, e_qkv, b0,
-                                                         G, xs, red, w, s, wp, sp, bias);
+                                                         G, xs, red, w, s, wp, sp, bias, hvd);
             const Phase q = ph_o(L);
             prefetch_block<PR, PKS, PU, PNT, Epi::Residual>(q.W, q.S, q.N, q.K, q.n_units, e_o,
                                                             b0, w, s, wp, sp);
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(kThreads) decode_persistent(PersistArgs a) {
             stage_activation<Pro::F16, true>(a.oin, xs, p.K, e_o, wsum);
             __syncthreads();
             run_units<PR, PKS, PU, PNT, Epi::Residual, true>(p.W, p.S, p.N, p.K, p.n_units, e_o, b0, G,
-                                                        xs, red, w, s, wp, sp, bias);
+                                                        xs, red, w, s, wp, sp, bias, hvd);
             const Phase q = ph_gu(L);
             prefetch_block<PR, PKS, PU, PNT, Epi::SiluPair>(q.W, q.S, q.N, q.K, q.n_units, e_gu,
                                                             b0, w, s, wp, sp);
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(kThreads) decode_persistent(PersistArgs a) {
             stage_activation<Pro::RmsNorm, true>(a.h, xs, p.K, e_gu, wsum);
             __syncthreads();
             run_units<PR, PKS, PU, PNT, Epi::SiluPair, true>(p.W, p.S, p.N, p.K, p.n_units, e_gu, b0, G,
-                                                        xs, red, w, s, wp, sp, bias);
+                                                        xs, red, w, s, wp, sp, bias, hvd);
             const Phase q = ph_down(L);
             prefetch_block<PR, PKS, PU, PNT, Epi::Residual>(q.W, q.S, q.N, q.K, q.n_units,
                                                             e_down, b0, w, s, wp, sp);
@@ -179,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) decode_persistent(PersistArgs a) {
             stage_activation<Pro::F16, true>(a.mlp, xs, p.K, e_down, wsum);
             __syncthreads();
             run_units<PR, PKS, PU, PNT, Epi::Residual, true>(p.W, p.S, p.N, p.K, p.n_units, e_down, b0,
-                                                        G, xs, red, w, s, wp, sp, bias);
+                                                        G, xs, red, w, s, wp, sp, bias, hvd);
             if (l + 1 < a.n_layers) {
                 const Phase q = ph_qkv(a.layers[l + 1]);
                 prefetch_block<PR, PKS, PU, PNT, Epi::QkvGather>(q.W, q.S, q.N, q.K, q.n_units,
