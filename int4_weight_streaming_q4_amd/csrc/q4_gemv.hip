@@ -53,15 +53,17 @@ gemv_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     // the prologue while the weights are in flight.  (Waiting for the
     // activation before issuing any weight load measured slower on every
     // decode shape.)
+    // The paired gate+up rows after an RMSNorm stage behind their first
+    // weight batch (measured faster, see stage_issue); every other variant
+    // issues that batch unconditionally and stages as soon as the activation
+    // has landed.
+    constexpr bool kEarly = !(E == Epi::SiluPair && P == Pro::RmsNorm);
     XStage st;
     float hv[R];
-    stage_issue<P, false>(xin, K, st);
+    stage_issue<P, false, kEarly>(xin, K, st);
     if constexpr (E == Epi::Residual)
         load_residual<R, KS, E>(ea, N, blockIdx.x, hv);
-    // (first batch issued unconditionally after a binary16 activation, see
-    // stage_issue)
-    prefetch_block<R, KS, U, NT, E, P == Pro::RmsNorm>(W, S, N, K, n_units, ea, blockIdx.x, w, s,
-                                                       wp, sp);
+    prefetch_block<R, KS, U, NT, E, !kEarly>(W, S, N, K, n_units, ea, blockIdx.x, w, s, wp, sp);
     stage_finish<P, false>(xin, xs, K, ea, wsum, st);
     __syncthreads();
     run_units<R, KS, U, NT, E>(W, S, N, K, n_units, ea, blockIdx.x, gridDim.x, xs, red, w, s,
@@ -228,7 +230,7 @@ Cfg choose_config(Epi e, Pro p, int64_t N, int64_t K) {
     // loads and keeps the measured defaults (QKV 6.9 us with eight vs 7.1-7.5
     // with two).
     const int64_t nl = (C + 16 * c.KS - 1) / (16 * c.KS);
-    while (p == Pro::F16 && c.U > 2 && c.U / 2 >= nl)
+    while (c.U > 2 && c.U / 2 >= nl)
         c.U /= 2;
     return c;
 }

@@ -268,10 +268,12 @@ struct XStage {
 // them): a load under a per-lane branch would make the compiler wait for
 // every load in flight, the weight prefetch included, before the first use
 // of the activation.
-// The RMSNorm prologue keeps the loads past the end skipped: measured on the
-// 8B shapes, issuing them all made its products slower (gate+up 15.05 vs
-// 14.55 us, QKV 7.06 vs 6.88), while the binary16 prologue gains.
-template <Pro P, bool COH>
+// The RMSNorm prologue (UNIFORM) skips the rows of blocks past the end on a
+// workgroup-uniform test instead (issuing them all made its products slower:
+// gate+up 15.05 vs 14.55 us, QKV 7.06 vs 6.88); without UNIFORM it skips
+// them per lane, so the staging waits for the first weight batch as well,
+// which measured faster for the paired gate+up rows (14.47 vs 15.45 us).
+template <Pro P, bool COH, bool UNIFORM = true>
 __device__ __forceinline__ void stage_issue(const void *xin, int K, XStage &st) {
     if constexpr (P == Pro::F16) {
         const uint16_t *x16 = static_cast<const uint16_t *>(xin);
@@ -286,10 +288,14 @@ __device__ __forceinline__ void stage_issue(const void *xin, int K, XStage &st) 
         const int nb8 = K >> 3;
 #pragma unroll
         for (int j = 0; j < kXR / 2; ++j) {
+            // UNIFORM: a workgroup-uniform bound (the whole group loads block
+            // row j or none of it; the last threads of a partial row wrap
+            // around), so no load sits behind a per-lane branch
             const int b = threadIdx.x + j * kThreads;
-            if (b < nb8) {
-                st.v[2 * j] = act_load16<COH>(h + 8 * (size_t)b);
-                st.v[2 * j + 1] = act_load16<COH>(h + 8 * (size_t)b + 4);
+            if (UNIFORM ? j * kThreads < nb8 : b < nb8) {
+                const size_t o = 8 * (size_t)(b < nb8 ? b : b % nb8);
+                st.v[2 * j] = act_load16<COH>(h + o);
+                st.v[2 * j + 1] = act_load16<COH>(h + o + 4);
             } else {
                 st.v[2 * j] = st.v[2 * j + 1] = uint4{0u, 0u, 0u, 0u};
             }
