@@ -177,10 +177,9 @@ int resident_blocks(KernelFn fn, size_t lds) {
 // Default launch shape, from back-to-back launch timings of every shape on
 // the decode matrices with their real prologues and epilogues (non-temporal
 // loads won or tied everywhere):
-//   * K = 4096: one row per 16-lane row, 4-way k split, 8 chunks in flight
-//     (6144 x 4096: 6.9 vs 7.3 us for two rows; 4096 x 4096: 5.45 vs 5.67);
-//     the paired gate+up rows prefer a 2-way split (28672 x 4096: 14.5-14.8
-//     vs 15.0-15.5 us);
+//   * K = 4096: one row per 16-lane row with a 2-way k split (see below);
+//     the paired gate+up rows also prefer a 2-way split (28672 x 4096:
+//     14.5-14.8 vs 15.0-15.5 us);
 //   * K = 8192 with 8192..12288 rows prefers one row per 16-lane row
 //     (10240 x 8192: 12.2 vs 14.5 us; 8192 x 8192 with 8 chunks in flight:
 //     11.0 vs 12.6 us);
