@@ -112,7 +112,8 @@ def test_gemv_every_launch_shape(rows_per_slot, k_split, chunks, nt):
 # enough row blocks that workgroups take several (even and odd counts).
 @pytest.mark.parametrize("N,K,rows_per_slot,k_split", [
     (64, 1024, 1, 1), (333, 2048, 1, 1), (5001, 3072, 1, 1), (4133, 4096, 2, 2),
-    (40000, 2048, 1, 1), (24577, 4096, 2, 1), (9000, 8192, 2, 4), (12289, 8192, 4, 2)])
+    (40000, 2048, 1, 1), (24577, 4096, 2, 1), (9000, 8192, 2, 4), (12289, 8192, 4, 2),
+    (200, 32768, 2, 2)])
 def test_gemv_pipelined_loop_bitwise(N, K, rows_per_slot, k_split):
     packed, scales = _mat(N, K, 81)
     x = inputs.act_f16(K, 82, device=DEV)
@@ -210,7 +211,7 @@ def _gemm(packed, scales, X, tuned=None):
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 16])
-@pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (65, 2080), (300, 1024)])
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (65, 2080), (300, 1024), (33, 32768)])
 def test_gemm_small_shapes(B, N, K):
     packed, scales = _mat(N, K, 300 + B + N + K)
     X = inputs.act_f16((B, K), 400 + B + K, device=DEV)
