@@ -115,14 +115,34 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
     const size_t gbase = (size_t)g * max_ctx + c0;
 
+    // The operands of this thread's first query rotation are loaded first,
+    // then the cache tile, so the rotation waits only for its own operands
+    // while the tile is in flight.  Every one of these loads is issued
+    // unconditionally (indices clamped into valid rows and elements): a
+    // load behind a per-lane branch makes the compiler's next wait cover
+    // every load in flight, which had the value tile wait for the key tile
+    // and the rotation for both.  Rows past the context (r >= n) load row
+    // n - 1, a written row: their scores are masked out of the softmax and
+    // their weights are 0, so the results are those of zero rows.
+    const float2 *rp = rope + (size_t)pos * HALF;
+    const int i0 = t < QH * HALF ? t : QH * HALF - 1;
+    const float *q0 = qkv + (size_t)(g * QH + i0 / HALF) * HD;
+    const float2 cs0 = rp[i0 % HALF];
+    const float qa0 = q0[i0 % HALF], qb0 = q0[i0 % HALF + HALF];
+    // the new token's key and value operands (used by the chunk holding its
+    // row; every workgroup loads them, clamped, so no load is conditional)
+    const int dk = t < HALF ? t : HALF - 1, dv = t < HD ? t : HD - 1;
+    const float *kq = qkv + (size_t)(H + g) * HD;
+    const float *vq = qkv + (size_t)(H + Hkv + g) * HD;
+    const float2 csk = rp[dk];
+    const float ka0 = kq[dk], kb0 = kq[dk + HALF], v0 = vq[dv];
+    __builtin_amdgcn_sched_barrier(0); // keep these loads ahead of the tile's
+
     // cache tile loads; the row of the new token is replaced from LDS below
     const int jj = t >> 2, qq = t & 3;
     uint4 kreg[KL];
-#pragma unroll
-    for (int b = 0; b < KL; ++b)
-        kreg[b] = make_uint4(0, 0, 0, 0);
-    if (jj < n) {
-        const uint16_t *kr = kc + (gbase + jj) * HD + qq * QD;
+    {
+        const uint16_t *kr = kc + (gbase + (jj < n ? jj : n - 1)) * HD + qq * QD;
 #pragma unroll
         for (int b = 0; b < KL; ++b)
             kreg[b] = *reinterpret_cast<const uint4 *>(kr + b * 8);
@@ -132,15 +152,22 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
         const int r = pg + i * PG;
-        vreg[i] = make_uint4(0, 0, 0, 0);
-        if (r < n)
-            vreg[i] = *reinterpret_cast<const uint4 *>(vc + (gbase + r) * HD + db * 8);
+        vreg[i] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < n ? r : n - 1)) * HD +
+                                                   db * 8);
     }
+    // The new token's operands are consumed here, so the compiler cannot
+    // sink their loads into the branch below, behind the tile's.
+    asm volatile("" ::"v"(ka0), "v"(kb0), "v"(v0), "v"(csk.x), "v"(csk.y));
 
     // rotate the group's queries; the chunk of the new token also rotates
     // its key and stores key and value into row pos of the caches
-    const float2 *rp = rope + (size_t)pos * HALF;
-    for (int i = t; i < QH * HALF; i += kAThreads) {
+    {   // threads past QH * HALF repeat the last element: the same values
+        // to the same place
+        const int h = i0 / HALF, d = i0 % HALF;
+        qr[h][d] = qa0 * cs0.x - qb0 * cs0.y;
+        qr[h][d + HALF] = qa0 * cs0.y + qb0 * cs0.x;
+    }
+    for (int i = t + kAThreads; i < QH * HALF; i += kAThreads) {
         const int h = i / HALF, d = i % HALF;
         const float *q = qkv + (size_t)(g * QH + h) * HD;
         const float2 cs = rp[d];
@@ -149,24 +176,20 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         qr[h][d + HALF] = a * cs.y + b * cs.x;
     }
     if (jn < kAP) {
-        const float *k = qkv + (size_t)(H + g) * HD;
-        const float *v = qkv + (size_t)(H + Hkv + g) * HD;
         uint16_t *krow = kc + (gbase + jn) * HD;
         uint16_t *vrow = vc + (gbase + jn) * HD;
-        for (int d = t; d < HALF; d += kAThreads) {
-            const float2 cs = rp[d];
-            const float a = k[d], b = k[d + HALF];
-            const uint16_t r0 = f2h(a * cs.x - b * cs.y);
-            const uint16_t r1 = f2h(a * cs.y + b * cs.x);
-            knew[d] = r0;
-            knew[d + HALF] = r1;
-            krow[d] = r0;
-            krow[d + HALF] = r1;
+        if (t < HALF) {
+            const uint16_t r0 = f2h(ka0 * csk.x - kb0 * csk.y);
+            const uint16_t r1 = f2h(ka0 * csk.y + kb0 * csk.x);
+            knew[t] = r0;
+            knew[t + HALF] = r1;
+            krow[t] = r0;
+            krow[t + HALF] = r1;
         }
-        for (int d = t; d < HD; d += kAThreads) {
-            const uint16_t r = f2h(v[d]);
-            vnew[d] = r;
-            vrow[d] = r;
+        if (t < HD) {
+            const uint16_t r = f2h(v0);
+            vnew[t] = r;
+            vrow[t] = r;
         }
     }
     __syncthreads();
