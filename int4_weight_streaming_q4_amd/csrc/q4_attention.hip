@@ -329,12 +329,16 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
     const int s = __builtin_amdgcn_readfirstlane(t / kCDims);
     const int g = hq / QH, h = hq % QH;
     const int col = BATCH ? (int)blockIdx.z : 0;
-    const int pos = *pos_dev + col;
     if (BATCH) {
         part += (size_t)col * (gridDim.x / QH) * nchunk * QH * (HD + 2);
         out += (size_t)col * gridDim.x * HD;
     }
-    const int nc = min(nchunk, pos / kAP + 1);
+    // One token: attn_partial wrote every chunk, those past the position as
+    // empty partials (max -inf, sum 0, o 0), whose merge changes nothing
+    // bitwise (weight exp(-inf) = 0, rescale exp(0) = 1), so all nchunk are
+    // read and the loads need not wait for the position word.  A batch reads
+    // only its column's chunks.
+    const int nc = BATCH ? min(nchunk, (*pos_dev + col) / kAP + 1) : nchunk;
     const size_t prow = (size_t)(HD + 2);
     const size_t cstride = (size_t)QH * prow;
     const float *base = part + ((size_t)g * nchunk * QH + h) * prow;
@@ -358,12 +362,15 @@ attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev
 #pragma unroll
         for (int u = 0; u < U; ++u)
             mn = fmaxf(mn, mv[u]);
-        const float r = expf(m - mn);
+        // an empty chunk (max -inf) has weight 0, and a running max of -inf
+        // means l = o = 0: the guards keep -inf - -inf out of expf and give
+        // the same bits as expf wherever that difference is defined
+        const float r = m == -INFINITY ? 1.0f : expf(m - mn);
         l *= r;
         o *= r;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float w = expf(mv[u] - mn);
+            const float w = mv[u] == -INFINITY ? 0.0f : expf(mv[u] - mn);
             l = fmaf(lv[u], w, l);
             o = fmaf(ov[u], w, o);
         }
