@@ -495,10 +495,10 @@ __device__ __forceinline__ int lane_chunks(int C) {
 
 // Issues the first chunk loads of row block `blk`.  GUARD: skip them when
 // the block does not exist (the persistent kernels prefetch a product whose
-// row blocks may be fewer than the workgroups); the per-product kernels
-// launch at most one workgroup per row block and issue them unconditionally
-// (a uniform branch around the loads would still make the compiler's next
-// wait cover them all).
+// row blocks may be fewer than the workgroups), and skip chunks past a
+// lane's count per lane; without GUARD (the per-product kernels, which
+// launch at most one workgroup per row block) every load is issued, so the
+// staging that follows waits only for the activation.
 template <int R, int KS, int U, bool NT, Epi E, bool GUARD = true>
 __device__ __forceinline__ void prefetch_block(const uint8_t *W, const uint16_t *S, int64_t N,
                                                int K, int64_t n_units, const EpiArgs &ea,
