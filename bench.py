@@ -330,6 +330,7 @@ KERNEL_SOURCES = ["int4_weight_streaming_q4_amd/csrc/q4_gemv.hip",
                   "int4_weight_streaming_q4_amd/csrc/q4_gemv_core.h",
                   "int4_weight_streaming_q4_amd/csrc/q4_internal.h"]
 PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
+PMC_SUMMARY_70B = "profiles/gate_up_70b_decode_pmc.md"
 
 
 def kernel_source_hash():
@@ -341,11 +342,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
+def recorded_traffic(summary=PMC_SUMMARY):
     """HBM bytes per gate+up launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
     root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, PMC_SUMMARY)
+    path = os.path.join(root, summary)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -511,6 +512,13 @@ def bench_70b_resident(args, q4, inputs, torch):
     if args.step_mode is not None:
         dec.set_persistent(args.step_mode)
     stream = torch.cuda.Stream()
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written by one plain copy kernel
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -545,7 +553,9 @@ def bench_70b_resident(args, q4, inputs, torch):
                                     "achieved": round(kb[2] / kern_us[2] / 1e3, 1),
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(kb[2] / kern_us[2] / 1e3 / HBM_PEAK_GBS, 4),
-                                    "traffic": None, "avg_launch_us": round(kern_us[2], 3)}})
+                                    "traffic": recorded_traffic(PMC_SUMMARY_70B),
+                                    "bytes_per_launch": kb[2],
+                                    "avg_launch_us": round(kern_us[2], 3)}})
     print(json.dumps(res), flush=True)
 
 
