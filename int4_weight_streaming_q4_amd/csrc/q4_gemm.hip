@@ -79,7 +79,8 @@ __device__ __forceinline__ uint16_t ntload2(const uint16_t *p) {
 }
 
 // Operands of one group quad: for each row tile the lane's 16-byte group of
-// codes and its scale, and the lane's 32 activations of its batch column.
+// codes and its scale, and four 16-byte blocks of activations in load order
+// (rearranged through LDS before the multiply).
 template <int RT>
 struct Quad {
     uint4 w[RT];
@@ -94,10 +95,17 @@ struct Quad {
 // group past the last one (K / 32 not a multiple of 4) gets scale 0, which
 // zeroes its weights; a padding column multiplies real activations of column
 // 0 and its outputs are never stored.
+//
+// Activations: a quad covers 256 contiguous bytes (4 groups x 32 halves) of
+// each column.  Load j brings columns 4j .. 4j+3, lane l taking the 16-byte
+// block l % 16 of column 4j + l / 16, so each load instruction reads whole
+// cache lines; `xoff[j]` is the lane's offset (in halves) of that block in
+// the quad at k = 0.
 template <int RT>
 __device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wrow)[RT],
                                           const uint16_t *const (&srow)[RT],
-                                          const uint16_t *xb, int q, int kq, int C) {
+                                          const uint16_t *X16, const uint32_t (&xoff)[4], int q,
+                                          int kq, int gq, int C) {
     const int g = q * 4 + kq;
     o.live = g < C;
     const int gc = o.live ? g : C - 1;
@@ -106,18 +114,37 @@ __device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wr
         o.w[t] = ntload16(wrow[t] + (size_t)gc * 16);
         o.s[t] = ntload2(srow[t] + gc);
     }
-    const uint16_t *xp = xb + (size_t)gc * 32;
+    const int gx = q * 4 + gq;
+    const uint32_t xg = (uint32_t)(gx < C ? gx : C - 1) * 32u;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        o.x[p] = gload16(xp + 8 * p);
+    for (int j = 0; j < 4; ++j)
+        o.x[j] = gload16(X16 + xoff[j] + xg);
 }
 
+// Column stride of the per-wave activation tile in LDS, in 16-byte blocks:
+// 16 blocks of data + 1 of padding, so the 16 lanes of a row reading the
+// same block of 16 different columns hit 16 different bank quads.
+constexpr int kXStride = 17;
+
+// The quad's activations go through the wave's own LDS tile `xs` (column c
+// at xs[c * kXStride], its 256 bytes in k order): the lane writes its four
+// loaded blocks, then reads the four blocks of group kq of its column `rc`.
+// Only this wave touches `xs`, and a wave's LDS operations execute in
+// order, so no workgroup barrier is needed; the wave barriers keep the
+// compiler from moving the reads above the writes or the next quad's writes
+// above these reads.
 template <int RT>
-__device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT], uint32_t bias) {
+__device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT], uint32_t bias,
+                                         uint4 *xs, int lane, int rc, int kq) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        xs[(4 * j + (lane >> 4)) * kXStride + (lane & 15)] = o.x[j];
+    __builtin_amdgcn_wave_barrier();
     half8_t bop[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        bop[p] = __builtin_bit_cast(half8_t, permute_block(o.x[p]));
+        bop[p] = __builtin_bit_cast(half8_t, permute_block(xs[rc * kXStride + kq * 4 + p]));
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(o.live ? o.s[t] : 0u));
@@ -144,6 +171,7 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  int B, uint16_t *__restrict__ M, int64_t npair) {
     static_assert(E != GEpi::SiluPair || RT % 2 == 0, "gate and up tiles come in pairs");
     __shared__ float4_t red[NW][RT][64];
+    __shared__ uint4 xs_all[NW][16 * kXStride];
     const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,7 +184,15 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int64_t row0 = (int64_t)blockIdx.x * (E == GEpi::SiluPair ? 8 * RT : 16 * RT);
 
     const bool bvalid = i16 < B;
-    const uint16_t *xb = X16 + (size_t)(bvalid ? i16 : 0) * K;
+    const int rc = bvalid ? i16 : 0;
+    const int gq = (lane >> 2) & 3;
+    uint32_t xoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = 4 * j + (lane >> 4);
+        xoff[j] = (uint32_t)(c < B ? c : 0) * (uint32_t)K + (uint32_t)(lane & 3) * 8u;
+    }
+    uint4 *xs = xs_all[wave];
 
     const uint8_t *wrow[RT];
     const uint16_t *srow[RT];
@@ -189,23 +225,23 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     Quad<RT> qa, qb;
     int q = wave;
     if (q < nquads) {
-        load_quad<RT>(qa, wrow, srow, xb, q, kq, C);
+        load_quad<RT>(qa, wrow, srow, X16, xoff, q, kq, gq, C);
         while (q + 2 * NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C);
+            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, gq, C);
             __builtin_amdgcn_sched_barrier(0); // issue before waiting for qa
-            mma_quad<RT>(qa, acc, bias);
-            load_quad<RT>(qa, wrow, srow, xb, q + 2 * NW, kq, C);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
+            load_quad<RT>(qa, wrow, srow, X16, xoff, q + 2 * NW, kq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qb, acc, bias);
+            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq);
             q += 2 * NW;
         }
         if (q + NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, xb, q + NW, kq, C);
+            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qa, acc, bias);
-            mma_quad<RT>(qb, acc, bias);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
+            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq);
         } else {
-            mma_quad<RT>(qa, acc, bias);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
         }
     }
 
