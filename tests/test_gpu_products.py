@@ -210,7 +210,7 @@ def _gemm(packed, scales, X, tuned=None):
     return Y.cpu().numpy()
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 8, 13, 16])
 @pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (65, 2080), (300, 1024), (33, 32768)])
 def test_gemm_small_shapes(B, N, K):
     packed, scales = _mat(N, K, 300 + B + N + K)
