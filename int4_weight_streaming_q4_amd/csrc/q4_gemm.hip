@@ -12,9 +12,10 @@
 //
 // One MFMA covers 16 weight rows x 32 k x 16 batch columns (B padded with
 // zeros).  Lane l supplies row (l % 16) / column (l % 16) and the 8-value k
-// block l / 16.  A lane loads one whole 16-byte group (32 codes) of its row
-// for the group g0 + l/16 of a "quad" of four groups; word p of that group
-// feeds MFMA p.  Because an MFMA then spans four different groups, each
+// block l / 16.  Lane l holds one whole 16-byte group (32 codes) of its row
+// for the group g0 + l/16 of a "quad" of four groups (loaded by lane
+// 4 * (l % 16) + l / 16 and passed over by ds_bpermute); word p of that
+// group feeds MFMA p.  Because an MFMA then spans four different groups, each
 // weight is scaled on the A side: (code - 8) * scale rounded once to
 // binary16, a relative change below 2^-11 per weight.  The k order inside a
 // word is the unpack order (k0,k4,k1,k5,k2,k6,k3,k7); the activation block is
@@ -101,14 +102,20 @@ struct Quad {
 // block l % 16 of column 4j + l / 16, so each load instruction reads whole
 // cache lines; `xoff[j]` is the lane's offset (in halves) of that block in
 // the quad at k = 0.
+//
+// Codes and scales: lane l loads group 4q + (l & 3) of row (l >> 2) of each
+// row tile, so each 16-lane quarter of a load reads 64 contiguous bytes of
+// four rows (a lane per row, as the matrix op's operand layout has it,
+// would touch sixteen rows per quarter and four times the cache accesses);
+// mma_quad moves each value to its matrix-op lane.
 template <int RT>
 __device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wrow)[RT],
                                           const uint16_t *const (&srow)[RT],
                                           const uint16_t *X16, const uint32_t (&xoff)[4], int q,
-                                          int kq, int gq, int C) {
-    const int g = q * 4 + kq;
-    o.live = g < C;
-    const int gc = o.live ? g : C - 1;
+                                          int kq, int wq, int gq, int C) {
+    o.live = q * 4 + kq < C; // the group of this lane's matrix-op operands
+    const int gw = q * 4 + wq;
+    const int gc = gw < C ? gw : C - 1;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         o.w[t] = ntload16(wrow[t] + (size_t)gc * 16);
@@ -133,9 +140,11 @@ constexpr int kXStride = 17;
 // order, so no workgroup barrier is needed; the wave barriers keep the
 // compiler from moving the reads above the writes or the next quad's writes
 // above these reads.
+// `perm` is the byte address of the loading lane of this lane's operands
+// (row i16, group kq: lane 4 * i16 + kq) for ds_bpermute.
 template <int RT>
 __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT], uint32_t bias,
-                                         uint4 *xs, int lane, int rc, int kq) {
+                                         uint4 *xs, int lane, int rc, int kq, int perm) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         xs[(4 * j + (lane >> 4)) * kXStride + (lane & 15)] = o.x[j];
@@ -147,9 +156,13 @@ __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT],
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(o.live ? o.s[t] : 0u));
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.s[t]);
+        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(o.live ? sb : 0u));
         const half2_t s2 = {sh, sh};
-        const uint32_t wd[4] = {o.w[t].x, o.w[t].y, o.w[t].z, o.w[t].w};
+        const uint32_t wd[4] = {(uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].x),
+                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].y),
+                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].z),
+                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].w)};
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(wd[p], s2, bias),
@@ -186,6 +199,8 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const bool bvalid = i16 < B;
     const int rc = bvalid ? i16 : 0;
     const int gq = (lane >> 2) & 3;
+    const int wq = lane & 3;
+    const int perm = (i16 * 4 + kq) * 4;
     uint32_t xoff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -201,12 +216,12 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
         int64_t row;
         if constexpr (E == GEpi::SiluPair) {
             const int th = t % (RT / 2);
-            row = row0 + th * 16 + i16;
+            row = row0 + th * 16 + (lane >> 2);
             row = row < npair ? row : npair - 1;
             if (t >= RT / 2)
                 row += npair;
         } else {
-            row = row0 + t * 16 + i16;
+            row = row0 + t * 16 + (lane >> 2);
             row = row < N ? row : N - 1;
         }
         wrow[t] = W + (size_t)row * row_bytes;
@@ -225,23 +240,23 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     Quad<RT> qa, qb;
     int q = wave;
     if (q < nquads) {
-        load_quad<RT>(qa, wrow, srow, X16, xoff, q, kq, gq, C);
+        load_quad<RT>(qa, wrow, srow, X16, xoff, q, kq, wq, gq, C);
         while (q + 2 * NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, gq, C);
+            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0); // issue before waiting for qa
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
-            load_quad<RT>(qa, wrow, srow, X16, xoff, q + 2 * NW, kq, gq, C);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
+            load_quad<RT>(qa, wrow, srow, X16, xoff, q + 2 * NW, kq, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq);
+            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq, perm);
             q += 2 * NW;
         }
         if (q + NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, gq, C);
+            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
-            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
+            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq, perm);
         } else {
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq);
+            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
         }
     }
 
