@@ -466,7 +466,7 @@ def bench_gemm(args, q4, inputs, torch):
             if B > 1:
                 # the two paths side by side (the matrix-core kernel at the
                 # library's own launch shape is q4_gemm_tuned's default here)
-                tiles, cap, rt = (N + 15) // 16, (2 if B <= 2 else (4 if B < 16 else 8)), 1
+                tiles, cap, rt = (N + 15) // 16, (2 if B <= 2 else 4), 1
                 while rt * 2 <= cap and tiles // (rt * 2) >= cus * 3 // 4:
                     rt *= 2
                 mf = [(lambda st, p=p, sc=sc: q4.q4_gemm_tuned(p, sc, X, Y, rt, 4, stream=st))
