@@ -79,15 +79,16 @@ __device__ __forceinline__ uint16_t ntload2(const uint16_t *p) {
     return __builtin_nontemporal_load((global_t *)p);
 }
 
-// Operands of one group quad: for each row tile the lane's 16-byte group of
-// codes and its scale, and four 16-byte blocks of activations in load order
+// Operands of one group quad as this lane loaded them: for each row tile a
+// 16-byte group of codes and its scale (handed to their matrix-op lane by
+// ds_bpermute before the multiply), and four 16-byte blocks of activations
 // (rearranged through LDS before the multiply).
 template <int RT>
 struct Quad {
     uint4 w[RT];
     uint32_t s[RT]; // binary16 bits, zero-extended (keeps the struct in registers)
     uint4 x[4];
-    bool live;      // the lane's group exists (false: scale taken as 0)
+    bool live;      // this lane's matrix-op group exists (false: scale taken as 0)
 };
 
 // Every load is unconditional (addresses clamped into the matrix and into
