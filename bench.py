@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for "
                          "hardware byte counters)")
+    ap.add_argument("--counter-sample", action="store_true",
+                    help="with --config 3: only a short sample for counter runs (a 1 GiB "
+                         "copy, then the 28672 x 4096 product at B = 16 on the matrix "
+                         "cores and at B = 1, four launches each)")
     return ap.parse_args()
 
 
@@ -434,6 +438,32 @@ def base_result(metric, value, unit, steps, warmup, workload, extra=None):
     return r
 
 
+def gemm_counter_sample(q4, inputs, torch):
+    """A few launches to read hardware counters on: one plain 1 GiB device
+    copy (calibration), then the 28672 x 4096 product on four weight copies
+    at B = 16 through the library's small-batch path (matrix cores) and at
+    B = 1 (the GEMV)."""
+    N, K, copies = 28672, 4096, 4
+    Ws = [(inputs.random_bytes(N, K, inputs.seed_of(3, i, 0), device="cuda"),
+           inputs.scales(N, K, inputs.seed_of(3, i, 1), device="cuda")) for i in range(copies)]
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    X = inputs.act_f16((16, K), inputs.seed_of(3, 0, 2) + 16, device="cuda")
+    Y = torch.empty(16, N, dtype=torch.float32, device="cuda")
+    for p, sc in Ws:
+        q4.q4_gemm_smallbatch(p, sc, X, Y)
+    x = inputs.act_f16(K, inputs.seed_of(3, 0, 2) + 1, device="cuda")
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    for p, sc in Ws:
+        q4.q4_gemv(p, sc, x, y)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_sample": "gate_up 28672x4096, B=16 and B=1, 4 launches each",
+                      "weight_bytes_per_launch": N * K // 2 + N * (K // 32) * 2}), flush=True)
+
+
 def bench_gemm(args, q4, inputs, torch):
     """Small-batch product on the four 8B matrix shapes, B in {1, 2, 4, 8,
     16}: distinct weight copies (> 512 MB per shape) launched round-robin
@@ -443,6 +473,8 @@ def bench_gemm(args, q4, inputs, torch):
     crossover in B."""
     shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096),
               "down": (4096, 14336)}
+    if args.counter_sample:
+        return gemm_counter_sample(q4, inputs, torch)
     stream = torch.cuda.Stream()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     table = {}
