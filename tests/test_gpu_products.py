@@ -233,6 +233,20 @@ def test_gemm_every_launch_shape(rt, nw):
         assert_within(Y[b], Y_ref[b], M[b], f"gemm rt={rt} nw={nw} col {b}")
 
 
+@pytest.mark.parametrize("B", [5, 7, 16])
+def test_gemm_row_tiles_do_not_change_bits(B):
+    """At four waves (the k split every matrix-core launch uses) the row
+    tiles per wave only regroup rows: every launch shape gives the same bits,
+    and the library's own choice is one of them."""
+    N, K = 300, 1184  # 37 groups: ragged group quads
+    packed, scales = _mat(N, K, 950 + B)
+    X = inputs.act_f16((B, K), 951 + B, device=DEV)
+    ref = _gemm(packed, scales, X, tuned=(1, 4))
+    for rt in (2, 4, 8):
+        assert np.array_equal(_gemm(packed, scales, X, tuned=(rt, 4)), ref), rt
+    assert np.array_equal(_gemm(packed, scales, X), ref)
+
+
 def test_gemm_b1_is_gemv_and_columns_match_gemv():
     N, K = 512, 2048
     packed, scales = _mat(N, K, 31)
