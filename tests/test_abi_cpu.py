@@ -330,3 +330,15 @@ def test_plain_c_consumer(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert "passed" in r.stdout
+
+
+def test_bench_refuses_several_gpus():
+    """The measurement script runs on one GPU: asking for more exits with
+    status 2 and says so, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
