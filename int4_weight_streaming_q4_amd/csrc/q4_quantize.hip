@@ -5,12 +5,17 @@
 // "Method", bullet "Computation optimization" runs its kernel on 4-bit
 // weights but gives no rule for producing them.  The rule here, per group:
 //   s = binary16(max |w| / 8)              the stored scale (nearest even)
-//   c = clamp(rint(w / s) + 8, 0, 15)      w / s one IEEE binary32 division,
+//   c = clamp(rint(w / s) + 8, 0, 15)      w / s the exact quotient,
 //                                          rint ties to even
-// and a group whose stored scale is 0 gets code 8 everywhere.  The code is
-// an integer decided by floating point, so the precision of that decision
-// is part of the definition: one correctly rounded binary32 division (the
-// compiler's default division; not a reciprocal product).
+// and a group whose stored scale is 0 gets code 8 everywhere.  One
+// correctly rounded binary32 division (the compiler's default division;
+// not a reciprocal product) decides that rounding exactly: w has at most 24
+// significant bits and s at most 11, so each boundary (n + 1/2) s is a
+// binary32 value; a weight next to it differs by at least one unit in the
+// last place of w, which moves the quotient by more than half a unit in the
+// last place of the quotient, so the rounded quotient never lands on
+// n + 1/2 or crosses it, and a weight on the boundary divides to n + 1/2
+// exactly.
 //
 // Four lanes per group: a lane loads 8 consecutive weights (32 bytes of
 // binary32 or 16 of binary16), the group maximum is taken across the quad

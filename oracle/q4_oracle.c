@@ -368,11 +368,13 @@ void q4o_attention(const double *qkv, int64_t H, int64_t Hkv, int64_t hd,
  *     amax = max |w| over the group
  *     s    = binary16(amax / 8), round to nearest even (the stored scale)
  *     c    = clamp(rint(w / s) + 8, 0, 15)   (rint: ties to even)
- * The quotient w / s is one IEEE binary32 division of the binary32 values
- * of w and s: a rounding step decides an integer code, so it is fixed to
- * the precision the kernel uses.  A group whose stored scale is 0 (all
- * zero, or amax / 8 below half the smallest binary16 subnormal) gets code 8
- * everywhere.  The largest weight of a group, when positive, maps to
+ * where w / s is the exact real quotient.  An fp64 division decides it
+ * exactly: w has at most 24 significant bits and s at most 11, so a
+ * quotient that is not a half-integer n + 1/2 (|n| <= 8) differs from one
+ * by at least 2^-26, while the fp64 division errs by less than 2^-49; and a
+ * half-integer quotient is computed exactly.  A group whose stored scale is
+ * 0 (all zero, or amax / 8 below half the smallest binary16 subnormal) gets
+ * code 8 everywhere.  The largest weight of a group, when positive, maps to
  * w / s = 8 and is clipped to code 15 (7 s).  Inputs are finite with
  * amax / 8 below 65520 (else the scale is infinite).
  * codes: u8[N][K], one code per byte; scales: u16[N][K/32].
@@ -387,19 +389,18 @@ static void quantize_group(const float *w, uint8_t *codes, uint16_t *scale)
     }
     uint16_t s16 = q4o_f64_to_f16(amax / 8.0); /* amax / 8 is exact in fp64 */
     *scale = s16;
-    float s = (float)q4o_f16_to_f64(s16);
+    double s = q4o_f16_to_f64(s16);
     for (int i = 0; i < 32; ++i) {
-        if (s == 0.0f) {
+        if (s == 0.0) {
             codes[i] = 8;
             continue;
         }
-        volatile float q = w[i] / s; /* one binary32 division */
-        float r = rintf(q);
-        float c = r + 8.0f;
-        if (c < 0.0f)
-            c = 0.0f;
-        if (c > 15.0f)
-            c = 15.0f;
+        double r = rint((double)w[i] / s); /* default rounding: ties to even */
+        double c = r + 8.0;
+        if (c < 0.0)
+            c = 0.0;
+        if (c > 15.0)
+            c = 15.0;
         codes[i] = (uint8_t)c;
     }
 }

@@ -354,11 +354,16 @@ def test_attention_equal_keys_average_the_values():
         kn = qkv[(H + g) * hd:(H + g + 1) * hd]
         k[g, :pos] = oracle.f64_to_f16(oracle.rope(kn, pos))        # the key this token writes
         v[g, :pos] = oracle.f64_to_f16(rng.standard_normal((pos, hd)))
-    o, _ = oracle.attention(qkv, ATT_DIMS, pos, k, v)
+    o, mag = oracle.attention(qkv, ATT_DIMS, pos, k, v)
     for hq in range(H):
         g = hq // (H // Hkv)
-        want = oracle.f16_to_f64(v[g, :pos + 1]).mean(axis=0)
+        vals = oracle.f16_to_f64(v[g, :pos + 1])
+        want = vals.mean(axis=0)
         assert np.allclose(o[hq * hd:(hq + 1) * hd], want, rtol=0, atol=1e-12)
+        # equal weights 1 / (pos + 1): the magnitude is the mean of |v|
+        assert np.allclose(mag[hq * hd:(hq + 1) * hd], np.abs(vals).mean(axis=0),
+                           rtol=0, atol=1e-12)
+        assert np.any(np.abs(want) < np.abs(vals).mean(axis=0) - 1e-3)  # signs differ
 
 
 def test_attention_dominant_key_selects_its_value():
@@ -372,8 +377,11 @@ def test_attention_dominant_key_selects_its_value():
     # row 1 of group 0 holds the rotated query direction, scaled: score 2^11 * 100 / sqrt(8)
     kdir = oracle.rope(np.eye(hd)[0], pos)
     k[0, 1] = oracle.f64_to_f16(kdir * 2048.0)
-    o, _ = oracle.attention(qkv, ATT_DIMS, pos, k, v)
+    o, mag = oracle.attention(qkv, ATT_DIMS, pos, k, v)
     assert np.allclose(o[:hd], oracle.f16_to_f64(v[0, 1]), rtol=0, atol=1e-12)
+    # all weight on one row: the magnitude is |v| of that row
+    assert np.allclose(mag[:hd], np.abs(oracle.f16_to_f64(v[0, 1])), rtol=0, atol=1e-12)
+    assert np.any(oracle.f16_to_f64(v[0, 1]) < 0)
 
 
 def test_attention_layer_at_position_zero_equals_stand_in_layer():
@@ -394,6 +402,116 @@ def test_attention_layer_at_position_zero_equals_stand_in_layer():
     assert np.array_equal(h1, h2) and np.array_equal(m1, m2)
 
 
+def _np_rms_f16(h, eps=1e-5):
+    return (h / np.sqrt(np.mean(h * h) + eps)).astype(np.float16).astype(np.float64)
+
+
+def _np_rotate(x, pos, base):
+    """Rotate-half rotary embedding written as a complex product: the pair
+    (x_i, x_{i+hd/2}) is the complex number x_i + j x_{i+hd/2}, turned by
+    the angle pos * base^(-2i/hd)."""
+    half = x.size // 2
+    ang = pos * base ** (-2.0 * np.arange(half) / x.size)
+    z = (x[:half] + 1j * x[half:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag])
+
+
+def _np_layer(W, dims, h, attend, eps=1e-5):
+    """One decoder layer composed in numpy from dense fp64 matrices W[name];
+    `attend(qkv)` returns the attention output (before rounding).  Returns
+    the new residual and the magnitudes sum |w x| of the two products added
+    into it."""
+    from scipy.special import expit
+    dff = dims["dff"]
+    a = _np_rms_f16(h, eps)
+    qkv = W["qkv"] @ a
+    o16 = attend(qkv).astype(np.float16).astype(np.float64)
+    h = h + W["o"] @ o16
+    mag = np.abs(W["o"]) @ np.abs(o16)
+    a2 = _np_rms_f16(h, eps)
+    gu = W["gate_up"] @ a2
+    m = (gu[:dff] * expit(gu[:dff]) * gu[dff:]).astype(np.float16).astype(np.float64)
+    h = h + W["down"] @ m
+    mag = mag + np.abs(W["down"]) @ np.abs(m)
+    return h, mag
+
+
+def _random_layer(rng, dims):
+    d, H, Hkv, hd, dff = (dims[k] for k in ("d", "H", "Hkv", "hd", "dff"))
+    shapes = {"qkv": ((H + 2 * Hkv) * hd, d), "o": (d, H * hd), "gate_up": (2 * dff, d),
+              "down": (d, dff)}
+    layer, dense = {}, {}
+    for name, (N, K) in shapes.items():
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        s = (np.abs(rng.standard_normal((N, K // 32))) * 0.05).astype(np.float16)
+        layer[name] = (oracle.pack(codes), s.view(np.uint16))
+        dense[name] = _dense_reference(codes, s, np.zeros(K))[1]
+    return layer, dense
+
+
+def test_decode_layer_against_numpy_composition():
+    """The stand-in layer and its magnitude output against the layer written
+    out in numpy (dense matrices, numpy's float16 rounding, the GQA gather by
+    slicing)."""
+    dims = dict(d=64, H=4, Hkv=2, hd=16, dff=96)
+    rng = np.random.default_rng(31)
+    layer, W = _random_layer(rng, dims)
+    H, Hkv, hd = dims["H"], dims["Hkv"], dims["hd"]
+
+    def gather(qkv):
+        V = qkv[(H + Hkv) * hd:].reshape(Hkv, hd)
+        return np.repeat(V, H // Hkv, axis=0).reshape(-1)
+
+    h0 = rng.standard_normal(64) * 2.0
+    want_h, want_m = _np_layer(W, dims, h0, gather)
+    h, mag = h0.copy(), np.zeros(64)
+    oracle.decode_layer(layer, dims, h, mag)
+    np.testing.assert_allclose(h, want_h, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(mag, want_m, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("pos", [1, 5])
+def test_attention_layer_above_position_zero_against_numpy(pos):
+    """The layer with attention over caches at position pos against the same
+    layer composed in numpy: rotation as a complex product, scipy's softmax
+    over rows 0..pos of the group's caches (earlier rows prefilled), the new
+    key and value rows written first."""
+    from scipy.special import softmax
+    dims = dict(d=64, H=4, Hkv=2, hd=16, dff=96)
+    H, Hkv, hd = dims["H"], dims["Hkv"], dims["hd"]
+    base = 10000.0
+    rng = np.random.default_rng(40 + pos)
+    layer, W = _random_layer(rng, dims)
+    k, v = oracle.kv_cache(dims, 8)
+    k[:, :pos] = rng.standard_normal((Hkv, pos, hd)).astype(np.float16).view(np.uint16)
+    v[:, :pos] = rng.standard_normal((Hkv, pos, hd)).astype(np.float16).view(np.uint16)
+    kn = k.view(np.float16).astype(np.float64).copy()
+    vn = v.view(np.float16).astype(np.float64).copy()
+
+    def attend(qkv):
+        q = qkv[:H * hd].reshape(H, hd)
+        kk = qkv[H * hd:(H + Hkv) * hd].reshape(Hkv, hd)
+        vv = qkv[(H + Hkv) * hd:].reshape(Hkv, hd)
+        for g in range(Hkv):
+            kn[g, pos] = _np_rotate(kk[g], pos, base).astype(np.float16)
+            vn[g, pos] = vv[g].astype(np.float16)
+        out = np.empty((H, hd))
+        for hq in range(H):
+            g = hq // (H // Hkv)
+            p = softmax(kn[g, :pos + 1] @ _np_rotate(q[hq], pos, base) / np.sqrt(hd))
+            out[hq] = p @ vn[g, :pos + 1]
+        return out.reshape(-1)
+
+    h0 = rng.standard_normal(64) * 2.0
+    want_h, want_m = _np_layer(W, dims, h0, attend)
+    h, mag = h0.copy(), np.zeros(64)
+    oracle.decode_layer_attn(layer, dims, h, pos, k, v, mag, base=base)
+    np.testing.assert_allclose(h, want_h, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(mag, want_m, rtol=1e-10, atol=0)
+    assert np.array_equal(k.view(np.float16).astype(np.float64), kn)
+    assert np.array_equal(v.view(np.float16).astype(np.float64), vn)
+
+
 def test_attention_two_positions_logistic_weights():
     """Two positions: the weights are the logistic function of the score
     difference, with scores (rotated q . k) / sqrt(hd); a 1/hd or unscaled
@@ -404,15 +522,18 @@ def test_attention_two_positions_logistic_weights():
     k, v = oracle.kv_cache(ATT_DIMS, 4)
     k[:, 0] = oracle.f64_to_f16(rng.standard_normal((Hkv, hd)) * 2.0)
     v[:, 0] = oracle.f64_to_f16(rng.standard_normal((Hkv, hd)))
-    o, _ = oracle.attention(qkv, ATT_DIMS, 1, k, v)
+    o, mag = oracle.attention(qkv, ATT_DIMS, 1, k, v)
     for hq in range(H):
         g = hq // (H // Hkv)
         qr = oracle.rope(qkv[hq * hd:(hq + 1) * hd], 1)
         s0 = qr @ oracle.f16_to_f64(k[g, 0]) / np.sqrt(hd)
         s1 = qr @ oracle.f16_to_f64(k[g, 1]) / np.sqrt(hd)
         p1 = 1.0 / (1.0 + np.exp(s0 - s1))
-        want = (1 - p1) * oracle.f16_to_f64(v[g, 0]) + p1 * oracle.f16_to_f64(v[g, 1])
+        v0, v1 = oracle.f16_to_f64(v[g, 0]), oracle.f16_to_f64(v[g, 1])
+        want = (1 - p1) * v0 + p1 * v1
         assert np.allclose(o[hq * hd:(hq + 1) * hd], want, rtol=0, atol=1e-12)
+        assert np.allclose(mag[hq * hd:(hq + 1) * hd], (1 - p1) * np.abs(v0) + p1 * np.abs(v1),
+                           rtol=0, atol=1e-12)
 
 
 # --------------------------------------------------------- quantization
@@ -454,8 +575,8 @@ def test_quantize_recovers_codes_on_the_grid():
 
 def test_quantize_is_nearest_code_and_error_bound():
     """Brute force over all 16 codes: the chosen code is a nearest grid
-    point for the stored scale (up to the binary32 quotient deciding near
-    ties), and the error is at most s/2, or the clip at +8 s."""
+    point for the stored scale, and the error is at most s/2, or the clip at
+    +8 s."""
     rng = np.random.default_rng(22)
     N, K = 32, 512
     w = (rng.standard_normal((N, K)) * rng.uniform(0.01, 3.0, (N, 1))).astype(np.float32)
@@ -466,9 +587,9 @@ def test_quantize_is_nearest_code_and_error_bound():
     err_all = np.abs(grid - wd[..., None])
     best = err_all.min(axis=2)
     got = np.take_along_axis(err_all, codes[..., None].astype(np.int64), axis=2)[..., 0]
-    assert np.all(got <= best + sg * 2.0 ** -20)
+    assert np.all(got == best)       # differences of exact fp64 values: no slack
     clipped = wd / sg > 7.5
-    assert np.all(got[~clipped] <= sg[~clipped] * (0.5 + 2.0 ** -20))
+    assert np.all(got[~clipped] <= sg[~clipped] * 0.5)
     # s = binary16(max|w| / 8) may sit half a binary16 ulp below max|w| / 8,
     # so w / s reaches 8 (1 + 2^-11) and the clip error s (1 + 2^-8)
     assert np.all(got[clipped] <= sg[clipped] * (1.0 + 2.0 ** -8))
@@ -492,18 +613,55 @@ def test_quantize_zero_and_tiny_groups_and_power_of_two_invariance():
         assert np.array_equal(oracle.f16_to_f64(sk), oracle.f16_to_f64(s1) * 2.0 ** k)
 
 
-def test_quantize_quotient_is_one_binary32_division():
-    """The code is decided by one IEEE binary32 division w / s (numpy's
-    float32 division is the independent reference).  Here w / s is exactly
-    3.5 in binary32 (ties to even: code 12), while multiplying by the
-    binary32 reciprocal of s gives just below 3.5 (code 11)."""
+def test_quantize_tie_goes_to_even_not_reciprocal():
+    """Here w / s is exactly 3.5 (ties to even: code 12), while multiplying
+    by the binary32 reciprocal of s gives just below 3.5 (code 11)."""
     s = np.float32(np.float16(1.612))
     w = np.zeros((1, 32), np.float32)
     w[0, 0] = np.float32(8.0) * s                        # max|w| = 8 s: stored scale is s
-    w[0, 1] = np.float32(float.fromhex("0x1.6928p+2"))   # 5.6430664
-    q_div = np.rint(w[0, 1] / s)
+    w[0, 1] = np.float32(float.fromhex("0x1.6928p+2"))   # 5.6430664 = 3.5 s
     q_rcp = np.rint(w[0, 1] * (np.float32(1.0) / s))
-    assert q_div == 4.0 and q_rcp == 3.0
+    assert q_rcp == 3.0
     codes, sc = oracle.quantize(w)
     assert oracle.f16_to_f64(sc)[0, 0] == float(s)
     assert codes[0, 0] == 15 and codes[0, 1] == 12 and np.all(codes[0, 2:] == 8)
+
+
+def test_quantize_code_is_the_exactly_rounded_quotient():
+    """Codes at and next to every rounding boundary, against exact rational
+    arithmetic (fractions.Fraction, round-half-even): for random binary16
+    scales s (normal and subnormal) and each half-integer n + 1/2, the weights
+    (n + 1/2) s and its binary32 neighbours one and two steps away on either
+    side.  A quotient rounded half up, truncated, or taken through a
+    reciprocal fails here."""
+    from fractions import Fraction
+    rng = np.random.default_rng(24)
+    bits = np.concatenate([rng.integers(0x0001, 0x0400, 40),      # subnormal scales
+                           rng.integers(0x0400, 0x6FFF, 160)]).astype(np.uint16)
+    halves = np.arange(-8, 8) + 0.5                               # n + 1/2, |.| <= 7.5
+    rows = []
+    for sb in bits:
+        s = np.float32(np.uint16(sb).view(np.float16))
+        for t in halves:
+            tie = np.float32(t) * s                               # exact: few bits
+            vals = [tie]
+            for direction in (np.inf, -np.inf):
+                v = tie
+                for _ in range(2):
+                    v = np.nextafter(v, np.float32(direction), dtype=np.float32)
+                    vals.append(v)
+            for v in vals:
+                rows.append((sb, v))
+    # one group per (scale, weight): w[0] = 8 s fixes the stored scale at s
+    w = np.zeros((len(rows), 32), np.float32)
+    for i, (sb, v) in enumerate(rows):
+        s = np.float32(np.uint16(sb).view(np.float16))
+        w[i, 0] = np.float32(8.0) * s
+        w[i, 1] = v
+    codes, sc = oracle.quantize(w)
+    assert np.array_equal(sc[:, 0], np.array([r[0] for r in rows], np.uint16))
+    for i, (sb, v) in enumerate(rows):
+        s = Fraction(float(np.uint16(sb).view(np.float16)))
+        want = min(15, max(0, round(Fraction(float(v)) / s) + 8))
+        assert codes[i, 1] == want, (hex(sb), float(v), codes[i, 1], want)
+    assert np.all(codes[:, 0] == 15) and np.all(codes[:, 2:] == 8)
