@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 4
+#define Q4_ABI_VERSION 5
 
 typedef int32_t q4_status;
 #define Q4_OK 0
@@ -76,13 +76,18 @@ int32_t q4_abi_version(void);
 /* Packing                                                              */
 /* ------------------------------------------------------------------ */
 
-/* codes u8[N][K] (one code per byte; only bits 0..3 are used, higher bits
+/* Packing of 4-bit codes (PIPO, "Method", bullet "Computation
+ * optimization": the product runs on 4-bit quantized weights; the pages fix
+ * no byte layout, so the layout is the reading stated at the top of this
+ * file: two codes per byte, the even column in the low nibble).
+ * codes u8[N][K] (one code per byte; only bits 0..3 are used, higher bits
  * are ignored) -> packed u8[N][K/2] in the layout above.  N >= 1, K >= 2
  * and even.  Bit-exact; no alignment requirement. */
 q4_status q4_pack(const uint8_t *codes, uint8_t *packed, int64_t N, int64_t K,
                   hipStream_t stream);
 
-/* packed u8[N][K/2] -> codes u8[N][K] (each 0..15). */
+/* The inverse of q4_pack (same passage and layout): packed u8[N][K/2] ->
+ * codes u8[N][K] (each 0..15).  Same limits and errors as q4_pack. */
 q4_status q4_unpack(const uint8_t *packed, uint8_t *codes, int64_t N,
                     int64_t K, hipStream_t stream);
 
@@ -97,8 +102,10 @@ q4_status q4_unpack(const uint8_t *packed, uint8_t *codes, int64_t N,
  * optimization" runs on 4-bit weights but gives no rule to produce them;
  * the rule here is symmetric round-to-nearest per group of 32 k):
  *   s = binary16(max|w| / 8) over the group (nearest even);
- *   code = clamp(rint(w / s) + 8, 0, 15), w / s one IEEE binary32 division,
- *   rint ties to even; a group whose s is 0 gets code 8 everywhere.
+ *   code = clamp(rint(w / s) + 8, 0, 15), w / s the exact quotient (one
+ *   IEEE binary32 division decides its rounding exactly for binary32 or
+ *   binary16 w and binary16 s), rint ties to even; a group whose s is 0
+ *   gets code 8 everywhere.
  * The largest positive weight of a group maps to w / s = 8, clipped to 15.
  *   w       device [N][K], row-major, w_dtype Q4_DTYPE_F32 (binary32) or
  *           Q4_DTYPE_F16 (binary16 bit patterns), 16-byte aligned; finite,
@@ -131,42 +138,14 @@ q4_status q4_gemv(const uint8_t *packed, const uint16_t *scales,
  *   with B * K * 2 <= 65536 runs the vector-ALU batch kernel, whose every
  *   column equals q4_gemv of that column bitwise; wider batches run the
  *   matrix-core kernel, whose columns do not depend on B or on the other
- *   columns (bitwise), and differ from q4_gemv within the product bound. */
+ *   columns (bitwise), and differ from q4_gemv within the product bound.
+ *   Every path forms each group's 32 products exactly (the codes as the
+ *   integers -8..7 against binary16 activations), sums them in fp32 and
+ *   scales the sum by the group's scale in fp32, so every finite binary16
+ *   scale, subnormal ones included, is honoured. */
 q4_status q4_gemm_smallbatch(const uint8_t *packed, const uint16_t *scales,
                              const uint16_t *X_f16, float *Y, int64_t N,
                              int64_t K, int32_t B, hipStream_t stream);
-
-/* Tuning variants of the two products, for measurement: the same
- * arithmetic with an explicit launch shape.  q4_gemv_tuned: rows_per_slot
- * and k_split in {1, 2, 4} (rows held by each 16-lane row of a wave, waves
- * sharing one row's k range), chunks_in_flight in {2, 4, 8} (16-byte chunks
- * of each row a lane loads before using them; 2 selects the software-
- * pipelined loop, two register buffers of two chunks with the next batch
- * always in flight, which needs K % (1024 * k_split) == 0 and nontemporal 1,
- * else UNSUPPORTED; at equal rows_per_slot and k_split it gives the same
- * bits as the single-buffer loop), nontemporal 0/1 (weight loads marked
- * non-temporal).  q4_gemm_tuned: row_tiles in {1, 2, 4, 8} and
- * waves in {4, 8, 16} (16-row tiles per workgroup, waves splitting k), with
- * row_tiles 8 only for 4 waves and 4 only up to 8 waves; B == 1 is allowed
- * and runs the matrix-core kernel.
- * INVALID_ARG / UNSUPPORTED for other values. */
-q4_status q4_gemv_tuned(const uint8_t *packed, const uint16_t *scales,
-                        const uint16_t *x_f16, float *y, int64_t N, int64_t K,
-                        int32_t rows_per_slot, int32_t k_split, int32_t chunks_in_flight,
-                        int32_t nontemporal, hipStream_t stream);
-q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
-                        const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
-                        int32_t B, int32_t row_tiles, int32_t waves,
-                        hipStream_t stream);
-
-/* Measurement variant: the vector-ALU batch kernel for B in {2, 3, 4, 8}
- * (8 only here: beyond four columns the library uses the matrix cores),
- * arguments as q4_gemm_smallbatch; needs B * K * 2 <= 65536 (the columns
- * are staged in LDS).  UNSUPPORTED otherwise; every column equals q4_gemv
- * of that column bitwise. */
-q4_status q4_gemm_valu(const uint8_t *packed, const uint16_t *scales,
-                       const uint16_t *X_f16, float *Y, int64_t N, int64_t K,
-                       int32_t B, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* Decode step (PipeLLM, "Layer 1: CUDA Graph Compilation")               */
@@ -307,14 +286,6 @@ q4_status q4_decode_step_eager(void *dec, hipStream_t stream);
  * Synchronises `stream` before returning. */
 q4_status q4_decode_step_profiled(void *dec, hipStream_t stream, float *ms_out,
                                   int32_t capacity, int32_t *n_out);
-/* Average duration in microseconds of one of the four kernels of a layer
- * (which: 0 QKV, 1 O, 2 gate+up, 3 down), launched `reps` times back to back
- * on `stream` between two timing events, cycling through the resident
- * layers so no launch rereads cached weights.  The O and down kernels add
- * into h on every launch: h is clobbered.  QKV is timed without attention.
- * Synchronises `stream`. */
-q4_status q4_decode_kernel_time(void *dec, int32_t which, int32_t reps,
-                                hipStream_t stream, float *avg_us);
 /* One layer, eagerly, with the weights given (e.g. a streamed slot).  With a
  * KV cache, layers driven one at a time must come in order 0..n_layers-1
  * per token (the cache slice follows that order); q4_decoder_set_context

@@ -10,16 +10,20 @@
 // products take over the VALU, so the multiply-adds go to
 // v_mfma_f32_16x16x32_f16 here and the VALU only unpacks.
 //
-// One MFMA covers 16 weight rows x 32 k x 16 batch columns (B padded with
-// zeros).  Lane l supplies row (l % 16) / column (l % 16) and the 8-value k
-// block l / 16.  Lane l holds one whole 16-byte group (32 codes) of its row
-// for the group g0 + l/16 of a "quad" of four groups (loaded by lane
-// 4 * (l % 16) + l / 16 and passed over by ds_bpermute); word p of that
-// group feeds MFMA p.  Because an MFMA then spans four different groups, each
-// weight is scaled on the A side: (code - 8) * scale rounded once to
-// binary16, a relative change below 2^-11 per weight.  The k order inside a
-// word is the unpack order (k0,k4,k1,k5,k2,k6,k3,k7); the activation block is
-// permuted in registers to match.
+// Arithmetic, per group g of 32 k and output (b, n): the matrix op forms
+// t = sum_{k in g} (code - 8) * x_b[k] from exact binary16 operands (the
+// codes enter as the small integers -8..7, never multiplied by the scale in
+// binary16), and the group scale is applied to t in fp32:
+// acc += float(s_g) * t.  So any finite binary16 scale, subnormal ones
+// included, is applied exactly as the batch-1 product applies it.
+//
+// One MFMA covers one group: 16 batch columns (the A operand, B padded with
+// column 0's data, never stored) x 32 k x 16 weight rows (the B operand).
+// Lane l supplies column / row l % 16 and the 8-value k block l / 16, which
+// is word l / 16 of the group (8 codes); the D tile leaves row l % 16 of
+// the weights and batch columns 4 (l / 16) .. +3 in lane l, so every lane
+// needs one scale per group.  The k order inside a word is the unpack order
+// (k0,k4,k1,k5,k2,k6,k3,k7); the activation block is permuted to match.
 #include <algorithm>
 
 #include "q4_internal.h"
@@ -55,14 +59,16 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
     return r;
 }
 
-// 8 codes of one 32-bit word -> 8 scaled binary16 weights in unpack order.
-// `bias` (0x64006400) lives in a VGPR so each pair is one v_and_or_b32.
-__device__ __forceinline__ half8_t dequant_word(uint32_t v, half2_t s2, uint32_t bias) {
+// 8 codes of one 32-bit word -> the 8 exact binary16 values code - 8 in
+// unpack order.  (v & 0x000F000F) | 0x64006400 is the pair (1024 + c0,
+// 1024 + c4); subtracting 1032 is exact.  `bias` (0x64006400) lives in a
+// VGPR so each pair is one v_and_or_b32.
+__device__ __forceinline__ half8_t codes_word(uint32_t v, uint32_t bias) {
     const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    half2_t p0 = (as_h2((v & 0x000F000Fu) | bias) - off) * s2;
-    half2_t p1 = (as_h2(((v >> 4) & 0x000F000Fu) | bias) - off) * s2;
-    half2_t p2 = (as_h2(((v >> 8) & 0x000F000Fu) | bias) - off) * s2;
-    half2_t p3 = (as_h2(((v >> 12) & 0x000F000Fu) | bias) - off) * s2;
+    half2_t p0 = as_h2((v & 0x000F000Fu) | bias) - off;
+    half2_t p1 = as_h2(((v >> 4) & 0x000F000Fu) | bias) - off;
+    half2_t p2 = as_h2(((v >> 8) & 0x000F000Fu) | bias) - off;
+    half2_t p3 = as_h2(((v >> 12) & 0x000F000Fu) | bias) - off;
     uint4 u = {as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
     return __builtin_bit_cast(half8_t, u);
 }
@@ -74,53 +80,62 @@ __device__ __forceinline__ uint4 ntload16(const void *p) {
     return uint4{v.x, v.y, v.z, v.w};
 }
 
-__device__ __forceinline__ uint16_t ntload2(const uint16_t *p) {
-    typedef const __attribute__((address_space(1))) uint16_t global_t;
-    return __builtin_nontemporal_load((global_t *)p);
+__device__ __forceinline__ uint2 gload8(const void *p) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef const __attribute__((address_space(1))) u32x2 global_t;
+    const u32x2 v = *(global_t *)(p);
+    return uint2{v.x, v.y};
 }
 
-// Operands of one group quad as this lane loaded them: for each row tile a
-// 16-byte group of codes and its scale (handed to their matrix-op lane by
-// ds_bpermute before the multiply), and four 16-byte blocks of activations
-// (rearranged through LDS before the multiply).
-template <int RT>
+// Operands of one group quad as this lane loaded them.
+//   w[t]: a 16-byte group of codes of row tile t: group 4q + (l & 3) of
+//         row l >> 2, so each 16-lane quarter of a load reads 64 contiguous
+//         bytes of four rows; mma_quad transposes them through LDS.
+//   s[t]: the scales of this lane's own row (l % 16) of tile t for the four
+//         groups of the quad.  SC8: one 8-byte load, s[t][0] = groups 0|1,
+//         s[t][1] = groups 2|3 (binary16 pairs).  Otherwise one 2-byte load
+//         per group, zero-extended into s[t][p].
+//   x[j]: four 16-byte blocks of activations, rearranged through LDS.
+template <int RT, bool SC8>
 struct Quad {
     uint4 w[RT];
-    uint32_t s[RT]; // binary16 bits, zero-extended (keeps the struct in registers)
+    uint32_t s[RT][SC8 ? 2 : 4];
     uint4 x[4];
-    bool live;      // this lane's matrix-op group exists (false: scale taken as 0)
 };
 
 // Every load is unconditional (addresses clamped into the matrix and into
 // column 0 of X), so the compiler's wait counts stay exact and the next
 // quad's loads remain in flight while the current quad is multiplied.  A
-// group past the last one (K / 32 not a multiple of 4) gets scale 0, which
-// zeroes its weights; a padding column multiplies real activations of column
-// 0 and its outputs are never stored.
+// group past the last one (K / 32 not a multiple of 4, only without SC8)
+// gets scale 0 at its use; a padding column multiplies real activations of
+// column 0 and its outputs are never stored.
 //
 // Activations: a quad covers 256 contiguous bytes (4 groups x 32 halves) of
 // each column.  Load j brings columns 4j .. 4j+3, lane l taking the 16-byte
 // block l % 16 of column 4j + l / 16, so each load instruction reads whole
 // cache lines; `xoff[j]` is the lane's offset (in halves) of that block in
 // the quad at k = 0.
-//
-// Codes and scales: lane l loads group 4q + (l & 3) of row (l >> 2) of each
-// row tile, so each 16-lane quarter of a load reads 64 contiguous bytes of
-// four rows (a lane per row, as the matrix op's operand layout has it,
-// would touch sixteen rows per quarter and four times the cache accesses);
-// mma_quad moves each value to its matrix-op lane.
-template <int RT>
-__device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wrow)[RT],
+template <int RT, bool SC8>
+__device__ __forceinline__ void load_quad(Quad<RT, SC8> &o, const uint8_t *const (&wrow)[RT],
                                           const uint16_t *const (&srow)[RT],
                                           const uint16_t *X16, const uint32_t (&xoff)[4], int q,
-                                          int kq, int wq, int gq, int C) {
-    o.live = q * 4 + kq < C; // the group of this lane's matrix-op operands
+                                          int wq, int gq, int C) {
     const int gw = q * 4 + wq;
     const int gc = gw < C ? gw : C - 1;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         o.w[t] = ntload16(wrow[t] + (size_t)gc * 16);
-        o.s[t] = ntload2(srow[t] + gc);
+        if constexpr (SC8) {
+            const uint2 v = gload8(srow[t] + (size_t)q * 4);
+            o.s[t][0] = v.x;
+            o.s[t][1] = v.y;
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int g = q * 4 + p;
+                o.s[t][p] = gload(srow[t] + (g < C ? g : C - 1));
+            }
+        }
     }
     const int gx = q * 4 + gq;
     const uint32_t xg = (uint32_t)(gx < C ? gx : C - 1) * 32u;
@@ -133,41 +148,70 @@ __device__ __forceinline__ void load_quad(Quad<RT> &o, const uint8_t *const (&wr
 // 16 blocks of data + 1 of padding, so the 16 lanes of a row reading the
 // same block of 16 different columns hit 16 different bank quads.
 constexpr int kXStride = 17;
+// Row stride of the per-wave code tile, in 32-bit words: 16 of data + 2 of
+// padding, so the 32 lanes of a half-wave reading word kq of group p of
+// rows 0..15 touch 32 different banks.
+constexpr int kCStride = 18;
+
+// Binary16 bits -> fp32.
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
 
 // The quad's activations go through the wave's own LDS tile `xs` (column c
-// at xs[c * kXStride], its 256 bytes in k order): the lane writes its four
-// loaded blocks, then reads the four blocks of group kq of its column `rc`.
-// Only this wave touches `xs`, and a wave's LDS operations execute in
-// order, so no workgroup barrier is needed; the wave barriers keep the
-// compiler from moving the reads above the writes or the next quad's writes
-// above these reads.
-// `perm` is the byte address of the loading lane of this lane's operands
-// (row i16, group kq: lane 4 * i16 + kq) for ds_bpermute.
-template <int RT>
-__device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT], uint32_t bias,
-                                         uint4 *xs, int lane, int rc, int kq, int perm) {
+// at xs[c * kXStride], its 256 bytes in k order) and its codes through the
+// wave's code tile `cs` (row r of tile t at cs[(t * 16 + r) * kCStride],
+// word w of group g at +4g + w): each lane writes what it loaded, then
+// reads what its matrix-op lane needs -- for MFMA p (group p of the quad)
+// block 4p + kq of its column and word kq of group p of its row.  Only this
+// wave touches its tiles, and a wave's LDS operations execute in order, so
+// no workgroup barrier is needed; the wave barriers keep the compiler from
+// moving the reads above the writes or the next quad's writes above these
+// reads.
+template <int RT, bool SC8>
+__device__ __forceinline__ void mma_quad(const Quad<RT, SC8> &o, float4_t (&acc)[RT],
+                                         uint32_t bias, uint4 *xs, uint32_t *cs, int lane,
+                                         int rc, int i16, int kq, int q, int C) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         xs[(4 * j + (lane >> 4)) * kXStride + (lane & 15)] = o.x[j];
-    __builtin_amdgcn_wave_barrier();
-    half8_t bop[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-        bop[p] = __builtin_bit_cast(half8_t, permute_block(xs[rc * kXStride + kq * 4 + p]));
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.s[t]);
-        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(o.live ? sb : 0u));
-        const half2_t s2 = {sh, sh};
-        const uint32_t wd[4] = {(uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].x),
-                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].y),
-                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].z),
-                                (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)o.w[t].w)};
+        uint2 *dst = reinterpret_cast<uint2 *>(cs + (t * 16 + (lane >> 2)) * kCStride +
+                                               (lane & 3) * 4);
+        dst[0] = uint2{o.w[t].x, o.w[t].y};
+        dst[1] = uint2{o.w[t].z, o.w[t].w};
+    }
+    __builtin_amdgcn_wave_barrier();
+    half8_t aop[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        aop[p] = __builtin_bit_cast(half8_t, permute_block(xs[rc * kXStride + p * 4 + kq]));
+    uint32_t wd[RT][4];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(wd[p], s2, bias),
-                                                            bop[p], acc[t], 0, 0, 0);
+            wd[t][p] = cs[(t * 16 + i16) * kCStride + p * 4 + kq];
+    __builtin_amdgcn_wave_barrier();
+    const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float sp;
+            if constexpr (SC8)
+                sp = h2f(p & 1 ? o.s[t][p >> 1] >> 16 : o.s[t][p >> 1] & 0xFFFFu);
+            else
+                sp = q * 4 + p < C ? h2f(o.s[t][p]) : 0.0f;
+            const float4_t d =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[p], codes_word(wd[t][p], bias),
+                                                       zero, 0, 0, 0);
+            acc[t][0] = fmaf(sp, d[0], acc[t][0]);
+            acc[t][1] = fmaf(sp, d[1], acc[t][1]);
+            acc[t][2] = fmaf(sp, d[2], acc[t][2]);
+            acc[t][3] = fmaf(sp, d[3], acc[t][3]);
+        }
     }
 }
 
@@ -178,14 +222,37 @@ __device__ __forceinline__ void mma_quad(const Quad<RT> &o, float4_t (&acc)[RT],
 // (silu(g) = g / (1 + exp(-g)), in fp32) instead of the fp32 products.
 enum class GEpi { Store, Acc, SiluPair };
 
-template <int RT, int NW, GEpi E>
+// Row of tile t, row-in-tile rr, for the workgroup starting at row0 (Store,
+// Acc) or unit row0 (SiluPair), clamped into the matrix.
+template <int RT, GEpi E>
+__device__ __forceinline__ int64_t tile_row(int64_t row0, int t, int rr, int64_t N,
+                                            int64_t npair) {
+    int64_t row;
+    if constexpr (E == GEpi::SiluPair) {
+        row = row0 + (t % (RT / 2)) * 16 + rr;
+        row = row < npair ? row : npair - 1;
+        if (t >= RT / 2)
+            row += npair;
+    } else {
+        row = row0 + t * 16 + rr;
+        row = row < N ? row : N - 1;
+    }
+    return row;
+}
+
+template <int RT, int NW, GEpi E, bool SC8>
 __global__ void __launch_bounds__(64 * NW)
 gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
                  int B, uint16_t *__restrict__ M, int64_t npair) {
     static_assert(E != GEpi::SiluPair || RT % 2 == 0, "gate and up tiles come in pairs");
-    __shared__ float4_t red[NW][RT][64];
-    __shared__ uint4 xs_all[NW][16 * kXStride];
+    // Per wave: the activation tile (16 x kXStride blocks) and the code tile
+    // (RT * 16 x kCStride words); after the loop the same memory holds the
+    // k-split partial sums.
+    constexpr int kWaveWords = 16 * kXStride * 4 + RT * 16 * kCStride;
+    constexpr int kTileWords = NW * kWaveWords;
+    constexpr int kRedWords = NW * RT * 64 * 4;
+    __shared__ uint4 lds_raw[((kTileWords > kRedWords ? kTileWords : kRedWords) + 3) / 4];
     const uint32_t bias = vgpr_const(0x64006400u);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -197,36 +264,25 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     // first row (Store, Acc) or first unit (SiluPair) of this workgroup
     const int64_t row0 = (int64_t)blockIdx.x * (E == GEpi::SiluPair ? 8 * RT : 16 * RT);
 
-    const bool bvalid = i16 < B;
-    const int rc = bvalid ? i16 : 0;
+    const int rc = i16 < B ? i16 : 0; // column whose activations this lane supplies
     const int gq = (lane >> 2) & 3;
     const int wq = lane & 3;
-    const int perm = (i16 * 4 + kq) * 4;
     uint32_t xoff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = 4 * j + (lane >> 4);
         xoff[j] = (uint32_t)(c < B ? c : 0) * (uint32_t)K + (uint32_t)(lane & 3) * 8u;
     }
-    uint4 *xs = xs_all[wave];
+    uint32_t *wave_lds = reinterpret_cast<uint32_t *>(lds_raw) + wave * kWaveWords;
+    uint4 *xs = reinterpret_cast<uint4 *>(wave_lds);
+    uint32_t *cs = wave_lds + 16 * kXStride * 4;
 
     const uint8_t *wrow[RT];
     const uint16_t *srow[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        int64_t row;
-        if constexpr (E == GEpi::SiluPair) {
-            const int th = t % (RT / 2);
-            row = row0 + th * 16 + (lane >> 2);
-            row = row < npair ? row : npair - 1;
-            if (t >= RT / 2)
-                row += npair;
-        } else {
-            row = row0 + t * 16 + (lane >> 2);
-            row = row < N ? row : N - 1;
-        }
-        wrow[t] = W + (size_t)row * row_bytes;
-        srow[t] = S + (size_t)row * C;
+        wrow[t] = W + (size_t)tile_row<RT, E>(row0, t, lane >> 2, N, npair) * row_bytes;
+        srow[t] = S + (size_t)tile_row<RT, E>(row0, t, i16, N, npair) * C;
     }
 
     float4_t acc[RT];
@@ -238,57 +294,59 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     // current one is unpacked and multiplied.  Inside the loop both
     // prefetches are unconditional, so the compiler's wait before each
     // multiply covers only the quad it needs.
-    Quad<RT> qa, qb;
+    Quad<RT, SC8> qa, qb;
     int q = wave;
     if (q < nquads) {
-        load_quad<RT>(qa, wrow, srow, X16, xoff, q, kq, wq, gq, C);
+        load_quad<RT, SC8>(qa, wrow, srow, X16, xoff, q, wq, gq, C);
         while (q + 2 * NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, wq, gq, C);
+            load_quad<RT, SC8>(qb, wrow, srow, X16, xoff, q + NW, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0); // issue before waiting for qa
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
-            load_quad<RT>(qa, wrow, srow, X16, xoff, q + 2 * NW, kq, wq, gq, C);
+            mma_quad<RT, SC8>(qa, acc, bias, xs, cs, lane, rc, i16, kq, q, C);
+            load_quad<RT, SC8>(qa, wrow, srow, X16, xoff, q + 2 * NW, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq, perm);
+            mma_quad<RT, SC8>(qb, acc, bias, xs, cs, lane, rc, i16, kq, q + NW, C);
             q += 2 * NW;
         }
         if (q + NW < nquads) {
-            load_quad<RT>(qb, wrow, srow, X16, xoff, q + NW, kq, wq, gq, C);
+            load_quad<RT, SC8>(qb, wrow, srow, X16, xoff, q + NW, wq, gq, C);
             __builtin_amdgcn_sched_barrier(0);
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
-            mma_quad<RT>(qb, acc, bias, xs, lane, rc, kq, perm);
+            mma_quad<RT, SC8>(qa, acc, bias, xs, cs, lane, rc, i16, kq, q, C);
+            mma_quad<RT, SC8>(qb, acc, bias, xs, cs, lane, rc, i16, kq, q + NW, C);
         } else {
-            mma_quad<RT>(qa, acc, bias, xs, lane, rc, kq, perm);
+            mma_quad<RT, SC8>(qa, acc, bias, xs, cs, lane, rc, i16, kq, q, C);
         }
     }
 
     if constexpr (NW > 1) {
+        float4_t *red = reinterpret_cast<float4_t *>(lds_raw); // [NW][RT][64]
+        __syncthreads(); // every wave is done with its tiles
 #pragma unroll
         for (int t = 0; t < RT; ++t)
-            red[wave][t][lane] = acc[t];
+            red[(wave * RT + t) * 64 + lane] = acc[t];
         __syncthreads();
         if (wave != 0)
             return;
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            float4_t v = red[0][t][lane];
+            float4_t v = red[t * 64 + lane];
             for (int w2 = 1; w2 < NW; ++w2)
-                v += red[w2][t][lane];
+                v += red[(w2 * RT + t) * 64 + lane];
             acc[t] = v;
         }
     }
-    // D layout: lane holds rows 4*(lane/16) + 0..3 of column lane % 16.
-    if (!bvalid)
-        return;
+    // D layout: lane holds weight row i16 of each tile for batch columns
+    // 4 * kq + 0..3.
     if constexpr (E == GEpi::SiluPair) {
 #pragma unroll
         for (int t = 0; t < RT / 2; ++t) {
+            const int64_t unit = row0 + t * 16 + i16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t unit = row0 + t * 16 + 4 * kq + e;
-                if (unit < npair) {
+                const int b = 4 * kq + e;
+                if (unit < npair && b < B) {
                     const float g = acc[t][e], up = acc[t + RT / 2][e];
                     const float silu = g / (1.0f + expf(-g));
-                    M[(size_t)i16 * npair + unit] =
+                    M[(size_t)b * npair + unit] =
                         __builtin_bit_cast(uint16_t, (_Float16)(silu * up));
                 }
             }
@@ -296,14 +354,15 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     } else {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
+            const int64_t row = row0 + t * 16 + i16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = row0 + t * 16 + 4 * kq + e;
-                if (row < N) {
+                const int b = 4 * kq + e;
+                if (row < N && b < B) {
                     if constexpr (E == GEpi::Acc)
-                        Y[(size_t)i16 * N + row] += acc[t][e];
+                        Y[(size_t)b * N + row] += acc[t][e];
                     else
-                        Y[(size_t)i16 * N + row] = acc[t][e];
+                        Y[(size_t)b * N + row] = acc[t][e];
                 }
             }
         }
@@ -313,11 +372,11 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
                         int, int, uint16_t *, int64_t);
 
-template <GEpi E>
-GemmFn pick_gemm(int RT, int NW) {
+template <GEpi E, bool SC8>
+GemmFn pick_gemm_sc(int RT, int NW) {
 #define Q4_PICK(rt, nw)                                                          \
     if (RT == rt && NW == nw)                                                    \
-        return gemm_mfma_kernel<rt, nw, E>;
+        return gemm_mfma_kernel<rt, nw, E, SC8>;
     if constexpr (E == GEpi::SiluPair) {
         Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
     } else {
@@ -327,6 +386,15 @@ GemmFn pick_gemm(int RT, int NW) {
     }
 #undef Q4_PICK
     return nullptr;
+}
+
+// The scales of a row quad are read with one 8-byte load when every row's
+// scale array starts 8-byte aligned (K / 32 a multiple of 4 and an aligned
+// base), else one 2-byte load per group.
+template <GEpi E>
+GemmFn pick_gemm(int RT, int NW, int64_t K, const uint16_t *scales) {
+    const bool sc8 = (K / 32) % 4 == 0 && aligned(scales, 8);
+    return sc8 ? pick_gemm_sc<E, true>(RT, NW) : pick_gemm_sc<E, false>(RT, NW);
 }
 
 // Row tiles per wave for a product of N rows and B columns, from a sweep
@@ -357,7 +425,8 @@ int pick_row_tiles(int64_t N, int32_t B) {
 q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
                                const uint16_t *X16, float *Y, int64_t N, int64_t K,
                                int32_t B, int RT, int NW, hipStream_t stream, bool accumulate) {
-    GemmFn fn = accumulate ? pick_gemm<GEpi::Acc>(RT, NW) : pick_gemm<GEpi::Store>(RT, NW);
+    GemmFn fn = accumulate ? pick_gemm<GEpi::Acc>(RT, NW, K, scales)
+                             : pick_gemm<GEpi::Store>(RT, NW, K, scales);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no kernel for row_tiles=%d waves=%d", RT, NW);
     const int64_t blocks = (N + 16 * RT - 1) / (16 * RT);
@@ -391,7 +460,7 @@ q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
                                  stream);
     }
     const int RT = std::max(2, pick_row_tiles(2 * npair, B));
-    GemmFn fn = pick_gemm<GEpi::SiluPair>(RT, kGemmWaves);
+    GemmFn fn = pick_gemm<GEpi::SiluPair>(RT, kGemmWaves, K, scales);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no paired kernel for row_tiles=%d", RT);
     const int64_t blocks = (npair + 8 * RT - 1) / (8 * RT);

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "q4.h"
+#include "q4_measure.h"
 
 namespace q4 {
 

@@ -13,13 +13,14 @@ import pytest
 import int4_weight_streaming_q4_amd as q4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q4.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 INVALID, UNSUPPORTED, STATE = 1, 2, 4
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(
         r"^\s*(?:q4_status|const char \*|int32_t)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
@@ -31,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 20, names
     for n in names:
         assert hasattr(L, n), n
-    assert q4.abi_version() == 4
+    assert q4.abi_version() == 5
+    assert {"q4_gemv_tuned", "q4_wstream_copy_times", "q4_pack"} <= set(names)
 
 
 def _err():

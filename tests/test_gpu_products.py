@@ -277,6 +277,42 @@ def test_gemm_workload_shapes_sampled_rows(name, B):
         assert_within(Y[b][rows], y_ref, mag, f"{name} B={B} col {b}")
 
 
+@pytest.mark.parametrize("B", [5, 16])
+def test_gemm_special_values(B):
+    """Matrix-core path (B >= 5): the codes enter the matrix op as exact
+    integers and each group's scale is applied in fp32, so the all-8 zero
+    point gives exactly 0, subnormal, zero and the largest binary16 scales
+    stay within the product bound, and an impulse column is exact."""
+    N, K = 80, 512
+    X = inputs.act_f16((B, K), 930 + B, device=DEV)
+    packed = torch.full((N, K // 2), 0x88, dtype=torch.uint8, device=DEV)
+    scales = inputs.scales(N, K, 931).to(DEV)
+    Y = _gemm(packed, scales, X)
+    assert np.all(Y == 0.0)
+    small = _f16(np.random.default_rng(2).standard_normal((B, K)) * 1e-3).to(DEV)
+    # codes all 0 / all 15 / mixed; scales: least subnormal, largest subnormal,
+    # zero, 8188 (8 * 8188 = 65504), 8192 and 65504 (the largest binary16)
+    for byte, sbits in [(0x00, 0x0001), (0xFF, 0x03FF), (0x00, 0x0000), (0x00, 0x6FFF),
+                        (0xFF, 0x7000), (0x00, 0x7BFF), (0x5A, 0x7BFF), (0x5A, 0x3C00)]:
+        packed = torch.full((N, K // 2), byte, dtype=torch.uint8, device=DEV)
+        sc = torch.full((N, K // 32), sbits, dtype=torch.int16, device=DEV)
+        Xs = small if sbits >= 0x6FFF else X
+        Y = _gemm(packed, sc, Xs)
+        assert np.all(np.isfinite(Y)), (byte, sbits)
+        Y_ref, M = oracle.gemm(u8(packed), u16(sc), u16(Xs))
+        for b in range(B):
+            assert_within(Y[b], Y_ref[b], M[b], f"B={B} byte {byte:#x} scale {sbits:#x} col {b}")
+    # impulse columns: column b is e_k for its own k, one exact product
+    packed, scales = _mat(N, K, 932)
+    ks = [0, 1, 4, 7, 31, 32, 200, 255, 256, 300, 411, 480, 481, 499, 510, 511][:B]
+    E = np.zeros((B, K))
+    for b, k in enumerate(ks):
+        E[b, k] = 1.0
+    Y = _gemm(packed, scales, _f16(E).to(DEV))
+    Y_ref, _ = oracle.gemm(u8(packed), u16(scales), u16(_f16(E)))
+    assert np.array_equal(Y.astype(np.float64), Y_ref)
+
+
 def _valu_path(B, K):
     """The library's rule: 2 <= B <= 4 columns whose binary16 copies fit 64 KB
     of LDS run the vector-ALU batch kernel; wider batches the matrix cores."""
@@ -321,11 +357,14 @@ def test_gemm_columns_independent_of_batch(name):
                                  (700, 14336)])
 @pytest.mark.parametrize("B", [2, 3, 4, 8])
 def test_gemm_valu_columns_are_gemv(N, K, B):
-    if B * K * 2 > 65536:
-        pytest.skip("the columns do not fit the 64 KB LDS stage (UNSUPPORTED by design)")
     packed, scales = _mat(N, K, 91)
     X = inputs.act_f16((B, K), 92, device=DEV)
     Y = torch.empty(B, N, dtype=torch.float32, device=DEV)
+    if B * K * 2 > 65536:
+        # the columns do not fit the 64 KB LDS stage: refused before any launch
+        with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
+            q4.q4_gemm_valu(packed, scales, X, Y)
+        return
     q4.q4_gemm_valu(packed, scales, X, Y)
     sync()
     Yh = Y.cpu().numpy()
