@@ -595,9 +595,12 @@ def bench_70b_offload(args, q4, inputs, torch):
     """70B weights in 80 pinned host blobs (one merged blob per layer),
     streamed through two device slots on a copy stream while the compute
     stream runs each layer.  Reports the host->device link peak (best pinned
-    copy of one blob), achieved H2D GB/s, the overlap fraction
-    (T_copy + T_compute - T_wall) / min(T_copy, T_compute) with T_copy the
-    80 copies alone and T_compute the 80 layers alone, and tokens/s."""
+    copy of one blob), achieved H2D GB/s, tokens/s and the overlap fraction
+    (sum T_copy + sum T_compute - T_wall) / min(sum T_copy, sum T_compute):
+    T_copy per layer from timing events the weight stream records where each
+    copy starts (after the wait for its slot) and ends, T_compute the 80
+    layers computed alone from resident slots, T_wall the streamed tokens
+    (1 = compute fully hidden behind the copies, 0 = serial)."""
     dims, n_layers = make_70b(q4, inputs, torch)
     steps = args.steps if args.steps != 256 else 64
     warmup = args.warmup if args.warmup != 8 else 2
@@ -634,53 +637,90 @@ def bench_70b_offload(args, q4, inputs, torch):
             copy_s.synchronize()
             best = min(best, e0.elapsed_time(e1))
     link_gbs = blob_bytes / (best * 1e-3) / 1e9
-    # copies alone
+    # copies alone, back to back
     with torch.cuda.stream(copy_s):
         e0.record(copy_s)
         for l in range(n_layers):
             slots[l % 2].copy_(blobs[l], non_blocking=True)
         e1.record(copy_s)
         copy_s.synchronize()
-    t_copy = e0.elapsed_time(e1)
+    t_copy_b2b = e0.elapsed_time(e1)
     h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
     ws = torch.zeros(q4.workspace_bytes(dims, n_layers), dtype=torch.uint8, device="cuda")
     dec = q4.Decoder(dims, None, h, ws, n_layers=n_layers)
-    # compute alone: the 80 layers from the two resident slots
+    # compute alone: the 80 layers from the two resident slots (after one
+    # untimed pass, so first-launch costs are not counted)
     slot_layers = [q4.layer_from_blob(dims, s.data_ptr()) for s in slots]
     h.copy_(inputs.residual_f32(dims["d"], inputs.seed_of(4, 0, 9), device="cuda"))
     torch.cuda.synchronize()
     with torch.cuda.stream(comp_s):
+        for l in range(n_layers):
+            dec.layer(slot_layers[l % 2], comp_s)
         e0.record(comp_s)
         for l in range(n_layers):
             dec.layer(slot_layers[l % 2], comp_s)
         e1.record(comp_s)
         comp_s.synchronize()
     t_compute = e0.elapsed_time(e1)
-    print(f"[config 5] link peak {link_gbs:.1f} GB/s, copies alone {t_copy:.1f} ms, "
+    print(f"[config 5] link peak {link_gbs:.1f} GB/s, copies alone {t_copy_b2b:.1f} ms, "
           f"compute alone {t_compute:.2f} ms", file=sys.stderr, flush=True)
-    wstream = q4.WeightStream(blobs, slots, copy_s)
     h0 = [inputs.residual_f32(dims["d"], inputs.seed_of(4, t, 9), device="cuda")
           for t in range(steps + warmup)]
-    torch.cuda.synchronize()
-    with torch.cuda.stream(comp_s):
-        for t in range(warmup):
-            h.copy_(h0[t], non_blocking=True)
-            dec.token_streamed(wstream, comp_s)
-        comp_s.synchronize()
-        copy_s.synchronize()
-        t0 = time.perf_counter()
-        e0.record(comp_s)
-        for t in range(warmup, warmup + steps):
-            h.copy_(h0[t], non_blocking=True)
-            dec.token_streamed(wstream, comp_s)
-        e1.record(comp_s)
-        comp_s.synchronize()
-        wall = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    t_wall = e0.elapsed_time(e1) / steps
+
+    def streamed(ws_obj, n_tok, n_timed_tok=0):
+        """(ms per token over n_tok timed tokens, overlap figures or None)."""
+        with torch.cuda.stream(comp_s):
+            for t in range(warmup):
+                h.copy_(h0[t % len(h0)], non_blocking=True)
+                dec.token_streamed(ws_obj, comp_s)
+            comp_s.synchronize()
+            copy_s.synchronize()
+            e0.record(comp_s)
+            for t in range(n_tok):
+                h.copy_(h0[(warmup + t) % len(h0)], non_blocking=True)
+                dec.token_streamed(ws_obj, comp_s)
+            e1.record(comp_s)
+            comp_s.synchronize()
+        ms = e0.elapsed_time(e1) / n_tok
+        ov = None
+        if n_timed_tok:
+            # instrumented tokens: per-copy start and end events
+            n_str = sum(1 for b in ws_obj._keep[0] if b is not None)
+            ws_obj.set_timing(n_str * n_timed_tok + 1)
+            with torch.cuda.stream(comp_s):
+                e0.record(comp_s)
+                for t in range(n_timed_tok):
+                    h.copy_(h0[t % len(h0)], non_blocking=True)
+                    dec.token_streamed(ws_obj, comp_s)
+                e1.record(comp_s)
+                comp_s.synchronize()
+            starts, ends = ws_obj.copy_times(n_str * n_timed_tok + 1)
+            ws_obj.set_timing(0)
+            wall = e0.elapsed_time(e1)
+            # the copies that belong to these tokens: the first was begun by
+            # the token before them (prefetch), the last begins the next token
+            k = n_str * n_timed_tok
+            sum_copy = sum(e - s for s, e in zip(starts[:k], ends[:k]))
+            sum_comp = t_compute * n_timed_tok  # every layer streamed here
+            gaps = sorted(starts[i + 1] - ends[i] for i in range(k - 1))
+            ov = {"tokens": n_timed_tok, "wall_ms": round(wall, 3),
+                  "sum_copy_ms": round(sum_copy, 3),
+                  "sum_compute_ms": round(sum_comp, 3),
+                  "overlap_fraction": round((sum_copy + sum_comp - wall) /
+                                            min(sum_copy, sum_comp), 4),
+                  "copy_ms_median": round(sorted(e - s for s, e in zip(starts[:k], ends[:k]))[k // 2], 4),
+                  "copy_gap_us_median": round(1000 * gaps[len(gaps) // 2], 2) if gaps else None,
+                  "copy_gap_us_max": round(1000 * gaps[-1], 2) if gaps else None}
+        torch.cuda.synchronize()
+        return ms, ov
+
+    wstream = q4.WeightStream(blobs, slots, copy_s)
+    t0 = time.perf_counter()
+    t_wall, ov1 = streamed(wstream, steps, n_timed_tok=4)
+    wall = time.perf_counter() - t0
+    wstream.close()
     tps = 1000.0 / t_wall
     h2d = blob_bytes * n_layers * tps / 1e9
-    overlap = (t_copy + t_compute - t_wall) / min(t_copy, t_compute)
     res = base_result("70B-shape offload decode tokens/s (pinned host -> 2-slot HBM pool)",
                       round(tps, 4), "tokens/s", steps, warmup,
                       "llama3-70b-shaped INT4 decode, batch 1, 80 layers streamed per token "
@@ -688,41 +728,29 @@ def bench_70b_offload(args, q4, inputs, torch):
                       {"ms_per_step": round(t_wall, 3), "wall_s_timed": round(wall, 3),
                        "h2d_gbps": round(h2d, 2), "link_peak_gbps": round(link_gbs, 2),
                        "frac_of_link_peak": round(h2d / link_gbs, 4),
-                       "t_copy_ms": round(t_copy, 3), "t_compute_ms": round(t_compute, 3),
-                       "overlap_fraction": round(overlap, 4),
+                       "t_copy_back_to_back_ms": round(t_copy_b2b, 3),
+                       "t_compute_ms": round(t_compute, 3),
+                       "overlap_fraction": ov1["overlap_fraction"],
+                       "overlap": ov1,
                        "roofline": {"bound": "host-to-device link", "kernel": "H2D layer copies",
                                     "achieved": round(h2d, 2), "peak": round(link_gbs, 2),
                                     "unit": "GB/s", "frac": round(h2d / link_gbs, 4),
                                     "traffic": None}})
-    wstream.close()
-
-    def streamed_rate(ws, n_tok):
-        with torch.cuda.stream(comp_s):
-            for t in range(warmup):
-                h.copy_(h0[t], non_blocking=True)
-                dec.token_streamed(ws, comp_s)
-            comp_s.synchronize()
-            e0.record(comp_s)
-            for t in range(n_tok):
-                h.copy_(h0[(warmup + t) % len(h0)], non_blocking=True)
-                dec.token_streamed(ws, comp_s)
-            e1.record(comp_s)
-            comp_s.synchronize()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n_tok
+    print(f"[config 5] one copy stream: {t_wall:.2f} ms/token, {h2d:.2f} GB/s, "
+          f"overlap {ov1}", file=sys.stderr, flush=True)
 
     # the same stream in 32 MB pieces alternating over two copy streams
     copy2_s = torch.cuda.Stream()
     chunk = 32 << 20
     ws2 = q4.WeightStream(blobs, slots, copy_s, copy2=copy2_s, chunk_bytes=chunk)
-    ms2 = streamed_rate(ws2, steps)
+    ms2, ov2 = streamed(ws2, max(4, steps // 4), n_timed_tok=2)
     ws2.close()
     variants = {"one_copy_stream_whole_blobs": {"ms_per_token": round(t_wall, 3),
                                                 "tokens_per_s": round(tps, 4),
                                                 "h2d_gbps": round(h2d, 2)},
                 "two_copy_streams_32MB_pieces": {
                     "ms_per_token": round(ms2, 3), "tokens_per_s": round(1000.0 / ms2, 4),
-                    "h2d_gbps": round(blob_bytes * n_layers / ms2 / 1e6, 2)}}
+                    "h2d_gbps": round(blob_bytes * n_layers / ms2 / 1e6, 2), "overlap": ov2}}
     # partial residency: a budget of 40 layer blobs of HBM, placed by
     # q4_offload_plan (two slots + 38 resident layers spread over the depth)
     budget = 40 * blob_bytes
@@ -730,8 +758,8 @@ def bench_70b_offload(args, q4, inputs, torch):
     resident = [blobs[l].to("cuda") if m else None for l, m in enumerate(mask)]
     torch.cuda.synchronize()
     ws3 = q4.WeightStream([None if m else b for b, m in zip(blobs, mask)], slots, copy_s,
-                          copy2=copy2_s, chunk_bytes=chunk, resident=resident)
-    ms3 = streamed_rate(ws3, max(4, steps // 2))
+                          resident=resident)
+    ms3, _ = streamed(ws3, max(4, steps // 4))
     ws3.close()
     n_str = n_layers - sum(mask)
     variants[f"resident_{sum(mask)}_of_{n_layers}_budget_40_blobs"] = {

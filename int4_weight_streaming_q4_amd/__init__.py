@@ -110,6 +110,10 @@ def lib() -> ctypes.CDLL:
         "weight_stream_wait": (S, [_P, _I32, _P, ctypes.POINTER(_P)]),
         "q4_wstream_destroy": (S, [_P]),
         "q4_decode_token_streamed": (S, [_P, _P, _P]),
+        "q4_wstream_set_timing": (S, [_P, _I32]),
+        "q4_wstream_copy_times": (S, [_P, ctypes.POINTER(ctypes.c_float),
+                                      ctypes.POINTER(ctypes.c_float), _I32,
+                                      ctypes.POINTER(_I32)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -397,6 +401,19 @@ class WeightStream:
         _check(lib().weight_stream_wait(self.handle, layer, _stream(compute_stream),
                                         ctypes.byref(out)))
         return out.value
+
+    def set_timing(self, capacity: int):
+        """Record start and end events for the next `capacity` copies."""
+        _check(lib().q4_wstream_set_timing(self.handle, int(capacity)))
+
+    def copy_times(self, capacity: int):
+        """(start_ms, end_ms) lists of the timed copies, relative to the
+        start of the first; waits for the last one."""
+        s = (ctypes.c_float * capacity)()
+        e = (ctypes.c_float * capacity)()
+        n = _I32()
+        _check(lib().q4_wstream_copy_times(self.handle, s, e, capacity, ctypes.byref(n)))
+        return list(s[:n.value]), list(e[:n.value])
 
     def close(self):
         if getattr(self, "handle", None):

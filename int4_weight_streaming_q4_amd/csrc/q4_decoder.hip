@@ -380,7 +380,24 @@ struct WStream {
     hipStream_t consumer[2] = {nullptr, nullptr};
     int64_t n_begun = 0;
     int64_t n_waited = 0;
+    // Copy timing (q4_wstream_set_timing): per timed begin, events where
+    // the copy starts (after the wait for its slot) and ends, on each copy
+    // stream (index 0: copy, 1: copy2).
+    std::vector<hipEvent_t> t_start[2], t_end[2];
+    int32_t n_timed = 0;
 };
+
+void free_timing(WStream *w) {
+    for (int c = 0; c < 2; ++c) {
+        for (hipEvent_t e : w->t_start[c])
+            (void)hipEventDestroy(e);
+        for (hipEvent_t e : w->t_end[c])
+            (void)hipEventDestroy(e);
+        w->t_start[c].clear();
+        w->t_end[c].clear();
+    }
+    w->n_timed = 0;
+}
 
 void destroy_wstream(WStream *w) {
     for (int i = 0; i < 2; ++i) {
@@ -391,6 +408,7 @@ void destroy_wstream(WStream *w) {
         if (w->freed[i])
             (void)hipEventDestroy(w->freed[i]);
     }
+    free_timing(w);
     delete w;
 }
 
@@ -800,6 +818,12 @@ extern "C" q4_status weight_stream_begin(void *wsp, int32_t layer) {
     const size_t piece = w->chunk ? w->chunk : total;
     char *dst = static_cast<char *>(w->slot[s]);
     const char *src = static_cast<const char *>(w->blobs[layer]);
+    const bool timed = w->n_timed < (int32_t)w->t_start[0].size();
+    if (timed) {
+        Q4_HIP(hipEventRecord(w->t_start[0][w->n_timed], w->copy));
+        if (w->copy2)
+            Q4_HIP(hipEventRecord(w->t_start[1][w->n_timed], w->copy2));
+    }
     int k = 0;
     for (size_t off = 0; off < total; off += piece, ++k) {
         const size_t n = std::min(piece, total - off);
@@ -809,6 +833,12 @@ extern "C" q4_status weight_stream_begin(void *wsp, int32_t layer) {
     Q4_HIP(hipEventRecord(w->loaded[s], w->copy));
     if (w->copy2)
         Q4_HIP(hipEventRecord(w->loaded2[s], w->copy2));
+    if (timed) {
+        Q4_HIP(hipEventRecord(w->t_end[0][w->n_timed], w->copy));
+        if (w->copy2)
+            Q4_HIP(hipEventRecord(w->t_end[1][w->n_timed], w->copy2));
+        ++w->n_timed;
+    }
     w->state[s] = q4::kLoading;
     w->layer_in[s] = layer;
     w->consumer[s] = nullptr;
@@ -834,6 +864,61 @@ extern "C" q4_status weight_stream_wait(void *wsp, int32_t layer, hipStream_t co
     w->consumer[s] = compute;
     ++w->n_waited;
     *slot_ptr = w->slot[s];
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_wstream_set_timing(void *wsp, int32_t capacity) {
+    WStream *w = static_cast<WStream *>(wsp);
+    if (!w || capacity < 0)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_set_timing: null stream or capacity < 0");
+    q4::free_timing(w);
+    const int nc = w->copy2 ? 2 : 1;
+    for (int c = 0; c < nc; ++c) {
+        w->t_start[c].assign((size_t)capacity, nullptr);
+        w->t_end[c].assign((size_t)capacity, nullptr);
+        for (int32_t i = 0; i < capacity; ++i) {
+            if (hipEventCreate(&w->t_start[c][i]) != hipSuccess ||
+                hipEventCreate(&w->t_end[c][i]) != hipSuccess) {
+                q4::free_timing(w);
+                return q4::fail(Q4_ERR_HIP, "q4_wstream_set_timing: event creation failed");
+            }
+        }
+    }
+    if (nc == 1) {
+        w->t_start[1].clear();
+        w->t_end[1].clear();
+    }
+    return Q4_OK;
+}
+
+extern "C" q4_status q4_wstream_copy_times(void *wsp, float *start_ms, float *end_ms,
+                                           int32_t capacity, int32_t *n_out) {
+    WStream *w = static_cast<WStream *>(wsp);
+    if (!w || !start_ms || !end_ms || !n_out)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_wstream_copy_times: null argument");
+    const int32_t n = std::min(capacity, w->n_timed);
+    *n_out = 0;
+    if (n <= 0)
+        return Q4_OK;
+    Q4_HIP(hipEventSynchronize(w->t_end[0][n - 1]));
+    if (!w->t_end[1].empty())
+        Q4_HIP(hipEventSynchronize(w->t_end[1][n - 1]));
+    const hipEvent_t ref = w->t_start[0][0];
+    for (int32_t i = 0; i < n; ++i) {
+        float s = 0.0f, e = 0.0f;
+        Q4_HIP(hipEventElapsedTime(&s, ref, w->t_start[0][i]));
+        Q4_HIP(hipEventElapsedTime(&e, ref, w->t_end[0][i]));
+        if (!w->t_start[1].empty()) {
+            float s2 = 0.0f, e2 = 0.0f;
+            Q4_HIP(hipEventElapsedTime(&s2, ref, w->t_start[1][i]));
+            Q4_HIP(hipEventElapsedTime(&e2, ref, w->t_end[1][i]));
+            s = std::min(s, s2);
+            e = std::max(e, e2);
+        }
+        start_ms[i] = s;
+        end_ms[i] = e;
+    }
+    *n_out = n;
     return Q4_OK;
 }
 

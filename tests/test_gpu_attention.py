@@ -7,8 +7,9 @@ forced: after the QKV product and attention of a layer, the oracle attends
 from the GPU's own fp32 QKV output over the same prefilled rows, in fp64.
 
 * the new cache row: V exactly the binary16 rounding of the GPU's V rows, the
-  rotated K within one binary16 ulp of the oracle's plus the fp32 rounding
-  of the rotation's terms (the rotation runs in fp32 on the GPU, in fp64 in
+  rotated K within one binary16 ulp of the oracle's plus 2^-22 times the
+  norm of the rotated pair (three fp32 roundings: the rotation runs in
+  fp32 on the GPU, in fp64 in
   the oracle);
 * the attention output: |o - o_ref| <= 2e-3 * sum_j p_j |v_j| + ulp16(o_ref)
   + 1e-6 per element (the product bound applied to the weighted value sum,
@@ -113,18 +114,26 @@ def check_attention(m, l, pos, what):
     # V row: the binary16 rounding of the GPU's fp32 V
     v32 = qkv[(d["H"] + d["Hkv"]) * d["hd"]:].reshape(d["Hkv"], d["hd"])
     assert np.array_equal(vg, v32.astype(np.float16).view(np.uint16)), f"{what}: V row"
-    # K row: the GPU rotates in fp32 (cos and sin rounded to fp32), the
-    # oracle in fp64; before rounding to binary16 the two differ by at most
-    # a few fp32 roundings of the terms, (|a| + |b|) * 2^-21 for the pair
-    # (a, b) of the element, which can exceed a binary16 ulp where the
-    # rotation cancels; then each side rounds to binary16 (one ulp apart)
+    # K row.  Both sides rotate the same fp32 pair (a, b) by the same angle;
+    # the oracle in fp64, the GPU in fp32 from a table whose cos and sin
+    # were taken in fp64 and rounded to fp32 once.  With u = 2^-24, the GPU
+    # value r of a c - b s (or a s + b c) carries at most three roundings
+    # of relative size u -- the table entry, the product, the difference
+    # (a fused multiply-add only removes one) -- each scaled by a term of
+    # the sum, so |r - R| <= 3u (|a||c| + |b||s|) (1 + 2u)
+    # <= 3u sqrt(a^2 + b^2) (1 + 2u) (Cauchy-Schwarz, c^2 + s^2 = 1); the
+    # fp64 angles and sums of both sides differ by less than 2^-40 of the
+    # same norm.  4u sqrt(a^2 + b^2) covers all of it.  Where the rotation
+    # cancels this exceeds a binary16 ulp of the result; then each side
+    # rounds to binary16, half an ulp each.
     kw = oracle.f16_to_f64(kref[:, pos, :])
     kgot = oracle.f16_to_f64(kg)
     k32 = qkv[d["H"] * d["hd"]:(d["H"] + d["Hkv"]) * d["hd"]].reshape(d["Hkv"], d["hd"])
     half = d["hd"] // 2
-    pair = np.abs(k32[:, :half]).astype(np.float64) + np.abs(k32[:, half:])
-    pair = np.concatenate([pair, pair], axis=1)
-    kbound = f16_ulp(np.maximum(np.abs(kw), np.abs(kgot))) + pair * 2.0 ** -21
+    k64 = k32.astype(np.float64)
+    norm = np.sqrt(k64[:, :half] ** 2 + k64[:, half:] ** 2)
+    norm = np.concatenate([norm, norm], axis=1)
+    kbound = f16_ulp(np.maximum(np.abs(kw), np.abs(kgot))) + norm * 2.0 ** -22
     assert np.all(np.abs(kgot - kw) <= kbound), f"{what}: rotated K row"
     got = oracle.f16_to_f64(oin)
     bound = 2e-3 * mag + f16_ulp(o_ref) + 1e-6
@@ -211,10 +220,12 @@ def test_attention_context_one_is_the_one_token_step():
 def test_attention_step_paths_agree_bitwise():
     """Eager step, graph replays (one graph serves every context length of
     its bucket), layer-by-layer steps and streamed tokens: same residual and
-    same caches bitwise; argument errors reported."""
+    same caches bitwise, the streamed token within rel. L2 1e-2 of the
+    free-running oracle; argument errors reported."""
     dims = VARIANTS["qh2_hd64"]
     n, max_ctx = 3, 200
     layers = [inputs.layer_weights(dims, 32, l, device=DEV) for l in range(n)]
+    host = [{k: (u8(p), u16(sc)) for k, (p, sc) in L.items()} for L in layers]
     m = KVModel(dims, layers, n, max_ctx, prefill_seed=inputs.seed_of(32, 0, 8))
     lw = KVModel(dims, None, n, max_ctx, resident=False, prefill_seed=inputs.seed_of(32, 0, 8))
     st = KVModel(dims, None, n, max_ctx, resident=False, prefill_seed=inputs.seed_of(32, 0, 8))
@@ -247,12 +258,24 @@ def test_attention_step_paths_agree_bitwise():
         assert torch.equal(lw.h.cpu(), h_e), ctx
         assert np.array_equal(lw.cache(), c_e), ctx
         st.reset_cache()
+        c0 = st.cache().copy()
         st.set_h(h0)
         st.dec.set_context(ctx, s)
         st.dec.token_streamed(wstream, s)
         s.synchronize()
         assert torch.equal(st.h.cpu(), h_e), ctx
         assert np.array_equal(st.cache(), c_e), ctx
+        # the streamed token against the free-running oracle from the same caches
+        h = h0.numpy().astype(np.float64)
+        for l in range(n):
+            kc, vc = c0[l, 0].copy(), c0[l, 1].copy()
+            oracle.decode_layer_attn(host[l], dims, h, ctx - 1, kc, vc, None, EPS, BASE)
+            got_k = oracle.f16_to_f64(st.cache()[l, 0, :, ctx - 1])
+            want_k = oracle.f16_to_f64(kc[:, ctx - 1])
+            assert np.linalg.norm(got_k - want_k) <= 1e-2 * np.linalg.norm(want_k), (ctx, l)
+        got = st.h.cpu().numpy().astype(np.float64)
+        rel = float(np.linalg.norm(got - h) / np.linalg.norm(h))
+        assert rel < 1e-2, (ctx, rel)
     copy.synchronize()
     with pytest.raises(q4.Q4Error, match="INVALID_ARG"):
         m.dec.step_graph(max_ctx + 1, s)

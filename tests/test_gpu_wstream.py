@@ -1,5 +1,7 @@
-"""Double-buffered layer streaming: results equal to resident weights bitwise,
-under host-forced stalls of either stream, and ordering errors reported.
+"""Double-buffered layer streaming: results equal to resident weights bitwise
+and within the product bound of the free-running oracle, under host-forced
+stalls of either stream and with every freed slot poisoned, and ordering
+errors reported.
 
 Stalls use torch's spin kernel (torch.cuda._sleep) enqueued on the copy or the
 compute stream; every kernel exits normally.  A missing read-after-write edge
@@ -12,6 +14,7 @@ import pytest
 import torch
 
 import int4_weight_streaming_q4_amd as q4
+import oracle
 from int4_weight_streaming_q4_amd import inputs
 from helpers import DEV, u16, u8
 
@@ -36,6 +39,27 @@ def blobs_for(dims, layers):
             b[offs[2 * i + 1]:offs[2 * i + 1] + sb.numel()] = sb
         out.append(b)
     return out, total
+
+
+def host_layers(layers):
+    return [{k: (u8(p), u16(s)) for k, (p, s) in L.items()} for L in layers]
+
+
+def check_oracle(dims, hl, h0, h_gpu, what):
+    """The streamed residual against the free-running fp64 oracle over the
+    same host layers: per element within 2e-3 * M + 1e-6, M the summed
+    magnitudes of every product added into that element."""
+    h = np.asarray(h0.numpy(), np.float64).copy()
+    mag = np.zeros_like(h)
+    for L in hl:
+        oracle.decode_layer(L, dims, h, mag, EPS)
+    got = np.asarray(h_gpu.numpy(), np.float64)
+    assert np.all(np.isfinite(got)), what
+    bound = 2e-3 * mag + 1e-6
+    err = np.abs(got - h)
+    assert np.all(err <= bound), (
+        f"{what}: {int((err > bound).sum())} elements outside the bound, worst ratio "
+        f"{float((err / bound).max()):.3g}")
 
 
 def resident_tokens(dims, layers, h0s):
@@ -92,9 +116,33 @@ class Streamed:
                 with torch.cuda.stream(cs):
                     torch.cuda._sleep(cycles)
 
-    def token_python(self, stall_copy=0, stall_compute=0, poison=False):
+    def _poison(self, ptr, where):
+        """Fill the slot at `ptr` with 0xFF bytes (codes 15, binary16 NaN
+        scales) right after its last use by the compute stream: on the
+        compute stream itself, or on the copy stream(s) after an event that
+        marks that last use.  Output unchanged iff no read of the slot can
+        see the poison (read-after-write edge) and the poison cannot land on
+        the next layer's copy (write-after-read edge)."""
+        slot = next(s for s in self.slots if s.data_ptr() == ptr)
+        if where == "compute":
+            with torch.cuda.stream(self.compute):
+                slot.fill_(0xFF)
+            return
+        used = torch.cuda.Event()
+        used.record(self.compute)
+        self.copy.wait_event(used)
+        with torch.cuda.stream(self.copy):
+            slot.fill_(0xFF)
+        if self.copy2 is not None:
+            filled = torch.cuda.Event()
+            filled.record(self.copy)
+            self.copy2.wait_event(filled)
+
+    def token_python(self, stall_copy=0, stall_compute=0, poison=None):
         """Same loop driven from Python (every layer streamed), with optional
-        stalls of the copy streams or of the compute stream."""
+        stalls of the copy streams or of the compute stream, and optionally
+        every slot poisoned after its last use ("compute" or "copy": the
+        stream the fill runs on)."""
         n = self.n
         for l in range(n):
             if l == 0 and not getattr(self, "_pref", False):
@@ -108,6 +156,8 @@ class Streamed:
                 with torch.cuda.stream(self.compute):
                     torch.cuda._sleep(stall_compute)
             self.dec.layer(q4.layer_from_blob(self.dims, ptr), self.compute)
+            if poison:
+                self._poison(ptr, poison)
         self.compute.synchronize()
         return self.h.cpu().clone()
 
@@ -121,10 +171,13 @@ def test_streamed_equals_resident(n_layers):
     layers = [inputs.layer_weights(TINY, 95, l, device=DEV) for l in range(n_layers)]
     h0s = _h0s(TINY, 95, 3)
     want = resident_tokens(TINY, layers, h0s)
+    hl = host_layers(layers)
     st = Streamed(TINY, layers)
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
-        assert torch.equal(st.token_native(), want[t]), (n_layers, t)
+        got = st.token_native()
+        assert torch.equal(got, want[t]), (n_layers, t)
+        check_oracle(TINY, hl, h0, got, f"streamed {n_layers} layers token {t}")
 
 
 def test_streamed_under_stalls_equals_resident():
@@ -132,6 +185,7 @@ def test_streamed_under_stalls_equals_resident():
     layers = [inputs.layer_weights(TINY, 96, l, device=DEV) for l in range(n)]
     h0s = _h0s(TINY, 96, 2)
     want = resident_tokens(TINY, layers, h0s)
+    hl = host_layers(layers)
     for kind in ("copy", "compute"):
         st = Streamed(TINY, layers)
         for t, h0 in enumerate(h0s):
@@ -139,6 +193,29 @@ def test_streamed_under_stalls_equals_resident():
             got = st.token_python(stall_copy=2_000_000 if kind == "copy" else 0,
                                   stall_compute=2_000_000 if kind == "compute" else 0)
             assert torch.equal(got, want[t]), (kind, t)
+            check_oracle(TINY, hl, h0, got, f"stalled {kind} token {t}")
+
+
+@pytest.mark.parametrize("copy2,chunk", [(False, 0), (True, 256)])
+@pytest.mark.parametrize("where", ["compute", "copy"])
+def test_poisoned_slots_leave_results_unchanged(where, copy2, chunk):
+    """Every slot is overwritten with 0xFF (NaN scales) as soon as its layer
+    is done, with the copies or the compute stalled: any read of a slot
+    before its copy landed, or a copy landing before the poison, turns the
+    residual into NaN; the tokens stay bitwise equal to resident ones."""
+    n = 5
+    layers = [inputs.layer_weights(TINY, 101, l, device=DEV) for l in range(n)]
+    h0s = _h0s(TINY, 101, 2)
+    want = resident_tokens(TINY, layers, h0s)
+    for stall in ("copy", "compute", None):
+        st = Streamed(TINY, layers, copy2=copy2, chunk=chunk)
+        for t, h0 in enumerate(h0s):
+            st.set_h(h0)
+            got = st.token_python(stall_copy=1_000_000 if stall == "copy" else 0,
+                                  stall_compute=1_000_000 if stall == "compute" else 0,
+                                  poison=where)
+            assert torch.equal(got, want[t]), (where, copy2, stall, t)
+        st.copy.synchronize()
 
 
 def test_wstream_ordering_errors():
@@ -169,7 +246,10 @@ def test_70b_shapes_streamed_equals_resident():
     st = Streamed(dims, layers)
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
-        assert torch.equal(st.token_native(), want[t]), t
+        got = st.token_native()
+        assert torch.equal(got, want[t]), t
+        if t == 0:
+            check_oracle(dims, host_layers(layers), h0, got, "70B shapes streamed, token 0")
 
 
 @pytest.mark.parametrize("mask", [[1, 0, 1, 0, 1, 0], [0, 1, 1, 1, 1, 1], [1, 1, 1, 1, 1, 0],
@@ -185,10 +265,13 @@ def test_partial_residency_equals_resident(mask):
         assert mask == [0, 1, 0, 1, 0, 1]
     h0s = _h0s(TINY, 98, 3)
     want = resident_tokens(TINY, layers, h0s)
+    hl = host_layers(layers)
     st = Streamed(TINY, layers, resident_mask=mask)
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
-        assert torch.equal(st.token_native(), want[t]), (mask, t)
+        got = st.token_native()
+        assert torch.equal(got, want[t]), (mask, t)
+        check_oracle(TINY, hl, h0, got, f"residency {mask} token {t}")
     if any(mask):
         with pytest.raises(q4.Q4Error, match="STATE"):
             st.ws.begin(mask.index(1))                     # a resident layer is not streamed
@@ -201,10 +284,13 @@ def test_chunked_two_streams_equals_resident(copy2, chunk):
     layers = [inputs.layer_weights(TINY, 99, l, device=DEV) for l in range(n)]
     h0s = _h0s(TINY, 99, 3)
     want = resident_tokens(TINY, layers, h0s)
+    hl = host_layers(layers)
     st = Streamed(TINY, layers, copy2=copy2, chunk=chunk)
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
-        assert torch.equal(st.token_native(), want[t]), (copy2, chunk, t)
+        got = st.token_native()
+        assert torch.equal(got, want[t]), (copy2, chunk, t)
+        check_oracle(TINY, hl, h0, got, f"chunked copy2={copy2} chunk={chunk} token {t}")
 
 
 def test_chunked_two_streams_under_stalls():
@@ -234,4 +320,8 @@ def test_70b_shapes_partial_residency_chunked():
     st = Streamed(dims, layers, copy2=True, chunk=32 << 20, resident_mask=[1, 0, 0, 1])
     for t, h0 in enumerate(h0s):
         st.set_h(h0)
-        assert torch.equal(st.token_native(), want[t]), t
+        got = st.token_native()
+        assert torch.equal(got, want[t]), t
+        if t == 0:
+            check_oracle(dims, host_layers(layers), h0, got,
+                         "70B shapes, two resident, two streamed in pieces, token 0")
