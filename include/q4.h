@@ -306,6 +306,29 @@ q4_status q4_decoder_set_context(void *dec, int32_t ctx_len, hipStream_t stream)
  * listed above).  INVALID_ARG for another index or bad shapes. */
 q4_status q4_decode_layer_part(void *dec, const q4_layer *layer, int32_t which,
                                hipStream_t stream);
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: one
+ * decoder layer on the fp32 residual h (device f32[d_model], 16-byte
+ * aligned, in/out) exactly as q4_decode_layer computes it on a decoder
+ * without a KV cache (the same kernels, so the same bits), without a
+ * decoder object or a workspace.  The four intermediates (normed
+ * activation, QKV output, attention output, gated MLP activation) live in
+ * a library-owned static device array of Q4_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends; the call allocates nothing, host or device.
+ * Dimensions as in q4_model_desc; the layer's matrices must have the
+ * decoder's shapes.  INVALID_ARG for bad dimensions, shapes or pointers;
+ * UNSUPPORTED when the intermediates,
+ *   align256(2 max(d_model, d_ff)) + align256(4 (n_heads + 2 n_kv_heads)
+ *   head_dim) + align256(2 n_heads head_dim) + align256(2 d_ff) bytes,
+ * exceed Q4_NOALLOC_SCRATCH_BYTES (the 70B shapes need 172,032).  Every
+ * call on one GPU uses that GPU's single array: calls whose work overlaps
+ * in time on one GPU (streams not ordered with each other) race.  Nothing
+ * in the array needs to start at zero: each call writes every intermediate
+ * before reading it, and the array keeps the last call's values. */
+#define Q4_NOALLOC_SCRATCH_BYTES (256 * 1024)
+q4_status q4_decode_layer_noalloc(const q4_layer *layer, int32_t d_model, int32_t n_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t d_ff,
+                                  float eps, float *h, hipStream_t stream);
 /* Verify step: the first B columns of h_batch (1 <= B <= max_batch), each
  * the residual of one token, go through all resident layers together: per
  * layer, per column RMSNorm to binary16, the QKV, O, gate+up and down

@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
         "weight_stream_wait": (S, [_P, _I32, _P, ctypes.POINTER(_P)]),
         "q4_wstream_destroy": (S, [_P]),
         "q4_decode_token_streamed": (S, [_P, _P, _P]),
+        "q4_decode_layer_noalloc": (S, [ctypes.POINTER(Layer), _I32, _I32, _I32, _I32, _I32,
+                                        ctypes.c_float, _P, _P]),
         "q4_wstream_set_timing": (S, [_P, _I32]),
         "q4_wstream_copy_times": (S, [_P, ctypes.POINTER(ctypes.c_float),
                                       ctypes.POINTER(ctypes.c_float), _I32,
@@ -363,6 +365,15 @@ class Decoder:
             self.close()
         except Exception:
             pass
+
+
+def decode_layer_noalloc(weights, dims: dict, h, eps: float = 1e-5, stream=None):
+    """One decoder layer on the device residual ``h`` with the library's
+    static scratch array (no decoder object, no workspace, no allocation)."""
+    L = weights if isinstance(weights, Layer) else make_layer(weights)
+    _check(lib().q4_decode_layer_noalloc(ctypes.byref(L), dims["d"], dims["H"], dims["Hkv"],
+                                         dims["hd"], dims["dff"], float(eps), _ptr(h),
+                                         _stream(stream)))
 
 
 def decode_step_graph(dec: Decoder, ctx_len: int, stream=None):

@@ -42,14 +42,22 @@ q4_status check_matrix(const void *packed, const void *scales, int64_t N,
 }
 
 int device_cus() {
+    // fixed table per device index (no heap allocation on the launch path)
+    constexpr int kMaxDevices = 64;
     static std::mutex mu;
-    static std::vector<int> cache;
+    static int cache[kMaxDevices] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return 256;
+    if (dev < 0 || dev >= kMaxDevices) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        return cus;
+    }
     std::lock_guard<std::mutex> lk(mu);
-    if ((int)cache.size() <= dev)
-        cache.resize(dev + 1, 0);
     if (cache[dev] == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=

@@ -16,6 +16,7 @@
 // merged into one transfer).  PIPO's three transfer threads become one copy
 // stream plus events: a pinned host->device copy needs no host thread.
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1122,4 +1123,94 @@ extern "C" q4_status q4_decoder_check(void *decp) {
                                     "results are invalid");
     }
     return Q4_OK;
+}
+
+// ------------------------------------------------- allocation-free layer
+// The intermediates of q4_decode_layer_noalloc live in this array: one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept in noalloc_ptr.
+static __device__ __align__(256) uint8_t scratch[Q4_NOALLOC_SCRATCH_BYTES];
+
+namespace q4 {
+namespace {
+
+constexpr int kNoAllocDevices = 64;
+
+// Device address of `scratch` on the current device (nullptr and a status
+// on failure), resolved on the first call per device.
+q4_status noalloc_ptr(uint8_t **out) {
+    static std::mutex mu;
+    static uint8_t *ptr[kNoAllocDevices] = {};
+    int dev = 0;
+    Q4_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kNoAllocDevices)
+        return fail(Q4_ERR_UNSUPPORTED, "q4_decode_layer_noalloc: device index %d >= %d", dev,
+                    kNoAllocDevices);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        Q4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || !aligned(p, 256))
+            return fail(Q4_ERR_HIP, "q4_decode_layer_noalloc: bad scratch address");
+        ptr[dev] = static_cast<uint8_t *>(p);
+    }
+    *out = ptr[dev];
+    return Q4_OK;
+}
+
+// Scratch bytes one layer needs: the normed activation (max(d, dff)
+// binary16 slots), the fp32 QKV output, the binary16 attention output and
+// the binary16 gated MLP activation, each 256-byte aligned.
+size_t noalloc_bytes(const Dims &d) {
+    return align256(std::max(d.d, d.dff) * 2) + align256(d.nqkv * 4) +
+           align256(d.H * d.hd * 2) + align256(d.dff * 2);
+}
+
+} // namespace
+} // namespace q4
+
+extern "C" q4_status q4_decode_layer_noalloc(const q4_layer *layer, int32_t d_model,
+                                             int32_t n_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t d_ff, float eps,
+                                             float *h, hipStream_t stream) {
+    if (!layer || !h)
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer_noalloc: null layer or h");
+    if (!q4::aligned(h, 16))
+        return q4::fail(Q4_ERR_INVALID_ARG, "q4_decode_layer_noalloc: h not 16-byte aligned");
+    q4_model_desc m{};
+    m.n_layers = 1;
+    m.d_model = d_model;
+    m.n_heads = n_heads;
+    m.n_kv_heads = n_kv_heads;
+    m.head_dim = head_dim;
+    m.d_ff = d_ff;
+    m.eps = eps;
+    m.h = h;
+    q4::Dims d;
+    Q4_CHECK(q4::dims_of(&m, &d));
+    Q4_CHECK(q4::check_layer(d, *layer, 0));
+    const size_t need = q4::noalloc_bytes(d);
+    if (need > (size_t)Q4_NOALLOC_SCRATCH_BYTES)
+        return q4::fail(Q4_ERR_UNSUPPORTED,
+                        "q4_decode_layer_noalloc: the layer needs %zu scratch bytes, more than "
+                        "the %d available",
+                        need, Q4_NOALLOC_SCRATCH_BYTES);
+    uint8_t *base = nullptr;
+    Q4_CHECK(q4::noalloc_ptr(&base));
+    // A decoder description on the stack pointing into the scratch array:
+    // the same kernels and arguments as q4_decode_layer's (no KV cache).
+    q4::Decoder dec;
+    dec.desc = m;
+    dec.dims = d;
+    uint8_t *p = base;
+    dec.a16 = reinterpret_cast<uint16_t *>(p);
+    p += q4::align256(std::max(d.d, d.dff) * 2);
+    dec.qkv = reinterpret_cast<float *>(p);
+    p += q4::align256(d.nqkv * 4);
+    dec.oin = reinterpret_cast<uint16_t *>(p);
+    p += q4::align256(d.H * d.hd * 2);
+    dec.mlp = reinterpret_cast<uint16_t *>(p);
+    return q4::enqueue_layer(&dec, *layer, -1, stream);
 }

@@ -155,22 +155,33 @@ KernelFn pick_kernel(Epi e, Pro p, const Cfg &c) {
     return nullptr;
 }
 
+// Resident workgroups per launch of kernel `fn` with `lds` bytes of LDS on
+// the current device, cached in a fixed table (no heap allocation, so the
+// launch path allocates nothing); a full table just recomputes.
 int resident_blocks(KernelFn fn, size_t lds) {
+    struct Entry {
+        KernelFn fn;
+        size_t lds;
+        int dev;
+        int total;
+    };
+    constexpr int kEntries = 512;
     static std::mutex mu;
-    static std::map<std::pair<int, std::pair<void *, size_t>>, int> cache;
+    static Entry cache[kEntries];
+    static int used = 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    auto key = std::make_pair(dev, std::make_pair((void *)fn, lds));
     std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(key);
-    if (it != cache.end())
-        return it->second;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev)
+            return cache[i].total;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, lds) != hipSuccess ||
         nb < 1)
         nb = 1;
-    int total = nb * device_cus();
-    cache[key] = total;
+    const int total = nb * device_cus();
+    if (used < kEntries)
+        cache[used++] = Entry{fn, lds, dev, total};
     return total;
 }
 

@@ -237,6 +237,29 @@ def test_decoder_host_object_and_step_checks():
     assert L.decode_step_graph(None, 100, 1234) == INVALID
 
 
+def test_noalloc_layer_checks():
+    """q4_decode_layer_noalloc validates before touching the device: null
+    or misaligned pointers and wrong shapes are INVALID_ARG, a layer whose
+    intermediates exceed the static scratch array is UNSUPPORTED."""
+    L = q4.lib()
+    buf = 1 << 20
+
+    def layer(d, H, Hkv, hd, dff):
+        M = lambda N, K: q4.Matrix(buf, buf, N, K)
+        return q4.Layer(M((H + 2 * Hkv) * hd, d), M(d, H * hd), M(2 * dff, d), M(d, dff))
+
+    f = L.q4_decode_layer_noalloc
+    lay = layer(64, 4, 2, 16, 96)
+    assert f(None, 64, 4, 2, 16, 96, 1e-5, buf, None) == INVALID
+    assert f(ctypes.byref(lay), 64, 4, 2, 16, 96, 1e-5, None, None) == INVALID
+    assert f(ctypes.byref(lay), 64, 4, 2, 16, 96, 1e-5, buf + 4, None) == INVALID
+    assert f(ctypes.byref(lay), 96, 4, 2, 16, 96, 1e-5, buf, None) == INVALID   # shapes
+    assert f(ctypes.byref(lay), 64, 4, 3, 16, 96, 1e-5, buf, None) == INVALID   # H % Hkv
+    big = layer(32768, 256, 8, 128, 32768)   # 335,872 scratch bytes > 262,144
+    assert f(ctypes.byref(big), 32768, 256, 8, 128, 32768, 1e-5, buf, None) == UNSUPPORTED
+    assert "scratch" in _err()
+
+
 def test_blob_layout_is_aligned_and_ordered():
     offs, total = q4.layer_blob_layout(DIMS)
     sizes = [(128 * 64) // 2, 128 * 2 * 2, 64 * 64 // 2, 64 * 2 * 2,
