@@ -597,10 +597,12 @@ def bench_70b_offload(args, q4, inputs, torch):
     stream runs each layer.  Reports the host->device link peak (best pinned
     copy of one blob), achieved H2D GB/s, tokens/s and the overlap fraction
     (sum T_copy + sum T_compute - T_wall) / min(sum T_copy, sum T_compute):
-    T_copy per layer from timing events the weight stream records where each
-    copy starts (after the wait for its slot) and ends, T_compute the 80
-    layers computed alone from resident slots, T_wall the streamed tokens
-    (1 = compute fully hidden behind the copies, 0 = serial)."""
+    T_copy from timing events the weight stream records where each copy
+    starts (after the wait for its slot) and ends (their union: the time the
+    copy streams were busy), T_compute the 80 layers computed alone from
+    resident slots, T_wall the streamed tokens (1 = compute fully hidden
+    behind the copies, 0 = serial).  q4_decode_token_streamed keeps the host
+    one token ahead of the device at most."""
     dims, n_layers = make_70b(q4, inputs, torch)
     steps = args.steps if args.steps != 256 else 64
     warmup = args.warmup if args.warmup != 8 else 2
@@ -700,15 +702,25 @@ def bench_70b_offload(args, q4, inputs, torch):
             # the copies that belong to these tokens: the first was begun by
             # the token before them (prefetch), the last begins the next token
             k = n_str * n_timed_tok
-            sum_copy = sum(e - s for s, e in zip(starts[:k], ends[:k]))
+            # time the copy streams were busy: the union of the copies'
+            # intervals (with two copy streams a layer's pieces and the next
+            # layer's overlap in time), and the idle gaps between them
+            merged = []
+            for s0, e0_ in sorted(zip(starts[:k], ends[:k])):
+                if merged and s0 <= merged[-1][1]:
+                    merged[-1][1] = max(merged[-1][1], e0_)
+                else:
+                    merged.append([s0, e0_])
+            sum_copy = sum(e - s for s, e in merged)
             sum_comp = t_compute * n_timed_tok  # every layer streamed here
-            gaps = sorted(starts[i + 1] - ends[i] for i in range(k - 1))
+            gaps = sorted(merged[i + 1][0] - merged[i][1] for i in range(len(merged) - 1))
             ov = {"tokens": n_timed_tok, "wall_ms": round(wall, 3),
                   "sum_copy_ms": round(sum_copy, 3),
                   "sum_compute_ms": round(sum_comp, 3),
                   "overlap_fraction": round((sum_copy + sum_comp - wall) /
                                             min(sum_copy, sum_comp), 4),
                   "copy_ms_median": round(sorted(e - s for s, e in zip(starts[:k], ends[:k]))[k // 2], 4),
+                  "copy_busy_intervals": len(merged),
                   "copy_gap_us_median": round(1000 * gaps[len(gaps) // 2], 2) if gaps else None,
                   "copy_gap_us_max": round(1000 * gaps[-1], 2) if gaps else None}
         torch.cuda.synchronize()

@@ -431,7 +431,10 @@ q4_status q4_wstream_destroy(void *ws);
  * (wrapping to the next token's first) begun before l is waited and
  * computed on `compute`.  The blob layout must be q4_layer_blob_layout of
  * the decoder's shapes.  With a KV cache layer l attends over cache slice
- * l at the context length set by q4_decoder_set_context. */
+ * l at the context length set by q4_decoder_set_context.  Returns once the
+ * previous call's work on `compute` has completed, so the host stays at
+ * most one token ahead of the device (deeper queues of copies and
+ * cross-stream waits made the copies slower). */
 q4_status q4_decode_token_streamed(void *dec, void *ws, hipStream_t compute);
 
 #ifdef __cplusplus

@@ -386,6 +386,10 @@ struct WStream {
     // stream (index 0: copy, 1: copy2).
     std::vector<hipEvent_t> t_start[2], t_end[2];
     int32_t n_timed = 0;
+    // End of each q4_decode_token_streamed call on the compute stream: the
+    // next call returns only after the previous token has completed.
+    hipEvent_t tok_done[2] = {nullptr, nullptr};
+    int64_t n_tokens = 0;
 };
 
 void free_timing(WStream *w) {
@@ -408,6 +412,8 @@ void destroy_wstream(WStream *w) {
             (void)hipEventDestroy(w->loaded2[i]);
         if (w->freed[i])
             (void)hipEventDestroy(w->freed[i]);
+        if (w->tok_done[i])
+            (void)hipEventDestroy(w->tok_done[i]);
     }
     free_timing(w);
     delete w;
@@ -785,7 +791,8 @@ extern "C" q4_status q4_wstream_create(const q4_wstream_desc *d, void **ws_out) 
         hipError_t e1 = hipEventCreateWithFlags(&w->loaded[i], hipEventDisableTiming);
         hipError_t e2 = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
         hipError_t e3 = hipEventCreateWithFlags(&w->loaded2[i], hipEventDisableTiming);
-        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+        hipError_t e4 = hipEventCreateWithFlags(&w->tok_done[i], hipEventDisableTiming);
+        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess) {
             q4::destroy_wstream(w);
             return q4::fail(Q4_ERR_HIP, "q4_wstream_create: event creation failed");
         }
@@ -1002,6 +1009,14 @@ extern "C" q4_status q4_decode_token_streamed(void *decp, void *wsp, hipStream_t
         }
         Q4_CHECK(q4::enqueue_layer(dec, layer, l, compute));
     }
+    // Keep the host at most one token ahead of the device: wait for the
+    // previous token's work before returning.  With several tokens of copies
+    // and cross-stream waits queued the copies themselves ran slower
+    // (70B shapes: 688-737 ms per token against 677 with this bound).
+    Q4_HIP(hipEventRecord(w->tok_done[w->n_tokens & 1], compute));
+    if (w->n_tokens > 0)
+        Q4_HIP(hipEventSynchronize(w->tok_done[(w->n_tokens - 1) & 1]));
+    ++w->n_tokens;
     return Q4_OK;
 }
 
