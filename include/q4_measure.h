@@ -38,6 +38,17 @@ q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
                         int32_t B, int32_t row_tiles, int32_t waves,
                         hipStream_t stream);
 
+/* The row-per-wave batch-1 kernel that q4_gemv runs for K <= 4096, with an
+ * explicit launch shape, for K up to 8192: rows_per_wave 2 or 4 (rows a
+ * wave holds at a time), workgroups of four waves (0: one group of rows per
+ * wave, capped at four workgroups per compute unit).  Arguments as q4_gemv;
+ * the rows per wave and the grid do not change any output's bits (for K <=
+ * 4096 they equal q4_gemv's).  UNSUPPORTED for K > 8192, INVALID_ARG for
+ * other values. */
+q4_status q4_gemv_rows_tuned(const uint8_t *packed, const uint16_t *scales,
+                             const uint16_t *x_f16, float *y, int64_t N, int64_t K,
+                             int32_t rows_per_wave, int32_t workgroups, hipStream_t stream);
+
 /* Measurement variant: the vector-ALU batch kernel for B in {2, 3, 4, 8}
  * (8 only here: beyond four columns the library uses the matrix cores),
  * arguments as q4_gemm_smallbatch; needs B * K * 2 <= 65536 (the columns

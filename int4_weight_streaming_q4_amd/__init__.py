@@ -15,7 +15,7 @@ import os
 __all__ = [
     "Q4Error", "lib", "abi_version",
     "q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_smallbatch", "q4_gemv_tuned",
-    "q4_gemm_tuned", "q4_gemm_valu", "Decoder", "WeightStream", "layer_blob_layout",
+    "q4_gemm_tuned", "q4_gemm_valu", "q4_gemv_rows_tuned", "Decoder", "WeightStream", "layer_blob_layout",
     "decode_step_graph", "weight_stream_begin", "weight_stream_wait",
 ]
 
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "q4_gemv_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P]),
         "q4_gemm_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P]),
         "q4_gemm_valu": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _P]),
+        "q4_gemv_rows_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
         "q4_decoder_workspace_bytes": (S, [ctypes.POINTER(ModelDesc),
                                            ctypes.POINTER(ctypes.c_size_t)]),
         "q4_decoder_create": (S, [ctypes.POINTER(ModelDesc), ctypes.POINTER(_P)]),
@@ -202,6 +203,12 @@ def q4_gemv_tuned(packed, scales, x16, y, rows_per_slot, k_split, chunks_in_flig
     _check(lib().q4_gemv_tuned(_ptr(packed), _ptr(scales), _ptr(x16), _ptr(y), N, K,
                                rows_per_slot, k_split, chunks_in_flight, nontemporal,
                                _stream(stream)))
+
+
+def q4_gemv_rows_tuned(packed, scales, x16, y, rows_per_wave, workgroups=0, stream=None):
+    N, K = packed.shape[0], 2 * packed.shape[1]
+    _check(lib().q4_gemv_rows_tuned(_ptr(packed), _ptr(scales), _ptr(x16), _ptr(y), N, K,
+                                    rows_per_wave, workgroups, _stream(stream)))
 
 
 def q4_gemm_valu(packed, scales, X16, Y, stream=None):

@@ -288,6 +288,8 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
 
 q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
                       int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream) {
+    if (gemv_row_fits(K))
+        return launch_gemv_row(packed, scales, xin, pro, N, K, epi, ea, 0, 0, stream);
     const Cfg c = choose_config(epi, pro, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K);
     return launch_gemv_cfg(packed, scales, xin, pro, N, K, epi, ea, c.R, c.KS, c.U, c.NT, c.pipe,
                            stream);

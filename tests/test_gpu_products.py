@@ -132,6 +132,34 @@ def _f16(v):
     return torch.from_numpy(np.asarray(v, np.float64).astype(np.float16).view(np.int16))
 
 
+@pytest.mark.parametrize("N,K", [(1, 32), (65, 2080), (333, 1056), (4133, 4096), (6144, 4096),
+                                 (1000, 8192), (77, 6176)])
+def test_gemv_rows_launch_shapes_bitwise(N, K):
+    """The row-per-wave kernel (q4_gemv's kernel for K <= 4096; up to 8192
+    through the measurement entry): rows per wave (2, 4) and the number of
+    workgroups (1 up to one group per wave) only regroup rows, so every
+    launch shape gives the same bits, for K <= 4096 those of q4_gemv; within
+    the product bound of the oracle (ragged chunk counts: K / 32 not a
+    multiple of 64; three and four chunks per lane read from LDS)."""
+    packed, scales = _mat(N, K, 700 + N % 97 + K % 89)
+    x = inputs.act_f16(K, 701 + K % 83, device=DEV)
+
+    def rows(R, grid):
+        y = torch.empty(N, dtype=torch.float32, device=DEV)
+        q4.q4_gemv_rows_tuned(packed, scales, x, y, R, grid)
+        sync()
+        return y.cpu().numpy()
+
+    ref = rows(2, 0)
+    if K <= 4096:
+        assert np.array_equal(_gemv(packed, scales, x), ref)
+    y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
+    assert_within(ref, y_ref, mag, f"rows kernel {N}x{K}")
+    for R in (2, 4):
+        for grid in (0, 1, 3, 64):
+            assert np.array_equal(rows(R, grid), ref), (N, K, R, grid)
+
+
 def test_gemv_special_values():
     N, K = 48, 256
     g = torch.Generator().manual_seed(5)
