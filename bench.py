@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--cpu-runs", type=int, default=5,
+                    help="single-core oracle runs (one token each) for the CPU baseline")
     ap.add_argument("--step-mode", type=int, default=None, choices=[0, 1, 2, 3],
                     help="decode step implementation: 0 four kernels per layer, 1 persistent, "
                          "2 streaming persistent, 3 streaming workgroups per product "
@@ -186,7 +187,7 @@ def main():
         del ws
         result["with_attention"] = attention_step(args, q4, inputs, torch, dims, layers, h0)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_runs)
     print(json.dumps(result), flush=True)
 
 
@@ -783,25 +784,79 @@ def bench_70b_offload(args, q4, inputs, torch):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(layers, dims, h0, n_tokens):
-    """The fp64 oracle (single thread) on a bounded sample: n_tokens tokens of
-    the same 32-layer model, same weights and inputs."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layers, dims, h0, runs=5):
+    """The fp64 oracle, single-threaded and pinned to one core, on a bounded
+    sample of the same workload: one token through the 32 layers per run,
+    median of `runs` runs (about 20 s), plus the 4096 x 4096 product as ns per
+    weight (median of 5).  Beside it, labelled as a baseline and not as the
+    oracle: the same loops from the oracle's source built with OpenMP
+    (product rows in parallel) on every core this process may use."""
+    import statistics
+
     import numpy as np
     import oracle
     from int4_weight_streaming_q4_amd import inputs
 
     host = [{k: (p.cpu().numpy(), inputs.to_numpy_u16(s)) for k, (p, s) in L.items()}
             for L in layers]
-    t0 = time.perf_counter()
-    for t in range(n_tokens):
-        hh = h0[t].cpu().numpy().astype(np.float64)
-        for L in host:
-            oracle.decode_layer(L, dims, hh)
-    dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 5), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_tokens} token(s) x {len(host)} layers of the same 8B-shaped "
-                      f"model, fp64 single-threaded C, {dt:.1f} s"}
+    N = K = 4096
+    gp = inputs.random_bytes(N, K, inputs.seed_of(1, 0, 0)).numpy()
+    gs = inputs.to_numpy_u16(inputs.scales(N, K, inputs.seed_of(1, 0, 1)))
+    gx = inputs.to_numpy_u16(inputs.act_f16(K, inputs.seed_of(1, 0, 2)))
+    h0s = [h.cpu().numpy().astype(np.float64) for h in h0[:runs]]
+
+    def product_s(all_cores):
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            oracle.gemv(gp, gs, gx, all_cores=all_cores)
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    def token_s(all_cores, n):
+        ts = []
+        for r in range(n):
+            hh = h0s[r % len(h0s)].copy()
+            t0 = time.perf_counter()
+            for L in host:
+                oracle.decode_layer(L, dims, hh, all_cores=all_cores)
+            ts.append(time.perf_counter() - t0)
+        return ts
+
+    allowed = sorted(os.sched_getaffinity(0))
+    pin = allowed[0]
+    os.sched_setaffinity(0, {pin})
+    try:
+        g1 = product_s(False)
+        tok = token_s(False, runs)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    threads = min(len(allowed), int(os.environ.get("OMP_NUM_THREADS", len(allowed))))
+    g1_all = product_s(True)
+    tok_all = token_s(True, 3)
+    med = statistics.median(tok)
+    return {"value": round(1.0 / med, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one token x {len(host)} layers of the same 8B-shaped model per run, "
+                      f"median of {runs} runs; fp64 single-threaded C pinned to cpu {pin}",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "cpus_allowed": len(allowed),
+            "pinned_cpu": pin, "s_per_token_runs": [round(t, 3) for t in tok],
+            "config1_gemv_4096x4096": {"ms_median_of_5": round(1000 * g1, 3),
+                                       "ns_per_weight": round(1e9 * g1 / (N * K), 3)},
+            "all_cores": {"label": "baseline, not the oracle: the oracle's source built with "
+                                   "OpenMP, product rows in parallel",
+                          "threads": threads,
+                          "tokens_per_s": round(1.0 / statistics.median(tok_all), 4),
+                          "config1_ns_per_weight": round(1e9 * g1_all / (N * K), 4)}}
 
 
 if __name__ == "__main__":

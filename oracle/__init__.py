@@ -21,62 +21,88 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q4_oracle.c")
 _LIB = os.path.join(_HERE, "libq4oracle.so")
+_LIB_OMP = os.path.join(_HERE, "libq4oracle_omp.so")
 
 # No fast-math and no contraction: every product and sum rounds once, in the
-# order the source states.
+# order the source states.  The oracle is single-threaded (its one OpenMP
+# pragma is ignored without -fopenmp).
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-          "-fno-fast-math", "-Wall", "-Wextra"]
+          "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unknown-pragmas"]
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc; returns the library path."""
+    """Compile the oracle with gcc (and its all-core baseline build);
+    returns the oracle's library path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
+    build_omp(force)
     return _LIB
 
 
+def build_omp(force: bool = True) -> str:
+    """The same source with -fopenmp: the all-core CPU baseline (product rows
+    split over threads).  Not the oracle; only the benchmark's CPU-baseline
+    leg loads it."""
+    if force or not os.path.exists(_LIB_OMP):
+        tmp = _LIB_OMP + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-fopenmp", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_OMP)
+    return _LIB_OMP
+
+
 _lib = None
+_lib_omp = None
 
 
-def lib() -> ctypes.CDLL:
-    global _lib
+def lib(all_cores: bool = False) -> ctypes.CDLL:
+    """The oracle library; all_cores=True: the OpenMP baseline build."""
+    global _lib, _lib_omp
+    if all_cores:
+        if _lib_omp is None:
+            if not os.path.exists(_LIB_OMP):
+                build_omp(force=False)
+            _lib_omp = _declare(ctypes.CDLL(_LIB_OMP))
+        return _lib_omp
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I = ctypes.c_int64
-        D = ctypes.c_double
-        L.q4o_f16_to_f64.restype = D
-        L.q4o_f16_to_f64.argtypes = [ctypes.c_uint16]
-        L.q4o_f64_to_f16.restype = ctypes.c_uint16
-        L.q4o_f64_to_f16.argtypes = [D]
-        for name, args in {
-            "q4o_f16_to_f64_array": [P, P, I],
-            "q4o_f64_to_f16_array": [P, P, I],
-            "q4o_pack": [P, P, I, I],
-            "q4o_unpack": [P, P, I, I],
-            "q4o_dequant": [P, P, P, I, I],
-            "q4o_gemv": [P, P, P, I, I, P, P],
-            "q4o_gemv_rows": [P, P, P, I, P, I, P, P],
-            "q4o_gemm": [P, P, P, I, I, I, P, P],
-            "q4o_rmsnorm_f16": [P, I, D, P],
-            "q4o_gqa_gather_f16": [P, I, I, I, P],
-            "q4o_silu_mul_f16": [P, I, P],
-            "q4o_decode_layer": [P, P, P, P, I, I, I, I, I, D, P, P],
-            "q4o_rope": [P, I, I, D],
-            "q4o_attention": [P, I, I, I, I, I, D, P, P, P, P],
-            "q4o_decode_layer_attn": [P, P, P, P, I, I, I, I, I, D, I, I, D, P, P, P, P],
-            "q4o_quantize_f32": [P, I, I, P, P],
-            "q4o_quantize_f16": [P, I, I, P, P],
-        }.items():
-            fn = getattr(L, name)
-            fn.restype = None
-            fn.argtypes = args
-        _lib = L
+        _lib = _declare(ctypes.CDLL(_LIB))
     return _lib
+
+
+def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    D = ctypes.c_double
+    L.q4o_f16_to_f64.restype = D
+    L.q4o_f16_to_f64.argtypes = [ctypes.c_uint16]
+    L.q4o_f64_to_f16.restype = ctypes.c_uint16
+    L.q4o_f64_to_f16.argtypes = [D]
+    for name, args in {
+        "q4o_f16_to_f64_array": [P, P, I],
+        "q4o_f64_to_f16_array": [P, P, I],
+        "q4o_pack": [P, P, I, I],
+        "q4o_unpack": [P, P, I, I],
+        "q4o_dequant": [P, P, P, I, I],
+        "q4o_gemv": [P, P, P, I, I, P, P],
+        "q4o_gemv_rows": [P, P, P, I, P, I, P, P],
+        "q4o_gemm": [P, P, P, I, I, I, P, P],
+        "q4o_rmsnorm_f16": [P, I, D, P],
+        "q4o_gqa_gather_f16": [P, I, I, I, P],
+        "q4o_silu_mul_f16": [P, I, P],
+        "q4o_decode_layer": [P, P, P, P, I, I, I, I, I, D, P, P],
+        "q4o_rope": [P, I, I, D],
+        "q4o_attention": [P, I, I, I, I, I, D, P, P, P, P],
+        "q4o_decode_layer_attn": [P, P, P, P, I, I, I, I, I, D, I, I, D, P, P, P, P],
+        "q4o_quantize_f32": [P, I, I, P, P],
+        "q4o_quantize_f16": [P, I, I, P, P],
+    }.items():
+        fn = getattr(L, name)
+        fn.restype = None
+        fn.argtypes = args
+    return L
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -146,14 +172,15 @@ def _check_mat(packed, scales):
     return packed, scales, N, K
 
 
-def gemv(packed, scales, x_f16):
-    """(y, mag): y[n] = sum_k w[n][k] x[k], mag[n] = sum_k |w[n][k] x[k]|."""
+def gemv(packed, scales, x_f16, all_cores=False):
+    """(y, mag): y[n] = sum_k w[n][k] x[k], mag[n] = sum_k |w[n][k] x[k]|.
+    all_cores: the OpenMP baseline build (same result, rows in parallel)."""
     packed, scales, N, K = _check_mat(packed, scales)
     x = _c(x_f16, np.uint16)
     assert x.shape == (K,)
     y = np.empty(N, np.float64)
     m = np.empty(N, np.float64)
-    lib().q4o_gemv(_ptr(packed), _ptr(scales), _ptr(x), N, K, _ptr(y), _ptr(m))
+    lib(all_cores).q4o_gemv(_ptr(packed), _ptr(scales), _ptr(x), N, K, _ptr(y), _ptr(m))
     return y, m
 
 
@@ -268,7 +295,7 @@ class _Mat(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
-def decode_layer(layer, dims, h, mag_h=None, eps=1e-5):
+def decode_layer(layer, dims, h, mag_h=None, eps=1e-5, all_cores=False):
     """Run one decoder layer in place on the fp64 residual ``h``.
 
     ``layer`` maps "qkv", "o", "gate_up", "down" to (packed, scales) numpy
@@ -288,9 +315,9 @@ def decode_layer(layer, dims, h, mag_h=None, eps=1e-5):
     assert h.dtype == np.float64 and h.flags["C_CONTIGUOUS"] and h.shape == (d,)
     if mag_h is not None:
         assert mag_h.dtype == np.float64 and mag_h.shape == (d,)
-    lib().q4o_decode_layer(*(ctypes.addressof(m) for m in mats), d, H, Hkv, hd,
-                           dff, eps, _ptr(h),
-                           _ptr(mag_h) if mag_h is not None else None)
+    lib(all_cores).q4o_decode_layer(*(ctypes.addressof(m) for m in mats), d, H, Hkv, hd,
+                                    dff, eps, _ptr(h),
+                                    _ptr(mag_h) if mag_h is not None else None)
     return h
 
 

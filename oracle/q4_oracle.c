@@ -35,6 +35,11 @@
  * to nearest-even by q4o_f64_to_f16 below.
  *
  * Parity pins for every function live in tests/test_oracle_pins.py.
+ *
+ * Built single-threaded (oracle.build).  Only the CPU-baseline leg of the
+ * benchmark also times an all-core build of this file (oracle.build_omp,
+ * -fopenmp: the product rows split over threads), labelled as a baseline,
+ * never used as the oracle.
  */
 #include <math.h>
 #include <stdint.h>
@@ -204,7 +209,10 @@ static void row_dot(const uint8_t *packed, const uint16_t *scales,
         *m = mag;
 }
 
-/* y[n] = sum_k w[n][k] * x[k] for binary16 x.  mag may be NULL. */
+/* y[n] = sum_k w[n][k] * x[k] for binary16 x.  mag may be NULL.
+ * The oracle is built without OpenMP, so the pragma below does nothing; the
+ * separately labelled all-core CPU baseline compiles this same file with
+ * -fopenmp, which splits the rows (each row's sum is unchanged). */
 void q4o_gemv(const uint8_t *packed, const uint16_t *scales,
               const uint16_t *x_f16, int64_t N, int64_t K,
               double *y, double *mag)
@@ -212,6 +220,7 @@ void q4o_gemv(const uint8_t *packed, const uint16_t *scales,
     double *x = (double *)malloc(sizeof(double) * (size_t)K);
     f16_table_init();
     q4o_f16_to_f64_array(x_f16, x, K);
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
         row_dot(packed, scales, x, K, n, &y[n], mag ? &mag[n] : NULL);
     free(x);
