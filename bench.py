@@ -331,23 +331,27 @@ def kernel_bytes(dims):
             w(d, dff) + 2 * dff + 8 * d]                     # down: gated in, h read + written
 
 
-KERNEL_SOURCES = ["int4_weight_streaming_q4_amd/csrc/q4_gemv.hip",
-                  "int4_weight_streaming_q4_amd/csrc/q4_gemv_core.h",
-                  "int4_weight_streaming_q4_amd/csrc/q4_internal.h"]
+_CSRC = "int4_weight_streaming_q4_amd/csrc/"
+# Source files of the kernels whose counters are committed: the 8B gate+up
+# (K = 4096) runs the row-per-wave kernel, the 70B gate+up (K = 8192) the
+# pipelined product kernel.
+KERNEL_SOURCES_8B = [_CSRC + f for f in ("q4_gemv_row.hip", "q4_gemv_core.h", "q4_lanes.h",
+                                         "q4_internal.h")]
+KERNEL_SOURCES_70B = [_CSRC + f for f in ("q4_gemv.hip", "q4_gemv_core.h", "q4_internal.h")]
 PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
 PMC_SUMMARY_70B = "profiles/gate_up_70b_decode_pmc.md"
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=KERNEL_SOURCES_8B):
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         h.update(open(os.path.join(root, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(summary=PMC_SUMMARY):
+def recorded_traffic(summary=PMC_SUMMARY, files=KERNEL_SOURCES_8B):
     """HBM bytes per gate+up launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
     root = os.path.dirname(os.path.abspath(__file__))
@@ -359,7 +363,7 @@ def recorded_traffic(summary=PMC_SUMMARY):
         if line.startswith("    ") and ":" in line:
             k, v = line.strip().split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(files):
         return None
     try:
         return int(rec["traffic_bytes_per_launch"])
@@ -586,7 +590,7 @@ def bench_70b_resident(args, q4, inputs, torch):
                                     "achieved": round(kb[2] / kern_us[2] / 1e3, 1),
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(kb[2] / kern_us[2] / 1e3 / HBM_PEAK_GBS, 4),
-                                    "traffic": recorded_traffic(PMC_SUMMARY_70B),
+                                    "traffic": recorded_traffic(PMC_SUMMARY_70B, KERNEL_SOURCES_70B),
                                     "bytes_per_launch": kb[2],
                                     "avg_launch_us": round(kern_us[2], 3)}})
     print(json.dumps(res), flush=True)

@@ -38,16 +38,29 @@ q4_status q4_gemm_tuned(const uint8_t *packed, const uint16_t *scales,
                         int32_t B, int32_t row_tiles, int32_t waves,
                         hipStream_t stream);
 
-/* The row-per-wave batch-1 kernel that q4_gemv runs for K <= 4096, with an
- * explicit launch shape, for K up to 8192: rows_per_wave 2 or 4 (rows a
- * wave holds at a time), workgroups of four waves (0: one group of rows per
- * wave, capped at four workgroups per compute unit).  Arguments as q4_gemv;
- * the rows per wave and the grid do not change any output's bits (for K <=
- * 4096 they equal q4_gemv's).  UNSUPPORTED for K > 8192, INVALID_ARG for
- * other values. */
+/* The row-per-wave batch-1 kernel that q4_gemv runs for K <= 4096 (all of
+ * a lane's chunks in flight at once), with an explicit launch shape:
+ * rows_per_wave 2 or 4 (rows a wave holds at a time), workgroups of four
+ * waves (0: one group of rows per wave, capped at four workgroups per
+ * compute unit).  Arguments as q4_gemv; the rows per wave and the grid do
+ * not change any output's bits, which equal q4_gemv's.  UNSUPPORTED for
+ * K > 4096, INVALID_ARG for other values. */
 q4_status q4_gemv_rows_tuned(const uint8_t *packed, const uint16_t *scales,
                              const uint16_t *x_f16, float *y, int64_t N, int64_t K,
                              int32_t rows_per_wave, int32_t workgroups, hipStream_t stream);
+
+/* The phased row-per-wave batch-1 kernel that q4_gemv runs for K > 4096,
+ * with an explicit launch shape: each wave takes rows_per_wave rows and
+ * walks them in phases of chunks_per_phase 16-byte chunks per lane (rows 1
+ * or 2 with 1, 2, 4 or 7 chunks; 4 rows with 2 or 4), the activation read
+ * from LDS; workgroups as in q4_gemv_rows_tuned.  Any K up to Q4_MAX_K;
+ * arguments as q4_gemv.  The launch shape does not change any output's
+ * bits, which equal q4_gemv's (also for K <= 4096).  INVALID_ARG for other
+ * values. */
+q4_status q4_gemv_rowp_tuned(const uint8_t *packed, const uint16_t *scales,
+                             const uint16_t *x_f16, float *y, int64_t N, int64_t K,
+                             int32_t rows_per_wave, int32_t chunks_per_phase,
+                             int32_t workgroups, hipStream_t stream);
 
 /* Measurement variant: the vector-ALU batch kernel for B in {2, 3, 4, 8}
  * (8 only here: beyond four columns the library uses the matrix cores),

@@ -15,7 +15,7 @@ import os
 __all__ = [
     "Q4Error", "lib", "abi_version",
     "q4_pack", "q4_unpack", "q4_gemv", "q4_gemm_smallbatch", "q4_gemv_tuned",
-    "q4_gemm_tuned", "q4_gemm_valu", "q4_gemv_rows_tuned", "Decoder", "WeightStream", "layer_blob_layout",
+    "q4_gemm_tuned", "q4_gemm_valu", "q4_gemv_rows_tuned", "q4_gemv_rowp_tuned", "Decoder", "WeightStream", "layer_blob_layout",
     "decode_step_graph", "weight_stream_begin", "weight_stream_wait",
 ]
 
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "q4_gemm_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P]),
         "q4_gemm_valu": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _P]),
         "q4_gemv_rows_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
+        "q4_gemv_rowp_tuned": (S, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P]),
         "q4_decoder_workspace_bytes": (S, [ctypes.POINTER(ModelDesc),
                                            ctypes.POINTER(ctypes.c_size_t)]),
         "q4_decoder_create": (S, [ctypes.POINTER(ModelDesc), ctypes.POINTER(_P)]),
@@ -209,6 +210,14 @@ def q4_gemv_rows_tuned(packed, scales, x16, y, rows_per_wave, workgroups=0, stre
     N, K = packed.shape[0], 2 * packed.shape[1]
     _check(lib().q4_gemv_rows_tuned(_ptr(packed), _ptr(scales), _ptr(x16), _ptr(y), N, K,
                                     rows_per_wave, workgroups, _stream(stream)))
+
+
+def q4_gemv_rowp_tuned(packed, scales, x16, y, rows_per_wave, chunks_per_phase, workgroups=0,
+                       stream=None):
+    N, K = packed.shape[0], 2 * packed.shape[1]
+    _check(lib().q4_gemv_rowp_tuned(_ptr(packed), _ptr(scales), _ptr(x16), _ptr(y), N, K,
+                                    rows_per_wave, chunks_per_phase, workgroups,
+                                    _stream(stream)))
 
 
 def q4_gemm_valu(packed, scales, X16, Y, stream=None):

@@ -185,9 +185,13 @@ int resident_blocks(KernelFn fn, size_t lds) {
     return total;
 }
 
-// Default launch shape, from back-to-back launch timings of every shape on
-// the decode matrices with their real prologues and epilogues (non-temporal
-// loads won or tied everywhere):
+// Launch shape of this kernel by product shape.  The library runs it only
+// for paired rows (SiluPair) with K > 4096 and their 2..4-column products;
+// every other product runs the row-per-wave kernels of q4_gemv_row.hip,
+// which were faster there.  The shapes below, from back-to-back launch
+// timings of every shape on the decode matrices with their real prologues
+// and epilogues (non-temporal loads won or tied everywhere), remain what
+// the measurement entry q4_gemv_tuned compares against:
 //   * K = 4096: one row per 16-lane row with a 2-way k split (see below);
 //     the paired gate+up rows also prefer a 2-way split (28672 x 4096:
 //     14.5-14.8 vs 15.0-15.5 us);
@@ -288,8 +292,8 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
 
 q4_status launch_gemv(const uint8_t *packed, const uint16_t *scales, const void *xin, Pro pro,
                       int64_t N, int64_t K, Epi epi, const EpiArgs &ea, hipStream_t stream) {
-    if (gemv_row_fits(K))
-        return launch_gemv_row(packed, scales, xin, pro, N, K, epi, ea, 0, 0, stream);
+    if (use_row_kernels(epi, K))
+        return launch_gemv_row(packed, scales, xin, pro, N, K, epi, ea, stream);
     const Cfg c = choose_config(epi, pro, epi == Epi::SiluPair ? 2 * ea.pair_off : N, K);
     return launch_gemv_cfg(packed, scales, xin, pro, N, K, epi, ea, c.R, c.KS, c.U, c.NT, c.pipe,
                            stream);

@@ -262,8 +262,8 @@ q4_status launch_gemv_batch(const uint8_t *packed, const uint16_t *scales, const
     if ((int64_t)B * K * 2 > kBatchStageBytes)
         return fail(Q4_ERR_UNSUPPORTED, "gemv batch: %d columns of K=%lld exceed %d LDS bytes",
                     B, (long long)K, kBatchStageBytes);
-    // K <= 8192: the batch-1 product is the row-per-wave kernel; so is this.
-    if (gemv_row_fits(K))
+    // Where the batch-1 product is a row-per-wave kernel, so is this.
+    if (use_row_kernels(epi, K))
         return launch_gemv_row_batch(packed, scales, X16, N, K, B, epi, ea, stream);
     // The batch-1 kernel's rows per slot and k split for this shape, so each
     // column's summation order is the batch-1 product's.

@@ -101,17 +101,17 @@ q4_status launch_gemv_cfg(const uint8_t *packed, const uint16_t *scales, const v
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
                           int KS, int U, bool NT, bool pipe, hipStream_t stream);
 
-// Products with K <= 4096 (at most two chunks per lane) run the row-per-
-// wave kernels of q4_gemv_row.hip (gemv_row_fits; launch_gemv_row takes K
-// up to 8192): each wave sweeps whole rows, the lane's
-// activation chunks in registers or LDS (batch 1) or the columns in LDS
-// (batch 2..4, 8 for measurement), each column in the batch-1 order.  R:
-// rows per wave and group (0: the default rule), grid: workgroups (0:
-// default).  Other K keep the product kernel of q4_gemv.hip.
-bool gemv_row_fits(int64_t K);
+// The row-per-wave kernels of q4_gemv_row.hip run every product for which
+// use_row_kernels holds (K <= 4096, or any epilogue but SiluPair): each wave
+// sweeps whole rows, its activation chunks in registers or read from LDS
+// (batch 1) or the columns in LDS (batch 2..4, 8 for measurement), each
+// column in the batch-1 order; launch_gemv_row picks the launch shape from
+// the product's.  Paired rows with K > 4096 keep the product kernel of
+// q4_gemv.hip.
+bool use_row_kernels(Epi e, int64_t K);
 q4_status launch_gemv_row(const uint8_t *packed, const uint16_t *scales, const void *xin,
-                          Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea, int R,
-                          int grid, hipStream_t stream);
+                          Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea,
+                          hipStream_t stream);
 q4_status launch_gemv_row_batch(const uint8_t *packed, const uint16_t *scales,
                                 const uint16_t *X16, int64_t N, int64_t K, int32_t B, Epi epi,
                                 const EpiArgs &ea, hipStream_t stream);

@@ -133,31 +133,41 @@ def _f16(v):
 
 
 @pytest.mark.parametrize("N,K", [(1, 32), (65, 2080), (333, 1056), (4133, 4096), (6144, 4096),
-                                 (1000, 8192), (77, 6176)])
+                                 (1000, 8192), (77, 6176), (130, 14368), (9, 28672),
+                                 (260, 32768)])
 def test_gemv_rows_launch_shapes_bitwise(N, K):
-    """The row-per-wave kernel (q4_gemv's kernel for K <= 4096; up to 8192
-    through the measurement entry): rows per wave (2, 4) and the number of
-    workgroups (1 up to one group per wave) only regroup rows, so every
-    launch shape gives the same bits, for K <= 4096 those of q4_gemv; within
+    """The two row-per-wave kernels that q4_gemv runs (all chunks in flight
+    for K <= 4096, phases of chunks for wider K): rows per wave, chunks per
+    phase and the number of workgroups (1 up to one group per wave) only
+    regroup the work, so every launch shape gives q4_gemv's bits; within
     the product bound of the oracle (ragged chunk counts: K / 32 not a
-    multiple of 64; three and four chunks per lane read from LDS)."""
+    multiple of 64; a last phase shorter than the others; K at its
+    maximum)."""
     packed, scales = _mat(N, K, 700 + N % 97 + K % 89)
     x = inputs.act_f16(K, 701 + K % 83, device=DEV)
 
-    def rows(R, grid):
+    def run(fn, *shape):
         y = torch.empty(N, dtype=torch.float32, device=DEV)
-        q4.q4_gemv_rows_tuned(packed, scales, x, y, R, grid)
+        fn(packed, scales, x, y, *shape)
         sync()
         return y.cpu().numpy()
 
-    ref = rows(2, 0)
-    if K <= 4096:
-        assert np.array_equal(_gemv(packed, scales, x), ref)
+    ref = _gemv(packed, scales, x)
     y_ref, mag = oracle.gemv(u8(packed), u16(scales), u16(x))
-    assert_within(ref, y_ref, mag, f"rows kernel {N}x{K}")
-    for R in (2, 4):
-        for grid in (0, 1, 3, 64):
-            assert np.array_equal(rows(R, grid), ref), (N, K, R, grid)
+    assert_within(ref, y_ref, mag, f"q4_gemv {N}x{K}")
+    grids = (0, 1, 3, 64)
+    if K <= 4096:
+        for R in (2, 4):
+            for grid in grids:
+                assert np.array_equal(run(q4.q4_gemv_rows_tuned, R, grid), ref), (N, K, R, grid)
+    else:
+        y = torch.empty(N, dtype=torch.float32, device=DEV)
+        with pytest.raises(q4.Q4Error, match="UNSUPPORTED"):
+            q4.q4_gemv_rows_tuned(packed, scales, x, y, 2, 0)
+    for R, PH in ((1, 1), (1, 2), (1, 4), (1, 7), (2, 1), (2, 2), (2, 4), (2, 7), (4, 2), (4, 4)):
+        for grid in grids:
+            assert np.array_equal(run(q4.q4_gemv_rowp_tuned, R, PH, grid), ref), \
+                (N, K, R, PH, grid)
 
 
 def test_gemv_special_values():
