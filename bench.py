@@ -147,6 +147,7 @@ def main():
     achieved = kbytes[2] / (gu_us * 1e-6) / 1e9
     traffic = recorded_traffic()
     gemv1 = single_gemv(q4, inputs, torch)
+    gemv1["traffic"] = recorded_traffic(PMC_SUMMARY_GEMV1)
 
     result = {
         "metric": "INT4 GEMV HBM GB/s (% of peak) + 8B-shape batch-1 decode tokens/s",
@@ -339,6 +340,7 @@ KERNEL_SOURCES_8B = [_CSRC + f for f in ("q4_gemv_row.hip", "q4_gemv_core.h", "q
                                          "q4_internal.h")]
 KERNEL_SOURCES_70B = [_CSRC + f for f in ("q4_gemv.hip", "q4_gemv_core.h", "q4_internal.h")]
 PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
+PMC_SUMMARY_GEMV1 = "profiles/gemv_4096_config1_pmc.md"
 PMC_SUMMARY_70B = "profiles/gate_up_70b_decode_pmc.md"
 
 
@@ -352,8 +354,8 @@ def kernel_source_hash(files=KERNEL_SOURCES_8B):
 
 
 def recorded_traffic(summary=PMC_SUMMARY, files=KERNEL_SOURCES_8B):
-    """HBM bytes per gate+up launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, summary)
     if not os.path.exists(path):

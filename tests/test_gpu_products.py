@@ -259,24 +259,31 @@ def test_gemm_small_shapes(B, N, K):
         assert_within(Y[b], Y_ref[b], M[b], f"gemm B={B} {N}x{K} col {b}")
 
 
-@pytest.mark.parametrize("rt,nw", [(1, 4), (2, 4), (4, 4), (8, 4), (1, 8), (2, 8), (4, 8),
-                                   (1, 16), (2, 16)])
-def test_gemm_every_launch_shape(rt, nw):
-    N, K, B = 200, 1184, 7  # 37 groups: ragged group quads
-    packed, scales = _mat(N, K, 900)
+GEMM_SHAPES = [(1, 4), (2, 4), (4, 4), (8, 4), (1, 8), (2, 8), (4, 8), (1, 16), (2, 16)]
+
+
+@pytest.mark.parametrize("rt,nw", GEMM_SHAPES)
+@pytest.mark.parametrize("K", [1184, 7584])
+def test_gemm_every_launch_shape(rt, nw, K):
+    """Every built launch shape (row tiles, waves) against the oracle; 37
+    and 237 groups: ragged group quads, and at K = 7584 every wave runs the
+    steady loop of its double buffer as well as the last quads."""
+    N, B = 200, 7
+    packed, scales = _mat(N, K, 900 + K % 7)
     X = inputs.act_f16((B, K), 901, device=DEV)
     Y = _gemm(packed, scales, X, tuned=(rt, nw))
     Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
     for b in range(B):
-        assert_within(Y[b], Y_ref[b], M[b], f"gemm rt={rt} nw={nw} col {b}")
+        assert_within(Y[b], Y_ref[b], M[b], f"gemm rt={rt} nw={nw} K={K} col {b}")
 
 
 @pytest.mark.parametrize("B", [5, 7, 16])
-def test_gemm_row_tiles_do_not_change_bits(B):
+@pytest.mark.parametrize("K", [1184, 7584])
+def test_gemm_row_tiles_do_not_change_bits(B, K):
     """At four waves (the k split every matrix-core launch uses) the row
     tiles per wave only regroup rows: every launch shape gives the same bits,
     and the library's own choice is one of them."""
-    N, K = 300, 1184  # 37 groups: ragged group quads
+    N = 300
     packed, scales = _mat(N, K, 950 + B)
     X = inputs.act_f16((B, K), 951 + B, device=DEV)
     ref = _gemm(packed, scales, X, tuned=(1, 4))
