@@ -339,8 +339,10 @@ _CSRC = "int4_weight_streaming_q4_amd/csrc/"
 KERNEL_SOURCES_8B = [_CSRC + f for f in ("q4_gemv_row.hip", "q4_gemv_core.h", "q4_lanes.h",
                                          "q4_internal.h")]
 KERNEL_SOURCES_70B = [_CSRC + f for f in ("q4_gemv.hip", "q4_gemv_core.h", "q4_internal.h")]
+KERNEL_SOURCES_GEMM = [_CSRC + f for f in ("q4_gemm.hip", "q4_internal.h")]
 PMC_SUMMARY = "profiles/gate_up_8b_decode_pmc.md"
 PMC_SUMMARY_GEMV1 = "profiles/gemv_4096_config1_pmc.md"
+PMC_SUMMARY_GEMM = "profiles/small_batch_gate_up_counters.md"
 PMC_SUMMARY_70B = "profiles/gate_up_70b_decode_pmc.md"
 
 
@@ -526,7 +528,8 @@ def bench_gemm(args, q4, inputs, torch):
                        "roofline": {"bound": "hbm", "kernel": "gate+up 28672x4096, B=16",
                                     "achieved": top["GB/s"], "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": round(top["GB/s"] / HBM_PEAK_GBS, 4),
-                                    "traffic": None}})
+                                    "traffic": recorded_traffic(PMC_SUMMARY_GEMM,
+                                                                KERNEL_SOURCES_GEMM)}})
     print(json.dumps(res), flush=True)
 
 

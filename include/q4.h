@@ -134,7 +134,7 @@ q4_status q4_gemv(const uint8_t *packed, const uint16_t *scales,
 /* Y[b][n] = sum_k w[n][k] * X[b][k] for b < B, n < N.
  *   X_f16 u16[B][K] binary16 (each activation vector contiguous),
  *   16-byte aligned;  Y f32[B][N], 4-byte aligned;  1 <= B <= Q4_MAX_BATCH;
- *   other arguments as q4_gemv.  B == 1 runs the q4_gemv kernel; 2 <= B <= 4
+ *   other arguments as q4_gemv.  B == 1 runs the q4_gemv kernel; 2 <= B <= 3
  *   with B * K * 2 <= 65536 runs the vector-ALU batch kernel, whose every
  *   column equals q4_gemv of that column bitwise; wider batches run the
  *   matrix-core kernel, whose columns do not depend on B or on the other

@@ -63,7 +63,8 @@ q4_status q4_gemv_rowp_tuned(const uint8_t *packed, const uint16_t *scales,
                              int32_t workgroups, hipStream_t stream);
 
 /* Measurement variant: the vector-ALU batch kernel for B in {2, 3, 4, 8}
- * (8 only here: beyond four columns the library uses the matrix cores),
+ * (4 and 8 only here: beyond three columns the library uses the matrix
+ * cores),
  * arguments as q4_gemm_smallbatch; needs B * K * 2 <= 65536 (the columns
  * are staged in LDS).  UNSUPPORTED otherwise; every column equals q4_gemv
  * of that column bitwise. */

@@ -5,7 +5,7 @@
 // Devices, "Method", bullets "Computation optimization" and "Automatic
 // configuration" -- the 4-bit kernel serves batches below 16; a batch of B
 // activation vectors (e.g. a speculative-verify batch) reuses every unpacked
-// weight B times.  Up to four columns (whose binary16 copies fit 64 KB of
+// weight B times.  Up to three columns (whose binary16 copies fit 64 KB of
 // LDS) the dot2 kernel of q4_gemv_batch.hip is faster; beyond that its dot
 // products take over the VALU, so the multiply-adds go to
 // v_mfma_f32_16x16x32_f16 here and the VALU only unpacks.

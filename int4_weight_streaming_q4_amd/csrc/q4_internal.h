@@ -126,7 +126,8 @@ void gemv_shape(Epi e, int64_t N, int64_t K, int *R, int *KS);
 // SiluPair: ea.out16 = M binary16 [B][pair_off].  Kernels exist for B in
 // {2, 3, 4} (and 8 for Store); the staged columns must fit kBatchStageBytes.
 constexpr int kBatchStageBytes = 65536;
-bool gemv_batch_fits(int32_t B, int64_t K); // 2 <= B <= 4 and B * K * 2 <= kBatchStageBytes
+constexpr int kBatchMaxCols = 3; // widest batch the library sends to these kernels
+bool gemv_batch_fits(int32_t B, int64_t K); // 2 <= B <= kBatchMaxCols, B * K * 2 <= kBatchStageBytes
 q4_status launch_gemv_batch(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
                             int64_t N, int64_t K, int32_t B, Epi epi, const EpiArgs &ea,
                             hipStream_t stream);
