@@ -8,6 +8,7 @@
 #pragma once
 
 #include "q4_internal.h"
+#include "q4_lanes.h"
 
 namespace q4 {
 namespace {
@@ -164,12 +165,17 @@ __device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x16, uint4 
 
 __device__ __forceinline__ float eps_of(const EpiArgs &ea) { return ea.eps; }
 
-// Sum over the 64 lanes of a wave; every lane gets the total.
+// Sum over the 64 lanes of a wave; every lane gets the total.  After the
+// row sums, the rows pair up as with lane xor 16 and the half-waves as with
+// lane xor 32, through gfx950's row and half-wave swaps (VALU operations,
+// not LDS permutes); each add takes the same two operands either way, so
+// the bits are those of the xor form.
 __device__ __forceinline__ float wave_sum(float v) {
     v = row16_sum(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const lanes::Rows16 r(v);
+    v = lanes::fa(r.a) + lanes::fa(r.b);
+    const lanes::Halves32 h(v);
+    return lanes::fa(h.a) + lanes::fa(h.b);
 }
 
 template <bool COH>
