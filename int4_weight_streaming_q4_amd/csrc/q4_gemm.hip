@@ -25,6 +25,8 @@
 // needs one scale per group.  The k order inside a word is the unpack order
 // (k0,k4,k1,k5,k2,k6,k3,k7); the activation block is permuted to match.
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "q4_internal.h"
 
@@ -492,8 +494,374 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Activation-resident launch: one workgroup per compute unit holds the whole
+// activation X[B][K] in LDS and walks a contiguous, balanced range of row
+// tiles; used where every compute unit gets four or more tiles (the 28672-row
+// gate+up product: 7 tiles each on 256 units).
+//
+// Staging: direct-to-LDS loads (no registers), each reading 1 KB of one
+// column into a column-major area (column stride 1 mod 8 blocks of 16
+// bytes), then one in-place pass that puts every 8-half block into the
+// matrix op's k order.  A wave then reads group g of its column l % 16,
+// block l / 16, as one 16-byte LDS read without bank conflicts.
+//
+// Waves: 4 NS per workgroup -- four k quarters (wave w takes quads w, w + 4,
+// ... exactly as gemm_mfma_kernel does, and the quarters' partial sums are
+// added in quarter order) times NS sets taking alternate tiles.  Every quad
+// is multiplied with the same operations in the same order as there, so
+// both kernels give the same bits.  What differs is the data movement: the
+// activation is read from the caches once per compute unit instead of once
+// per wave, quad and row block, it needs no per-quad rearranging, and a
+// wave's registers carry only codes and scales, so xres_ring quads of them
+// are in flight.  Paired rows (SiluPair) use tiles of 8 gate rows and the 8
+// up rows of the same units, so their tiles divide as evenly as 8-unit
+// steps allow (14336 units: 1792 tiles).
+// Measured on the 8B gate+up shape (28672 x 4096, µs, against the row-tile
+// launch on the same box): B = 4 23.1 / 24.6, B = 8 21.6 / 24.6, B = 16
+// 23.0 / 25.9.  With one or two tiles per unit (QKV, O) one workgroup per
+// unit has too little to hide its staging (O at B = 16: 11 µs against 6.7),
+// so those keep the row-tile launch.
+//
+// LDS: [0, xa) the activation; then one code tile per wave; then the
+// partial sums of every tile but the sets' last ones, per k quarter (the
+// last tiles' stay in registers and go through the activation area at the
+// end).
+constexpr int kXresWaves = 4; // the k split, as in gemm_mfma_kernel
+constexpr int kCTileBytes = 16 * kCStride * 4;
+// Blocks per staged activation column: the column's 4 C blocks plus 1..8
+// of padding, so that consecutive columns start 16 bytes further along the
+// LDS banks (stride = 1 mod 8 blocks) and the 16 columns one matrix-op read
+// touches fall into different banks.
+__host__ __device__ constexpr int xres_col_blocks(int C) {
+    return C * 4 + ((1 - C * 4) % 8 + 8) % 8;
+}
+constexpr int kPartBytes = 64 * 16;
+// NS wave sets take tiles set, set + NS, ...; quads in flight per wave
+// (registers: two sets may hold 256 VGPRs a wave, four 128).
+template <int NS>
+constexpr int xres_ring() {
+    return NS <= 2 ? 8 : 4;
+}
+// Four sets (16 waves, four per SIMD) measured ahead of two on the gate+up
+// shape (B = 4: 23.7 against 25.4 µs, B = 8: 22.4 against 23.2).
+constexpr int kXresSetsUsed = 4;
+
+// Codes and scales of one quad for one lane, as gemm_mfma_kernel loads them
+// for one row tile (lane l: group 4q + l % 4 of tile row l / 4; the scales
+// of tile row l % 16).
+template <bool SC8>
+struct WSlot {
+    uint4 w;
+    uint32_t s[SC8 ? 2 : 4];
+};
+
+// Matrix row of tile row rr (0..15) of tile t, clamped into the matrix.
+// SiluPair: rows 0..7 gate rows of units 8t .. 8t+7, rows 8..15 their up
+// rows (npair further on).
+template <GEpi E>
+__device__ __forceinline__ int64_t xres_row(int64_t t, int rr, int64_t N, int64_t npair) {
+    if constexpr (E == GEpi::SiluPair) {
+        int64_t unit = t * 8 + (rr & 7);
+        unit = unit < npair ? unit : npair - 1;
+        return rr >= 8 ? unit + npair : unit;
+    } else {
+        const int64_t row = t * 16 + rr;
+        return row < N ? row : N - 1;
+    }
+}
+
+template <bool SC8>
+__device__ __forceinline__ void xres_load(WSlot<SC8> &o, const uint8_t *wrow,
+                                          const uint16_t *srow, int q, int wq, int C) {
+    const int gw = q * 4 + wq;
+    o.w = ntload16(wrow + (size_t)(gw < C ? gw : C - 1) * 16);
+    if constexpr (SC8) {
+        const uint2 v = gload8(srow + (size_t)q * 4);
+        o.s[0] = v.x;
+        o.s[1] = v.y;
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int g = q * 4 + p;
+            o.s[p] = gload(srow + (g < C ? g : C - 1));
+        }
+    }
+}
+
+// A quad's operands after staging: the raw activation blocks, the code
+// words of the matrix-op lanes and the group scales already widened to fp32
+// (the exact conversion compute_quad applies; done here, it consumes the
+// loaded scale registers in the step that waits for them, so a ring slot's
+// registers are free to be refilled and the compiler has no loaded value to
+// carry around the loop).
+struct XOps {
+    uint4 a[4];
+    uint32_t wd[4];
+    float sf[4];
+};
+
+// Binary16 bits (low half) -> fp32, as an instruction the compiler cannot
+// fold into the multiply-adds (v_fma_mix_f32 would keep the loaded scale
+// registers live up to the matrix ops); the same exact conversion.
+__device__ __forceinline__ float h2f_now(uint32_t bits) {
+    float r;
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(r) : "v"(bits));
+    return r;
+}
+
+// Codes of a loaded quad through the wave's code tile into the matrix-op
+// lanes (as stage_quad does), activation blocks straight from the staged
+// activation.
+// xl = rc * xres_col_blocks(C) + kq: the lane's block within group 0 of
+// its column; the group offset 4 g is wave-uniform.
+template <bool SC8>
+__device__ __forceinline__ void xres_stage(const WSlot<SC8> &o, XOps &op, const uint4 *xs,
+                                           uint32_t *cs, int lane, int xl, int i16, int kq,
+                                           int q, int C, int B) {
+    uint2 *dst = reinterpret_cast<uint2 *>(cs + (lane >> 2) * kCStride + (lane & 3) * 4);
+    dst[0] = uint2{o.w.x, o.w.y};
+    dst[1] = uint2{o.w.z, o.w.w};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int g = q * 4 + p;
+        op.a[p] = xs[(g < C ? g : C - 1) * 4 + xl];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        op.wd[p] = cs[i16 * kCStride + p * 4 + kq];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if constexpr (SC8)
+            op.sf[p] = h2f_now(p & 1 ? o.s[p >> 1] >> 16 : o.s[p >> 1]);
+        else
+            op.sf[p] = q * 4 + p < C ? h2f_now(o.s[p]) : 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// compute_quad for one row tile with the scales staged in fp32 and the
+// activation blocks already in unpack order: the same operations in the
+// same order.
+__device__ __forceinline__ void xres_compute(const XOps &op, float4_t &acc, uint32_t bias) {
+    half8_t aop[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        aop[p] = __builtin_bit_cast(half8_t, op.a[p]);
+    // the four matrix ops first (independent, so they overlap), then the
+    // scales in group order
+    const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[p], codes_word(op.wd[p], bias), zero,
+                                                     0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        acc[0] = fmaf(op.sf[p], d[p][0], acc[0]);
+        acc[1] = fmaf(op.sf[p], d[p][1], acc[1]);
+        acc[2] = fmaf(op.sf[p], d[p][2], acc[2]);
+        acc[3] = fmaf(op.sf[p], d[p][3], acc[3]);
+    }
+}
+
+template <GEpi E, bool SC8, int NS>
+__global__ void __launch_bounds__(64 * kXresWaves * NS)
+gemm_xres_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
+                 const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
+                 int B, uint16_t *__restrict__ M, int64_t npair, int64_t ntiles, int xa) {
+    constexpr int kXresSets = NS;
+    constexpr int kXresThreads = 64 * kXresWaves * NS;
+    constexpr int kXresRing = xres_ring<NS>();
+    static_assert(kXresRing % 2 == 0, "the staged operands alternate between two buffers");
+    extern __shared__ uint4 xres_lds[];
+    uint8_t *lds8 = reinterpret_cast<uint8_t *>(xres_lds);
+    const uint4 *xs = xres_lds;
+    const uint32_t bias = vgpr_const(0x64006400u);
+    const int lane = threadIdx.x & 63;
+    // wave wid: k quarter `wave`, tile set `set` (tiles set, set + 2, ...)
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wid % kXresWaves;
+    const int set = wid / kXresWaves;
+    const int i16 = lane & 15;
+    const int kq = lane >> 4;
+    const int wq = lane & 3;
+    const int C = K >> 5;
+    const int SB = xres_col_blocks(C);
+    const int xl = (i16 < B ? i16 : 0) * SB + kq;
+    const int nquads = (C + 3) >> 2;
+    const size_t row_bytes = (size_t)K >> 1;
+    uint32_t *cs = reinterpret_cast<uint32_t *>(lds8 + xa + wid * kCTileBytes);
+    float4_t *red =
+        reinterpret_cast<float4_t *>(lds8 + xa + kXresWaves * kXresSets * kCTileBytes);
+
+    const int64_t t0 = (int64_t)blockIdx.x * ntiles / gridDim.x;
+    const int ntl = (int)((int64_t)(blockIdx.x + 1) * ntiles / gridDim.x - t0);
+    const int nts = set < ntl ? (ntl - set + kXresSets - 1) / kXresSets : 0; // this set's tiles
+    const int nqw = wave < nquads ? (nquads - 1 - wave) / kXresWaves + 1 : 0;
+    const int nitems = nqw * nts;
+
+    // Stage the activation column by column: each direct-to-LDS load reads
+    // 64 consecutive 16-byte blocks (1 KB) of one column into consecutive
+    // LDS blocks; lanes past the column's end are masked off.
+    const int ncb = C * 4;              // blocks per column
+    const int nic = (ncb + 63) >> 6;    // loads per column
+    {
+        typedef const void __attribute__((address_space(1))) *gptr_t;
+        typedef void __attribute__((address_space(3))) *lptr_t;
+        for (int k = wid; k < B * nic; k += kXresWaves * kXresSets) {
+            const int b = k / nic, j = k - b * nic;
+            const int blk = j * 64 + lane;
+            if (blk < ncb)
+                __builtin_amdgcn_global_load_lds(
+                    (gptr_t)(X16 + (size_t)b * K + (size_t)blk * 8),
+                    (lptr_t)(lds8 + ((size_t)b * SB + j * 64) * 16), 16, 0, 0);
+        }
+    }
+
+    // Load stream (item li: the set's tile lt, quad index lj of this wave),
+    // clamped to the wave's last item; every slot refill is unconditional.
+    int lt = 0, lj = 0, li = 0;
+    const int64_t tset = t0 + (set < ntl ? set : ntl - 1);
+    const uint8_t *wrow = W + (size_t)xres_row<E>(tset, lane >> 2, N, npair) * row_bytes;
+    const uint16_t *srow = S + (size_t)xres_row<E>(tset, i16, N, npair) * C;
+    auto load_next = [&](WSlot<SC8> &slot) {
+        const int q = wave + kXresWaves * lj; // a wave without quads reloads the last
+        xres_load<SC8>(slot, wrow, srow, q < nquads ? q : nquads - 1, wq, C);
+        if (li + 1 < nitems) {
+            ++li;
+            if (++lj == nqw) {
+                lj = 0;
+                ++lt;
+                const int64_t t = tset + (int64_t)kXresSets * lt;
+                wrow = W + (size_t)xres_row<E>(t, lane >> 2, N, npair) * row_bytes;
+                srow = S + (size_t)xres_row<E>(t, i16, N, npair) * C;
+            }
+        }
+    };
+
+    WSlot<SC8> ring[kXresRing];
+#pragma unroll
+    for (int d = 0; d < kXresRing; ++d) {
+        load_next(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // vmcnt(0) (gfx9 encoding, other counters unconstrained): this wave's
+    // activation blocks have landed (and its first quads with them)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // Every block into the matrix op's k order, once, in place.
+    for (int b = 0; b < B; ++b)
+        for (int blk = threadIdx.x; blk < ncb; blk += kXresThreads)
+            xres_lds[(size_t)b * SB + blk] = permute_block(xres_lds[(size_t)b * SB + blk]);
+    __syncthreads();
+
+    const float4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t acc[1] = {zero4};
+    // stage side: quad index sj of the next item; compute side: the set's
+    // tile ct, quad index cj
+    int sj = 0, ct = 0, cj = 0;
+    // Staging runs every step, past the wave's last item too (it then
+    // stages a copy of the last item, never multiplied): with it under a
+    // condition the compiler could no longer count the LDS reads in flight
+    // and waited for all of them before every quad's matrix ops.
+    XOps ops[2];
+    if (nitems > 0) {
+        xres_stage<SC8>(ring[0], ops[0], xs, cs, lane, xl, i16, kq, wave, C, B);
+        sj = nqw > 1 ? 1 : 0;
+    }
+    load_next(ring[0]);
+    for (int base = 0; base < nitems; base += kXresRing) {
+#pragma unroll
+        for (int d = 0; d < kXresRing; ++d) {
+            const int i = base + d;
+            xres_stage<SC8>(ring[(d + 1) % kXresRing], ops[(d + 1) & 1], xs, cs, lane, xl, i16,
+                            kq, wave + kXresWaves * sj, C, B);
+            if (i + 1 < nitems && ++sj == nqw)
+                sj = 0;
+            // the slot's old registers are consumed before its refill is
+            // issued, so the refill reuses them (otherwise the compiler
+            // renames them and copies them back at the loop's end, where it
+            // must wait for every load in flight)
+            __builtin_amdgcn_sched_barrier(0);
+            load_next(ring[(d + 1) % kXresRing]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < nitems) {
+                xres_compute(ops[d & 1], acc[0], bias);
+                if (++cj == nqw) {
+                    cj = 0;
+                    if (ct < nts - 1) { // not the set's last tile
+                        red[((set + kXresSets * ct) * kXresWaves + wave) * 64 + lane] = acc[0];
+                        acc[0] = zero4;
+                    }
+                    ++ct;
+                }
+            }
+        }
+    }
+    if (nqw == 0) {
+        for (int j = 0; j + 1 < nts; ++j)
+            red[((set + kXresSets * j) * kXresWaves + wave) * 64 + lane] = zero4;
+    }
+    __syncthreads(); // every wave is done with the activation and its code tile
+    // The sets' last tiles are the workgroup's last NS (tl >= ntl - NS);
+    // their partial sums go through the start of the activation area.
+    float4_t *last = reinterpret_cast<float4_t *>(lds8);
+    last[wid * 64 + lane] = acc[0];
+    __syncthreads();
+
+    // Tile tl's sum over the k quarters, in quarter order, as
+    // gemm_mfma_kernel adds them; wave wid finishes the tiles wid, wid + 4 NS, ...
+    auto part = [&](int tl, int w2, int l) -> float4_t {
+        return tl >= ntl - NS ? last[((tl % kXresSets) * kXresWaves + w2) * 64 + l]
+                              : red[(tl * kXresWaves + w2) * 64 + l];
+    };
+    for (int tl = wid; tl < ntl; tl += kXresWaves * kXresSets) {
+        const int64_t t = t0 + tl;
+        float4_t v = part(tl, 0, lane);
+#pragma unroll
+        for (int w2 = 1; w2 < kXresWaves; ++w2)
+            v += part(tl, w2, lane);
+        if constexpr (E == GEpi::SiluPair) {
+            float4_t u = part(tl, 0, lane + 8 < 64 ? lane + 8 : lane);
+#pragma unroll
+            for (int w2 = 1; w2 < kXresWaves; ++w2)
+                u += part(tl, w2, lane + 8 < 64 ? lane + 8 : lane);
+            const int64_t unit = t * 8 + i16;
+            if (i16 < 8 && unit < npair) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int b = 4 * kq + e;
+                    if (b < B) {
+                        const float g = v[e], up = u[e];
+                        const float silu = g / (1.0f + expf(-g));
+                        M[(size_t)b * npair + unit] =
+                            __builtin_bit_cast(uint16_t, (_Float16)(silu * up));
+                    }
+                }
+            }
+        } else {
+            const int64_t row = t * 16 + i16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int b = 4 * kq + e;
+                if (row < N && b < B) {
+                    if constexpr (E == GEpi::Acc)
+                        Y[(size_t)b * N + row] += v[e];
+                    else
+                        Y[(size_t)b * N + row] = v[e];
+                }
+            }
+        }
+    }
+}
+
 using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
                         int, int, uint16_t *, int64_t);
+
+using GemmXresFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *,
+                            int64_t, int, int, uint16_t *, int64_t, int64_t, int);
 
 template <GEpi E, bool SC8>
 GemmFn pick_gemm_sc(int RT, int NW) {
@@ -543,6 +911,94 @@ int pick_row_tiles(int64_t N, int32_t B) {
     return RT;
 }
 
+
+// Activation-resident launch shape: one workgroup per compute unit (at most
+// one per tile), each holding the activation, the code tiles and the partial
+// sums of all its tiles but the last.  grid == 0: it does not fit in the
+// LDS one workgroup may take, and the row-tile launch above is used (same
+// bits).
+struct XresCfg {
+    int grid = 0;
+    int xa = 0;
+    int sets = 0;
+    size_t lds = 0;
+    int64_t ntiles = 0;
+};
+
+template <GEpi E, bool SC8, int NS>
+GemmXresFn xres_fn() {
+    return gemm_xres_kernel<E, SC8, NS>;
+}
+
+// The largest LDS allocation one workgroup may opt into on the current
+// device, with every activation-resident kernel opted in (once per device).
+size_t xres_lds_limit() {
+    static std::mutex mu;
+    static std::map<int, size_t> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end())
+        return it->second;
+    int max_lds = 0, optin = 0;
+    if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+        hipSuccess)
+        max_lds = 0;
+    if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) !=
+        hipSuccess)
+        optin = 0;
+    size_t lim = (size_t)std::max(max_lds, optin);
+    for (GemmXresFn fn :
+         {xres_fn<GEpi::Store, true, kXresSetsUsed>(), xres_fn<GEpi::Store, false, kXresSetsUsed>(),
+          xres_fn<GEpi::Acc, true, kXresSetsUsed>(), xres_fn<GEpi::Acc, false, kXresSetsUsed>(),
+          xres_fn<GEpi::SiluPair, true, kXresSetsUsed>(),
+          xres_fn<GEpi::SiluPair, false, kXresSetsUsed>()})
+        if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lim) != hipSuccess)
+            lim = std::min<size_t>(lim, 65536);
+    cache[dev] = lim;
+    return lim;
+}
+
+// rows: N (Store, Acc) or the unit count npair (SiluPair, 8 units a tile).
+XresCfg xres_config(int64_t rows, int64_t K, int32_t B, bool paired) {
+    XresCfg c;
+    const int64_t C = K / 32;
+    const int64_t xa = ((int64_t)B * xres_col_blocks((int)C) * 16 + 1023) / 1024 * 1024;
+    c.ntiles = paired ? (rows + 7) / 8 : (rows + 15) / 16;
+    const int64_t grid = std::min<int64_t>(device_cus(), c.ntiles);
+    const int64_t maxt = (c.ntiles + grid - 1) / grid;
+    if (maxt < kXresSetsUsed)
+        return c; // a tile or two per compute unit: the row-tile launch is faster
+    const int sets = kXresSetsUsed;
+    const size_t lds = (size_t)xa + kXresWaves * sets * kCTileBytes +
+                       (size_t)std::max<int64_t>(maxt - sets, 0) * kXresWaves * kPartBytes;
+    if (grid < 1 || lds > xres_lds_limit())
+        return c;
+    c.grid = (int)grid;
+    c.xa = (int)xa;
+    c.sets = sets;
+    c.lds = lds;
+    return c;
+}
+
+template <GEpi E>
+GemmXresFn pick_xres(int64_t K, const uint16_t *scales) {
+    const bool sc8 = (K / 32) % 4 == 0 && aligned(scales, 8);
+    return sc8 ? xres_fn<E, true, kXresSetsUsed>() : xres_fn<E, false, kXresSetsUsed>();
+}
+
+q4_status launch_xres(GemmXresFn fn, const XresCfg &c, const uint8_t *packed,
+                      const uint16_t *scales, const uint16_t *X16, float *Y, int64_t N,
+                      int64_t K, int32_t B, uint16_t *M, int64_t npair, hipStream_t stream) {
+    hipLaunchKernelGGL(fn, dim3((unsigned)c.grid), dim3(64 * kXresWaves * c.sets), c.lds, stream,
+                       packed,
+                       scales, X16, Y, N, (int)K, B, M, npair, c.ntiles, c.xa);
+    Q4_HIP(hipGetLastError());
+    return Q4_OK;
+}
+
 } // namespace
 
 q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
@@ -568,6 +1024,11 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
         return launch_gemv_batch(packed, scales, X16, N, K, B,
                                  accumulate ? Epi::Residual : Epi::Store, ea, stream);
     }
+    const XresCfg c = xres_config(N, K, B, false);
+    if (c.grid > 0)
+        return launch_xres(accumulate ? pick_xres<GEpi::Acc>(K, scales)
+                                      : pick_xres<GEpi::Store>(K, scales),
+                           c, packed, scales, X16, Y, N, K, B, nullptr, 0, stream);
     return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, pick_row_tiles(N, B),
                                 kGemmWaves, stream, accumulate);
 }
@@ -582,6 +1043,10 @@ q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
         return launch_gemv_batch(packed, scales, X16, 2 * npair, K, B, Epi::SiluPair, ea,
                                  stream);
     }
+    const XresCfg c = xres_config(npair, K, B, true);
+    if (c.grid > 0)
+        return launch_xres(pick_xres<GEpi::SiluPair>(K, scales), c, packed, scales, X16,
+                           nullptr, 2 * npair, K, B, M, npair, stream);
     const int RT = std::max(2, pick_row_tiles(2 * npair, B));
     GemmFn fn = pick_gemm<GEpi::SiluPair>(RT, kGemmWaves, K, scales);
     if (!fn)

@@ -292,6 +292,28 @@ def test_gemm_row_tiles_do_not_change_bits(B, K):
     assert np.array_equal(_gemm(packed, scales, X), ref)
 
 
+@pytest.mark.parametrize("N,K,B", [(16400, 4096, 16), (16384, 2048, 5), (20000, 1024, 9),
+                                   (16400, 1184, 7), (16400, 32, 6), (28672, 4096, 4),
+                                   (9600, 4096, 16)])
+def test_gemm_activation_resident_equals_row_tiles(N, K, B):
+    """With four or more row tiles per compute unit and an activation that
+    fits in one workgroup's LDS the library runs the activation-resident
+    launch (one workgroup per compute unit; at K = 32 three of the four k
+    quarters have no quad, at K = 1184 the scales take 2-byte loads): the
+    same k split and order as the row-tile launch, so the same bits, with a
+    ragged last tile.  9600 rows (three tiles per unit) take the row-tile
+    launch itself."""
+    packed, scales = _mat(N, K, 960 + N % 97 + B)
+    X = inputs.act_f16((B, K), 961 + B, device=DEV)
+    ref = _gemm(packed, scales, X, tuned=(1, 4))
+    got = _gemm(packed, scales, X)
+    assert np.array_equal(got, ref)
+    rows = np.linspace(0, N - 1, 24).astype(int)
+    Y_ref, M = oracle.gemm(u8(packed)[rows], u16(scales)[rows], u16(X))
+    for b in range(B):
+        assert_within(got[b][rows], Y_ref[b], M[b], f"resident {N}x{K} B={B} col {b}")
+
+
 def test_gemm_b1_is_gemv_and_columns_match_gemv():
     N, K = 512, 2048
     packed, scales = _mat(N, K, 31)
