@@ -538,7 +538,8 @@ __host__ __device__ constexpr int xres_col_blocks(int C) {
 }
 constexpr int kPartBytes = 64 * 16;
 // NS wave sets take tiles set, set + NS, ...; quads in flight per wave
-// (registers: two sets may hold 256 VGPRs a wave, four 128).
+// (registers: two sets may hold 256 VGPRs a wave, four 128; six quads in
+// flight with four sets measured slower than four).
 template <int NS>
 constexpr int xres_ring() {
     return NS <= 2 ? 8 : 4;
@@ -571,11 +572,16 @@ __device__ __forceinline__ int64_t xres_row(int64_t t, int rr, int64_t N, int64_
     }
 }
 
+// Plain loads for the codes: the two 64-byte halves of a 128-byte line of a
+// row belong to neighbouring quads, read by two k quarters of the same
+// workgroup; with non-temporal loads the line was often gone from L2 when
+// the second half was read (1.16 x the weight bytes fetched from HBM on the
+// gate+up shape, and 3-6% slower).
 template <bool SC8>
 __device__ __forceinline__ void xres_load(WSlot<SC8> &o, const uint8_t *wrow,
                                           const uint16_t *srow, int q, int wq, int C) {
     const int gw = q * 4 + wq;
-    o.w = ntload16(wrow + (size_t)(gw < C ? gw : C - 1) * 16);
+    o.w = gload16(wrow + (size_t)(gw < C ? gw : C - 1) * 16);
     if constexpr (SC8) {
         const uint2 v = gload8(srow + (size_t)q * 4);
         o.s[0] = v.x;
