@@ -903,9 +903,20 @@ GemmFn pick_gemm(int RT, int NW, int64_t K, const uint16_t *scales) {
 // tiles no longer pay at B = 16 (28672 x 4096: 28.9 us against 28.0 with
 // four).  The row tiles do not change
 // any output's summation order; the k split (waves per workgroup) does, so
-// it stays fixed at kGemmWaves: a column's result is then independent of B
-// and of the other columns.
+// it depends on the shape only (kGemmWaves, or pick_waves below): a
+// column's result is then independent of B and of the other columns.
 constexpr int kGemmWaves = 4;
+
+// Products of at most one row tile per compute unit (the 4096-row O and
+// down products on 256 units) split k eight ways instead: more waves share
+// each unit's few rows (µs, eight / four waves: O 4096 x 4096 at B = 4
+// 5.98 / 6.83, B = 8 6.09 / 6.63, B = 16 6.61 / 6.73; down 4096 x 14336
+// 13.7 / 17.4, 14.4 / 16.7, 16.9 / 17.2; QKV 6144 rows and wider products
+// gain nothing).  Decided by the shape alone, so every column's result
+// stays independent of B.
+int pick_waves(int64_t N) {
+    return (N + 15) / 16 <= device_cus() ? 8 : kGemmWaves;
+}
 
 int pick_row_tiles(int64_t N, int32_t B) {
     const int64_t tiles = (N + 15) / 16;
@@ -1036,7 +1047,7 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
                                       : pick_xres<GEpi::Store>(K, scales),
                            c, packed, scales, X16, Y, N, K, B, nullptr, 0, stream);
     return launch_gemm_mfma_cfg(packed, scales, X16, Y, N, K, B, pick_row_tiles(N, B),
-                                kGemmWaves, stream, accumulate);
+                                pick_waves(N), stream, accumulate);
 }
 
 q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,

@@ -277,19 +277,30 @@ def test_gemm_every_launch_shape(rt, nw, K):
         assert_within(Y[b], Y_ref[b], M[b], f"gemm rt={rt} nw={nw} K={K} col {b}")
 
 
+def _lib_waves(N):
+    """The row-tile launch's k split for N rows: eight waves up to one row
+    tile of 16 rows per compute unit, else four (a function of the shape)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 8 if (N + 15) // 16 <= cus else 4
+
+
 @pytest.mark.parametrize("B", [5, 7, 16])
 @pytest.mark.parametrize("K", [1184, 7584])
-def test_gemm_row_tiles_do_not_change_bits(B, K):
-    """At four waves (the k split every matrix-core launch uses) the row
-    tiles per wave only regroup rows: every launch shape gives the same bits,
-    and the library's own choice is one of them."""
-    N = 300
+@pytest.mark.parametrize("N", [300, 4200])
+def test_gemm_row_tiles_do_not_change_bits(B, K, N):
+    """At a fixed k split (waves per workgroup) the row tiles per wave only
+    regroup rows: every launch shape gives the same bits, and the library's
+    own choice is one of them (300 rows: eight waves; 4200 rows, more than
+    one row tile per compute unit: four)."""
     packed, scales = _mat(N, K, 950 + B)
     X = inputs.act_f16((B, K), 951 + B, device=DEV)
-    ref = _gemm(packed, scales, X, tuned=(1, 4))
-    for rt in (2, 4, 8):
-        assert np.array_equal(_gemm(packed, scales, X, tuned=(rt, 4)), ref), rt
-    assert np.array_equal(_gemm(packed, scales, X), ref)
+    lib = _gemm(packed, scales, X)
+    for nw, rts in ((4, (2, 4, 8)), (8, (2, 4))):
+        ref = _gemm(packed, scales, X, tuned=(1, nw))
+        for rt in rts:
+            assert np.array_equal(_gemm(packed, scales, X, tuned=(rt, nw)), ref), (rt, nw)
+        if nw == _lib_waves(N):
+            assert np.array_equal(lib, ref)
 
 
 @pytest.mark.parametrize("N,K,B", [(16400, 4096, 16), (16384, 2048, 5), (20000, 1024, 9),
