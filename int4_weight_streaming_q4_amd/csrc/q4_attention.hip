@@ -14,19 +14,20 @@
 //
 // Two kernels per layer, split over the context like flash decoding:
 //   attn_partial  one workgroup per (key/value head, chunk of 64 positions):
-//                 loads its cache tile, rotates the group's queries (a
-//                 table of cos/sin per position, angles taken in fp64 once
-//                 when the decoder is created), the chunk that holds the
-//                 current position also rotates the new key and stores it
-//                 and the new value into the caches; then scores, a softmax
-//                 over the chunk and the weighted value sum, written as a
-//                 partial (chunk max, chunk sum, unnormalised output).
-//   attn_combine  one workgroup per query head: merges the partials of the
-//                 chunks up to the current position and writes the
-//                 binary16 attention output the O product reads.
+//                 rotates the group's queries (a table of cos/sin per
+//                 position, angles taken in fp64 once when the decoder is
+//                 created); the chunk that holds the current position also
+//                 rotates the new key and stores it and the new value into
+//                 the caches; scores on the matrix cores, a softmax over the
+//                 chunk and the weighted value sum, written as a partial
+//                 (chunk max, chunk sum, unnormalised output).
+//   attn_merge    one wave per (query head, 64 dims): merges the partials
+//                 of the chunks and writes the binary16 attention output the
+//                 O product reads.
 // The position comes from a device word, so one captured graph serves every
 // context length of its bucket: chunks past the position write an empty
-// partial.
+// partial.  Draft batches (several token columns) take kv_append_batch and
+// attn_tile_mfma in place of attn_partial, then the same merge.
 #include <algorithm>
 #include <cmath>
 
@@ -40,7 +41,6 @@ using namespace lanes;
 
 constexpr int kAP = 64;        // positions per chunk
 constexpr int kAThreads = 256;
-constexpr int kCThreads = 1024; // combine workgroup
 
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -64,41 +64,50 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
     rope[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-__device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[2 * e] = h2f((uint16_t)(w[e] & 0xFFFFu));
-        f[2 * e + 1] = h2f((uint16_t)(w[e] >> 16));
-    }
-}
-
-// QH query heads per key/value head, HD head dimension.  The workgroup's
-// cache tile (64 K rows and 64 V rows of its group) is loaded into
-// registers first, so its latency overlaps the rotation of the queries.
+// QH query heads per key/value head, HD head dimension; four waves.
+//   scores   S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
+//            accumulation): wave w takes positions 16w .. 16w + 15, whose
+//            key rows it loads from the cache straight into the operand
+//            layout (no LDS).  The rotated fp32 queries enter as two
+//            binary16 halves (x = hi + lo, hi = f16(x), lo = f16(x - hi)),
+//            so each product is two passes and agrees with an fp32
+//            evaluation to about 2^-22 relative (queries beyond binary16
+//            range are not supported); keys are binary16 already.
+//   softmax  wave w takes heads w, w + 4, ...; lane = position.
+//   values   o = sum_j p_j v_j on the vector units: wave w takes a quarter
+//            of the dimensions, a lane two dimensions of every head over
+//            one residue class of positions, the classes summed by lane
+//            swaps; the value tile and the weights come from LDS.
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
              const float2 *__restrict__ rope, const int32_t *__restrict__ pos_dev,
              int32_t max_ctx, int32_t H, int32_t Hkv, float *__restrict__ part, int32_t nchunk) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
     constexpr int HALF = HD / 2;
-    constexpr int QD = HD / 4;                 // dims per lane in the scores
-    constexpr int KL = QD / 8;                 // 16-byte K loads per lane
-    constexpr int DB = HD / 8;                 // 16-byte blocks per row
-    constexpr int PG = kAThreads / DB;         // position groups in the value sum
-    constexpr int VL = kAP / PG;               // V rows per lane
+    constexpr int KT = HD / 32;                 // k steps of the scores
+    constexpr int DB = HD / 8;                  // 16-byte blocks per row
+    constexpr int TL = kAP * DB / kAThreads;    // value-tile blocks per thread
     constexpr int NW = kAThreads / 64;
-    static_assert(HD % 32 == 0 && HD <= 256, "head dimension");
-    static_assert(kAThreads % DB == 0 && kAP % PG == 0 && (DB == 8 || DB == 16), "value-sum layout");
-    __shared__ float qr[QH][HD];               // rotated queries
+    constexpr int QP = HD + 8;                  // query-half row stride (halves)
+    constexpr int NDP = HD / 8;                 // dimension pairs per wave (values)
+    constexpr int NPG = 64 / NDP;               // position classes (values)
+    constexpr int SV = HD / 2 + NDP;            // value row stride (dwords): the
+                                                // classes' rows on distinct banks
+    constexpr int EP = 8;                       // weight row stride (floats)
+    static_assert(HD == 64 || HD == 128, "head dimension");
+    static_assert(QH <= 8 && NW == 4 && kAP == 64 && TL >= 1, "layout");
+    __shared__ __align__(16) uint16_t qhi[QH][QP];
+    __shared__ __align__(16) uint16_t qlo[QH][QP];
     __shared__ __align__(16) uint16_t knew[HD];
     __shared__ __align__(16) uint16_t vnew[HD];
-    __shared__ float sc[QH][kAP];              // scores, then weights
-    __shared__ float mx[QH], sm[QH];
-    __shared__ float vred[NW][QH][HD];
+    __shared__ __align__(16) uint32_t vsh[kAP * SV];
+    __shared__ __align__(16) float ssh[QH][kAP];
+    __shared__ __align__(16) float esh[kAP][EP];
 
     const int g = blockIdx.x, c = blockIdx.y;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int pos = *pos_dev;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
@@ -115,287 +124,269 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
     const size_t gbase = (size_t)g * max_ctx + c0;
 
-    // The operands of this thread's first query rotation are loaded first,
-    // then the cache tile, so the rotation waits only for its own operands
-    // while the tile is in flight.  Every one of these loads is issued
-    // unconditionally (indices clamped into valid rows and elements): a
-    // load behind a per-lane branch makes the compiler's next wait cover
-    // every load in flight, which had the value tile wait for the key tile
-    // and the rotation for both.  Rows past the context (r >= n) load row
-    // n - 1, a written row: their scores are masked out of the softmax and
-    // their weights are 0, so the results are those of zero rows.
+    // The first query rotation's operands and the new token's key and value
+    // operands are loaded first, then the cache tiles; every load is
+    // unconditional (indices clamped), rows past the context read row n - 1:
+    // their scores are masked and their value rows replaced by zeros.
     const float2 *rp = rope + (size_t)pos * HALF;
     const int i0 = t < QH * HALF ? t : QH * HALF - 1;
     const float *q0 = qkv + (size_t)(g * QH + i0 / HALF) * HD;
     const float2 cs0 = rp[i0 % HALF];
     const float qa0 = q0[i0 % HALF], qb0 = q0[i0 % HALF + HALF];
-    // the new token's key and value operands (used by the chunk holding its
-    // row; every workgroup loads them, clamped, so no load is conditional)
     const int dk = t < HALF ? t : HALF - 1, dv = t < HD ? t : HD - 1;
     const float *kq = qkv + (size_t)(H + g) * HD;
     const float *vq = qkv + (size_t)(H + Hkv + g) * HD;
     const float2 csk = rp[dk];
     const float ka0 = kq[dk], kb0 = kq[dk + HALF], v0 = vq[dv];
-    __builtin_amdgcn_sched_barrier(0); // keep these loads ahead of the tile's
-
-    // cache tile loads; the row of the new token is replaced from LDS below
-    const int jj = t >> 2, qq = t & 3;
-    uint4 kreg[KL];
+    __builtin_amdgcn_sched_barrier(0);
+    // key rows in the operand layout: lane (li, lk) of wave w holds row
+    // 16w + li, dimensions 32k + 8lk .. + 7 of step k
+    const int li = lane & 15, lk = lane >> 4;
+    const int kr = w * 16 + li;
+    uint4 kt[KT];
     {
-        const uint16_t *kr = kc + (gbase + (jj < n ? jj : n - 1)) * HD + qq * QD;
+        const uint16_t *krow = kc + (gbase + (kr < n ? kr : n - 1)) * HD + lk * 8;
 #pragma unroll
-        for (int b = 0; b < KL; ++b)
-            kreg[b] = *reinterpret_cast<const uint4 *>(kr + b * 8);
+        for (int k = 0; k < KT; ++k)
+            kt[k] = *reinterpret_cast<const uint4 *>(krow + k * 32);
     }
-    const int db = t % DB, pg = t / DB;
-    uint4 vreg[VL];
+    uint4 vt[TL];
 #pragma unroll
-    for (int i = 0; i < VL; ++i) {
-        const int r = pg + i * PG;
-        vreg[i] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < n ? r : n - 1)) * HD +
-                                                   db * 8);
+    for (int m = 0; m < TL; ++m) {
+        const int blk = t + m * kAThreads;
+        const int r = blk / DB, cb = blk % DB;
+        vt[m] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < n ? r : n - 1)) * HD + cb * 8);
     }
-    // The new token's operands are consumed here, so the compiler cannot
-    // sink their loads into the branch below, behind the tile's.
     asm volatile("" ::"v"(ka0), "v"(kb0), "v"(v0), "v"(csk.x), "v"(csk.y));
 
-    // rotate the group's queries; the chunk of the new token also rotates
-    // its key and stores key and value into row pos of the caches
+    // rotated queries as binary16 halves; the new token's rotated key and
+    // its value, rounded to binary16, into LDS and (the chunk holding its
+    // position) into row pos of the caches
     {   // threads past QH * HALF repeat the last element: the same values
         // to the same place
         const int h = i0 / HALF, d = i0 % HALF;
-        qr[h][d] = qa0 * cs0.x - qb0 * cs0.y;
-        qr[h][d + HALF] = qa0 * cs0.y + qb0 * cs0.x;
+        const float r0 = qa0 * cs0.x - qb0 * cs0.y, r1 = qa0 * cs0.y + qb0 * cs0.x;
+        const _Float16 h0 = (_Float16)r0, h1 = (_Float16)r1;
+        qhi[h][d] = __builtin_bit_cast(uint16_t, h0);
+        qhi[h][d + HALF] = __builtin_bit_cast(uint16_t, h1);
+        qlo[h][d] = f2h(r0 - (float)h0);
+        qlo[h][d + HALF] = f2h(r1 - (float)h1);
     }
     for (int i = t + kAThreads; i < QH * HALF; i += kAThreads) {
         const int h = i / HALF, d = i % HALF;
         const float *q = qkv + (size_t)(g * QH + h) * HD;
         const float2 cs = rp[d];
         const float a = q[d], b = q[d + HALF];
-        qr[h][d] = a * cs.x - b * cs.y;
-        qr[h][d + HALF] = a * cs.y + b * cs.x;
+        const float r0 = a * cs.x - b * cs.y, r1 = a * cs.y + b * cs.x;
+        const _Float16 h0 = (_Float16)r0, h1 = (_Float16)r1;
+        qhi[h][d] = __builtin_bit_cast(uint16_t, h0);
+        qhi[h][d + HALF] = __builtin_bit_cast(uint16_t, h1);
+        qlo[h][d] = f2h(r0 - (float)h0);
+        qlo[h][d + HALF] = f2h(r1 - (float)h1);
     }
-    if (jn < kAP) {
-        uint16_t *krow = kc + (gbase + jn) * HD;
-        uint16_t *vrow = vc + (gbase + jn) * HD;
-        if (t < HALF) {
-            const uint16_t r0 = f2h(ka0 * csk.x - kb0 * csk.y);
-            const uint16_t r1 = f2h(ka0 * csk.y + kb0 * csk.x);
-            knew[t] = r0;
-            knew[t + HALF] = r1;
+    if (t < HALF) {
+        const uint16_t r0 = f2h(ka0 * csk.x - kb0 * csk.y);
+        const uint16_t r1 = f2h(ka0 * csk.y + kb0 * csk.x);
+        knew[t] = r0;
+        knew[t + HALF] = r1;
+        if (jn < kAP) {
+            uint16_t *krow = kc + (gbase + jn) * HD;
             krow[t] = r0;
             krow[t + HALF] = r1;
         }
-        if (t < HD) {
-            const uint16_t r = f2h(v0);
-            vnew[t] = r;
-            vrow[t] = r;
-        }
+    }
+    if (t < HD) {
+        const uint16_t r = f2h(v0);
+        vnew[t] = r;
+        if (jn < kAP)
+            vc[(gbase + jn) * HD + t] = r;
     }
     __syncthreads();
 
-    // scores: four lanes per position, each a quarter of the head dimension
+    // scores: rows of the product are query heads (rows QH .. 15 zero),
+    // columns the wave's 16 positions; the new token's column takes its key
+    // from LDS
     {
-        if (jj == jn) {
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const bool qlive = li < QH;
+        const int qrow = qlive ? li : 0;
 #pragma unroll
-            for (int b = 0; b < KL; ++b)
-                kreg[b] = *reinterpret_cast<const uint4 *>(knew + qq * QD + b * 8);
+        for (int k = 0; k < KT; ++k) {
+            const int d0 = k * 32 + lk * 8;
+            const uint4 kn = *reinterpret_cast<const uint4 *>(knew + d0);
+            const bool isnew = kr == jn;
+            const uint4 kk = make_uint4(isnew ? kn.x : kt[k].x, isnew ? kn.y : kt[k].y,
+                                        isnew ? kn.z : kt[k].z, isnew ? kn.w : kt[k].w);
+            const h8 bk = __builtin_bit_cast(h8, kk);
+            uint4 uh = make_uint4(0u, 0u, 0u, 0u), ul = make_uint4(0u, 0u, 0u, 0u);
+            if (qlive) {
+                uh = *reinterpret_cast<const uint4 *>(&qhi[qrow][d0]);
+                ul = *reinterpret_cast<const uint4 *>(&qlo[qrow][d0]);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, uh), bk, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ul), bk, acc, 0, 0, 0);
         }
-        float acc[QH];
-#pragma unroll
-        for (int h = 0; h < QH; ++h)
-            acc[h] = 0.0f;
-#pragma unroll
-        for (int b = 0; b < KL; ++b) {
-            const int d0 = qq * QD + b * 8;
-            float kf[8];
-            unpack8(kreg[b], kf);
-#pragma unroll
-            for (int e = 0; e < 8; e += 2)
-#pragma unroll
-                for (int h = 0; h < QH; ++h)
-                    acc[h] = fmaf(qr[h][d0 + e], kf[e], fmaf(qr[h][d0 + e + 1], kf[e + 1], acc[h]));
-        }
+        // lane (li, lk) holds heads 4lk .. 4lk + 3 of position 16w + li
         const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
-        for (int h = 0; h < QH; ++h) {
-            float v = acc[h];
-            v += dpp<kQuadXor1>(v);
-            v += dpp<kQuadXor2>(v);
-            if (qq == 0)
-                sc[h][jj] = v * scale;
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * lk + e;
+            if (h < QH)
+                ssh[h][kr] = kr < n ? acc[e] * scale : -INFINITY;
+        }
+    }
+    // value tile into LDS: the new token's row from LDS, rows past the
+    // context zero (their weights are 0, whatever the cache held there)
+#pragma unroll
+    for (int m = 0; m < TL; ++m) {
+        const int blk = t + m * kAThreads;
+        const int r = blk / DB, cb = blk % DB;
+        const uint4 vn = *reinterpret_cast<const uint4 *>(vnew + cb * 8);
+        const bool isnew = r == jn, live = r < n;
+        const uint4 vv = make_uint4(isnew ? vn.x : (live ? vt[m].x : 0u),
+                                    isnew ? vn.y : (live ? vt[m].y : 0u),
+                                    isnew ? vn.z : (live ? vt[m].z : 0u),
+                                    isnew ? vn.w : (live ? vt[m].w : 0u));
+        *reinterpret_cast<uint4 *>(vsh + r * SV + cb * 4) = vv;
+    }
+    __syncthreads();
+
+    // softmax over the chunk: wave w takes heads w, w + 4; lane = position
+    for (int h = w; h < QH; h += NW) {
+        const float sv = ssh[h][lane];
+        const float m = wave_max(sv);
+        const float e = lane < n ? expf(sv - m) : 0.0f;
+        const float l = wave_sum(e);
+        esh[lane][h] = e;
+        if (lane == 0) {
+            pout[h * prow + HD] = m;
+            pout[h * prow + HD + 1] = l;
         }
     }
     __syncthreads();
 
-    // softmax over the chunk: one wave per head
+    // weighted value sum: lane (pg, dp) of wave w takes dimensions
+    // 2 (w NDP + dp) and the next of every head, positions pg, pg + NPG, ...
     {
-        const int w = t >> 6, lane = t & 63;
-        for (int h = w; h < QH; h += NW) {
-            const float s = lane < n ? sc[h][lane] : -INFINITY;
-            const float m = wave_max(s);
-            const float e = lane < n ? expf(s - m) : 0.0f;
-            const float l = wave_sum(e);
-            sc[h][lane] = e;
-            if (lane == 0) {
-                mx[h] = m;
-                sm[h] = l;
+        const int dp = lane % NDP, pg = lane / NDP;
+        const int dw = w * NDP + dp;
+        float o0[QH], o1[QH];
+#pragma unroll
+        for (int h = 0; h < QH; ++h) {
+            o0[h] = 0.0f;
+            o1[h] = 0.0f;
+        }
+        constexpr int PL = kAP / NPG;           // positions per lane
+        // every read first (values, then weights), so their latencies overlap
+        uint32_t vw[PL];
+        float ev[PL][QH];
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            vw[i] = vsh[(pg + i * NPG) * SV + dw];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int j = pg + i * NPG;
+            if constexpr (QH >= 4) {
+#pragma unroll
+                for (int h4 = 0; h4 < QH; h4 += 4) {
+                    const float4 e4 = *reinterpret_cast<const float4 *>(&esh[j][h4]);
+                    ev[i][h4] = e4.x;
+                    ev[i][h4 + 1] = e4.y;
+                    ev[i][h4 + 2] = e4.z;
+                    ev[i][h4 + 3] = e4.w;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < QH; ++h)
+                    ev[i][h] = esh[j][h];
             }
         }
-    }
-    __syncthreads();
-
-    // weighted value sum: lane = (16-byte block of the row, position group);
-    // rows past the context have weight 0 and zero values
-    {
-        float acc[QH][8];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int h = 0; h < QH; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[h][e] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VL; ++i) {
-            const int r = pg + i * PG;
-            if (r == jn)
-                vreg[i] = *reinterpret_cast<const uint4 *>(vnew + db * 8);
-            float vf[8];
-            unpack8(vreg[i], vf);
+        for (int i = 0; i < PL; ++i) {
+            const float va = h2f((uint16_t)(vw[i] & 0xFFFFu)), vb = h2f((uint16_t)(vw[i] >> 16));
 #pragma unroll
             for (int h = 0; h < QH; ++h) {
-                const float p = sc[h][r];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+                o0[h] = fmaf(ev[i][h], va, o0[h]);
+                o1[h] = fmaf(ev[i][h], vb, o1[h]);
             }
         }
-        // position groups of one wave (lanes DB, 2 DB, ... apart): half
-        // rows for 8 blocks per row, then rows, then wave halves
+        // sum the position classes: lanes NDP apart (8: within 16-lane
+        // rows), then 16-lane rows, then wave halves
 #pragma unroll
-        for (int h = 0; h < QH; ++h)
+        for (int h = 0; h < QH; ++h) {
+            float x[2] = {o0[h], o1[h]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = acc[h][e];
-                if (DB == 8)
-                    x += dpp<kRowRor8>(x);
-                const Rows16 r(x);
-                x = fa(r.a) + fa(r.b);
-                const Halves32 hh(x);
-                acc[h][e] = fa(hh.a) + fa(hh.b);
+            for (int u = 0; u < 2; ++u) {
+                if constexpr (NDP == 8)
+                    x[u] += dpp<kRowRor8>(x[u]);
+                const Rows16 r(x[u]);
+                x[u] = fa(r.a) + fa(r.b);
+                const Halves32 hh(x[u]);
+                x[u] = fa(hh.a) + fa(hh.b);
             }
-        const int w = t >> 6, lane = t & 63;
-        if (lane < DB) {
-#pragma unroll
-            for (int h = 0; h < QH; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vred[w][h][db * 8 + e] = acc[h][e];
-        }
-        __syncthreads();
-        for (int i = t; i < QH * HD; i += kAThreads) {
-            const int h = i / HD, d = i % HD;
-            float s = 0.0f;
-#pragma unroll
-            for (int q = 0; q < NW; ++q)
-                s += vred[q][h][d];
-            pout[h * prow + d] = s;
-        }
-        if (t < QH) {
-            pout[t * prow + HD] = mx[t];
-            pout[t * prow + HD + 1] = sm[t];
+            if (pg == 0)
+                *reinterpret_cast<float2 *>(pout + h * prow + 2 * dw) = make_float2(x[0], x[1]);
         }
     }
 }
 
-// One workgroup per (query head, 64 dims of it) merges the chunk partials
-// (chunk max m_c, chunk sum l_c, unnormalised o_c): o = sum_c o_c e^(m_c -
-// M) / sum_c l_c e^(m_c - M), M the largest m_c.  Wave s merges chunks s,
-// s + S, ... with a running maximum, U chunks per round, then the S waves
-// merge through LDS.
-constexpr int kCDims = 64;
+// One wave per (query head, 64 dims of it, token column) merges the chunk
+// partials (chunk max m_c, chunk sum l_c, unnormalised o_c): o = sum_c o_c
+// e^(m_c - M) / sum_c l_c e^(m_c - M), M the largest m_c.  Lane c takes
+// chunk c's maximum and sum (64 chunks per round, a running maximum across
+// rounds), so the weights are one exponential per lane; lane d's output
+// dimension then sums o_c[d] times chunk c's weight, read from lane c.  A
+// round's loads are all in flight at once; no LDS, no barrier.  One token
+// (BATCH false) reads every chunk without waiting for the position word:
+// attn_partial wrote those past the position as empty partials (max -inf,
+// weight 0).  Column b of a batch reads the chunks up to its position.
 template <int QH, int HD, bool BATCH>
-__global__ void __launch_bounds__(kCThreads)
-attn_combine(const float *__restrict__ part, const int32_t *__restrict__ pos_dev,
-             int32_t nchunk, uint16_t *__restrict__ out) {
-    constexpr int S = kCThreads / kCDims;
-    static_assert(HD % kCDims == 0, "dims per workgroup");
-    constexpr int U = 4;
-    __shared__ float ored[S][kCDims];
-    __shared__ float ms[S], ls[S];
-    const int hq = blockIdx.x, t = threadIdx.x;
-    const int d = blockIdx.y * kCDims + t % kCDims;
-    // the wave index is the slice: every chunk index is wave-uniform, so
-    // chunk max and sum come from scalar loads
-    const int s = __builtin_amdgcn_readfirstlane(t / kCDims);
+__global__ void __launch_bounds__(64)
+attn_merge(const float *__restrict__ part, const int32_t *__restrict__ pos_dev, int32_t nchunk,
+           uint16_t *__restrict__ out) {
+    static_assert(HD % 64 == 0, "dims per wave");
+    const int hq = blockIdx.x, lane = threadIdx.x;
+    const int d = blockIdx.y * 64 + lane;
     const int g = hq / QH, h = hq % QH;
-    const int col = BATCH ? (int)blockIdx.z : 0;
-    if (BATCH) {
-        part += (size_t)col * (gridDim.x / QH) * nchunk * QH * (HD + 2);
-        out += (size_t)col * gridDim.x * HD;
-    }
-    // One token: attn_partial wrote every chunk, those past the position as
-    // empty partials (max -inf, sum 0, o 0), whose merge changes nothing
-    // bitwise (weight exp(-inf) = 0, rescale exp(0) = 1), so all nchunk are
-    // read and the loads need not wait for the position word.  A batch reads
-    // only its column's chunks.
-    const int nc = BATCH ? min(nchunk, (*pos_dev + col) / kAP + 1) : nchunk;
     const size_t prow = (size_t)(HD + 2);
     const size_t cstride = (size_t)QH * prow;
+    int nc = nchunk;
+    if (BATCH) {
+        const int col = (int)blockIdx.z;
+        part += (size_t)col * (gridDim.x / QH) * nchunk * QH * prow;
+        out += (size_t)col * gridDim.x * HD;
+        nc = min(nchunk, (*pos_dev + col) / kAP + 1);
+    }
     const float *base = part + ((size_t)g * nchunk * QH + h) * prow;
-    float m = -INFINITY, l = 0.0f, o = 0.0f;
-    for (int c1 = s; c1 < nc; c1 += S * U) {
-        float mv[U], lv[U], ov[U];
+    const int last = nc - 1;
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int cb = 0; cb < nc; cb += 64) {
+        // lanes and values past the last chunk: weight 0, and the clamped
+        // loads read a written chunk
+        const float2 ml =
+            *reinterpret_cast<const float2 *>(base + (size_t)min(cb + lane, last) * cstride + HD);
+        float ov[64];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int cc = c1 + u * S;
-            mv[u] = -INFINITY;
-            lv[u] = 0.0f;
-            ov[u] = 0.0f;
-            if (cc < nc) {
-                const float *pc = base + (size_t)cc * cstride;
-                mv[u] = pc[HD];
-                lv[u] = pc[HD + 1];
-                ov[u] = pc[d];
-            }
-        }
-        float mn = m;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            mn = fmaxf(mn, mv[u]);
+        for (int k = 0; k < 64; ++k)
+            ov[k] = base[(size_t)min(cb + k, last) * cstride + d];
+        const float mc = cb + lane <= last ? ml.x : -INFINITY;
+        const float Mn = fmaxf(M, wave_max(mc));
         // an empty chunk (max -inf) has weight 0, and a running max of -inf
-        // means l = o = 0: the guards keep -inf - -inf out of expf and give
-        // the same bits as expf wherever that difference is defined
-        const float r = m == -INFINITY ? 1.0f : expf(m - mn);
-        l *= r;
-        o *= r;
+        // means L = O = 0: the guards keep -inf - -inf out of expf
+        const float r = M == -INFINITY ? 1.0f : expf(M - Mn);
+        const float wc = mc == -INFINITY ? 0.0f : expf(mc - Mn);
+        L = fmaf(L, r, wave_sum(ml.y * wc));
+        O *= r;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float w = mv[u] == -INFINITY ? 0.0f : expf(mv[u] - mn);
-            l = fmaf(lv[u], w, l);
-            o = fmaf(ov[u], w, o);
-        }
-        m = mn;
+        for (int k = 0; k < 64; ++k)
+            O = fmaf(ov[k],
+                     __builtin_bit_cast(float,
+                                        __builtin_amdgcn_readlane(__builtin_bit_cast(int, wc), k)),
+                     O);
+        M = Mn;
     }
-    ored[s][t % kCDims] = o;
-    if (t % kCDims == 0) {
-        ms[s] = m;
-        ls[s] = l;
-    }
-    __syncthreads();
-    if (s == 0) {
-        float M = ms[0];
-#pragma unroll
-        for (int q = 1; q < S; ++q)
-            M = fmaxf(M, ms[q]);
-        float L = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int q = 0; q < S; ++q) {
-            const float w = expf(ms[q] - M);
-            L = fmaf(ls[q], w, L);
-            O = fmaf(ored[q][t], w, O);
-        }
-        out[(size_t)hq * HD + d] = f2h(O / L);
-    }
+    out[(size_t)hq * HD + d] = f2h(O / L);
 }
 
 // Key and value rows of a batch of token columns: column b (blockIdx.y) at
@@ -431,8 +422,9 @@ kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
 // already.  LDS: the K rows (row-major) and the V rows transposed (so both
 // operands are 16-byte reads), the query halves, the scores/weights.  Every
 // row comes from the caches: kv_append_batch stored the columns' rows
-// first.  Used for draft batches; a single token takes attn_partial, whose
-// loads overlap its arithmetic (this tile's fixed staging costs more there).
+// first.  Used for draft batches; a single token takes attn_partial, which
+// needs no staging of the key rows (they load straight into the operand
+// layout) and no transposed value tile.
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
 attn_tile_mfma(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
@@ -610,14 +602,14 @@ using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *,
 
 using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *,
                            const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
-using CombineFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
+using MergeFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
 using TileFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
                         const int32_t *, int32_t, int32_t, int32_t, float *, int32_t, int32_t);
 
 struct AttnFns {
     PartialFn partial = nullptr;
-    CombineFn combine = nullptr;
+    MergeFn merge = nullptr;
     AppendFn append = nullptr;
     TileFn tile = nullptr;
     size_t tile_lds_max = 0; // dynamic LDS the tile kernel may use (0: not usable)
@@ -652,7 +644,7 @@ bool pick(int qh, int hd, bool batch, AttnFns &f) {
     if (qh != QH || hd != HD)
         return false;
     f.partial = attn_partial<QH, HD>;
-    f.combine = batch ? attn_combine<QH, HD, true> : attn_combine<QH, HD, false>;
+    f.merge = batch ? attn_merge<QH, HD, true> : attn_merge<QH, HD, false>;
     f.append = kv_append_batch<HD>;
     f.tile = attn_tile_mfma<QH, HD>;
     f.tile_lds_max = tile_lds_limit<QH, HD>();
@@ -727,9 +719,8 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
                            a.pos_dev, a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
     }
     Q4_HIP(hipGetLastError());
-    hipLaunchKernelGGL(f.combine, dim3((unsigned)a.H, (unsigned)(a.hd / kCDims), (unsigned)a.batch),
-                       dim3(kCThreads), 0, s,
-                       a.part, a.pos_dev, a.nchunk, a.out);
+    hipLaunchKernelGGL(f.merge, dim3((unsigned)a.H, (unsigned)(a.hd / 64), (unsigned)a.batch),
+                       dim3(64), 0, s, a.part, a.pos_dev, a.nchunk, a.out);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }
