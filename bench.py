@@ -186,7 +186,13 @@ def main():
     if not (args.no_attention or args.no_extras):
         dec.close()
         del ws
-        result["with_attention"] = attention_step(args, q4, inputs, torch, dims, layers, h0)
+        wa = attention_step(args, q4, inputs, torch, dims, layers, h0)
+        # in-graph cost of attention: the replayed step over 4096-row caches
+        # against the configured step (whose one-token attention is the V
+        # gather in the QKV epilogue), per layer
+        wa["graph_delta_us_per_layer"] = round(
+            (wa["ms_per_step"] - ms_per_step) * 1000.0 / n_layers, 3)
+        result["with_attention"] = wa
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers, dims, h0, args.cpu_runs)
     print(json.dumps(result), flush=True)
@@ -257,7 +263,9 @@ def attention_step(args, q4, inputs, torch, dims, layers, h0, max_ctx=4096):
     (all in the 4096 bucket), rows before the first of them prefilled with
     N(0,1) binary16 values standing in for earlier tokens.  Returns
     tokens/s and the attention kernels' share, timed per kernel with
-    events at the final context length."""
+    events around the attention launches of one eager step at the final
+    context length (those events also hold the host's launch gaps of an
+    eager step; the caller adds the in-graph difference per layer)."""
     n_layers = len(layers)
     total = args.warmup + args.steps
     first = max_ctx - total + 1

@@ -42,10 +42,6 @@ using namespace lanes;
 constexpr int kAP = 64;        // positions per chunk
 constexpr int kAThreads = 256;
 
-__device__ __forceinline__ float h2f(uint16_t h) {
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-
 __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
@@ -73,11 +69,12 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
 //            so each product is two passes and agrees with an fp32
 //            evaluation to about 2^-22 relative (queries beyond binary16
 //            range are not supported); keys are binary16 already.
-//   softmax  wave w takes heads w, w + 4, ...; lane = position.
-//   values   o = sum_j p_j v_j on the vector units: wave w takes a quarter
-//            of the dimensions, a lane two dimensions of every head over
-//            one residue class of positions, the classes summed by lane
-//            swaps; the value tile and the weights come from LDS.
+//   softmax  wave w takes heads w, w + 4; lane = position.  It runs before
+//            the value tile is staged, while the value rows are in flight.
+//   values   O = P V on the matrix cores the same way (weights as two
+//            binary16 halves): wave w takes the 16-dimension tiles w,
+//            w + 4, ...; the value tile is staged row-major in LDS and each
+//            lane gathers its operand's eight positions of one dimension.
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
 attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
@@ -91,11 +88,9 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     constexpr int TL = kAP * DB / kAThreads;    // value-tile blocks per thread
     constexpr int NW = kAThreads / 64;
     constexpr int QP = HD + 8;                  // query-half row stride (halves)
-    constexpr int NDP = HD / 8;                 // dimension pairs per wave (values)
-    constexpr int NPG = 64 / NDP;               // position classes (values)
-    constexpr int SV = HD / 2 + NDP;            // value row stride (dwords): the
-                                                // classes' rows on distinct banks
-    constexpr int EP = 8;                       // weight row stride (floats)
+    constexpr int SV = HD / 2 + 2;              // value row stride (dwords): rows
+                                                // 8 apart 16 banks apart
+    constexpr int EP = kAP + 4;                 // weight row stride (floats)
     static_assert(HD == 64 || HD == 128, "head dimension");
     static_assert(QH <= 8 && NW == 4 && kAP == 64 && TL >= 1, "layout");
     __shared__ __align__(16) uint16_t qhi[QH][QP];
@@ -104,7 +99,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     __shared__ __align__(16) uint16_t vnew[HD];
     __shared__ __align__(16) uint32_t vsh[kAP * SV];
     __shared__ __align__(16) float ssh[QH][kAP];
-    __shared__ __align__(16) float esh[kAP][EP];
+    __shared__ __align__(16) float esh[QH][EP];
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -235,20 +230,6 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
                 ssh[h][kr] = kr < n ? acc[e] * scale : -INFINITY;
         }
     }
-    // value tile into LDS: the new token's row from LDS, rows past the
-    // context zero (their weights are 0, whatever the cache held there)
-#pragma unroll
-    for (int m = 0; m < TL; ++m) {
-        const int blk = t + m * kAThreads;
-        const int r = blk / DB, cb = blk % DB;
-        const uint4 vn = *reinterpret_cast<const uint4 *>(vnew + cb * 8);
-        const bool isnew = r == jn, live = r < n;
-        const uint4 vv = make_uint4(isnew ? vn.x : (live ? vt[m].x : 0u),
-                                    isnew ? vn.y : (live ? vt[m].y : 0u),
-                                    isnew ? vn.z : (live ? vt[m].z : 0u),
-                                    isnew ? vn.w : (live ? vt[m].w : 0u));
-        *reinterpret_cast<uint4 *>(vsh + r * SV + cb * 4) = vv;
-    }
     __syncthreads();
 
     // softmax over the chunk: wave w takes heads w, w + 4; lane = position
@@ -257,76 +238,71 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
         const float m = wave_max(sv);
         const float e = lane < n ? expf(sv - m) : 0.0f;
         const float l = wave_sum(e);
-        esh[lane][h] = e;
+        esh[h][lane] = e;
         if (lane == 0) {
             pout[h * prow + HD] = m;
             pout[h * prow + HD + 1] = l;
         }
     }
+    // value tile into LDS (row-major, 8-byte stores): the new token's row
+    // from LDS, rows past the context zero (their weights are 0, whatever
+    // the cache held there)
+#pragma unroll
+    for (int m = 0; m < TL; ++m) {
+        const int blk = t + m * kAThreads;
+        const int r = blk / DB, cb = blk % DB;
+        const uint4 vn = *reinterpret_cast<const uint4 *>(vnew + cb * 8);
+        const bool isnew = r == jn, live = r < n;
+        const uint2 v0 = make_uint2(isnew ? vn.x : (live ? vt[m].x : 0u),
+                                    isnew ? vn.y : (live ? vt[m].y : 0u));
+        const uint2 v1 = make_uint2(isnew ? vn.z : (live ? vt[m].z : 0u),
+                                    isnew ? vn.w : (live ? vt[m].w : 0u));
+        *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4) = v0;
+        *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4 + 2) = v1;
+    }
     __syncthreads();
 
-    // weighted value sum: lane (pg, dp) of wave w takes dimensions
-    // 2 (w NDP + dp) and the next of every head, positions pg, pg + NPG, ...
+    // O = P V: rows of the product are query heads (rows QH .. 15 zero),
+    // columns the tile's 16 dimensions; lane (li, lk) takes positions
+    // 32s + 8lk .. + 7 of step s
     {
-        const int dp = lane % NDP, pg = lane / NDP;
-        const int dw = w * NDP + dp;
-        float o0[QH], o1[QH];
+        const bool plive = li < QH;
+        const int prow_ = plive ? li : 0;
+        h8 ph[2], pl[2];
 #pragma unroll
-        for (int h = 0; h < QH; ++h) {
-            o0[h] = 0.0f;
-            o1[h] = 0.0f;
-        }
-        constexpr int PL = kAP / NPG;           // positions per lane
-        // every read first (values, then weights), so their latencies overlap
-        uint32_t vw[PL];
-        float ev[PL][QH];
+        for (int k = 0; k < 2; ++k) {
+            float4 p0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), p1 = p0;
+            if (plive) {
+                p0 = *reinterpret_cast<const float4 *>(&esh[prow_][k * 32 + lk * 8]);
+                p1 = *reinterpret_cast<const float4 *>(&esh[prow_][k * 32 + lk * 8 + 4]);
+            }
+            const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-        for (int i = 0; i < PL; ++i)
-            vw[i] = vsh[(pg + i * NPG) * SV + dw];
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int j = pg + i * NPG;
-            if constexpr (QH >= 4) {
-#pragma unroll
-                for (int h4 = 0; h4 < QH; h4 += 4) {
-                    const float4 e4 = *reinterpret_cast<const float4 *>(&esh[j][h4]);
-                    ev[i][h4] = e4.x;
-                    ev[i][h4 + 1] = e4.y;
-                    ev[i][h4 + 2] = e4.z;
-                    ev[i][h4 + 3] = e4.w;
-                }
-            } else {
-#pragma unroll
-                for (int h = 0; h < QH; ++h)
-                    ev[i][h] = esh[j][h];
+            for (int e = 0; e < 8; ++e) {
+                ph[k][e] = (_Float16)pv[e];
+                pl[k][e] = (_Float16)(pv[e] - (float)ph[k][e]);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
+        const uint16_t *vs16 = reinterpret_cast<const uint16_t *>(vsh);
+        for (int dt = w; dt < HD / 16; dt += NW) {
+            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const float va = h2f((uint16_t)(vw[i] & 0xFFFFu)), vb = h2f((uint16_t)(vw[i] >> 16));
+            for (int k = 0; k < 2; ++k) {
+                const uint16_t *col = vs16 + (k * 32 + lk * 8) * (2 * SV) + dt * 16 + li;
+                h8 bv;
 #pragma unroll
-            for (int h = 0; h < QH; ++h) {
-                o0[h] = fmaf(ev[i][h], va, o0[h]);
-                o1[h] = fmaf(ev[i][h], vb, o1[h]);
+                for (int e = 0; e < 8; ++e)
+                    bv[e] = __builtin_bit_cast(_Float16, col[e * 2 * SV]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[k], bv, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[k], bv, acc, 0, 0, 0);
             }
-        }
-        // sum the position classes: lanes NDP apart (8: within 16-lane
-        // rows), then 16-lane rows, then wave halves
+            // lane (li, lk) holds heads 4lk .. 4lk + 3 of dimension 16dt + li
 #pragma unroll
-        for (int h = 0; h < QH; ++h) {
-            float x[2] = {o0[h], o1[h]};
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if constexpr (NDP == 8)
-                    x[u] += dpp<kRowRor8>(x[u]);
-                const Rows16 r(x[u]);
-                x[u] = fa(r.a) + fa(r.b);
-                const Halves32 hh(x[u]);
-                x[u] = fa(hh.a) + fa(hh.b);
+            for (int e = 0; e < 4; ++e) {
+                const int h = 4 * lk + e;
+                if (h < QH)
+                    pout[h * prow + dt * 16 + li] = acc[e];
             }
-            if (pg == 0)
-                *reinterpret_cast<float2 *>(pout + h * prow + 2 * dw) = make_float2(x[0], x[1]);
         }
     }
 }
