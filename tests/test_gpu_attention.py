@@ -187,6 +187,22 @@ def test_attention_positions_match_oracle(variant):
         teacher_forced_token(m, layers, pos, h0, s, f"{variant} pos {pos}")
 
 
+def test_attention_beyond_one_merge_round():
+    """Contexts past 4096 positions (eager steps): more than 64 chunk
+    partials, so the merge runs a second round of chunks with a running
+    maximum; positions on both sides of the 64th chunk boundary and the
+    last row of a 4200-row cache."""
+    dims = VARIANTS["qh4_hd128"]
+    n, max_ctx = 2, 4200
+    layers = [inputs.layer_weights(dims, 33, l, device=DEV) for l in range(n)]
+    m = KVModel(dims, layers, n, max_ctx, resident=False,
+                prefill_seed=inputs.seed_of(33, 0, 8))
+    s = torch.cuda.Stream()
+    for pos in (4095, 4096, 4159, 4160, 4199):
+        h0 = inputs.residual_f32(dims["d"], inputs.seed_of(33, pos, 9))
+        teacher_forced_token(m, layers, pos, h0, s, f"qh4_hd128 pos {pos}")
+
+
 def test_attention_context_one_is_the_one_token_step():
     """At context length 1 the softmax has one term: the attention output is
     the binary16 V of the group, and the step equals the decoder without a
