@@ -194,8 +194,9 @@ typedef struct {
      * length c stores the current token's rotated key and its value in row
      * c - 1 and attends over rows 0..c-1.  With a cache the workspace also
      * holds, after the layer table, a position word (256 bytes), the
-     * per-chunk attention partials and a rotation table (max_ctx * head_dim
-     * * 4 bytes).  Needs n_heads / n_kv_heads in {1, 2, 4, 8} and head_dim
+     * per-chunk attention partials, the token's rotated queries (n_heads *
+     * head_dim * 4 bytes) and a rotation table (max_ctx * head_dim * 4
+     * bytes), each 256-byte aligned.  Needs n_heads / n_kv_heads in {1, 2, 4, 8} and head_dim
      * 64 or 128; only the four-kernels step (mode 0). */
     void *kv_cache;
     int32_t max_ctx;           /* rows per cache, 1..2^20 */

@@ -8,9 +8,13 @@ namespace q4 {
 struct AttnArgs {
     const float *qkv;       // this token's Q | K | V (fp32)
     uint16_t *kc, *vc;      // this layer's caches, [Hkv][max_ctx][hd] binary16
+                            // (one token: row pos already stored)
     const int32_t *pos_dev; // device word: position of the token (context - 1)
     int32_t max_ctx, H, Hkv, hd;
     const void *rope;       // rotation table, float2 [max_ctx][hd/2] (cos, sin)
+    // one token: the rotated queries f32 [H * hd], stored with the token's
+    // key and value rows by the QKV product's epilogue (Epi::QkvRope)
+    const float *qrot = nullptr;
     float *part;            // partials, attention_partial_bytes()
     int32_t nchunk;         // chunks launched (covers the context bucket)
     uint16_t *out;          // binary16 [H * hd] attention output

@@ -12,22 +12,23 @@
 // rotate-half rotary embedding, scores (q . k) / sqrt(hd), softmax, o =
 // sum_j p_j v_j.
 //
-// Two kernels per layer, split over the context like flash decoding:
+// One token: the QKV product's epilogue rotates the queries and the new key
+// (a table of cos/sin per position, angles taken in fp64 once when the
+// decoder is created) and stores the token's key and value rows into the
+// caches (Epi::QkvRope); then two kernels per layer, split over the context
+// like flash decoding:
 //   attn_partial  one workgroup per (key/value head, chunk of 64 positions):
-//                 rotates the group's queries (a table of cos/sin per
-//                 position, angles taken in fp64 once when the decoder is
-//                 created); the chunk that holds the current position also
-//                 rotates the new key and stores it and the new value into
-//                 the caches; scores on the matrix cores, a softmax over the
-//                 chunk and the weighted value sum, written as a partial
-//                 (chunk max, chunk sum, unnormalised output).
+//                 scores on the matrix cores, a softmax over the chunk and
+//                 the weighted value sum, written as a partial (chunk max,
+//                 chunk sum, unnormalised output).
 //   attn_merge    one wave per (query head, 64 dims): merges the partials
 //                 of the chunks and writes the binary16 attention output the
 //                 O product reads.
 // The position comes from a device word, so one captured graph serves every
 // context length of its bucket: chunks past the position write an empty
 // partial.  Draft batches (several token columns) take kv_append_batch and
-// attn_tile_mfma in place of attn_partial, then the same merge.
+// attn_tile_mfma in place of the epilogue and attn_partial, then the same
+// merge.
 #include <algorithm>
 #include <cmath>
 
@@ -60,7 +61,11 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
     rope[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// QH query heads per key/value head, HD head dimension; four waves.
+// QH query heads per key/value head, HD head dimension; four waves.  The
+// QKV product before it stored the token's rotated queries (qrot) and its
+// key and value rows (cache row pos), so every load here is known at
+// launch: the queries first, then the cache tiles, all in flight while the
+// position word is read; the position only masks.
 //   scores   S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
 //            accumulation): wave w takes positions 16w .. 16w + 15, whose
 //            key rows it loads from the cache straight into the operand
@@ -75,72 +80,53 @@ __global__ void rope_table_kernel(float2 *rope, int32_t max_ctx, int32_t hd, dou
 //            binary16 halves): wave w takes the 16-dimension tiles w,
 //            w + 4, ...; the value tile is staged row-major in LDS and each
 //            lane gathers its operand's eight positions of one dimension.
+// A chunk past the position runs the same path with no position in the
+// context: its partial is empty (max -inf, sum 0, o 0).
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
-attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
-             const float2 *__restrict__ rope, const int32_t *__restrict__ pos_dev,
-             int32_t max_ctx, int32_t H, int32_t Hkv, float *__restrict__ part, int32_t nchunk) {
+attn_partial(const float *__restrict__ qrot, const uint16_t *__restrict__ kc,
+             const uint16_t *__restrict__ vc, const int32_t *__restrict__ pos_dev,
+             int32_t max_ctx, float *__restrict__ part, int32_t nchunk) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     typedef float f4 __attribute__((ext_vector_type(4)));
-    constexpr int HALF = HD / 2;
     constexpr int KT = HD / 32;                 // k steps of the scores
     constexpr int DB = HD / 8;                  // 16-byte blocks per row
     constexpr int TL = kAP * DB / kAThreads;    // value-tile blocks per thread
     constexpr int NW = kAThreads / 64;
     constexpr int QP = HD + 8;                  // query-half row stride (halves)
+    constexpr int Q4N = QH * HD / 4;            // float4 blocks of the queries
     constexpr int SV = HD / 2 + 2;              // value row stride (dwords): rows
                                                 // 8 apart 16 banks apart
     constexpr int EP = kAP + 4;                 // weight row stride (floats)
     static_assert(HD == 64 || HD == 128, "head dimension");
     static_assert(QH <= 8 && NW == 4 && kAP == 64 && TL >= 1, "layout");
+    static_assert(Q4N <= kAThreads, "one query block per thread");
     __shared__ __align__(16) uint16_t qhi[QH][QP];
     __shared__ __align__(16) uint16_t qlo[QH][QP];
-    __shared__ __align__(16) uint16_t knew[HD];
-    __shared__ __align__(16) uint16_t vnew[HD];
     __shared__ __align__(16) uint32_t vsh[kAP * SV];
     __shared__ __align__(16) float ssh[QH][kAP];
     __shared__ __align__(16) float esh[QH][EP];
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int pos = *pos_dev;
+    const int li = lane & 15, lk = lane >> 4;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
     float *pout = part + (((size_t)g * nchunk + c) * QH) * prow;
-    if (c0 > pos) {
-        // empty partial: no positions of this chunk are in the context
-        for (int i = t; i < QH * (HD + 2); i += kAThreads) {
-            const int h = i / (HD + 2), e = i % (HD + 2);
-            pout[h * prow + e] = e == HD ? -INFINITY : 0.0f;
-        }
-        return;
-    }
-    const int n = min(kAP, pos + 1 - c0);
-    const int jn = pos - c0;                   // row of the new token (>= kAP: not here)
     const size_t gbase = (size_t)g * max_ctx + c0;
+    const int rlim = max_ctx - 1 - c0;         // last cache row of the chunk
 
-    // The first query rotation's operands and the new token's key and value
-    // operands are loaded first, then the cache tiles; every load is
-    // unconditional (indices clamped), rows past the context read row n - 1:
-    // their scores are masked and their value rows replaced by zeros.
-    const float2 *rp = rope + (size_t)pos * HALF;
-    const int i0 = t < QH * HALF ? t : QH * HALF - 1;
-    const float *q0 = qkv + (size_t)(g * QH + i0 / HALF) * HD;
-    const float2 cs0 = rp[i0 % HALF];
-    const float qa0 = q0[i0 % HALF], qb0 = q0[i0 % HALF + HALF];
-    const int dk = t < HALF ? t : HALF - 1, dv = t < HD ? t : HD - 1;
-    const float *kq = qkv + (size_t)(H + g) * HD;
-    const float *vq = qkv + (size_t)(H + Hkv + g) * HD;
-    const float2 csk = rp[dk];
-    const float ka0 = kq[dk], kb0 = kq[dk + HALF], v0 = vq[dv];
-    __builtin_amdgcn_sched_barrier(0);
-    // key rows in the operand layout: lane (li, lk) of wave w holds row
-    // 16w + li, dimensions 32k + 8lk .. + 7 of step k
-    const int li = lane & 15, lk = lane >> 4;
+    // the group's queries (threads past the last block repeat it), then the
+    // cache tiles: rows past the cache read its last row; rows past the
+    // context, whatever the cache holds there, get masked scores and zero
+    // value rows below.  Key rows in the operand layout: lane (li, lk) of
+    // wave w holds row 16w + li, dimensions 32k + 8lk .. + 7 of step k.
+    const int qb = t < Q4N ? t : Q4N - 1;
+    const float4 qv = *reinterpret_cast<const float4 *>(qrot + (size_t)g * QH * HD + qb * 4);
     const int kr = w * 16 + li;
     uint4 kt[KT];
     {
-        const uint16_t *krow = kc + (gbase + (kr < n ? kr : n - 1)) * HD + lk * 8;
+        const uint16_t *krow = kc + (gbase + (kr < rlim ? kr : rlim)) * HD + lk * 8;
 #pragma unroll
         for (int k = 0; k < KT; ++k)
             kt[k] = *reinterpret_cast<const uint4 *>(krow + k * 32);
@@ -150,57 +136,29 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
     for (int m = 0; m < TL; ++m) {
         const int blk = t + m * kAThreads;
         const int r = blk / DB, cb = blk % DB;
-        vt[m] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < n ? r : n - 1)) * HD + cb * 8);
+        vt[m] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < rlim ? r : rlim)) * HD +
+                                                 cb * 8);
     }
-    asm volatile("" ::"v"(ka0), "v"(kb0), "v"(v0), "v"(csk.x), "v"(csk.y));
+    __builtin_amdgcn_sched_barrier(0);
+    // positions of the chunk in the context (0 for a chunk past it)
+    const int pos = *pos_dev;
+    const int n = max(0, min(kAP, pos + 1 - c0));
 
-    // rotated queries as binary16 halves; the new token's rotated key and
-    // its value, rounded to binary16, into LDS and (the chunk holding its
-    // position) into row pos of the caches
-    {   // threads past QH * HALF repeat the last element: the same values
-        // to the same place
-        const int h = i0 / HALF, d = i0 % HALF;
-        const float r0 = qa0 * cs0.x - qb0 * cs0.y, r1 = qa0 * cs0.y + qb0 * cs0.x;
-        const _Float16 h0 = (_Float16)r0, h1 = (_Float16)r1;
-        qhi[h][d] = __builtin_bit_cast(uint16_t, h0);
-        qhi[h][d + HALF] = __builtin_bit_cast(uint16_t, h1);
-        qlo[h][d] = f2h(r0 - (float)h0);
-        qlo[h][d + HALF] = f2h(r1 - (float)h1);
-    }
-    for (int i = t + kAThreads; i < QH * HALF; i += kAThreads) {
-        const int h = i / HALF, d = i % HALF;
-        const float *q = qkv + (size_t)(g * QH + h) * HD;
-        const float2 cs = rp[d];
-        const float a = q[d], b = q[d + HALF];
-        const float r0 = a * cs.x - b * cs.y, r1 = a * cs.y + b * cs.x;
-        const _Float16 h0 = (_Float16)r0, h1 = (_Float16)r1;
-        qhi[h][d] = __builtin_bit_cast(uint16_t, h0);
-        qhi[h][d + HALF] = __builtin_bit_cast(uint16_t, h1);
-        qlo[h][d] = f2h(r0 - (float)h0);
-        qlo[h][d + HALF] = f2h(r1 - (float)h1);
-    }
-    if (t < HALF) {
-        const uint16_t r0 = f2h(ka0 * csk.x - kb0 * csk.y);
-        const uint16_t r1 = f2h(ka0 * csk.y + kb0 * csk.x);
-        knew[t] = r0;
-        knew[t + HALF] = r1;
-        if (jn < kAP) {
-            uint16_t *krow = kc + (gbase + jn) * HD;
-            krow[t] = r0;
-            krow[t + HALF] = r1;
+    // queries as binary16 halves
+    {
+        const int h = (qb * 4) / HD, d = (qb * 4) % HD;
+        const float qx[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const _Float16 hi = (_Float16)qx[e];
+            qhi[h][d + e] = __builtin_bit_cast(uint16_t, hi);
+            qlo[h][d + e] = f2h(qx[e] - (float)hi);
         }
-    }
-    if (t < HD) {
-        const uint16_t r = f2h(v0);
-        vnew[t] = r;
-        if (jn < kAP)
-            vc[(gbase + jn) * HD + t] = r;
     }
     __syncthreads();
 
     // scores: rows of the product are query heads (rows QH .. 15 zero),
-    // columns the wave's 16 positions; the new token's column takes its key
-    // from LDS
+    // columns the wave's 16 positions
     {
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         const bool qlive = li < QH;
@@ -208,10 +166,7 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             const int d0 = k * 32 + lk * 8;
-            const uint4 kn = *reinterpret_cast<const uint4 *>(knew + d0);
-            const bool isnew = kr == jn;
-            const uint4 kk = make_uint4(isnew ? kn.x : kt[k].x, isnew ? kn.y : kt[k].y,
-                                        isnew ? kn.z : kt[k].z, isnew ? kn.w : kt[k].w);
+            const uint4 kk = make_uint4(kt[k].x, kt[k].y, kt[k].z, kt[k].w);
             const h8 bk = __builtin_bit_cast(h8, kk);
             uint4 uh = make_uint4(0u, 0u, 0u, 0u), ul = make_uint4(0u, 0u, 0u, 0u);
             if (qlive) {
@@ -244,19 +199,15 @@ attn_partial(const float *__restrict__ qkv, uint16_t *__restrict__ kc, uint16_t 
             pout[h * prow + HD + 1] = l;
         }
     }
-    // value tile into LDS (row-major, 8-byte stores): the new token's row
-    // from LDS, rows past the context zero (their weights are 0, whatever
-    // the cache held there)
+    // value tile into LDS (row-major, 8-byte stores), rows past the context
+    // zero (their weights are 0, whatever the cache holds there)
 #pragma unroll
     for (int m = 0; m < TL; ++m) {
         const int blk = t + m * kAThreads;
         const int r = blk / DB, cb = blk % DB;
-        const uint4 vn = *reinterpret_cast<const uint4 *>(vnew + cb * 8);
-        const bool isnew = r == jn, live = r < n;
-        const uint2 v0 = make_uint2(isnew ? vn.x : (live ? vt[m].x : 0u),
-                                    isnew ? vn.y : (live ? vt[m].y : 0u));
-        const uint2 v1 = make_uint2(isnew ? vn.z : (live ? vt[m].z : 0u),
-                                    isnew ? vn.w : (live ? vt[m].w : 0u));
+        const bool live = r < n;
+        const uint2 v0 = make_uint2(live ? vt[m].x : 0u, live ? vt[m].y : 0u);
+        const uint2 v1 = make_uint2(live ? vt[m].z : 0u, live ? vt[m].w : 0u);
         *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4) = v0;
         *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4 + 2) = v1;
     }
@@ -576,8 +527,8 @@ size_t tile_mfma_lds(int qh, int hd, int batch) {
 using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *, const int32_t *,
                           int32_t, int32_t, int32_t);
 
-using PartialFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *,
-                           const int32_t *, int32_t, int32_t, int32_t, float *, int32_t);
+using PartialFn = void (*)(const float *, const uint16_t *, const uint16_t *, const int32_t *,
+                           int32_t, float *, int32_t);
 using MergeFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
 using TileFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
@@ -690,9 +641,10 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
                            s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
                            a.max_ctx, a.H, a.Hkv, a.part, a.nchunk, a.batch);
     } else {
+        if (!a.qrot)
+            return fail(Q4_ERR_INVALID_ARG, "attention: no rotated queries");
         hipLaunchKernelGGL(f.partial, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads),
-                           0, s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope),
-                           a.pos_dev, a.max_ctx, a.H, a.Hkv, a.part, a.nchunk);
+                           0, s, a.qrot, a.kc, a.vc, a.pos_dev, a.max_ctx, a.part, a.nchunk);
     }
     Q4_HIP(hipGetLastError());
     hipLaunchKernelGGL(f.merge, dim3((unsigned)a.H, (unsigned)(a.hd / 64), (unsigned)a.batch),

@@ -54,6 +54,7 @@ struct Decoder {
     uint16_t *kv = nullptr;
     int32_t *pos_dev = nullptr;  // position word the attention kernels read
     float *att_part = nullptr;   // per-chunk partials
+    float *qrot = nullptr;       // rotated queries of the token, f32 [H * hd]
     void *rope = nullptr;        // rotation table
     int32_t ctx = 1;             // context length of eager / layer-by-layer steps
     int32_t att_chunks = 1;      // chunks the attention kernels cover
@@ -124,6 +125,7 @@ size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) 
              align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv, (int32_t)d.hd,
                                               m->max_ctx) *
                       (size_t)std::max(1, m->max_batch)) +
+             align256((size_t)d.H * d.hd * 4) +
              align256(rope_table_bytes(m->max_ctx, (int32_t)d.hd));
     if (m)
         b += verify_bytes(d, m->max_batch);
@@ -191,6 +193,7 @@ q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s, int32_t 
     a.Hkv = (int32_t)d.Hkv;
     a.hd = (int32_t)d.hd;
     a.rope = dec->rope;
+    a.qrot = dec->qrot;
     a.part = dec->att_part;
     a.nchunk = dec->att_chunks;
     a.out = out ? out : dec->oin;
@@ -198,28 +201,52 @@ q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s, int32_t 
     return launch_attention(a, s);
 }
 
+// The QKV product of one token column with the first RMSNorm in its
+// prologue: x the fp32 residual, y the fp32 QKV rows.  When attention over
+// the cache slice of `layer` follows (a KV cache and layer >= 0), the
+// epilogue also rotates the query heads into dec->qrot and stores the
+// token's rotated key and its value, in binary16, into cache row
+// *pos_dev; otherwise the V rows land, as binary16, in `oin` for every
+// query head of their group (the one-token output).
+q4_status launch_qkv(Decoder *dec, const q4_layer &L, int32_t layer, const float *x, float *y,
+                     uint16_t *oin, hipStream_t s) {
+    const Dims &d = dec->dims;
+    EpiArgs ea{};
+    ea.y = y;
+    ea.hd = (int32_t)d.hd;
+    ea.eps = dec->desc.eps;
+    if (dec->kv && layer >= 0) {
+        const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
+        ea.pos_dev = dec->pos_dev;
+        ea.rope = static_cast<const float2 *>(dec->rope);
+        ea.qrot = dec->qrot;
+        ea.kc = dec->kv + 2 * (size_t)layer * S;
+        ea.vc = ea.kc + S;
+        ea.n_q_heads = (int32_t)d.H;
+        ea.n_kv_heads = (int32_t)d.Hkv;
+        ea.max_ctx = dec->desc.max_ctx;
+        return launch_gemv(L.qkv.packed, L.qkv.scales, x, Pro::RmsNorm, L.qkv.N, L.qkv.K,
+                           Epi::QkvRope, ea, s);
+    }
+    ea.out16 = oin;
+    ea.v_off = (d.H + d.Hkv) * d.hd;
+    ea.group = (int32_t)(d.H / d.Hkv);
+    return launch_gemv(L.qkv.packed, L.qkv.scales, x, Pro::RmsNorm, L.qkv.N, L.qkv.K,
+                       Epi::QkvGather, ea, s);
+}
+
 // One product of a layer; `layer` >= 0 names its cache slice: with a KV
-// cache the QKV product is followed by attention over that slice (layer < 0:
-// the product alone, for timing).
+// cache the QKV product prepares attention over that slice and, with
+// `attention`, is followed by it (layer < 0: the product alone, for timing).
 q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int32_t layer, int which,
-                         hipStream_t s) {
+                         hipStream_t s, bool attention = true) {
     const Dims &d = dec->dims;
     float *h = dec->desc.h;
     EpiArgs ea{};
     switch (which) {
     case kQkv:
-        // QKV with the first RMSNorm in its prologue; V rows also land, as
-        // binary16, in the attention output of every query head of their
-        // group (the one-token output; attention overwrites it).
-        ea.y = dec->qkv;
-        ea.out16 = dec->oin;
-        ea.v_off = (d.H + d.Hkv) * d.hd;
-        ea.hd = (int32_t)d.hd;
-        ea.group = (int32_t)(d.H / d.Hkv);
-        ea.eps = dec->desc.eps;
-        Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, h, Pro::RmsNorm, L.qkv.N, L.qkv.K,
-                             Epi::QkvGather, ea, s));
-        if (dec->kv && layer >= 0)
+        Q4_CHECK(launch_qkv(dec, L, layer, h, dec->qkv, dec->oin, s));
+        if (dec->kv && layer >= 0 && attention)
             return enqueue_attention(dec, layer, s);
         return Q4_OK;
     case kO:
@@ -247,7 +274,7 @@ q4_status enqueue_kernel(Decoder *dec, const q4_layer &L, int32_t layer, int whi
 q4_status enqueue_layer(Decoder *dec, const q4_layer &L, int32_t layer, hipStream_t s,
                         Marks marks = {}) {
     for (int k = kQkv; k <= kDown; ++k) {
-        Q4_CHECK(enqueue_kernel(dec, L, -1, k, s));
+        Q4_CHECK(enqueue_kernel(dec, L, layer, k, s, false));
         Q4_CHECK(marks.mark(s));
         if (k == kQkv && dec->kv && layer >= 0) {
             Q4_CHECK(enqueue_attention(dec, layer, s));
@@ -295,18 +322,10 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
     for (int32_t l = 0; l < (int32_t)dec->layers.size(); ++l) {
         const q4_layer &L = dec->layers[(size_t)l];
         if (B == 1) {
-            EpiArgs ea{};
-            ea.y = dec->qkvb;
-            ea.out16 = dec->oinb;
-            ea.v_off = (d.H + d.Hkv) * d.hd;
-            ea.hd = (int32_t)d.hd;
-            ea.group = (int32_t)(d.H / d.Hkv);
-            ea.eps = eps;
-            Q4_CHECK(launch_gemv(L.qkv.packed, L.qkv.scales, dec->hb, Pro::RmsNorm, L.qkv.N,
-                                 L.qkv.K, Epi::QkvGather, ea, s));
+            Q4_CHECK(launch_qkv(dec, L, l, dec->hb, dec->qkvb, dec->oinb, s));
             if (dec->kv)
                 Q4_CHECK(enqueue_attention(dec, l, s, 1, dec->qkvb, dec->oinb));
-            ea = EpiArgs{};
+            EpiArgs ea{};
             ea.y = dec->hb;
             Q4_CHECK(launch_gemv(L.o.packed, L.o.scales, dec->oinb, Pro::F16, L.o.N, L.o.K,
                                  Epi::Residual, ea, s));
@@ -485,6 +504,8 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
         ws += q4::align256(q4::attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv,
                                                        (int32_t)d.hd, m->max_ctx) *
                            (size_t)std::max(1, m->max_batch));
+        dec->qrot = reinterpret_cast<float *>(ws);
+        ws += q4::align256((size_t)d.H * d.hd * 4);
         dec->rope = ws;
         // context length 1 until the caller sets another; the rotation table
         q4_status st = q4::launch_rope_table(dec->rope, m->max_ctx, (int32_t)d.hd,

@@ -151,6 +151,7 @@ KernelFn pick_kernel(Epi e, Pro p, const Cfg &c) {
     case Epi::Residual: return pick<Epi::Residual, Pro::F16>(c);
     case Epi::QkvGather: return pick<Epi::QkvGather, Pro::F16>(c);
     case Epi::SiluPair: return pick<Epi::SiluPair, Pro::F16>(c);
+    case Epi::QkvRope: return nullptr; // row kernels only
     }
     return nullptr;
 }

@@ -76,10 +76,11 @@ __device__ __forceinline__ RowChunks<NC> row_chunks(int lane, int C, int first =
 }
 
 // Output units per group of R rows: SiluPair pairs gate row u with up row
-// u + pair_off, so R rows hold R / 2 units.
+// u + pair_off, QkvRope row j of a head with row j + hd / 2 (the two halves
+// the rotation mixes), so R rows hold R / 2 units.
 template <Epi E, int R>
 constexpr int units_per_group() {
-    return E == Epi::SiluPair ? R / 2 : R;
+    return E == Epi::SiluPair || E == Epi::QkvRope ? R / 2 : R;
 }
 
 // Matrix row of row slot r of group g (units past the end repeat the last).
@@ -89,10 +90,15 @@ __device__ __forceinline__ int64_t group_row(int64_t g, int r, int64_t n_units,
     constexpr int UP = units_per_group<E, R>();
     int64_t unit = g * UP + r % UP;
     unit = unit < n_units ? unit : n_units - 1;
-    if constexpr (E == Epi::SiluPair)
+    if constexpr (E == Epi::SiluPair) {
         return unit + (r / UP) * ea.pair_off;
-    else
+    } else if constexpr (E == Epi::QkvRope) {
+        const int half = ea.hd >> 1;
+        const int u = (int)unit;
+        return (int64_t)(u / half) * ea.hd + u % half + (r / UP) * half;
+    } else {
         return unit;
+    }
 }
 
 // Loads of the chunks `ch` of the R rows of group g.  Always all NC of
@@ -128,14 +134,68 @@ __device__ __forceinline__ float residual_of(const EpiArgs &ea, int64_t g, int l
         return 0.0f;
 }
 
+// QkvRope: the rotation table entry (cos, sin) of the unit that this lane
+// stores in group g (lane i stores unit i) at position pos; read with the
+// group's weights, so the store does not wait for it.  (0, 0) otherwise.
+template <int R, Epi E>
+__device__ __forceinline__ float2 rope_of(const EpiArgs &ea, int64_t g, int lane,
+                                          int64_t n_units, int pos) {
+    if constexpr (E == Epi::QkvRope) {
+        constexpr int UP = units_per_group<E, R>();
+        int64_t unit = g * UP + (lane < UP ? lane : 0);
+        unit = unit < n_units ? unit : n_units - 1;
+        const int half = ea.hd >> 1;
+        return ea.rope[(size_t)pos * half + (int)unit % half];
+    } else {
+        return make_float2(0.0f, 0.0f);
+    }
+}
+
 // Writes the row totals of group g (every lane holds them) through
-// epilogue E: lane r stores row r, SiluPair lane i unit i.
+// epilogue E: lane r stores row r, SiluPair and QkvRope lane i unit i.
 template <int R, Epi E>
 __device__ __forceinline__ void group_store(const float (&tot)[R], int64_t g, int lane,
                                             float hcur, int64_t N, int64_t n_units,
-                                            const EpiArgs &ea) {
+                                            const EpiArgs &ea, float2 cs = {}, int pos = 0) {
     constexpr int UP = units_per_group<E, R>();
-    if constexpr (E == Epi::SiluPair) {
+    if constexpr (E == Epi::QkvRope) {
+        // The unrotated rows to y as every QKV product stores them; then
+        // the rotate-half rotation of the pair (a, b) at angle pos * base^(-2d/hd)
+        // for query and key heads, in fp32 from the table entry (cos, sin):
+        // query heads to qrot, key heads rounded to binary16 into the key
+        // cache; value heads rounded into the value cache.
+        const int half = ea.hd >> 1;
+#pragma unroll
+        for (int i = 0; i < UP; ++i) {
+            const int64_t unit = g * UP + i;
+            if (lane == i && unit < n_units) {
+                const int u = (int)unit;
+                const int head = u / half, d = u % half;
+                const float a = tot[i], b = tot[i + UP];
+                const size_t ra = (size_t)head * ea.hd + d;
+                ea.y[ra] = a;
+                ea.y[ra + half] = b;
+                const float r0 = a * cs.x - b * cs.y, r1 = a * cs.y + b * cs.x;
+                if (head < ea.n_q_heads) {
+                    ea.qrot[ra] = r0;
+                    ea.qrot[ra + half] = r1;
+                } else if (head < ea.n_q_heads + ea.n_kv_heads) {
+                    uint16_t *k = ea.kc +
+                                  ((size_t)(head - ea.n_q_heads) * ea.max_ctx + pos) * ea.hd + d;
+                    k[0] = f32_to_f16(r0);
+                    k[half] = f32_to_f16(r1);
+                } else {
+                    uint16_t *v =
+                        ea.vc +
+                        ((size_t)(head - ea.n_q_heads - ea.n_kv_heads) * ea.max_ctx + pos) *
+                            ea.hd +
+                        d;
+                    v[0] = f32_to_f16(a);
+                    v[half] = f32_to_f16(b);
+                }
+            }
+        }
+    } else if constexpr (E == Epi::SiluPair) {
 #pragma unroll
         for (int i = 0; i < UP; ++i) {
             const int64_t unit = g * UP + i;
@@ -178,7 +238,8 @@ template <int NC, int R, Epi E, Pro P>
 __global__ void __launch_bounds__(kRowThreads)
 gemv_row_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                 const void *__restrict__ xin, int64_t N, int K, int64_t n_units, EpiArgs ea) {
-    static_assert(E != Epi::SiluPair || R % 2 == 0, "paired rows come in pairs");
+    static_assert((E != Epi::SiluPair && E != Epi::QkvRope) || R % 2 == 0,
+                  "paired rows come in pairs");
     constexpr int UP = units_per_group<E, R>();
     extern __shared__ uint4 xs[];
     __shared__ float wsum[kWaves];
@@ -189,6 +250,7 @@ gemv_row_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int C = K >> 5;
     const int64_t ngroups = (n_units + UP - 1) / UP;
     int64_t g = wave;
+    const int pos = E == Epi::QkvRope ? *ea.pos_dev : 0;
     const uint32_t bias = vgpr_const(0x64006400u);
     const RowChunks<NC> ch = row_chunks<NC>(lane, C);
 
@@ -199,6 +261,7 @@ gemv_row_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int64_t g0 = g < ngroups ? g : ngroups - 1;
     group_loads<NC, R, E>(W, S, C, n_units, ea, g0, ch, w, s);
     float hv = residual_of<R, E>(ea, g0, lane, n_units);
+    float2 cs = rope_of<R, E>(ea, g0, lane, n_units, pos);
     stage_finish<P, false>(xin, xs, K, ea, wsum, st);
     __syncthreads();
     if (g >= ngroups)
@@ -225,12 +288,13 @@ gemv_row_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 #pragma unroll
         for (int r = 0; r < R; ++r)
             tot[r] = wave_total(tot[r]);
-        group_store<R, E>(tot, g, lane, hv, N, n_units, ea);
+        group_store<R, E>(tot, g, lane, hv, N, n_units, ea, cs, pos);
         g += nwaves;
         if (g >= ngroups)
             break;
         group_loads<NC, R, E>(W, S, C, n_units, ea, g, ch, w, s);
         hv = residual_of<R, E>(ea, g, lane, n_units);
+        cs = rope_of<R, E>(ea, g, lane, n_units, pos);
     }
 }
 
@@ -242,7 +306,8 @@ template <int PH, int R, Epi E, Pro P>
 __global__ void __launch_bounds__(kRowThreads)
 gemv_rowp_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const void *__restrict__ xin, int64_t N, int K, int64_t n_units, EpiArgs ea) {
-    static_assert(E != Epi::SiluPair || R % 2 == 0, "paired rows come in pairs");
+    static_assert((E != Epi::SiluPair && E != Epi::QkvRope) || R % 2 == 0,
+                  "paired rows come in pairs");
     constexpr int UP = units_per_group<E, R>();
     extern __shared__ uint4 xs[];
     __shared__ float wsum[kWaves];
@@ -251,6 +316,7 @@ gemv_rowp_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
         __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kRowWaves + (threadIdx.x >> 6)));
     const int64_t nwaves = (int64_t)gridDim.x * kRowWaves;
     const int C = K >> 5;
+    const int pos = E == Epi::QkvRope ? *ea.pos_dev : 0;
     const int nc = (C + 63) / 64;       // chunks per lane
     const int nph = (nc + PH - 1) / PH; // phases per group
     const int64_t ngroups = (n_units + UP - 1) / UP;
@@ -265,6 +331,7 @@ gemv_rowp_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int64_t g0 = g < ngroups ? g : ngroups - 1;
     group_loads<PH, R, E>(W, S, C, n_units, ea, g0, ch, w, s);
     float hv = residual_of<R, E>(ea, g0, lane, n_units);
+    float2 cs = rope_of<R, E>(ea, g0, lane, n_units, pos);
     stage_finish<P, false>(xin, xs, K, ea, wsum, st);
     __syncthreads();
     if (g >= ngroups)
@@ -299,13 +366,14 @@ gemv_rowp_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 #pragma unroll
         for (int r = 0; r < R; ++r)
             tot[r] = wave_total(acc[r]);
-        group_store<R, E>(tot, g, lane, hv, N, n_units, ea);
+        group_store<R, E>(tot, g, lane, hv, N, n_units, ea, cs, pos);
         g += nwaves;
         if (g >= ngroups)
             break;
         ch = row_chunks<PH>(lane, C);
         group_loads<PH, R, E>(W, S, C, n_units, ea, g, ch, w, s);
         hv = residual_of<R, E>(ea, g, lane, n_units);
+        cs = rope_of<R, E>(ea, g, lane, n_units, pos);
     }
 }
 
@@ -474,6 +542,8 @@ RowFn pick_rowp(int PH, int R) {
         Q4_PICK(1, 1) Q4_PICK(2, 1) Q4_PICK(4, 1) Q4_PICK(7, 1)
         Q4_PICK(1, 2) Q4_PICK(2, 2) Q4_PICK(4, 2) Q4_PICK(7, 2)
         Q4_PICK(2, 4) Q4_PICK(4, 4)
+    } else if constexpr (E == Epi::QkvRope) {
+        Q4_PICK(1, 2) Q4_PICK(4, 2) Q4_PICK(7, 2)
     } else if constexpr (E != Epi::SiluPair) {
         Q4_PICK(1, 2) Q4_PICK(4, 1) Q4_PICK(7, 1)
     }
@@ -492,6 +562,7 @@ RowFn pick_any(Epi e, Pro p, int NC, int PH, int R) {
         switch (e) {
         case Epi::QkvGather: return pick_shape<Epi::QkvGather, Pro::RmsNorm>(NC, PH, R);
         case Epi::SiluPair: return pick_shape<Epi::SiluPair, Pro::RmsNorm>(NC, PH, R);
+        case Epi::QkvRope: return pick_shape<Epi::QkvRope, Pro::RmsNorm>(NC, PH, R);
         default: return nullptr;
         }
     }
@@ -500,6 +571,7 @@ RowFn pick_any(Epi e, Pro p, int NC, int PH, int R) {
     case Epi::Residual: return pick_shape<Epi::Residual, Pro::F16>(NC, PH, R);
     case Epi::QkvGather: return pick_shape<Epi::QkvGather, Pro::F16>(NC, PH, R);
     case Epi::SiluPair: return pick_shape<Epi::SiluPair, Pro::F16>(NC, PH, R);
+    case Epi::QkvRope: return nullptr; // always behind the RMSNorm prologue
     }
     return nullptr;
 }
@@ -572,6 +644,11 @@ q4_status row_units(Epi epi, int64_t N, const EpiArgs &ea, int64_t *n_units, con
         if (ea.pair_off * 2 != N)
             return fail(Q4_ERR_INVALID_ARG, "%s: paired rows need N == 2*pair_off", what);
         *n_units = ea.pair_off;
+    } else if (epi == Epi::QkvRope) {
+        if (ea.hd < 2 || ea.hd % 2 || N % ea.hd ||
+            N != (int64_t)(ea.n_q_heads + 2 * ea.n_kv_heads) * ea.hd)
+            return fail(Q4_ERR_INVALID_ARG, "%s: rotary rows need N == (H + 2 Hkv) * hd", what);
+        *n_units = N / 2;
     } else {
         *n_units = N;
     }
@@ -583,7 +660,7 @@ q4_status launch_row_fn(RowFn fn, const uint8_t *packed, const uint16_t *scales,
                         int grid, hipStream_t stream) {
     int64_t n_units = 0;
     Q4_CHECK(row_units(epi, N, ea, &n_units, "gemv rows"));
-    const int UP = epi == Epi::SiluPair ? R / 2 : R;
+    const int UP = epi == Epi::SiluPair || epi == Epi::QkvRope ? R / 2 : R;
     const int64_t blocks = row_grid((n_units + UP - 1) / UP, grid);
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kRowThreads), (size_t)K * 2, stream,
                        packed, scales, xin, N, (int)K, n_units, ea);
@@ -602,7 +679,9 @@ bool use_row_kernels(Epi e, int64_t K) { return K <= 4096 || e != Epi::SiluPair;
 q4_status launch_gemv_row(const uint8_t *packed, const uint16_t *scales, const void *xin,
                           Pro pro, int64_t N, int64_t K, Epi epi, const EpiArgs &ea,
                           hipStream_t stream) {
-    const RowCfg c = row_config(N, K);
+    RowCfg c = row_config(N, K);
+    if (epi == Epi::QkvRope && c.R == 1)
+        c.R = 2; // the rotation's row pairs share a group
     const RowFn fn = pick_any(epi, pro, c.NC, c.PH, c.R);
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemv rows: no kernel for K=%lld", (long long)K);

@@ -70,6 +70,9 @@ enum class Epi : int {
     Residual = 1, // h[n] += acc
     QkvGather = 2,// y[n] = acc; V rows also written as f16 per query head
     SiluPair = 3, // rows (j, j + dff): out_f16[j] = f16(silu(gate) * up)
+    QkvRope = 4,  // rows (j, j + hd/2) of a head: y = both; query heads also
+                  // rotated into qrot, key heads rotated and value heads as
+                  // they are, in binary16, into row *pos_dev of the caches
 };
 
 // How the workgroup stages its activation vector.
@@ -87,6 +90,14 @@ struct EpiArgs {
     int64_t pair_off;  // SiluPair: dff
     float eps;         // RmsNorm prologue: epsilon
     uint16_t *norm_out;// RmsNorm prologue: workgroup 0 writes the normed f16 x here
+    // QkvRope (hd, n_q_heads, n_kv_heads as the layer's): position word,
+    // rotation table (cos, sin) [max_ctx][hd/2], rotated queries f32
+    // [n_q_heads * hd], this layer's caches [n_kv_heads][max_ctx][hd]
+    const int32_t *pos_dev;
+    const float2 *rope;
+    float *qrot;
+    uint16_t *kc, *vc;
+    int32_t n_q_heads, n_kv_heads, max_ctx;
 };
 
 // Launches the product kernel: rows of W (N x K) against the activation

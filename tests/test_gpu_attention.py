@@ -203,6 +203,21 @@ def test_attention_beyond_one_merge_round():
         teacher_forced_token(m, layers, pos, h0, s, f"qh4_hd128 pos {pos}")
 
 
+def test_attention_wide_model_rows():
+    """A model width of 8192 (Llama-3-70B's: 64 query heads, 8 key/value
+    heads): the QKV product runs the phased row kernel, whose epilogue
+    rotates the query and key rows and stores the token's cache rows."""
+    dims = dict(d=8192, H=64, Hkv=8, hd=128, dff=256)
+    n, max_ctx = 1, 300
+    layers = [inputs.layer_weights(dims, 34, l, device=DEV) for l in range(n)]
+    m = KVModel(dims, layers, n, max_ctx, resident=False,
+                prefill_seed=inputs.seed_of(34, 0, 8))
+    s = torch.cuda.Stream()
+    for pos in (0, 65, 299):
+        h0 = inputs.residual_f32(dims["d"], inputs.seed_of(34, pos, 9))
+        teacher_forced_token(m, layers, pos, h0, s, f"d8192 pos {pos}")
+
+
 def test_attention_context_one_is_the_one_token_step():
     """At context length 1 the softmax has one term: the attention output is
     the binary16 V of the group, and the step equals the decoder without a
