@@ -194,8 +194,8 @@ typedef struct {
      * length c stores the current token's rotated key and its value in row
      * c - 1 and attends over rows 0..c-1.  With a cache the workspace also
      * holds, after the layer table, a position word (256 bytes), the
-     * per-chunk attention partials, the token's rotated queries (n_heads *
-     * head_dim * 4 bytes) and a rotation table (max_ctx * head_dim * 4
+     * per-chunk attention partials, the rotated queries (n_heads * head_dim *
+     * 4 bytes per column) and a rotation table (max_ctx * head_dim * 4
      * bytes), each 256-byte aligned.  Needs n_heads / n_kv_heads in {1, 2, 4, 8} and head_dim
      * 64 or 128; only the four-kernels step (mode 0). */
     void *kv_cache;
@@ -211,7 +211,8 @@ typedef struct {
      * fp32 [max_batch][(H + 2 Hkv) hd] (QKV), binary16 [max_batch][H hd]
      * (attention output), binary16 [max_batch][d_ff] (gated MLP
      * activation).  With a KV cache too, the
-     * attention partials are sized for max_batch columns. */
+     * attention partials and rotated queries are sized for max_batch
+     * columns. */
     int32_t max_batch;
     float *h_batch;
 } q4_model_desc;

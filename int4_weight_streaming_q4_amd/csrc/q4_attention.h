@@ -12,8 +12,9 @@ struct AttnArgs {
     const int32_t *pos_dev; // device word: position of the token (context - 1)
     int32_t max_ctx, H, Hkv, hd;
     const void *rope;       // rotation table, float2 [max_ctx][hd/2] (cos, sin)
-    // one token: the rotated queries f32 [H * hd], stored with the token's
-    // key and value rows by the QKV product's epilogue (Epi::QkvRope)
+    // rotated queries f32 [batch][H * hd]: one token reads those the QKV
+    // product's epilogue stored with its key and value rows
+    // (Epi::QkvRope); a batch has kv_append_batch write them
     const float *qrot = nullptr;
     float *part;            // partials, attention_partial_bytes()
     int32_t nchunk;         // chunks launched (covers the context bucket)

@@ -317,12 +317,14 @@ attn_merge(const float *__restrict__ part, const int32_t *__restrict__ pos_dev, 
 }
 
 // Key and value rows of a batch of token columns: column b (blockIdx.y) at
-// position *pos_dev + b, key rotated, both rounded to binary16.
-template <int HD>
+// position *pos_dev + b, key rotated, both rounded to binary16; the
+// column's query heads of the group rotated into qrot (f32 [b][H * hd]).
+template <int QH, int HD>
 __global__ void __launch_bounds__(HD / 2)
 kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
                 uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
-                const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv) {
+                const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
+                float *__restrict__ qrot) {
     constexpr int HALF = HD / 2;
     const int g = blockIdx.x, col = blockIdx.y, d = threadIdx.x;
     const int pos = *pos_dev + col;
@@ -337,129 +339,140 @@ kv_append_batch(const float *__restrict__ qkv, uint16_t *__restrict__ kc,
     krow[d + HALF] = f2h(a * cs.y + b * cs.x);
     vrow[d] = f2h(v[d]);
     vrow[d + HALF] = f2h(v[d + HALF]);
+    float *qo = qrot + (size_t)col * H * HD;
+#pragma unroll
+    for (int h = 0; h < QH; ++h) {
+        const float *q = row + (size_t)(g * QH + h) * HD;
+        const float x = q[d], y = q[d + HALF];
+        qo[(size_t)(g * QH + h) * HD + d] = x * cs.x - y * cs.y;
+        qo[(size_t)(g * QH + h) * HD + d + HALF] = x * cs.y + y * cs.x;
+    }
 }
 
-// Matrix-core attention tile: one workgroup per (key/value head, chunk of
-// 64 positions) for all `batch` columns (column b at position *pos_dev + b;
-// rows r = b * QH + h of the query matrix).  Scores S = Q K^T and outputs
-// O = P V are v_mfma_f32_16x16x32_f16 products with fp32 accumulation; the
-// fp32 queries and weights enter as two binary16 halves (x = hi + lo, hi =
+// Matrix-core attention tile for draft batches: one workgroup per
+// (key/value head, chunk of 64 positions) for all `batch` columns (column b
+// at position *pos_dev + b; rows r = b * QH + h of the query matrix), the
+// single-token pass extended to several row tiles.  kv_append_batch stored
+// the columns' key and value rows and their rotated queries first, so
+// every load is known at launch: the queries, the key rows (each wave the
+// 16 positions 16w .. 16w + 15, straight into the operand layout) and the
+// value tile go out before the position word is read.  S = Q K^T and O =
+// P V are v_mfma_f32_16x16x32_f16 products with fp32 accumulation; the fp32
+// queries and weights enter as two binary16 halves (x = hi + lo, hi =
 // f16(x), lo = f16(x - hi)), so each product is two passes and agrees with
 // an fp32 evaluation to about 2^-22 relative; keys and values are binary16
-// already.  LDS: the K rows (row-major) and the V rows transposed (so both
-// operands are 16-byte reads), the query halves, the scores/weights.  Every
-// row comes from the caches: kv_append_batch stored the columns' rows
-// first.  Used for draft batches; a single token takes attn_partial, which
-// needs no staging of the key rows (they load straight into the operand
-// layout) and no transposed value tile.
+// already.  Scores are masked causally per column (position <= its own);
+// a row with no position in the chunk gets an empty partial.  LDS: the
+// query halves, the value tile (row-major, each lane gathering its
+// operand's eight positions of one dimension), the scores/weights.
 template <int QH, int HD>
 __global__ void __launch_bounds__(kAThreads)
-attn_tile_mfma(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
-               const uint16_t *__restrict__ vc, const float2 *__restrict__ rope,
-               const int32_t *__restrict__ pos_dev, int32_t max_ctx, int32_t H, int32_t Hkv,
-               float *__restrict__ part, int32_t nchunk, int32_t batch) {
+attn_tile_mfma(const float *__restrict__ qrot, const uint16_t *__restrict__ kc,
+               const uint16_t *__restrict__ vc, const int32_t *__restrict__ pos_dev,
+               int32_t max_ctx, int32_t H, int32_t Hkv, float *__restrict__ part,
+               int32_t nchunk, int32_t batch) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     typedef float f4 __attribute__((ext_vector_type(4)));
-    constexpr int HALF = HD / 2;
-    constexpr int HP = HD + 8;     // K tile / query row stride, halves
-    constexpr int VP = kAP + 8;    // transposed V row stride, halves
-    constexpr int SP = kAP + 4;    // score row stride, floats
-    constexpr int KT = HD / 32;    // k tiles of the scores
-    constexpr int DT = HD / 16;    // output column tiles
+    constexpr int KT = HD / 32;                 // k steps of the scores
+    constexpr int DB = HD / 8;                  // 16-byte blocks per row
+    constexpr int TL = kAP * DB / kAThreads;    // value-tile blocks per thread
     constexpr int NW = kAThreads / 64;
+    constexpr int QP = HD + 8;                  // query-half row stride (halves)
+    constexpr int SV = HD / 2 + 2;              // value row stride (dwords)
+    constexpr int SP = kAP + 4;                 // score row stride (floats)
+    constexpr int QB = HD / 4;                  // float4 blocks per query row
+    constexpr int QL = (Q4_MAX_BATCH * QH * QB + kAThreads - 1) / kAThreads; // per thread, at most
     static_assert(HD == 64 || HD == 128, "head dimension");
+    static_assert(QH <= 8 && NW == 4 && kAP == 64 && TL >= 1, "layout");
     extern __shared__ __align__(16) unsigned char smem[];
     const int rows = batch * QH;
     const int RT = (rows + 15) / 16;
-    const int RP = RT * 16;        // padded rows
-    uint16_t *kt = reinterpret_cast<uint16_t *>(smem);                 // [64][HP]
-    uint16_t *vt = kt + kAP * HP;                                      // [HD][VP]
-    uint16_t *qh = vt + HD * VP;                                       // [RP][HP]
-    uint16_t *ql = qh + RP * HP;                                       // [RP][HP]
-    float *ps = reinterpret_cast<float *>(ql + RP * HP);               // [RP][SP]
-    float *mrow = ps + RP * SP;                                        // [RP]
-    float *lrow = mrow + RP;                                           // [RP]
+    const int RP = RT * 16;                     // padded rows
+    uint16_t *qh = reinterpret_cast<uint16_t *>(smem);                 // [RP][QP]
+    uint16_t *ql = qh + RP * QP;                                       // [RP][QP]
+    uint32_t *vsh = reinterpret_cast<uint32_t *>(ql + RP * QP);        // [64][SV]
+    float *ps = reinterpret_cast<float *>(vsh + kAP * SV);             // [RP][SP]
 
     const int g = blockIdx.x, c = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int pos0 = *pos_dev;
-    const int pmax = pos0 + batch - 1;
+    const int li = lane & 15, lk = lane >> 4;
     const int c0 = c * kAP;
     const size_t prow = (size_t)(HD + 2);
-    const size_t nqkv = (size_t)(H + 2 * Hkv) * HD;
     const size_t colstride = (size_t)Hkv * nchunk * QH * prow;
-    if (c0 > pmax) {
-        for (int i = t; i < rows * (HD + 2); i += kAThreads) {
-            const int r = i / (HD + 2), e = i % (HD + 2);
-            const int b = r / QH, h = r % QH;
-            part[b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow + e] =
-                e == HD ? -INFINITY : 0.0f;
-        }
-        return;
-    }
-    const int nrow = min(kAP, pmax + 1 - c0);   // rows any column reads
-    const size_t gbase = ((size_t)g * max_ctx + c0) * HD;
+    const size_t gbase = (size_t)g * max_ctx + c0;
+    const int rlim = max_ctx - 1 - c0;          // last cache row of the chunk
 
-    // stage K (row-major) and V (transposed) of the chunk
-    {
-        constexpr int CPR = HD / 8;
-        for (int i = t; i < kAP * CPR; i += kAThreads) {
-            const int r = i / CPR, cb = i % CPR;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (r < nrow) {
-                kv = *reinterpret_cast<const uint4 *>(kc + gbase + (size_t)r * HD + cb * 8);
-                vv = *reinterpret_cast<const uint4 *>(vc + gbase + (size_t)r * HD + cb * 8);
-            }
-            *reinterpret_cast<uint4 *>(kt + r * HP + cb * 8) = kv;
-            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    // queries of the rows (r = b * QH + h, float4 blocks; padding rows and
+    // blocks past them repeat the last block), key rows, value tile
+    const int nqb = rows * QB;
+    float4 qv[QL];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[(cb * 8 + 2 * e) * VP + r] = (uint16_t)(vw[e] & 0xFFFFu);
-                vt[(cb * 8 + 2 * e + 1) * VP + r] = (uint16_t)(vw[e] >> 16);
+    for (int m = 0; m < QL; ++m) {
+        const int i = t + m * kAThreads;
+        const int ic = i < nqb ? i : nqb - 1;
+        const int r = ic / QB, e = ic % QB;
+        qv[m] = *reinterpret_cast<const float4 *>(
+            qrot + (size_t)(r / QH) * H * HD + (size_t)(g * QH + r % QH) * HD + e * 4);
+    }
+    const int kr = w * 16 + li;
+    uint4 kt[KT];
+    {
+        const uint16_t *krow = kc + (gbase + (kr < rlim ? kr : rlim)) * HD + lk * 8;
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+            kt[k] = *reinterpret_cast<const uint4 *>(krow + k * 32);
+    }
+    uint4 vt[TL];
+#pragma unroll
+    for (int m = 0; m < TL; ++m) {
+        const int blk = t + m * kAThreads;
+        const int r = blk / DB, cb = blk % DB;
+        vt[m] = *reinterpret_cast<const uint4 *>(vc + (gbase + (r < rlim ? r : rlim)) * HD +
+                                                 cb * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int pos0 = *pos_dev;
+    const int nrow = max(0, min(kAP, pos0 + batch - c0)); // rows any column reads
+
+    // query halves; padding rows zero
+#pragma unroll
+    for (int m = 0; m < QL; ++m) {
+        const int i = t + m * kAThreads;
+        if (i < RP * QB) {
+            const int r = i / QB, e = i % QB;
+            const bool live = r < rows;
+            const float qx[4] = {qv[m].x, qv[m].y, qv[m].z, qv[m].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float x = live ? qx[u] : 0.0f;
+                const _Float16 hi = (_Float16)x;
+                qh[r * QP + e * 4 + u] = __builtin_bit_cast(uint16_t, hi);
+                ql[r * QP + e * 4 + u] = f2h(x - (float)hi);
             }
         }
-    }
-    // rotated queries as binary16 halves; padding rows are zero
-    for (int i = t; i < RP * HALF; i += kAThreads) {
-        const int r = i / HALF, d = i % HALF;
-        float a0 = 0.0f, a1 = 0.0f;
-        if (r < rows) {
-            const int b = r / QH, h = r % QH;
-            const float *q = qkv + (size_t)b * nqkv + (size_t)(g * QH + h) * HD;
-            const float2 cs = rope[(size_t)(pos0 + b) * HALF + d];
-            const float x = q[d], y = q[d + HALF];
-            a0 = x * cs.x - y * cs.y;
-            a1 = x * cs.y + y * cs.x;
-        }
-        const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
-        qh[r * HP + d] = __builtin_bit_cast(uint16_t, h0);
-        qh[r * HP + d + HALF] = __builtin_bit_cast(uint16_t, h1);
-        ql[r * HP + d] = f2h(a0 - (float)h0);
-        ql[r * HP + d + HALF] = f2h(a1 - (float)h1);
     }
     __syncthreads();
 
-    // scores: wave w takes positions 16w .. 16w + 15 of every row tile
+    // scores of every row tile for the wave's 16 positions
     const float scale = 1.0f / sqrtf((float)HD);
-    const int li = lane & 15, lk = lane >> 4;
     for (int rt = 0; rt < RT; ++rt) {
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             const int d0 = k * 32 + lk * 8;
-            const h8 bk = *reinterpret_cast<const h8 *>(kt + (w * 16 + li) * HP + d0);
-            const h8 ah = *reinterpret_cast<const h8 *>(qh + (rt * 16 + li) * HP + d0);
-            const h8 al = *reinterpret_cast<const h8 *>(ql + (rt * 16 + li) * HP + d0);
+            const uint4 kk = make_uint4(kt[k].x, kt[k].y, kt[k].z, kt[k].w);
+            const h8 bk = __builtin_bit_cast(h8, kk);
+            const h8 ah = *reinterpret_cast<const h8 *>(qh + (rt * 16 + li) * QP + d0);
+            const h8 al = *reinterpret_cast<const h8 *>(ql + (rt * 16 + li) * QP + d0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bk, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bk, acc, 0, 0, 0);
         }
-        // lane holds rows rt*16 + 4*lk + e of position column w*16 + li
+        // lane (li, lk) holds rows rt * 16 + 4lk .. + 3 of position kr
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rt * 16 + 4 * lk + e;
-            const int j = w * 16 + li;
-            const bool live = r < rows && c0 + j <= pos0 + r / QH;
-            ps[r * SP + j] = live ? acc[e] * scale : -INFINITY;
+            const bool live = r < rows && c0 + kr <= pos0 + r / QH;
+            ps[r * SP + kr] = live ? acc[e] * scale : -INFINITY;
         }
     }
     __syncthreads();
@@ -471,21 +484,44 @@ attn_tile_mfma(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
         const float e = m == -INFINITY ? 0.0f : expf(sv - m);
         const float l = wave_sum(e);
         ps[r * SP + lane] = e;
-        if (lane == 0) {
-            mrow[r] = m;
-            lrow[r] = l;
+        if (lane == 0 && r < rows) {
+            float *pout = part + (size_t)(r / QH) * colstride +
+                          (((size_t)g * nchunk + c) * QH + r % QH) * prow;
+            pout[HD] = m;
+            pout[HD + 1] = l;
         }
+    }
+    // value tile into LDS (row-major, 8-byte stores), rows no column reads
+    // zero
+#pragma unroll
+    for (int m = 0; m < TL; ++m) {
+        const int blk = t + m * kAThreads;
+        const int r = blk / DB, cb = blk % DB;
+        const bool live = r < nrow;
+        const uint2 v0 = make_uint2(live ? vt[m].x : 0u, live ? vt[m].y : 0u);
+        const uint2 v1 = make_uint2(live ? vt[m].z : 0u, live ? vt[m].w : 0u);
+        *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4) = v0;
+        *reinterpret_cast<uint2 *>(vsh + r * SV + cb * 4 + 2) = v1;
     }
     __syncthreads();
 
-    // outputs: wave w takes column tiles w, w + 4, ... of every row tile
-    for (int dt = w; dt < DT; dt += NW) {
+    // O = P V: wave w takes the 16-dimension tiles w, w + 4 of every row
+    // tile; the value operand of a (tile, k step) serves every row tile
+    const uint16_t *vs16 = reinterpret_cast<const uint16_t *>(vsh);
+    for (int dt = w; dt < HD / 16; dt += NW) {
+        h8 bv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint16_t *col = vs16 + (k * 32 + lk * 8) * (2 * SV) + dt * 16 + li;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                bv[k][e] = __builtin_bit_cast(_Float16, col[e * 2 * SV]);
+        }
         for (int rt = 0; rt < RT; ++rt) {
             f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < kAP / 32; ++k) {
-                const int j0 = k * 32 + lk * 8;
-                const float *pr = ps + (rt * 16 + li) * SP + j0;
+            for (int k = 0; k < 2; ++k) {
+                const float *pr = ps + (rt * 16 + li) * SP + k * 32 + lk * 8;
                 const float4 p0 = *reinterpret_cast<const float4 *>(pr);
                 const float4 p1 = *reinterpret_cast<const float4 *>(pr + 4);
                 const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -495,44 +531,35 @@ attn_tile_mfma(const float *__restrict__ qkv, const uint16_t *__restrict__ kc,
                     ph[e] = (_Float16)pv[e];
                     pl[e] = (_Float16)(pv[e] - (float)ph[e]);
                 }
-                const h8 bv = *reinterpret_cast<const h8 *>(vt + (dt * 16 + li) * VP + j0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv[k], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv[k], acc, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = rt * 16 + 4 * lk + e;
-                if (r < rows) {
-                    const int b = r / QH, h = r % QH;
-                    float *pout = part + b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow;
-                    pout[dt * 16 + li] = acc[e];
-                }
+                if (r < rows)
+                    part[(size_t)(r / QH) * colstride +
+                         (((size_t)g * nchunk + c) * QH + r % QH) * prow + dt * 16 + li] = acc[e];
             }
         }
-    }
-    for (int r = t; r < rows; r += kAThreads) {
-        const int b = r / QH, h = r % QH;
-        float *pout = part + b * colstride + (((size_t)g * nchunk + c) * QH + h) * prow;
-        pout[HD] = mrow[r];
-        pout[HD + 1] = lrow[r];
     }
 }
 
 size_t tile_mfma_lds(int qh, int hd, int batch) {
     const int rp = (batch * qh + 15) / 16 * 16;
-    return (size_t)kAP * (hd + 8) * 2 + (size_t)hd * (kAP + 8) * 2 + 2 * (size_t)rp * (hd + 8) * 2 +
-           (size_t)rp * (kAP + 4) * 4 + 2 * (size_t)rp * 4;
+    return 2 * (size_t)rp * (hd + 8) * 2 + (size_t)kAP * (hd / 2 + 2) * 4 +
+           (size_t)rp * (kAP + 4) * 4;
 }
 
 using AppendFn = void (*)(const float *, uint16_t *, uint16_t *, const float2 *, const int32_t *,
-                          int32_t, int32_t, int32_t);
+                          int32_t, int32_t, int32_t, float *);
 
 using PartialFn = void (*)(const float *, const uint16_t *, const uint16_t *, const int32_t *,
                            int32_t, float *, int32_t);
 using MergeFn = void (*)(const float *, const int32_t *, int32_t, uint16_t *);
 
-using TileFn = void (*)(const float *, const uint16_t *, const uint16_t *, const float2 *,
-                        const int32_t *, int32_t, int32_t, int32_t, float *, int32_t, int32_t);
+using TileFn = void (*)(const float *, const uint16_t *, const uint16_t *, const int32_t *,
+                        int32_t, int32_t, int32_t, float *, int32_t, int32_t);
 
 struct AttnFns {
     PartialFn partial = nullptr;
@@ -572,7 +599,7 @@ bool pick(int qh, int hd, bool batch, AttnFns &f) {
         return false;
     f.partial = attn_partial<QH, HD>;
     f.merge = batch ? attn_merge<QH, HD, true> : attn_merge<QH, HD, false>;
-    f.append = kv_append_batch<HD>;
+    f.append = kv_append_batch<QH, HD>;
     f.tile = attn_tile_mfma<QH, HD>;
     f.tile_lds_max = tile_lds_limit<QH, HD>();
     return true;
@@ -633,13 +660,15 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
         if (lds > f.tile_lds_max)
             return fail(Q4_ERR_UNSUPPORTED, "attention: tile needs %zu bytes of LDS, %zu available",
                         lds, f.tile_lds_max);
+        if (!a.qrot)
+            return fail(Q4_ERR_INVALID_ARG, "attention: no rotated-query buffer");
         hipLaunchKernelGGL(f.append, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0,
                            s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
-                           a.max_ctx, a.H, a.Hkv);
+                           a.max_ctx, a.H, a.Hkv, const_cast<float *>(a.qrot));
         Q4_HIP(hipGetLastError());
         hipLaunchKernelGGL(f.tile, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), lds,
-                           s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
-                           a.max_ctx, a.H, a.Hkv, a.part, a.nchunk, a.batch);
+                           s, a.qrot, a.kc, a.vc, a.pos_dev, a.max_ctx, a.H, a.Hkv, a.part,
+                           a.nchunk, a.batch);
     } else {
         if (!a.qrot)
             return fail(Q4_ERR_INVALID_ARG, "attention: no rotated queries");

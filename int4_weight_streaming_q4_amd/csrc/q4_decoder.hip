@@ -54,7 +54,7 @@ struct Decoder {
     uint16_t *kv = nullptr;
     int32_t *pos_dev = nullptr;  // position word the attention kernels read
     float *att_part = nullptr;   // per-chunk partials
-    float *qrot = nullptr;       // rotated queries of the token, f32 [H * hd]
+    float *qrot = nullptr;       // rotated queries, f32 [max(1, max_batch)][H * hd]
     void *rope = nullptr;        // rotation table
     int32_t ctx = 1;             // context length of eager / layer-by-layer steps
     int32_t att_chunks = 1;      // chunks the attention kernels cover
@@ -125,7 +125,7 @@ size_t workspace_bytes(const Dims &d, int64_t n_layers, const q4_model_desc *m) 
              align256(attention_partial_bytes((int32_t)d.H, (int32_t)d.Hkv, (int32_t)d.hd,
                                               m->max_ctx) *
                       (size_t)std::max(1, m->max_batch)) +
-             align256((size_t)d.H * d.hd * 4) +
+             align256((size_t)d.H * d.hd * 4 * (size_t)std::max(1, m->max_batch)) +
              align256(rope_table_bytes(m->max_ctx, (int32_t)d.hd));
     if (m)
         b += verify_bytes(d, m->max_batch);
@@ -505,7 +505,7 @@ extern "C" q4_status q4_decoder_create(const q4_model_desc *m, void **dec_out) {
                                                        (int32_t)d.hd, m->max_ctx) *
                            (size_t)std::max(1, m->max_batch));
         dec->qrot = reinterpret_cast<float *>(ws);
-        ws += q4::align256((size_t)d.H * d.hd * 4);
+        ws += q4::align256((size_t)d.H * d.hd * 4 * (size_t)std::max(1, m->max_batch));
         dec->rope = ws;
         // context length 1 until the caller sets another; the rotation table
         q4_status st = q4::launch_rope_table(dec->rope, m->max_ctx, (int32_t)d.hd,
