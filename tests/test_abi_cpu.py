@@ -144,8 +144,9 @@ def test_quantize_argument_checks():
 
 
 def test_decoder_kv_cache_description_checks():
-    """A KV cache adds a position word and the attention partials to the
-    workspace; its description is validated before any HIP call."""
+    """A KV cache adds a position word, the attention partials, the rotated
+    queries and the rotation table to the workspace; its description is
+    validated before any HIP call."""
     L = q4.lib()
     dims = dict(d=128, H=4, Hkv=2, hd=64, dff=96)
     base = dict(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=64, d_ff=96)
@@ -154,9 +155,10 @@ def test_decoder_kv_cache_description_checks():
     desc = _desc(**base, kv_cache=4096, max_ctx=100, rope_base=500000.0)
     assert L.q4_decoder_workspace_bytes(ctypes.byref(desc), ctypes.byref(with_kv)) == 0
     # position word (256) + partials H * ceil(max_ctx / 64) * (hd + 2) fp32,
-    # rounded up to 256: 4 * 2 * 66 * 4 = 2112 -> 2304, + rotation table
-    # max_ctx * hd/2 (cos, sin) fp32 pairs: 100 * 32 * 8 = 25600
-    assert with_kv.value - plain.value == 256 + 2304 + 25600
+    # rounded up to 256: 4 * 2 * 66 * 4 = 2112 -> 2304, + rotated queries
+    # H * hd fp32: 4 * 64 * 4 = 1024, + rotation table max_ctx * hd/2
+    # (cos, sin) fp32 pairs: 100 * 32 * 8 = 25600
+    assert with_kv.value - plain.value == 256 + 2304 + 1024 + 25600
     assert q4.workspace_bytes(dims, n_layers=2, max_ctx=100) == with_kv.value
     assert q4.kv_cache_elems(dims, 2, 100) == 2 * 2 * 2 * 100 * 64
     out = ctypes.c_size_t()
