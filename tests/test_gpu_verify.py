@@ -17,7 +17,7 @@ import int4_weight_streaming_q4_amd as q4
 from int4_weight_streaming_q4_amd import inputs
 from helpers import DEV, u16
 from test_gpu_decode import SMALL, TINY, EPS, check_h, make_layers, oracle_run, to_host
-from test_gpu_attention import BASE, f16_ulp
+from test_gpu_attention import BASE, VARIANTS, f16_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -224,6 +224,20 @@ def test_verify_attention_teacher_forced(ctx, B):
     prefill = u16(inputs.act_f16((q4.kv_cache_elems(dims, n, max_ctx),), inputs.seed_of(70, 0, 8)))
     H0 = columns(dims, 70, B)
     teacher_forced_verify(dims, layers, max_ctx, ctx, B, prefill, H0, f"ctx {ctx} B {B}")
+
+
+@pytest.mark.parametrize("variant,ctx,B", [("qh8_hd128", 120, 16), ("qh8_hd128", 60, 9),
+                                           ("qh1_hd64", 120, 16), ("qh4_hd128", 192, 9)])
+def test_verify_attention_head_layouts(variant, ctx, B):
+    """The draft-batch attention tile for every head layout: 1, 4 and 8
+    query heads per group (up to 128 rows of the query matrix, eight row
+    tiles), head dims 64 and 128, draft columns across chunk boundaries."""
+    dims = VARIANTS[variant]
+    n, max_ctx = 1, 200
+    layers = make_layers(dims, 72, n)
+    prefill = u16(inputs.act_f16((q4.kv_cache_elems(dims, n, max_ctx),), inputs.seed_of(72, 0, 8)))
+    H0 = columns(dims, 72, B)
+    teacher_forced_verify(dims, layers, max_ctx, ctx, B, prefill, H0, f"{variant} ctx {ctx} B {B}")
 
 
 def test_verify_attention_paths_agree():
