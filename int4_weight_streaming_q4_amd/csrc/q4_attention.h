@@ -23,6 +23,9 @@ struct AttnArgs {
     // block per column, column b sits at position *pos_dev + b, and all
     // key/value rows are stored before any column attends (causal batch).
     int32_t batch = 1;
+    // a batch whose QKV product's epilogue already stored the key and value
+    // rows and the rotated queries (launch_gemm_qkv_rope): no append kernel
+    bool rows_stored = false;
 };
 
 bool attention_supported(int32_t H, int32_t Hkv, int32_t hd);

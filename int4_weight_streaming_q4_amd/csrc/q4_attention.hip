@@ -27,8 +27,9 @@
 // The position comes from a device word, so one captured graph serves every
 // context length of its bucket: chunks past the position write an empty
 // partial.  Draft batches (several token columns) take kv_append_batch and
-// attn_tile_mfma in place of the epilogue and attn_partial, then the same
-// merge.
+// attn_tile_mfma in place of attn_partial (the rows and rotated queries
+// stored by the batched QKV product's epilogue, or by kv_append_batch after
+// the launches that keep a plain epilogue), then the same merge.
 #include <algorithm>
 #include <cmath>
 
@@ -662,10 +663,13 @@ q4_status launch_attention(const AttnArgs &a, hipStream_t s) {
                         lds, f.tile_lds_max);
         if (!a.qrot)
             return fail(Q4_ERR_INVALID_ARG, "attention: no rotated-query buffer");
-        hipLaunchKernelGGL(f.append, dim3((unsigned)a.Hkv, (unsigned)a.batch), dim3(a.hd / 2), 0,
-                           s, a.qkv, a.kc, a.vc, static_cast<const float2 *>(a.rope), a.pos_dev,
-                           a.max_ctx, a.H, a.Hkv, const_cast<float *>(a.qrot));
-        Q4_HIP(hipGetLastError());
+        if (!a.rows_stored) {
+            hipLaunchKernelGGL(f.append, dim3((unsigned)a.Hkv, (unsigned)a.batch),
+                               dim3(a.hd / 2), 0, s, a.qkv, a.kc, a.vc,
+                               static_cast<const float2 *>(a.rope), a.pos_dev, a.max_ctx, a.H,
+                               a.Hkv, const_cast<float *>(a.qrot));
+            Q4_HIP(hipGetLastError());
+        }
         hipLaunchKernelGGL(f.tile, dim3((unsigned)a.Hkv, (unsigned)a.nchunk), dim3(kAThreads), lds,
                            s, a.qrot, a.kc, a.vc, a.pos_dev, a.max_ctx, a.H, a.Hkv, a.part,
                            a.nchunk, a.batch);

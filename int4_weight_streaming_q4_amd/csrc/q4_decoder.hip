@@ -180,7 +180,8 @@ enum Kern { kQkv = 0, kO = 1, kGateUp = 2, kDown = 3 };
 // Attention of layer `layer` over its cache slice, after the QKV product:
 // `batch` token columns of qkv (default: the single-token buffers).
 q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s, int32_t batch = 1,
-                            const float *qkv = nullptr, uint16_t *out = nullptr) {
+                            const float *qkv = nullptr, uint16_t *out = nullptr,
+                            bool rows_stored = false) {
     const Dims &d = dec->dims;
     const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
     AttnArgs a{};
@@ -198,6 +199,7 @@ q4_status enqueue_attention(Decoder *dec, int32_t layer, hipStream_t s, int32_t 
     a.nchunk = dec->att_chunks;
     a.out = out ? out : dec->oin;
     a.batch = batch;
+    a.rows_stored = rows_stored;
     return launch_attention(a, s);
 }
 
@@ -343,13 +345,30 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
             continue;
         }
         Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
-        Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb, L.qkv.N,
-                                  L.qkv.K, B, s));
-        if (dec->kv)
-            Q4_CHECK(enqueue_attention(dec, l, s, B, dec->qkvb, dec->oinb));
-        else
+        if (dec->kv) {
+            // the QKV epilogue stores the columns' key and value rows and
+            // rotated queries where the matrix-core row-tile launch runs
+            const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
+            GRope rp;
+            rp.pos_dev = dec->pos_dev;
+            rp.rope = static_cast<const float2 *>(dec->rope);
+            rp.qrot = dec->qrot;
+            rp.kc = dec->kv + 2 * (size_t)l * S;
+            rp.vc = rp.kc + S;
+            rp.hd = (int32_t)d.hd;
+            rp.nq = (int32_t)d.H;
+            rp.nkv = (int32_t)d.Hkv;
+            rp.max_ctx = dec->desc.max_ctx;
+            bool stored = false;
+            Q4_CHECK(launch_gemm_qkv_rope(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb,
+                                          L.qkv.N, L.qkv.K, B, rp, s, &stored));
+            Q4_CHECK(enqueue_attention(dec, l, s, B, dec->qkvb, dec->oinb, stored));
+        } else {
+            Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb, L.qkv.N,
+                                      L.qkv.K, B, s));
             Q4_CHECK(launch_gather_batch(dec->qkvb, dec->oinb, B, (int32_t)d.H, (int32_t)d.Hkv,
                                          (int32_t)d.hd, s));
+        }
         Q4_CHECK(launch_gemm_mfma(L.o.packed, L.o.scales, dec->oinb, dec->hb, L.o.N, L.o.K, B, s,
                                   true));
         Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));

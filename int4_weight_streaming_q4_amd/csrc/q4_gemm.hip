@@ -293,19 +293,27 @@ __device__ __forceinline__ void compute_quad(const Ops<RT, SC8> &op, float4_t (&
 // the first RT/2 row tiles of a wave are gate rows and the rest the up rows
 // of the same units, and the kernel writes M[b][u] = binary16(silu(g) * up)
 // (silu(g) = g / (1 + exp(-g)), in fp32) instead of the fp32 products.
-enum class GEpi { Store, Acc, SiluPair };
+// Rope: the QKV product whose epilogue stores the attention inputs (see
+// launch_gemm_qkv_rope); its units are the row pairs (j, j + hd / 2) of a
+// head, unit u = head * hd / 2 + j.
+enum class GEpi { Store, Acc, SiluPair, Rope };
 
 // Row of tile t, row-in-tile rr, for the workgroup starting at row0 (Store,
-// Acc) or unit row0 (SiluPair), clamped into the matrix.
+// Acc) or unit row0 (SiluPair, Rope), clamped into the matrix.
 template <int RT, GEpi E>
 __device__ __forceinline__ int64_t tile_row(int64_t row0, int t, int rr, int64_t N,
-                                            int64_t npair) {
+                                            int64_t npair, int hd = 0) {
     int64_t row;
     if constexpr (E == GEpi::SiluPair) {
         row = row0 + (t % (RT / 2)) * 16 + rr;
         row = row < npair ? row : npair - 1;
         if (t >= RT / 2)
             row += npair;
+    } else if constexpr (E == GEpi::Rope) {
+        int64_t unit = row0 + (t % (RT / 2)) * 16 + rr;
+        unit = unit < npair ? unit : npair - 1;
+        const int half = hd >> 1;
+        row = (unit / half) * hd + unit % half + (t >= RT / 2 ? half : 0);
     } else {
         row = row0 + t * 16 + rr;
         row = row < N ? row : N - 1;
@@ -317,8 +325,9 @@ template <int RT, int NW, GEpi E, bool SC8>
 __global__ void __launch_bounds__(64 * NW)
 gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                  const uint16_t *__restrict__ X16, float *__restrict__ Y, int64_t N, int K,
-                 int B, uint16_t *__restrict__ M, int64_t npair) {
+                 int B, uint16_t *__restrict__ M, int64_t npair, GRope rp) {
     static_assert(E != GEpi::SiluPair || RT % 2 == 0, "gate and up tiles come in pairs");
+    static_assert(E != GEpi::Rope || RT == 2, "a rotation pair is one tile and its partner");
     // Per wave: the activation tile (16 x kXStride blocks) and the code tile
     // (RT * 16 x kCStride words); after the loop the same memory holds the
     // k-split partial sums.
@@ -334,8 +343,10 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const int C = K >> 5;
     const int nquads = (C + 3) >> 2;
     const size_t row_bytes = (size_t)K >> 1;
-    // first row (Store, Acc) or first unit (SiluPair) of this workgroup
-    const int64_t row0 = (int64_t)blockIdx.x * (E == GEpi::SiluPair ? 8 * RT : 16 * RT);
+    // first row (Store, Acc) or first unit (SiluPair, Rope) of this workgroup
+    const int64_t row0 =
+        (int64_t)blockIdx.x * (E == GEpi::SiluPair || E == GEpi::Rope ? 8 * RT : 16 * RT);
+    const int pos0 = E == GEpi::Rope ? *rp.pos_dev : 0;
 
     const int rc = i16 < B ? i16 : 0; // column whose activations this lane supplies
     const int gq = (lane >> 2) & 3;
@@ -354,8 +365,8 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *srow[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        wrow[t] = W + (size_t)tile_row<RT, E>(row0, t, lane >> 2, N, npair) * row_bytes;
-        srow[t] = S + (size_t)tile_row<RT, E>(row0, t, i16, N, npair) * C;
+        wrow[t] = W + (size_t)tile_row<RT, E>(row0, t, lane >> 2, N, npair, rp.hd) * row_bytes;
+        srow[t] = S + (size_t)tile_row<RT, E>(row0, t, i16, N, npair, rp.hd) * C;
     }
 
     float4_t acc[RT];
@@ -442,6 +453,21 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
         }
     }
 
+    // Rope: the rotation table entries of the lane's unit at the positions
+    // of its four columns, loaded before the k-split merge
+    float2 rcs[4];
+    if constexpr (E == GEpi::Rope) {
+        const int half = rp.hd >> 1;
+        int64_t unit = row0 + i16;
+        unit = unit < npair ? unit : npair - 1;
+        const int d = (int)(unit % half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int b = 4 * kq + e < B ? 4 * kq + e : B - 1;
+            rcs[e] = rp.rope[(size_t)(pos0 + b) * half + d];
+        }
+    }
+
     if constexpr (NW > 1) {
         float4_t *red = reinterpret_cast<float4_t *>(lds_raw); // [NW][RT][64]
         __syncthreads(); // every wave is done with its tiles
@@ -461,7 +487,43 @@ gemm_mfma_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     }
     // D layout: lane holds weight row i16 of each tile for batch columns
     // 4 * kq + 0..3.
-    if constexpr (E == GEpi::SiluPair) {
+    if constexpr (E == GEpi::Rope) {
+        // the unrotated rows to Y; then the rotate-half rotation of the pair
+        // (a, b) in fp32 from the table entry (cos, sin): query heads to
+        // qrot, key heads rounded to binary16 into the key cache, value heads
+        // rounded into the value cache, at row *pos_dev + column
+        const int half = rp.hd >> 1;
+        const int64_t unit = row0 + i16;
+        const int head = (int)(unit / half), d = (int)(unit % half);
+        const size_t ra = (size_t)head * rp.hd + d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int b = 4 * kq + e;
+            if (unit < npair && b < B) {
+                const float a = acc[0][e], bb = acc[1][e];
+                Y[(size_t)b * N + ra] = a;
+                Y[(size_t)b * N + ra + half] = bb;
+                const float2 cs = rcs[e];
+                const float r0 = a * cs.x - bb * cs.y, r1 = a * cs.y + bb * cs.x;
+                if (head < rp.nq) {
+                    float *q = rp.qrot + (size_t)b * rp.nq * rp.hd + ra;
+                    q[0] = r0;
+                    q[half] = r1;
+                } else if (head < rp.nq + rp.nkv) {
+                    uint16_t *k = rp.kc +
+                                  ((size_t)(head - rp.nq) * rp.max_ctx + pos0 + b) * rp.hd + d;
+                    k[0] = __builtin_bit_cast(uint16_t, (_Float16)r0);
+                    k[half] = __builtin_bit_cast(uint16_t, (_Float16)r1);
+                } else {
+                    uint16_t *v =
+                        rp.vc +
+                        ((size_t)(head - rp.nq - rp.nkv) * rp.max_ctx + pos0 + b) * rp.hd + d;
+                    v[0] = __builtin_bit_cast(uint16_t, (_Float16)a);
+                    v[half] = __builtin_bit_cast(uint16_t, (_Float16)bb);
+                }
+            }
+        }
+    } else if constexpr (E == GEpi::SiluPair) {
 #pragma unroll
         for (int t = 0; t < RT / 2; ++t) {
             const int64_t unit = row0 + t * 16 + i16;
@@ -864,7 +926,7 @@ gemm_xres_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
 }
 
 using GemmFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *, int64_t,
-                        int, int, uint16_t *, int64_t);
+                        int, int, uint16_t *, int64_t, GRope);
 
 using GemmXresFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, float *,
                             int64_t, int, int, uint16_t *, int64_t, int64_t, int);
@@ -876,6 +938,8 @@ GemmFn pick_gemm_sc(int RT, int NW) {
         return gemm_mfma_kernel<rt, nw, E, SC8>;
     if constexpr (E == GEpi::SiluPair) {
         Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
+    } else if constexpr (E == GEpi::Rope) {
+        Q4_PICK(2, 4) Q4_PICK(2, 8)
     } else {
         Q4_PICK(1, 4) Q4_PICK(2, 4) Q4_PICK(4, 4) Q4_PICK(8, 4)
         Q4_PICK(1, 8) Q4_PICK(2, 8) Q4_PICK(4, 8)
@@ -1027,7 +1091,7 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no kernel for row_tiles=%d waves=%d", RT, NW);
     const int64_t blocks = (N + 16 * RT - 1) / (16 * RT);
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, packed, scales,
-                       X16, Y, N, (int)K, B, nullptr, (int64_t)0);
+                       X16, Y, N, (int)K, B, nullptr, (int64_t)0, GRope{});
     Q4_HIP(hipGetLastError());
     return Q4_OK;
 }
@@ -1070,8 +1134,31 @@ q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
         return fail(Q4_ERR_UNSUPPORTED, "gemm: no paired kernel for row_tiles=%d", RT);
     const int64_t blocks = (npair + 8 * RT - 1) / (8 * RT);
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * kGemmWaves), 0, stream, packed,
-                       scales, X16, nullptr, 2 * npair, (int)K, B, M, npair);
+                       scales, X16, nullptr, 2 * npair, (int)K, B, M, npair, GRope{});
     Q4_HIP(hipGetLastError());
+    return Q4_OK;
+}
+
+q4_status launch_gemm_qkv_rope(const uint8_t *packed, const uint16_t *scales,
+                               const uint16_t *X16, float *Y, int64_t N, int64_t K, int32_t B,
+                               const GRope &rp, hipStream_t stream, bool *stored) {
+    *stored = false;
+    // the vector-ALU and activation-resident launches keep their plain
+    // epilogue; the caller appends the rows after them
+    if (gemv_batch_fits(B, K) || xres_config(N, K, B, false).grid > 0)
+        return launch_gemm_mfma(packed, scales, X16, Y, N, K, B, stream);
+    if (rp.hd < 32 || rp.hd % 32 || N != (int64_t)(rp.nq + 2 * rp.nkv) * rp.hd)
+        return fail(Q4_ERR_INVALID_ARG, "gemm: rotary rows need N == (H + 2 Hkv) * hd");
+    const int NW = pick_waves(N);
+    GemmFn fn = pick_gemm<GEpi::Rope>(2, NW, K, scales);
+    if (!fn)
+        return fail(Q4_ERR_UNSUPPORTED, "gemm: no rotary kernel for waves=%d", NW);
+    const int64_t npair = N / 2;
+    const int64_t blocks = (npair + 15) / 16;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, packed, scales,
+                       X16, Y, N, (int)K, B, nullptr, npair, rp);
+    Q4_HIP(hipGetLastError());
+    *stored = true;
     return Q4_OK;
 }
 

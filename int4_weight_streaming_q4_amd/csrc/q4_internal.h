@@ -147,6 +147,23 @@ q4_status launch_gemv_batch(const uint8_t *packed, const uint16_t *scales, const
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales,
                            const uint16_t *X16, float *Y, int64_t N, int64_t K,
                            int32_t B, hipStream_t stream, bool accumulate = false);
+// The QKV product of B token columns (column b at position *pos_dev + b)
+// whose epilogue, where the matrix-core row-tile launch takes the product,
+// also stores what attention over the KV cache needs: the query heads
+// rotated into qrot (f32 [B][nq * hd]), the rotated key and the value of
+// every key/value head, in binary16, into cache rows *pos_dev + b (caches
+// [nkv][max_ctx][hd]).  Y holds the unrotated rows either way; *stored
+// tells whether the epilogue ran (otherwise the caller appends the rows).
+struct GRope {
+    const int32_t *pos_dev = nullptr;
+    const float2 *rope = nullptr; // (cos, sin) [max_ctx][hd / 2]
+    float *qrot = nullptr;
+    uint16_t *kc = nullptr, *vc = nullptr;
+    int32_t hd = 0, nq = 0, nkv = 0, max_ctx = 0;
+};
+q4_status launch_gemm_qkv_rope(const uint8_t *packed, const uint16_t *scales,
+                               const uint16_t *X16, float *Y, int64_t N, int64_t K, int32_t B,
+                               const GRope &rp, hipStream_t stream, bool *stored);
 // Small-batch gate+up product with the SiLU gate fused: `packed` holds npair
 // gate rows then npair up rows; M[b][u] = binary16(silu(gate) * up).
 q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
