@@ -200,7 +200,7 @@ def main():
 
 def verify_rates(q4, inputs, torch, dims, layers, decode_ms, reps=20):
     """Verify step of a speculative draft (B token columns through the 32
-    layers together, graph-captured) at B = 1, 2, 4, 8, 9, 16: ms per step
+    layers together, graph-captured) at B = 1, 2, 3, 4, 8, 9, 16: ms per step
     and the tokens it checks per second, next to B single-token steps."""
     mb = 16
     h = torch.zeros(dims["d"], dtype=torch.float32, device="cuda")
@@ -211,7 +211,7 @@ def verify_rates(q4, inputs, torch, dims, layers, decode_ms, reps=20):
     dec = q4.Decoder(dims, layers, h, ws, max_batch=mb, h_batch=hb)
     stream = torch.cuda.Stream()
     out = {}
-    for B in (1, 2, 4, 8, 9, 16):
+    for B in (1, 2, 3, 4, 8, 9, 16):
         with torch.cuda.stream(stream):
             dec.verify_graph(B, stream)
             dec.verify_graph(B, stream)
@@ -482,8 +482,8 @@ def gemm_counter_sample(q4, inputs, torch):
 
 
 def bench_gemm(args, q4, inputs, torch):
-    """Small-batch product on the four 8B matrix shapes, B in {1, 2, 4, 8,
-    16}: distinct weight copies (> 512 MB per shape) launched round-robin
+    """Small-batch product on the four 8B matrix shapes, B in {1, 2, 3, 4,
+    8, 16}: distinct weight copies (> 512 MB per shape) launched round-robin
     inside a captured graph; GB/s and effective TFLOP/s = 2NKB / t for the
     library's choice of kernel, plus both paths side by side (vector-ALU
     batch kernel where its columns fit, matrix-core kernel) to show the
@@ -501,7 +501,7 @@ def bench_gemm(args, q4, inputs, torch):
         Ws = [(inputs.random_bytes(N, K, inputs.seed_of(3, i, 0), device="cuda"),
                inputs.scales(N, K, inputs.seed_of(3, i, 1), device="cuda"))
               for i in range(copies)]
-        for B in (1, 2, 4, 8, 16):
+        for B in (1, 2, 3, 4, 8, 16):
             X = inputs.act_f16((B, K), inputs.seed_of(3, 0, 2) + B, device="cuda")
             Y = torch.empty(B, N, dtype=torch.float32, device="cuda")
             nbytes = wbytes + 2 * B * K + 4 * B * N
@@ -521,7 +521,7 @@ def bench_gemm(args, q4, inputs, torch):
                 mf = [(lambda st, p=p, sc=sc: q4.q4_gemm_tuned(p, sc, X, Y, rt, 4, stream=st))
                       for p, sc in Ws]
                 table[f"{name}_B{B}"]["mfma_us"] = round(graph_avg_us(torch, mf, stream), 3)
-                if B in (2, 4, 8) and B * K * 2 <= 65536:
+                if B in (2, 3, 4, 8) and B * K * 2 <= 65536:
                     va = [(lambda st, p=p, sc=sc: q4.q4_gemm_valu(p, sc, X, Y, stream=st))
                           for p, sc in Ws]
                     table[f"{name}_B{B}"]["valu_us"] = round(graph_avg_us(torch, va, stream), 3)

@@ -18,8 +18,10 @@
 //   gemv_rowp_kernel  wider rows: a group's chunks in phases of PH chunks
 //                     per lane (the wave's registers hold one phase), the
 //                     activation read from LDS chunk by chunk;
-//   gemv_row_batch_kernel  2..4 (8) binary16 columns staged in LDS, the
-//                     chunks in phases as well.
+//   gemv_row_batch_kernel  2..4 (8) binary16 columns staged in LDS; up to
+//                     K = 4096 and three columns every column's activation
+//                     chunks of the lane held in registers as above, wider
+//                     rows or batches in phases read from LDS.
 // The workgroup stages the activation, or its RMSNorm, once with linear
 // loads, with the staging code of the other product kernel (the same bits).
 //
@@ -377,37 +379,81 @@ gemv_rowp_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
     }
 }
 
+// Residual epilogue of the batch kernel: the old value of the output that
+// this lane stores in group g (lane r * B + b stores row r of column b).
+template <int R, int B, Epi E>
+__device__ __forceinline__ float batch_residual_of(const EpiArgs &ea, int64_t N, int64_t g,
+                                                   int lane, int64_t n_units) {
+    if constexpr (E == Epi::Residual) {
+        const int l = lane < R * B ? lane : 0;
+        return gload(ea.y + (size_t)(l % B) * N + group_row<E, R>(g, l / B, n_units, ea));
+    } else {
+        return 0.0f;
+    }
+}
+
 // B binary16 columns X16[B][K] staged in LDS (pair order, [B][4][C]); per
 // column the batch-1 kernels' arithmetic and order, the chunks in phases of
-// PH per lane (PH = chunks per lane up to K = 4096, else four).  Store /
-// Residual: ea.y = Y f32 [B][N]; SiluPair: ea.out16 = M binary16
-// [B][pair_off].
-template <int PH, int R, int B, Epi E>
-__global__ void __launch_bounds__(kRowThreads)
+// PH per lane.  XR (PH = all chunks of a lane, K <= 4096): the lane's
+// activation chunks of every column copied from LDS into registers once,
+// as the batch-1 kernel does, and each row unpacked once per chunk for all
+// columns; otherwise every chunk's column pairs are read from LDS.  WV
+// waves per workgroup: more where the staged columns leave room for few
+// workgroups per compute unit.  Store / Residual: ea.y = Y f32 [B][N];
+// SiluPair: ea.out16 = M binary16 [B][pair_off].
+template <int PH, int R, int B, Epi E, int WV, bool XR>
+__global__ void __launch_bounds__(64 * WV)
 gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
                       const uint16_t *__restrict__ X16, int64_t N, int K, int64_t n_units,
                       EpiArgs ea) {
     static_assert(E != Epi::SiluPair || R % 2 == 0, "paired rows come in pairs");
+    static_assert(!XR || PH <= 2, "register-held activations: at most two chunks per lane");
     constexpr int UP = units_per_group<E, R>();
     extern __shared__ uint4 xs[];
     const int lane = threadIdx.x & 63;
     const int64_t wave =
-        __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kRowWaves + (threadIdx.x >> 6)));
-    const int64_t nwaves = (int64_t)gridDim.x * kRowWaves;
+        __builtin_amdgcn_readfirstlane((int)(blockIdx.x * WV + (threadIdx.x >> 6)));
+    const int64_t nwaves = (int64_t)gridDim.x * WV;
     const int C = K >> 5;
     const int nb = K >> 3; // 8-value blocks per column
     const int nc = (C + 63) / 64;
-    const int nph = (nc + PH - 1) / PH;
+    const int nph = XR ? 1 : (nc + PH - 1) / PH;
     const int64_t ngroups = (n_units + UP - 1) / UP;
+    // The columns' first SB blocks per thread are loaded before the weights,
+    // as the batch-1 kernels stage theirs: a wave's loads complete in issue
+    // order, so staging loads issued after the weights would wait for them.
+    // Indices past the end wrap around (no load behind a per-lane branch);
+    // blocks beyond SB per thread are staged after the weights by a loop.
+    constexpr int kT = 64 * WV;
+    constexpr int SB = XR ? (B * 512 + kT - 1) / kT : 8;
+    const int nblk = B * nb;
+    uint4 sv[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int i = threadIdx.x + j * kT;
+        sv[j] = gload16(X16 + 8 * (size_t)(i < nblk ? i : i % nblk));
+    }
     uint4 w[R][PH];
     uint16_t s[R][PH];
     RowChunks<PH> ch = row_chunks<PH>(lane, C);
     int64_t g = wave;
-    if (g < ngroups)
-        group_loads<PH, R, E>(W, S, C, n_units, ea, g, ch, w, s);
-    for (int i = threadIdx.x; i < B * nb; i += kRowThreads) {
-        const int b = i / nb, k8 = i - b * nb;
-        xs[(size_t)b * 4 * C + (k8 & 3) * C + (k8 >> 2)] = permute8(gload16(X16 + 8 * (size_t)i));
+    const int64_t g0 = g < ngroups ? g : ngroups - 1;
+    group_loads<PH, R, E>(W, S, C, n_units, ea, g0, ch, w, s);
+    float hv = batch_residual_of<R, B, E>(ea, N, g0, lane, n_units);
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int i = threadIdx.x + j * kT;
+        if (i < nblk) {
+            const int b = i / nb, k8 = i - b * nb;
+            xs[(size_t)b * 4 * C + (k8 & 3) * C + (k8 >> 2)] = permute8(sv[j]);
+        }
+    }
+    if constexpr (!XR) { // XR: SB covers every block of K <= 4096
+        for (int i = threadIdx.x + SB * kT; i < nblk; i += kT) {
+            const int b = i / nb, k8 = i - b * nb;
+            xs[(size_t)b * 4 * C + (k8 & 3) * C + (k8 >> 2)] =
+                permute8(gload16(X16 + 8 * (size_t)i));
+        }
     }
     __syncthreads();
     if (g >= ngroups)
@@ -415,6 +461,16 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
     const uint32_t bias = vgpr_const(0x64006400u);
     const half2_t off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
     const half2_t off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
+    uint4 xr[XR ? B : 1][XR ? PH : 1][4];
+    if constexpr (XR) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < PH; ++j)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    xr[b][j][p] = xs[(size_t)b * 4 * C + p * C + ch.c[j]];
+    }
     while (true) {
         float acc[R][B];
 #pragma unroll
@@ -423,8 +479,8 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
             for (int b = 0; b < B; ++b)
                 acc[r][b] = 0.0f;
         for (int ph = 0; ph < nph; ++ph) {
-            const int live = min(PH, nc - ph * PH);
-            if (ph > 0) {
+            const int live = XR ? PH : min(PH, nc - ph * PH);
+            if (!XR && ph > 0) {
                 ch = row_chunks<PH>(lane, C, ph * PH);
                 group_loads<PH, R, E>(W, S, C, n_units, ea, g, ch, w, s);
             }
@@ -432,50 +488,89 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
             for (int j = 0; j < PH; ++j) {
                 if (j >= live)
                     continue;
-                half2_t q[R][16];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint4 wv = w[r][j];
-                    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t v = wd[i], u = v >> 8;
-                        q[r][4 * i + 0] = as_h2((v & 0x000F000Fu) | bias) - off_lo;
-                        q[r][4 * i + 1] = as_h2((v & 0x00F000F0u) | bias) - off_hi;
-                        q[r][4 * i + 2] = as_h2((u & 0x000F000Fu) | bias) - off_lo;
-                        q[r][4 * i + 3] = as_h2((u & 0x00F000F0u) | bias) - off_hi;
-                    }
-                }
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    uint4 xq[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        xq[p] = xs[(size_t)b * 4 * C + p * C + ch.c[j]];
+                if constexpr (XR) {
+                    // one row at a time: its chunk unpacked once, then
+                    // multiplied with every column's registers
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float sc = ch.valid[j] ? f16_to_f32(s[r][j]) : 0.0f;
-                        float tlo = 0.0f, thi = 0.0f;
+                        half2_t q[16];
+                        const uint4 wv = w[r][j];
+                        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            tlo = __builtin_amdgcn_fdot2(q[r][4 * i + 0], as_h2(xq[i].x), tlo,
-                                                         false);
-                            thi = __builtin_amdgcn_fdot2(q[r][4 * i + 1], as_h2(xq[i].y), thi,
-                                                         false);
-                            tlo = __builtin_amdgcn_fdot2(q[r][4 * i + 2], as_h2(xq[i].z), tlo,
-                                                         false);
-                            thi = __builtin_amdgcn_fdot2(q[r][4 * i + 3], as_h2(xq[i].w), thi,
-                                                         false);
+                            const uint32_t v = wd[i], u = v >> 8;
+                            q[4 * i + 0] = as_h2((v & 0x000F000Fu) | bias) - off_lo;
+                            q[4 * i + 1] = as_h2((v & 0x00F000F0u) | bias) - off_hi;
+                            q[4 * i + 2] = as_h2((u & 0x000F000Fu) | bias) - off_lo;
+                            q[4 * i + 3] = as_h2((u & 0x00F000F0u) | bias) - off_hi;
                         }
-                        acc[r][b] = fmaf(sc, fmaf(thi, 0.0625f, tlo), acc[r][b]);
+                        const float sc = ch.valid[j] ? f16_to_f32(s[r][j]) : 0.0f;
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            float tlo = 0.0f, thi = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                tlo = __builtin_amdgcn_fdot2(q[4 * i + 0], as_h2(xr[b][j][i].x),
+                                                             tlo, false);
+                                thi = __builtin_amdgcn_fdot2(q[4 * i + 1], as_h2(xr[b][j][i].y),
+                                                             thi, false);
+                                tlo = __builtin_amdgcn_fdot2(q[4 * i + 2], as_h2(xr[b][j][i].z),
+                                                             tlo, false);
+                                thi = __builtin_amdgcn_fdot2(q[4 * i + 3], as_h2(xr[b][j][i].w),
+                                                             thi, false);
+                            }
+                            acc[r][b] = fmaf(sc, fmaf(thi, 0.0625f, tlo), acc[r][b]);
+                        }
+                    }
+                } else {
+                    half2_t q[R][16];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint4 wv = w[r][j];
+                        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t v = wd[i], u = v >> 8;
+                            q[r][4 * i + 0] = as_h2((v & 0x000F000Fu) | bias) - off_lo;
+                            q[r][4 * i + 1] = as_h2((v & 0x00F000F0u) | bias) - off_hi;
+                            q[r][4 * i + 2] = as_h2((u & 0x000F000Fu) | bias) - off_lo;
+                            q[r][4 * i + 3] = as_h2((u & 0x00F000F0u) | bias) - off_hi;
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        uint4 xq[4];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            xq[p] = xs[(size_t)b * 4 * C + p * C + ch.c[j]];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const float sc = ch.valid[j] ? f16_to_f32(s[r][j]) : 0.0f;
+                            float tlo = 0.0f, thi = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                tlo = __builtin_amdgcn_fdot2(q[r][4 * i + 0], as_h2(xq[i].x),
+                                                             tlo, false);
+                                thi = __builtin_amdgcn_fdot2(q[r][4 * i + 1], as_h2(xq[i].y),
+                                                             thi, false);
+                                tlo = __builtin_amdgcn_fdot2(q[r][4 * i + 2], as_h2(xq[i].z),
+                                                             tlo, false);
+                                thi = __builtin_amdgcn_fdot2(q[r][4 * i + 3], as_h2(xq[i].w),
+                                                             thi, false);
+                            }
+                            acc[r][b] = fmaf(sc, fmaf(thi, 0.0625f, tlo), acc[r][b]);
+                        }
                     }
                 }
             }
         }
         const int64_t gn = g + nwaves;
+        float hvn = 0.0f;
         if (gn < ngroups) {
-            ch = row_chunks<PH>(lane, C);
+            if constexpr (!XR)
+                ch = row_chunks<PH>(lane, C);
             group_loads<PH, R, E>(W, S, C, n_units, ea, gn, ch, w, s);
+            hvn = batch_residual_of<R, B, E>(ea, N, gn, lane, n_units);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -503,7 +598,7 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
                     if (lane == r * B + b && row < N) {
                         float *y = ea.y + (size_t)b * N + row;
                         if constexpr (E == Epi::Residual)
-                            *y = *y + acc[r][b];
+                            *y = hv + acc[r][b];
                         else
                             *y = acc[r][b];
                     }
@@ -511,6 +606,7 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
         }
         if (gn >= ngroups)
             break;
+        hv = hvn;
         g = gn;
     }
 }
@@ -576,29 +672,54 @@ RowFn pick_any(Epi e, Pro p, int NC, int PH, int R) {
     return nullptr;
 }
 
-template <int PH, Epi E>
-RowBatchFn pick_row_batch_b(int B) {
-    switch (B) {
-    case 2: return gemv_row_batch_kernel<PH, 2, 2, E>;
-    case 3: return gemv_row_batch_kernel<PH, 2, 3, E>;
-    case 4: return gemv_row_batch_kernel<PH, 2, 4, E>;
-    case 8:
-        if constexpr (E == Epi::Store)
-            return gemv_row_batch_kernel<PH, 2, 8, E>;
-        return nullptr;
-    default: return nullptr;
-    }
+// Launch shape of the 2..8-column product (PH chunks per phase, R rows per
+// group, WV waves per workgroup, XR register-held activations), from
+// graph-replayed launches over weight copies larger than the last-level
+// cache (us at two columns, 8B shapes):
+//   K <= 4096: two rows per group; at two and three columns the activation
+//     in registers (4096 x 4096: 4.8 against 5.3 from LDS, 6144 x 4096 6.2
+//     against 6.5); four rows per group hold too many registers (28672 x
+//     4096: 20.4 against 18.7 at two rows);
+//   K >= 12288 (two columns fill 56 KB of LDS, two workgroups per compute
+//     unit): one row in phases of seven with eight waves per workgroup
+//     (4096 x 14336: 12.3-12.7 against 18.5 with four waves and 13.0 with
+//     two rows per group).
+struct BatchCfg {
+    int PH, R, WV;
+    bool XR;
+};
+
+BatchCfg batch_config(int64_t K, int B) {
+    const int nc = (int)((K / 32 + 63) / 64);
+    if (nc <= 2)
+        return BatchCfg{nc, 2, 4, B <= 3};
+    if (nc >= 7)
+        return BatchCfg{7, 1, 8, false};
+    return BatchCfg{4, 2, 4, false};
 }
 
 template <Epi E>
-RowBatchFn pick_row_batch(int PH, int B) {
-    switch (PH) {
-    case 1: return pick_row_batch_b<1, E>(B);
-    case 2: return pick_row_batch_b<2, E>(B);
-    case 4: return pick_row_batch_b<4, E>(B);
-    default: return nullptr;
+RowBatchFn pick_row_batch(const BatchCfg &c, int B) {
+#define Q4_PICK(ph, r, b, wv, xr)                                                        \
+    if (c.PH == ph && c.R == r && B == b && c.WV == wv && c.XR == xr)                    \
+        return gemv_row_batch_kernel<ph, r, b, E, wv, xr>;
+    // two chunks or fewer per lane, two or three columns: registers
+    Q4_PICK(1, 2, 2, 4, true) Q4_PICK(1, 2, 3, 4, true)
+    Q4_PICK(2, 2, 2, 4, true) Q4_PICK(2, 2, 3, 4, true)
+    // four columns (eight for Store) at K <= 4096, and K = 8192
+    Q4_PICK(1, 2, 4, 4, false) Q4_PICK(2, 2, 4, 4, false)
+    Q4_PICK(4, 2, 2, 4, false) Q4_PICK(4, 2, 3, 4, false) Q4_PICK(4, 2, 4, 4, false)
+    if constexpr (E == Epi::Store) {
+        Q4_PICK(1, 2, 8, 4, false) Q4_PICK(2, 2, 8, 4, false) Q4_PICK(4, 2, 8, 4, false)
     }
+    // seven or more chunks per lane (two columns fit the stage up to K = 16384)
+    if constexpr (E != Epi::SiluPair) {
+        Q4_PICK(7, 1, 2, 8, false)
+    }
+#undef Q4_PICK
+    return nullptr;
 }
+
 
 // Launch shape of the batch-1 product by its shape (NC chunks per lane; PH
 // 0 for the all-chunks kernel, else chunks per phase; R rows per group;
@@ -692,20 +813,23 @@ q4_status launch_gemv_row_batch(const uint8_t *packed, const uint16_t *scales,
                                 const uint16_t *X16, int64_t N, int64_t K, int32_t B, Epi epi,
                                 const EpiArgs &ea, hipStream_t stream) {
     const int C = (int)(K / 32);
-    const int nc = (C + 63) / 64;
-    const int PH = nc <= 2 ? nc : 4;
-    const RowBatchFn fn = epi == Epi::SiluPair  ? pick_row_batch<Epi::SiluPair>(PH, B)
-                          : epi == Epi::Residual ? pick_row_batch<Epi::Residual>(PH, B)
-                          : epi == Epi::Store    ? pick_row_batch<Epi::Store>(PH, B)
+    const BatchCfg c = batch_config(K, B);
+    const RowBatchFn fn = epi == Epi::SiluPair  ? pick_row_batch<Epi::SiluPair>(c, B)
+                          : epi == Epi::Residual ? pick_row_batch<Epi::Residual>(c, B)
+                          : epi == Epi::Store    ? pick_row_batch<Epi::Store>(c, B)
                                                  : nullptr;
     if (!fn)
-        return fail(Q4_ERR_UNSUPPORTED, "gemv rows batch: no kernel for B=%d", B);
+        return fail(Q4_ERR_UNSUPPORTED, "gemv rows batch: no kernel for B=%d K=%lld", B,
+                    (long long)K);
     int64_t n_units = 0;
     Q4_CHECK(row_units(epi, N, ea, &n_units, "gemv rows batch"));
-    const int UP = epi == Epi::SiluPair ? 1 : 2;
-    const int64_t blocks = row_grid((n_units + UP - 1) / UP, 0);
+    const int UP = epi == Epi::SiluPair ? c.R / 2 : c.R;
+    const int64_t ngroups = (n_units + UP - 1) / UP;
+    // one group per wave, at most sixteen waves per compute unit
+    const int64_t blocks = std::max<int64_t>(
+        1, std::min<int64_t>((ngroups + c.WV - 1) / c.WV, 16 / c.WV * (int64_t)device_cus()));
     const size_t lds = (size_t)B * 4 * C * 16;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kRowThreads), lds, stream, packed, scales,
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * c.WV), lds, stream, packed, scales,
                        X16, N, (int)K, n_units, ea);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
