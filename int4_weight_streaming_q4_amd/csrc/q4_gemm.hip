@@ -1096,18 +1096,10 @@ q4_status launch_gemm_mfma_cfg(const uint8_t *packed, const uint16_t *scales,
     return Q4_OK;
 }
 
-// Two columns go to the vector-ALU batch kernel wherever they fit its LDS
-// stage, three only where the activation-resident launch does not apply
-// (three columns of the 28672 x 4096 gate+up: 22.0 us on the vector ALU,
-// the matrix cores' time at four columns is 20.8).
-static bool valu_batch(int64_t rows, int64_t K, int32_t B, bool paired) {
-    return gemv_batch_fits(B, K) && (B < 3 || xres_config(rows, K, B, paired).grid == 0);
-}
-
 q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const uint16_t *X16,
                            float *Y, int64_t N, int64_t K, int32_t B, hipStream_t stream,
                            bool accumulate) {
-    if (valu_batch(N, K, B, false)) {
+    if (gemv_batch_fits(B, K)) {
         EpiArgs ea{};
         ea.y = Y;
         return launch_gemv_batch(packed, scales, X16, N, K, B,
@@ -1125,7 +1117,12 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
 q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
                                 const uint16_t *X16, uint16_t *M, int64_t npair, int64_t K,
                                 int32_t B, hipStream_t stream) {
-    if (valu_batch(npair, K, B, true)) {
+    // Three columns take the activation-resident launch where it applies:
+    // the vector-ALU kernel's paired form needs 171 registers there (two
+    // waves per SIMD), and the 8B verify step at three columns took 1.82 ms
+    // with it against 1.72 ms with the matrix cores.
+    const bool xres3 = B == 3 && xres_config(npair, K, B, true).grid > 0;
+    if (gemv_batch_fits(B, K) && !xres3) {
         EpiArgs ea{};
         ea.out16 = M;
         ea.pair_off = npair;

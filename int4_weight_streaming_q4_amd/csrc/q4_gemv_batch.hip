@@ -252,10 +252,10 @@ int batch_resident_blocks(BatchFn fn, size_t lds) {
 
 } // namespace
 
-// Up to three columns; from four the matrix-core kernel is faster on every
-// 8B shape (B = 4, vector ALU / matrix cores: 6144 x 4096 9.55 / 8.63 us,
-// 4096 x 4096 7.88 / 7.06, 28672 x 4096 25.6 / 24.2; at B = 3 8.29 / 8.64,
-// 6.79 / 7.07, 22.3 / 24.5).
+// Up to three columns.  From four the matrix cores win or tie on the 8B
+// shapes (B = 4, vector ALU / the library's matrix-core launch, us: 6144 x
+// 4096 8.49 / 8.63, 4096 x 4096 6.48 / 5.86, 28672 x 4096 24.7 / 20.0); at
+// three 7.13 / 8.66, 5.31 / 6.59 and 20.9 / 24.6 (row-tile launch).
 bool gemv_batch_fits(int32_t B, int64_t K) {
     return B >= 2 && B <= kBatchMaxCols && (int64_t)B * K * 2 <= kBatchStageBytes;
 }

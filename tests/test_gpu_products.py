@@ -391,15 +391,10 @@ def test_gemm_special_values(B):
     assert np.array_equal(Y.astype(np.float64), Y_ref)
 
 
-def _valu_path(B, K, N):
-    """The library's rule: two columns whose binary16 copies fit 64 KB of LDS
-    run the vector-ALU batch kernel, three as well unless the product is tall
-    enough for the activation-resident launch (four or more 16-row tiles per
-    compute unit); wider batches the matrix cores."""
-    tiles = -(-N // 16)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    resident = -(-tiles // min(cus, tiles)) >= 4
-    return 2 <= B <= 3 and B * K * 2 <= 65536 and not (B == 3 and resident)
+def _valu_path(B, K):
+    """The library's rule: 2 <= B <= 3 columns whose binary16 copies fit 64 KB
+    of LDS run the vector-ALU batch kernel; wider batches the matrix cores."""
+    return 2 <= B <= 3 and B * K * 2 <= 65536
 
 
 @pytest.mark.parametrize("name", ["8b_gate_up", "8b_down"])
@@ -416,14 +411,14 @@ def test_gemm_columns_independent_of_batch(name):
     gemv_cols = [_gemv(packed, scales, X[b].contiguous()) for b in range(4)]
     for B in (2, 3, 4, 5, 9):
         Y = _gemm(packed, scales, X[:B].contiguous())
-        if _valu_path(B, K, N):
+        if _valu_path(B, K):
             for b in range(B):
                 assert np.array_equal(Y[b], gemv_cols[b]), (B, b)
         else:
             assert np.array_equal(Y, full[:B]), B
     perm = torch.tensor([5, 0, 3])
     Yp = _gemm(packed, scales, X[perm].contiguous())
-    if _valu_path(3, K, N):
+    if _valu_path(3, K):
         for i, b in enumerate(perm.tolist()):
             assert np.array_equal(Yp[i], _gemv(packed, scales, X[b].contiguous()))
     else:
@@ -453,7 +448,7 @@ def test_gemm_valu_columns_are_gemv(N, K, B):
     Yh = Y.cpu().numpy()
     for b in range(B):
         assert np.array_equal(Yh[b], _gemv(packed, scales, X[b].contiguous())), (N, K, B, b)
-    if _valu_path(B, K, N):
+    if _valu_path(B, K):
         assert np.array_equal(_gemm(packed, scales, X), Yh)
     Y_ref, M = oracle.gemm(u8(packed), u16(scales), u16(X))
     for b in (0, B - 1):
