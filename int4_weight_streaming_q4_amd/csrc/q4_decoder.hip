@@ -344,8 +344,21 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
                                  L.down.K, Epi::Residual, ea, s));
             continue;
         }
-        Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
-        if (dec->kv) {
+        // Two or three columns of K <= 4096: the QKV product normalises its
+        // columns itself (one launch less), else a norm kernel first.
+        const bool norm_qkv = batch_norm_fits(L.qkv.K, B);
+        if (norm_qkv) {
+            EpiArgs ea{};
+            ea.y = dec->qkvb;
+            ea.eps = eps;
+            Q4_CHECK(launch_batch_norm_product(L.qkv.packed, L.qkv.scales, dec->hb, L.qkv.N,
+                                               L.qkv.K, B, Epi::Store, ea, s));
+        } else {
+            Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
+        }
+        if (dec->kv && norm_qkv) {
+            Q4_CHECK(enqueue_attention(dec, l, s, B, dec->qkvb, dec->oinb, false));
+        } else if (dec->kv) {
             // the QKV epilogue stores the columns' key and value rows and
             // rotated queries where the matrix-core row-tile launch runs
             const size_t S = (size_t)d.Hkv * (size_t)dec->desc.max_ctx * (size_t)d.hd;
@@ -364,16 +377,28 @@ q4_status enqueue_verify(Decoder *dec, int32_t B, hipStream_t s) {
                                           L.qkv.N, L.qkv.K, B, rp, s, &stored));
             Q4_CHECK(enqueue_attention(dec, l, s, B, dec->qkvb, dec->oinb, stored));
         } else {
-            Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb, L.qkv.N,
-                                      L.qkv.K, B, s));
+            if (!norm_qkv)
+                Q4_CHECK(launch_gemm_mfma(L.qkv.packed, L.qkv.scales, dec->xb, dec->qkvb,
+                                          L.qkv.N, L.qkv.K, B, s));
             Q4_CHECK(launch_gather_batch(dec->qkvb, dec->oinb, B, (int32_t)d.H, (int32_t)d.Hkv,
                                          (int32_t)d.hd, s));
         }
         Q4_CHECK(launch_gemm_mfma(L.o.packed, L.o.scales, dec->oinb, dec->hb, L.o.N, L.o.K, B, s,
                                   true));
-        Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
-        Q4_CHECK(launch_gemm_silu_pair(L.gate_up.packed, L.gate_up.scales, dec->xb,
-                                       dec->mlpb, d.dff, L.gate_up.K, B, s));
+        // gate+up likewise where its columns run on the vector ALU
+        if (silu_pair_on_valu(d.dff, L.gate_up.K, B) && batch_norm_fits(L.gate_up.K, B)) {
+            EpiArgs ea{};
+            ea.out16 = dec->mlpb;
+            ea.pair_off = d.dff;
+            ea.eps = eps;
+            Q4_CHECK(launch_batch_norm_product(L.gate_up.packed, L.gate_up.scales, dec->hb,
+                                               L.gate_up.N, L.gate_up.K, B, Epi::SiluPair, ea,
+                                               s));
+        } else {
+            Q4_CHECK(launch_rmsnorm_batch(dec->hb, dec->xb, B, (int32_t)d.d, eps, s));
+            Q4_CHECK(launch_gemm_silu_pair(L.gate_up.packed, L.gate_up.scales, dec->xb,
+                                           dec->mlpb, d.dff, L.gate_up.K, B, s));
+        }
         Q4_CHECK(launch_gemm_mfma(L.down.packed, L.down.scales, dec->mlpb, dec->hb, L.down.N,
                                   L.down.K, B, s, true));
     }

@@ -29,6 +29,7 @@
 #include <mutex>
 
 #include "q4_internal.h"
+#include "q4_verify.h"
 
 namespace q4 {
 namespace {
@@ -1114,15 +1115,18 @@ q4_status launch_gemm_mfma(const uint8_t *packed, const uint16_t *scales, const 
                                 pick_waves(N), stream, accumulate);
 }
 
+// Three columns take the activation-resident launch where it applies: the
+// vector-ALU kernel's paired form needs 171 registers there (two waves per
+// SIMD), and the 8B verify step at three columns took 1.82 ms with it
+// against 1.72 ms with the matrix cores.
+bool silu_pair_on_valu(int64_t npair, int64_t K, int32_t B) {
+    return gemv_batch_fits(B, K) && !(B == 3 && xres_config(npair, K, B, true).grid > 0);
+}
+
 q4_status launch_gemm_silu_pair(const uint8_t *packed, const uint16_t *scales,
                                 const uint16_t *X16, uint16_t *M, int64_t npair, int64_t K,
                                 int32_t B, hipStream_t stream) {
-    // Three columns take the activation-resident launch where it applies:
-    // the vector-ALU kernel's paired form needs 171 registers there (two
-    // waves per SIMD), and the 8B verify step at three columns took 1.82 ms
-    // with it against 1.72 ms with the matrix cores.
-    const bool xres3 = B == 3 && xres_config(npair, K, B, true).grid > 0;
-    if (gemv_batch_fits(B, K) && !xres3) {
+    if (silu_pair_on_valu(npair, K, B)) {
         EpiArgs ea{};
         ea.out16 = M;
         ea.pair_off = npair;

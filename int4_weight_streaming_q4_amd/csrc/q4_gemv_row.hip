@@ -35,6 +35,7 @@
 
 #include "q4_gemv_core.h"
 #include "q4_lanes.h"
+#include "q4_verify.h"
 
 namespace q4 {
 namespace {
@@ -392,24 +393,104 @@ __device__ __forceinline__ float batch_residual_of(const EpiArgs &ea, int64_t N,
     }
 }
 
-// B binary16 columns X16[B][K] staged in LDS (pair order, [B][4][C]); per
-// column the batch-1 kernels' arithmetic and order, the chunks in phases of
-// PH per lane.  XR (PH = all chunks of a lane, K <= 4096): the lane's
-// activation chunks of every column copied from LDS into registers once,
-// as the batch-1 kernel does, and each row unpacked once per chunk for all
-// columns; otherwise every chunk's column pairs are read from LDS.  WV
-// waves per workgroup: more where the staged columns leave room for few
-// workgroups per compute unit.  Store / Residual: ea.y = Y f32 [B][N];
-// SiluPair: ea.out16 = M binary16 [B][pair_off].
-template <int PH, int R, int B, Epi E, int WV, bool XR>
+// RMSNorm prologue of the batch kernel for B fp32 columns h[B][K], K <=
+// 4096, four waves: per column exactly the single-token prologue's
+// operations in its order (thread t sums the squares of its blocks t,
+// t + 256 in that order, then the wave sums and the four wave totals in
+// wave order), so every column stages the bits its token alone would.
+// Loads: issued by rmsnorm_issue before the weights; blocks past the
+// column's end wrap around (no load behind a per-lane branch).
+constexpr int kNormBlocks = 2; // blocks of 8 values per thread and column (K <= 4096)
+
+template <int B>
+struct NormStage {
+    uint4 v[B][kNormBlocks][2];
+};
+
+template <int B>
+__device__ __forceinline__ void rmsnorm_issue(const float *h, int K, NormStage<B> &st) {
+    const int nb8 = K >> 3;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < kNormBlocks; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            const float *p = h + (size_t)b * K + 8 * (size_t)(i < nb8 ? i : i % nb8);
+            st.v[b][j][0] = gload16(p);
+            st.v[b][j][1] = gload16(p + 4);
+        }
+}
+
+template <int B>
+__device__ __forceinline__ void rmsnorm_finish(uint4 *xs, int K, const EpiArgs &ea,
+                                               float (*wsum)[kWaves], const NormStage<B> &st) {
+    const int C = K >> 5;
+    const int nb8 = K >> 3;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kNormBlocks; ++j) {
+            if (threadIdx.x + j * kThreads < nb8) {
+                float f[8];
+                unpack_f32x8(st.v[b][j][0], st.v[b][j][1], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    ss = fmaf(f[i], f[i], ss);
+            }
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0)
+            wsum[b][threadIdx.x >> 6] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float tot = wsum[b][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            tot += wsum[b][w];
+        const float r = 1.0f / sqrtf(tot / (float)K + eps_of(ea));
+#pragma unroll
+        for (int j = 0; j < kNormBlocks; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (i < nb8) {
+                float f[8];
+                unpack_f32x8(st.v[b][j][0], st.v[b][j][1], f);
+                uint32_t p[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    p[q] = (uint32_t)f32_to_f16(f[2 * q] * r) |
+                           ((uint32_t)f32_to_f16(f[2 * q + 1] * r) << 16);
+                xs[(size_t)b * 4 * C + (i & 3) * C + (i >> 2)] =
+                    permute8(uint4{p[0], p[1], p[2], p[3]});
+            }
+        }
+    }
+}
+
+// B columns staged in LDS (pair order, [B][4][C]): binary16 columns
+// X16[B][K] (P = F16), or the RMSNorm of fp32 columns h[B][K] (P =
+// RmsNorm, with XR and four waves; ea.eps).  Per column the batch-1
+// kernels' arithmetic and order, the chunks in phases of PH per lane.  XR
+// (PH = all chunks of a lane, K <= 4096): the lane's activation chunks of
+// every column copied from LDS into registers once, as the batch-1 kernel
+// does, and each row unpacked once per chunk for all columns; otherwise
+// every chunk's column pairs are read from LDS.  WV waves per workgroup:
+// more where the staged columns leave room for few workgroups per compute
+// unit.  Store / Residual: ea.y = Y f32 [B][N]; SiluPair: ea.out16 = M
+// binary16 [B][pair_off].
+template <int PH, int R, int B, Epi E, int WV, bool XR, Pro P>
 __global__ void __launch_bounds__(64 * WV)
 gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ S,
-                      const uint16_t *__restrict__ X16, int64_t N, int K, int64_t n_units,
+                      const void *__restrict__ xin, int64_t N, int K, int64_t n_units,
                       EpiArgs ea) {
     static_assert(E != Epi::SiluPair || R % 2 == 0, "paired rows come in pairs");
     static_assert(!XR || PH <= 2, "register-held activations: at most two chunks per lane");
+    static_assert(P == Pro::F16 || (XR && WV == kWaves), "the norm prologue: XR, four waves");
     constexpr int UP = units_per_group<E, R>();
     extern __shared__ uint4 xs[];
+    const uint16_t *X16 = static_cast<const uint16_t *>(xin);
     const int lane = threadIdx.x & 63;
     const int64_t wave =
         __builtin_amdgcn_readfirstlane((int)(blockIdx.x * WV + (threadIdx.x >> 6)));
@@ -425,13 +506,18 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
     // Indices past the end wrap around (no load behind a per-lane branch);
     // blocks beyond SB per thread are staged after the weights by a loop.
     constexpr int kT = 64 * WV;
-    constexpr int SB = XR ? (B * 512 + kT - 1) / kT : 8;
+    constexpr int SB = P == Pro::RmsNorm ? 1 : XR ? (B * 512 + kT - 1) / kT : 8;
     const int nblk = B * nb;
     uint4 sv[SB];
+    NormStage<P == Pro::RmsNorm ? B : 1> nst;
+    if constexpr (P == Pro::RmsNorm) {
+        rmsnorm_issue<B>(static_cast<const float *>(xin), K, nst);
+    } else {
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-        const int i = threadIdx.x + j * kT;
-        sv[j] = gload16(X16 + 8 * (size_t)(i < nblk ? i : i % nblk));
+        for (int j = 0; j < SB; ++j) {
+            const int i = threadIdx.x + j * kT;
+            sv[j] = gload16(X16 + 8 * (size_t)(i < nblk ? i : i % nblk));
+        }
     }
     uint4 w[R][PH];
     uint16_t s[R][PH];
@@ -440,12 +526,17 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
     const int64_t g0 = g < ngroups ? g : ngroups - 1;
     group_loads<PH, R, E>(W, S, C, n_units, ea, g0, ch, w, s);
     float hv = batch_residual_of<R, B, E>(ea, N, g0, lane, n_units);
+    if constexpr (P == Pro::RmsNorm) {
+        __shared__ float wsum[B][kWaves];
+        rmsnorm_finish<B>(xs, K, ea, wsum, nst);
+    } else {
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-        const int i = threadIdx.x + j * kT;
-        if (i < nblk) {
-            const int b = i / nb, k8 = i - b * nb;
-            xs[(size_t)b * 4 * C + (k8 & 3) * C + (k8 >> 2)] = permute8(sv[j]);
+        for (int j = 0; j < SB; ++j) {
+            const int i = threadIdx.x + j * kT;
+            if (i < nblk) {
+                const int b = i / nb, k8 = i - b * nb;
+                xs[(size_t)b * 4 * C + (k8 & 3) * C + (k8 >> 2)] = permute8(sv[j]);
+            }
         }
     }
     if constexpr (!XR) { // XR: SB covers every block of K <= 4096
@@ -613,7 +704,7 @@ gemv_row_batch_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict_
 
 using RowFn = void (*)(const uint8_t *, const uint16_t *, const void *, int64_t, int, int64_t,
                        EpiArgs);
-using RowBatchFn = void (*)(const uint8_t *, const uint16_t *, const uint16_t *, int64_t, int,
+using RowBatchFn = void (*)(const uint8_t *, const uint16_t *, const void *, int64_t, int,
                             int64_t, EpiArgs);
 
 template <Epi E, Pro P>
@@ -698,11 +789,25 @@ BatchCfg batch_config(int64_t K, int B) {
     return BatchCfg{4, 2, 4, false};
 }
 
+// RMSNorm prologue (P = RmsNorm): the register-held shapes of the products
+// that follow a norm in the verify step (QKV: Store; gate+up: SiluPair).
+template <Epi E>
+RowBatchFn pick_row_batch_norm(const BatchCfg &c, int B) {
+#define Q4_PICK(ph, b)                                                                   \
+    if (c.PH == ph && c.R == 2 && B == b && c.WV == kWaves && c.XR)                      \
+        return gemv_row_batch_kernel<ph, 2, b, E, kWaves, true, Pro::RmsNorm>;
+    if constexpr (E == Epi::Store || E == Epi::SiluPair) {
+        Q4_PICK(1, 2) Q4_PICK(1, 3) Q4_PICK(2, 2) Q4_PICK(2, 3)
+    }
+#undef Q4_PICK
+    return nullptr;
+}
+
 template <Epi E>
 RowBatchFn pick_row_batch(const BatchCfg &c, int B) {
 #define Q4_PICK(ph, r, b, wv, xr)                                                        \
     if (c.PH == ph && c.R == r && B == b && c.WV == wv && c.XR == xr)                    \
-        return gemv_row_batch_kernel<ph, r, b, E, wv, xr>;
+        return gemv_row_batch_kernel<ph, r, b, E, wv, xr, Pro::F16>;
     // two chunks or fewer per lane, two or three columns: registers
     Q4_PICK(1, 2, 2, 4, true) Q4_PICK(1, 2, 3, 4, true)
     Q4_PICK(2, 2, 2, 4, true) Q4_PICK(2, 2, 3, 4, true)
@@ -809,15 +914,11 @@ q4_status launch_gemv_row(const uint8_t *packed, const uint16_t *scales, const v
     return launch_row_fn(fn, packed, scales, xin, N, K, epi, ea, c.R, c.grid, stream);
 }
 
-q4_status launch_gemv_row_batch(const uint8_t *packed, const uint16_t *scales,
-                                const uint16_t *X16, int64_t N, int64_t K, int32_t B, Epi epi,
-                                const EpiArgs &ea, hipStream_t stream) {
-    const int C = (int)(K / 32);
-    const BatchCfg c = batch_config(K, B);
-    const RowBatchFn fn = epi == Epi::SiluPair  ? pick_row_batch<Epi::SiluPair>(c, B)
-                          : epi == Epi::Residual ? pick_row_batch<Epi::Residual>(c, B)
-                          : epi == Epi::Store    ? pick_row_batch<Epi::Store>(c, B)
-                                                 : nullptr;
+namespace {
+
+q4_status launch_row_batch_fn(RowBatchFn fn, const BatchCfg &c, const uint8_t *packed,
+                              const uint16_t *scales, const void *xin, int64_t N, int64_t K,
+                              int32_t B, Epi epi, const EpiArgs &ea, hipStream_t stream) {
     if (!fn)
         return fail(Q4_ERR_UNSUPPORTED, "gemv rows batch: no kernel for B=%d K=%lld", B,
                     (long long)K);
@@ -828,11 +929,40 @@ q4_status launch_gemv_row_batch(const uint8_t *packed, const uint16_t *scales,
     // one group per wave, at most sixteen waves per compute unit
     const int64_t blocks = std::max<int64_t>(
         1, std::min<int64_t>((ngroups + c.WV - 1) / c.WV, 16 / c.WV * (int64_t)device_cus()));
-    const size_t lds = (size_t)B * 4 * C * 16;
+    const size_t lds = (size_t)B * 4 * (size_t)(K / 32) * 16;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * c.WV), lds, stream, packed, scales,
-                       X16, N, (int)K, n_units, ea);
+                       xin, N, (int)K, n_units, ea);
     Q4_HIP(hipGetLastError());
     return Q4_OK;
+}
+
+} // namespace
+
+q4_status launch_gemv_row_batch(const uint8_t *packed, const uint16_t *scales,
+                                const uint16_t *X16, int64_t N, int64_t K, int32_t B, Epi epi,
+                                const EpiArgs &ea, hipStream_t stream) {
+    const BatchCfg c = batch_config(K, B);
+    const RowBatchFn fn = epi == Epi::SiluPair  ? pick_row_batch<Epi::SiluPair>(c, B)
+                          : epi == Epi::Residual ? pick_row_batch<Epi::Residual>(c, B)
+                          : epi == Epi::Store    ? pick_row_batch<Epi::Store>(c, B)
+                                                 : nullptr;
+    return launch_row_batch_fn(fn, c, packed, scales, X16, N, K, B, epi, ea, stream);
+}
+
+bool batch_norm_fits(int64_t K, int32_t B) {
+    return gemv_batch_fits(B, K) && batch_config(K, B).XR;
+}
+
+q4_status launch_batch_norm_product(const uint8_t *packed, const uint16_t *scales,
+                                    const float *H, int64_t N, int64_t K, int32_t B, Epi epi,
+                                    const EpiArgs &ea, hipStream_t stream) {
+    if (!batch_norm_fits(K, B))
+        return fail(Q4_ERR_UNSUPPORTED, "batch norm product: B=%d K=%lld", B, (long long)K);
+    const BatchCfg c = batch_config(K, B);
+    const RowBatchFn fn = epi == Epi::SiluPair ? pick_row_batch_norm<Epi::SiluPair>(c, B)
+                          : epi == Epi::Store  ? pick_row_batch_norm<Epi::Store>(c, B)
+                                               : nullptr;
+    return launch_row_batch_fn(fn, c, packed, scales, H, N, K, B, epi, ea, stream);
 }
 
 } // namespace q4

@@ -78,6 +78,27 @@ def test_verify_single_column_is_the_decode_step():
     assert torch.equal(m.run(h0[None], True, s)[0], m.h.cpu())
 
 
+@pytest.mark.parametrize("B", [2, 3])
+def test_verify_few_columns_are_decode_steps(B):
+    """Two and three columns on shapes whose products all run on the
+    vector-ALU batch kernel (columns in the single-token order, the norm in
+    the QKV and gate+up prologues exactly as the single-token step computes
+    it, the V gather the same binary16 copy): every column equals the
+    single-token step of its token bitwise."""
+    n = 3
+    layers = make_layers(SMALL, 64, n)
+    m = VModel(SMALL, layers, max_batch=4)
+    s = torch.cuda.Stream()
+    H0 = columns(SMALL, 64, B)
+    got = m.run(H0, False, s)
+    for b in range(B):
+        m.h.copy_(H0[b].to(DEV))
+        torch.cuda.synchronize()
+        m.dec.step_eager(s)
+        s.synchronize()
+        assert torch.equal(got[b], m.h.cpu()), (B, b)
+
+
 def test_verify_column_independent_of_batch():
     """Within each product path a column's result does not depend on B or on
     the other columns (bitwise): up to three columns run the vector-ALU batch
