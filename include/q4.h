@@ -337,8 +337,10 @@ q4_status q4_decode_layer_noalloc(const q4_layer *layer, int32_t d_model, int32_
  * products as small-batch INT4 products of B columns (q4_gemm_smallbatch's
  * kernels; O and down add into h_batch), and the one-token glue between
  * them per column.  Column b ends exactly as if its token were decoded
- * alone (B = 1 runs the single-token kernels and equals
- * q4_decode_step_eager bitwise).  With a KV cache the columns are draft
+ * alone, within the product bound (B = 1 runs the single-token kernels and
+ * equals q4_decode_step_eager bitwise; two or three columns of a model
+ * whose products all fit the vector-ALU batch kernel, with the RMSNorm in
+ * the QKV and gate+up products' prologue, equal it bitwise as well).  With a KV cache the columns are draft
  * tokens at consecutive positions: column b at position ctx - 1 + b, ctx
  * the context length of the last q4_decoder_set_context; per layer all B
  * key/value rows are stored first, then every column attends causally over
